@@ -1,0 +1,255 @@
+/*
+ * sa.h -- C ABI of the top-k sparse decode attention library (libsa.so).
+ *
+ * One decode step of one attention layer, for a batch of sequences whose keys
+ * and values sit in a device-resident KV cache:
+ *   1. score every cached token against the current query   (sa_score)
+ *   2. keep the top-k tokens or token blocks per row          (sa_topk)
+ *   3. gather only those K/V rows and run a split-K
+ *      online-softmax decode over them                        (sa_sparse_decode)
+ * plus full-attention decode for layers routed dense (sa_dense_decode) and a
+ * per-layer mode flag that runs one of these paths or reuses the index set of
+ * an earlier layer (sa_decode_layer, sa_plan_validate).
+ *
+ * Sources for what each call computes (pages describing the method):
+ *   [P1] "Flux Attention: Context-Aware Hybrid Attention for Efficient LLMs
+ *        Inference", paper review: per-layer hard choice of full or sparse
+ *        attention (key terms; method).
+ *   [P2] "HyLRA: Hybrid Layer Reuse Attention", technical summary: index reuse
+ *        across layers (sections 2.2-2.3), 128-token blocks (section 2.4).
+ *   [P3] "Inference-time context sparsity: illusion or opportunity?",
+ *        technical summary: oracle top-k (section 2), a sparse decode kernel
+ *        with irregular token-level sparsity and O(k*d) traffic (section 3.C).
+ *   [P5] "Flash Attention vs Sparse Attention": tiling with online softmax;
+ *        DSA indexer (Stage 1) and selective attention (Stage 2); IndexCache.
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument named *_cache, q, out, scores, idx*, kmin, kmax,
+ *     ws is a DEVICE pointer; descriptors and plan arrays are HOST pointers.
+ *   - The caller owns every buffer.  No call allocates or frees device memory
+ *     or keeps state between calls.
+ *   - Every call validates its arguments on the host first.  On an invalid
+ *     argument it returns an error code with NOTHING enqueued; the reason is
+ *     available from sa_last_error() on the calling thread.
+ *   - On success the work is enqueued on `stream` and the call returns
+ *     without synchronising.  A launch failure returns SA_ERR_HIP.
+ *   - Calls are thread-safe.  Two calls that run concurrently must not share
+ *     a workspace.
+ *   - Workspaces: any call taking (ws, ws_bytes) needs at least the bytes the
+ *     matching *_workspace_size() function returns, 256-byte aligned.  A
+ *     workspace belongs to one call kind and one set of argument shapes (the
+ *     ones it was sized for).  Zero it once before its first use
+ *     (sa_workspace_init or any zero fill) and again after a failed call;
+ *     every completed call leaves the workspace ready for the next call of
+ *     the same kind and shapes (the split counters inside it are back at
+ *     zero), so it is not re-initialised per call.
+ *   - Layouts are row-major.  "Row" means one (sequence, KV head) pair.
+ *     Query head h belongs to KV head h / G with G = n_q_heads / n_kv_heads.
+ */
+#ifndef SA_H_
+#define SA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SA_OK = 0,
+  SA_ERR_NULL = 1,        /* a required pointer is null */
+  SA_ERR_SHAPE = 2,       /* a size, count, stride or k is out of range */
+  SA_ERR_ALIGN = 3,       /* a pointer or stride breaks 16-byte (ws: 256-byte) alignment */
+  SA_ERR_DTYPE = 4,       /* unknown dtype, or a dtype the call does not take */
+  SA_ERR_WORKSPACE = 5,   /* workspace missing or too small */
+  SA_ERR_UNSUPPORTED = 6, /* valid but not built (e.g. head_dim 96, group size 3) */
+  SA_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed */
+} sa_status;
+
+typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+
+/* One layer's KV cache and query shape.
+ *   K and V: element (b, h, t, i) at base + b*kv_stride_b + h*kv_stride_h
+ *            + t*kv_stride_t + i   (strides in ELEMENTS; K and V share them).
+ *   q:       [batch, n_q_heads, head_dim], contiguous, q_dtype.
+ * Limits: head_dim in {64, 128}; n_q_heads % n_kv_heads == 0 with the group
+ * size G in {1, 2, 4, 8}; 1 <= ctx_len < 2^31; kv_stride_t >= head_dim; every
+ * stride times the element size a multiple of 16 bytes; cache and q base
+ * pointers 16-byte aligned.  softmax_scale 0 means 1/sqrt(head_dim). */
+typedef struct {
+  int32_t batch;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int64_t ctx_len;
+  sa_dtype q_dtype;
+  sa_dtype kv_dtype;
+  int64_t kv_stride_b;
+  int64_t kv_stride_h;
+  int64_t kv_stride_t;
+  float softmax_scale;
+} sa_kv_desc;
+
+/* ---------------------------------------------------------------- scoring */
+
+typedef enum {
+  /* Exact score of every token of every row: [P3] section 2 (oracle top-k).
+   *   scores[b, r, t] = scale * sum_{g < G} q[b, r*G + g, :] . K[b, r, t, :]
+   * Output [batch, n_kv_heads, ctx_len] fp32. */
+  SA_SCORE_EXACT = 0,
+  /* Block upper bound from per-block key summaries: [P2] section 2.4.
+   *   scores[b, r, j] = sum_{g<G} sum_i max(q_gi * kmin[b,r,j,i], q_gi * kmax[b,r,j,i])
+   * (no scale).  Output [batch, n_kv_heads, ceil(ctx_len / block_size)] fp32. */
+  SA_SCORE_BLOCK_MINMAX = 1,
+  /* Low-dimensional indexer: [P5] DSA Stage 1.
+   *   scores[b, t] = sum_{h < n_idx_heads} w[b, h] * max(0, q_idx[b, h, :] . k_idx[b, t, :])
+   * Output [batch, ctx_len] fp32 (one row per sequence, shared by its KV heads). */
+  SA_SCORE_INDEXER = 2
+} sa_score_kind;
+
+typedef struct {
+  /* SA_SCORE_BLOCK_MINMAX: summaries from sa_block_summarize, kv_dtype,
+   * [batch, n_kv_heads, ceil(ctx_len / block_size), head_dim], contiguous. */
+  const void* kmin;
+  const void* kmax;
+  int32_t block_size;
+  /* SA_SCORE_INDEXER: q_idx [batch, n_idx_heads, idx_dim] bf16,
+   * k_idx [batch, ctx_len, idx_dim] bf16, w [batch, n_idx_heads] fp32, all
+   * contiguous; 1 <= n_idx_heads <= 16, idx_dim in {32, 64, 128}. */
+  const void* q_idx;
+  const void* k_idx;
+  const float* idx_w;
+  int32_t n_idx_heads;
+  int32_t idx_dim;
+} sa_score_aux;
+
+/* Score every cached token (or block).  `aux` may be null for SA_SCORE_EXACT. */
+sa_status sa_score(const sa_kv_desc* desc, sa_score_kind kind, const void* q, const void* k_cache,
+                   const sa_score_aux* aux, float* scores, hipStream_t stream);
+
+/* Per-block elementwise min and max of the keys: [P2] section 2.4 (fixed
+ * blocks, QUEST-compatible summaries).  kmin/kmax: [batch, n_kv_heads,
+ * ceil(ctx_len / block_size), head_dim] in kv_dtype, contiguous.  The last
+ * block summarises only the tokens below ctx_len.  1 <= block_size <= 4096. */
+sa_status sa_block_summarize(const sa_kv_desc* desc, int32_t block_size, const void* k_cache,
+                             void* kmin, void* kmax, hipStream_t stream);
+
+/* ------------------------------------------------------------------ top-k */
+
+/* Top-k of each row of an fp32 score matrix: [P3] section 2 (oracle top-k)
+ * and [P5] DSA Stage 1 (a top-K index list).
+ *   scores: [n_rows] rows of n values, row r starting at scores + r*row_stride
+ *           (row_stride >= n, in elements).
+ *   idx_out: [n_rows, k] int32, each row the k positions with the largest
+ *           scores in ASCENDING position order; equal scores are taken from
+ *           the lower position first; -0.0 equals +0.0; NaN ranks below
+ *           -inf.  The result is exact and deterministic.
+ * Limits: 1 <= n_rows < 2^22, 1 <= k <= n < 2^31. */
+sa_status sa_topk(const float* scores, int64_t n_rows, int64_t n, int64_t row_stride, int32_t k,
+                  int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t sa_topk_workspace_size(int64_t n_rows, int64_t n, int32_t k);
+
+/* ------------------------------------------------------------ attention */
+
+typedef enum {
+  /* idx [batch, n_kv_heads, n_idx] token positions, one set per row. */
+  SA_IDX_TOKEN_PER_KV_HEAD = 0,
+  /* idx [batch, n_idx] token positions shared by every KV head of a sequence. */
+  SA_IDX_TOKEN_SHARED = 1,
+  /* idx [batch, n_idx_rows=n_kv_heads, n_idx] ids of block_size-token blocks;
+   * a block covers tokens [j*block_size, min((j+1)*block_size, ctx_len)). */
+  SA_IDX_BLOCK_PER_KV_HEAD = 2
+} sa_index_kind;
+
+/* Attention of every query head over the selected set of its row only:
+ * [P5] DSA Stage 2 and [P3] section 3.C (a decode kernel for irregular
+ * token-level sparsity that reads O(k*d) of the cache).  For query head h of
+ * sequence b, with S the selected tokens of row (b, h / G):
+ *   out[b, h, :] = sum_{t in S} softmax_S(scale * q[b,h,:] . K[b,h/G,t,:]) * V[b,h/G,t,:]
+ * out: [batch, n_q_heads, head_dim] fp32.  Preconditions: every index in
+ * range and the indices of one row distinct (not checked); 1 <= n_idx.
+ * Computed as a split-K online softmax whose partial results are merged with
+ * a log-sum-exp combine inside the same launch ([P5] tiling + online softmax). */
+sa_status sa_sparse_decode(const sa_kv_desc* desc, const void* q, const void* k_cache,
+                           const void* v_cache, sa_index_kind ik, const int32_t* idx, int32_t n_idx,
+                           int32_t block_size, float* out, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+size_t sa_sparse_workspace_size(const sa_kv_desc* desc, sa_index_kind ik, int32_t n_idx,
+                                int32_t block_size);
+
+/* Full decode attention over all ctx_len tokens (layers routed to full
+ * attention, [P1]; the dense baseline of [P3] section 3.C).  Same output as
+ * sa_sparse_decode with S = [0, ctx_len). */
+sa_status sa_dense_decode(const sa_kv_desc* desc, const void* q, const void* k_cache,
+                          const void* v_cache, float* out, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+size_t sa_dense_workspace_size(const sa_kv_desc* desc);
+
+/* ----------------------------------------------------- per-layer mode flag */
+
+typedef enum {
+  SA_LAYER_DENSE = 0,  /* full attention; idx untouched */
+  SA_LAYER_SPARSE = 1, /* score -> top-k -> selected-set attention; WRITES idx */
+  SA_LAYER_REUSE = 2   /* selected-set attention over idx as given; READS idx */
+} sa_layer_mode;
+
+/* Everything one layer's decode step needs.  The score kind fixes the index
+ * kind: EXACT -> SA_IDX_TOKEN_PER_KV_HEAD, BLOCK_MINMAX ->
+ * SA_IDX_BLOCK_PER_KV_HEAD (aux.block_size), INDEXER -> SA_IDX_TOKEN_SHARED.
+ * k is the number of tokens (blocks for BLOCK_MINMAX) kept per row. */
+typedef struct {
+  sa_kv_desc desc;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  sa_score_kind score_kind;
+  sa_score_aux aux;
+  int32_t k;
+  float* out;
+  void* ws;
+  size_t ws_bytes;
+} sa_layer_args;
+
+/* One layer of decode under a per-layer mode: [P1] hard routing between full
+ * and sparse attention; [P2] sections 2.2-2.3 and [P5] IndexCache: a layer may
+ * reuse the top-k index set an earlier layer produced, unchanged.
+ *   DENSE:  sa_dense_decode.
+ *   SPARSE: sa_score -> sa_topk -> sa_sparse_decode, the index set written to
+ *           idx ([batch, n_kv_heads, k] or [batch, k] for INDEXER).
+ *   REUSE:  sa_sparse_decode over idx exactly as given (no scoring, no top-k);
+ *           idx must hold the set of an earlier SPARSE layer with the same
+ *           score kind and k.
+ * idx may be null for DENSE. */
+sa_status sa_decode_layer(const sa_layer_args* a, sa_layer_mode mode, int32_t* idx,
+                          hipStream_t stream);
+size_t sa_layer_workspace_size(const sa_layer_args* a, sa_layer_mode mode);
+
+/* Check a per-layer plan on the host: modes[l] in sa_layer_mode; a REUSE layer
+ * needs 0 <= src[l] < l with layer src[l] owning an index set (SPARSE, or a
+ * REUSE layer, which carries its source's set).  src[l] is ignored for other
+ * modes.  Returns SA_OK or SA_ERR_SHAPE (reason in sa_last_error). */
+sa_status sa_plan_validate(const int32_t* modes, const int32_t* src, int32_t n_layers);
+
+/* ----------------------------------------------------------------- misc */
+
+/* Zero a workspace region on `stream` (a fill kernel, so it is safe inside
+ * stream capture). */
+sa_status sa_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* sa_status_string(sa_status s);
+
+/* Detail of the last failing call on the calling thread ("" if none). */
+const char* sa_last_error(void);
+
+/* Library version string. */
+const char* sa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA_H_ */

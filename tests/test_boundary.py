@@ -1,0 +1,156 @@
+"""The C-ABI library: it loads, exports every call declared in include/sa.h,
+and rejects invalid arguments on the host with the documented status code
+(before anything could reach a GPU).  Runs without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import top_sparse_decode_sa_amd as T
+from top_sparse_decode_sa_amd import _binding as Bn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "sa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_call():
+    L = T.lib()
+    names = _declared()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), "libsa.so lacks %s" % n
+    assert set(names) == set(Bn.EXPORTED)
+    assert T.sa_version().startswith("sa ")
+
+
+def _desc(**kw):
+    d = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, ctx_len=1000, q_dtype=Bn.SA_BF16,
+             kv_dtype=Bn.SA_BF16, kv_stride_b=2 * 1000 * 128, kv_stride_h=1000 * 128,
+             kv_stride_t=128, softmax_scale=0.0)
+    d.update(kw)
+    return Bn.KVDesc(**d)
+
+
+FAKE = ctypes.c_void_p(1 << 20)     # aligned, never dereferenced (calls fail first)
+MIS = ctypes.c_void_p((1 << 20) + 4)
+
+
+def _sparse(desc, q=FAKE, k=FAKE, v=FAKE, ik=0, idx=FAKE, n_idx=10, bs=0, out=FAKE, ws=None,
+            nbytes=0):
+    return T.lib().sa_sparse_decode(ctypes.byref(desc) if desc is not None else None, q, k, v, ik,
+                                    idx, n_idx, bs, out, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), Bn.SA_ERR_UNSUPPORTED),
+    (dict(n_q_heads=12, n_kv_heads=4), Bn.SA_ERR_UNSUPPORTED),   # group of 3
+    (dict(n_q_heads=9), Bn.SA_ERR_SHAPE),
+    (dict(batch=0), Bn.SA_ERR_SHAPE),
+    (dict(ctx_len=0), Bn.SA_ERR_SHAPE),
+    (dict(ctx_len=1 << 31), Bn.SA_ERR_SHAPE),
+    (dict(kv_stride_t=64), Bn.SA_ERR_SHAPE),
+    (dict(kv_stride_t=132), Bn.SA_ERR_ALIGN),
+    (dict(q_dtype=5), Bn.SA_ERR_DTYPE),
+    (dict(softmax_scale=-1.0), Bn.SA_ERR_SHAPE),
+    (dict(softmax_scale=float("inf")), Bn.SA_ERR_SHAPE),
+])
+def test_descriptor_errors(kw, code):
+    assert _sparse(_desc(**kw)) == code
+    assert T.lib().sa_last_error().decode() != ""
+
+
+def test_pointer_index_and_workspace_errors():
+    L = T.lib()
+    d = _desc()
+    assert _sparse(None) == Bn.SA_ERR_NULL
+    assert _sparse(d, q=None) == Bn.SA_ERR_NULL
+    assert _sparse(d, k=MIS) == Bn.SA_ERR_ALIGN
+    assert _sparse(d, idx=None) == Bn.SA_ERR_NULL
+    assert _sparse(d, n_idx=0) == Bn.SA_ERR_SHAPE
+    assert _sparse(d, ik=9) == Bn.SA_ERR_SHAPE
+    assert _sparse(d, ik=Bn.SA_IDX_BLOCK_PER_KV_HEAD, bs=0) == Bn.SA_ERR_SHAPE
+    need = L.sa_sparse_workspace_size(ctypes.byref(d), 0, 10, 0)
+    assert need > 0 and need % 256 == 0
+    assert _sparse(d, ws=None, nbytes=0) == Bn.SA_ERR_WORKSPACE
+    assert _sparse(d, ws=FAKE, nbytes=need - 1) == Bn.SA_ERR_WORKSPACE
+    assert _sparse(d, ws=ctypes.c_void_p((1 << 20) + 16), nbytes=need) == Bn.SA_ERR_ALIGN
+    assert L.sa_dense_decode(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 0, None) == \
+        Bn.SA_ERR_WORKSPACE
+    assert L.sa_dense_workspace_size(ctypes.byref(_desc(head_dim=96))) == 0
+
+
+def test_topk_errors():
+    L = T.lib()
+    assert L.sa_topk(None, 1, 10, 10, 3, FAKE, None, 0, None) == Bn.SA_ERR_NULL
+    assert L.sa_topk(FAKE, 1, 10, 10, 0, FAKE, None, 0, None) == Bn.SA_ERR_SHAPE
+    assert L.sa_topk(FAKE, 1, 10, 10, 11, FAKE, None, 0, None) == Bn.SA_ERR_SHAPE
+    assert L.sa_topk(FAKE, 0, 10, 10, 3, FAKE, None, 0, None) == Bn.SA_ERR_SHAPE
+    assert L.sa_topk(FAKE, 1, 10, 9, 3, FAKE, None, 0, None) == Bn.SA_ERR_SHAPE
+    assert L.sa_topk(FAKE, 1 << 22, 10, 10, 3, FAKE, None, 0, None) == Bn.SA_ERR_SHAPE
+    assert L.sa_topk_workspace_size(1, 10, 11) == 0
+
+
+def test_score_and_summary_errors():
+    L = T.lib()
+    d = _desc()
+    aux = Bn.ScoreAux()
+    assert L.sa_score(ctypes.byref(d), 7, FAKE, FAKE, None, FAKE, None) == Bn.SA_ERR_SHAPE
+    assert L.sa_score(ctypes.byref(d), 0, FAKE, FAKE, None, None, None) == Bn.SA_ERR_NULL
+    assert L.sa_score(ctypes.byref(d), 1, FAKE, FAKE, None, FAKE, None) == Bn.SA_ERR_NULL
+    aux.block_size = 0
+    assert L.sa_score(ctypes.byref(d), 1, FAKE, FAKE, ctypes.byref(aux), FAKE, None) == Bn.SA_ERR_SHAPE
+    aux.n_idx_heads, aux.idx_dim = 17, 64
+    assert L.sa_score(ctypes.byref(d), 2, FAKE, FAKE, ctypes.byref(aux), FAKE, None) == Bn.SA_ERR_SHAPE
+    aux.n_idx_heads, aux.idx_dim = 4, 48
+    assert L.sa_score(ctypes.byref(d), 2, FAKE, FAKE, ctypes.byref(aux), FAKE, None) == \
+        Bn.SA_ERR_UNSUPPORTED
+    assert L.sa_block_summarize(ctypes.byref(d), 0, FAKE, FAKE, FAKE, None) == Bn.SA_ERR_SHAPE
+    assert L.sa_block_summarize(ctypes.byref(d), 128, FAKE, MIS, FAKE, None) == Bn.SA_ERR_ALIGN
+
+
+def test_layer_errors_and_sizes():
+    L = T.lib()
+    a = Bn.LayerArgs()
+    a.desc = _desc()
+    a.q = a.k_cache = a.v_cache = a.out = 1 << 20
+    a.score_kind = Bn.SA_SCORE_EXACT
+    a.k = 0
+    assert L.sa_decode_layer(ctypes.byref(a), Bn.SA_LAYER_SPARSE, FAKE, None) == Bn.SA_ERR_SHAPE
+    a.k = 1001
+    assert L.sa_decode_layer(ctypes.byref(a), Bn.SA_LAYER_SPARSE, FAKE, None) == Bn.SA_ERR_SHAPE
+    a.k = 64
+    assert L.sa_decode_layer(ctypes.byref(a), 5, FAKE, None) == Bn.SA_ERR_SHAPE
+    assert L.sa_decode_layer(ctypes.byref(a), Bn.SA_LAYER_SPARSE, None, None) == Bn.SA_ERR_NULL
+    assert L.sa_decode_layer(ctypes.byref(a), Bn.SA_LAYER_SPARSE, FAKE, None) == Bn.SA_ERR_WORKSPACE
+    s_sparse = L.sa_layer_workspace_size(ctypes.byref(a), Bn.SA_LAYER_SPARSE)
+    s_reuse = L.sa_layer_workspace_size(ctypes.byref(a), Bn.SA_LAYER_REUSE)
+    # SPARSE holds the [B, Hkv, N] fp32 scores on top of what REUSE needs
+    assert s_sparse >= s_reuse + 2 * 2 * 1000 * 4
+    a.score_kind = Bn.SA_SCORE_BLOCK_MINMAX
+    a.aux.block_size = 128
+    a.k = 9   # 8 blocks of 128 cover 1000 tokens
+    assert L.sa_decode_layer(ctypes.byref(a), Bn.SA_LAYER_REUSE, FAKE, None) == Bn.SA_ERR_NULL  # kmin
+    assert L.sa_layer_workspace_size(None, 0) == 0
+
+
+def test_plan_validate():
+    T.sa_plan_validate([1, 2, 2, 2], [-1, 0, 0, 0])
+    T.sa_plan_validate([0, 0, 1, 1, 1, 1, 1, 1], [-1] * 8)
+    T.sa_plan_validate([1, 2, 0, 2], [-1, 0, -1, 1])
+    for modes, src in [([2], [0]), ([1, 2], [-1, 1]), ([0, 2], [-1, 0]), ([1, 3], [-1, -1]),
+                       ([1, 2], [-1, -5])]:
+        with pytest.raises(T.SAError):
+            T.sa_plan_validate(modes, src)
+    assert T.lib().sa_plan_validate(None, None, 3) == Bn.SA_ERR_NULL
+    assert T.lib().sa_plan_validate(FAKE, FAKE, 0) == Bn.SA_ERR_SHAPE
+
+
+def test_status_strings():
+    for s in range(8):
+        assert T.lib().sa_status_string(s).decode().startswith("SA_")

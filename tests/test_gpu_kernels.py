@@ -1,0 +1,252 @@
+"""GPU parity of each C-ABI call against the CPU oracle on small and ragged
+inputs: every kernel family, every index kind, dtype, head size and group
+size, edge cases (k = 1, k = n, ties, -0.0, NaN, partial blocks, strided
+caches), at sizes the oracle finishes in seconds."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sa_synth as S
+import top_sparse_decode_sa_amd as T
+from gpu_util import check_out, dev, say, score_tol, to_dev, to_host_bits, verdicts
+
+pytestmark = pytest.mark.gpu
+
+RNG = np.random.default_rng(7)
+
+
+def _rand_cache(B, Hq, Hkv, N, d, dtype, seed):
+    rng = np.random.default_rng(seed)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = torch.from_numpy(rng.standard_normal((B, Hq, d)).astype(np.float32)).to(tdt)
+    k = torch.from_numpy(rng.standard_normal((B, Hkv, N, d)).astype(np.float32)).to(tdt)
+    v = torch.from_numpy(rng.standard_normal((B, Hkv, N, d)).astype(np.float32)).to(tdt)
+    return q, k, v
+
+
+def _f64(t):
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+# --------------------------------------------------------------------- top-k
+
+@pytest.mark.parametrize("n", [1, 2, 7, 100, 1000, 4097, 32773])
+def test_topk_bit_exact(n):
+    say("topk n=%d" % n)
+    rows = 5
+    vals = RNG.standard_normal((rows, n)).astype(np.float32)
+    vals[1] = np.round(vals[1] * 2) / 2          # heavy ties
+    vals[2, ::3] = -0.0
+    vals[2, 1::3] = 0.0
+    if n > 4:
+        vals[3, :4] = [np.inf, -np.inf, np.nan, np.nan]
+    vals[4] = 1.0                                 # all equal
+    x = torch.from_numpy(vals).to(dev())
+    for k in sorted({1, max(1, n // 50), max(1, n // 3), n}):
+        got = T.sa_topk(x, k).cpu().numpy()
+        for r in range(rows):
+            want = O.topk(vals[r].astype(np.float64), k)
+            assert np.array_equal(got[r], want), (n, k, r)
+
+
+def test_topk_row_stride():
+    say("topk row_stride")
+    base = RNG.standard_normal((6, 3000)).astype(np.float32)
+    view = torch.from_numpy(base).to(dev())[:, :2500]  # rows 3000 apart, n = 2500
+    got = T.sa_topk(view, 40).cpu().numpy()
+    for r in range(6):
+        assert np.array_equal(got[r], O.topk(base[r, :2500].astype(np.float64), 40))
+
+
+# ------------------------------------------------------------------- scoring
+
+@pytest.mark.parametrize("dtype,d,G", [("f32", 64, 4), ("bf16", 128, 4), ("bf16", 64, 8),
+                                       ("f32", 128, 1), ("bf16", 128, 2)])
+def test_score_exact(dtype, d, G):
+    say("score_exact", dtype, d, G)
+    B, Hkv, N = 2, 2, 1000
+    q, k, v = _rand_cache(B, Hkv * G, Hkv, N, d, dtype, 11)
+    s = T.sa_score(q.to(dev()), k.to(dev())).cpu().numpy()
+    qf, kf = _f64(q), _f64(k)
+    for b in range(B):
+        for r in range(Hkv):
+            want = O.scores_exact(qf[b, r * G:(r + 1) * G], kf[b, r], O.default_scale(d))
+            assert np.max(np.abs(s[b, r] - want)) <= score_tol(want)
+
+
+@pytest.mark.parametrize("dtype,d,bs,N", [("bf16", 128, 128, 1000), ("f32", 64, 16, 257),
+                                          ("bf16", 64, 128, 128)])
+def test_block_summaries_and_scores(dtype, d, bs, N):
+    say("block", dtype, d, bs, N)
+    B, Hkv, G = 2, 2, 4
+    q, k, v = _rand_cache(B, Hkv * G, Hkv, N, d, dtype, 12)
+    kd = k.to(dev())
+    kmin, kmax = T.sa_block_summarize(kd, bs)
+    sb = T.sa_score(q.to(dev()), kd, T.SA_SCORE_BLOCK_MINMAX, kmin=kmin, kmax=kmax,
+                    block_size=bs).cpu().numpy()
+    qf, kf = _f64(q), _f64(k)
+    mn_g, mx_g = _f64(kmin), _f64(kmax)
+    for b in range(B):
+        for r in range(Hkv):
+            mn, mx = O.block_summaries(kf[b, r], bs)
+            assert np.array_equal(mn_g[b, r], mn) and np.array_equal(mx_g[b, r], mx)
+            want = O.scores_block(qf[b, r * G:(r + 1) * G], mn, mx)
+            assert np.max(np.abs(sb[b, r] - want)) <= score_tol(want)
+
+
+@pytest.mark.parametrize("H,Di", [(4, 64), (3, 128), (16, 32)])
+def test_score_indexer(H, Di):
+    say("indexer", H, Di)
+    B, N = 2, 3001
+    rng = np.random.default_rng(13)
+    qi = torch.from_numpy(rng.standard_normal((B, H, Di)).astype(np.float32)).to(torch.bfloat16)
+    ki = torch.from_numpy(rng.standard_normal((B, N, Di)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy(rng.uniform(size=(B, H)).astype(np.float32))
+    q, kc, vc = _rand_cache(B, 8, 2, N, 128, "bf16", 1)
+    s = T.sa_score(q.to(dev()), kc.to(dev()), T.SA_SCORE_INDEXER, q_idx=qi.to(dev()),
+                   k_idx=ki.to(dev()), idx_w=w.to(dev())).cpu().numpy()
+    for b in range(B):
+        want = O.scores_indexer(_f64(qi)[b], _f64(ki)[b], w.numpy()[b].astype(np.float64))
+        assert np.max(np.abs(s[b] - want)) <= score_tol(want)
+
+
+# ---------------------------------------------------------------- attention
+
+def _oracle_out(qf, kf, vf, sets, G, scale):
+    B, Hq, d = qf.shape
+    out = np.empty((B, Hq, d))
+    for b in range(B):
+        for r in range(Hq // G):
+            out[b, r * G:(r + 1) * G] = O.attend(qf[b, r * G:(r + 1) * G], kf[b, r], vf[b, r],
+                                                 sets[b][r], scale)
+    return out
+
+
+@pytest.mark.parametrize("dtype,d,G,N,n_idx", [("bf16", 128, 4, 5000, 655), ("f32", 64, 4, 1024, 64),
+                                               ("bf16", 64, 8, 777, 1), ("f32", 128, 2, 3000, 1500),
+                                               ("bf16", 128, 1, 2048, 333)])
+def test_sparse_token_per_head(dtype, d, G, N, n_idx):
+    say("sparse per-head", dtype, d, G, N, n_idx)
+    B, Hkv = 3, 2
+    q, k, v = _rand_cache(B, Hkv * G, Hkv, N, d, dtype, 21)
+    rng = np.random.default_rng(22)
+    idx = np.stack([np.stack([np.sort(rng.choice(N, n_idx, replace=False)) for _ in range(Hkv)])
+                    for _ in range(B)]).astype(np.int32)
+    out = T.sa_sparse_decode(q.to(dev()), k.to(dev()), v.to(dev()),
+                             torch.from_numpy(idx).to(dev())).cpu().numpy()
+    want = _oracle_out(_f64(q), _f64(k), _f64(v), [[idx[b, r] for r in range(Hkv)] for b in range(B)],
+                       G, O.default_scale(d))
+    check_out(out, want, dtype, "sparse per-head")
+
+
+def test_sparse_shared_and_unsorted_indices():
+    say("sparse shared")
+    B, Hkv, G, N, d, n_idx = 2, 4, 4, 4000, 128, 700
+    q, k, v = _rand_cache(B, Hkv * G, Hkv, N, d, "bf16", 31)
+    rng = np.random.default_rng(32)
+    idx = np.stack([rng.choice(N, n_idx, replace=False) for _ in range(B)]).astype(np.int32)
+    out = T.sa_sparse_decode(q.to(dev()), k.to(dev()), v.to(dev()), torch.from_numpy(idx).to(dev()),
+                             T.SA_IDX_TOKEN_SHARED).cpu().numpy()
+    want = _oracle_out(_f64(q), _f64(k), _f64(v), [[idx[b]] * Hkv for b in range(B)], G,
+                       O.default_scale(d))
+    check_out(out, want, "bf16", "sparse shared")
+
+
+@pytest.mark.parametrize("N,bs,n_blk", [(1000, 128, 3), (61440, 128, 24), (300, 16, 19)])
+def test_sparse_blocks_with_partial_last_block(N, bs, n_blk):
+    say("sparse blocks", N, bs, n_blk)
+    B, Hkv, G, d = 2, 2, 4, 128
+    q, k, v = _rand_cache(B, Hkv * G, Hkv, N, d, "bf16", 41)
+    nb = (N + bs - 1) // bs
+    rng = np.random.default_rng(42)
+    # every row holds the last (possibly partial) block plus random others
+    idx = np.stack([np.stack([rng.permutation(np.r_[rng.choice(nb - 1, n_blk - 1, replace=False), nb - 1])
+                              for _ in range(Hkv)]) for _ in range(B)]).astype(np.int32)
+    out = T.sa_sparse_decode(q.to(dev()), k.to(dev()), v.to(dev()), torch.from_numpy(idx).to(dev()),
+                             T.SA_IDX_BLOCK_PER_KV_HEAD, block_size=bs).cpu().numpy()
+    sets = [[O.block_tokens(idx[b, r], bs, N) for r in range(Hkv)] for b in range(B)]
+    want = _oracle_out(_f64(q), _f64(k), _f64(v), sets, G, O.default_scale(d))
+    check_out(out, want, "bf16", "sparse blocks")
+
+
+@pytest.mark.parametrize("dtype,d,G,N", [("f32", 64, 4, 1024), ("bf16", 128, 4, 20000),
+                                         ("bf16", 64, 2, 999), ("f32", 128, 8, 3333)])
+def test_dense_and_all_tokens_sparse(dtype, d, G, N):
+    say("dense", dtype, d, G, N)
+    B, Hkv = 2, 2
+    q, k, v = _rand_cache(B, Hkv * G, Hkv, N, d, dtype, 51)
+    qd, kd, vd = q.to(dev()), k.to(dev()), v.to(dev())
+    dense = T.sa_dense_decode(qd, kd, vd).cpu().numpy()
+    want = _oracle_out(_f64(q), _f64(k), _f64(v), [[np.arange(N)] * Hkv] * B, G, O.default_scale(d))
+    check_out(dense, want, dtype, "dense")
+    allidx = torch.arange(N, dtype=torch.int32, device=dev()).repeat(B, Hkv, 1).contiguous()
+    sparse = T.sa_sparse_decode(qd, kd, vd, allidx).cpu().numpy()
+    check_out(sparse, want, dtype, "sparse k=N")
+    tol = 1e-5 if dtype == "f32" else 1e-4
+    assert np.max(np.abs(sparse - dense)) <= tol
+
+
+def test_window_equals_dense_on_window_and_strided_cache():
+    """Top-k on recency is a sliding window: sparse over the last W tokens
+    equals dense decode over a strided view holding only those tokens."""
+    say("window")
+    B, Hkv, G, N, d, W = 2, 2, 4, 5000, 128, 300
+    q, k, v = _rand_cache(B, Hkv * G, Hkv, N, d, "bf16", 61)
+    qd, kd, vd = q.to(dev()), k.to(dev()), v.to(dev())
+    rec = torch.arange(N, dtype=torch.float32, device=dev()).repeat(B, Hkv, 1).contiguous()
+    idx = T.sa_topk(rec, W)
+    assert np.array_equal(idx.cpu().numpy()[0, 0], np.arange(N - W, N))
+    sparse = T.sa_sparse_decode(qd, kd, vd, idx).cpu().numpy()
+    dense_w = T.sa_dense_decode(qd, kd[:, :, N - W:], vd[:, :, N - W:]).cpu().numpy()
+    assert np.max(np.abs(sparse - dense_w)) <= 1e-4
+    # token-major cache [B, N, Hkv, d] viewed as [B, Hkv, N, d]
+    ktm = kd.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    vtm = vd.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    sparse_tm = T.sa_sparse_decode(qd, ktm, vtm, idx).cpu().numpy()
+    assert np.max(np.abs(sparse_tm - sparse)) <= 1e-5
+
+
+# -------------------------------------------------------------- tiny config
+
+def test_tiny_config_end_to_end():
+    """Tiny exact-top-k decode (fp32, 8/2 heads, d 64, N 1024, k 64) through
+    every call, plus k = N against dense."""
+    say("tiny config")
+    w = S.Workload("tiny", 0)
+    c = w.cfg
+    q_h, k_h, v_h = w.q(), w.k(), w.v()
+    qd, kd, vd = to_dev(q_h), to_dev(k_h), to_dev(v_h)
+    qf, kf, vf = O.widen(q_h), O.widen(k_h), O.widen(v_h)
+    scale = O.default_scale(c.head_dim)
+    scores = T.sa_score(qd, kd)
+    s_gpu = scores.cpu().numpy()
+    s64 = [O.scores_exact(qf[0, r * c.group:(r + 1) * c.group], kf[0, r], scale)
+           for r in range(c.n_kv_heads)]
+    for r in range(c.n_kv_heads):
+        assert np.max(np.abs(s_gpu[0, r] - s64[r])) <= score_tol(s64[r])
+    idx = T.sa_topk(scores, c.k)
+    idx_h = idx.cpu().numpy()
+    for r in range(c.n_kv_heads):
+        assert np.array_equal(idx_h[0, r], O.topk(s_gpu[0, r].astype(np.float64), c.k))
+        assert set(w.planted(0, 0, r)).issubset(idx_h[0, r])
+    counts, fails = verdicts(s64, idx_h[0], c.k)
+    assert not fails, fails
+    out = T.sa_sparse_decode(qd, kd, vd, idx).cpu().numpy()
+    want = _oracle_out(qf, kf, vf, [[idx_h[0, r] for r in range(c.n_kv_heads)]], c.group, scale)
+    check_out(out, want, "f32", "tiny sparse")
+    # the same through the layer entry point
+    args, out2, d_ = T.layer_args(qd, kd, vd, T.SA_SCORE_EXACT, c.k)
+    idx2 = torch.full((1, c.n_kv_heads, c.k), -1, dtype=torch.int32, device=dev())
+    T.sa_decode_layer(args, T.SA_LAYER_SPARSE, idx2, d_)
+    assert torch.equal(idx2, idx)
+    assert np.max(np.abs(out2.cpu().numpy() - out)) <= 1e-6
+    # k = N equals dense
+    dense = T.sa_dense_decode(qd, kd, vd).cpu().numpy()
+    wantd = _oracle_out(qf, kf, vf, [[np.arange(c.ctx_len)] * c.n_kv_heads], c.group, scale)
+    check_out(dense, wantd, "f32", "tiny dense")
+    idx_all = T.sa_topk(scores, c.ctx_len)
+    assert np.array_equal(idx_all.cpu().numpy()[0, 0], np.arange(c.ctx_len))
+    full = T.sa_sparse_decode(qd, kd, vd, idx_all).cpu().numpy()
+    check_out(full, wantd, "f32", "tiny k=N")
+    assert np.max(np.abs(full - dense)) <= 1e-5

@@ -1,0 +1,352 @@
+"""ctypes binding of ``libsa.so`` (declared in ``include/sa.h``).
+
+Argument marshalling only: every function below validates tensor placement,
+builds the C descriptor from torch tensor shapes/strides, passes
+``tensor.data_ptr()`` and the current HIP stream, and raises ``RuntimeError``
+with the library's message on a non-OK status.  All computation happens in the
+HIP kernels of the library; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsa.so")
+
+# sa_status
+SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_ALIGN, SA_ERR_DTYPE, SA_ERR_WORKSPACE, \
+    SA_ERR_UNSUPPORTED, SA_ERR_HIP = range(8)
+# sa_dtype
+SA_F32, SA_BF16 = 0, 1
+# sa_score_kind
+SA_SCORE_EXACT, SA_SCORE_BLOCK_MINMAX, SA_SCORE_INDEXER = 0, 1, 2
+# sa_index_kind
+SA_IDX_TOKEN_PER_KV_HEAD, SA_IDX_TOKEN_SHARED, SA_IDX_BLOCK_PER_KV_HEAD = 0, 1, 2
+# sa_layer_mode
+SA_LAYER_DENSE, SA_LAYER_SPARSE, SA_LAYER_REUSE = 0, 1, 2
+
+EXPORTED = [
+    "sa_score", "sa_block_summarize", "sa_topk", "sa_topk_workspace_size", "sa_sparse_decode",
+    "sa_sparse_workspace_size", "sa_dense_decode", "sa_dense_workspace_size", "sa_decode_layer",
+    "sa_layer_workspace_size", "sa_plan_validate", "sa_workspace_init", "sa_status_string",
+    "sa_last_error", "sa_version",
+]
+
+
+class KVDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("ctx_len", ctypes.c_int64), ("q_dtype", ctypes.c_int),
+                ("kv_dtype", ctypes.c_int), ("kv_stride_b", ctypes.c_int64),
+                ("kv_stride_h", ctypes.c_int64), ("kv_stride_t", ctypes.c_int64),
+                ("softmax_scale", ctypes.c_float)]
+
+
+class ScoreAux(ctypes.Structure):
+    _fields_ = [("kmin", ctypes.c_void_p), ("kmax", ctypes.c_void_p),
+                ("block_size", ctypes.c_int32), ("q_idx", ctypes.c_void_p),
+                ("k_idx", ctypes.c_void_p), ("idx_w", ctypes.c_void_p),
+                ("n_idx_heads", ctypes.c_int32), ("idx_dim", ctypes.c_int32)]
+
+
+class LayerArgs(ctypes.Structure):
+    _fields_ = [("desc", KVDesc), ("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p),
+                ("v_cache", ctypes.c_void_p), ("score_kind", ctypes.c_int),
+                ("aux", ScoreAux), ("k", ctypes.c_int32), ("out", ctypes.c_void_p),
+                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            "libsa.so is not built (expected at %s); run `python -m top_sparse_decode_sa_amd.build`"
+            % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    P = ctypes.POINTER
+    L.sa_score.argtypes = [P(KVDesc), st, vp, vp, P(ScoreAux), vp, vp]
+    L.sa_block_summarize.argtypes = [P(KVDesc), i32, vp, vp, vp, vp]
+    L.sa_topk.argtypes = [vp, i64, i64, i64, i32, vp, vp, sz, vp]
+    L.sa_topk_workspace_size.argtypes = [i64, i64, i32]
+    L.sa_topk_workspace_size.restype = sz
+    L.sa_sparse_decode.argtypes = [P(KVDesc), vp, vp, vp, st, vp, i32, i32, vp, vp, sz, vp]
+    L.sa_sparse_workspace_size.argtypes = [P(KVDesc), st, i32, i32]
+    L.sa_sparse_workspace_size.restype = sz
+    L.sa_dense_decode.argtypes = [P(KVDesc), vp, vp, vp, vp, vp, sz, vp]
+    L.sa_dense_workspace_size.argtypes = [P(KVDesc)]
+    L.sa_dense_workspace_size.restype = sz
+    L.sa_decode_layer.argtypes = [P(LayerArgs), st, vp, vp]
+    L.sa_layer_workspace_size.argtypes = [P(LayerArgs), st]
+    L.sa_layer_workspace_size.restype = sz
+    L.sa_plan_validate.argtypes = [vp, vp, i32]
+    L.sa_workspace_init.argtypes = [vp, sz, vp]
+    L.sa_status_string.argtypes = [st]
+    L.sa_status_string.restype = ctypes.c_char_p
+    L.sa_last_error.argtypes = []
+    L.sa_last_error.restype = ctypes.c_char_p
+    L.sa_version.restype = ctypes.c_char_p
+    for name in ["sa_score", "sa_block_summarize", "sa_topk", "sa_sparse_decode", "sa_dense_decode",
+                 "sa_decode_layer", "sa_plan_validate", "sa_workspace_init"]:
+        getattr(L, name).restype = st
+    _lib = L
+    return L
+
+
+class SAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.detail = detail
+        super().__init__("%s (%s)" % (lib().sa_status_string(status).decode(), detail))
+
+
+def check(status: int):
+    if status != SA_OK:
+        raise SAError(status, lib().sa_last_error().decode())
+
+
+# ---------------------------------------------------------------- helpers
+
+_DT = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError("dtype %s not supported (float32 or bfloat16)" % t.dtype)
+    return _DT[t.dtype]
+
+
+def _dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live on a GPU device (got %s)" % t.device)
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors on different devices: %s vs %s" % (dev, t.device))
+    return dev
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def make_desc(q: torch.Tensor, k_cache: torch.Tensor, softmax_scale: float = 0.0) -> KVDesc:
+    """Descriptor from q [B, Hq, d] (contiguous) and a K cache [B, Hkv, N, d]."""
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, Hq, d] and the cache [B, Hkv, N, d]")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    if k_cache.stride(3) != 1:
+        raise ValueError("the cache's last dimension must be contiguous")
+    B, Hkv, N, d = k_cache.shape
+    if q.shape[0] != B or q.shape[2] != d:
+        raise ValueError("q shape %s does not match cache shape %s" % (tuple(q.shape), tuple(k_cache.shape)))
+    return KVDesc(B, q.shape[1], Hkv, d, N, _dtype(q), _dtype(k_cache), k_cache.stride(0),
+                  k_cache.stride(1), k_cache.stride(2), float(softmax_scale))
+
+
+class Workspaces:
+    """Zero-initialised device workspaces, one per (device, call signature).
+
+    A workspace is tied to the call kind and shapes it was sized for (see the
+    workspace contract in sa.h), so each signature gets its own buffer.
+    """
+
+    def __init__(self):
+        self._bufs = {}
+
+    def get(self, dev, key, nbytes: int) -> torch.Tensor | None:
+        if nbytes == 0:
+            return None
+        k = (str(dev), key)
+        buf = self._bufs.get(k)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(nbytes + 256, dtype=torch.uint8, device=dev)
+            off = (-buf.data_ptr()) % 256
+            buf = buf[off:off + nbytes]
+            self._bufs[k] = buf
+        return buf
+
+    def clear(self):
+        self._bufs.clear()
+
+
+WORKSPACES = Workspaces()
+
+
+def _desc_key(desc: KVDesc):
+    return tuple(getattr(desc, f[0]) for f in KVDesc._fields_)
+
+
+# ---------------------------------------------------------------- C calls
+
+def sa_score(q, k_cache, kind=SA_SCORE_EXACT, *, kmin=None, kmax=None, block_size=0, q_idx=None,
+             k_idx=None, idx_w=None, scores=None, softmax_scale=0.0):
+    """sa_score: returns fp32 scores ([B, Hkv, N], [B, Hkv, nb] or [B, N])."""
+    dev = _dev(q, k_cache, kmin, kmax, q_idx, k_idx, idx_w)
+    desc = make_desc(q, k_cache, softmax_scale)
+    aux = ScoreAux()
+    B, Hkv, N = desc.batch, desc.n_kv_heads, desc.ctx_len
+    if kind == SA_SCORE_BLOCK_MINMAX:
+        aux.kmin, aux.kmax, aux.block_size = kmin.data_ptr(), kmax.data_ptr(), block_size
+        shape = (B, Hkv, (N + block_size - 1) // block_size)
+    elif kind == SA_SCORE_INDEXER:
+        aux.q_idx, aux.k_idx, aux.idx_w = q_idx.data_ptr(), k_idx.data_ptr(), idx_w.data_ptr()
+        aux.n_idx_heads, aux.idx_dim = q_idx.shape[1], q_idx.shape[2]
+        if k_idx.shape != (B, N, q_idx.shape[2]) or idx_w.shape != (B, q_idx.shape[1]):
+            raise ValueError("indexer tensors: q_idx [B,H,Di], k_idx [B,N,Di], idx_w [B,H]")
+        shape = (B, N)
+    else:
+        shape = (B, Hkv, N)
+    if scores is None:
+        scores = torch.empty(shape, dtype=torch.float32, device=dev)
+    check(lib().sa_score(ctypes.byref(desc), kind, _ptr(q), _ptr(k_cache), ctypes.byref(aux),
+                         _ptr(scores), ctypes.c_void_p(_stream(dev))))
+    return scores
+
+
+def sa_block_summarize(k_cache, block_size, q_like=None):
+    """sa_block_summarize: returns (kmin, kmax) [B, Hkv, nb, d] in the cache dtype."""
+    dev = _dev(k_cache)
+    B, Hkv, N, d = k_cache.shape
+    q = q_like if q_like is not None else torch.empty((B, Hkv, d), dtype=k_cache.dtype, device=dev)
+    desc = make_desc(q, k_cache)
+    nb = (N + block_size - 1) // block_size
+    kmin = torch.empty((B, Hkv, nb, d), dtype=k_cache.dtype, device=dev)
+    kmax = torch.empty_like(kmin)
+    check(lib().sa_block_summarize(ctypes.byref(desc), block_size, _ptr(k_cache), _ptr(kmin),
+                                   _ptr(kmax), ctypes.c_void_p(_stream(dev))))
+    return kmin, kmax
+
+
+def sa_topk(scores, k, idx_out=None):
+    """sa_topk over the last dimension of a 2-D (or higher) fp32 tensor."""
+    dev = _dev(scores)
+    if scores.dtype != torch.float32:
+        raise TypeError("scores must be float32")
+    n = scores.shape[-1]
+    rows = scores.numel() // n if n else 0
+    if scores.stride(-1) != 1:
+        raise ValueError("scores rows must be contiguous")
+    flat = scores.reshape(rows, n)
+    row_stride = flat.stride(0) if rows > 1 else n
+    if idx_out is None:
+        idx_out = torch.empty(scores.shape[:-1] + (k,), dtype=torch.int32, device=dev)
+    L = lib()
+    nbytes = L.sa_topk_workspace_size(rows, n, k)
+    ws = WORKSPACES.get(dev, ("topk", rows, n, k), nbytes)
+    check(L.sa_topk(_ptr(flat), rows, n, row_stride, k, _ptr(idx_out), _ptr(ws), nbytes,
+                    ctypes.c_void_p(_stream(dev))))
+    return idx_out
+
+
+def sa_sparse_decode(q, k_cache, v_cache, idx, index_kind=SA_IDX_TOKEN_PER_KV_HEAD, block_size=0,
+                     out=None, softmax_scale=0.0, ws=None):
+    """sa_sparse_decode: returns out [B, Hq, d] fp32."""
+    dev = _dev(q, k_cache, v_cache, idx)
+    if v_cache.shape != k_cache.shape or v_cache.stride() != k_cache.stride():
+        raise ValueError("K and V caches must share shape and strides")
+    if idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be a contiguous int32 tensor")
+    desc = make_desc(q, k_cache, softmax_scale)
+    n_idx = idx.shape[-1]
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    L = lib()
+    nbytes = L.sa_sparse_workspace_size(ctypes.byref(desc), index_kind, n_idx, block_size)
+    if ws is None:
+        ws = WORKSPACES.get(dev, ("sparse", _desc_key(desc), index_kind, n_idx, block_size), nbytes)
+    check(L.sa_sparse_decode(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), index_kind,
+                             _ptr(idx), n_idx, block_size, _ptr(out), _ptr(ws), nbytes,
+                             ctypes.c_void_p(_stream(dev))))
+    return out
+
+
+def sa_dense_decode(q, k_cache, v_cache, out=None, softmax_scale=0.0, ws=None):
+    """sa_dense_decode: returns out [B, Hq, d] fp32."""
+    dev = _dev(q, k_cache, v_cache)
+    if v_cache.shape != k_cache.shape or v_cache.stride() != k_cache.stride():
+        raise ValueError("K and V caches must share shape and strides")
+    desc = make_desc(q, k_cache, softmax_scale)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    L = lib()
+    nbytes = L.sa_dense_workspace_size(ctypes.byref(desc))
+    if ws is None:
+        ws = WORKSPACES.get(dev, ("dense", _desc_key(desc)), nbytes)
+    check(L.sa_dense_decode(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+                            _ptr(ws), nbytes, ctypes.c_void_p(_stream(dev))))
+    return out
+
+
+def layer_args(q, k_cache, v_cache, score_kind=SA_SCORE_EXACT, k=0, *, kmin=None, kmax=None,
+               block_size=0, q_idx=None, k_idx=None, idx_w=None, out=None, softmax_scale=0.0):
+    """Build an sa_layer_args structure (and the output tensor) for sa_decode_layer."""
+    dev = _dev(q, k_cache, v_cache, kmin, kmax, q_idx, k_idx, idx_w)
+    a = LayerArgs()
+    a.desc = make_desc(q, k_cache, softmax_scale)
+    a.q, a.k_cache, a.v_cache = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr()
+    a.score_kind = score_kind
+    if kmin is not None:
+        a.aux.kmin, a.aux.kmax = kmin.data_ptr(), kmax.data_ptr()
+    a.aux.block_size = block_size
+    if q_idx is not None:
+        a.aux.q_idx, a.aux.k_idx, a.aux.idx_w = q_idx.data_ptr(), k_idx.data_ptr(), idx_w.data_ptr()
+        a.aux.n_idx_heads, a.aux.idx_dim = q_idx.shape[1], q_idx.shape[2]
+    a.k = k
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    a.out = out.data_ptr()
+    return a, out, dev
+
+
+def sa_layer_workspace_size(args: LayerArgs, mode: int) -> int:
+    return int(lib().sa_layer_workspace_size(ctypes.byref(args), mode))
+
+
+def sa_decode_layer(args: LayerArgs, mode: int, idx=None, dev=None, ws=None):
+    """sa_decode_layer: runs one layer under `mode`; SPARSE writes idx, REUSE reads it."""
+    if dev is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    nbytes = sa_layer_workspace_size(args, mode)
+    if ws is None:
+        key = ("layer", mode, _desc_key(args.desc), args.score_kind, args.k, args.aux.block_size)
+        ws = WORKSPACES.get(dev, key, nbytes)
+    args.ws = None if ws is None else ws.data_ptr()
+    args.ws_bytes = nbytes
+    check(lib().sa_decode_layer(ctypes.byref(args), mode, _ptr(idx), ctypes.c_void_p(_stream(dev))))
+
+
+def sa_plan_validate(modes, src):
+    """sa_plan_validate on host lists; raises SAError if the plan is invalid."""
+    n = len(modes)
+    m = (ctypes.c_int32 * max(n, 1))(*modes)
+    s = (ctypes.c_int32 * max(n, 1))(*src)
+    check(lib().sa_plan_validate(m, s, n))
+
+
+def sa_workspace_init(ws):
+    dev = _dev(ws)
+    check(lib().sa_workspace_init(_ptr(ws), ws.numel() * ws.element_size(),
+                                  ctypes.c_void_p(_stream(dev))))
+
+
+def sa_version() -> str:
+    return lib().sa_version().decode()

@@ -1,0 +1,446 @@
+// C ABI of libsa: argument validation, workspace planning and dispatch.
+// Every entry point checks its arguments on the host and returns an error
+// code before anything is enqueued; kernels are launched only on success.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "common.hpp"
+#include "internal.hpp"
+#include "sa.h"
+
+namespace sa {
+namespace {
+
+thread_local std::string g_last_error;
+
+sa_status fail(sa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+sa_status fail(sa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+sa_status ok() {
+  g_last_error.clear();
+  return SA_OK;
+}
+
+sa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int elt_bytes(sa_dtype d) { return d == SA_BF16 ? 2 : 4; }
+
+bool valid_dtype(sa_dtype d) { return d == SA_F32 || d == SA_BF16; }
+
+// Validate a descriptor and produce the internal cache view.
+sa_status check_desc(const sa_kv_desc* d, Cache* c) {
+  if (!d) return fail(SA_ERR_NULL, "descriptor is null");
+  if (!valid_dtype(d->q_dtype) || !valid_dtype(d->kv_dtype))
+    return fail(SA_ERR_DTYPE, "unknown dtype (q %d, kv %d)", (int)d->q_dtype, (int)d->kv_dtype);
+  if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1)
+    return fail(SA_ERR_SHAPE, "batch, n_q_heads and n_kv_heads must be >= 1");
+  if (d->n_q_heads % d->n_kv_heads != 0)
+    return fail(SA_ERR_SHAPE, "n_q_heads %d is not a multiple of n_kv_heads %d", d->n_q_heads,
+                d->n_kv_heads);
+  const int G = d->n_q_heads / d->n_kv_heads;
+  if (d->ctx_len < 1 || d->ctx_len > INT32_MAX)
+    return fail(SA_ERR_SHAPE, "ctx_len %lld outside [1, 2^31)", (long long)d->ctx_len);
+  if ((int64_t)d->batch * d->n_kv_heads > 65535)
+    return fail(SA_ERR_SHAPE, "batch * n_kv_heads above 65535");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(SA_ERR_UNSUPPORTED, "head_dim %d (built: 64, 128)", d->head_dim);
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(SA_ERR_UNSUPPORTED, "group size %d (built: 1, 2, 4, 8)", G);
+  const int eb = elt_bytes(d->kv_dtype);
+  if (d->kv_stride_t < d->head_dim || d->kv_stride_h < 0 || d->kv_stride_b < 0)
+    return fail(SA_ERR_SHAPE, "strides must satisfy kv_stride_t >= head_dim, others >= 0");
+  if ((d->kv_stride_t * eb) % 16 || (d->kv_stride_h * eb) % 16 || (d->kv_stride_b * eb) % 16)
+    return fail(SA_ERR_ALIGN, "cache strides must be multiples of 16 bytes");
+  if (!(d->softmax_scale >= 0.0f) || isinf(d->softmax_scale))
+    return fail(SA_ERR_SHAPE, "softmax_scale must be finite and >= 0");
+  c->B = d->batch;
+  c->Hq = d->n_q_heads;
+  c->Hkv = d->n_kv_heads;
+  c->G = G;
+  c->D = d->head_dim;
+  c->N = d->ctx_len;
+  c->q_dtype = d->q_dtype;
+  c->kv_dtype = d->kv_dtype;
+  c->sb = d->kv_stride_b;
+  c->sh = d->kv_stride_h;
+  c->st = d->kv_stride_t;
+  c->scale = d->softmax_scale > 0.0f ? d->softmax_scale : 1.0f / sqrtf((float)d->head_dim);
+  return SA_OK;
+}
+
+sa_status check_ptr(const void* p, const char* name, size_t align) {
+  if (!p) return fail(SA_ERR_NULL, "%s is null", name);
+  if (!aligned(p, align)) return fail(SA_ERR_ALIGN, "%s is not %zu-byte aligned", name, align);
+  return SA_OK;
+}
+
+sa_status check_ws(void* ws, size_t have, size_t need, const char* what) {
+  if (need == 0) return SA_OK;
+  if (!ws) return fail(SA_ERR_WORKSPACE, "%s needs a %zu-byte workspace, got null", what, need);
+  if (!aligned(ws, 256)) return fail(SA_ERR_ALIGN, "workspace is not 256-byte aligned");
+  if (have < need)
+    return fail(SA_ERR_WORKSPACE, "%s needs %zu workspace bytes, got %zu", what, need, have);
+  return SA_OK;
+}
+
+int mode_of(sa_index_kind ik) {
+  switch (ik) {
+    case SA_IDX_TOKEN_PER_KV_HEAD: return kIdxTokenPerHead;
+    case SA_IDX_TOKEN_SHARED: return kIdxTokenShared;
+    case SA_IDX_BLOCK_PER_KV_HEAD: return kIdxBlockPerHead;
+  }
+  return -1;
+}
+
+sa_status check_indexer_aux(const Cache& c, const sa_score_aux* aux) {
+  if (!aux) return fail(SA_ERR_NULL, "indexer scoring needs aux");
+  if (aux->n_idx_heads < 1 || aux->n_idx_heads > 16)
+    return fail(SA_ERR_SHAPE, "n_idx_heads %d outside [1, 16]", aux->n_idx_heads);
+  if (aux->idx_dim != 32 && aux->idx_dim != 64 && aux->idx_dim != 128)
+    return fail(SA_ERR_UNSUPPORTED, "idx_dim %d (built: 32, 64, 128)", aux->idx_dim);
+  sa_status st;
+  if ((st = check_ptr(aux->q_idx, "aux.q_idx", 16)) != SA_OK) return st;
+  if ((st = check_ptr(aux->k_idx, "aux.k_idx", 16)) != SA_OK) return st;
+  if ((st = check_ptr(aux->idx_w, "aux.idx_w", 4)) != SA_OK) return st;
+  (void)c;
+  return SA_OK;
+}
+
+sa_status check_block_aux(const Cache& c, const sa_score_aux* aux) {
+  if (!aux) return fail(SA_ERR_NULL, "block scoring needs aux");
+  if (aux->block_size < 1 || aux->block_size > 4096)
+    return fail(SA_ERR_SHAPE, "block_size %d outside [1, 4096]", aux->block_size);
+  sa_status st;
+  if ((st = check_ptr(aux->kmin, "aux.kmin", 16)) != SA_OK) return st;
+  if ((st = check_ptr(aux->kmax, "aux.kmax", 16)) != SA_OK) return st;
+  (void)c;
+  return SA_OK;
+}
+
+int64_t score_row_len(const Cache& c, sa_score_kind kind, const sa_score_aux* aux) {
+  if (kind == SA_SCORE_BLOCK_MINMAX) return (c.N + aux->block_size - 1) / aux->block_size;
+  return c.N;
+}
+
+int64_t score_rows(const Cache& c, sa_score_kind kind) {
+  return kind == SA_SCORE_INDEXER ? (int64_t)c.B : (int64_t)c.B * c.Hkv;
+}
+
+sa_status do_score(const Cache& c, sa_score_kind kind, const void* q, const void* k,
+                   const sa_score_aux* aux, float* scores, hipStream_t s) {
+  hipError_t e;
+  switch (kind) {
+    case SA_SCORE_EXACT: e = launch_score_exact(c, q, k, scores, s); break;
+    case SA_SCORE_BLOCK_MINMAX:
+      e = launch_score_block(c, aux->block_size, q, aux->kmin, aux->kmax, scores, s);
+      break;
+    default:
+      e = launch_score_indexer(c.B, c.N, aux->n_idx_heads, aux->idx_dim, aux->q_idx, aux->k_idx,
+                               aux->idx_w, scores, s);
+      break;
+  }
+  return hip_status(e, "sa_score launch");
+}
+
+sa_status check_score_args(const sa_kv_desc* desc, sa_score_kind kind, const void* q,
+                           const void* k_cache, const sa_score_aux* aux, const float* scores,
+                           Cache* c) {
+  sa_status st;
+  if ((st = check_desc(desc, c)) != SA_OK) return st;
+  if (kind != SA_SCORE_EXACT && kind != SA_SCORE_BLOCK_MINMAX && kind != SA_SCORE_INDEXER)
+    return fail(SA_ERR_SHAPE, "unknown score kind %d", (int)kind);
+  if ((st = check_ptr(scores, "scores", 4)) != SA_OK) return st;
+  if (kind == SA_SCORE_INDEXER) return check_indexer_aux(*c, aux);
+  if ((st = check_ptr(q, "q", 16)) != SA_OK) return st;
+  if (kind == SA_SCORE_BLOCK_MINMAX) return check_block_aux(*c, aux);
+  return check_ptr(k_cache, "k_cache", 16);
+}
+
+sa_status check_attend_args(const Cache& c, const void* q, const void* k, const void* v,
+                            const float* out) {
+  sa_status st;
+  if ((st = check_ptr(q, "q", 16)) != SA_OK) return st;
+  if ((st = check_ptr(k, "k_cache", 16)) != SA_OK) return st;
+  if ((st = check_ptr(v, "v_cache", 16)) != SA_OK) return st;
+  if ((st = check_ptr(out, "out", 4)) != SA_OK) return st;
+  (void)c;
+  return SA_OK;
+}
+
+sa_status check_sparse_idx(const Cache& c, sa_index_kind ik, const int32_t* idx, int32_t n_idx,
+                           int32_t bs) {
+  if (mode_of(ik) < 0) return fail(SA_ERR_SHAPE, "unknown index kind %d", (int)ik);
+  sa_status st;
+  if ((st = check_ptr(idx, "idx", 4)) != SA_OK) return st;
+  if (n_idx < 1) return fail(SA_ERR_SHAPE, "n_idx %d must be >= 1", n_idx);
+  if (ik == SA_IDX_BLOCK_PER_KV_HEAD) {
+    if (bs < 1 || bs > 4096) return fail(SA_ERR_SHAPE, "block_size %d outside [1, 4096]", bs);
+    if ((int64_t)n_idx * bs > (int64_t)INT32_MAX)
+      return fail(SA_ERR_SHAPE, "n_idx * block_size overflows");
+  }
+  return SA_OK;
+}
+
+// Workspace layout of one SPARSE layer step: [scores | top-k | attention].
+struct LayerWs {
+  size_t scores, topk, attend, total;
+};
+
+LayerWs layer_ws(const Cache& c, const sa_layer_args* a, sa_layer_mode mode) {
+  LayerWs w{};
+  if (mode == SA_LAYER_DENSE) {
+    w.attend = plan_attend(c, kIdxDense, 0, 0).ws_bytes;
+  } else {
+    const sa_index_kind ik = a->score_kind == SA_SCORE_EXACT ? SA_IDX_TOKEN_PER_KV_HEAD
+                             : a->score_kind == SA_SCORE_BLOCK_MINMAX ? SA_IDX_BLOCK_PER_KV_HEAD
+                                                                      : SA_IDX_TOKEN_SHARED;
+    const int32_t bs = a->score_kind == SA_SCORE_BLOCK_MINMAX ? a->aux.block_size : 0;
+    w.attend = plan_attend(c, mode_of(ik), a->k, bs).ws_bytes;
+    if (mode == SA_LAYER_SPARSE) {
+      const int64_t rows = score_rows(c, a->score_kind);
+      const int64_t len = score_row_len(c, a->score_kind, &a->aux);
+      w.scores = align_up((size_t)rows * len * sizeof(float), 256);
+      w.topk = align_up(topk_workspace_bytes(rows, len, a->k), 256);
+    }
+  }
+  w.total = w.scores + w.topk + align_up(w.attend, 256);
+  return w;
+}
+
+__global__ void zero_kernel(uint4* p, size_t n16, uint8_t* tail, size_t ntail) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t j = i; j < n16; j += stride) p[j] = make_uint4(0, 0, 0, 0);
+  if (i < ntail) tail[i] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  const size_t ntail = bytes % 16;
+  const unsigned blocks = (unsigned)std::max<size_t>(1, std::min<size_t>((n16 + 255) / 256, 4096));
+  hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, s, static_cast<uint4*>(p), n16,
+                     static_cast<uint8_t*>(p) + n16 * 16, ntail);
+  return hipGetLastError();
+}
+
+}  // namespace sa
+
+using namespace sa;
+
+extern "C" {
+
+const char* sa_version(void) { return "sa 0.1.0 (gfx950)"; }
+
+const char* sa_status_string(sa_status s) {
+  switch (s) {
+    case SA_OK: return "SA_OK";
+    case SA_ERR_NULL: return "SA_ERR_NULL: a required pointer is null";
+    case SA_ERR_SHAPE: return "SA_ERR_SHAPE: a size, count, stride or k is out of range";
+    case SA_ERR_ALIGN: return "SA_ERR_ALIGN: misaligned pointer or stride";
+    case SA_ERR_DTYPE: return "SA_ERR_DTYPE: unsupported dtype";
+    case SA_ERR_WORKSPACE: return "SA_ERR_WORKSPACE: workspace missing or too small";
+    case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED: configuration not built";
+    case SA_ERR_HIP: return "SA_ERR_HIP: HIP runtime error";
+  }
+  return "unknown sa_status";
+}
+
+const char* sa_last_error(void) { return g_last_error.c_str(); }
+
+sa_status sa_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (ws_bytes == 0) return ok();
+  if (!ws) return fail(SA_ERR_NULL, "workspace is null");
+  return hip_status(launch_zero(ws, ws_bytes, stream), "sa_workspace_init launch");
+}
+
+sa_status sa_score(const sa_kv_desc* desc, sa_score_kind kind, const void* q, const void* k_cache,
+                   const sa_score_aux* aux, float* scores, hipStream_t stream) {
+  Cache c;
+  sa_status st = check_score_args(desc, kind, q, k_cache, aux, scores, &c);
+  if (st != SA_OK) return st;
+  return do_score(c, kind, q, k_cache, aux, scores, stream);
+}
+
+sa_status sa_block_summarize(const sa_kv_desc* desc, int32_t block_size, const void* k_cache,
+                             void* kmin, void* kmax, hipStream_t stream) {
+  Cache c;
+  sa_status st;
+  if ((st = check_desc(desc, &c)) != SA_OK) return st;
+  if (block_size < 1 || block_size > 4096)
+    return fail(SA_ERR_SHAPE, "block_size %d outside [1, 4096]", block_size);
+  if ((st = check_ptr(k_cache, "k_cache", 16)) != SA_OK) return st;
+  if ((st = check_ptr(kmin, "kmin", 16)) != SA_OK) return st;
+  if ((st = check_ptr(kmax, "kmax", 16)) != SA_OK) return st;
+  return hip_status(launch_block_summarize(c, block_size, k_cache, kmin, kmax, stream),
+                    "sa_block_summarize launch");
+}
+
+size_t sa_topk_workspace_size(int64_t n_rows, int64_t n, int32_t k) {
+  if (n_rows < 1 || n < 1 || k < 1 || k > n) return 0;
+  return align_up(topk_workspace_bytes(n_rows, n, k), 256);
+}
+
+sa_status sa_topk(const float* scores, int64_t n_rows, int64_t n, int64_t row_stride, int32_t k,
+                  int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  sa_status st;
+  if ((st = check_ptr(scores, "scores", 4)) != SA_OK) return st;
+  if ((st = check_ptr(idx_out, "idx_out", 4)) != SA_OK) return st;
+  if (n_rows < 1 || n_rows >= (1 << 22))
+    return fail(SA_ERR_SHAPE, "n_rows %lld outside [1, 2^22)", (long long)n_rows);
+  if (n < 1 || n > INT32_MAX) return fail(SA_ERR_SHAPE, "n %lld outside [1, 2^31)", (long long)n);
+  if (k < 1 || k > n) return fail(SA_ERR_SHAPE, "k %d outside [1, n=%lld]", k, (long long)n);
+  if (row_stride < n) return fail(SA_ERR_SHAPE, "row_stride < n");
+  if ((st = check_ws(ws, ws_bytes, sa_topk_workspace_size(n_rows, n, k), "sa_topk")) != SA_OK)
+    return st;
+  return hip_status(launch_topk(scores, n_rows, n, row_stride, k, idx_out, ws, stream),
+                    "sa_topk launch");
+}
+
+size_t sa_sparse_workspace_size(const sa_kv_desc* desc, sa_index_kind ik, int32_t n_idx,
+                                int32_t block_size) {
+  Cache c;
+  if (check_desc(desc, &c) != SA_OK || mode_of(ik) < 0 || n_idx < 1) return 0;
+  if (ik == SA_IDX_BLOCK_PER_KV_HEAD && (block_size < 1 || block_size > 4096)) return 0;
+  return align_up(plan_attend(c, mode_of(ik), n_idx, block_size).ws_bytes, 256);
+}
+
+sa_status sa_sparse_decode(const sa_kv_desc* desc, const void* q, const void* k_cache,
+                           const void* v_cache, sa_index_kind ik, const int32_t* idx, int32_t n_idx,
+                           int32_t block_size, float* out, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  Cache c;
+  sa_status st;
+  if ((st = check_desc(desc, &c)) != SA_OK) return st;
+  if ((st = check_attend_args(c, q, k_cache, v_cache, out)) != SA_OK) return st;
+  if ((st = check_sparse_idx(c, ik, idx, n_idx, block_size)) != SA_OK) return st;
+  const AttendPlan p = plan_attend(c, mode_of(ik), n_idx, block_size);
+  if ((st = check_ws(ws, ws_bytes, p.ws_bytes, "sa_sparse_decode")) != SA_OK) return st;
+  return hip_status(
+      launch_attend(c, p, q, k_cache, v_cache, idx, n_idx, block_size, out, ws, stream),
+      "sa_sparse_decode launch");
+}
+
+size_t sa_dense_workspace_size(const sa_kv_desc* desc) {
+  Cache c;
+  if (check_desc(desc, &c) != SA_OK) return 0;
+  return align_up(plan_attend(c, kIdxDense, 0, 0).ws_bytes, 256);
+}
+
+sa_status sa_dense_decode(const sa_kv_desc* desc, const void* q, const void* k_cache,
+                          const void* v_cache, float* out, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  Cache c;
+  sa_status st;
+  if ((st = check_desc(desc, &c)) != SA_OK) return st;
+  if ((st = check_attend_args(c, q, k_cache, v_cache, out)) != SA_OK) return st;
+  const AttendPlan p = plan_attend(c, kIdxDense, 0, 0);
+  if ((st = check_ws(ws, ws_bytes, p.ws_bytes, "sa_dense_decode")) != SA_OK) return st;
+  return hip_status(launch_attend(c, p, q, k_cache, v_cache, nullptr, 0, 0, out, ws, stream),
+                    "sa_dense_decode launch");
+}
+
+size_t sa_layer_workspace_size(const sa_layer_args* a, sa_layer_mode mode) {
+  Cache c;
+  if (!a || check_desc(&a->desc, &c) != SA_OK) return 0;
+  if (mode != SA_LAYER_DENSE && a->k < 1) return 0;
+  if (mode != SA_LAYER_DENSE && a->score_kind == SA_SCORE_BLOCK_MINMAX &&
+      (a->aux.block_size < 1 || a->aux.block_size > 4096))
+    return 0;
+  return layer_ws(c, a, mode).total;
+}
+
+sa_status sa_decode_layer(const sa_layer_args* a, sa_layer_mode mode, int32_t* idx,
+                          hipStream_t stream) {
+  if (!a) return fail(SA_ERR_NULL, "layer args are null");
+  Cache c;
+  sa_status st;
+  if ((st = check_desc(&a->desc, &c)) != SA_OK) return st;
+  if (mode != SA_LAYER_DENSE && mode != SA_LAYER_SPARSE && mode != SA_LAYER_REUSE)
+    return fail(SA_ERR_SHAPE, "unknown layer mode %d", (int)mode);
+  if ((st = check_attend_args(c, a->q, a->k_cache, a->v_cache, a->out)) != SA_OK) return st;
+  if (mode == SA_LAYER_DENSE) {
+    const LayerWs w = layer_ws(c, a, mode);
+    if ((st = check_ws(a->ws, a->ws_bytes, w.total, "sa_decode_layer(DENSE)")) != SA_OK) return st;
+    const AttendPlan p = plan_attend(c, kIdxDense, 0, 0);
+    return hip_status(launch_attend(c, p, a->q, a->k_cache, a->v_cache, nullptr, 0, 0, a->out,
+                                    a->ws, stream),
+                      "sa_decode_layer(DENSE) launch");
+  }
+  // selection-based modes
+  if (a->score_kind != SA_SCORE_EXACT && a->score_kind != SA_SCORE_BLOCK_MINMAX &&
+      a->score_kind != SA_SCORE_INDEXER)
+    return fail(SA_ERR_SHAPE, "unknown score kind %d", (int)a->score_kind);
+  const sa_index_kind ik = a->score_kind == SA_SCORE_EXACT ? SA_IDX_TOKEN_PER_KV_HEAD
+                           : a->score_kind == SA_SCORE_BLOCK_MINMAX ? SA_IDX_BLOCK_PER_KV_HEAD
+                                                                    : SA_IDX_TOKEN_SHARED;
+  const int32_t bs = a->score_kind == SA_SCORE_BLOCK_MINMAX ? a->aux.block_size : 0;
+  if (a->score_kind == SA_SCORE_BLOCK_MINMAX) {
+    if ((st = check_block_aux(c, &a->aux)) != SA_OK) return st;
+  } else if (a->score_kind == SA_SCORE_INDEXER && mode == SA_LAYER_SPARSE) {
+    if ((st = check_indexer_aux(c, &a->aux)) != SA_OK) return st;
+  }
+  const int64_t len = score_row_len(c, a->score_kind, &a->aux);
+  if (a->k < 1 || a->k > len)
+    return fail(SA_ERR_SHAPE, "k %d outside [1, %lld]", a->k, (long long)len);
+  if ((st = check_sparse_idx(c, ik, idx, a->k, bs)) != SA_OK) return st;
+  const LayerWs w = layer_ws(c, a, mode);
+  if ((st = check_ws(a->ws, a->ws_bytes, w.total, "sa_decode_layer")) != SA_OK) return st;
+  uint8_t* base = static_cast<uint8_t*>(a->ws);
+  float* scores = reinterpret_cast<float*>(base);
+  void* topk_ws = base + w.scores;
+  void* att_ws = base + w.scores + w.topk;
+  const AttendPlan p = plan_attend(c, mode_of(ik), a->k, bs);
+  if (mode == SA_LAYER_SPARSE) {
+    if ((st = do_score(c, a->score_kind, a->q, a->k_cache, &a->aux, scores, stream)) != SA_OK)
+      return st;
+    const int64_t rows = score_rows(c, a->score_kind);
+    if ((st = hip_status(launch_topk(scores, rows, len, len, a->k, idx, topk_ws, stream),
+                         "sa_decode_layer top-k launch")) != SA_OK)
+      return st;
+  }
+  return hip_status(
+      launch_attend(c, p, a->q, a->k_cache, a->v_cache, idx, a->k, bs, a->out, att_ws, stream),
+      "sa_decode_layer attention launch");
+}
+
+sa_status sa_plan_validate(const int32_t* modes, const int32_t* src, int32_t n_layers) {
+  if (n_layers < 1) return fail(SA_ERR_SHAPE, "n_layers %d must be >= 1", n_layers);
+  if (!modes || !src) return fail(SA_ERR_NULL, "modes or src is null");
+  if (n_layers > 4096) return fail(SA_ERR_SHAPE, "n_layers %d above 4096", n_layers);
+  bool has_idx[4096];
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const int32_t m = modes[l];
+    if (m != SA_LAYER_DENSE && m != SA_LAYER_SPARSE && m != SA_LAYER_REUSE)
+      return fail(SA_ERR_SHAPE, "layer %d: unknown mode %d", l, m);
+    if (m == SA_LAYER_REUSE) {
+      const int32_t s = src[l];
+      if (s < 0 || s >= l)
+        return fail(SA_ERR_SHAPE, "layer %d: reuse source %d is not an earlier layer", l, s);
+      if (!has_idx[s]) return fail(SA_ERR_SHAPE, "layer %d: reuse source %d holds no index set", l, s);
+    }
+    has_idx[l] = (m != SA_LAYER_DENSE);
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+// Device helpers shared by the HIP kernels of libsa (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sa.h"
+
+namespace sa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- storage
+
+struct bf16_t {
+  uint16_t bits;
+};
+
+template <typename T>
+struct Elt;
+template <>
+struct Elt<float> {
+  static constexpr int kBytes = 4;
+  static constexpr int kPer16B = 4;
+};
+template <>
+struct Elt<bf16_t> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPer16B = 8;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 16-byte vector load (global_load_dwordx4).
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Unpack one 16-byte chunk into floats (8 bf16 or 4 fp32 values).
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4& w, float* f);
+template <>
+__device__ __forceinline__ void unpack16<bf16_t>(const uint4& w, float* f) {
+  f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x);
+  f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+  f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z);
+  f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+}
+template <>
+__device__ __forceinline__ void unpack16<float>(const uint4& w, float* f) {
+  f[0] = __uint_as_float(w.x); f[1] = __uint_as_float(w.y);
+  f[2] = __uint_as_float(w.z); f[3] = __uint_as_float(w.w);
+}
+
+// Read `n` consecutive query values of either storage type as fp32.
+__device__ __forceinline__ float load_q(const void* q, sa_dtype dt, int64_t i) {
+  if (dt == SA_BF16) {
+    const uint16_t b = reinterpret_cast<const uint16_t*>(q)[i];
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+  }
+  return reinterpret_cast<const float*>(q)[i];
+}
+
+// ------------------------------------------------------ lane-group reductions
+// A "lane group" is LPR consecutive lanes of a wave (LPR in {4, 8, 16, 32}) that
+// together hold one cache row.  The first steps use DPP within a 16-lane DPP
+// row; LPR = 32 adds one cross-row exchange.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_amdgcn_update_dpp(0.0f, x, CTRL, 0xf, 0xf, false);
+}
+
+constexpr int kQuadXor1 = 0xb1;    // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4e;    // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(LPR == 4 || LPR == 8 || LPR == 16 || LPR == 32, "lane group of 4 to 32");
+  x += dpp<kQuadXor1>(x);
+  x += dpp<kQuadXor2>(x);
+  if constexpr (LPR >= 8) x += dpp<kRowHalfMirror>(x);
+  if constexpr (LPR >= 16) x += dpp<kRowMirror>(x);
+  if constexpr (LPR == 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+template <int LPR>
+__device__ __forceinline__ float group_max(float x) {
+  x = fmaxf(x, dpp<kQuadXor1>(x));
+  x = fmaxf(x, dpp<kQuadXor2>(x));
+  if constexpr (LPR >= 8) x = fmaxf(x, dpp<kRowHalfMirror>(x));
+  if constexpr (LPR >= 16) x = fmaxf(x, dpp<kRowMirror>(x));
+  if constexpr (LPR == 32) x = fmaxf(x, __shfl_xor(x, 16));
+  return x;
+}
+
+// Wave-wide inclusive prefix sum of a uint32 (64 lanes).
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// ------------------------------------------------------------ top-k keys
+// Order-preserving map of fp32 bit patterns onto uint32: a larger float maps
+// to a larger key; -0.0 maps like +0.0; every NaN maps to 0, below -inf.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;  // NaN
+  if (u == 0x80000000u) u = 0u;                     // -0.0 -> +0.0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace sa

@@ -1,0 +1,56 @@
+// Host-side interfaces between the C ABI (api.cpp) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sa.h"
+
+namespace sa {
+
+// Validated view of one layer's KV cache (strides in elements).
+struct Cache {
+  int32_t B, Hq, Hkv, G, D;
+  int64_t N;
+  sa_dtype q_dtype, kv_dtype;
+  int64_t sb, sh, st;
+  float scale;  // softmax scale (already defaulted)
+};
+
+// ------------------------------------------------------------- scoring
+hipError_t launch_score_exact(const Cache& c, const void* q, const void* k, float* scores,
+                              hipStream_t s);
+hipError_t launch_block_summarize(const Cache& c, int32_t bs, const void* k, void* kmin, void* kmax,
+                                  hipStream_t s);
+hipError_t launch_score_block(const Cache& c, int32_t bs, const void* q, const void* kmin,
+                              const void* kmax, float* scores, hipStream_t s);
+hipError_t launch_score_indexer(int32_t B, int64_t N, int32_t H, int32_t Di, const void* q_idx,
+                                const void* k_idx, const float* w, float* scores, hipStream_t s);
+
+// --------------------------------------------------------------- top-k
+size_t topk_workspace_bytes(int64_t n_rows, int64_t n, int32_t k);
+hipError_t launch_topk(const float* scores, int64_t n_rows, int64_t n, int64_t row_stride, int32_t k,
+                       int32_t* idx, void* ws, hipStream_t s);
+
+// ----------------------------------------------------------- attention
+enum IndexMode : int { kIdxTokenPerHead = 0, kIdxTokenShared = 1, kIdxBlockPerHead = 2, kIdxDense = 3 };
+
+struct AttendPlan {
+  int mode;
+  int64_t n_slots;  // selected slots per row (tokens, or block slots)
+  int32_t chunk;    // slots per workgroup
+  int32_t nsplit;   // workgroups per row
+  size_t ws_bytes;  // counters + partials
+};
+
+AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs);
+hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, const void* k,
+                         const void* v, const int32_t* idx, int32_t n_idx, int32_t bs, float* out,
+                         void* ws, hipStream_t s);
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace sa

@@ -1,0 +1,437 @@
+// Token and block scoring kernels.
+//
+//  * score_exact: exact score of every cached token of every (sequence, KV
+//    head) row -- the "oracle top-k" selection criterion of "Inference-time
+//    context sparsity: illusion or opportunity?" (section 2).  The G query
+//    heads of a row are summed first (sum_g q_g . k = (sum_g q_g) . k), kept in
+//    fp32, so one dot product per token streams the key cache once.
+//  * block_summarize / score_block: per-128-token-block elementwise key
+//    min/max and the block upper bound sum_i max(q_i kmin_i, q_i kmax_i),
+//    summed over the group ("HyLRA" summary, section 2.4).  The kernel uses
+//    max(q kmin, q kmax) = q+ kmax + q- kmin with q+ = max(q, 0), q- =
+//    min(q, 0), which holds because kmin <= kmax, and folds the group sum into
+//    Q+ = sum_g q_g+ and Q- = sum_g q_g-.
+//  * score_indexer: the low-dimensional indexer of "Flash Attention vs Sparse
+//    Attention" (DSA, Stage 1): sum_h w_h max(0, q_idx_h . k_idx_t).
+//
+// All kernels are HBM-streaming: a lane group of LPR lanes reads one cache row
+// with 16-byte loads, reduces its dot product with DPP inside the group, and
+// each wave covers a contiguous run of tokens so both loads and score stores
+// are coalesced.
+#include <math.h>
+
+#include <algorithm>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace sa {
+namespace {
+
+constexpr int kThreads = 256;
+
+// ------------------------------------------------------------ exact score
+
+struct ExactArgs {
+  const void* q;
+  sa_dtype q_dtype;
+  const uint8_t* k;
+  int64_t sb, sh, st;
+  int32_t Hq, Hkv, G;
+  int64_t N;
+  float scale;
+  float* scores;
+  int32_t tile;  // tokens per workgroup
+};
+
+template <typename KT, int D, int U>
+__global__ __launch_bounds__(kThreads) void score_exact_kernel(ExactArgs a) {
+  constexpr int EB = Elt<KT>::kBytes;
+  constexpr int E = Elt<KT>::kPer16B;
+  constexpr int LPR = D * EB / 16;
+  constexpr int RPW = 64 / LPR;  // rows per wave load
+  static_assert(U <= LPR, "one storing lane per unrolled token");
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lg = (tid & 63) / LPR;
+  const int sl = tid % LPR;
+  const int row = blockIdx.y;
+  const int b = row / a.Hkv;
+  const int r = row % a.Hkv;
+
+  float qs[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    float acc = 0.0f;
+    for (int g = 0; g < a.G; ++g)
+      acc += load_q(a.q, a.q_dtype, ((int64_t)b * a.Hq + (int64_t)r * a.G + g) * D + sl * E + e);
+    qs[e] = acc * a.scale;
+  }
+
+  const uint8_t* kbase = a.k + ((int64_t)b * a.sb + (int64_t)r * a.sh) * EB + sl * 16;
+  const int64_t row_bytes = a.st * EB;
+  float* srow = a.scores + (int64_t)row * a.N;
+
+  const int64_t t_tile = (int64_t)blockIdx.x * a.tile;
+  const int64_t t_end = min(t_tile + (int64_t)a.tile, a.N);
+  constexpr int per_wave_iter = RPW * U;
+  constexpr int per_iter = 4 * per_wave_iter;
+  for (int64_t base = t_tile; base < t_end; base += per_iter) {
+    const int64_t wbase = base + wave * per_wave_iter;
+    uint4 kw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t t = wbase + u * RPW + lg;
+      kw[u] = (t < t_end) ? ld16(kbase + t * row_bytes) : make_uint4(0, 0, 0, 0);
+    }
+    float mine = 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[E];
+      unpack16<KT>(kw[u], kf);
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc = fmaf(qs[e], kf[e], acc);
+      acc = group_sum<LPR>(acc);
+      if (sl == u) mine = acc;
+    }
+    const int64_t t = wbase + sl * RPW + lg;
+    if (sl < U && t < t_end) srow[t] = mine;
+  }
+}
+
+// -------------------------------------------------------- block summaries
+
+struct SumArgs {
+  const uint8_t* k;
+  int64_t sb, sh, st;
+  int32_t Hkv;
+  int64_t N;
+  int32_t bs;
+  int32_t nb;
+  uint8_t* kmin;
+  uint8_t* kmax;
+};
+
+template <typename KT>
+__device__ __forceinline__ void store_elem(uint8_t* base, int64_t i, float f);
+template <>
+__device__ __forceinline__ void store_elem<bf16_t>(uint8_t* base, int64_t i, float f) {
+  // f is a widened bf16 value: its low 16 bits are zero, so this is exact.
+  reinterpret_cast<uint16_t*>(base)[i] = (uint16_t)(__float_as_uint(f) >> 16);
+}
+template <>
+__device__ __forceinline__ void store_elem<float>(uint8_t* base, int64_t i, float f) {
+  reinterpret_cast<float*>(base)[i] = f;
+}
+
+template <typename KT, int D>
+__global__ __launch_bounds__(kThreads) void block_summarize_kernel(SumArgs a) {
+  constexpr int EB = Elt<KT>::kBytes;
+  constexpr int E = Elt<KT>::kPer16B;
+  constexpr int LPR = D * EB / 16;
+  constexpr int NG = kThreads / LPR;
+  __shared__ float s_mn[NG][D];
+  __shared__ float s_mx[NG][D];
+
+  const int tid = threadIdx.x;
+  const int grp = tid / LPR;
+  const int sl = tid % LPR;
+  const int row = blockIdx.y;
+  const int j = blockIdx.x;
+  const int b = row / a.Hkv;
+  const int r = row % a.Hkv;
+  const uint8_t* kbase = a.k + ((int64_t)b * a.sb + (int64_t)r * a.sh) * EB + sl * 16;
+  const int64_t row_bytes = a.st * EB;
+  const int64_t t0 = (int64_t)j * a.bs;
+  const int64_t t1 = min(t0 + (int64_t)a.bs, a.N);
+
+  float mn[E], mx[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    mn[e] = INFINITY;
+    mx[e] = -INFINITY;
+  }
+  for (int64_t t = t0 + grp; t < t1; t += NG) {
+    float kf[E];
+    unpack16<KT>(ld16(kbase + t * row_bytes), kf);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      mn[e] = fminf(mn[e], kf[e]);
+      mx[e] = fmaxf(mx[e], kf[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    s_mn[grp][sl * E + e] = mn[e];
+    s_mx[grp][sl * E + e] = mx[e];
+  }
+  __syncthreads();
+  const int64_t out = ((int64_t)row * a.nb + j) * D;
+  for (int x = tid; x < 2 * D; x += kThreads) {
+    const int dim = x % D;
+    if (x < D) {
+      float v = INFINITY;
+#pragma unroll
+      for (int q = 0; q < NG; ++q) v = fminf(v, s_mn[q][dim]);
+      store_elem<KT>(a.kmin, out + dim, v);
+    } else {
+      float v = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < NG; ++q) v = fmaxf(v, s_mx[q][dim]);
+      store_elem<KT>(a.kmax, out + dim, v);
+    }
+  }
+}
+
+// ------------------------------------------------------------ block score
+
+struct BlockArgs {
+  const void* q;
+  sa_dtype q_dtype;
+  const uint8_t* kmin;
+  const uint8_t* kmax;
+  int32_t Hq, Hkv, G;
+  int32_t nb;
+  float* scores;
+};
+
+template <typename KT, int D>
+__global__ __launch_bounds__(kThreads) void score_block_kernel(BlockArgs a) {
+  constexpr int EB = Elt<KT>::kBytes;
+  constexpr int E = Elt<KT>::kPer16B;
+  constexpr int LPR = D * EB / 16;
+  constexpr int NG = kThreads / LPR;
+  const int tid = threadIdx.x;
+  const int grp = tid / LPR;
+  const int sl = tid % LPR;
+  const int row = blockIdx.y;
+  const int b = row / a.Hkv;
+  const int r = row % a.Hkv;
+
+  float qp[E], qn[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    float p = 0.0f, n = 0.0f;
+    for (int g = 0; g < a.G; ++g) {
+      const float v =
+          load_q(a.q, a.q_dtype, ((int64_t)b * a.Hq + (int64_t)r * a.G + g) * D + sl * E + e);
+      p += fmaxf(v, 0.0f);
+      n += fminf(v, 0.0f);
+    }
+    qp[e] = p;
+    qn[e] = n;
+  }
+  for (int j = blockIdx.x * NG + grp; j < a.nb; j += gridDim.x * NG) {
+    const int64_t off = (((int64_t)row * a.nb + j) * D) * EB + sl * 16;
+    float mn[E], mx[E];
+    unpack16<KT>(ld16(a.kmin + off), mn);
+    unpack16<KT>(ld16(a.kmax + off), mx);
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc = fmaf(qp[e], mx[e], fmaf(qn[e], mn[e], acc));
+    acc = group_sum<LPR>(acc);
+    if (sl == 0) a.scores[(int64_t)row * a.nb + j] = acc;
+  }
+}
+
+// --------------------------------------------------------------- indexer
+
+struct IndexerArgs {
+  const uint8_t* q_idx;  // [B, H, DI] bf16
+  const uint8_t* k_idx;  // [B, N, DI] bf16
+  const float* w;        // [B, H]
+  int32_t H;
+  int64_t N;
+  float* scores;         // [B, N]
+  int32_t tile;
+};
+
+template <int DI, int HP, int U>
+__global__ __launch_bounds__(kThreads) void score_indexer_kernel(IndexerArgs a) {
+  constexpr int E = 8;
+  constexpr int LPR = DI * 2 / 16;
+  constexpr int RPW = 64 / LPR;
+  static_assert(U <= LPR, "one storing lane per unrolled token");
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lg = (tid & 63) / LPR;
+  const int sl = tid % LPR;
+  const int b = blockIdx.y;
+
+  float qv[HP][E];
+  float wv[HP];
+#pragma unroll
+  for (int h = 0; h < HP; ++h) {
+    const bool live = h < a.H;
+    wv[h] = live ? a.w[(int64_t)b * a.H + h] : 0.0f;
+    float f[E];
+    if (live) {
+      unpack16<bf16_t>(ld16(a.q_idx + (((int64_t)b * a.H + h) * DI) * 2 + sl * 16), f);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) f[e] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) qv[h][e] = f[e];
+  }
+
+  const uint8_t* kbase = a.k_idx + (int64_t)b * a.N * DI * 2 + sl * 16;
+  float* srow = a.scores + (int64_t)b * a.N;
+  const int64_t t_tile = (int64_t)blockIdx.x * a.tile;
+  const int64_t t_end = min(t_tile + (int64_t)a.tile, a.N);
+  constexpr int per_wave_iter = RPW * U;
+  constexpr int per_iter = 4 * per_wave_iter;
+  for (int64_t base = t_tile; base < t_end; base += per_iter) {
+    const int64_t wbase = base + wave * per_wave_iter;
+    uint4 kw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t t = wbase + u * RPW + lg;
+      kw[u] = (t < t_end) ? ld16(kbase + t * (DI * 2)) : make_uint4(0, 0, 0, 0);
+    }
+    float mine = 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[E];
+      unpack16<bf16_t>(kw[u], kf);
+      float sc = 0.0f;
+#pragma unroll
+      for (int h = 0; h < HP; ++h) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc = fmaf(qv[h][e], kf[e], acc);
+        acc = group_sum<LPR>(acc);
+        sc = fmaf(wv[h], fmaxf(acc, 0.0f), sc);
+      }
+      if (sl == u) mine = sc;
+    }
+    const int64_t t = wbase + sl * RPW + lg;
+    if (sl < U && t < t_end) srow[t] = mine;
+  }
+}
+
+template <int DI, int HP>
+hipError_t launch_indexer_hp(const IndexerArgs& a, dim3 grid, hipStream_t s) {
+  constexpr int LPR = DI * 2 / 16;
+  constexpr int U = LPR < 8 ? LPR : 8;
+  hipLaunchKernelGGL((score_indexer_kernel<DI, HP, U>), grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DI>
+hipError_t launch_indexer_di(const IndexerArgs& a, dim3 grid, hipStream_t s) {
+  if (a.H <= 4) return launch_indexer_hp<DI, 4>(a, grid, s);
+  if (a.H <= 8) return launch_indexer_hp<DI, 8>(a, grid, s);
+  return launch_indexer_hp<DI, 16>(a, grid, s);
+}
+
+}  // namespace
+
+hipError_t launch_score_exact(const Cache& c, const void* q, const void* k, float* scores,
+                              hipStream_t s) {
+  ExactArgs a{};
+  a.q = q;
+  a.q_dtype = c.q_dtype;
+  a.k = static_cast<const uint8_t*>(k);
+  a.sb = c.sb;
+  a.sh = c.sh;
+  a.st = c.st;
+  a.Hq = c.Hq;
+  a.Hkv = c.Hkv;
+  a.G = c.G;
+  a.N = c.N;
+  a.scale = c.scale;
+  a.scores = scores;
+  a.tile = 1024;
+  const dim3 grid((unsigned)((c.N + a.tile - 1) / a.tile), (unsigned)(c.B * c.Hkv));
+  if (c.kv_dtype == SA_BF16) {
+    if (c.D == 64)
+      hipLaunchKernelGGL((score_exact_kernel<bf16_t, 64, 8>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((score_exact_kernel<bf16_t, 128, 8>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    if (c.D == 64)
+      hipLaunchKernelGGL((score_exact_kernel<float, 64, 8>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((score_exact_kernel<float, 128, 8>), grid, dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_block_summarize(const Cache& c, int32_t bs, const void* k, void* kmin, void* kmax,
+                                  hipStream_t s) {
+  SumArgs a{};
+  a.k = static_cast<const uint8_t*>(k);
+  a.sb = c.sb;
+  a.sh = c.sh;
+  a.st = c.st;
+  a.Hkv = c.Hkv;
+  a.N = c.N;
+  a.bs = bs;
+  a.nb = (int32_t)((c.N + bs - 1) / bs);
+  a.kmin = static_cast<uint8_t*>(kmin);
+  a.kmax = static_cast<uint8_t*>(kmax);
+  const dim3 grid((unsigned)a.nb, (unsigned)(c.B * c.Hkv));
+  if (c.kv_dtype == SA_BF16) {
+    if (c.D == 64)
+      hipLaunchKernelGGL((block_summarize_kernel<bf16_t, 64>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((block_summarize_kernel<bf16_t, 128>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    if (c.D == 64)
+      hipLaunchKernelGGL((block_summarize_kernel<float, 64>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((block_summarize_kernel<float, 128>), grid, dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_score_block(const Cache& c, int32_t bs, const void* q, const void* kmin,
+                              const void* kmax, float* scores, hipStream_t s) {
+  BlockArgs a{};
+  a.q = q;
+  a.q_dtype = c.q_dtype;
+  a.kmin = static_cast<const uint8_t*>(kmin);
+  a.kmax = static_cast<const uint8_t*>(kmax);
+  a.Hq = c.Hq;
+  a.Hkv = c.Hkv;
+  a.G = c.G;
+  a.nb = (int32_t)((c.N + bs - 1) / bs);
+  a.scores = scores;
+  const int lpr = c.D * (c.kv_dtype == SA_BF16 ? 2 : 4) / 16;
+  const int ng = kThreads / lpr;
+  const unsigned gx = (unsigned)std::min<int64_t>((a.nb + ng - 1) / ng, 65535);
+  const dim3 grid(gx, (unsigned)(c.B * c.Hkv));
+  if (c.kv_dtype == SA_BF16) {
+    if (c.D == 64)
+      hipLaunchKernelGGL((score_block_kernel<bf16_t, 64>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((score_block_kernel<bf16_t, 128>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    if (c.D == 64)
+      hipLaunchKernelGGL((score_block_kernel<float, 64>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((score_block_kernel<float, 128>), grid, dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_score_indexer(int32_t B, int64_t N, int32_t H, int32_t Di, const void* q_idx,
+                                const void* k_idx, const float* w, float* scores, hipStream_t s) {
+  IndexerArgs a{};
+  a.q_idx = static_cast<const uint8_t*>(q_idx);
+  a.k_idx = static_cast<const uint8_t*>(k_idx);
+  a.w = w;
+  a.H = H;
+  a.N = N;
+  a.scores = scores;
+  a.tile = 1024;
+  const dim3 grid((unsigned)((N + a.tile - 1) / a.tile), (unsigned)B);
+  if (Di == 32) return launch_indexer_di<32>(a, grid, s);
+  if (Di == 64) return launch_indexer_di<64>(a, grid, s);
+  return launch_indexer_di<128>(a, grid, s);
+}
+
+}  // namespace sa
