@@ -1,0 +1,247 @@
+"""Benchmark of the top-k sparse decode attention path on one MI355X.
+
+Workload (default): the Llama-3.1-8B-shaped decode step -- batch 16, 32 query
+/ 8 KV heads, head_dim 128, bf16 KV cache of 32768 tokens per sequence, exact
+top-k per (sequence, KV head) at 50x sparsity (k = 655).  One step is one pass
+of the whole hot path through the C ABI:
+    sa_score (exact) -> sa_topk -> sa_sparse_decode (gather + split-K attend).
+Queries rotate over 8 pre-generated variants so consecutive steps select
+different tokens; the cache (2.15 GB) is resident in HBM before timing starts.
+
+Timing: W untimed warmup steps, then K timed steps bracketed by
+torch.cuda.synchronize(); HIP events recorded on the launch stream between
+the three calls give each kernel's average duration over the same region.
+
+Prints ONE JSON line.  `value` is the step's achieved HBM bandwidth
+(algorithmic bytes of score + top-k + attend per step / time per step);
+`steps_per_s` is the decode-step rate; `roofline` is the dominant kernel
+(exact scoring); `kernels` holds every kernel's bytes, time and fraction of
+the 8 TB/s peak, including the gather-attend kernel alone and a dense decode
+over the same cache for comparison.  `cpu_baseline` times the CPU oracle on a
+bounded sample of the same step (rows of the batch), scaled to a full step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E peak, GB/s
+N_QVAR = 8
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="llama32k")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="bound on the oracle's CPU time for cpu_baseline (0 disables)")
+    p.add_argument("--dense-steps", type=int, default=20)
+    p.add_argument("--profile", action="store_true",
+                   help="short run for a profiler: few steps, no dense, no cpu baseline")
+    return p.parse_args()
+
+
+def step_bytes(cfg):
+    """Algorithmic HBM bytes of one step's kernels (each input read once,
+    each output written once)."""
+    B, Hq, Hkv, d, N, k = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ctx_len, cfg.k
+    e = cfg.elt
+    rows = B * Hkv
+    q_bytes = B * Hq * d * e
+    scores = rows * N * 4
+    idx = rows * k * 4
+    out = B * Hq * d * 4
+    return {
+        "score_exact": rows * N * d * e + q_bytes + scores,
+        "topk": scores + idx,
+        "sparse_attend": 2 * rows * k * d * e + idx + q_bytes + out,
+        "dense_decode": 2 * rows * N * d * e + q_bytes + out,
+    }
+
+
+def cpu_baseline(w, q_host, k_host, v_host, seconds):
+    """Time the oracle, one BLAS thread, on whole rows of the step until
+    `seconds` elapse; returns (seconds per full step, rows timed, rows)."""
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+
+    c = w.cfg
+    scale = O.default_scale(c.head_dim)
+    rows = c.batch * c.n_kv_heads
+    rows_done = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        qf = O.widen(q_host[0])
+        for row in range(rows):
+            b, r = divmod(row, c.n_kv_heads)
+            qg = qf[b, r * c.group:(r + 1) * c.group]
+            kf = O.widen(k_host[b, r])
+            s = O.scores_exact(qg, kf, scale)
+            sel = O.topk(s, c.k)
+            O.attend(qg, kf, O.widen(v_host[b, r]), sel, scale)
+            rows_done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+    return dt * rows / rows_done, rows_done, rows
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if args.profile:
+        args.steps, args.warmup, args.cpu_seconds, args.dense_steps = 20, 5, 0.0, 0
+
+    import torch
+    import sa_synth as S
+    import top_sparse_decode_sa_amd as T
+
+    T.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda", 0)
+    w = S.Workload(args.workload, args.seed)
+    c = w.cfg
+    assert c.planting == "direction" and c.block_size == 0, "bench workload must be exact top-k"
+    log("bench: generating %s (%.2f GB of KV) ..." % (c.name, c.kv_bytes() / 1e9))
+    t0 = time.perf_counter()
+    k_host, v_host = w.k(), w.v()
+    q_host = [w.q(qvar=i) for i in range(N_QVAR)]
+    log("bench: generated in %.1f s; uploading" % (time.perf_counter() - t0))
+
+    def up(x):
+        t = torch.from_numpy(x)
+        return (t.view(torch.bfloat16) if t.dtype == torch.uint16 else t).to(dev)
+
+    kd, vd = up(k_host), up(v_host)
+    qd = [up(q) for q in q_host]
+    rows = c.batch * c.n_kv_heads
+    scores = torch.empty((c.batch, c.n_kv_heads, c.ctx_len), dtype=torch.float32, device=dev)
+    idx = torch.empty((c.batch, c.n_kv_heads, c.k), dtype=torch.int32, device=dev)
+    out = torch.empty((c.batch, c.n_q_heads, c.head_dim), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        q = qd[i % N_QVAR]
+        if ev is not None:
+            ev[0].record()
+        T.sa_score(q, kd, T.SA_SCORE_EXACT, scores=scores)
+        if ev is not None:
+            ev[1].record()
+        T.sa_topk(scores, c.k, idx_out=idx)
+        if ev is not None:
+            ev[2].record()
+        T.sa_sparse_decode(q, kd, vd, idx, out=out)
+        if ev is not None:
+            ev[3].record()
+
+    log("bench: warmup %d steps" % args.warmup)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log("bench: timing %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_score = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    ms_topk = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    ms_attend = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+    ms_step = wall * 1e3 / args.steps
+
+    # dense decode over the same cache (comparison for the sparse/dense ratio)
+    ms_dense = None
+    if args.dense_steps > 0:
+        dout = torch.empty_like(out)
+        for i in range(3):
+            T.sa_dense_decode(qd[i % N_QVAR], kd, vd, out=dout)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.dense_steps):
+            T.sa_dense_decode(qd[i % N_QVAR], kd, vd, out=dout)
+        e1.record()
+        torch.cuda.synchronize()
+        ms_dense = e0.elapsed_time(e1) / args.dense_steps
+
+    nbytes = step_bytes(c)
+    step_total = nbytes["score_exact"] + nbytes["topk"] + nbytes["sparse_attend"]
+    gbps = step_total / (ms_step * 1e-3) / 1e9
+
+    def kern(name, ms):
+        if ms is None:
+            return None
+        g = nbytes[name] / (ms * 1e-3) / 1e9
+        return {"bytes": nbytes[name], "us": round(ms * 1e3, 3), "gbps": round(g, 1),
+                "frac": round(g / HBM_PEAK_GBPS, 4)}
+
+    kernels = {"score_exact": kern("score_exact", ms_score), "topk": kern("topk", ms_topk),
+               "sparse_attend": kern("sparse_attend", ms_attend),
+               "dense_decode": kern("dense_decode", ms_dense)}
+    # dominant kernel of the step: the one with the largest share of its time
+    dom = max(["score_exact", "topk", "sparse_attend"], key=lambda n: kernels[n]["us"])
+    roof = {"bound": "hbm", "achieved": kernels[dom]["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": kernels[dom]["frac"], "traffic": None, "kernel": dom,
+            "bytes_per_launch": nbytes[dom]}
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("bench: oracle cpu baseline (bounded to %.0f s)" % args.cpu_seconds)
+        step_s, done, total = cpu_baseline(w, q_host, k_host, v_host, args.cpu_seconds)
+        cpu = {"value": round(step_total / step_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle", "steps_per_s": round(1.0 / step_s, 4),
+               "sample": "fp64 numpy oracle, one thread: score+top-k+attend of %d of the %d "
+                         "(sequence, KV head) rows of one step, scaled by %d/%d" % (
+                             done, total, total, done)}
+
+    line = {
+        "metric": "sparse-decode attn: achieved HBM GB/s (% of peak) + decode steps/s at 50x",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "steps_per_s": round(1e3 / ms_step, 1),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based generator; planted heavy keys)",
+        "config": {"workload": "llama3.1-8b-shaped decode, exact top-k at 50x sparsity",
+                   "batch": c.batch, "n_q_heads": c.n_q_heads, "n_kv_heads": c.n_kv_heads,
+                   "head_dim": c.head_dim, "ctx_len": c.ctx_len, "k": c.k,
+                   "kv_dtype": c.dtype, "parallelism": "single GPU"},
+        "roofline": roof,
+        "kernels": kernels,
+        "sparse_over_dense_speedup": (round(ms_dense / ms_attend, 2) if ms_dense else None),
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(0),
+        "hip": torch.version.hip,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

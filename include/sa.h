@@ -36,13 +36,10 @@
  *   - Calls are thread-safe.  Two calls that run concurrently must not share
  *     a workspace.
  *   - Workspaces: any call taking (ws, ws_bytes) needs at least the bytes the
- *     matching *_workspace_size() function returns, 256-byte aligned.  A
- *     workspace belongs to one call kind and one set of argument shapes (the
- *     ones it was sized for).  Zero it once before its first use
- *     (sa_workspace_init or any zero fill) and again after a failed call;
- *     every completed call leaves the workspace ready for the next call of
- *     the same kind and shapes (the split counters inside it are back at
- *     zero), so it is not re-initialised per call.
+ *     matching *_workspace_size() function returns (0 means none; ws may then
+ *     be null), 256-byte aligned.  The library only uses it as scratch
+ *     between the launches of one call: no initialisation is needed and
+ *     nothing is kept in it between calls.
  *   - Layouts are row-major.  "Row" means one (sequence, KV head) pair.
  *     Query head h belongs to KV head h / G with G = n_q_heads / n_kv_heads.
  */
@@ -235,8 +232,8 @@ sa_status sa_plan_validate(const int32_t* modes, const int32_t* src, int32_t n_l
 
 /* ----------------------------------------------------------------- misc */
 
-/* Zero a workspace region on `stream` (a fill kernel, so it is safe inside
- * stream capture). */
+/* Zero a device region on `stream` with a fill kernel (safe inside stream
+ * capture).  Workspaces need no initialisation; this is a utility. */
 sa_status sa_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Static description of a status code. */

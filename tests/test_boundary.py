@@ -75,11 +75,12 @@ def test_pointer_index_and_workspace_errors():
     assert _sparse(d, n_idx=0) == Bn.SA_ERR_SHAPE
     assert _sparse(d, ik=9) == Bn.SA_ERR_SHAPE
     assert _sparse(d, ik=Bn.SA_IDX_BLOCK_PER_KV_HEAD, bs=0) == Bn.SA_ERR_SHAPE
-    need = L.sa_sparse_workspace_size(ctypes.byref(d), 0, 10, 0)
+    # a selection long enough to be split across workgroups needs scratch
+    need = L.sa_sparse_workspace_size(ctypes.byref(d), 0, 500, 0)
     assert need > 0 and need % 256 == 0
-    assert _sparse(d, ws=None, nbytes=0) == Bn.SA_ERR_WORKSPACE
-    assert _sparse(d, ws=FAKE, nbytes=need - 1) == Bn.SA_ERR_WORKSPACE
-    assert _sparse(d, ws=ctypes.c_void_p((1 << 20) + 16), nbytes=need) == Bn.SA_ERR_ALIGN
+    assert _sparse(d, n_idx=500, ws=None, nbytes=0) == Bn.SA_ERR_WORKSPACE
+    assert _sparse(d, n_idx=500, ws=FAKE, nbytes=need - 1) == Bn.SA_ERR_WORKSPACE
+    assert _sparse(d, n_idx=500, ws=ctypes.c_void_p((1 << 20) + 16), nbytes=need) == Bn.SA_ERR_ALIGN
     assert L.sa_dense_decode(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 0, None) == \
         Bn.SA_ERR_WORKSPACE
     assert L.sa_dense_workspace_size(ctypes.byref(_desc(head_dim=96))) == 0

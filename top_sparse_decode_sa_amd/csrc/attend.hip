@@ -1,6 +1,5 @@
 // Split-K online-softmax decode attention over a selected token set (or over
-// the whole cache), with the log-sum-exp combine of the splits fused into the
-// same launch.
+// the whole cache), and the log-sum-exp combine of the splits.
 //
 // What is computed ("Flash Attention vs Sparse Attention", DSA Stage 2 and
 // the tiling + online-softmax section; "Inference-time context sparsity",
@@ -8,18 +7,33 @@
 // attention restricted to the row's selected tokens, reading only those K/V
 // rows from HBM.
 //
-// Work split (gfx950, wave64):
-//   grid = (nsplit, rows).  A 256-thread workgroup takes `chunk` consecutive
-//   slots of its row's selection.  A "lane group" of LPR lanes holds one cache
-//   row as LPR 16-byte pieces (bf16, d=128: 16 lanes x 8 values), so one wave
-//   load instruction fetches 64/LPR whole rows with 128-bit loads.
-//   Every lane group runs its own online softmax (running max m, sum l,
-//   unnormalised output o, all fp32, exp in base 2 with log2(e) folded into
-//   q), groups merge through LDS, and the workgroup writes one partial
-//   (m, l, o) per query head.  The last workgroup of a row to finish (device
-//   atomic counter) merges the nsplit partials and writes the output, then
-//   resets the counter to zero for the next call.
+// Two launches:
+//   1. attend: grid (nsplit, rows).  A workgroup takes `chunk` consecutive
+//      slots of its row's selection and writes one partial per query head:
+//      (o = sum_t exp2(l_t - m) V_t, m, l = sum_t exp2(l_t - m)), logits in
+//      base 2 (log2(e) folded into q).  With nsplit == 1 it writes o / l
+//      directly and there is no second launch.
+//   2. combine: grid (rows, G); merges the nsplit partials of a row with a
+//      log-sum-exp combine and writes the fp32 output.
+// The partials travel through the workspace between the two launches; the
+// kernel boundary makes them visible, so no cross-workgroup synchronisation
+// (and no zero-initialised counter) is needed.
+//
+// Kernels:
+//   * attend_wave_kernel (bf16, head_dim 128, G <= 4): one wave processes
+//     16-token tiles.  Lane l holds token l%16's key dims [32c + 8(l/16), +8)
+//     (c = 0..3) -- the B operand of v_mfma_f32_16x16x32_bf16 with the
+//     group's queries as the A operand -- so four MFMAs give the G logits of
+//     16 tokens in lanes 0..15.  Value loads use 128-bit row pieces (token
+//     4u + l/16, dims [8(l%16), +8)); p reaches that layout through a 256-byte
+//     LDS slot of the wave; o accumulates in fp32.  Loads of tile t+1 are in
+//     flight while tile t computes.  Sparse selections use one-wave
+//     workgroups (no barrier, waves retire independently); dense decode uses
+//     four waves per workgroup merged through LDS.
+//   * attend_kernel (any other dtype / head_dim / group): lane groups of LPR
+//     lanes hold whole cache rows; logits reduce with DPP inside the group.
 #include <math.h>
+#include <stdlib.h>
 
 #include <algorithm>
 
@@ -30,8 +44,7 @@ namespace sa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;        // slots per lane group in flight per iteration
-constexpr int kTargetGroups = 4096;
+constexpr int kUnroll = 4;  // generic kernel: slots per lane group in flight
 
 struct AttendArgs {
   const void* q;
@@ -49,8 +62,7 @@ struct AttendArgs {
   int32_t chunk;
   int32_t nsplit;
   float* out;
-  float* part;
-  uint32_t* counters;
+  float* part;  // [rows, nsplit, G, D + 2]: o[G][D], m[G], l[G]
 };
 
 template <int MODE>
@@ -70,6 +82,25 @@ __device__ __forceinline__ int64_t resolve_slot(const AttendArgs& a, int row, in
   }
 }
 
+// Write one workgroup's value for query head h, dimension dim: the final
+// output when the row has one split, else the partial (o, and m/l once).
+template <int G, int D>
+__device__ __forceinline__ void write_result(const AttendArgs& a, int row, int split, int b, int r,
+                                             int h, int dim, float O, float M, float L) {
+  if (a.nsplit == 1) {
+    a.out[((int64_t)b * a.Hq + (int64_t)r * G + h) * D + dim] = O / L;
+  } else {
+    float* p = a.part + ((int64_t)row * a.nsplit + split) * (G * (D + 2));
+    p[h * D + dim] = O;
+    if (dim == 0) {
+      p[G * D + h] = M;
+      p[G * D + G + h] = L;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Generic kernel: lane groups hold whole rows, DPP reductions.
 template <typename KT, int D, int G, int MODE>
 __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
   constexpr int EB = Elt<KT>::kBytes;
@@ -81,7 +112,6 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
   __shared__ float s_m[NG][G];
   __shared__ float s_l[NG][G];
   __shared__ float s_o[NG][G][D];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int grp = tid / LPR;
@@ -133,7 +163,6 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
         vw[u] = make_uint4(0, 0, 0, 0);
       }
     }
-
     float lg[U][G];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -148,11 +177,9 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
         lg[u][g] = ok[u] ? acc : -INFINITY;
       }
     }
-
     float vf[U][E];
 #pragma unroll
     for (int u = 0; u < U; ++u) unpack16<KT>(vw[u], vf[u]);
-
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float bm = lg[0][g];
@@ -179,7 +206,6 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
     }
   }
 
-  // ---- merge the lane groups of this workgroup
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     if (sl == 0) {
@@ -190,10 +216,6 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
     for (int e = 0; e < E; ++e) s_o[grp][g][sl * E + e] = o[g][e];
   }
   __syncthreads();
-
-  const int64_t out_base = ((int64_t)b * a.Hq + (int64_t)r * G) * D;
-  constexpr int PS = G * (D + 2);  // floats per partial: o[G][D], m[G], l[G]
-  float* my_part = a.part + ((int64_t)row * a.nsplit + split) * PS;
   for (int x = tid; x < G * D; x += kThreads) {
     const int g = x / D;
     const int dim = x % D;
@@ -209,45 +231,408 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
         O = fmaf(s_o[q][g][dim], w, O);
       }
     }
-    if (a.nsplit == 1) {
-      a.out[out_base + x] = O / L;
-    } else {
-      my_part[x] = O;
-      if (dim == 0) {
-        my_part[G * D + g] = M;
-        my_part[G * D + G + g] = L;
-      }
-    }
+    write_result<G, D>(a, row, split, b, r, g, dim, O, M, L);
   }
-  if (a.nsplit == 1) return;
-
-  // ---- fused split combine: the last workgroup of the row merges
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = atomicAdd(&a.counters[row], 1u);
-    s_last = (prev == (uint32_t)(a.nsplit - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const float* pr = a.part + (int64_t)row * a.nsplit * PS;
-  for (int x = tid; x < G * D; x += kThreads) {
-    const int g = x / D;
-    float M = -INFINITY;
-    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, pr[(int64_t)s * PS + G * D + g]);
-    float L = 0.0f, O = 0.0f;
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float* ps = pr + (int64_t)s * PS;
-      const float w = exp2f(ps[G * D + g] - M);
-      L = fmaf(ps[G * D + G + g], w, L);
-      O = fmaf(ps[x], w, O);
-    }
-    a.out[out_base + x] = O / L;
-  }
-  if (tid == 0) a.counters[row] = 0u;
 }
 
+// ---------------------------------------------------------------------------
+// bf16, head_dim 128, G <= 4: MFMA logits, one wave per 16-token tile.
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+__device__ __forceinline__ float wave_bcast0(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+struct TileLoads {
+  uint4 kw[4];
+  uint4 vw[4];
+  bool okk;
+};
+
+template <int MODE>
+__device__ __forceinline__ void load_tile(const AttendArgs& a, int row, int b, int64_t jbase,
+                                          int64_t s1, int n, int rq, const uint8_t* kbase,
+                                          const uint8_t* vbase, int64_t row_bytes, TileLoads& T) {
+  T.okk = jbase + n < s1;
+  int64_t tk = 0;
+  if (T.okk) tk = resolve_slot<MODE>(a, row, b, jbase + n, T.okk);
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    T.kw[c] = T.okk ? ld16(kbase + tk * row_bytes + 64 * c) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t jv = jbase + 4 * u + rq;
+    bool okv = jv < s1;
+    int64_t tv = 0;
+    if (okv) tv = resolve_slot<MODE>(a, row, b, jv, okv);
+    T.vw[u] = okv ? ld16(vbase + tv * row_bytes) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+
+// One 16-token tile: MFMA logits, online-softmax update of (m_run, l_run, o).
+// m_run / l_run are wave-uniform; o holds this lane's dims [8n, 8n+8) for the
+// tile's tokens 4u + rq.  s_p is this wave's 16x4 LDS slot.
+template <int G>
+__device__ __forceinline__ void tile_step(const TileLoads& T, const bf16x8_t (&qa)[4], float qscale,
+                                          int n, int rq, float (*s_p)[4], float (&m_run)[G],
+                                          float (&l_run)[G], float (&o)[G][8]) {
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    bf16x8_t kb;
+    __builtin_memcpy(&kb, &T.kw[c], 16);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[c], kb, acc, 0, 0, 0);
+  }
+  float lg[G], tmax[G];
+  bool any = false;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    lg[h] = (rq == 0 && T.okk) ? acc[h] * qscale : -INFINITY;
+    tmax[h] = wave_bcast0(group_max<16>(lg[h]));
+    any |= (tmax[h] != -INFINITY);
+  }
+  if (!any) return;  // wave-uniform: no valid token in this tile
+  float p[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float mn = fmaxf(m_run[h], tmax[h]);
+    const float alpha = exp2f(m_run[h] - mn);
+    p[h] = exp2f(lg[h] - mn);
+    const float tsum = wave_bcast0(group_sum<16>(p[h]));
+    l_run[h] = l_run[h] * alpha + tsum;
+    m_run[h] = mn;
+    if (alpha != 1.0f) {  // wave-uniform
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
+    }
+  }
+  // p to the value layout through the wave's LDS slot (in-order LDS access)
+  if (rq == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) s_p[n][h] = p[h];
+  }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    float pv[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) pv[h] = s_p[4 * u + rq][h];
+    float vf[8];
+    unpack16<bf16_t>(T.vw[u], vf);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] = fmaf(pv[h], vf[e], o[h][e]);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Sum o over the four 16-lane rows (tokens 4u + rq): lanes 0..15 end with the
+// wave's o for dims [8n, 8n + 8).
+template <int G>
+__device__ __forceinline__ void reduce_rows(float (&o)[G][8]) {
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = o[h][e];
+      v += __shfl_xor(v, 32);
+      v += __shfl_xor(v, 16);
+      o[h][e] = v;
+    }
+}
+
+// q of the row's G heads as MFMA A fragments: lane (n, rq) holds head n's dims
+// [32c + 8rq, +8) for c = 0..3 (zero for n >= G).
+template <int G>
+__device__ __forceinline__ void load_q_frag(const AttendArgs& a, int b, int r, int n, int rq,
+                                            bf16x8_t (&qa)[4]) {
+  const uint8_t* qb = static_cast<const uint8_t*>(a.q) +
+                      (((int64_t)b * a.Hq + (int64_t)r * G + (n < G ? n : 0)) * 128 + 8 * rq) * 2;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint4 w = n < G ? ld16(qb + 64 * c) : make_uint4(0, 0, 0, 0);
+    __builtin_memcpy(&qa[c], &w, 16);
+  }
+}
+
+// Selected-set decode, up to 16 * TILES slots per one-wave workgroup.  The
+// memory operations are ordered for the in-order load counter: first one index
+// load per lane per tile (lane l reads the token of slot l % 16), then every
+// key and value load of every tile (value-row token ids come from the owning
+// lane by a shuffle, not from memory), then the compute.
+template <int G, int MODE, int TILES>
+__global__ __launch_bounds__(64) void attend_sparse_kernel(AttendArgs a) {
+  static_assert(G >= 1 && G <= 4, "query heads of a group fit MFMA rows 0..3");
+  constexpr int D = 128;
+  __shared__ float s_p[TILES][16][4];
+  const int lane = threadIdx.x;
+  const int n = lane & 15;
+  const int rq = lane >> 4;
+  const int row = blockIdx.y;
+  const int split = blockIdx.x;
+  const int b = row / a.Hkv;
+  const int r = row % a.Hkv;
+  const int64_t s0 = (int64_t)split * a.chunk;
+  const int64_t s1 = min(s0 + (int64_t)a.chunk, a.n_slots);
+
+  // 1. token of slot 16i + n for every tile i (-1: no token)
+  int32_t tok[TILES];
+#pragma unroll
+  for (int i = 0; i < TILES; ++i) {
+    const int64_t j = s0 + 16 * i + n;
+    bool ok = j < s1;
+    int64_t t = 0;
+    if (ok) t = resolve_slot<MODE>(a, row, b, j, ok);
+    tok[i] = ok ? (int32_t)t : -1;
+  }
+  bf16x8_t qa[4];
+  load_q_frag<G>(a, b, r, n, rq, qa);
+
+  // 2. all key and value loads
+  const int64_t kv_off = ((int64_t)b * a.sb + (int64_t)r * a.sh) * 2;
+  const uint8_t* kbase = a.k + kv_off + 16 * rq;
+  const uint8_t* vbase = a.v + kv_off + 16 * n;
+  const int64_t row_bytes = a.st * 2;
+  // keys of every tile first, then values: the logits and the softmax can
+  // proceed while the value rows are still arriving
+  TileLoads T[TILES];
+#pragma unroll
+  for (int i = 0; i < TILES; ++i) {
+    T[i].okk = tok[i] >= 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      T[i].kw[c] = T[i].okk ? ld16(kbase + (int64_t)tok[i] * row_bytes + 64 * c)
+                            : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < TILES; ++i) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int32_t tv = __shfl(tok[i], 4 * u + rq);
+      T[i].vw[u] = tv >= 0 ? ld16(vbase + (int64_t)tv * row_bytes) : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  // 3. logits of every tile: rows 0..G-1 of the MFMA results, in lanes 0..15
+  float lg[TILES][G];
+#pragma unroll
+  for (int i = 0; i < TILES; ++i) {
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      bf16x8_t kb;
+      __builtin_memcpy(&kb, &T[i].kw[c], 16);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[c], kb, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) lg[i][h] = (rq == 0 && T[i].okk) ? acc[h] * a.qscale : -INFINITY;
+  }
+  // 4. one max per head over the wave's tokens (valid in lanes 0..15), then
+  //    p = 2^(logit - max) and its sum -- no running rescale is needed
+  float M[G], Lsum[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float mx = lg[0][h];
+#pragma unroll
+    for (int i = 1; i < TILES; ++i) mx = fmaxf(mx, lg[i][h]);
+    M[h] = group_max<16>(mx);
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float ls = 0.0f;
+#pragma unroll
+    for (int i = 0; i < TILES; ++i) {
+      const float pv = M[h] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(lg[i][h] - M[h]);
+      lg[i][h] = pv;
+      ls += pv;
+    }
+    Lsum[h] = group_sum<16>(ls);
+  }
+  // 5. p to the value layout through LDS (one wave: in-order LDS access)
+  if (rq == 0) {
+#pragma unroll
+    for (int i = 0; i < TILES; ++i)
+#pragma unroll
+      for (int h = 0; h < G; ++h) s_p[i][n][h] = lg[i][h];
+  }
+  __builtin_amdgcn_wave_barrier();
+  float o[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < TILES; ++i)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float pv[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) pv[h] = s_p[i][4 * u + rq][h];
+      float vf[8];
+      unpack16<bf16_t>(T[i].vw[u], vf);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] = fmaf(pv[h], vf[e], o[h][e]);
+    }
+
+  // 6. lanes 0..15 hold M, Lsum and, after the row reduction, o
+  reduce_rows<G>(o);
+  if (rq == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        write_result<G, D>(a, row, split, b, r, h, 8 * n + e, o[h][e], M[h], Lsum[h]);
+  }
+}
+
+template <int G, int MODE, int WPW>
+__global__ __launch_bounds__(64 * WPW) void attend_wave_kernel(AttendArgs a) {
+  static_assert(G >= 1 && G <= 4, "query heads of a group fit MFMA rows 0..3");
+  constexpr int D = 128;
+  __shared__ float s_p[WPW][16][4];
+  __shared__ float s_o[WPW > 1 ? WPW : 1][G][D];
+  __shared__ float s_ml[WPW > 1 ? WPW : 1][2][G];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 15;
+  const int rq = lane >> 4;
+  const int row = blockIdx.y;
+  const int split = blockIdx.x;
+  const int b = row / a.Hkv;
+  const int r = row % a.Hkv;
+
+  bf16x8_t qa[4];
+  load_q_frag<G>(a, b, r, n, rq, qa);
+
+  const int64_t kv_off = ((int64_t)b * a.sb + (int64_t)r * a.sh) * 2;
+  const uint8_t* kbase = a.k + kv_off + 16 * rq;
+  const uint8_t* vbase = a.v + kv_off + 16 * n;
+  const int64_t row_bytes = a.st * 2;
+
+  float m_run[G], l_run[G], o[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m_run[h] = -INFINITY;
+    l_run[h] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.0f;
+  }
+
+  const int64_t s0 = (int64_t)split * a.chunk;
+  const int64_t s1 = min(s0 + (int64_t)a.chunk, a.n_slots);
+  // tiles of this wave: wave, wave + WPW, ... inside [s0, s1); the next tile's
+  // loads are in flight while the current one computes
+  const int64_t n_tiles = (s1 - s0 + 15) / 16;
+
+  TileLoads cur, nxt;
+  int64_t t = wave;
+  if (t < n_tiles) load_tile<MODE>(a, row, b, s0 + 16 * t, s1, n, rq, kbase, vbase, row_bytes, cur);
+  for (; t < n_tiles; t += WPW) {
+    const bool more = t + WPW < n_tiles;  // wave-uniform
+    if (more)
+      load_tile<MODE>(a, row, b, s0 + 16 * (t + WPW), s1, n, rq, kbase, vbase, row_bytes, nxt);
+
+    tile_step<G>(cur, qa, a.qscale, n, rq, s_p[wave], m_run, l_run, o);
+    if (more) cur = nxt;
+  }
+
+  reduce_rows<G>(o);
+
+  if constexpr (WPW == 1) {
+    if (rq == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          write_result<G, D>(a, row, split, b, r, h, 8 * n + e, o[h][e], m_run[h], l_run[h]);
+    }
+  } else {
+    if (rq == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_o[wave][h][8 * n + e] = o[h][e];
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        s_ml[wave][0][h] = m_run[h];
+        s_ml[wave][1][h] = l_run[h];
+      }
+    }
+    __syncthreads();
+    for (int x = tid; x < G * D; x += 64 * WPW) {
+      const int h = x / D;
+      const int dim = x % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < WPW; ++w) M = fmaxf(M, s_ml[w][0][h]);
+      float L = 0.0f, O = 0.0f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < WPW; ++w) {
+          const float wt = exp2f(s_ml[w][0][h] - M);
+          L = fmaf(s_ml[w][1][h], wt, L);
+          O = fmaf(s_o[w][h][dim], wt, O);
+        }
+      }
+      write_result<G, D>(a, row, split, b, r, h, dim, O, M, L);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine: one workgroup of D threads per (row, query head); thread = one
+// output dimension.  Sixteen splits' (o, m, l) are loaded at a time, all
+// independent, and merged with a running log-sum-exp.
+template <int D>
+__global__ __launch_bounds__(D) void combine_kernel(const float* __restrict__ part, int nsplit,
+                                                    int G, int Hq, int Hkv, float* __restrict__ out) {
+  constexpr int K = 16;
+  const int row = blockIdx.x;
+  const int h = blockIdx.y;
+  const int dim = threadIdx.x;
+  const int PS = G * (D + 2);
+  const float* pr = part + (int64_t)row * nsplit * PS;
+  float M = -INFINITY, L = 0.0f, O = 0.0f;
+  for (int s0 = 0; s0 < nsplit; s0 += K) {
+    float ov[K], mv[K], lv[K];
+#pragma unroll
+    for (int u = 0; u < K; ++u) {
+      const bool ok = s0 + u < nsplit;
+      const float* ps = pr + (int64_t)(s0 + u) * PS;
+      ov[u] = ok ? ps[h * D + dim] : 0.0f;
+      mv[u] = ok ? ps[G * D + h] : -INFINITY;
+      lv[u] = ok ? ps[G * D + G + h] : 0.0f;
+    }
+    float mn = M;
+#pragma unroll
+    for (int u = 0; u < K; ++u) mn = fmaxf(mn, mv[u]);
+    if (mn == -INFINITY) continue;
+    const float alpha = exp2f(M - mn);
+    L *= alpha;
+    O *= alpha;
+#pragma unroll
+    for (int u = 0; u < K; ++u) {
+      const float w = exp2f(mv[u] - mn);
+      L = fmaf(lv[u], w, L);
+      O = fmaf(ov[u], w, O);
+    }
+    M = mn;
+  }
+  const int b = row / Hkv;
+  const int r = row % Hkv;
+  out[((int64_t)b * Hq + (int64_t)r * G + h) * D + dim] = O / L;
+}
+
+// ---------------------------------------------------------------------------
 template <typename KT, int D, int G>
 hipError_t dispatch_mode(int mode, dim3 grid, const AttendArgs& a, hipStream_t s) {
   switch (mode) {
@@ -277,6 +662,66 @@ hipError_t dispatch_group(int G, int mode, dim3 grid, const AttendArgs& a, hipSt
   }
 }
 
+template <int G, int WPW>
+hipError_t dispatch_wave_mode(int mode, dim3 grid, const AttendArgs& a, hipStream_t s) {
+  const dim3 block(64 * WPW);
+  switch (mode) {
+    case kIdxTokenPerHead:
+      hipLaunchKernelGGL((attend_wave_kernel<G, kIdxTokenPerHead, WPW>), grid, block, 0, s, a);
+      break;
+    case kIdxTokenShared:
+      hipLaunchKernelGGL((attend_wave_kernel<G, kIdxTokenShared, WPW>), grid, block, 0, s, a);
+      break;
+    case kIdxBlockPerHead:
+      hipLaunchKernelGGL((attend_wave_kernel<G, kIdxBlockPerHead, WPW>), grid, block, 0, s, a);
+      break;
+    default:
+      hipLaunchKernelGGL((attend_wave_kernel<G, kIdxDense, WPW>), grid, block, 0, s, a);
+      break;
+  }
+  return hipGetLastError();
+}
+
+template <int G, int TILES>
+hipError_t dispatch_sparse(int mode, dim3 grid, const AttendArgs& a, hipStream_t s) {
+  switch (mode) {
+    case kIdxTokenPerHead:
+      hipLaunchKernelGGL((attend_sparse_kernel<G, kIdxTokenPerHead, TILES>), grid, dim3(64), 0, s, a);
+      break;
+    case kIdxTokenShared:
+      hipLaunchKernelGGL((attend_sparse_kernel<G, kIdxTokenShared, TILES>), grid, dim3(64), 0, s, a);
+      break;
+    default:
+      hipLaunchKernelGGL((attend_sparse_kernel<G, kIdxBlockPerHead, TILES>), grid, dim3(64), 0, s, a);
+      break;
+  }
+  return hipGetLastError();
+}
+
+template <int G>
+hipError_t dispatch_wave(int wpw, int chunk, int mode, dim3 grid, const AttendArgs& a,
+                         hipStream_t s) {
+  if (wpw == 4) return dispatch_wave_mode<G, 4>(mode, grid, a, s);
+  if (chunk <= 16) return dispatch_sparse<G, 1>(mode, grid, a, s);
+  if (chunk <= 32) return dispatch_sparse<G, 2>(mode, grid, a, s);
+  return dispatch_sparse<G, 4>(mode, grid, a, s);
+}
+
+bool use_wave_kernel(const Cache& c) {
+  return c.kv_dtype == SA_BF16 && c.q_dtype == SA_BF16 && c.D == 128 && c.G <= 4;
+}
+
+// Slots per one-wave workgroup for selected-set decode (16, 32 or 64); the
+// SA_SPARSE_CHUNK environment variable overrides the default for tuning.
+int64_t sparse_chunk_default() {
+  static const int64_t v = [] {
+    const char* e = getenv("SA_SPARSE_CHUNK");
+    const int64_t x = e ? atoll(e) : 64;
+    return (x == 16 || x == 32 || x == 64) ? x : (int64_t)64;
+  }();
+  return v;
+}
+
 int lanes_per_row(const Cache& c) { return c.D * (c.kv_dtype == SA_BF16 ? 2 : 4) / 16; }
 
 }  // namespace
@@ -292,18 +737,32 @@ AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs) {
     p.n_slots = n_idx;
   }
   const int64_t rows = (int64_t)c.B * c.Hkv;
-  const int64_t unit = (int64_t)(kThreads / lanes_per_row(c)) * kUnroll;
-  int64_t chunk = (rows * p.n_slots + kTargetGroups - 1) / kTargetGroups;
-  chunk = (chunk + unit - 1) / unit * unit;
-  chunk = std::max<int64_t>(unit, std::min<int64_t>(chunk, 256 * unit));
-  // keep the number of splits per row bounded so the combine stays cheap
-  while ((p.n_slots + chunk - 1) / chunk > 4096) chunk *= 2;
+  int64_t chunk;
+  if (use_wave_kernel(c)) {
+    if (mode == kIdxDense) {
+      // four-wave workgroups over contiguous token ranges; about 2048
+      // workgroups in total, at most 1024 splits per row
+      p.waves = 4;
+      chunk = (rows * p.n_slots + 2047) / 2048;
+      chunk = std::max<int64_t>(256, (chunk + 63) / 64 * 64);
+      while ((p.n_slots + chunk - 1) / chunk > 1024) chunk *= 2;
+    } else {
+      // one-wave workgroups of 64 slots; shorter when that leaves the chip idle
+      p.waves = 1;
+      chunk = sparse_chunk_default();
+      while (chunk > 16 && rows * ((p.n_slots + chunk - 1) / chunk) < 1024) chunk /= 2;
+    }
+  } else {
+    p.waves = 4;
+    const int64_t unit = (int64_t)(kThreads / lanes_per_row(c)) * kUnroll;
+    chunk = (rows * p.n_slots + 4095) / 4096;
+    chunk = (chunk + unit - 1) / unit * unit;
+    chunk = std::max<int64_t>(unit, std::min<int64_t>(chunk, 256 * unit));
+    while ((p.n_slots + chunk - 1) / chunk > 1024) chunk *= 2;
+  }
   p.chunk = (int32_t)chunk;
   p.nsplit = (int32_t)((p.n_slots + chunk - 1) / chunk);
-  const size_t counters = align_up((size_t)rows * sizeof(uint32_t), 256);
-  const size_t part =
-      p.nsplit > 1 ? (size_t)rows * p.nsplit * c.G * (c.D + 2) * sizeof(float) : 0;
-  p.ws_bytes = counters + align_up(part, 256);
+  p.ws_bytes = p.nsplit > 1 ? (size_t)rows * p.nsplit * c.G * (c.D + 2) * sizeof(float) : 0;
   return p;
 }
 
@@ -329,17 +788,32 @@ hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, con
   a.chunk = p.chunk;
   a.nsplit = p.nsplit;
   a.out = out;
+  a.part = static_cast<float*>(ws);
   const int64_t rows = (int64_t)c.B * c.Hkv;
-  a.counters = static_cast<uint32_t*>(ws);
-  a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
-                                    align_up((size_t)rows * sizeof(uint32_t), 256));
   const dim3 grid(p.nsplit, (unsigned)rows);
-  if (c.kv_dtype == SA_BF16) {
-    if (c.D == 64) return dispatch_group<bf16_t, 64>(c.G, p.mode, grid, a, s);
-    return dispatch_group<bf16_t, 128>(c.G, p.mode, grid, a, s);
+  hipError_t e;
+  if (use_wave_kernel(c)) {
+    switch (c.G) {
+      case 1: e = dispatch_wave<1>(p.waves, p.chunk, p.mode, grid, a, s); break;
+      case 2: e = dispatch_wave<2>(p.waves, p.chunk, p.mode, grid, a, s); break;
+      default: e = dispatch_wave<4>(p.waves, p.chunk, p.mode, grid, a, s); break;
+    }
+  } else if (c.kv_dtype == SA_BF16) {
+    e = c.D == 64 ? dispatch_group<bf16_t, 64>(c.G, p.mode, grid, a, s)
+                  : dispatch_group<bf16_t, 128>(c.G, p.mode, grid, a, s);
+  } else {
+    e = c.D == 64 ? dispatch_group<float, 64>(c.G, p.mode, grid, a, s)
+                  : dispatch_group<float, 128>(c.G, p.mode, grid, a, s);
   }
-  if (c.D == 64) return dispatch_group<float, 64>(c.G, p.mode, grid, a, s);
-  return dispatch_group<float, 128>(c.G, p.mode, grid, a, s);
+  if (e != hipSuccess || p.nsplit == 1) return e;
+  const dim3 cgrid((unsigned)rows, (unsigned)c.G);
+  if (c.D == 64)
+    hipLaunchKernelGGL(combine_kernel<64>, cgrid, dim3(64), 0, s, a.part, p.nsplit, c.G, c.Hq, c.Hkv,
+                       out);
+  else
+    hipLaunchKernelGGL(combine_kernel<128>, cgrid, dim3(128), 0, s, a.part, p.nsplit, c.G, c.Hq,
+                       c.Hkv, out);
+  return hipGetLastError();
 }
 
 }  // namespace sa

@@ -41,7 +41,8 @@ struct AttendPlan {
   int64_t n_slots;  // selected slots per row (tokens, or block slots)
   int32_t chunk;    // slots per workgroup
   int32_t nsplit;   // workgroups per row
-  size_t ws_bytes;  // counters + partials
+  int32_t waves;    // waves per workgroup
+  size_t ws_bytes;  // split partials (0 when nsplit == 1)
 };
 
 AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs);
