@@ -257,16 +257,20 @@ __device__ __forceinline__ void load_tile(const AttendArgs& a, int row, int b, i
   T.okk = jbase + n < s1;
   int64_t tk = 0;
   if (T.okk) tk = resolve_slot<MODE>(a, row, b, jbase + n, T.okk);
+  // a dense scan reads every row once: streaming (nontemporal) loads
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-    T.kw[c] = T.okk ? ld16(kbase + tk * row_bytes + 64 * c) : make_uint4(0, 0, 0, 0);
+  for (int c = 0; c < 4; ++c) {
+    const uint8_t* p = kbase + tk * row_bytes + 64 * c;
+    T.kw[c] = !T.okk ? make_uint4(0, 0, 0, 0) : (MODE == kIdxDense ? ld16_nt(p) : ld16(p));
+  }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int64_t jv = jbase + 4 * u + rq;
     bool okv = jv < s1;
     int64_t tv = 0;
     if (okv) tv = resolve_slot<MODE>(a, row, b, jv, okv);
-    T.vw[u] = okv ? ld16(vbase + tv * row_bytes) : make_uint4(0, 0, 0, 0);
+    const uint8_t* p = vbase + tv * row_bytes;
+    T.vw[u] = !okv ? make_uint4(0, 0, 0, 0) : (MODE == kIdxDense ? ld16_nt(p) : ld16(p));
   }
 }
 

@@ -35,6 +35,14 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // 16-byte vector load (global_load_dwordx4).
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// 16-byte streaming load with the nontemporal hint: for data read once (a
+// scan of the whole cache), so it does not displace reusable cache lines.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Unpack one 16-byte chunk into floats (8 bf16 or 4 fp32 values).
 template <typename T>
 __device__ __forceinline__ void unpack16(const uint4& w, float* f);

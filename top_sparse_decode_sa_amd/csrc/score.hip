@@ -77,14 +77,21 @@ __global__ __launch_bounds__(kThreads) void score_exact_kernel(ExactArgs a) {
   const int64_t t_end = min(t_tile + (int64_t)a.tile, a.N);
   constexpr int per_wave_iter = RPW * U;
   constexpr int per_iter = 4 * per_wave_iter;
-  for (int64_t base = t_tile; base < t_end; base += per_iter) {
+  // Each wave covers per_wave_iter consecutive tokens per iteration; the next
+  // iteration's keys are in flight while this one reduces.
+  auto load = [&](int64_t base, uint4 (&kw)[U]) {
     const int64_t wbase = base + wave * per_wave_iter;
-    uint4 kw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t t = wbase + u * RPW + lg;
-      kw[u] = (t < t_end) ? ld16(kbase + t * row_bytes) : make_uint4(0, 0, 0, 0);
+      kw[u] = (t < t_end) ? ld16_nt(kbase + t * row_bytes) : make_uint4(0, 0, 0, 0);
     }
+  };
+  uint4 kw[U], kn[U];
+  load(t_tile, kw);
+  for (int64_t base = t_tile; base < t_end; base += per_iter) {
+    const bool more = base + per_iter < t_end;
+    if (more) load(base + per_iter, kn);
     float mine = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -96,8 +103,12 @@ __global__ __launch_bounds__(kThreads) void score_exact_kernel(ExactArgs a) {
       acc = group_sum<LPR>(acc);
       if (sl == u) mine = acc;
     }
-    const int64_t t = wbase + sl * RPW + lg;
+    const int64_t t = base + wave * per_wave_iter + sl * RPW + lg;
     if (sl < U && t < t_end) srow[t] = mine;
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) kw[u] = kn[u];
+    }
   }
 }
 
@@ -155,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void block_summarize_kernel(SumArgs a) {
   }
   for (int64_t t = t0 + grp; t < t1; t += NG) {
     float kf[E];
-    unpack16<KT>(ld16(kbase + t * row_bytes), kf);
+    unpack16<KT>(ld16_nt(kbase + t * row_bytes), kf);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       mn[e] = fminf(mn[e], kf[e]);
@@ -289,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void score_indexer_kernel(IndexerArgs a) 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t t = wbase + u * RPW + lg;
-      kw[u] = (t < t_end) ? ld16(kbase + t * (DI * 2)) : make_uint4(0, 0, 0, 0);
+      kw[u] = (t < t_end) ? ld16_nt(kbase + t * (DI * 2)) : make_uint4(0, 0, 0, 0);
     }
     float mine = 0.0f;
 #pragma unroll
@@ -350,12 +361,12 @@ hipError_t launch_score_exact(const Cache& c, const void* q, const void* k, floa
     if (c.D == 64)
       hipLaunchKernelGGL((score_exact_kernel<bf16_t, 64, 8>), grid, dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((score_exact_kernel<bf16_t, 128, 8>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((score_exact_kernel<bf16_t, 128, 16>), grid, dim3(kThreads), 0, s, a);
   } else {
     if (c.D == 64)
-      hipLaunchKernelGGL((score_exact_kernel<float, 64, 8>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((score_exact_kernel<float, 64, 16>), grid, dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((score_exact_kernel<float, 128, 8>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((score_exact_kernel<float, 128, 16>), grid, dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }
