@@ -52,8 +52,71 @@ def parse():
                    help="bound on the oracle's CPU time for cpu_baseline (0 disables)")
     p.add_argument("--dense-steps", type=int, default=20)
     p.add_argument("--profile", action="store_true",
-                   help="short run for a profiler: few steps, no dense, no cpu baseline")
+                   help="short run for a profiler: few steps, no dense, no cpu baseline, plus "
+                        "three 1 GiB device-to-device copies that calibrate HBM byte counters")
+    p.add_argument("--summarize", metavar="DB",
+                   help="print a per-kernel summary of a rocprofv3 results database and exit")
     return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 results -> text summary; HBM traffic from the byte counters
+# ---------------------------------------------------------------------------
+
+COPY_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_exact_llama32k_traffic.txt")
+TRAFFIC_SOURCES = ["top_sparse_decode_sa_amd/csrc/score.hip", "top_sparse_decode_sa_amd/csrc/common.hpp"]
+
+
+def source_hash(paths=TRAFFIC_SOURCES):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def summarize(db_path):
+    """Per-kernel dispatch count and duration stats; with counter data, the
+    per-dispatch mean of each counter."""
+    import sqlite3
+    db = sqlite3.connect(db_path)
+    rows = db.execute("select name, count(*), avg(end-start), min(end-start), max(end-start) "
+                      "from kernels group by name order by sum(end-start) desc").fetchall()
+    lines = ["%-70s %6s %10s %10s %10s" % ("kernel", "calls", "avg_us", "min_us", "max_us")]
+    for name, n, avg, mn, mx in rows:
+        lines.append("%-70s %6d %10.2f %10.2f %10.2f" % (name[:70], n, avg / 1e3, mn / 1e3, mx / 1e3))
+    try:
+        pmc = db.execute("select k.name, p.counter_name, avg(p.value), count(*) from kernels k "
+                         "join pmc_events p on p.event_id = k.event_id "
+                         "group by k.name, p.counter_name").fetchall()
+    except Exception:
+        pmc = []
+    counters = {}
+    if pmc:
+        lines.append("")
+        lines.append("%-70s %-14s %16s %6s" % ("kernel", "counter", "mean/dispatch", "n"))
+        for name, cname, val, n in pmc:
+            lines.append("%-70s %-14s %16.1f %6d" % (name[:70], cname, val, n))
+            counters[(name, cname)] = val
+    return "\n".join(lines), rows, counters
+
+
+def read_traffic():
+    """Measured HBM bytes per score_exact launch, if measured on this source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            a, b = line.split(":", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("source_sha256_16") != source_hash():
+        return None  # the kernel changed since the counters were taken
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def step_bytes(cfg):
@@ -103,6 +166,9 @@ def cpu_baseline(w, q_host, k_host, v_host, seconds):
 
 def main():
     args = parse()
+    if args.summarize:
+        print(summarize(args.summarize)[0])
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
@@ -169,6 +235,16 @@ def main():
     ms_attend = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
     ms_step = wall * 1e3 / args.steps
 
+    if args.profile:
+        # plain device-to-device copies of known size: the byte counters of
+        # these launches calibrate the counters of the kernels above
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     # dense decode over the same cache (comparison for the sparse/dense ratio)
     ms_dense = None
     if args.dense_steps > 0:
@@ -201,7 +277,8 @@ def main():
     # dominant kernel of the step: the one with the largest share of its time
     dom = max(["score_exact", "topk", "sparse_attend"], key=lambda n: kernels[n]["us"])
     roof = {"bound": "hbm", "achieved": kernels[dom]["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": kernels[dom]["frac"], "traffic": None, "kernel": dom,
+            "frac": kernels[dom]["frac"],
+            "traffic": read_traffic() if dom == "score_exact" else None, "kernel": dom,
             "bytes_per_launch": nbytes[dom]}
 
     cpu = None
