@@ -36,6 +36,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <initializer_list>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -239,6 +240,8 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
 // bf16, head_dim 128, G <= 4: MFMA logits, one wave per 16-token tile.
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float wave_bcast0(float x) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
@@ -362,63 +365,110 @@ __device__ __forceinline__ void load_q_frag(const AttendArgs& a, int b, int r, i
   }
 }
 
-// Selected-set decode, up to 16 * TILES slots per one-wave workgroup.  The
-// memory operations are ordered for the in-order load counter: first one index
-// load per lane per tile (lane l reads the token of slot l % 16), then every
-// key and value load of every tile (value-row token ids come from the owning
-// lane by a shuffle, not from memory), then the compute.
+// Slot j of a row (s0 <= j < s1) -> token position, for a slot that may lie
+// past the selection: the load is always made at an in-range position (the
+// last slot, the last token) and `ok` reports whether the slot is real.  No
+// load sits under a branch, so the wave's loads stay in flight together.
+template <int MODE>
+__device__ __forceinline__ int32_t slot_token(const AttendArgs& a, int row, int b, int64_t j,
+                                              int64_t s1, bool& ok) {
+  ok = j < s1;
+  const int64_t jj = ok ? j : s1 - 1;
+  if constexpr (MODE == kIdxTokenPerHead) {
+    return a.idx[(int64_t)row * a.n_idx + jj];
+  } else if constexpr (MODE == kIdxTokenShared) {
+    return a.idx[(int64_t)b * a.n_idx + jj];
+  } else {
+    const int64_t t = (int64_t)a.idx[(int64_t)row * a.n_idx + jj / a.bs] * a.bs + jj % a.bs;
+    ok = ok && t < a.N;
+    return (int32_t)(t < a.N ? t : a.N - 1);
+  }
+}
+
+// Selected-set decode: 1 to kMaxSparseWaves waves per workgroup (the block
+// size says how many), up to 16 * TILES slots per wave.  The memory operations are ordered for the in-order load counter: one
+// index load per lane per tile (lane l reads the token of slot l % 16), then
+// every key row piece of every tile, then every value row piece (value-row
+// token ids come from the owning lane by a shuffle), then the compute.  Both
+// Q.K and P.V run on MFMA; the softmax is computed in two passes over the
+// wave's tokens (one max, one sum per head), so no running rescale is needed.
+// Several waves merge their (o, max, sum) in LDS and write one result.
+constexpr int kMaxSparseWaves = 12;
+
 template <int G, int MODE, int TILES>
-__global__ __launch_bounds__(64) void attend_sparse_kernel(AttendArgs a) {
+__global__ __launch_bounds__(64 * kMaxSparseWaves) void attend_sparse_kernel(AttendArgs a) {
   static_assert(G >= 1 && G <= 4, "query heads of a group fit MFMA rows 0..3");
   constexpr int D = 128;
-  __shared__ float s_p[TILES][16][4];
-  const int lane = threadIdx.x;
+  constexpr int W = kMaxSparseWaves;
+  // p of slot 16i + 4u + g for head h at s_pa[wave][h][i][g][u]: the MFMA
+  // A-fragment order of the P.V product
+  __shared__ __align__(16) float s_pa[W][G][TILES][4][4];
+  __shared__ __align__(16) float s_o[W][G][D];
+  __shared__ float s_ml[W][2][G];
+  const int nw = blockDim.x >> 6;  // waves in this workgroup
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int n = lane & 15;
   const int rq = lane >> 4;
   const int row = blockIdx.y;
   const int split = blockIdx.x;
   const int b = row / a.Hkv;
   const int r = row % a.Hkv;
-  const int64_t s0 = (int64_t)split * a.chunk;
-  const int64_t s1 = min(s0 + (int64_t)a.chunk, a.n_slots);
+  // this wave's slots: [s0, s1) of the workgroup's chunk, 16 * TILES per wave
+  const int64_t wg0 = (int64_t)split * a.chunk;
+  const int64_t wg1 = min(wg0 + (int64_t)a.chunk, a.n_slots);
+  const int64_t s0 = wg0 + (int64_t)wave * 16 * TILES;
+  const int64_t s1 = min(s0 + 16 * TILES, wg1);
+  const bool idle = s0 >= wg1;  // wave-uniform: nothing left for this wave
 
-  // 1. token of slot 16i + n for every tile i (-1: no token)
+  // 1. token of slot 16i + n of every tile
   int32_t tok[TILES];
+  bool ok[TILES];
+  // an idle wave reads the workgroup's first slot (always valid) and masks it:
+  // no branch around the loads
+  const int64_t r0 = idle ? wg0 : s0;
+  const int64_t r1 = idle ? wg0 + 1 : s1;
 #pragma unroll
   for (int i = 0; i < TILES; ++i) {
-    const int64_t j = s0 + 16 * i + n;
-    bool ok = j < s1;
-    int64_t t = 0;
-    if (ok) t = resolve_slot<MODE>(a, row, b, j, ok);
-    tok[i] = ok ? (int32_t)t : -1;
+    tok[i] = slot_token<MODE>(a, row, b, r0 + 16 * i + n, r1, ok[i]);
+    ok[i] = ok[i] && !idle;
   }
-  bf16x8_t qa[4];
-  load_q_frag<G>(a, b, r, n, rq, qa);
 
-  // 2. all key and value loads
+  // q of head n (lanes n >= G carry zeros): MFMA A fragments, dims [32c + 8rq, +8)
+  bf16x8_t qa[4];
+  {
+    const uint8_t* qb = static_cast<const uint8_t*>(a.q) +
+                        (((int64_t)b * a.Hq + (int64_t)r * G + (n < G ? n : 0)) * D + 8 * rq) * 2;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint4 w = ld16(qb + 64 * c);
+      if (n >= G) w = make_uint4(0, 0, 0, 0);
+      __builtin_memcpy(&qa[c], &w, 16);
+    }
+  }
+
+  // 2. key pieces of every tile, then value rows (token 4u + rq of each tile)
   const int64_t kv_off = ((int64_t)b * a.sb + (int64_t)r * a.sh) * 2;
   const uint8_t* kbase = a.k + kv_off + 16 * rq;
   const uint8_t* vbase = a.v + kv_off + 16 * n;
   const int64_t row_bytes = a.st * 2;
-  // keys of every tile first, then values: the logits and the softmax can
-  // proceed while the value rows are still arriving
-  TileLoads T[TILES];
+  uint4 kw[TILES][4], vw[TILES][4];
 #pragma unroll
-  for (int i = 0; i < TILES; ++i) {
-    T[i].okk = tok[i] >= 0;
+  for (int i = 0; i < TILES; ++i)
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      T[i].kw[c] = T[i].okk ? ld16(kbase + (int64_t)tok[i] * row_bytes + 64 * c)
-                            : make_uint4(0, 0, 0, 0);
-  }
+    for (int c = 0; c < 4; ++c) kw[i][c] = ld16(kbase + (int64_t)tok[i] * row_bytes + 64 * c);
+  int32_t tv[TILES][4];
 #pragma unroll
-  for (int i = 0; i < TILES; ++i) {
+  for (int i = 0; i < TILES; ++i)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int32_t tv = __shfl(tok[i], 4 * u + rq);
-      T[i].vw[u] = tv >= 0 ? ld16(vbase + (int64_t)tv * row_bytes) : make_uint4(0, 0, 0, 0);
-    }
-  }
+    for (int u = 0; u < 4; ++u) tv[i][u] = __shfl(tok[i], 4 * u + rq);
+#pragma unroll
+  for (int i = 0; i < TILES; ++i)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) vw[i][u] = ld16(vbase + (int64_t)tv[i][u] * row_bytes);
+  // keep every load above this point: all rows of the wave are requested
+  // before the first logit is computed
+  __builtin_amdgcn_sched_barrier(0);
 
   // 3. logits of every tile: rows 0..G-1 of the MFMA results, in lanes 0..15
   float lg[TILES][G];
@@ -428,14 +478,14 @@ __global__ __launch_bounds__(64) void attend_sparse_kernel(AttendArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       bf16x8_t kb;
-      __builtin_memcpy(&kb, &T[i].kw[c], 16);
+      __builtin_memcpy(&kb, &kw[i][c], 16);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[c], kb, acc, 0, 0, 0);
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h) lg[i][h] = (rq == 0 && T[i].okk) ? acc[h] * a.qscale : -INFINITY;
+    for (int h = 0; h < G; ++h) lg[i][h] = (rq == 0 && ok[i]) ? acc[h] * a.qscale : -INFINITY;
   }
   // 4. one max per head over the wave's tokens (valid in lanes 0..15), then
-  //    p = 2^(logit - max) and its sum -- no running rescale is needed
+  //    p = 2^(logit - max) and its sum
   float M[G], Lsum[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -455,44 +505,156 @@ __global__ __launch_bounds__(64) void attend_sparse_kernel(AttendArgs a) {
     }
     Lsum[h] = group_sum<16>(ls);
   }
-  // 5. p to the value layout through LDS (one wave: in-order LDS access)
+  // 5. O = P.V on MFMA.  K-step t covers tiles 2t and 2t+1; its k index
+  //    8g + j stands for slot 16(2t + j/4) + 4(j%4) + g.  B fragment of lane
+  //    (n, g): value dim 8n + e of those 8 slots, which this lane loaded as
+  //    vw[2t + j/4][j%4] (MFMA e takes the dims 8n + e, n = 0..15).  A
+  //    fragment: P enters as two bf16 parts, p = hi + lo to 2^-16 relative
+  //    (hi: p truncated to bf16; lo: the rest, rounded), so the product keeps
+  //    fp32 accuracy: row 4h carries head h's hi part, row 4h + 1 its lo part.
+  //    Lane (n, h) ends with O[h][8n + e] = acc[e][0] + acc[e][1].
   if (rq == 0) {
 #pragma unroll
     for (int i = 0; i < TILES; ++i)
 #pragma unroll
-      for (int h = 0; h < G; ++h) s_p[i][n][h] = lg[i][h];
+      for (int h = 0; h < G; ++h) s_pa[wave][h][i][n & 3][n >> 2] = lg[i][h];
   }
   __builtin_amdgcn_wave_barrier();
-  float o[G][8];
+  const int ha = n >> 2;
+  const bool arow = (n & 3) < 2 && ha < G;
+  const bool lo_row = (n & 1) != 0;
+  const int hc = ha < G ? ha : G - 1;
+  f32x4_t acc[8];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int e = 0; e < 8; ++e) acc[e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[h][e] = 0.0f;
+  for (int t = 0; t < (TILES + 1) / 2; ++t) {
+    float pj[8];
 #pragma unroll
-  for (int i = 0; i < TILES; ++i)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float pv[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) pv[h] = s_p[i][4 * u + rq][h];
-      float vf[8];
-      unpack16<bf16_t>(T[i].vw[u], vf);
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] = fmaf(pv[h], vf[e], o[h][e]);
+    for (int half = 0; half < 2; ++half) {
+      const int i = 2 * t + half;
+      float4 q4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (i < TILES) q4 = *reinterpret_cast<const float4*>(&s_pa[wave][hc][i < TILES ? i : 0][rq][0]);
+      pj[4 * half + 0] = arow ? q4.x : 0.0f;
+      pj[4 * half + 1] = arow ? q4.y : 0.0f;
+      pj[4 * half + 2] = arow ? q4.z : 0.0f;
+      pj[4 * half + 3] = arow ? q4.w : 0.0f;
     }
+    uint32_t af[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t b0 = __float_as_uint(pj[2 * d]);
+      const uint32_t b1 = __float_as_uint(pj[2 * d + 1]);
+      const uint32_t hi = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // truncated bf16 pair
+      f32x2_t rest = {pj[2 * d] - __uint_as_float(b0 & 0xffff0000u),
+                      pj[2 * d + 1] - __uint_as_float(b1 & 0xffff0000u)};
+      bf16x2_t lo2 = __builtin_convertvector(rest, bf16x2_t);
+      uint32_t lo;
+      __builtin_memcpy(&lo, &lo2, 4);
+      af[d] = lo_row ? lo : hi;
+    }
+    bf16x8_t a_p;
+    __builtin_memcpy(&a_p, af, 16);
+  const uint4 z = make_uint4(0, 0, 0, 0);
+    const uint4 v0 = vw[2 * t][0], v1 = vw[2 * t][1], v2 = vw[2 * t][2], v3 = vw[2 * t][3];
+    const uint4 v4 = 2 * t + 1 < TILES ? vw[2 * t + 1 < TILES ? 2 * t + 1 : 0][0] : z;
+    const uint4 v5 = 2 * t + 1 < TILES ? vw[2 * t + 1 < TILES ? 2 * t + 1 : 0][1] : z;
+    const uint4 v6 = 2 * t + 1 < TILES ? vw[2 * t + 1 < TILES ? 2 * t + 1 : 0][2] : z;
+    const uint4 v7 = 2 * t + 1 < TILES ? vw[2 * t + 1 < TILES ? 2 * t + 1 : 0][3] : z;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // word e/2 of each row holds dims 8n + 2(e/2) (low half) and +1 (high)
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      auto word = [&](const uint4& x) -> uint32_t {
+        return (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
+      };
+      uint32_t bw[4];
+      bw[0] = __builtin_amdgcn_perm(word(v1), word(v0), sel);
+      bw[1] = __builtin_amdgcn_perm(word(v3), word(v2), sel);
+      bw[2] = __builtin_amdgcn_perm(word(v5), word(v4), sel);
+      bw[3] = __builtin_amdgcn_perm(word(v7), word(v6), sel);
+      bf16x8_t bv;
+      __builtin_memcpy(&bv, bw, 16);
+      acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_p, bv, acc[e], 0, 0, 0);
+    }
+  }
 
-  // 6. lanes 0..15 hold M, Lsum and, after the row reduction, o
-  reduce_rows<G>(o);
-  if (rq == 0) {
+  // M and Lsum hold the row-0 reductions (valid in lanes 0..15): broadcast
+  // them from lane 0, then every row keeps its own head
+  float mine[8];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+  for (int e = 0; e < 8; ++e) mine[e] = acc[e][0] + acc[e][1];
+  float m_me = wave_bcast0(M[0]), l_me = wave_bcast0(Lsum[0]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        write_result<G, D>(a, row, split, b, r, h, 8 * n + e, o[h][e], M[h], Lsum[h]);
+  for (int h = 1; h < G; ++h) {
+    const float mh = wave_bcast0(M[h]);
+    const float lh = wave_bcast0(Lsum[h]);
+    if (rq == h) {
+      m_me = mh;
+      l_me = lh;
+    }
+  }
+  if (nw > 1) {
+    // merge the workgroup's waves in LDS (log-sum-exp); thread t of the
+    // workgroup then owns output (head t / D, dim t % D)
+    if (rq < G) {
+      float* so = &s_o[wave][rq][8 * n];
+      *reinterpret_cast<float4*>(so) = make_float4(mine[0], mine[1], mine[2], mine[3]);
+      *reinterpret_cast<float4*>(so + 4) = make_float4(mine[4], mine[5], mine[6], mine[7]);
+      if (n == 0) {
+        s_ml[wave][0][rq] = m_me;
+        s_ml[wave][1][rq] = l_me;
+      }
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < G * D; t += 64 * nw) {
+      const int h = t / D;
+      const int dim = t % D;
+      float Mx = -INFINITY;
+      for (int w = 0; w < nw; ++w) Mx = fmaxf(Mx, s_ml[w][0][h]);
+      float Lx = 0.0f, Ox = 0.0f;
+      if (Mx != -INFINITY) {
+        for (int w = 0; w < nw; ++w) {
+          const float wt = __builtin_amdgcn_exp2f(s_ml[w][0][h] - Mx);
+          Lx = fmaf(s_ml[w][1][h], wt, Lx);
+          Ox = fmaf(s_o[w][h][dim], wt, Ox);
+        }
+      }
+      if (a.nsplit == 1) {
+        a.out[((int64_t)b * a.Hq + (int64_t)r * G + h) * D + dim] = Ox / Lx;
+      } else {
+        float* p = a.part + ((int64_t)row * a.nsplit + split) * (G * (D + 2));
+        p[h * D + dim] = Ox;
+        if (dim == 0) {
+          p[G * D + h] = Mx;
+          p[G * D + G + h] = Lx;
+        }
+      }
+    }
+    return;
+  }
+  if (rq < G) {
+    if (a.nsplit == 1) {
+      float* dst = a.out + ((int64_t)b * a.Hq + (int64_t)r * G + rq) * D + 8 * n;
+      const float inv = 1.0f / l_me;
+      *reinterpret_cast<float4*>(dst) =
+          make_float4(mine[0] * inv, mine[1] * inv, mine[2] * inv, mine[3] * inv);
+      *reinterpret_cast<float4*>(dst + 4) =
+          make_float4(mine[4] * inv, mine[5] * inv, mine[6] * inv, mine[7] * inv);
+    } else {
+      // partial layout per head: [half][n][4] -> dims 8n + 4*half + j
+      float* p = a.part + ((int64_t)row * a.nsplit + split) * (G * (D + 2));
+      float* ph = p + rq * D + 4 * n;
+      *reinterpret_cast<float4*>(ph) = make_float4(mine[0], mine[1], mine[2], mine[3]);
+      *reinterpret_cast<float4*>(ph + 64) = make_float4(mine[4], mine[5], mine[6], mine[7]);
+      if (n == 0) {
+        p[G * D + rq] = m_me;
+        p[G * D + G + rq] = l_me;
+      }
+    }
   }
 }
+
 
 template <int G, int MODE, int WPW>
 __global__ __launch_bounds__(64 * WPW) void attend_wave_kernel(AttendArgs a) {
@@ -598,13 +760,17 @@ __global__ __launch_bounds__(64 * WPW) void attend_wave_kernel(AttendArgs a) {
 // independent, and merged with a running log-sum-exp.
 template <int D>
 __global__ __launch_bounds__(D) void combine_kernel(const float* __restrict__ part, int nsplit,
-                                                    int G, int Hq, int Hkv, float* __restrict__ out) {
+                                                    int G, int Hq, int Hkv, float* __restrict__ out,
+                                                    bool vec_layout) {
   constexpr int K = 16;
   const int row = blockIdx.x;
   const int h = blockIdx.y;
   const int dim = threadIdx.x;
   const int PS = G * (D + 2);
   const float* pr = part + (int64_t)row * nsplit * PS;
+  // where dim lives inside a partial's head block: dim itself, or (sparse
+  // one-wave kernel) [half][n][4] with dim = 8n + 4 half + j
+  const int pos = vec_layout ? ((dim & 7) >> 2) * 64 + (dim >> 3) * 4 + (dim & 3) : dim;
   float M = -INFINITY, L = 0.0f, O = 0.0f;
   for (int s0 = 0; s0 < nsplit; s0 += K) {
     float ov[K], mv[K], lv[K];
@@ -612,7 +778,7 @@ __global__ __launch_bounds__(D) void combine_kernel(const float* __restrict__ pa
     for (int u = 0; u < K; ++u) {
       const bool ok = s0 + u < nsplit;
       const float* ps = pr + (int64_t)(s0 + u) * PS;
-      ov[u] = ok ? ps[h * D + dim] : 0.0f;
+      ov[u] = ok ? ps[h * D + pos] : 0.0f;
       mv[u] = ok ? ps[G * D + h] : -INFINITY;
       lv[u] = ok ? ps[G * D + G + h] : 0.0f;
     }
@@ -687,42 +853,58 @@ hipError_t dispatch_wave_mode(int mode, dim3 grid, const AttendArgs& a, hipStrea
 }
 
 template <int G, int TILES>
-hipError_t dispatch_sparse(int mode, dim3 grid, const AttendArgs& a, hipStream_t s) {
+hipError_t dispatch_sparse(int waves, int mode, dim3 grid, const AttendArgs& a, hipStream_t s) {
+  const dim3 block(64 * waves);
   switch (mode) {
     case kIdxTokenPerHead:
-      hipLaunchKernelGGL((attend_sparse_kernel<G, kIdxTokenPerHead, TILES>), grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL((attend_sparse_kernel<G, kIdxTokenPerHead, TILES>), grid, block, 0, s, a);
       break;
     case kIdxTokenShared:
-      hipLaunchKernelGGL((attend_sparse_kernel<G, kIdxTokenShared, TILES>), grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL((attend_sparse_kernel<G, kIdxTokenShared, TILES>), grid, block, 0, s, a);
       break;
     default:
-      hipLaunchKernelGGL((attend_sparse_kernel<G, kIdxBlockPerHead, TILES>), grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL((attend_sparse_kernel<G, kIdxBlockPerHead, TILES>), grid, block, 0, s, a);
       break;
   }
   return hipGetLastError();
 }
 
+// Dense decode takes the four-wave streaming kernel; selected sets take the
+// gather kernel with `waves` waves of chunk / waves slots each.
 template <int G>
-hipError_t dispatch_wave(int wpw, int chunk, int mode, dim3 grid, const AttendArgs& a,
+hipError_t dispatch_wave(int waves, int chunk, int mode, dim3 grid, const AttendArgs& a,
                          hipStream_t s) {
-  if (wpw == 4) return dispatch_wave_mode<G, 4>(mode, grid, a, s);
-  if (chunk <= 16) return dispatch_sparse<G, 1>(mode, grid, a, s);
-  if (chunk <= 32) return dispatch_sparse<G, 2>(mode, grid, a, s);
-  return dispatch_sparse<G, 4>(mode, grid, a, s);
+  if (mode == kIdxDense) return dispatch_wave_mode<G, 4>(mode, grid, a, s);
+  const int per_wave = chunk / waves;
+  if (per_wave <= 16) return dispatch_sparse<G, 1>(waves, mode, grid, a, s);
+  if (per_wave <= 32) return dispatch_sparse<G, 2>(waves, mode, grid, a, s);
+  if (per_wave <= 48) return dispatch_sparse<G, 3>(waves, mode, grid, a, s);
+  return dispatch_sparse<G, 4>(waves, mode, grid, a, s);
 }
 
 bool use_wave_kernel(const Cache& c) {
   return c.kv_dtype == SA_BF16 && c.q_dtype == SA_BF16 && c.D == 128 && c.G <= 4;
 }
 
-// Slots per one-wave workgroup for selected-set decode (16, 32 or 64); the
-// SA_SPARSE_CHUNK environment variable overrides the default for tuning.
-int64_t sparse_chunk_default() {
-  static const int64_t v = [] {
-    const char* e = getenv("SA_SPARSE_CHUNK");
-    const int64_t x = e ? atoll(e) : 64;
-    return (x == 16 || x == 32 || x == 64) ? x : (int64_t)64;
-  }();
+// Tuning overrides for selected-set decode: SA_SPARSE_CHUNK fixes the slots
+// per wave (16, 32, 48 or 64), SA_SPARSE_WAVES the waves per workgroup (1 to
+// 12); 0 (unset) leaves the choice to plan_attend.
+int env_choice(const char* name, std::initializer_list<int> allowed) {
+  const char* e = getenv(name);
+  if (!e) return 0;
+  const int x = atoi(e);
+  for (int v : allowed)
+    if (v == x) return x;
+  return 0;
+}
+
+int sparse_chunk_override() {
+  static const int v = env_choice("SA_SPARSE_CHUNK", {16, 32, 48, 64});
+  return v;
+}
+
+int sparse_waves_override() {
+  static const int v = env_choice("SA_SPARSE_WAVES", {1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12});
   return v;
 }
 
@@ -751,10 +933,42 @@ AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs) {
       chunk = std::max<int64_t>(256, (chunk + 63) / 64 * 64);
       while ((p.n_slots + chunk - 1) / chunk > 1024) chunk *= 2;
     } else {
-      // one-wave workgroups of 64 slots; shorter when that leaves the chip idle
-      p.waves = 1;
-      chunk = sparse_chunk_default();
-      while (chunk > 16 && rows * ((p.n_slots + chunk - 1) / chunk) < 1024) chunk /= 2;
+      // Each wave gathers up to 64 slots with every load in flight at once;
+      // the waves of a workgroup merge in LDS.  With at least 128 rows (half
+      // the chip's CUs at one workgroup each) and at most 12 waves' worth of
+      // slots, one workgroup takes a whole row: no split partials and no
+      // combine launch (on 128 rows of 655 slots, 14.6 us against 14.2 us +
+      // 4.5 us for one-wave splits and their combine).  Otherwise rows are
+      // split so that about 512 workgroups (two per CU) run, and a combine
+      // pass merges the splits.
+      const int64_t wn = (p.n_slots + 63) / 64;
+      int waves = 1;
+      int64_t per_wave = 64;
+      if (rows >= 128 && wn <= kMaxSparseWaves) {
+        // the fewest slots per wave (32, 48 or 64) that still fit: more,
+        // shorter waves finish sooner (measured on 1024 rows of 262 slots:
+        // 9 x 32 beats 5 x 64 by 10 %)
+        for (int pw : {32, 48, 64}) {
+          if ((p.n_slots + pw - 1) / pw <= kMaxSparseWaves) {
+            per_wave = pw;
+            break;
+          }
+        }
+        waves = (int)((p.n_slots + per_wave - 1) / per_wave);
+      } else {
+        for (int w : {12, 8, 4}) {
+          if (rows * ((wn + w - 1) / w) >= 512) {
+            waves = w;
+            break;
+          }
+        }
+        if (waves == 1)
+          while (per_wave > 16 && rows * ((p.n_slots + per_wave - 1) / per_wave) < 512) per_wave /= 2;
+      }
+      if (sparse_waves_override()) waves = sparse_waves_override();
+      if (sparse_chunk_override()) per_wave = sparse_chunk_override();
+      p.waves = waves;
+      chunk = per_wave * waves;
     }
   } else {
     p.waves = 4;
@@ -811,12 +1025,14 @@ hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, con
   }
   if (e != hipSuccess || p.nsplit == 1) return e;
   const dim3 cgrid((unsigned)rows, (unsigned)c.G);
+  // one-wave selected-set workgroups write the interleaved partial layout
+  const bool vec_layout = use_wave_kernel(c) && p.mode != kIdxDense && p.waves == 1;
   if (c.D == 64)
     hipLaunchKernelGGL(combine_kernel<64>, cgrid, dim3(64), 0, s, a.part, p.nsplit, c.G, c.Hq, c.Hkv,
-                       out);
+                       out, vec_layout);
   else
     hipLaunchKernelGGL(combine_kernel<128>, cgrid, dim3(128), 0, s, a.part, p.nsplit, c.G, c.Hq,
-                       c.Hkv, out);
+                       c.Hkv, out, vec_layout);
   return hipGetLastError();
 }
 
