@@ -50,6 +50,26 @@ def test_topk_bit_exact(n):
             assert np.array_equal(got[r], want), (n, k, r)
 
 
+@pytest.mark.parametrize("rows,n,k", [(3, 40000, 1), (3, 200003, 2048), (2, 200003, 8192),
+                                       (2, 100000, 9000), (1, 1048576, 2048)])
+def test_topk_long_rows(rows, n, k):
+    """Rows longer than the LDS-resident limit: few rows take the
+    multi-workgroup path (k <= 8192), larger k the row path; tied rows whose
+    candidate bin overflows exercise the in-kernel fallback."""
+    say("topk long rows=%d n=%d k=%d" % (rows, n, k))
+    rng = np.random.default_rng(n + k)
+    vals = rng.standard_normal((rows, n)).astype(np.float32)
+    if rows > 1:
+        vals[1] = np.round(vals[1] * 2) / 2      # heavy ties: bin overflow
+    if rows > 2:
+        vals[2, ::7] = 5.0                       # ties above everything else
+    x = torch.from_numpy(vals).to(dev())
+    got = T.sa_topk(x, k).cpu().numpy()
+    for r in range(rows):
+        want = O.topk(vals[r].astype(np.float64), k)
+        assert np.array_equal(got[r], want), (rows, n, k, r)
+
+
 def test_topk_row_stride():
     say("topk row_stride")
     base = RNG.standard_normal((6, 3000)).astype(np.float32)

@@ -123,11 +123,14 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
   const int r = row % a.Hkv;
 
   float qv[G][E];
+  {
+    float q8[8][E];
+    load_q_group<E, D>(a.q, a.q_dtype, (int64_t)b * a.Hq + (int64_t)r * G, G, sl * E, q8);
 #pragma unroll
-  for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      qv[g][e] = load_q(a.q, a.q_dtype, ((int64_t)b * a.Hq + r * G + g) * D + sl * E + e) * a.qscale;
+      for (int e = 0; e < E; ++e) qv[g][e] = q8[g][e] * a.qscale;
+  }
 
   const int64_t kv_off = ((int64_t)b * a.sb + (int64_t)r * a.sh) * EB + sl * 16;
   const uint8_t* kbase = a.k + kv_off;

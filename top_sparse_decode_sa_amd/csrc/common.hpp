@@ -68,6 +68,58 @@ __device__ __forceinline__ float load_q(const void* q, sa_dtype dt, int64_t i) {
   return reinterpret_cast<const float*>(q)[i];
 }
 
+// E (4 or 8) consecutive q values from element i with vector loads; the
+// element offset i is a multiple of E and q is 16-byte aligned.
+template <int E, bool BF16>
+__device__ __forceinline__ void load_q_vec(const void* q, int64_t i, float (&v)[E]) {
+  static_assert(E == 4 || E == 8, "E is 4 or 8");
+  if constexpr (BF16) {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(q) + i;
+    uint32_t w[E / 2];
+    if constexpr (E == 8) {
+      const uint4 x = *reinterpret_cast<const uint4*>(p);
+      w[0] = x.x;
+      w[1] = x.y;
+      w[2] = x.z;
+      w[3] = x.w;
+    } else {
+      const uint2 x = *reinterpret_cast<const uint2*>(p);
+      w[0] = x.x;
+      w[1] = x.y;
+    }
+#pragma unroll
+    for (int j = 0; j < E / 2; ++j) {
+      v[2 * j] = bf16_lo(w[j]);
+      v[2 * j + 1] = bf16_hi(w[j]);
+    }
+  } else {
+    const float* p = reinterpret_cast<const float*>(q) + i;
+#pragma unroll
+    for (int j = 0; j < E; j += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(p + j);
+      v[j] = x.x;
+      v[j + 1] = x.y;
+      v[j + 2] = x.z;
+      v[j + 3] = x.w;
+    }
+  }
+}
+
+// The E-value slices at element offset `off` of the G (<= 8) query heads
+// g0, g0 + 1, ... of a group (head stride D): every load is issued before
+// any value is used; slices of heads g >= G repeat head g0 and are unused.
+template <int E, int D>
+__device__ __forceinline__ void load_q_group(const void* q, sa_dtype dt, int64_t g0, int G,
+                                             int off, float (&v)[8][E]) {
+  if (dt == SA_BF16) {
+#pragma unroll
+    for (int g = 0; g < 8; ++g) load_q_vec<E, true>(q, (g0 + (g < G ? g : 0)) * D + off, v[g]);
+  } else {
+#pragma unroll
+    for (int g = 0; g < 8; ++g) load_q_vec<E, false>(q, (g0 + (g < G ? g : 0)) * D + off, v[g]);
+  }
+}
+
 // ------------------------------------------------------ lane-group reductions
 // A "lane group" is LPR consecutive lanes of a wave (LPR in {4, 8, 16, 32}) that
 // together hold one cache row.  The first steps use DPP within a 16-lane DPP

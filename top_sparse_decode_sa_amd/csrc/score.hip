@@ -29,6 +29,7 @@ namespace sa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kScoreTile = 1024;  // tokens per workgroup of the exact score
 
 // ------------------------------------------------------------ exact score
 
@@ -41,7 +42,6 @@ struct ExactArgs {
   int64_t N;
   float scale;
   float* scores;
-  int32_t tile;  // tokens per workgroup
 };
 
 template <typename KT, int D, int U>
@@ -60,38 +60,41 @@ __global__ __launch_bounds__(kThreads) void score_exact_kernel(ExactArgs a) {
   const int b = row / a.Hkv;
   const int r = row % a.Hkv;
 
+  // sum of the group's queries (G <= 8): all loads issued before any add
   float qs[E];
+  {
+    float qv[8][E];
+    load_q_group<E, D>(a.q, a.q_dtype, (int64_t)b * a.Hq + (int64_t)r * a.G, a.G, sl * E, qv);
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    float acc = 0.0f;
-    for (int g = 0; g < a.G; ++g)
-      acc += load_q(a.q, a.q_dtype, ((int64_t)b * a.Hq + (int64_t)r * a.G + g) * D + sl * E + e);
-    qs[e] = acc * a.scale;
+    for (int e = 0; e < E; ++e) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) acc += g < a.G ? qv[g][e] : 0.0f;
+      qs[e] = acc * a.scale;
+    }
   }
 
   const uint8_t* kbase = a.k + ((int64_t)b * a.sb + (int64_t)r * a.sh) * EB + sl * 16;
   const int64_t row_bytes = a.st * EB;
   float* srow = a.scores + (int64_t)row * a.N;
 
-  const int64_t t_tile = (int64_t)blockIdx.x * a.tile;
-  const int64_t t_end = min(t_tile + (int64_t)a.tile, a.N);
   constexpr int per_wave_iter = RPW * U;
   constexpr int per_iter = 4 * per_wave_iter;
-  // Each wave covers per_wave_iter consecutive tokens per iteration; the next
-  // iteration's keys are in flight while this one reduces.
-  auto load = [&](int64_t base, uint4 (&kw)[U]) {
-    const int64_t wbase = base + wave * per_wave_iter;
+  constexpr int kIters = kScoreTile / per_iter;
+  static_assert(kScoreTile % per_iter == 0, "whole iterations per tile");
+  const int64_t t_tile = (int64_t)blockIdx.x * kScoreTile;
+  const int64_t t_end = min(t_tile + (int64_t)kScoreTile, a.N);
+  // Each wave covers per_wave_iter consecutive tokens per iteration.
+  auto load = [&](int64_t base, uint4 (&kw)[U], bool clamp) {
+    const int64_t wbase = base + wave * per_wave_iter + lg;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t t = wbase + u * RPW + lg;
-      kw[u] = (t < t_end) ? ld16_nt(kbase + t * row_bytes) : make_uint4(0, 0, 0, 0);
+      int64_t t = wbase + u * RPW;
+      if (clamp) t = std::min<int64_t>(t, t_end - 1);
+      kw[u] = ld16_nt(kbase + t * row_bytes);
     }
   };
-  uint4 kw[U], kn[U];
-  load(t_tile, kw);
-  for (int64_t base = t_tile; base < t_end; base += per_iter) {
-    const bool more = base + per_iter < t_end;
-    if (more) load(base + per_iter, kn);
+  auto reduce = [&](int64_t base, const uint4 (&kw)[U], bool check) {
     float mine = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -104,10 +107,27 @@ __global__ __launch_bounds__(kThreads) void score_exact_kernel(ExactArgs a) {
       if (sl == u) mine = acc;
     }
     const int64_t t = base + wave * per_wave_iter + sl * RPW + lg;
-    if (sl < U && t < t_end) srow[t] = mine;
-    if (more) {
+    if (sl < U && (!check || t < t_end)) srow[t] = mine;
+  };
+  if (t_end - t_tile == kScoreTile) {
+    // whole tile: a fixed number of iterations, fully unrolled, so every
+    // load is unconditional; the next iteration's keys are requested before
+    // this one's are reduced (sched_barrier keeps that order) and the
+    // in-order load counter waits only for the buffer being reduced
+    uint4 kb[2][U];
+    load(t_tile, kb[0], false);
 #pragma unroll
-      for (int u = 0; u < U; ++u) kw[u] = kn[u];
+    for (int i = 0; i < kIters; ++i) {
+      if (i + 1 < kIters) load(t_tile + (i + 1) * per_iter, kb[(i + 1) & 1], false);
+      __builtin_amdgcn_sched_barrier(0);
+      reduce(t_tile + i * per_iter, kb[i & 1], false);
+    }
+  } else {
+    // the row's ragged last tile: loads clamped to its last token
+    for (int64_t base = t_tile; base < t_end; base += per_iter) {
+      uint4 kw[U];
+      load(base, kw, true);
+      reduce(base, kw, true);
     }
   }
 }
@@ -222,12 +242,14 @@ __global__ __launch_bounds__(kThreads) void score_block_kernel(BlockArgs a) {
   const int r = row % a.Hkv;
 
   float qp[E], qn[E];
+  float qv[8][E];
+  load_q_group<E, D>(a.q, a.q_dtype, (int64_t)b * a.Hq + (int64_t)r * a.G, a.G, sl * E, qv);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     float p = 0.0f, n = 0.0f;
-    for (int g = 0; g < a.G; ++g) {
-      const float v =
-          load_q(a.q, a.q_dtype, ((int64_t)b * a.Hq + (int64_t)r * a.G + g) * D + sl * E + e);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const float v = g < a.G ? qv[g][e] : 0.0f;
       p += fmaxf(v, 0.0f);
       n += fminf(v, 0.0f);
     }
@@ -355,8 +377,7 @@ hipError_t launch_score_exact(const Cache& c, const void* q, const void* k, floa
   a.N = c.N;
   a.scale = c.scale;
   a.scores = scores;
-  a.tile = 1024;
-  const dim3 grid((unsigned)((c.N + a.tile - 1) / a.tile), (unsigned)(c.B * c.Hkv));
+  const dim3 grid((unsigned)((c.N + kScoreTile - 1) / kScoreTile), (unsigned)(c.B * c.Hkv));
   if (c.kv_dtype == SA_BF16) {
     if (c.D == 64)
       hipLaunchKernelGGL((score_exact_kernel<bf16_t, 64, 8>), grid, dim3(kThreads), 0, s, a);

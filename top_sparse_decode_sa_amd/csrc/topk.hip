@@ -5,23 +5,38 @@
 // list): the k positions of a row with the largest scores, equal scores taken
 // from the lower position, returned in ascending position order.
 //
-// Method: radix select on order-preserving uint32 keys (score_key), then an
-// ordered compaction.  One 1024-thread workgroup per row.
-//   1. One pass over the row (global memory, 16-byte loads, many in flight)
-//      builds a histogram of the top 12 key bits (4096 bins: fp32 scores of
-//      one magnitude spread over 16 bins, so LDS atomics rarely collide);
-//      rows of up to kResident keys are kept in LDS at the same time.  The
-//      histogram fixes the top 12 bits of T, the key of the k-th largest
-//      element.
-//   2. The positions whose top 12 bits equal T's are collected into an LDS
-//      candidate list; digit passes over the candidates only (bits 19..12,
-//      11..4, 3..0) give T exactly, and `need`, the count of elements equal
-//      to T that belong to the result.  If the candidates do not fit the
-//      list, those passes run over the whole row instead.
-//   3. One pass in position order keeps every key > T and the first `need`
-//      keys == T; a workgroup prefix sum over (count above, count equal) gives
-//      each kept element its output slot, so the output is ascending.
-// Resident rows read global memory once; larger rows read it three times.
+// Method: radix select on order-preserving uint32 keys (score_key).
+//
+// Row path, one 1024-thread workgroup per row:
+//   1. One pass over the row (16-byte loads, many in flight) builds a
+//      histogram of the top 12 key bits (4096 bins); rows of up to kResident
+//      keys are kept in LDS at the same time.  A prefix sum over the bins
+//      gives d1, the bin of the k-th largest key, and kleft, how many result
+//      elements lie inside that bin.
+//   2. Each wave owns a contiguous, 64-aligned range of positions.  One pass
+//      in that order counts, per wave, the keys in bins above d1 (all of them
+//      are in the result) and collects the keys of bin d1 (the candidates)
+//      with their positions into LDS.
+//   3. The candidates are resolved into T, the key of the last result element
+//      in selection order, and `need`, how many keys equal to T belong to the
+//      result: up to kRankCap candidates by pairwise ranking (rank = number of
+//      candidates with a larger key or an equal key at a lower position; rank
+//      < kleft is kept), more by 8- and 4-bit digit passes over the list.  If
+//      the list overflows, digit passes run over the whole row instead.
+//   4. Ordered write: each wave walks its range in position order; ballots
+//      give every kept element its output slot, the number of kept elements
+//      at lower positions = (keys above T before it) + min(keys equal to T
+//      before it, need).  One block-wide sum of the per-wave counts is the
+//      only cross-wave step.
+//
+// Multi-workgroup path, for few rows longer than kResident (a single 1M-token
+// sequence): (a) zero a per-row histogram; (b) workgroups of kMwChunk keys add
+// their 12-bit histograms with global atomics; (c) the same workgroups each
+// recompute d1 from the finished histogram and append the positions of keys
+// above bin d1 and the (key, position) candidates of bin d1 to per-row lists;
+// (d) one workgroup per row sorts the candidates by (key descending, position
+// ascending), keeps the first kleft, and sorts the k positions ascending.  If
+// the candidates overflow their list, (d) runs the row path on the row.
 #include <algorithm>
 
 #include "common.hpp"
@@ -33,9 +48,22 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kResident = 32768;  // keys kept in LDS (128 KB)
-constexpr int kCandRes = 2048;    // candidate positions, resident rows
-constexpr int kCandGlob = 8192;   // candidate (key, position) pairs, other rows
+constexpr int kTile = 16384;      // keys per LDS tile of the ordered write, other rows
 constexpr int kBins = 4096;       // first digit: 12 bits
+constexpr int kCandRes = 1024;    // candidate (key, position) pairs, resident rows
+constexpr int kCandGlob = 8192;   // candidate pairs, other rows
+constexpr int kRankCap = 256;     // candidates resolved by pairwise ranking
+
+constexpr int kMwChunk = 8192;       // keys per workgroup, multi-workgroup path
+constexpr int kMwCand = 8192;        // candidate capacity per row
+constexpr int kMwMaxRows = 64;       // rows at most, multi-workgroup path
+constexpr int kMwMaxChunks = 1024;   // chunks per row at most (n <= 8M)
+
+struct Shared {
+  uint32_t hist[kBins];
+  uint32_t tot[kWaves];
+  uint32_t digit, above, count, T, cgt, base;
+};
 
 // Workgroup-wide exclusive prefix sum; also returns the total.  Uses s_tot
 // (kWaves entries) as scratch; contains two barriers.
@@ -57,12 +85,6 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   total = all;
   return before + incl - v;
 }
-
-struct Shared {
-  uint32_t hist[kBins];
-  uint32_t tot[kWaves];
-  uint32_t digit, above, count;
-};
 
 __device__ __forceinline__ void zero_hist(Shared& sh, int bins) {
   for (int i = threadIdx.x; i < bins; i += kThreads) sh.hist[i] = 0u;
@@ -103,37 +125,69 @@ __device__ __forceinline__ uint32_t select_digit(Shared& sh, int shift, int widt
   return cnt;
 }
 
-template <bool RES>
-__global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores, int64_t n,
-                                                        int64_t row_stride, int32_t k,
-                                                        int32_t* __restrict__ idx_out, bool vec4) {
-  __shared__ Shared sh;
-  // RES: keys[kResident] then candidate positions; else (key, position) pairs
-  __shared__ uint32_t buf[RES ? kResident + kCandRes : 2 * kCandGlob];
-  uint32_t* keys = buf;                                  // RES only
-  uint32_t* cand = RES ? buf + kResident : buf;          // positions
-  uint32_t* ckey = RES ? nullptr : buf + kCandGlob;      // keys of candidates (!RES)
-  const int cap = RES ? kCandRes : kCandGlob;
+// LDS key layout for a tile in which thread t owns the E keys at positions
+// [E*t, E*t + E): groups of four keys stay together and group g of thread t
+// sits at group g ^ (t & SW), so the 16-byte reads of eight neighbouring
+// threads fall in different banks.
+template <int E>
+__device__ __forceinline__ uint32_t swz(uint32_t p) {
+  constexpr uint32_t G = E / 4;
+  constexpr uint32_t SW = G >= 8 ? 7 : G - 1;
+  const uint32_t t = p / E;
+  const uint32_t g = (p % E) >> 2;
+  return E * t + 4 * (g ^ (t & SW)) + (p & 3);
+}
 
+// Keys of s[0, n) into LDS tile `keys` (swizzled for E keys per thread); with
+// `hist`, the 12-bit histogram is counted too.
+template <int E>
+__device__ __forceinline__ void load_tile(const float* __restrict__ s, int n, bool vec4,
+                                          uint32_t* keys, Shared* hist) {
   const int tid = threadIdx.x;
-  const float* s = scores + (int64_t)blockIdx.x * row_stride;
-  int32_t* out = idx_out + (int64_t)blockIdx.x * k;
-
-  auto key_at = [&](int64_t i) -> uint32_t {
-    if constexpr (RES) return keys[i];
-    else return score_key(s[i]);
-  };
-
-  // ---- pass 1: 12-bit histogram (and the LDS copy of resident rows)
-  zero_hist(sh, kBins);
-  __syncthreads();
-  auto count_key = [&](int64_t i, float v) {
-    const uint32_t key = score_key(v);
-    if constexpr (RES) keys[i] = key;
-    atomicAdd(&sh.hist[key >> 20], 1u);
-  };
+  int done = 0;
   if (vec4) {
-    constexpr int U = 8;  // 8 x 16 bytes per thread in flight
+    constexpr int U = (E >= 8 ? E / 4 : 1);  // float4 per thread in flight
+    const int n4 = n / 4;
+    const float4* s4 = reinterpret_cast<const float4*>(s);
+    for (int base = 0; base < n4; base += kThreads * U) {
+      float4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = base + u * kThreads + tid;
+        v[u] = i < n4 ? s4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = base + u * kThreads + tid;
+        if (i < n4) {
+          const uint4 kk = make_uint4(score_key(v[u].x), score_key(v[u].y), score_key(v[u].z),
+                                      score_key(v[u].w));
+          if (keys) *reinterpret_cast<uint4*>(&keys[swz<E>(4 * i)]) = kk;
+          if (hist) {
+            atomicAdd(&hist->hist[kk.x >> 20], 1u);
+            atomicAdd(&hist->hist[kk.y >> 20], 1u);
+            atomicAdd(&hist->hist[kk.z >> 20], 1u);
+            atomicAdd(&hist->hist[kk.w >> 20], 1u);
+          }
+        }
+      }
+    }
+    done = 4 * n4;
+  }
+  for (int p = done + tid; p < n; p += kThreads) {
+    const uint32_t kk = score_key(s[p]);
+    if (keys) keys[swz<E>(p)] = kk;
+    if (hist) atomicAdd(&hist->hist[kk >> 20], 1u);
+  }
+}
+
+// 12-bit histogram of s[0, n) from global memory (rows not kept in LDS).
+__device__ __forceinline__ void hist_global(const float* __restrict__ s, int64_t n, bool vec4,
+                                            Shared& sh) {
+  const int tid = threadIdx.x;
+  constexpr int U = 8;  // 8 x 16 bytes per thread in flight
+  int64_t done = 0;
+  if (vec4) {
     const int64_t n4 = n / 4;
     const float4* s4 = reinterpret_cast<const float4*>(s);
     for (int64_t base = 0; base < n4; base += (int64_t)kThreads * U) {
@@ -147,124 +201,412 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
       for (int u = 0; u < U; ++u) {
         const int64_t i = base + (int64_t)u * kThreads + tid;
         if (i < n4) {
-          count_key(4 * i + 0, v[u].x);
-          count_key(4 * i + 1, v[u].y);
-          count_key(4 * i + 2, v[u].z);
-          count_key(4 * i + 3, v[u].w);
+          atomicAdd(&sh.hist[score_key(v[u].x) >> 20], 1u);
+          atomicAdd(&sh.hist[score_key(v[u].y) >> 20], 1u);
+          atomicAdd(&sh.hist[score_key(v[u].z) >> 20], 1u);
+          atomicAdd(&sh.hist[score_key(v[u].w) >> 20], 1u);
         }
       }
     }
-    for (int64_t i = 4 * n4 + tid; i < n; i += kThreads) count_key(i, s[i]);
-  } else {
-    constexpr int U = 8;
-    for (int64_t base = 0; base < n; base += (int64_t)kThreads * U) {
-      float v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t i = base + (int64_t)u * kThreads + tid;
-        v[u] = i < n ? s[i] : 0.0f;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t i = base + (int64_t)u * kThreads + tid;
-        if (i < n) count_key(i, v[u]);
-      }
-    }
+    done = 4 * n4;
   }
-  __syncthreads();
-  uint32_t prefix = 0, mask = 0, kleft = (uint32_t)k;
-  const uint32_t c1 = select_digit(sh, 20, 12, prefix, mask, kleft);
+  for (int64_t i = done + tid; i < n; i += kThreads) atomicAdd(&sh.hist[score_key(s[i]) >> 20], 1u);
+}
 
-  // ---- pass 2: candidates sharing the top 12 bits, then the remaining digits
-  constexpr int kShift[3] = {12, 4, 0};
-  constexpr int kWidth[3] = {8, 8, 4};
-  if (c1 <= (uint32_t)cap) {
-    if (tid == 0) sh.count = 0;
+// Resolve the candidates cand[0, c1) (key, position) of the bin fixed by
+// (prefix, mask), of which kleft1 belong to the result: T, the key of the
+// last kept candidate in selection order, and `need`, the kept candidates
+// equal to T.  cand must have room for c1 rounded up to 32.
+__device__ void resolve(uint2* cand, uint32_t c1, uint32_t kleft1, uint32_t prefix, uint32_t mask,
+                        Shared& sh, uint32_t& T, uint32_t& need) {
+  const int tid = threadIdx.x;
+  if (c1 <= (uint32_t)kRankCap) {
+    // rank = candidates with a larger key or an equal key at a lower
+    // position; four threads per candidate, each over a quarter of the list
+    const uint32_t c1p = (c1 + 31u) & ~31u;
+    for (uint32_t c = c1 + tid; c < c1p; c += kThreads) cand[c] = make_uint2(0u, 0xffffffffu);
     __syncthreads();
-    for (int64_t i = tid; i < n; i += kThreads) {
-      const uint32_t key = key_at(i);
-      if ((key & mask) == prefix) {
-        const uint32_t pos = atomicAdd(&sh.count, 1u);
-        cand[pos] = (uint32_t)i;
-        if constexpr (!RES) ckey[pos] = key;
+    const uint32_t ci = tid >> 2, part = tid & 3;
+    const uint2 me = cand[ci < c1 ? ci : 0];
+    uint32_t rank = 0;
+    if (ci < c1) {
+      const uint32_t q = c1p / 4;
+      for (uint32_t j0 = part * q; j0 < (part + 1) * q; j0 += 8) {
+        uint2 o[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o[u] = cand[j0 + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          rank += (o[u].x > me.x || (o[u].x == me.x && o[u].y < me.y)) ? 1u : 0u;
       }
     }
+    rank += __shfl_xor(rank, 1, 64);
+    rank += __shfl_xor(rank, 2, 64);
+    if (ci < c1 && part == 0 && rank == kleft1 - 1) sh.T = me.x;
     __syncthreads();
+    T = sh.T;
+  } else {
+    constexpr int kShift[3] = {12, 4, 0};
+    constexpr int kWidth[3] = {8, 8, 4};
+    uint32_t kleft = kleft1;
+#pragma unroll
     for (int d = 0; d < 3; ++d) {
       zero_hist(sh, 1 << kWidth[d]);
       __syncthreads();
       for (uint32_t c = tid; c < c1; c += kThreads) {
-        const uint32_t key = RES ? keys[cand[c]] : ckey[c];
+        const uint32_t key = cand[c].x;
         if ((key & mask) == prefix)
           atomicAdd(&sh.hist[(key >> kShift[d]) & ((1u << kWidth[d]) - 1u)], 1u);
       }
       __syncthreads();
       select_digit(sh, kShift[d], kWidth[d], prefix, mask, kleft);
     }
-  } else {
-    for (int d = 0; d < 3; ++d) {
-      zero_hist(sh, 1 << kWidth[d]);
-      __syncthreads();
-      for (int64_t i = tid; i < n; i += kThreads) {
-        const uint32_t key = key_at(i);
-        if ((key & mask) == prefix)
-          atomicAdd(&sh.hist[(key >> kShift[d]) & ((1u << kWidth[d]) - 1u)], 1u);
-      }
-      __syncthreads();
-      select_digit(sh, kShift[d], kWidth[d], prefix, mask, kleft);
-    }
+    T = prefix;
   }
-  const uint32_t T = prefix;
-  const uint32_t need = kleft;  // keys == T to keep, lowest positions first
+  if (tid == 0) sh.cgt = 0;
+  __syncthreads();
+  uint32_t g = 0;
+  for (uint32_t c = tid; c < c1; c += kThreads) g += cand[c].x > T ? 1u : 0u;
+  if (g) atomicAdd(&sh.cgt, g);
+  __syncthreads();
+  need = kleft1 - sh.cgt;  // kept candidates: those above T and `need` equal to T
+}
 
-  // ---- pass 3: ordered compaction
-  uint32_t gt_run = 0, eq_run = 0;
-  constexpr int PER = 4;
-  for (int64_t base = 0; base < n; base += (int64_t)kThreads * PER) {
-    const int64_t i0 = base + (int64_t)tid * PER;
-    uint32_t key[PER];
-    uint32_t cg = 0, ce = 0;
+// Digit passes over a whole row when the candidates overflow: T and need.
+template <typename KeyAt>
+__device__ void resolve_row(KeyAt key_at, int64_t n, uint32_t kleft, uint32_t prefix, uint32_t mask,
+                            Shared& sh, uint32_t& T, uint32_t& need) {
+  constexpr int kShift[3] = {12, 4, 0};
+  constexpr int kWidth[3] = {8, 8, 4};
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const bool valid = i0 + e < n;
-      key[e] = valid ? key_at(i0 + e) : 0u;
-      cg += (valid && key[e] > T) ? 1u : 0u;
-      ce += (valid && key[e] == T) ? 1u : 0u;
+  for (int d = 0; d < 3; ++d) {
+    zero_hist(sh, 1 << kWidth[d]);
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < n; i += kThreads) {
+      const uint32_t key = key_at(i);
+      if ((key & mask) == prefix)
+        atomicAdd(&sh.hist[(key >> kShift[d]) & ((1u << kWidth[d]) - 1u)], 1u);
     }
-    uint32_t total;
-    const uint32_t excl = block_exclusive_scan((cg << 16) | ce, sh.tot, total);
-    uint32_t gt_b = gt_run + (excl >> 16);
-    uint32_t eq_b = eq_run + (excl & 0xffffu);
+    __syncthreads();
+    select_digit(sh, kShift[d], kWidth[d], prefix, mask, kleft);
+  }
+  T = prefix;
+  need = kleft;
+}
+
+// Ordered write of one LDS tile (positions tile0 + [0, n_valid), E per
+// thread): every key above T, and keys equal to T while fewer than `need`
+// came before, go to out at slot = kept keys at lower positions.  run_gt /
+// run_eq carry the counts of earlier tiles.  Contains barriers.
+template <int E>
+__device__ __forceinline__ void write_tile(const uint32_t* keys, int64_t tile0, int n_valid,
+                                           uint32_t T, uint32_t need, uint32_t& run_gt,
+                                           uint32_t& run_eq, int32_t* __restrict__ out,
+                                           Shared& sh) {
+  static_assert(E % 4 == 0 && E <= 32, "E keys per thread in groups of four");
+  constexpr int G = E / 4;
+  constexpr int SW = G >= 8 ? 7 : G - 1;
+  const int t = threadIdx.x;
+  uint32_t key[E];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      if (i0 + e >= n) break;
-      if (key[e] > T) {
-        out[gt_b + min(eq_b, need)] = (int32_t)(i0 + e);
-        ++gt_b;
-      } else if (key[e] == T) {
-        if (eq_b < need) out[gt_b + eq_b] = (int32_t)(i0 + e);
-        ++eq_b;
+  for (int g = 0; g < G; ++g) {
+    const uint4 v = *reinterpret_cast<const uint4*>(&keys[E * t + 4 * (g ^ (t & SW))]);
+    key[4 * g + 0] = v.x;
+    key[4 * g + 1] = v.y;
+    key[4 * g + 2] = v.z;
+    key[4 * g + 3] = v.w;
+  }
+  uint32_t cg = 0, ce = 0, mg = 0, me = 0;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const bool valid = E * t + j < n_valid;
+    const bool gt = valid && key[j] > T;
+    const bool eq = valid && key[j] == T;
+    cg += gt ? 1u : 0u;
+    ce += eq ? 1u : 0u;
+    mg |= (gt ? 1u : 0u) << j;
+    me |= (eq ? 1u : 0u) << j;
+  }
+  uint32_t total;
+  const uint32_t excl = block_exclusive_scan((cg << 16) | ce, sh.tot, total);
+  uint32_t gb = run_gt + (excl >> 16);
+  uint32_t eb = run_eq + (excl & 0xffffu);
+  uint32_t m = mg | me;
+  while (m) {
+    const int j = __builtin_ctz(m);
+    m &= m - 1u;
+    const int32_t pos = (int32_t)(tile0 + E * t + j);
+    if ((mg >> j) & 1u) {
+      out[gb + std::min(eb, need)] = pos;
+      ++gb;
+    } else {
+      if (eb < need) out[gb + eb] = pos;
+      ++eb;
+    }
+  }
+  run_gt += total >> 16;
+  run_eq += total & 0xffffu;
+}
+
+// The row path for one row, by the whole workgroup.  RES: the row is kept in
+// LDS (n <= kResident); otherwise it is read from global memory again for the
+// candidates and, tile by tile, for the ordered write.
+// buf: RES: kResident keys + kCandRes pairs; otherwise kTile keys + kCandGlob
+// pairs.
+template <bool RES>
+__device__ void topk_row(const float* __restrict__ s, int64_t n, int32_t k,
+                         int32_t* __restrict__ out, bool vec4, Shared& sh, uint32_t* buf) {
+  constexpr int E = RES ? kResident / kThreads : kTile / kThreads;
+  uint32_t* keys = buf;
+  uint2* cand = reinterpret_cast<uint2*>(buf + (RES ? kResident : kTile));
+  constexpr uint32_t cap = RES ? kCandRes : kCandGlob;
+  const int tid = threadIdx.x;
+  auto key_at = [&](int64_t i) -> uint32_t {
+    if constexpr (RES) return keys[swz<E>((uint32_t)i)];
+    else return score_key(s[i]);
+  };
+
+  // ---- 1. histogram of the top 12 bits
+  zero_hist(sh, kBins);
+  __syncthreads();
+  if constexpr (RES) load_tile<E>(s, (int)n, vec4, keys, &sh);
+  else hist_global(s, n, vec4, sh);
+  __syncthreads();
+  uint32_t prefix = 0, mask = 0, kleft = (uint32_t)k;
+  const uint32_t c1 = select_digit(sh, 20, 12, prefix, mask, kleft);
+  const uint32_t d1 = prefix >> 20;
+
+  // ---- 2-3. candidates of bin d1, resolved to T and need
+  uint32_t T, need;
+  if (c1 <= cap) {
+    if (tid == 0) sh.count = 0;
+    __syncthreads();
+    constexpr int U = 8;
+    for (int64_t base = 0; base < n; base += (int64_t)kThreads * U) {
+      uint32_t kk[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = base + (int64_t)u * kThreads + tid;
+        kk[u] = i < n ? key_at(i) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = base + (int64_t)u * kThreads + tid;
+        if (i < n && (kk[u] >> 20) == d1) cand[atomicAdd(&sh.count, 1u)] = make_uint2(kk[u], (uint32_t)i);
       }
     }
-    gt_run += total >> 16;
-    eq_run += total & 0xffffu;
+    __syncthreads();
+    resolve(cand, c1, kleft, prefix, mask, sh, T, need);
+  } else {
+    resolve_row(key_at, n, kleft, prefix, mask, sh, T, need);
   }
+
+  // ---- 4. ordered write
+  uint32_t run_gt = 0, run_eq = 0;
+  if constexpr (RES) {
+    write_tile<E>(keys, 0, (int)n, T, need, run_gt, run_eq, out, sh);
+  } else {
+    for (int64_t tile0 = 0; tile0 < n; tile0 += kTile) {
+      const int nv = (int)std::min<int64_t>(kTile, n - tile0);
+      __syncthreads();  // the previous tile is consumed
+      load_tile<E>(s + tile0, nv, vec4, keys, nullptr);
+      __syncthreads();
+      write_tile<E>(keys, tile0, nv, T, need, run_gt, run_eq, out, sh);
+    }
+  }
+}
+
+template <bool RES>
+__global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores, int64_t n,
+                                                        int64_t row_stride, int32_t k,
+                                                        int32_t* __restrict__ idx_out, bool vec4) {
+  __shared__ Shared sh;
+  __shared__ __align__(16) uint32_t buf[RES ? kResident + 2 * kCandRes : kTile + 2 * kCandGlob];
+  topk_row<RES>(scores + (int64_t)blockIdx.x * row_stride, n, k,
+                idx_out + (int64_t)blockIdx.x * k, vec4, sh, buf);
+}
+
+// ------------------------------------------------- multi-workgroup path
+
+// Per-row workspace.
+struct MwRow {
+  uint32_t hist[kBins];            // 12-bit histogram of the row
+  uint32_t n_cand, T, need, fallback;
+  uint2 cand[kMwCand];             // (key, position) of bin d1, any order
+  uint32_t n_above[kMwMaxChunks];  // per chunk: keys above bin d1
+  uint32_t base_gt[kMwMaxChunks];  // per chunk: result keys above T before it
+  uint32_t base_eq[kMwMaxChunks];  // per chunk: keys equal to T before it
+};
+
+__global__ __launch_bounds__(256) void topk_mw_zero(MwRow* rows) {
+  MwRow& w = rows[blockIdx.x];
+  for (int i = threadIdx.x; i < kBins; i += 256) w.hist[i] = 0u;
+  if (threadIdx.x == 0) w.n_cand = 0u;
+}
+
+__global__ __launch_bounds__(kThreads) void topk_mw_hist(const float* __restrict__ scores, int64_t n,
+                                                         int64_t row_stride, bool vec4, MwRow* rows) {
+  __shared__ Shared sh;
+  const int64_t c0 = (int64_t)blockIdx.x * kMwChunk;
+  zero_hist(sh, kBins);
+  __syncthreads();
+  load_tile<kMwChunk / kThreads>(scores + (int64_t)blockIdx.y * row_stride + c0,
+                                 (int)std::min<int64_t>(kMwChunk, n - c0), vec4, nullptr, &sh);
+  __syncthreads();
+  uint32_t* g = rows[blockIdx.y].hist;
+  for (int b = threadIdx.x; b < kBins; b += kThreads)
+    if (sh.hist[b]) atomicAdd(&g[b], sh.hist[b]);
+}
+
+// d1's prefix and mask, kleft and the count of bin d1 from the finished
+// per-row histogram.
+__device__ __forceinline__ uint32_t mw_select(const MwRow& w, int32_t k, Shared& sh,
+                                              uint32_t& prefix, uint32_t& mask, uint32_t& kleft) {
+  for (int b = threadIdx.x; b < kBins; b += kThreads) sh.hist[b] = w.hist[b];
+  __syncthreads();
+  prefix = 0;
+  mask = 0;
+  kleft = (uint32_t)k;
+  return select_digit(sh, 20, 12, prefix, mask, kleft);
+}
+
+__global__ __launch_bounds__(kThreads) void topk_mw_collect(const float* __restrict__ scores,
+                                                            int64_t n, int64_t row_stride,
+                                                            int32_t k, MwRow* rows) {
+  __shared__ Shared sh;
+  MwRow& w = rows[blockIdx.y];
+  uint32_t prefix, mask, kleft;
+  const uint32_t c1 = mw_select(w, k, sh, prefix, mask, kleft);
+  const uint32_t d1 = prefix >> 20;
+  const int64_t c0 = (int64_t)blockIdx.x * kMwChunk;
+  const float* s = scores + (int64_t)blockIdx.y * row_stride;
+  constexpr int PER = kMwChunk / kThreads;
+  uint32_t key[PER];
+  uint32_t n_above = 0, n_cand = 0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int64_t i = c0 + (int64_t)e * kThreads + threadIdx.x;
+    const bool valid = i < n;
+    key[e] = valid ? score_key(s[i]) : 0u;
+    n_above += (valid && (key[e] >> 20) > d1) ? 1u : 0u;
+    n_cand += (valid && (key[e] >> 20) == d1) ? 1u : 0u;
+  }
+  uint32_t total;
+  const uint32_t excl = block_exclusive_scan((n_above << 16) | n_cand, sh.tot, total);
+  if (threadIdx.x == 0) {
+    w.n_above[blockIdx.x] = total >> 16;
+    sh.base = 0;
+    if (c1 <= (uint32_t)kMwCand && (total & 0xffffu)) sh.base = atomicAdd(&w.n_cand, total & 0xffffu);
+  }
+  __syncthreads();
+  if (c1 > (uint32_t)kMwCand) return;  // the resolving kernel runs the row path
+  uint32_t pc = sh.base + (excl & 0xffffu);
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int64_t i = c0 + (int64_t)e * kThreads + threadIdx.x;
+    if (i < n && (key[e] >> 20) == d1) w.cand[pc++] = make_uint2(key[e], (uint32_t)i);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void topk_mw_resolve(const float* __restrict__ scores,
+                                                            int64_t n, int64_t row_stride,
+                                                            int32_t k, bool vec4, MwRow* rows,
+                                                            int32_t* __restrict__ idx_out) {
+  __shared__ Shared sh;
+  __shared__ __align__(16) uint32_t buf[kTile + 2 * kCandGlob];
+  __shared__ uint32_t s_gt[kMwMaxChunks], s_eq[kMwMaxChunks];
+  MwRow& w = rows[blockIdx.x];
+  uint32_t prefix, mask, kleft;
+  const uint32_t c1 = mw_select(w, k, sh, prefix, mask, kleft);
+  if (c1 > (uint32_t)kMwCand) {
+    if (threadIdx.x == 0) w.fallback = 1u;
+    topk_row<false>(scores + (int64_t)blockIdx.x * row_stride, n, k,
+                    idx_out + (int64_t)blockIdx.x * k, vec4, sh, buf);
+    return;
+  }
+  uint2* cand = reinterpret_cast<uint2*>(buf + kTile);
+  for (uint32_t c = threadIdx.x; c < c1; c += kThreads) cand[c] = w.cand[c];
+  const int n_chunks = (int)((n + kMwChunk - 1) / kMwChunk);
+  for (int c = threadIdx.x; c < n_chunks; c += kThreads) {
+    s_gt[c] = w.n_above[c];
+    s_eq[c] = 0u;
+  }
+  __syncthreads();
+  uint32_t T, need;
+  resolve(cand, c1, kleft, prefix, mask, sh, T, need);
+  for (uint32_t c = threadIdx.x; c < c1; c += kThreads) {
+    const uint2 e = cand[c];
+    const int ch = (int)(e.y / kMwChunk);
+    if (e.x > T) atomicAdd(&s_gt[ch], 1u);
+    else if (e.x == T) atomicAdd(&s_eq[ch], 1u);
+  }
+  __syncthreads();
+  // per-chunk counts (each < 2^14) to exclusive prefix sums
+  const int c = threadIdx.x;
+  const uint32_t v = c < n_chunks ? (s_gt[c] << 16) | s_eq[c] : 0u;
+  uint32_t total;
+  const uint32_t excl = block_exclusive_scan(v, sh.tot, total);
+  if (c < n_chunks) {
+    w.base_gt[c] = excl >> 16;
+    w.base_eq[c] = excl & 0xffffu;
+  }
+  if (c == 0) {
+    w.T = T;
+    w.need = need;
+    w.fallback = 0u;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void topk_mw_write(const float* __restrict__ scores,
+                                                          int64_t n, int64_t row_stride,
+                                                          int32_t k, bool vec4, MwRow* rows,
+                                                          int32_t* __restrict__ idx_out) {
+  __shared__ Shared sh;
+  __shared__ __align__(16) uint32_t keys[kMwChunk];
+  const MwRow& w = rows[blockIdx.y];
+  if (w.fallback) return;  // the resolving kernel wrote this row
+  const int64_t c0 = (int64_t)blockIdx.x * kMwChunk;
+  const int nv = (int)std::min<int64_t>(kMwChunk, n - c0);
+  load_tile<kMwChunk / kThreads>(scores + (int64_t)blockIdx.y * row_stride + c0, nv, vec4, keys,
+                                 nullptr);
+  __syncthreads();
+  uint32_t run_gt = w.base_gt[blockIdx.x], run_eq = w.base_eq[blockIdx.x];
+  write_tile<kMwChunk / kThreads>(keys, c0, nv, w.T, w.need, run_gt, run_eq,
+                                  idx_out + (int64_t)blockIdx.y * k, sh);
+}
+
+bool use_mw(int64_t n_rows, int64_t n, int32_t k) {
+  return n > kResident && n_rows <= kMwMaxRows && n <= (int64_t)kMwChunk * kMwMaxChunks &&
+         k <= kMwCand;
 }
 
 }  // namespace
 
-size_t topk_workspace_bytes(int64_t, int64_t, int32_t) { return 0; }
+size_t topk_workspace_bytes(int64_t n_rows, int64_t n, int32_t k) {
+  return use_mw(n_rows, n, k) ? (size_t)n_rows * sizeof(MwRow) : 0;
+}
 
 hipError_t launch_topk(const float* scores, int64_t n_rows, int64_t n, int64_t row_stride, int32_t k,
-                       int32_t* idx, void*, hipStream_t s) {
+                       int32_t* idx, void* ws, hipStream_t s) {
   // 16-byte loads when every row starts 16-byte aligned
   const bool vec4 = (reinterpret_cast<uintptr_t>(scores) % 16 == 0) && (row_stride % 4 == 0);
-  if (n <= kResident)
+  if (n <= kResident) {
     hipLaunchKernelGGL(topk_kernel<true>, dim3((unsigned)n_rows), dim3(kThreads), 0, s, scores, n,
                        row_stride, k, idx, vec4);
-  else
+  } else if (use_mw(n_rows, n, k)) {
+    MwRow* rows = static_cast<MwRow*>(ws);
+    const dim3 grid((unsigned)((n + kMwChunk - 1) / kMwChunk), (unsigned)n_rows);
+    hipLaunchKernelGGL(topk_mw_zero, dim3((unsigned)n_rows), dim3(256), 0, s, rows);
+    hipLaunchKernelGGL(topk_mw_hist, grid, dim3(kThreads), 0, s, scores, n, row_stride, vec4, rows);
+    hipLaunchKernelGGL(topk_mw_collect, grid, dim3(kThreads), 0, s, scores, n, row_stride, k, rows);
+    hipLaunchKernelGGL(topk_mw_resolve, dim3((unsigned)n_rows), dim3(kThreads), 0, s, scores, n,
+                       row_stride, k, vec4, rows, idx);
+    hipLaunchKernelGGL(topk_mw_write, grid, dim3(kThreads), 0, s, scores, n, row_stride, k, vec4,
+                       rows, idx);
+  } else {
     hipLaunchKernelGGL(topk_kernel<false>, dim3((unsigned)n_rows), dim3(kThreads), 0, s, scores, n,
                        row_stride, k, idx, vec4);
+  }
   return hipGetLastError();
 }
 
