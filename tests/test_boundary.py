@@ -81,7 +81,10 @@ def test_pointer_index_and_workspace_errors():
     assert _sparse(d, n_idx=500, ws=None, nbytes=0) == Bn.SA_ERR_WORKSPACE
     assert _sparse(d, n_idx=500, ws=FAKE, nbytes=need - 1) == Bn.SA_ERR_WORKSPACE
     assert _sparse(d, n_idx=500, ws=ctypes.c_void_p((1 << 20) + 16), nbytes=need) == Bn.SA_ERR_ALIGN
-    assert L.sa_dense_decode(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 0, None) == \
+    # a long cache is split over several workgroups per row: it needs a workspace
+    dl = _desc(ctx_len=100000, kv_stride_b=2 * 100000 * 128, kv_stride_h=100000 * 128)
+    assert L.sa_dense_workspace_size(ctypes.byref(dl)) > 0
+    assert L.sa_dense_decode(ctypes.byref(dl), FAKE, FAKE, FAKE, FAKE, None, 0, None) == \
         Bn.SA_ERR_WORKSPACE
     assert L.sa_dense_workspace_size(ctypes.byref(_desc(head_dim=96))) == 0
 

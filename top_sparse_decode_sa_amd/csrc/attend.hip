@@ -20,16 +20,17 @@
 // (and no zero-initialised counter) is needed.
 //
 // Kernels:
-//   * attend_wave_kernel (bf16, head_dim 128, G <= 4): one wave processes
-//     16-token tiles.  Lane l holds token l%16's key dims [32c + 8(l/16), +8)
-//     (c = 0..3) -- the B operand of v_mfma_f32_16x16x32_bf16 with the
-//     group's queries as the A operand -- so four MFMAs give the G logits of
-//     16 tokens in lanes 0..15.  Value loads use 128-bit row pieces (token
-//     4u + l/16, dims [8(l%16), +8)); p reaches that layout through a 256-byte
-//     LDS slot of the wave; o accumulates in fp32.  Loads of tile t+1 are in
-//     flight while tile t computes.  Sparse selections use one-wave
-//     workgroups (no barrier, waves retire independently); dense decode uses
-//     four waves per workgroup merged through LDS.
+//   * attend_sparse_kernel (bf16, head_dim 128, G <= 4), for selected sets
+//     and for dense decode alike: a workgroup of 1 to 12 waves; each wave
+//     takes rounds of up to 64 slots.  Per round every index, key and value
+//     load is issued before any is used (no load sits under a branch, so the
+//     in-order load counter keeps them all in flight).  Lane l holds token
+//     l%16's key dims [32c + 8(l/16), +8) -- the B operand of
+//     v_mfma_f32_16x16x32_bf16 with the group's queries as the A operand --
+//     so four MFMAs give the G logits of 16 tokens.  P.V also runs on MFMA
+//     (P split into two bf16 parts).  Rounds merge online per wave; the
+//     waves of a workgroup merge through LDS.  Dense decode walks contiguous
+//     tokens without index loads.
 //   * attend_kernel (any other dtype / head_dim / group): lane groups of LPR
 //     lanes hold whole cache rows; logits reduce with DPP inside the group.
 #include <math.h>
@@ -62,6 +63,7 @@ struct AttendArgs {
   int64_t n_slots;
   int32_t chunk;
   int32_t nsplit;
+  int32_t rounds;  // gather kernel: slot rounds per wave
   float* out;
   float* part;  // [rows, nsplit, G, D + 2]: o[G][D], m[G], l[G]
 };
@@ -250,124 +252,6 @@ __device__ __forceinline__ float wave_bcast0(float x) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
 }
 
-struct TileLoads {
-  uint4 kw[4];
-  uint4 vw[4];
-  bool okk;
-};
-
-template <int MODE>
-__device__ __forceinline__ void load_tile(const AttendArgs& a, int row, int b, int64_t jbase,
-                                          int64_t s1, int n, int rq, const uint8_t* kbase,
-                                          const uint8_t* vbase, int64_t row_bytes, TileLoads& T) {
-  T.okk = jbase + n < s1;
-  int64_t tk = 0;
-  if (T.okk) tk = resolve_slot<MODE>(a, row, b, jbase + n, T.okk);
-  // a dense scan reads every row once: streaming (nontemporal) loads
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const uint8_t* p = kbase + tk * row_bytes + 64 * c;
-    T.kw[c] = !T.okk ? make_uint4(0, 0, 0, 0) : (MODE == kIdxDense ? ld16_nt(p) : ld16(p));
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t jv = jbase + 4 * u + rq;
-    bool okv = jv < s1;
-    int64_t tv = 0;
-    if (okv) tv = resolve_slot<MODE>(a, row, b, jv, okv);
-    const uint8_t* p = vbase + tv * row_bytes;
-    T.vw[u] = !okv ? make_uint4(0, 0, 0, 0) : (MODE == kIdxDense ? ld16_nt(p) : ld16(p));
-  }
-}
-
-
-// One 16-token tile: MFMA logits, online-softmax update of (m_run, l_run, o).
-// m_run / l_run are wave-uniform; o holds this lane's dims [8n, 8n+8) for the
-// tile's tokens 4u + rq.  s_p is this wave's 16x4 LDS slot.
-template <int G>
-__device__ __forceinline__ void tile_step(const TileLoads& T, const bf16x8_t (&qa)[4], float qscale,
-                                          int n, int rq, float (*s_p)[4], float (&m_run)[G],
-                                          float (&l_run)[G], float (&o)[G][8]) {
-  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    bf16x8_t kb;
-    __builtin_memcpy(&kb, &T.kw[c], 16);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[c], kb, acc, 0, 0, 0);
-  }
-  float lg[G], tmax[G];
-  bool any = false;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    lg[h] = (rq == 0 && T.okk) ? acc[h] * qscale : -INFINITY;
-    tmax[h] = wave_bcast0(group_max<16>(lg[h]));
-    any |= (tmax[h] != -INFINITY);
-  }
-  if (!any) return;  // wave-uniform: no valid token in this tile
-  float p[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float mn = fmaxf(m_run[h], tmax[h]);
-    const float alpha = exp2f(m_run[h] - mn);
-    p[h] = exp2f(lg[h] - mn);
-    const float tsum = wave_bcast0(group_sum<16>(p[h]));
-    l_run[h] = l_run[h] * alpha + tsum;
-    m_run[h] = mn;
-    if (alpha != 1.0f) {  // wave-uniform
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
-    }
-  }
-  // p to the value layout through the wave's LDS slot (in-order LDS access)
-  if (rq == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) s_p[n][h] = p[h];
-  }
-  __builtin_amdgcn_wave_barrier();
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    float pv[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) pv[h] = s_p[4 * u + rq][h];
-    float vf[8];
-    unpack16<bf16_t>(T.vw[u], vf);
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] = fmaf(pv[h], vf[e], o[h][e]);
-  }
-  __builtin_amdgcn_wave_barrier();
-}
-
-// Sum o over the four 16-lane rows (tokens 4u + rq): lanes 0..15 end with the
-// wave's o for dims [8n, 8n + 8).
-template <int G>
-__device__ __forceinline__ void reduce_rows(float (&o)[G][8]) {
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = o[h][e];
-      v += __shfl_xor(v, 32);
-      v += __shfl_xor(v, 16);
-      o[h][e] = v;
-    }
-}
-
-// q of the row's G heads as MFMA A fragments: lane (n, rq) holds head n's dims
-// [32c + 8rq, +8) for c = 0..3 (zero for n >= G).
-template <int G>
-__device__ __forceinline__ void load_q_frag(const AttendArgs& a, int b, int r, int n, int rq,
-                                            bf16x8_t (&qa)[4]) {
-  const uint8_t* qb = static_cast<const uint8_t*>(a.q) +
-                      (((int64_t)b * a.Hq + (int64_t)r * G + (n < G ? n : 0)) * 128 + 8 * rq) * 2;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    uint4 w = n < G ? ld16(qb + 64 * c) : make_uint4(0, 0, 0, 0);
-    __builtin_memcpy(&qa[c], &w, 16);
-  }
-}
-
 // Slot j of a row (s0 <= j < s1) -> token position, for a slot that may lie
 // past the selection: the load is always made at an in-range position (the
 // last slot, the last token) and `ok` reports whether the slot is real.  No
@@ -377,7 +261,9 @@ __device__ __forceinline__ int32_t slot_token(const AttendArgs& a, int row, int 
                                               int64_t s1, bool& ok) {
   ok = j < s1;
   const int64_t jj = ok ? j : s1 - 1;
-  if constexpr (MODE == kIdxTokenPerHead) {
+  if constexpr (MODE == kIdxDense) {
+    return (int32_t)jj;
+  } else if constexpr (MODE == kIdxTokenPerHead) {
     return a.idx[(int64_t)row * a.n_idx + jj];
   } else if constexpr (MODE == kIdxTokenShared) {
     return a.idx[(int64_t)b * a.n_idx + jj];
@@ -388,14 +274,24 @@ __device__ __forceinline__ int32_t slot_token(const AttendArgs& a, int row, int 
   }
 }
 
-// Selected-set decode: 1 to kMaxSparseWaves waves per workgroup (the block
-// size says how many), up to 16 * TILES slots per wave.  The memory operations are ordered for the in-order load counter: one
-// index load per lane per tile (lane l reads the token of slot l % 16), then
-// every key row piece of every tile, then every value row piece (value-row
-// token ids come from the owning lane by a shuffle), then the compute.  Both
-// Q.K and P.V run on MFMA; the softmax is computed in two passes over the
-// wave's tokens (one max, one sum per head), so no running rescale is needed.
-// Several waves merge their (o, max, sum) in LDS and write one result.
+// K/V row pieces: a dense scan reads every row once, so its loads are
+// nontemporal (streaming); gathered rows use ordinary loads.
+template <int MODE>
+__device__ __forceinline__ uint4 ld_kv(const uint8_t* p) {
+  if constexpr (MODE == kIdxDense) return ld16_nt(p);
+  else return ld16(p);
+}
+
+// Gather-attend over selected slots (or all tokens): 1 to kMaxSparseWaves
+// waves per workgroup (the block size says how many), `rounds` rounds of up
+// to 16 * TILES slots per wave.  Within a round the memory operations are
+// ordered for the in-order load counter: one index load per lane per tile
+// (lane l reads the token of slot l % 16), then every key row piece of every
+// tile, then every value row piece (value-row token ids come from the owning
+// lane by a shuffle), then the compute.  Q.K and P.V run on MFMA; a round's
+// softmax takes two passes over its tokens (one max, one sum per head), and
+// rounds merge into a running (max, sum, o) per head.  The waves of a
+// workgroup merge in LDS and write one result.
 constexpr int kMaxSparseWaves = 12;
 
 template <int G, int MODE, int TILES>
@@ -417,25 +313,8 @@ __global__ __launch_bounds__(64 * kMaxSparseWaves) void attend_sparse_kernel(Att
   const int split = blockIdx.x;
   const int b = row / a.Hkv;
   const int r = row % a.Hkv;
-  // this wave's slots: [s0, s1) of the workgroup's chunk, 16 * TILES per wave
   const int64_t wg0 = (int64_t)split * a.chunk;
   const int64_t wg1 = min(wg0 + (int64_t)a.chunk, a.n_slots);
-  const int64_t s0 = wg0 + (int64_t)wave * 16 * TILES;
-  const int64_t s1 = min(s0 + 16 * TILES, wg1);
-  const bool idle = s0 >= wg1;  // wave-uniform: nothing left for this wave
-
-  // 1. token of slot 16i + n of every tile
-  int32_t tok[TILES];
-  bool ok[TILES];
-  // an idle wave reads the workgroup's first slot (always valid) and masks it:
-  // no branch around the loads
-  const int64_t r0 = idle ? wg0 : s0;
-  const int64_t r1 = idle ? wg0 + 1 : s1;
-#pragma unroll
-  for (int i = 0; i < TILES; ++i) {
-    tok[i] = slot_token<MODE>(a, row, b, r0 + 16 * i + n, r1, ok[i]);
-    ok[i] = ok[i] && !idle;
-  }
 
   // q of head n (lanes n >= G carry zeros): MFMA A fragments, dims [32c + 8rq, +8)
   bf16x8_t qa[4];
@@ -450,153 +329,181 @@ __global__ __launch_bounds__(64 * kMaxSparseWaves) void attend_sparse_kernel(Att
     }
   }
 
-  // 2. key pieces of every tile, then value rows (token 4u + rq of each tile)
   const int64_t kv_off = ((int64_t)b * a.sb + (int64_t)r * a.sh) * 2;
   const uint8_t* kbase = a.k + kv_off + 16 * rq;
   const uint8_t* vbase = a.v + kv_off + 16 * n;
   const int64_t row_bytes = a.st * 2;
-  uint4 kw[TILES][4], vw[TILES][4];
-#pragma unroll
-  for (int i = 0; i < TILES; ++i)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) kw[i][c] = ld16(kbase + (int64_t)tok[i] * row_bytes + 64 * c);
-  int32_t tv[TILES][4];
-#pragma unroll
-  for (int i = 0; i < TILES; ++i)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) tv[i][u] = __shfl(tok[i], 4 * u + rq);
-#pragma unroll
-  for (int i = 0; i < TILES; ++i)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) vw[i][u] = ld16(vbase + (int64_t)tv[i][u] * row_bytes);
-  // keep every load above this point: all rows of the wave are requested
-  // before the first logit is computed
-  __builtin_amdgcn_sched_barrier(0);
 
-  // 3. logits of every tile: rows 0..G-1 of the MFMA results, in lanes 0..15
-  float lg[TILES][G];
+  // running (max, sum, o) of head rq over this wave's rounds; lane (n, rq)
+  // holds o for dims [8n, 8n + 8)
+  float m_me = -INFINITY, l_me = 0.0f;
+  float mine[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  for (int rd = 0; rd < a.rounds; ++rd) {
+    // this wave's slots of round rd: [s0, s1), 16 * TILES of them; a wave with
+    // none skips the round whole (a uniform branch around it, not around loads)
+    const int64_t s0 = wg0 + ((int64_t)rd * nw + wave) * 16 * TILES;
+    const int64_t s1 = min(s0 + 16 * TILES, wg1);
+    if (s0 >= wg1) break;
+
+    // 1. token of slot 16i + n of every tile
+    int32_t tok[TILES];
+    bool ok[TILES];
 #pragma unroll
-  for (int i = 0; i < TILES; ++i) {
-    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      bf16x8_t kb;
-      __builtin_memcpy(&kb, &kw[i][c], 16);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[c], kb, acc, 0, 0, 0);
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) lg[i][h] = (rq == 0 && ok[i]) ? acc[h] * a.qscale : -INFINITY;
-  }
-  // 4. one max per head over the wave's tokens (valid in lanes 0..15), then
-  //    p = 2^(logit - max) and its sum
-  float M[G], Lsum[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float mx = lg[0][h];
-#pragma unroll
-    for (int i = 1; i < TILES; ++i) mx = fmaxf(mx, lg[i][h]);
-    M[h] = group_max<16>(mx);
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float ls = 0.0f;
-#pragma unroll
-    for (int i = 0; i < TILES; ++i) {
-      const float pv = M[h] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(lg[i][h] - M[h]);
-      lg[i][h] = pv;
-      ls += pv;
-    }
-    Lsum[h] = group_sum<16>(ls);
-  }
-  // 5. O = P.V on MFMA.  K-step t covers tiles 2t and 2t+1; its k index
-  //    8g + j stands for slot 16(2t + j/4) + 4(j%4) + g.  B fragment of lane
-  //    (n, g): value dim 8n + e of those 8 slots, which this lane loaded as
-  //    vw[2t + j/4][j%4] (MFMA e takes the dims 8n + e, n = 0..15).  A
-  //    fragment: P enters as two bf16 parts, p = hi + lo to 2^-16 relative
-  //    (hi: p truncated to bf16; lo: the rest, rounded), so the product keeps
-  //    fp32 accuracy: row 4h carries head h's hi part, row 4h + 1 its lo part.
-  //    Lane (n, h) ends with O[h][8n + e] = acc[e][0] + acc[e][1].
-  if (rq == 0) {
+    for (int i = 0; i < TILES; ++i)
+      tok[i] = slot_token<MODE>(a, row, b, s0 + 16 * i + n, s1, ok[i]);
+
+    // 2. key pieces of every tile, then value rows (token 4u + rq of each tile)
+    uint4 kw[TILES][4], vw[TILES][4];
 #pragma unroll
     for (int i = 0; i < TILES; ++i)
 #pragma unroll
-      for (int h = 0; h < G; ++h) s_pa[wave][h][i][n & 3][n >> 2] = lg[i][h];
-  }
-  __builtin_amdgcn_wave_barrier();
-  const int ha = n >> 2;
-  const bool arow = (n & 3) < 2 && ha < G;
-  const bool lo_row = (n & 1) != 0;
-  const int hc = ha < G ? ha : G - 1;
-  f32x4_t acc[8];
+      for (int c = 0; c < 4; ++c) kw[i][c] = ld_kv<MODE>(kbase + (int64_t)tok[i] * row_bytes + 64 * c);
+    int32_t tv[TILES][4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < TILES; ++i)
 #pragma unroll
-  for (int t = 0; t < (TILES + 1) / 2; ++t) {
-    float pj[8];
+      for (int u = 0; u < 4; ++u) tv[i][u] = __shfl(tok[i], 4 * u + rq);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int i = 2 * t + half;
-      float4 q4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      if (i < TILES) q4 = *reinterpret_cast<const float4*>(&s_pa[wave][hc][i < TILES ? i : 0][rq][0]);
-      pj[4 * half + 0] = arow ? q4.x : 0.0f;
-      pj[4 * half + 1] = arow ? q4.y : 0.0f;
-      pj[4 * half + 2] = arow ? q4.z : 0.0f;
-      pj[4 * half + 3] = arow ? q4.w : 0.0f;
-    }
-    uint32_t af[4];
+    for (int i = 0; i < TILES; ++i)
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const uint32_t b0 = __float_as_uint(pj[2 * d]);
-      const uint32_t b1 = __float_as_uint(pj[2 * d + 1]);
-      const uint32_t hi = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // truncated bf16 pair
-      f32x2_t rest = {pj[2 * d] - __uint_as_float(b0 & 0xffff0000u),
-                      pj[2 * d + 1] - __uint_as_float(b1 & 0xffff0000u)};
-      bf16x2_t lo2 = __builtin_convertvector(rest, bf16x2_t);
-      uint32_t lo;
-      __builtin_memcpy(&lo, &lo2, 4);
-      af[d] = lo_row ? lo : hi;
-    }
-    bf16x8_t a_p;
-    __builtin_memcpy(&a_p, af, 16);
-  const uint4 z = make_uint4(0, 0, 0, 0);
-    const uint4 v0 = vw[2 * t][0], v1 = vw[2 * t][1], v2 = vw[2 * t][2], v3 = vw[2 * t][3];
-    const uint4 v4 = 2 * t + 1 < TILES ? vw[2 * t + 1 < TILES ? 2 * t + 1 : 0][0] : z;
-    const uint4 v5 = 2 * t + 1 < TILES ? vw[2 * t + 1 < TILES ? 2 * t + 1 : 0][1] : z;
-    const uint4 v6 = 2 * t + 1 < TILES ? vw[2 * t + 1 < TILES ? 2 * t + 1 : 0][2] : z;
-    const uint4 v7 = 2 * t + 1 < TILES ? vw[2 * t + 1 < TILES ? 2 * t + 1 : 0][3] : z;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // word e/2 of each row holds dims 8n + 2(e/2) (low half) and +1 (high)
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      auto word = [&](const uint4& x) -> uint32_t {
-        return (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
-      };
-      uint32_t bw[4];
-      bw[0] = __builtin_amdgcn_perm(word(v1), word(v0), sel);
-      bw[1] = __builtin_amdgcn_perm(word(v3), word(v2), sel);
-      bw[2] = __builtin_amdgcn_perm(word(v5), word(v4), sel);
-      bw[3] = __builtin_amdgcn_perm(word(v7), word(v6), sel);
-      bf16x8_t bv;
-      __builtin_memcpy(&bv, bw, 16);
-      acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_p, bv, acc[e], 0, 0, 0);
-    }
-  }
+      for (int u = 0; u < 4; ++u) vw[i][u] = ld_kv<MODE>(vbase + (int64_t)tv[i][u] * row_bytes);
+    // keep every load above this point: all rows of the wave are requested
+    // before the first logit is computed
+    __builtin_amdgcn_sched_barrier(0);
 
-  // M and Lsum hold the row-0 reductions (valid in lanes 0..15): broadcast
-  // them from lane 0, then every row keeps its own head
-  float mine[8];
+    // 3. logits of every tile: rows 0..G-1 of the MFMA results, in lanes 0..15
+    float lg[TILES][G];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) mine[e] = acc[e][0] + acc[e][1];
-  float m_me = wave_bcast0(M[0]), l_me = wave_bcast0(Lsum[0]);
+    for (int i = 0; i < TILES; ++i) {
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int h = 1; h < G; ++h) {
-    const float mh = wave_bcast0(M[h]);
-    const float lh = wave_bcast0(Lsum[h]);
-    if (rq == h) {
-      m_me = mh;
-      l_me = lh;
+      for (int c = 0; c < 4; ++c) {
+        bf16x8_t kb;
+        __builtin_memcpy(&kb, &kw[i][c], 16);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[c], kb, acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) lg[i][h] = (rq == 0 && ok[i]) ? acc[h] * a.qscale : -INFINITY;
     }
-  }
+    // 4. one max per head over the wave's tokens (valid in lanes 0..15), then
+    //    p = 2^(logit - max) and its sum
+    float M[G], Lsum[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mx = lg[0][h];
+#pragma unroll
+      for (int i = 1; i < TILES; ++i) mx = fmaxf(mx, lg[i][h]);
+      M[h] = group_max<16>(mx);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float ls = 0.0f;
+#pragma unroll
+      for (int i = 0; i < TILES; ++i) {
+        const float pv = M[h] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(lg[i][h] - M[h]);
+        lg[i][h] = pv;
+        ls += pv;
+      }
+      Lsum[h] = group_sum<16>(ls);
+    }
+    // 5. O = P.V on MFMA.  K-step t covers tiles 2t and 2t+1; its k index
+    //    8g + j stands for slot 16(2t + j/4) + 4(j%4) + g.  B fragment of lane
+    //    (n, g): value dim 8n + e of those 8 slots, which this lane loaded as
+    //    vw[2t + j/4][j%4] (MFMA e takes the dims 8n + e, n = 0..15).  A
+    //    fragment: P enters as two bf16 parts, p = hi + lo to 2^-16 relative
+    //    (hi: p truncated to bf16; lo: the rest, rounded), so the product keeps
+    //    fp32 accuracy: row 4h carries head h's hi part, row 4h + 1 its lo part.
+    //    Lane (n, h) ends with O[h][8n + e] = acc[e][0] + acc[e][1].
+    if (rq == 0) {
+#pragma unroll
+      for (int i = 0; i < TILES; ++i)
+#pragma unroll
+        for (int h = 0; h < G; ++h) s_pa[wave][h][i][n & 3][n >> 2] = lg[i][h];
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int ha = n >> 2;
+    const bool arow = (n & 3) < 2 && ha < G;
+    const bool lo_row = (n & 1) != 0;
+    const int hc = ha < G ? ha : G - 1;
+    f32x4_t acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < (TILES + 1) / 2; ++t) {
+      float pj[8];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int i = 2 * t + half;
+        float4 q4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (i < TILES)
+          q4 = *reinterpret_cast<const float4*>(&s_pa[wave][hc][i < TILES ? i : 0][rq][0]);
+        pj[4 * half + 0] = arow ? q4.x : 0.0f;
+        pj[4 * half + 1] = arow ? q4.y : 0.0f;
+        pj[4 * half + 2] = arow ? q4.z : 0.0f;
+        pj[4 * half + 3] = arow ? q4.w : 0.0f;
+      }
+      uint32_t af[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t b0 = __float_as_uint(pj[2 * d]);
+        const uint32_t b1 = __float_as_uint(pj[2 * d + 1]);
+        const uint32_t hi = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // truncated bf16 pair
+        f32x2_t rest = {pj[2 * d] - __uint_as_float(b0 & 0xffff0000u),
+                        pj[2 * d + 1] - __uint_as_float(b1 & 0xffff0000u)};
+        bf16x2_t lo2 = __builtin_convertvector(rest, bf16x2_t);
+        uint32_t lo;
+        __builtin_memcpy(&lo, &lo2, 4);
+        af[d] = lo_row ? lo : hi;
+      }
+      bf16x8_t a_p;
+      __builtin_memcpy(&a_p, af, 16);
+    const uint4 z = make_uint4(0, 0, 0, 0);
+      const uint4 v0 = vw[2 * t][0], v1 = vw[2 * t][1], v2 = vw[2 * t][2], v3 = vw[2 * t][3];
+      const uint4 v4 = 2 * t + 1 < TILES ? vw[2 * t + 1 < TILES ? 2 * t + 1 : 0][0] : z;
+      const uint4 v5 = 2 * t + 1 < TILES ? vw[2 * t + 1 < TILES ? 2 * t + 1 : 0][1] : z;
+      const uint4 v6 = 2 * t + 1 < TILES ? vw[2 * t + 1 < TILES ? 2 * t + 1 : 0][2] : z;
+      const uint4 v7 = 2 * t + 1 < TILES ? vw[2 * t + 1 < TILES ? 2 * t + 1 : 0][3] : z;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // word e/2 of each row holds dims 8n + 2(e/2) (low half) and +1 (high)
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        auto word = [&](const uint4& x) -> uint32_t {
+          return (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
+        };
+        uint32_t bw[4];
+        bw[0] = __builtin_amdgcn_perm(word(v1), word(v0), sel);
+        bw[1] = __builtin_amdgcn_perm(word(v3), word(v2), sel);
+        bw[2] = __builtin_amdgcn_perm(word(v5), word(v4), sel);
+        bw[3] = __builtin_amdgcn_perm(word(v7), word(v6), sel);
+        bf16x8_t bv;
+        __builtin_memcpy(&bv, bw, 16);
+        acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_p, bv, acc[e], 0, 0, 0);
+      }
+    }
+
+    // M and Lsum hold the row-0 reductions (valid in lanes 0..15): broadcast
+    // them from lane 0; row rq keeps head rq and merges the round into its
+    // running (max, sum, o)
+    float m_r = wave_bcast0(M[0]), l_r = wave_bcast0(Lsum[0]);
+#pragma unroll
+    for (int h = 1; h < G; ++h) {
+      const float mh = wave_bcast0(M[h]);
+      const float lh = wave_bcast0(Lsum[h]);
+      if (rq == h) {
+        m_r = mh;
+        l_r = lh;
+      }
+    }
+    const float m_new = fmaxf(m_me, m_r);
+    if (m_new != -INFINITY) {
+      const float so = __builtin_amdgcn_exp2f(m_me - m_new);
+      const float sr = __builtin_amdgcn_exp2f(m_r - m_new);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mine[e] = mine[e] * so + (acc[e][0] + acc[e][1]) * sr;
+      l_me = l_me * so + l_r * sr;
+      m_me = m_new;
+    }
+  }  // rounds
   if (nw > 1) {
     // merge the workgroup's waves in LDS (log-sum-exp); thread t of the
     // workgroup then owns output (head t / D, dim t % D)
@@ -658,104 +565,6 @@ __global__ __launch_bounds__(64 * kMaxSparseWaves) void attend_sparse_kernel(Att
   }
 }
 
-
-template <int G, int MODE, int WPW>
-__global__ __launch_bounds__(64 * WPW) void attend_wave_kernel(AttendArgs a) {
-  static_assert(G >= 1 && G <= 4, "query heads of a group fit MFMA rows 0..3");
-  constexpr int D = 128;
-  __shared__ float s_p[WPW][16][4];
-  __shared__ float s_o[WPW > 1 ? WPW : 1][G][D];
-  __shared__ float s_ml[WPW > 1 ? WPW : 1][2][G];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int n = lane & 15;
-  const int rq = lane >> 4;
-  const int row = blockIdx.y;
-  const int split = blockIdx.x;
-  const int b = row / a.Hkv;
-  const int r = row % a.Hkv;
-
-  bf16x8_t qa[4];
-  load_q_frag<G>(a, b, r, n, rq, qa);
-
-  const int64_t kv_off = ((int64_t)b * a.sb + (int64_t)r * a.sh) * 2;
-  const uint8_t* kbase = a.k + kv_off + 16 * rq;
-  const uint8_t* vbase = a.v + kv_off + 16 * n;
-  const int64_t row_bytes = a.st * 2;
-
-  float m_run[G], l_run[G], o[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m_run[h] = -INFINITY;
-    l_run[h] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[h][e] = 0.0f;
-  }
-
-  const int64_t s0 = (int64_t)split * a.chunk;
-  const int64_t s1 = min(s0 + (int64_t)a.chunk, a.n_slots);
-  // tiles of this wave: wave, wave + WPW, ... inside [s0, s1); the next tile's
-  // loads are in flight while the current one computes
-  const int64_t n_tiles = (s1 - s0 + 15) / 16;
-
-  TileLoads cur, nxt;
-  int64_t t = wave;
-  if (t < n_tiles) load_tile<MODE>(a, row, b, s0 + 16 * t, s1, n, rq, kbase, vbase, row_bytes, cur);
-  for (; t < n_tiles; t += WPW) {
-    const bool more = t + WPW < n_tiles;  // wave-uniform
-    if (more)
-      load_tile<MODE>(a, row, b, s0 + 16 * (t + WPW), s1, n, rq, kbase, vbase, row_bytes, nxt);
-
-    tile_step<G>(cur, qa, a.qscale, n, rq, s_p[wave], m_run, l_run, o);
-    if (more) cur = nxt;
-  }
-
-  reduce_rows<G>(o);
-
-  if constexpr (WPW == 1) {
-    if (rq == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          write_result<G, D>(a, row, split, b, r, h, 8 * n + e, o[h][e], m_run[h], l_run[h]);
-    }
-  } else {
-    if (rq == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s_o[wave][h][8 * n + e] = o[h][e];
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        s_ml[wave][0][h] = m_run[h];
-        s_ml[wave][1][h] = l_run[h];
-      }
-    }
-    __syncthreads();
-    for (int x = tid; x < G * D; x += 64 * WPW) {
-      const int h = x / D;
-      const int dim = x % D;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < WPW; ++w) M = fmaxf(M, s_ml[w][0][h]);
-      float L = 0.0f, O = 0.0f;
-      if (M != -INFINITY) {
-#pragma unroll
-        for (int w = 0; w < WPW; ++w) {
-          const float wt = exp2f(s_ml[w][0][h] - M);
-          L = fmaf(s_ml[w][1][h], wt, L);
-          O = fmaf(s_o[w][h][dim], wt, O);
-        }
-      }
-      write_result<G, D>(a, row, split, b, r, h, dim, O, M, L);
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Combine: one workgroup of D threads per (row, query head); thread = one
@@ -835,26 +644,6 @@ hipError_t dispatch_group(int G, int mode, dim3 grid, const AttendArgs& a, hipSt
   }
 }
 
-template <int G, int WPW>
-hipError_t dispatch_wave_mode(int mode, dim3 grid, const AttendArgs& a, hipStream_t s) {
-  const dim3 block(64 * WPW);
-  switch (mode) {
-    case kIdxTokenPerHead:
-      hipLaunchKernelGGL((attend_wave_kernel<G, kIdxTokenPerHead, WPW>), grid, block, 0, s, a);
-      break;
-    case kIdxTokenShared:
-      hipLaunchKernelGGL((attend_wave_kernel<G, kIdxTokenShared, WPW>), grid, block, 0, s, a);
-      break;
-    case kIdxBlockPerHead:
-      hipLaunchKernelGGL((attend_wave_kernel<G, kIdxBlockPerHead, WPW>), grid, block, 0, s, a);
-      break;
-    default:
-      hipLaunchKernelGGL((attend_wave_kernel<G, kIdxDense, WPW>), grid, block, 0, s, a);
-      break;
-  }
-  return hipGetLastError();
-}
-
 template <int G, int TILES>
 hipError_t dispatch_sparse(int waves, int mode, dim3 grid, const AttendArgs& a, hipStream_t s) {
   const dim3 block(64 * waves);
@@ -865,20 +654,22 @@ hipError_t dispatch_sparse(int waves, int mode, dim3 grid, const AttendArgs& a, 
     case kIdxTokenShared:
       hipLaunchKernelGGL((attend_sparse_kernel<G, kIdxTokenShared, TILES>), grid, block, 0, s, a);
       break;
-    default:
+    case kIdxBlockPerHead:
       hipLaunchKernelGGL((attend_sparse_kernel<G, kIdxBlockPerHead, TILES>), grid, block, 0, s, a);
+      break;
+    default:
+      hipLaunchKernelGGL((attend_sparse_kernel<G, kIdxDense, TILES>), grid, block, 0, s, a);
       break;
   }
   return hipGetLastError();
 }
 
-// Dense decode takes the four-wave streaming kernel; selected sets take the
-// gather kernel with `waves` waves of chunk / waves slots each.
+// The gather kernel with `waves` waves of chunk / (waves * rounds) slots per
+// round.
 template <int G>
-hipError_t dispatch_wave(int waves, int chunk, int mode, dim3 grid, const AttendArgs& a,
-                         hipStream_t s) {
-  if (mode == kIdxDense) return dispatch_wave_mode<G, 4>(mode, grid, a, s);
-  const int per_wave = chunk / waves;
+hipError_t dispatch_wave(int waves, int rounds, int chunk, int mode, dim3 grid,
+                         const AttendArgs& a, hipStream_t s) {
+  const int per_wave = chunk / (waves * rounds);
   if (per_wave <= 16) return dispatch_sparse<G, 1>(waves, mode, grid, a, s);
   if (per_wave <= 32) return dispatch_sparse<G, 2>(waves, mode, grid, a, s);
   if (per_wave <= 48) return dispatch_sparse<G, 3>(waves, mode, grid, a, s);
@@ -911,6 +702,17 @@ int sparse_waves_override() {
   return v;
 }
 
+// Dense decode: SA_DENSE_WAVES (1 to 12) and SA_DENSE_ROUNDS (1 to 64).
+int dense_waves_override() {
+  static const int v = env_choice("SA_DENSE_WAVES", {1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12});
+  return v;
+}
+
+int dense_rounds_override() {
+  static const int v = env_choice("SA_DENSE_ROUNDS", {1, 2, 4, 8, 16, 32, 64});
+  return v;
+}
+
 int lanes_per_row(const Cache& c) { return c.D * (c.kv_dtype == SA_BF16 ? 2 : 4) / 16; }
 
 }  // namespace
@@ -929,12 +731,15 @@ AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs) {
   int64_t chunk;
   if (use_wave_kernel(c)) {
     if (mode == kIdxDense) {
-      // four-wave workgroups over contiguous token ranges; about 2048
-      // workgroups in total, at most 1024 splits per row
-      p.waves = 4;
-      chunk = (rows * p.n_slots + 2047) / 2048;
-      chunk = std::max<int64_t>(256, (chunk + 63) / 64 * 64);
-      while ((p.n_slots + chunk - 1) / chunk > 1024) chunk *= 2;
+      // contiguous tokens through the gather kernel: waves of 64 tokens per
+      // round, several rounds per wave merged online, so a workgroup covers
+      // waves * rounds * 64 tokens and few split partials are written
+      // (measured on 128 rows of 32768 tokens: 4 waves x 8 rounds, 2048
+      // tokens per workgroup, 323 us + 6 us combine, against 328-340 us for
+      // 4 x 4, 8 x 4 and 8 x 8)
+      p.waves = dense_waves_override() ? dense_waves_override() : 4;
+      p.rounds = dense_rounds_override() ? dense_rounds_override() : 8;
+      chunk = (int64_t)64 * p.waves * p.rounds;
     } else {
       // Each wave gathers up to 64 slots with every load in flight at once;
       // the waves of a workgroup merge in LDS.  With at least 128 rows (half
@@ -971,10 +776,12 @@ AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs) {
       if (sparse_waves_override()) waves = sparse_waves_override();
       if (sparse_chunk_override()) per_wave = sparse_chunk_override();
       p.waves = waves;
+      p.rounds = 1;
       chunk = per_wave * waves;
     }
   } else {
     p.waves = 4;
+    p.rounds = 1;
     const int64_t unit = (int64_t)(kThreads / lanes_per_row(c)) * kUnroll;
     chunk = (rows * p.n_slots + 4095) / 4096;
     chunk = (chunk + unit - 1) / unit * unit;
@@ -1008,6 +815,7 @@ hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, con
   a.n_slots = p.n_slots;
   a.chunk = p.chunk;
   a.nsplit = p.nsplit;
+  a.rounds = p.rounds;
   a.out = out;
   a.part = static_cast<float*>(ws);
   const int64_t rows = (int64_t)c.B * c.Hkv;
@@ -1015,9 +823,9 @@ hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, con
   hipError_t e;
   if (use_wave_kernel(c)) {
     switch (c.G) {
-      case 1: e = dispatch_wave<1>(p.waves, p.chunk, p.mode, grid, a, s); break;
-      case 2: e = dispatch_wave<2>(p.waves, p.chunk, p.mode, grid, a, s); break;
-      default: e = dispatch_wave<4>(p.waves, p.chunk, p.mode, grid, a, s); break;
+      case 1: e = dispatch_wave<1>(p.waves, p.rounds, p.chunk, p.mode, grid, a, s); break;
+      case 2: e = dispatch_wave<2>(p.waves, p.rounds, p.chunk, p.mode, grid, a, s); break;
+      default: e = dispatch_wave<4>(p.waves, p.rounds, p.chunk, p.mode, grid, a, s); break;
     }
   } else if (c.kv_dtype == SA_BF16) {
     e = c.D == 64 ? dispatch_group<bf16_t, 64>(c.G, p.mode, grid, a, s)
@@ -1029,7 +837,7 @@ hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, con
   if (e != hipSuccess || p.nsplit == 1) return e;
   const dim3 cgrid((unsigned)rows, (unsigned)c.G);
   // one-wave selected-set workgroups write the interleaved partial layout
-  const bool vec_layout = use_wave_kernel(c) && p.mode != kIdxDense && p.waves == 1;
+  const bool vec_layout = use_wave_kernel(c) && p.waves == 1;
   if (c.D == 64)
     hipLaunchKernelGGL(combine_kernel<64>, cgrid, dim3(64), 0, s, a.part, p.nsplit, c.G, c.Hq, c.Hkv,
                        out, vec_layout);

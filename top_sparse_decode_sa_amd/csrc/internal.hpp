@@ -42,6 +42,7 @@ struct AttendPlan {
   int32_t chunk;    // slots per workgroup
   int32_t nsplit;   // workgroups per row
   int32_t waves;    // waves per workgroup
+  int32_t rounds;   // slot rounds per wave (gather kernel)
   size_t ws_bytes;  // split partials (0 when nsplit == 1)
 };
 
