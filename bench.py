@@ -54,8 +54,13 @@ def parse():
     p.add_argument("--profile", action="store_true",
                    help="short run for a profiler: few steps, no dense, no cpu baseline, plus "
                         "three 1 GiB device-to-device copies that calibrate HBM byte counters")
+    p.add_argument("--cold-iters", type=int, default=30,
+                   help="cache-cold gather-attend launches timed after the steps (0 disables)")
     p.add_argument("--summarize", metavar="DB",
                    help="print a per-kernel summary of a rocprofv3 results database and exit")
+    p.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                   help="print the calibrated HBM traffic per dispatch from two rocprofv3 --pmc "
+                        "runs of `bench.py --profile` (FETCH_SIZE, then WRITE_SIZE) and exit")
     return p.parse_args()
 
 
@@ -64,11 +69,19 @@ def parse():
 # ---------------------------------------------------------------------------
 
 COPY_BYTES = 1 << 30
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_exact_llama32k_traffic.txt")
-TRAFFIC_SOURCES = ["top_sparse_decode_sa_amd/csrc/score.hip", "top_sparse_decode_sa_amd/csrc/common.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "llama32k_hbm_traffic.txt")
+# kernel -> (name fragment in the trace, sources whose hash the counters belong to)
+TRAFFIC_KERNELS = {
+    "score_exact": ("score_exact_kernel", ["top_sparse_decode_sa_amd/csrc/score.hip",
+                                           "top_sparse_decode_sa_amd/csrc/common.hpp"]),
+    "sparse_attend": ("attend_sparse_kernel", ["top_sparse_decode_sa_amd/csrc/attend.hip",
+                                               "top_sparse_decode_sa_amd/csrc/common.hpp"]),
+    "topk": ("topk_kernel", ["top_sparse_decode_sa_amd/csrc/topk.hip",
+                             "top_sparse_decode_sa_amd/csrc/common.hpp"]),
+}
 
 
-def source_hash(paths=TRAFFIC_SOURCES):
+def source_hash(paths):
     import hashlib
     h = hashlib.sha256()
     for p in paths:
@@ -87,9 +100,8 @@ def summarize(db_path):
     for name, n, avg, mn, mx in rows:
         lines.append("%-70s %6d %10.2f %10.2f %10.2f" % (name[:70], n, avg / 1e3, mn / 1e3, mx / 1e3))
     try:
-        pmc = db.execute("select k.name, p.counter_name, avg(p.value), count(*) from kernels k "
-                         "join pmc_events p on p.event_id = k.event_id "
-                         "group by k.name, p.counter_name").fetchall()
+        pmc = db.execute("select kernel_name, counter_name, avg(value), count(*) "
+                         "from counters_collection group by kernel_name, counter_name").fetchall()
     except Exception:
         pmc = []
     counters = {}
@@ -102,19 +114,81 @@ def summarize(db_path):
     return "\n".join(lines), rows, counters
 
 
-def read_traffic():
-    """Measured HBM bytes per score_exact launch, if measured on this source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def pmc_means(db_path, counter):
+    """Per-kernel-name mean of one counter per dispatch (KiB for the byte
+    counters) and the dispatch count."""
+    import sqlite3
+    db = sqlite3.connect(db_path)
+    rows = db.execute("select kernel_name, avg(value), count(*) from counters_collection "
+                      "where counter_name = ? group by kernel_name", (counter,)).fetchall()
+    return {name: (val, n) for name, val, n in rows}
+
+
+def traffic_report(fetch_db, write_db):
+    """HBM bytes per dispatch of the step's kernels.  FETCH_SIZE and
+    WRITE_SIZE are scaled by what they read for the calibration copies that
+    `bench.py --profile` runs (1 GiB read and 1 GiB written each)."""
+    fetch = pmc_means(fetch_db, "FETCH_SIZE")
+    write = pmc_means(write_db, "WRITE_SIZE")
+    copy = [n for n in fetch if "copyBuffer" in n]
+    if not copy:
+        raise SystemExit("no calibration copy in %s" % fetch_db)
+    ff = COPY_BYTES / (fetch[copy[0]][0] * 1024.0)
+    wf = COPY_BYTES / (write[copy[0]][0] * 1024.0)
+    c = None
+    try:
+        import sa_synth as S
+        c = S.CONFIGS["llama32k"]
+    except Exception:
+        pass
+    alg = step_bytes(c) if c is not None else {}
+    lines = ["# HBM traffic per dispatch, calibrated byte counters",
+             "#",
+             "# commands (one counter per run, then this report):",
+             "#   rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof_fetch -o fetch -- "
+             "python -u bench.py --profile",
+             "#   rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof_write -o write -- "
+             "python -u bench.py --profile",
+             "#   python bench.py --traffic gpurun_out/prof_fetch/fetch_results.db "
+             "gpurun_out/prof_write/write_results.db",
+             "# bench.py --profile runs three 1 GiB device-to-device copies that read and write",
+             "# exactly 1073741824 bytes each; factor = 1073741824 / (counter KiB of a copy * 1024)",
+             "#",
+             "%-70s %6s %14s %14s %14s" % ("kernel", "n", "FETCH_KiB", "WRITE_KiB", "bytes(calib.)")]
+    for name in sorted(fetch, key=lambda n: -fetch[n][0]):
+        fk, n = fetch[name]
+        wk = write.get(name, (0.0, 0))[0]
+        lines.append("%-70s %6d %14.1f %14.1f %14d" % (name[:70], n, fk, wk,
+                                                        round(fk * 1024 * ff + wk * 1024 * wf)))
+    lines += ["", "fetch_factor: %.6f" % ff, "write_factor: %.6f" % wf]
+    for key, (frag, srcs) in TRAFFIC_KERNELS.items():
+        names = [n for n in fetch if frag in n]
+        if not names:
+            continue
+        name = max(names, key=lambda n: fetch[n][1])
+        t = round(fetch[name][0] * 1024 * ff + write.get(name, (0.0, 0))[0] * 1024 * wf)
+        lines.append("%s.traffic_bytes_per_launch: %d" % (key, t))
+        if key in alg:
+            lines.append("%s.algorithmic_bytes_per_launch: %d" % (key, alg[key]))
+            lines.append("%s.traffic_over_algorithmic: %.4f" % (key, t / alg[key]))
+        lines.append("%s.source_sha256_16: %s" % (key, source_hash(srcs)))
+    return "\n".join(lines)
+
+
+def read_traffic(kernel):
+    """Measured HBM bytes per launch of `kernel`, if its counters were taken on
+    the current source (null otherwise)."""
+    if kernel not in TRAFFIC_KERNELS or not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
     for line in open(TRAFFIC_FILE):
         if ":" in line and not line.startswith("#"):
             a, b = line.split(":", 1)
             kv[a.strip()] = b.strip()
-    if kv.get("source_sha256_16") != source_hash():
+    if kv.get(kernel + ".source_sha256_16") != source_hash(TRAFFIC_KERNELS[kernel][1]):
         return None  # the kernel changed since the counters were taken
     try:
-        return int(kv["traffic_bytes_per_launch"])
+        return int(kv[kernel + ".traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -169,12 +243,16 @@ def main():
     if args.summarize:
         print(summarize(args.summarize)[0])
         return
+    if args.traffic:
+        print(traffic_report(*args.traffic))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     if args.profile:
         args.steps, args.warmup, args.cpu_seconds, args.dense_steps = 20, 5, 0.0, 0
+        args.cold_iters = 0
 
     import torch
     import sa_synth as S
@@ -260,6 +338,33 @@ def main():
         torch.cuda.synchronize()
         ms_dense = e0.elapsed_time(e1) / args.dense_steps
 
+    # cache-cold gather-attend: before each launch a 1 GiB read evicts L2 and
+    # the 256 MB last-level cache, as other layers' traffic would between
+    # decode steps; beside it, the same kernel over the same number of bytes
+    # read contiguously (a dense decode of the first k tokens of every row),
+    # the cold-read floor at this size
+    cold = None
+    if args.cold_iters > 0:
+        flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+        kpre, vpre = kd[:, :, :c.k], vd[:, :, :c.k]
+        cout = torch.empty_like(out)
+        times = {"sparse": [], "contig": []}
+        for i in range(args.cold_iters + 2):
+            for name in ("sparse", "contig"):
+                flush.sum()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                if name == "sparse":
+                    T.sa_sparse_decode(qd[0], kd, vd, idx, out=cout)
+                else:
+                    T.sa_dense_decode(qd[0], kpre, vpre, out=cout)
+                e1.record()
+                torch.cuda.synchronize()
+                if i >= 2:
+                    times[name].append(e0.elapsed_time(e1))
+        del flush
+        cold = {name: float(np.median(v)) for name, v in times.items()}
+
     nbytes = step_bytes(c)
     step_total = nbytes["score_exact"] + nbytes["topk"] + nbytes["sparse_attend"]
     gbps = step_total / (ms_step * 1e-3) / 1e9
@@ -274,11 +379,14 @@ def main():
     kernels = {"score_exact": kern("score_exact", ms_score), "topk": kern("topk", ms_topk),
                "sparse_attend": kern("sparse_attend", ms_attend),
                "dense_decode": kern("dense_decode", ms_dense)}
+    if cold:
+        kernels["sparse_attend_cold"] = kern("sparse_attend", cold["sparse"])
+        kernels["contiguous_same_bytes_cold"] = kern("sparse_attend", cold["contig"])
     # dominant kernel of the step: the one with the largest share of its time
     dom = max(["score_exact", "topk", "sparse_attend"], key=lambda n: kernels[n]["us"])
     roof = {"bound": "hbm", "achieved": kernels[dom]["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": kernels[dom]["frac"],
-            "traffic": read_traffic() if dom == "score_exact" else None, "kernel": dom,
+            "traffic": read_traffic(dom), "kernel": dom,
             "bytes_per_launch": nbytes[dom]}
 
     cpu = None

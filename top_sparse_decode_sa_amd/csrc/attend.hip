@@ -730,55 +730,52 @@ AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs) {
   const int64_t rows = (int64_t)c.B * c.Hkv;
   int64_t chunk;
   if (use_wave_kernel(c)) {
-    if (mode == kIdxDense) {
-      // contiguous tokens through the gather kernel: waves of 64 tokens per
-      // round, several rounds per wave merged online, so a workgroup covers
-      // waves * rounds * 64 tokens and few split partials are written
-      // (measured on 128 rows of 32768 tokens: 4 waves x 8 rounds, 2048
-      // tokens per workgroup, 323 us + 6 us combine, against 328-340 us for
-      // 4 x 4, 8 x 4 and 8 x 8)
-      p.waves = dense_waves_override() ? dense_waves_override() : 4;
-      p.rounds = dense_rounds_override() ? dense_rounds_override() : 8;
-      chunk = (int64_t)64 * p.waves * p.rounds;
-    } else {
-      // Each wave gathers up to 64 slots with every load in flight at once;
-      // the waves of a workgroup merge in LDS.  With at least 128 rows (half
-      // the chip's CUs at one workgroup each) and at most 12 waves' worth of
-      // slots, one workgroup takes a whole row: no split partials and no
-      // combine launch (on 128 rows of 655 slots, 14.6 us against 14.2 us +
-      // 4.5 us for one-wave splits and their combine).  Otherwise rows are
-      // split so that about 512 workgroups (two per CU) run, and a combine
-      // pass merges the splits.
-      const int64_t wn = (p.n_slots + 63) / 64;
-      int waves = 1;
-      int64_t per_wave = 64;
-      if (rows >= 128 && wn <= kMaxSparseWaves) {
-        // the fewest slots per wave (32, 48 or 64) that still fit: more,
-        // shorter waves finish sooner (measured on 1024 rows of 262 slots:
-        // 9 x 32 beats 5 x 64 by 10 %)
-        for (int pw : {32, 48, 64}) {
-          if ((p.n_slots + pw - 1) / pw <= kMaxSparseWaves) {
-            per_wave = pw;
-            break;
-          }
+    // Each wave takes rounds of up to 64 slots with every load of a round in
+    // flight at once; the waves of a workgroup merge in LDS.
+    const int64_t wn = (p.n_slots + 63) / 64;
+    int waves = 1, rounds = 1;
+    int64_t per_wave = 64;
+    if (rows >= 128 && wn <= kMaxSparseWaves) {
+      // At least 128 rows (half the chip's CUs at one workgroup each) and at
+      // most 12 waves' worth of slots: one workgroup takes a whole row in one
+      // round, so no split partials and no combine launch (on 128 rows of
+      // 655 slots, 14.6 us against 14.2 us + 4.5 us for one-wave splits and
+      // their combine).  The fewest slots per wave (32, 48 or 64) that still
+      // fit: more, shorter waves finish sooner (on 1024 rows of 262 slots,
+      // 9 x 32 beats 5 x 64 by 10 %).
+      for (int pw : {32, 48, 64}) {
+        if ((p.n_slots + pw - 1) / pw <= kMaxSparseWaves) {
+          per_wave = pw;
+          break;
         }
-        waves = (int)((p.n_slots + per_wave - 1) / per_wave);
-      } else {
-        for (int w : {12, 8, 4}) {
-          if (rows * ((wn + w - 1) / w) >= 512) {
-            waves = w;
-            break;
-          }
-        }
-        if (waves == 1)
-          while (per_wave > 16 && rows * ((p.n_slots + per_wave - 1) / per_wave) < 512) per_wave /= 2;
       }
+      waves = (int)((p.n_slots + per_wave - 1) / per_wave);
+    } else if (mode == kIdxDense) {
+      // long contiguous scans: several rounds per wave merged online, so a
+      // workgroup covers waves * rounds * 64 tokens and few split partials
+      // are written (on 128 rows of 32768 tokens, 4 waves x 8 rounds: 323 us
+      // + 6 us combine, against 328-340 us for 4 x 4, 8 x 4 and 8 x 8)
+      waves = dense_waves_override() ? dense_waves_override() : 4;
+      rounds = dense_rounds_override() ? dense_rounds_override() : 8;
+    } else {
+      // selections split so that about 512 workgroups (two per CU) run; a
+      // combine pass merges the splits
+      for (int w : {12, 8, 4}) {
+        if (rows * ((wn + w - 1) / w) >= 512) {
+          waves = w;
+          break;
+        }
+      }
+      if (waves == 1)
+        while (per_wave > 16 && rows * ((p.n_slots + per_wave - 1) / per_wave) < 512) per_wave /= 2;
+    }
+    if (mode != kIdxDense) {
       if (sparse_waves_override()) waves = sparse_waves_override();
       if (sparse_chunk_override()) per_wave = sparse_chunk_override();
-      p.waves = waves;
-      p.rounds = 1;
-      chunk = per_wave * waves;
     }
+    p.waves = waves;
+    p.rounds = rounds;
+    chunk = per_wave * waves * rounds;
   } else {
     p.waves = 4;
     p.rounds = 1;
