@@ -58,6 +58,11 @@ def parse():
                    help="cache-cold gather-attend launches timed after the steps (0 disables)")
     p.add_argument("--summarize", metavar="DB",
                    help="print a per-kernel summary of a rocprofv3 results database and exit")
+    p.add_argument("--sweep", action="store_true",
+                   help="indexer-inclusive break-even sweep: full step (exact scores or a "
+                        "per-KV-head low-dim indexer, then top-k and attend) against dense decode "
+                        "at 2x-500x sparsity on the llama32k and batch128k shapes; prints a table "
+                        "and one JSON line")
     p.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                    help="print the calibrated HBM traffic per dispatch from two rocprofv3 --pmc "
                         "runs of `bench.py --profile` (FETCH_SIZE, then WRITE_SIZE) and exit")
@@ -238,6 +243,132 @@ def cpu_baseline(w, q_host, k_host, v_host, seconds):
     return dt * rows / rows_done, rows_done, rows
 
 
+SWEEP_X = (2, 5, 10, 20, 50, 100, 200, 500)
+IDX_HEADS, IDX_DIM = 4, 64
+
+
+def sweep(args):
+    """Full decode step against dense decode across sparsity.
+
+    Two selection front ends feed the same top-k and gather-attend: exact
+    scores (every key row read) and a per-KV-head lightning indexer (keys
+    projected to 64 dims, 4 indexer heads = the KV head's 4 grouped queries
+    projected the same way, weights U(0,1)), which reads a quarter of the
+    key bytes.  The llama32k shape uses the seeded workload; batch128k (68.7
+    GB of K/V) is drawn N(0,1) on the device, since only the selection sizes,
+    not the values, drive the timings there."""
+    import torch
+    import sa_synth as S
+    import top_sparse_decode_sa_amd as T
+
+    T.lib()
+    dev = torch.device("cuda", 0)
+    reps = max(3, min(args.steps, 10))
+    results = []
+
+    def timed(fn, n, blocker=None):
+        # a long kernel ahead of the timed launches lets the host queue them
+        # all before the GPU reaches them, so host-side call overhead does
+        # not show up as idle GPU time between short kernels
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        if blocker is not None:
+            blocker()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3  # us
+
+    for shape in ("llama32k", "batch128k"):
+        c = S.CONFIGS[shape]
+        B, Hq, Hkv, d, N = c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.ctx_len
+        G = Hq // Hkv
+        log("sweep: %s inputs" % shape)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed)
+        if shape == "llama32k":
+            w = S.Workload(shape, args.seed)
+
+            def up(x):
+                t = torch.from_numpy(x)
+                return (t.view(torch.bfloat16) if t.dtype == torch.uint16 else t).to(dev)
+
+            q, kd, vd = up(w.q()), up(w.k()), up(w.v())
+            data = "seeded workload (planted heavy keys)"
+        else:
+            q = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev).normal_(generator=gen)
+            kd = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=dev).normal_(generator=gen)
+            vd = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=dev).normal_(generator=gen)
+            data = "N(0,1) drawn on the device"
+        # per-KV-head indexer inputs (projection P [64, d], N(0, 1/d) entries)
+        P = torch.randn((IDX_DIM, d), generator=gen, device=dev) / d ** 0.5
+        k_idx = torch.empty((B, Hkv, N, IDX_DIM), dtype=torch.bfloat16, device=dev)
+        for b in range(B):
+            kb = kd[b].float() @ P.t()
+            kb += 0.1 * torch.randn(kb.shape, generator=gen, device=dev)
+            k_idx[b] = kb.to(torch.bfloat16)
+            del kb
+        q_idx = (q.float().view(B, Hkv, G, d)[:, :, :IDX_HEADS] @ P.t()).to(torch.bfloat16).contiguous()
+        idx_w = torch.rand((B, Hkv, IDX_HEADS), generator=gen, device=dev)
+        scores = torch.empty((B, Hkv, N), dtype=torch.float32, device=dev)
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+
+        def dense():
+            T.sa_dense_decode(q, kd, vd, out=out)
+
+        us_dense = timed(dense, reps)
+        dense_bytes = 2 * B * Hkv * N * d * 2
+        for x in SWEEP_X:
+            k = N // x
+            idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+
+            def exact_score():
+                T.sa_score(q, kd, T.SA_SCORE_EXACT, scores=scores)
+
+            def idx_score():
+                T.sa_score(q, kd, T.SA_SCORE_INDEXER_PER_KV_HEAD, q_idx=q_idx, k_idx=k_idx,
+                           idx_w=idx_w, scores=scores)
+
+            def select():
+                T.sa_topk(scores, k, idx_out=idx)
+
+            def attend():
+                T.sa_sparse_decode(q, kd, vd, idx, out=out)
+
+            row = {"shape": shape, "x": x, "k": k, "dense_us": round(us_dense, 1)}
+            row["exact_score_us"] = round(timed(exact_score, reps, dense), 1)
+            row["indexer_us"] = round(timed(idx_score, reps, dense), 1)
+            row["topk_us"] = round(timed(select, reps, dense), 1)
+            row["attend_us"] = round(timed(attend, reps, dense), 1)
+            row["exact_step_us"] = round(timed(lambda: (exact_score(), select(), attend()), reps,
+                                               dense), 1)
+            row["indexer_step_us"] = round(timed(lambda: (idx_score(), select(), attend()), reps,
+                                                 dense), 1)
+            row["attend_only_speedup"] = round(us_dense / row["attend_us"], 2)
+            row["exact_step_speedup"] = round(us_dense / row["exact_step_us"], 2)
+            row["indexer_step_speedup"] = round(us_dense / row["indexer_step_us"], 2)
+            row["attend_gbps"] = round((2 * B * Hkv * k * d * 2) / row["attend_us"] / 1e3, 1)
+            row["data"] = data
+            results.append(row)
+            log("sweep: %s x=%d done" % (shape, x))
+        log("sweep: %s dense %.1f us (%.0f GB/s)" % (shape, us_dense, dense_bytes / us_dense / 1e3))
+        del q, kd, vd, k_idx, q_idx, idx_w, scores, out
+        torch.cuda.empty_cache()
+
+    cols = ["shape", "x", "k", "dense_us", "exact_score_us", "indexer_us", "topk_us", "attend_us",
+            "exact_step_us", "indexer_step_us", "attend_only_speedup", "exact_step_speedup",
+            "indexer_step_speedup", "attend_gbps"]
+    print("  ".join("%12s" % c_ for c_ in cols))
+    for r in results:
+        print("  ".join("%12s" % r[c_] for c_ in cols))
+    print(json.dumps({"sweep": "indexer-inclusive break-even", "unit": "us per step (HIP events)",
+                      "rows": results, "device": torch.cuda.get_device_name(0)}), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -245,6 +376,9 @@ def main():
         return
     if args.traffic:
         print(traffic_report(*args.traffic))
+        return
+    if args.gpus == 1 and args.sweep:
+        sweep(args)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

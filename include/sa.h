@@ -104,7 +104,15 @@ typedef enum {
   /* Low-dimensional indexer: [P5] DSA Stage 1.
    *   scores[b, t] = sum_{h < n_idx_heads} w[b, h] * max(0, q_idx[b, h, :] . k_idx[b, t, :])
    * Output [batch, ctx_len] fp32 (one row per sequence, shared by its KV heads). */
-  SA_SCORE_INDEXER = 2
+  SA_SCORE_INDEXER = 2,
+  /* The same indexer form with one indexer per KV head, so selection is per
+   * (sequence, KV head) as for SA_SCORE_EXACT:
+   *   scores[b, r, t] = sum_{h < n_idx_heads} w[b, r, h] *
+   *                     max(0, q_idx[b, r, h, :] . k_idx[b, r, t, :])
+   * q_idx [batch, n_kv_heads, n_idx_heads, idx_dim] bf16, k_idx [batch,
+   * n_kv_heads, ctx_len, idx_dim] bf16, w [batch, n_kv_heads, n_idx_heads]
+   * fp32, all contiguous.  Output [batch, n_kv_heads, ctx_len] fp32. */
+  SA_SCORE_INDEXER_PER_KV_HEAD = 3
 } sa_score_kind;
 
 typedef struct {
@@ -194,8 +202,9 @@ typedef enum {
 } sa_layer_mode;
 
 /* Everything one layer's decode step needs.  The score kind fixes the index
- * kind: EXACT -> SA_IDX_TOKEN_PER_KV_HEAD, BLOCK_MINMAX ->
- * SA_IDX_BLOCK_PER_KV_HEAD (aux.block_size), INDEXER -> SA_IDX_TOKEN_SHARED.
+ * kind: EXACT and INDEXER_PER_KV_HEAD -> SA_IDX_TOKEN_PER_KV_HEAD,
+ * BLOCK_MINMAX -> SA_IDX_BLOCK_PER_KV_HEAD (aux.block_size), INDEXER ->
+ * SA_IDX_TOKEN_SHARED.
  * k is the number of tokens (blocks for BLOCK_MINMAX) kept per row. */
 typedef struct {
   sa_kv_desc desc;

@@ -109,8 +109,11 @@ def test_score_and_summary_errors():
     assert L.sa_score(ctypes.byref(d), 1, FAKE, FAKE, None, FAKE, None) == Bn.SA_ERR_NULL
     aux.block_size = 0
     assert L.sa_score(ctypes.byref(d), 1, FAKE, FAKE, ctypes.byref(aux), FAKE, None) == Bn.SA_ERR_SHAPE
+    assert L.sa_score(ctypes.byref(d), Bn.SA_SCORE_INDEXER_PER_KV_HEAD, FAKE, FAKE, None, FAKE,
+                      None) == Bn.SA_ERR_NULL
     aux.n_idx_heads, aux.idx_dim = 17, 64
     assert L.sa_score(ctypes.byref(d), 2, FAKE, FAKE, ctypes.byref(aux), FAKE, None) == Bn.SA_ERR_SHAPE
+    assert L.sa_score(ctypes.byref(d), 3, FAKE, FAKE, ctypes.byref(aux), FAKE, None) == Bn.SA_ERR_SHAPE
     aux.n_idx_heads, aux.idx_dim = 4, 48
     assert L.sa_score(ctypes.byref(d), 2, FAKE, FAKE, ctypes.byref(aux), FAKE, None) == \
         Bn.SA_ERR_UNSUPPORTED

@@ -131,6 +131,65 @@ def test_score_indexer(H, Di):
         assert np.max(np.abs(s[b] - want)) <= score_tol(want)
 
 
+@pytest.mark.parametrize("N,k", [(3001, 60), (8192, 17)])
+def test_indexer_per_kv_head_layer(N, k):
+    """The indexer applied per (sequence, KV head): scores against the oracle
+    row by row, then one SPARSE layer through sa_decode_layer (indexer ->
+    top-k -> attend) judged on its index sets and outputs."""
+    say("indexer per KV head", N, k)
+    B, Hq, Hkv, d, H, Di = 2, 8, 2, 128, 4, 64
+    rng = np.random.default_rng(N + k)
+    q, kc, vc = _rand_cache(B, Hq, Hkv, N, d, "bf16", 31)
+    qi = torch.from_numpy(rng.standard_normal((B, Hkv, H, Di)).astype(np.float32)).to(torch.bfloat16)
+    ki = torch.from_numpy(rng.standard_normal((B, Hkv, N, Di)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy(rng.uniform(size=(B, Hkv, H)).astype(np.float32))
+    qd, kd, vd = q.to(dev()), kc.to(dev()), vc.to(dev())
+    qid, kid, wd = qi.to(dev()), ki.to(dev()), w.to(dev())
+    s = T.sa_score(qd, kd, T.SA_SCORE_INDEXER_PER_KV_HEAD, q_idx=qid, k_idx=kid,
+                   idx_w=wd).cpu().numpy()
+    want = np.empty((B, Hkv, N))
+    for b in range(B):
+        for r in range(Hkv):
+            want[b, r] = O.scores_indexer(_f64(qi)[b, r], _f64(ki)[b, r],
+                                          w.numpy()[b, r].astype(np.float64))
+            assert np.max(np.abs(s[b, r] - want[b, r])) <= score_tol(want[b, r])
+    a, out, dv = T.layer_args(qd, kd, vd, T.SA_SCORE_INDEXER_PER_KV_HEAD, k, q_idx=qid, k_idx=kid,
+                              idx_w=wd)
+    idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev())
+    T.sa_decode_layer(a, T.SA_LAYER_SPARSE, idx, dv)
+    got = idx.cpu().numpy()
+    counts, fails = verdicts(want.reshape(B * Hkv, N), got.reshape(B * Hkv, k), k)
+    assert not fails, fails[:3]
+    scale = O.default_scale(d)
+    ref = _oracle_out(_f64(q), _f64(kc), _f64(vc), got, Hq // Hkv, scale)
+    check_out(out.cpu().numpy(), ref, "bf16", "indexer per KV head layer")
+
+
+@pytest.mark.parametrize("x", [2, 5, 20, 100, 500])
+def test_sparse_across_sparsity(x):
+    """Exact step (score -> top-k -> attend) at k = N/x, 2x to 500x: every
+    launch plan of the gather kernel (split rows with a combine, whole-row
+    workgroups) against the oracle."""
+    say("sparsity sweep x=%d" % x)
+    B, Hq, Hkv, d, N = 2, 8, 2, 128, 8192
+    k = N // x
+    q, kc, vc = _rand_cache(B, Hq, Hkv, N, d, "bf16", 40 + x)
+    qd, kd, vd = q.to(dev()), kc.to(dev()), vc.to(dev())
+    s = T.sa_score(qd, kd, T.SA_SCORE_EXACT)
+    idx = T.sa_topk(s, k)
+    out = T.sa_sparse_decode(qd, kd, vd, idx).cpu().numpy()
+    scale = O.default_scale(d)
+    qf, kf, vf = _f64(q), _f64(kc), _f64(vc)
+    rows_s, rows_g = [], []
+    for b in range(B):
+        for r in range(Hkv):
+            rows_s.append(O.scores_exact(qf[b, r * (Hq // Hkv):(r + 1) * (Hq // Hkv)], kf[b, r], scale))
+    got = idx.cpu().numpy()
+    counts, fails = verdicts(rows_s, got.reshape(B * Hkv, k), k)
+    assert not fails, fails[:3]
+    check_out(out, _oracle_out(qf, kf, vf, got, Hq // Hkv, scale), "bf16", "x=%d" % x)
+
+
 # ---------------------------------------------------------------- attention
 
 def _oracle_out(qf, kf, vf, sets, G, scale):

@@ -22,7 +22,7 @@ SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_ALIGN, SA_ERR_DTYPE, SA_ERR_WORKSPACE, 
 # sa_dtype
 SA_F32, SA_BF16 = 0, 1
 # sa_score_kind
-SA_SCORE_EXACT, SA_SCORE_BLOCK_MINMAX, SA_SCORE_INDEXER = 0, 1, 2
+SA_SCORE_EXACT, SA_SCORE_BLOCK_MINMAX, SA_SCORE_INDEXER, SA_SCORE_INDEXER_PER_KV_HEAD = 0, 1, 2, 3
 # sa_index_kind
 SA_IDX_TOKEN_PER_KV_HEAD, SA_IDX_TOKEN_SHARED, SA_IDX_BLOCK_PER_KV_HEAD = 0, 1, 2
 # sa_layer_mode
@@ -207,12 +207,19 @@ def sa_score(q, k_cache, kind=SA_SCORE_EXACT, *, kmin=None, kmax=None, block_siz
     if kind == SA_SCORE_BLOCK_MINMAX:
         aux.kmin, aux.kmax, aux.block_size = kmin.data_ptr(), kmax.data_ptr(), block_size
         shape = (B, Hkv, (N + block_size - 1) // block_size)
-    elif kind == SA_SCORE_INDEXER:
+    elif kind in (SA_SCORE_INDEXER, SA_SCORE_INDEXER_PER_KV_HEAD):
         aux.q_idx, aux.k_idx, aux.idx_w = q_idx.data_ptr(), k_idx.data_ptr(), idx_w.data_ptr()
-        aux.n_idx_heads, aux.idx_dim = q_idx.shape[1], q_idx.shape[2]
-        if k_idx.shape != (B, N, q_idx.shape[2]) or idx_w.shape != (B, q_idx.shape[1]):
-            raise ValueError("indexer tensors: q_idx [B,H,Di], k_idx [B,N,Di], idx_w [B,H]")
-        shape = (B, N)
+        H, Di = q_idx.shape[-2], q_idx.shape[-1]
+        aux.n_idx_heads, aux.idx_dim = H, Di
+        lead = (B,) if kind == SA_SCORE_INDEXER else (B, Hkv)
+        if (tuple(q_idx.shape) != lead + (H, Di) or tuple(k_idx.shape) != lead + (N, Di)
+                or tuple(idx_w.shape) != lead + (H,)):
+            raise ValueError("indexer tensors: q_idx %s+[H,Di], k_idx %s+[N,Di], idx_w %s+[H]"
+                             % (list(lead), list(lead), list(lead)))
+        for t in (q_idx, k_idx, idx_w):
+            if not t.is_contiguous():
+                raise ValueError("indexer tensors must be contiguous")
+        shape = lead + (N,)
     else:
         shape = (B, Hkv, N)
     if scores is None:
@@ -309,7 +316,7 @@ def layer_args(q, k_cache, v_cache, score_kind=SA_SCORE_EXACT, k=0, *, kmin=None
     a.aux.block_size = block_size
     if q_idx is not None:
         a.aux.q_idx, a.aux.k_idx, a.aux.idx_w = q_idx.data_ptr(), k_idx.data_ptr(), idx_w.data_ptr()
-        a.aux.n_idx_heads, a.aux.idx_dim = q_idx.shape[1], q_idx.shape[2]
+        a.aux.n_idx_heads, a.aux.idx_dim = q_idx.shape[-2], q_idx.shape[-1]
     a.k = k
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=dev)

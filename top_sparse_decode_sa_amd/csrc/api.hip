@@ -144,6 +144,24 @@ int64_t score_rows(const Cache& c, sa_score_kind kind) {
   return kind == SA_SCORE_INDEXER ? (int64_t)c.B : (int64_t)c.B * c.Hkv;
 }
 
+bool known_score_kind(sa_score_kind kind) {
+  return kind == SA_SCORE_EXACT || kind == SA_SCORE_BLOCK_MINMAX || kind == SA_SCORE_INDEXER ||
+         kind == SA_SCORE_INDEXER_PER_KV_HEAD;
+}
+
+bool is_indexer(sa_score_kind kind) {
+  return kind == SA_SCORE_INDEXER || kind == SA_SCORE_INDEXER_PER_KV_HEAD;
+}
+
+// The index kind a score kind selects into.
+sa_index_kind index_kind_of(sa_score_kind kind) {
+  switch (kind) {
+    case SA_SCORE_BLOCK_MINMAX: return SA_IDX_BLOCK_PER_KV_HEAD;
+    case SA_SCORE_INDEXER: return SA_IDX_TOKEN_SHARED;
+    default: return SA_IDX_TOKEN_PER_KV_HEAD;
+  }
+}
+
 sa_status do_score(const Cache& c, sa_score_kind kind, const void* q, const void* k,
                    const sa_score_aux* aux, float* scores, hipStream_t s) {
   hipError_t e;
@@ -153,8 +171,11 @@ sa_status do_score(const Cache& c, sa_score_kind kind, const void* q, const void
       e = launch_score_block(c, aux->block_size, q, aux->kmin, aux->kmax, scores, s);
       break;
     default:
-      e = launch_score_indexer(c.B, c.N, aux->n_idx_heads, aux->idx_dim, aux->q_idx, aux->k_idx,
-                               aux->idx_w, scores, s);
+      // the per-KV-head indexer is the shared one over B * Hkv sequences:
+      // its tensors are the shared layout with (batch, KV head) flattened
+      e = launch_score_indexer(
+          kind == SA_SCORE_INDEXER_PER_KV_HEAD ? c.B * c.Hkv : c.B, c.N, aux->n_idx_heads,
+          aux->idx_dim, aux->q_idx, aux->k_idx, aux->idx_w, scores, s);
       break;
   }
   return hip_status(e, "sa_score launch");
@@ -165,10 +186,9 @@ sa_status check_score_args(const sa_kv_desc* desc, sa_score_kind kind, const voi
                            Cache* c) {
   sa_status st;
   if ((st = check_desc(desc, c)) != SA_OK) return st;
-  if (kind != SA_SCORE_EXACT && kind != SA_SCORE_BLOCK_MINMAX && kind != SA_SCORE_INDEXER)
-    return fail(SA_ERR_SHAPE, "unknown score kind %d", (int)kind);
+  if (!known_score_kind(kind)) return fail(SA_ERR_SHAPE, "unknown score kind %d", (int)kind);
   if ((st = check_ptr(scores, "scores", 4)) != SA_OK) return st;
-  if (kind == SA_SCORE_INDEXER) return check_indexer_aux(*c, aux);
+  if (is_indexer(kind)) return check_indexer_aux(*c, aux);
   if ((st = check_ptr(q, "q", 16)) != SA_OK) return st;
   if (kind == SA_SCORE_BLOCK_MINMAX) return check_block_aux(*c, aux);
   return check_ptr(k_cache, "k_cache", 16);
@@ -209,9 +229,7 @@ LayerWs layer_ws(const Cache& c, const sa_layer_args* a, sa_layer_mode mode) {
   if (mode == SA_LAYER_DENSE) {
     w.attend = plan_attend(c, kIdxDense, 0, 0).ws_bytes;
   } else {
-    const sa_index_kind ik = a->score_kind == SA_SCORE_EXACT ? SA_IDX_TOKEN_PER_KV_HEAD
-                             : a->score_kind == SA_SCORE_BLOCK_MINMAX ? SA_IDX_BLOCK_PER_KV_HEAD
-                                                                      : SA_IDX_TOKEN_SHARED;
+    const sa_index_kind ik = index_kind_of(a->score_kind);
     const int32_t bs = a->score_kind == SA_SCORE_BLOCK_MINMAX ? a->aux.block_size : 0;
     w.attend = plan_attend(c, mode_of(ik), a->k, bs).ws_bytes;
     if (mode == SA_LAYER_SPARSE) {
@@ -387,16 +405,13 @@ sa_status sa_decode_layer(const sa_layer_args* a, sa_layer_mode mode, int32_t* i
                       "sa_decode_layer(DENSE) launch");
   }
   // selection-based modes
-  if (a->score_kind != SA_SCORE_EXACT && a->score_kind != SA_SCORE_BLOCK_MINMAX &&
-      a->score_kind != SA_SCORE_INDEXER)
+  if (!known_score_kind(a->score_kind))
     return fail(SA_ERR_SHAPE, "unknown score kind %d", (int)a->score_kind);
-  const sa_index_kind ik = a->score_kind == SA_SCORE_EXACT ? SA_IDX_TOKEN_PER_KV_HEAD
-                           : a->score_kind == SA_SCORE_BLOCK_MINMAX ? SA_IDX_BLOCK_PER_KV_HEAD
-                                                                    : SA_IDX_TOKEN_SHARED;
+  const sa_index_kind ik = index_kind_of(a->score_kind);
   const int32_t bs = a->score_kind == SA_SCORE_BLOCK_MINMAX ? a->aux.block_size : 0;
   if (a->score_kind == SA_SCORE_BLOCK_MINMAX) {
     if ((st = check_block_aux(c, &a->aux)) != SA_OK) return st;
-  } else if (a->score_kind == SA_SCORE_INDEXER && mode == SA_LAYER_SPARSE) {
+  } else if (is_indexer(a->score_kind) && mode == SA_LAYER_SPARSE) {
     if ((st = check_indexer_aux(c, &a->aux)) != SA_OK) return st;
   }
   const int64_t len = score_row_len(c, a->score_kind, &a->aux);

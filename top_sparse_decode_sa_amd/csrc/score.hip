@@ -278,7 +278,6 @@ struct IndexerArgs {
   int32_t H;
   int64_t N;
   float* scores;         // [B, N]
-  int32_t tile;
 };
 
 template <int DI, int HP, int U>
@@ -312,18 +311,24 @@ __global__ __launch_bounds__(kThreads) void score_indexer_kernel(IndexerArgs a) 
 
   const uint8_t* kbase = a.k_idx + (int64_t)b * a.N * DI * 2 + sl * 16;
   float* srow = a.scores + (int64_t)b * a.N;
-  const int64_t t_tile = (int64_t)blockIdx.x * a.tile;
-  const int64_t t_end = min(t_tile + (int64_t)a.tile, a.N);
   constexpr int per_wave_iter = RPW * U;
   constexpr int per_iter = 4 * per_wave_iter;
-  for (int64_t base = t_tile; base < t_end; base += per_iter) {
-    const int64_t wbase = base + wave * per_wave_iter;
-    uint4 kw[U];
+  constexpr int kIters = kScoreTile / per_iter;
+  static_assert(kScoreTile % per_iter == 0, "whole iterations per tile");
+  const int64_t t_tile = (int64_t)blockIdx.x * kScoreTile;
+  const int64_t t_end = min(t_tile + (int64_t)kScoreTile, a.N);
+  // same load structure as the exact score: clamped, branch-free loads and a
+  // ping-pong over two buffers on whole tiles
+  auto load = [&](int64_t base, uint4 (&kw)[U], bool clamp) {
+    const int64_t wbase = base + wave * per_wave_iter + lg;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t t = wbase + u * RPW + lg;
-      kw[u] = (t < t_end) ? ld16_nt(kbase + t * (DI * 2)) : make_uint4(0, 0, 0, 0);
+      int64_t t = wbase + u * RPW;
+      if (clamp) t = std::min<int64_t>(t, t_end - 1);
+      kw[u] = ld16_nt(kbase + t * (DI * 2));
     }
+  };
+  auto reduce = [&](int64_t base, const uint4 (&kw)[U], bool check) {
     float mine = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -340,8 +345,24 @@ __global__ __launch_bounds__(kThreads) void score_indexer_kernel(IndexerArgs a) 
       }
       if (sl == u) mine = sc;
     }
-    const int64_t t = wbase + sl * RPW + lg;
-    if (sl < U && t < t_end) srow[t] = mine;
+    const int64_t t = base + wave * per_wave_iter + sl * RPW + lg;
+    if (sl < U && (!check || t < t_end)) srow[t] = mine;
+  };
+  if (t_end - t_tile == kScoreTile) {
+    uint4 kb[2][U];
+    load(t_tile, kb[0], false);
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      if (i + 1 < kIters) load(t_tile + (i + 1) * per_iter, kb[(i + 1) & 1], false);
+      __builtin_amdgcn_sched_barrier(0);
+      reduce(t_tile + i * per_iter, kb[i & 1], false);
+    }
+  } else {
+    for (int64_t base = t_tile; base < t_end; base += per_iter) {
+      uint4 kw[U];
+      load(base, kw, true);
+      reduce(base, kw, true);
+    }
   }
 }
 
@@ -459,8 +480,7 @@ hipError_t launch_score_indexer(int32_t B, int64_t N, int32_t H, int32_t Di, con
   a.H = H;
   a.N = N;
   a.scores = scores;
-  a.tile = 1024;
-  const dim3 grid((unsigned)((N + a.tile - 1) / a.tile), (unsigned)B);
+  const dim3 grid((unsigned)((N + kScoreTile - 1) / kScoreTile), (unsigned)B);
   if (Di == 32) return launch_indexer_di<32>(a, grid, s);
   if (Di == 64) return launch_indexer_di<64>(a, grid, s);
   return launch_indexer_di<128>(a, grid, s);
