@@ -193,12 +193,27 @@ sa_status sa_dense_decode(const sa_kv_desc* desc, const void* q, const void* k_c
                           hipStream_t stream);
 size_t sa_dense_workspace_size(const sa_kv_desc* desc);
 
+/* Full decode attention that also writes the exact score of every token
+ * ([P2] section 2.3: a sensitive layer runs full attention and passes the
+ * top-k indices it extracts on to the layers that reuse them).  out is what
+ * sa_dense_decode writes; scores [batch, n_kv_heads, ctx_len] fp32 is what
+ * sa_score(SA_SCORE_EXACT) writes, up to fp32 summation order:
+ *   scores[b, r, t] = scale * sum_{g < G} q[b, r*G + g, :] . K[b, r, t, :]
+ * For bf16 q and K with head_dim 128 and G <= 4 the scores come out of the
+ * attention kernel's own logits (one pass over K); other shapes run the
+ * scoring and the attention as two launches. */
+sa_status sa_dense_decode_scored(const sa_kv_desc* desc, const void* q, const void* k_cache,
+                                 const void* v_cache, float* out, float* scores, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+size_t sa_dense_scored_workspace_size(const sa_kv_desc* desc);
+
 /* ----------------------------------------------------- per-layer mode flag */
 
 typedef enum {
   SA_LAYER_DENSE = 0,  /* full attention; idx untouched */
   SA_LAYER_SPARSE = 1, /* score -> top-k -> selected-set attention; WRITES idx */
-  SA_LAYER_REUSE = 2   /* selected-set attention over idx as given; READS idx */
+  SA_LAYER_REUSE = 2,  /* selected-set attention over idx as given; READS idx */
+  SA_LAYER_DENSE_SELECT = 3 /* full attention + top-k of its exact scores; WRITES idx */
 } sa_layer_mode;
 
 /* Everything one layer's decode step needs.  The score kind fixes the index
@@ -226,18 +241,60 @@ typedef struct {
  *   SPARSE: sa_score -> sa_topk -> sa_sparse_decode, the index set written to
  *           idx ([batch, n_kv_heads, k] or [batch, k] for INDEXER).
  *   REUSE:  sa_sparse_decode over idx exactly as given (no scoring, no top-k);
- *           idx must hold the set of an earlier SPARSE layer with the same
- *           score kind and k.
+ *           idx must hold the set of an earlier SPARSE or DENSE_SELECT layer
+ *           with the same score kind and k.
+ *   DENSE_SELECT: [P2] sections 2.2-2.3, a "reset" layer: sa_dense_decode_scored
+ *           -> sa_topk of those exact scores into idx [batch, n_kv_heads, k].
+ *           Needs score_kind SA_SCORE_EXACT (else SA_ERR_UNSUPPORTED).
  * idx may be null for DENSE. */
 sa_status sa_decode_layer(const sa_layer_args* a, sa_layer_mode mode, int32_t* idx,
                           hipStream_t stream);
 size_t sa_layer_workspace_size(const sa_layer_args* a, sa_layer_mode mode);
 
 /* Check a per-layer plan on the host: modes[l] in sa_layer_mode; a REUSE layer
- * needs 0 <= src[l] < l with layer src[l] owning an index set (SPARSE, or a
- * REUSE layer, which carries its source's set).  src[l] is ignored for other
- * modes.  Returns SA_OK or SA_ERR_SHAPE (reason in sa_last_error). */
+ * needs 0 <= src[l] < l with layer src[l] owning an index set (SPARSE,
+ * DENSE_SELECT, or a REUSE layer, which carries its source's set).  src[l] is
+ * ignored for other modes.  Returns SA_OK or SA_ERR_SHAPE (reason in
+ * sa_last_error). */
 sa_status sa_plan_validate(const int32_t* modes, const int32_t* src, int32_t n_layers);
+
+/* ------------------------------------------- layer-reuse policy ([P2] 2.2) */
+
+/* Top-k overlap of two index sets per row: [P2] section 2.2, the entries of
+ * the similarity matrix count how many top-k token indices a source layer and
+ * a target layer share.  idx_a, idx_b: [n_rows, k] int32 (device), each row
+ * k distinct positions in ASCENDING order (what sa_topk writes; not checked:
+ * an unsorted row gives a wrong count, never an out-of-range access).
+ *   counts[r] = |{idx_a[r, :]} intersect {idx_b[r, :]}|   (int32, device)
+ * Limits: 1 <= n_rows < 2^31, 1 <= k. */
+sa_status sa_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t n_rows, int32_t k,
+                           int32_t* counts, hipStream_t stream);
+
+/* Offline layer policy by dynamic programming: [P2] section 2.2 (HOST call,
+ * host arrays).  Layer j either runs full attention and refreshes the index
+ * set (a "reset jump" to state (j, j)) or reuses the set of the last reset
+ * layer i (a "vertical move" (i, j-1) -> (i, j)), allowed only when their
+ * overlap ratio exceeds theta:
+ *   overlap[i * n_layers + j] / total > theta      (compared in double)
+ * where overlap[i * n_layers + j] (i < j; other entries unread) is the summed
+ * sa_index_overlap count of layers i and j over all rows and total = n_rows * k.
+ * Layer 0 and every layer with sensitive[l] != 0 (may be null) run full
+ * attention.  Among feasible plans the one with the fewest full layers wins,
+ * then the largest summed overlap of the reused layers; remaining ties go to
+ * the plan whose list of full layers is lexicographically largest (resets as
+ * late as possible).  Output: modes[l] is SA_LAYER_DENSE_SELECT for a full
+ * layer whose set a later layer reuses, SA_LAYER_DENSE for any other full
+ * layer, SA_LAYER_REUSE with src[l] = its reset layer otherwise (src[l] = -1
+ * for full layers).  Limits: 1 <= n_layers <= 256, total >= 1, overlap
+ * entries in [0, total]. */
+sa_status sa_plan_reuse(const int64_t* overlap, int64_t total, int32_t n_layers, double theta,
+                        const int32_t* sensitive, int32_t* modes, int32_t* src);
+
+/* The static baseline of [P2] section 4 ("Jump" with a fixed step): layers
+ * 0, step, 2*step, ... run full attention and every other layer reuses the
+ * set of the full layer before it.  modes/src as in sa_plan_reuse.  Limits:
+ * 1 <= n_layers <= 256, step >= 1. */
+sa_status sa_plan_fixed_jump(int32_t n_layers, int32_t step, int32_t* modes, int32_t* src);
 
 /* ----------------------------------------------------------------- misc */
 

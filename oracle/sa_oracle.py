@@ -38,7 +38,7 @@ import math
 
 import numpy as np
 
-DENSE, SPARSE, REUSE = 0, 1, 2
+DENSE, SPARSE, REUSE, DENSE_SELECT = 0, 1, 2, 3
 
 
 # ---------------------------------------------------------------------------
@@ -223,13 +223,15 @@ def plan_check(modes, src):
     attention.  [P2] sections 2.2-2.3 and [P5] "IndexCache": a tolerant layer
     reuses the top-k indices of an earlier layer unchanged.  A REUSE layer
     names a source layer that comes before it and that owns an index set
-    (a SPARSE layer, or a REUSE layer, which carries its source's set).
+    (a SPARSE layer, a DENSE_SELECT layer -- full attention that hands its
+    top-k on, [P2] section 2.3 -- or a REUSE layer, which carries its
+    source's set).
     """
     if len(modes) != len(src):
         return "modes and src differ in length"
     has_idx = []
     for l, m in enumerate(modes):
-        if m not in (DENSE, SPARSE, REUSE):
+        if m not in (DENSE, SPARSE, REUSE, DENSE_SELECT):
             return "layer %d: unknown mode %r" % (l, m)
         if m == REUSE:
             s = src[l]
@@ -245,8 +247,9 @@ def run_plan(modes, src, k, score_fn, attend_fn, dense_fn):
     """Run a layer plan.
 
     For layer l: DENSE -> dense_fn(l), no index set; SPARSE -> idx =
-    topk(score_fn(l), k), attend_fn(l, idx); REUSE -> idx = index set of layer
-    src[l] (the same array), attend_fn(l, idx).  Returns (outputs, index sets).
+    topk(score_fn(l), k), attend_fn(l, idx); DENSE_SELECT -> dense_fn(l) and
+    idx = topk(score_fn(l), k); REUSE -> idx = index set of layer src[l] (the
+    same array), attend_fn(l, idx).  Returns (outputs, index sets).
     """
     why = plan_check(modes, src)
     if why is not None:
@@ -256,6 +259,9 @@ def run_plan(modes, src, k, score_fn, attend_fn, dense_fn):
         if m == DENSE:
             outs.append(dense_fn(l))
             idxs.append(None)
+        elif m == DENSE_SELECT:
+            outs.append(dense_fn(l))
+            idxs.append(topk(score_fn(l), k))
         elif m == SPARSE:
             idx = topk(score_fn(l), k)
             outs.append(attend_fn(l, idx))
@@ -265,6 +271,95 @@ def run_plan(modes, src, k, score_fn, attend_fn, dense_fn):
             outs.append(attend_fn(l, idx))
             idxs.append(idx)
     return outs, idxs
+
+
+# ---------------------------------------------------------------------------
+# Layer-reuse policy ([P2] section 2.2)
+# ---------------------------------------------------------------------------
+
+def index_overlap(a, b) -> int:
+    """Number of token indices two top-k sets share ([P2] section 2.2: the
+    similarity matrix holds the overlap of a source and a target layer's
+    top-k indices)."""
+    return int(np.intersect1d(np.asarray(a), np.asarray(b)).shape[0])
+
+
+def reuse_plan_feasible(full, overlap, total, theta, sensitive):
+    """Whether a set of full-attention layers gives a valid policy.
+
+    [P2] section 2.2: a full layer j is the state (j, j) (a "reset jump");
+    every other layer t stays on the column of the last full layer i before it
+    (a "vertical move" into (i, t)), which is allowed only when the overlap
+    ratio of layers i and t exceeds theta.  Layer 0 has no earlier set, so it
+    is full; a sensitive layer ([P2] section 2.1) is full too.
+    """
+    n = len(overlap)
+    if 0 not in full:
+        return False
+    last = None
+    for t in range(n):
+        if t in full:
+            last = t
+            continue
+        if sensitive is not None and sensitive[t]:
+            return False
+        if not float(overlap[last][t]) / float(total) > theta:
+            return False
+    return True
+
+
+def reuse_plan_bruteforce(overlap, total, theta, sensitive=None):
+    """The optimal policy of [P2] section 2.2 by exhaustive search.
+
+    Every set of full layers is tried (2^(L-1) of them).  Objective, in this
+    order: fewest full layers (full attention is the cost the policy
+    minimises), then the largest summed overlap over the reused layers
+    (maximise cumulative similarity), then -- a tie rule of this
+    implementation -- the lexicographically largest sorted list of full layers.
+    Returns (modes, src): a full layer is DENSE_SELECT when a later layer
+    reuses its set and DENSE otherwise; a reused layer is REUSE with src = its
+    full layer; src = -1 for full layers.
+    """
+    n = len(overlap)
+    best = None
+    for mask in range(1 << (n - 1)):
+        full = [0] + [t for t in range(1, n) if mask >> (t - 1) & 1]
+        fs = set(full)
+        if not reuse_plan_feasible(fs, overlap, total, theta, sensitive):
+            continue
+        sim, last = 0, 0
+        for t in range(n):
+            if t in fs:
+                last = t
+            else:
+                sim += int(overlap[last][t])
+        key = (len(full), -sim, [-x for x in full])
+        if best is None or key < best[0]:
+            best = (key, full)
+    full = best[1]
+    return _plan_from_full(full, n)
+
+
+def _plan_from_full(full, n):
+    fs = set(full)
+    modes, src = [], []
+    last = -1
+    for t in range(n):
+        if t in fs:
+            last = t
+            reused = t + 1 < n and (t + 1) not in fs
+            modes.append(DENSE_SELECT if reused else DENSE)
+            src.append(-1)
+        else:
+            modes.append(REUSE)
+            src.append(last)
+    return modes, src
+
+
+def fixed_jump_plan(n_layers: int, step: int):
+    """The static baseline of [P2] section 4: full attention at layers 0,
+    step, 2*step, ...; every other layer reuses the full layer before it."""
+    return _plan_from_full(list(range(0, n_layers, step)), n_layers)
 
 
 # ---------------------------------------------------------------------------

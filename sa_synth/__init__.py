@@ -68,6 +68,8 @@ def lib():
         L.synth_round.argtypes = [vp, i64, ctypes.c_int, vp]
         L.synth_fill_ar1.argtypes = [u64, u32, u32, dbl, i64, i64, i64, i64, ctypes.c_int, vp]
         L.synth_fill_ar1.restype = ctypes.c_int
+        L.synth_fill_ar1_sched.argtypes = [u64, u32, u32, vp, i64, i64, i64, i64, ctypes.c_int, vp]
+        L.synth_fill_ar1_sched.restype = ctypes.c_int
         L.synth_project_bf16.argtypes = [vp, i64, i64, i64, i64, vp, i64, dbl, u64, u64, vp]
         L.synth_plant_rows.argtypes = [u64, u64, vp, i64, i64, vp, dbl, dbl, ctypes.c_int, vp]
         _lib = L
@@ -142,6 +144,9 @@ class Config:
     indexer_noise: float = 0.0
     modes: tuple = field(default_factory=tuple)  # per-layer plan (strings)
     src: tuple = field(default_factory=tuple)
+    # per-layer correlation of BOTH queries and keys with the layer before
+    # (entry 0 unused); empty: no such chain
+    rho_sched: tuple = field(default_factory=tuple)
 
     @property
     def group(self) -> int:
@@ -182,6 +187,11 @@ CONFIGS = {
     "indexer1m": Config("indexer1m", 1, 32, 8, 128, 1 << 20, "bf16", 2048, n_layers=8,
                         indexer_heads=4, indexer_dim=64, indexer_noise=0.1,
                         modes=("dense", "dense") + ("sparse",) * 6, src=(-1,) * 8),
+    # Layer-reuse policy workload: the llama32k shape over 8 layers whose
+    # queries and keys follow a per-layer correlation chain (a weakly
+    # correlated layer 4 breaks the run), k = 655 per (sequence, KV head).
+    "hylra32k": Config("hylra32k", 16, 32, 8, 128, 32768, "bf16", 32768 // 50, n_layers=8,
+                       rho_sched=(0.0, 0.97, 0.95, 0.95, 0.3, 0.97, 0.95, 0.95)),
 }
 CONFIG_ORDER = ["tiny", "llama32k", "block61k", "batch128k", "indexer1m"]
 
@@ -204,7 +214,18 @@ class Workload:
     # -- building blocks ----------------------------------------------------
     def _q_noise(self, layer: int, qvar: int, b: int, h: int) -> np.ndarray:
         c = self.cfg
-        return normal(self.seed, stream_id(TAG_Q + _QVAR_STRIDE * qvar, layer, b, h), 0, c.head_dim)
+        tag = TAG_Q + _QVAR_STRIDE * qvar
+        if c.rho_sched:
+            x = normal(self.seed, stream_id(tag, 0, b, h), 0, c.head_dim)
+            for l in range(1, layer + 1):
+                r = c.rho_sched[l]
+                x = r * x + math.sqrt(1.0 - r * r) * normal(self.seed, stream_id(tag, l, b, h), 0,
+                                                            c.head_dim)
+            return x
+        return normal(self.seed, stream_id(tag, layer, b, h), 0, c.head_dim)
+
+    def _rhos(self) -> np.ndarray:
+        return np.ascontiguousarray(np.asarray(self.cfg.rho_sched, dtype=np.float64))
 
     def direction(self, layer: int, b: int, r: int) -> np.ndarray:
         """Per-(sequence, KV head) direction u with |u| = sqrt(d), fp64."""
@@ -240,7 +261,12 @@ class Workload:
         nb = b1 - b0
         out = np.empty((nb, c.n_kv_heads, c.ctx_len, c.head_dim), dtype=c.np_dtype)
         per = c.ctx_len * c.head_dim
-        if c.rho > 0.0:
+        if c.rho_sched:
+            rhos = self._rhos()
+            if lib().synth_fill_ar1_sched(self.seed, TAG_K, layer, _ptr(rhos), b0, nb, c.n_kv_heads,
+                                          per, c.kind, _ptr(out)) != 0:
+                raise ValueError("layer index too large for the correlated-key chain")
+        elif c.rho > 0.0:
             if lib().synth_fill_ar1(self.seed, TAG_K, layer, c.rho, b0, nb, c.n_kv_heads, per,
                                     c.kind, _ptr(out)) != 0:
                 raise ValueError("layer index too large for the correlated-key chain")
@@ -283,11 +309,12 @@ class Workload:
         c = self.cfg
         out = np.empty((c.ctx_len, c.head_dim), dtype=c.np_dtype)
         per = c.ctx_len * c.head_dim
-        if c.rho > 0.0:
+        if c.rho_sched or c.rho > 0.0:
             x = normal(self.seed, stream_id(TAG_K, 0, b, r), 0, per)
-            innov = math.sqrt(1.0 - c.rho * c.rho)
             for l in range(1, layer + 1):
-                x = c.rho * x + innov * normal(self.seed, stream_id(TAG_K, l, b, r), 0, per)
+                rho = c.rho_sched[l] if c.rho_sched else c.rho
+                x = rho * x + math.sqrt(1.0 - rho * rho) * normal(
+                    self.seed, stream_id(TAG_K, l, b, r), 0, per)
             out[...] = round_to(x, c.kind).reshape(out.shape)
         else:
             lib().synth_normal(self.seed, stream_id(TAG_K, layer, b, r), 0, per, 0.0, 1.0, c.kind,

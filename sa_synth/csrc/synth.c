@@ -229,6 +229,36 @@ int synth_fill_ar1(uint64_t seed, uint32_t tag, uint32_t layer, double rho, int6
   return 0;
 }
 
+/*
+ * The same chain with a correlation per layer:
+ *   x_0 = z_0,  x_l = rhos[l] * x_{l-1} + sqrt(1 - rhos[l]^2) * z_l  (rhos[0] unused).
+ */
+int synth_fill_ar1_sched(uint64_t seed, uint32_t tag, uint32_t layer, const double* rhos,
+                         int64_t b0, int64_t B, int64_t H, int64_t per_slab, int kind, void* out) {
+  if (layer >= 64) return -1;
+  const int64_t n_slab = B * H;
+  const int64_t chunk = 4096;
+  const int64_t chunks_per_slab = (per_slab + chunk - 1) / chunk;
+  double innov[64];
+  for (uint32_t l = 1; l <= layer; ++l) innov[l] = sqrt(1.0 - rhos[l] * rhos[l]);
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t w = 0; w < n_slab * chunks_per_slab; ++w) {
+    const int64_t slab = w / chunks_per_slab;
+    const uint32_t b = (uint32_t)(b0 + slab / H), h = (uint32_t)(slab % H);
+    const int64_t c0 = (w % chunks_per_slab) * chunk;
+    const int64_t c1 = c0 + chunk < per_slab ? c0 + chunk : per_slab;
+    uint64_t keys[64];
+    const uint32_t nl = layer + 1;
+    for (uint32_t l = 0; l < nl; ++l) keys[l] = make_key(seed, synth_stream_id(tag, l, b, h));
+    for (int64_t c = c0; c < c1; ++c) {
+      double x = normal_at(keys[0], (uint64_t)c);
+      for (uint32_t l = 1; l < nl; ++l) x = rhos[l] * x + innov[l] * normal_at(keys[l], (uint64_t)c);
+      store(out, kind, slab * per_slab + c, x);
+    }
+  }
+  return 0;
+}
+
 static inline double bf16_bits_to_f64(uint16_t v) {
   uint32_t u = (uint32_t)v << 16;
   float f;

@@ -150,7 +150,7 @@ def test_plan_validate():
     T.sa_plan_validate([1, 2, 2, 2], [-1, 0, 0, 0])
     T.sa_plan_validate([0, 0, 1, 1, 1, 1, 1, 1], [-1] * 8)
     T.sa_plan_validate([1, 2, 0, 2], [-1, 0, -1, 1])
-    for modes, src in [([2], [0]), ([1, 2], [-1, 1]), ([0, 2], [-1, 0]), ([1, 3], [-1, -1]),
+    for modes, src in [([2], [0]), ([1, 2], [-1, 1]), ([0, 2], [-1, 0]), ([1, 7], [-1, -1]),
                        ([1, 2], [-1, -5])]:
         with pytest.raises(T.SAError):
             T.sa_plan_validate(modes, src)
@@ -161,3 +161,101 @@ def test_plan_validate():
 def test_status_strings():
     for s in range(8):
         assert T.lib().sa_status_string(s).decode().startswith("SA_")
+
+
+# ---------------------------------------------------------------------------
+# layer-reuse planner (host-only calls): the C dynamic programme against the
+# oracle's exhaustive search, bit-exact, plus its error paths
+# ---------------------------------------------------------------------------
+
+def test_plan_reuse_matches_exhaustive_search():
+    import numpy as np
+    import oracle as O
+    rng = np.random.default_rng(11)
+    cases = 0
+    for n in range(1, 10):
+        for trial in range(40):
+            total = int(rng.integers(1, 1000))
+            m = np.triu(rng.integers(0, total + 1, (n, n)), 1).astype(np.int64)
+            if trial % 4 == 0:       # coarse values: many exact ties
+                m = np.triu(rng.integers(0, 3, (n, n)) * (total // 2), 1).astype(np.int64)
+            theta = float(rng.choice([-0.1, 0.0, 0.3, 0.5, 0.7, 0.95, 1.0]))
+            sens = (rng.random(n) < 0.2).astype(int).tolist() if trial % 3 == 0 else None
+            want = O.reuse_plan_bruteforce(m, total, theta, sens)
+            got = T.sa_plan_reuse(m, total, theta, sens)
+            assert got == (list(want[0]), list(want[1])), (n, trial, theta)
+            T.sa_plan_validate(*got)
+            cases += 1
+    assert cases == 9 * 40
+
+
+def test_plan_fixed_jump_matches_oracle():
+    import oracle as O
+    for n in range(1, 12):
+        for step in range(1, 6):
+            want = O.fixed_jump_plan(n, step)
+            assert T.sa_plan_fixed_jump(n, step) == (list(want[0]), list(want[1]))
+
+
+def test_planner_errors():
+    import numpy as np
+    L = T.lib()
+    m = (ctypes.c_int32 * 4)()
+    s = (ctypes.c_int32 * 4)()
+    ov = np.zeros((4, 4), dtype=np.int64)
+    p = ctypes.c_void_p(ov.ctypes.data)
+    assert L.sa_plan_reuse(None, 10, 4, 0.5, None, m, s) == Bn.SA_ERR_NULL
+    assert L.sa_plan_reuse(p, 10, 0, 0.5, None, m, s) == Bn.SA_ERR_SHAPE
+    assert L.sa_plan_reuse(p, 10, 257, 0.5, None, m, s) == Bn.SA_ERR_SHAPE
+    assert L.sa_plan_reuse(p, 0, 4, 0.5, None, m, s) == Bn.SA_ERR_SHAPE
+    assert L.sa_plan_reuse(p, 10, 4, float("nan"), None, m, s) == Bn.SA_ERR_SHAPE
+    ov[0, 3] = 11
+    assert L.sa_plan_reuse(p, 10, 4, 0.5, None, m, s) == Bn.SA_ERR_SHAPE
+    ov[0, 3] = -1
+    assert L.sa_plan_reuse(p, 10, 4, 0.5, None, m, s) == Bn.SA_ERR_SHAPE
+    ov[0, 3] = 0
+    ov[3, 0] = 99            # below the diagonal: never read
+    assert L.sa_plan_reuse(p, 10, 4, 0.5, None, m, s) == Bn.SA_OK
+    assert L.sa_plan_fixed_jump(4, 0, m, s) == Bn.SA_ERR_SHAPE
+    assert L.sa_plan_fixed_jump(0, 1, m, s) == Bn.SA_ERR_SHAPE
+    assert L.sa_plan_fixed_jump(4, 1, None, s) == Bn.SA_ERR_NULL
+    assert L.sa_index_overlap(None, FAKE, 4, 8, FAKE, None) == Bn.SA_ERR_NULL
+    assert L.sa_index_overlap(FAKE, FAKE, 0, 8, FAKE, None) == Bn.SA_ERR_SHAPE
+    assert L.sa_index_overlap(FAKE, FAKE, 4, 0, FAKE, None) == Bn.SA_ERR_SHAPE
+    assert L.sa_index_overlap(FAKE, ctypes.c_void_p((1 << 20) + 2), 4, 8, FAKE,
+                              None) == Bn.SA_ERR_ALIGN
+
+
+def test_dense_scored_and_dense_select_errors():
+    L = T.lib()
+    d = _desc()
+    nb = L.sa_dense_scored_workspace_size(ctypes.byref(d))
+    ws = ctypes.c_void_p(1 << 24) if nb else None
+    assert L.sa_dense_decode_scored(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, ws, nb,
+                                    None) == Bn.SA_ERR_NULL
+    assert L.sa_dense_decode_scored(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE,
+                                    ctypes.c_void_p((1 << 20) + 2), ws, nb, None) == Bn.SA_ERR_ALIGN
+    assert L.sa_dense_decode_scored(ctypes.byref(_desc(head_dim=96)), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    ws, nb, None) == Bn.SA_ERR_UNSUPPORTED
+    a = Bn.LayerArgs()
+    a.desc = d
+    a.q = a.k_cache = a.v_cache = a.out = 1 << 20
+    a.score_kind = Bn.SA_SCORE_EXACT
+    a.k = 10
+    need = L.sa_layer_workspace_size(ctypes.byref(a), Bn.SA_LAYER_DENSE_SELECT)
+    # scores [B, Hkv, N] fp32 on top of what DENSE needs
+    assert need >= 2 * 2 * 1000 * 4 + L.sa_layer_workspace_size(ctypes.byref(a), Bn.SA_LAYER_DENSE)
+    a.ws, a.ws_bytes = 1 << 24, need
+    assert L.sa_decode_layer(ctypes.byref(a), Bn.SA_LAYER_DENSE_SELECT, None, None) == Bn.SA_ERR_NULL
+    a.ws_bytes = need - 256
+    assert L.sa_decode_layer(ctypes.byref(a), Bn.SA_LAYER_DENSE_SELECT, FAKE,
+                             None) == Bn.SA_ERR_WORKSPACE
+    a.ws_bytes = need
+    a.k = 1001
+    assert L.sa_decode_layer(ctypes.byref(a), Bn.SA_LAYER_DENSE_SELECT, FAKE, None) == Bn.SA_ERR_SHAPE
+    a.k = 10
+    a.score_kind = Bn.SA_SCORE_BLOCK_MINMAX
+    assert L.sa_decode_layer(ctypes.byref(a), Bn.SA_LAYER_DENSE_SELECT, FAKE,
+                             None) == Bn.SA_ERR_UNSUPPORTED
+    assert L.sa_decode_layer(ctypes.byref(a), 4, FAKE, None) == Bn.SA_ERR_SHAPE
+    T.sa_plan_validate([Bn.SA_LAYER_DENSE_SELECT, Bn.SA_LAYER_REUSE], [-1, 0])

@@ -329,6 +329,78 @@ def test_plan_check_rejects_bad_plans():
     assert O.plan_check([O.SPARSE, 7], [-1, -1]) is not None
 
 
+def test_plan_dense_select_hands_its_topk_on():
+    d, n, k = 16, 64, 8
+    layers = [(_rand(4, d), _rand(n, d), _rand(n, d)) for _ in range(3)]
+    outs, idxs = O.run_plan([O.DENSE_SELECT, O.REUSE, O.REUSE], [-1, 0, 0], k,
+                            lambda l: O.scores_exact(layers[l][0], layers[l][1], 0.25),
+                            lambda l, i: O.attend(*layers[l], i, 0.25),
+                            lambda l: O.dense(*layers[l], 0.25))
+    np.testing.assert_array_equal(outs[0], O.dense(*layers[0], 0.25))
+    np.testing.assert_array_equal(idxs[0], O.topk(O.scores_exact(layers[0][0], layers[0][1], 0.25), k))
+    assert idxs[1] is idxs[0] and idxs[2] is idxs[0]
+    assert O.plan_check([O.DENSE_SELECT, O.REUSE], [-1, 0]) is None
+
+
+# ---------------------------------------------------------------------------
+# layer-reuse policy (HyLRA, section 2.2)
+# ---------------------------------------------------------------------------
+
+DS, RU, DN = O.DENSE_SELECT, O.REUSE, O.DENSE
+
+
+def _tri(n, entries):
+    m = np.zeros((n, n), dtype=np.int64)
+    for (i, j), v in entries.items():
+        m[i, j] = v
+    return m
+
+
+def test_index_overlap_counts_shared_positions():
+    assert O.index_overlap([1, 5, 9, 12], [0, 5, 12, 30]) == 2
+    assert O.index_overlap([3], [4]) == 0
+    assert O.index_overlap(np.arange(10), np.arange(10)) == 10
+
+
+def test_reuse_plan_worked_example():
+    # total 100, theta 0.5.  Worked by hand: {0} fails (layer 3 shares only
+    # 40 with layer 0); {0,3}: 90+60 = 150; {0,1}: 95+70 = 165; {0,2}: 90+80
+    # = 170 -> full attention at 0 and 2, layers 1 and 3 reuse them.
+    m = _tri(4, {(0, 1): 90, (0, 2): 60, (0, 3): 40, (1, 2): 95, (1, 3): 70, (2, 3): 80})
+    assert O.reuse_plan_bruteforce(m, 100, 0.5) == ([DS, RU, DS, RU], [-1, 0, -1, 2])
+
+
+def test_reuse_plan_limits_of_theta():
+    rng = np.random.default_rng(3)
+    n = 6
+    m = np.triu(rng.integers(0, 101, (n, n)), 1)
+    # no reuse possible: every layer runs full attention, no set is handed on
+    assert O.reuse_plan_bruteforce(m, 100, 1.0) == ([DN] * n, [-1] * n)
+    # every reuse allowed: one reset at layer 0 serves all
+    assert O.reuse_plan_bruteforce(m, 100, -1.0) == ([DS] + [RU] * (n - 1), [-1] + [0] * (n - 1))
+    # "exceeds theta" is strict: a ratio equal to theta is no reuse
+    m2 = _tri(2, {(0, 1): 50})
+    assert O.reuse_plan_bruteforce(m2, 100, 0.5) == ([DN, DN], [-1, -1])
+    assert O.reuse_plan_bruteforce(m2, 100, 0.49) == ([DS, RU], [-1, 0])
+
+
+def test_reuse_plan_sensitive_layers_and_ties():
+    m = np.full((5, 5), 100, dtype=np.int64)
+    # a sensitive layer always resets; the others reuse the latest reset
+    assert O.reuse_plan_bruteforce(m, 100, 0.5, sensitive=[0, 0, 1, 0, 0]) == \
+        ([DS, RU, DS, RU, RU], [-1, 0, -1, 2, 2])
+    # tie: {0,1} and {0,2} both keep 50 -> the later reset wins
+    t = _tri(3, {(0, 1): 50, (0, 2): 10, (1, 2): 50})
+    assert O.reuse_plan_bruteforce(t, 100, 0.4) == ([DS, RU, DN], [-1, 0, -1])
+
+
+def test_fixed_jump_plan():
+    assert O.fixed_jump_plan(8, 3) == ([DS, RU, RU, DS, RU, RU, DS, RU],
+                                       [-1, 0, 0, -1, 3, 3, -1, 6])
+    assert O.fixed_jump_plan(4, 1) == ([DN] * 4, [-1] * 4)
+    assert O.fixed_jump_plan(7, 3)[0][6] == DN        # a last full layer hands nothing on
+
+
 # ---------------------------------------------------------------------------
 # acceptance rule
 # ---------------------------------------------------------------------------

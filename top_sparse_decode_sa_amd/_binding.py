@@ -26,13 +26,14 @@ SA_SCORE_EXACT, SA_SCORE_BLOCK_MINMAX, SA_SCORE_INDEXER, SA_SCORE_INDEXER_PER_KV
 # sa_index_kind
 SA_IDX_TOKEN_PER_KV_HEAD, SA_IDX_TOKEN_SHARED, SA_IDX_BLOCK_PER_KV_HEAD = 0, 1, 2
 # sa_layer_mode
-SA_LAYER_DENSE, SA_LAYER_SPARSE, SA_LAYER_REUSE = 0, 1, 2
+SA_LAYER_DENSE, SA_LAYER_SPARSE, SA_LAYER_REUSE, SA_LAYER_DENSE_SELECT = 0, 1, 2, 3
 
 EXPORTED = [
     "sa_score", "sa_block_summarize", "sa_topk", "sa_topk_workspace_size", "sa_sparse_decode",
-    "sa_sparse_workspace_size", "sa_dense_decode", "sa_dense_workspace_size", "sa_decode_layer",
-    "sa_layer_workspace_size", "sa_plan_validate", "sa_workspace_init", "sa_status_string",
-    "sa_last_error", "sa_version",
+    "sa_sparse_workspace_size", "sa_dense_decode", "sa_dense_workspace_size",
+    "sa_dense_decode_scored", "sa_dense_scored_workspace_size", "sa_decode_layer",
+    "sa_layer_workspace_size", "sa_plan_validate", "sa_index_overlap", "sa_plan_reuse",
+    "sa_plan_fixed_jump", "sa_workspace_init", "sa_status_string", "sa_last_error", "sa_version",
 ]
 
 
@@ -85,6 +86,12 @@ def lib() -> ctypes.CDLL:
     L.sa_dense_decode.argtypes = [P(KVDesc), vp, vp, vp, vp, vp, sz, vp]
     L.sa_dense_workspace_size.argtypes = [P(KVDesc)]
     L.sa_dense_workspace_size.restype = sz
+    L.sa_dense_decode_scored.argtypes = [P(KVDesc), vp, vp, vp, vp, vp, vp, sz, vp]
+    L.sa_dense_scored_workspace_size.argtypes = [P(KVDesc)]
+    L.sa_dense_scored_workspace_size.restype = sz
+    L.sa_index_overlap.argtypes = [vp, vp, i64, i32, vp, vp]
+    L.sa_plan_reuse.argtypes = [vp, i64, i32, ctypes.c_double, vp, vp, vp]
+    L.sa_plan_fixed_jump.argtypes = [i32, i32, vp, vp]
     L.sa_decode_layer.argtypes = [P(LayerArgs), st, vp, vp]
     L.sa_layer_workspace_size.argtypes = [P(LayerArgs), st]
     L.sa_layer_workspace_size.restype = sz
@@ -96,7 +103,8 @@ def lib() -> ctypes.CDLL:
     L.sa_last_error.restype = ctypes.c_char_p
     L.sa_version.restype = ctypes.c_char_p
     for name in ["sa_score", "sa_block_summarize", "sa_topk", "sa_sparse_decode", "sa_dense_decode",
-                 "sa_decode_layer", "sa_plan_validate", "sa_workspace_init"]:
+                 "sa_dense_decode_scored", "sa_decode_layer", "sa_plan_validate",
+                 "sa_index_overlap", "sa_plan_reuse", "sa_plan_fixed_jump", "sa_workspace_init"]:
         getattr(L, name).restype = st
     _lib = L
     return L
@@ -301,6 +309,71 @@ def sa_dense_decode(q, k_cache, v_cache, out=None, softmax_scale=0.0, ws=None):
     check(L.sa_dense_decode(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
                             _ptr(ws), nbytes, ctypes.c_void_p(_stream(dev))))
     return out
+
+
+def sa_dense_decode_scored(q, k_cache, v_cache, out=None, scores=None, softmax_scale=0.0, ws=None):
+    """sa_dense_decode_scored: returns (out [B, Hq, d] fp32, scores [B, Hkv, N] fp32)."""
+    dev = _dev(q, k_cache, v_cache)
+    if v_cache.shape != k_cache.shape or v_cache.stride() != k_cache.stride():
+        raise ValueError("K and V caches must share shape and strides")
+    desc = make_desc(q, k_cache, softmax_scale)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    if scores is None:
+        scores = torch.empty((desc.batch, desc.n_kv_heads, desc.ctx_len), dtype=torch.float32,
+                             device=dev)
+    L = lib()
+    nbytes = L.sa_dense_scored_workspace_size(ctypes.byref(desc))
+    if ws is None:
+        ws = WORKSPACES.get(dev, ("dense_scored", _desc_key(desc)), nbytes)
+    check(L.sa_dense_decode_scored(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                   _ptr(out), _ptr(scores), _ptr(ws), nbytes,
+                                   ctypes.c_void_p(_stream(dev))))
+    return out, scores
+
+
+def sa_index_overlap(idx_a, idx_b, counts=None):
+    """sa_index_overlap over the last dimension: int32 counts of shape idx_a.shape[:-1]."""
+    dev = _dev(idx_a, idx_b)
+    for t in (idx_a, idx_b):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("index sets must be contiguous int32 tensors")
+    if idx_a.shape != idx_b.shape:
+        raise ValueError("index sets differ in shape: %s vs %s" % (tuple(idx_a.shape), tuple(idx_b.shape)))
+    k = idx_a.shape[-1]
+    rows = idx_a.numel() // k
+    if counts is None:
+        counts = torch.empty(idx_a.shape[:-1], dtype=torch.int32, device=dev)
+    check(lib().sa_index_overlap(_ptr(idx_a), _ptr(idx_b), rows, k, _ptr(counts),
+                                 ctypes.c_void_p(_stream(dev))))
+    return counts
+
+
+def _plan_out(n):
+    return (ctypes.c_int32 * max(n, 1))(), (ctypes.c_int32 * max(n, 1))()
+
+
+def sa_plan_reuse(overlap, total: int, theta: float, sensitive=None):
+    """sa_plan_reuse on a host [L, L] int64 overlap matrix; returns (modes, src) lists."""
+    import numpy as np
+    ov = np.ascontiguousarray(np.asarray(overlap, dtype=np.int64))
+    n = ov.shape[0]
+    if ov.shape != (n, n):
+        raise ValueError("overlap must be a square matrix")
+    sens = None
+    if sensitive is not None:
+        sens = (ctypes.c_int32 * max(n, 1))(*[int(bool(x)) for x in sensitive])
+    modes, src = _plan_out(n)
+    check(lib().sa_plan_reuse(ctypes.c_void_p(ov.ctypes.data), int(total), n, float(theta), sens,
+                              modes, src))
+    return list(modes)[:n], list(src)[:n]
+
+
+def sa_plan_fixed_jump(n_layers: int, step: int):
+    """sa_plan_fixed_jump; returns (modes, src) lists."""
+    modes, src = _plan_out(n_layers)
+    check(lib().sa_plan_fixed_jump(n_layers, step, modes, src))
+    return list(modes)[:n_layers], list(src)[:n_layers]
 
 
 def layer_args(q, k_cache, v_cache, score_kind=SA_SCORE_EXACT, k=0, *, kmin=None, kmax=None,

@@ -228,6 +228,11 @@ LayerWs layer_ws(const Cache& c, const sa_layer_args* a, sa_layer_mode mode) {
   LayerWs w{};
   if (mode == SA_LAYER_DENSE) {
     w.attend = plan_attend(c, kIdxDense, 0, 0).ws_bytes;
+  } else if (mode == SA_LAYER_DENSE_SELECT) {
+    const int64_t rows = (int64_t)c.B * c.Hkv;
+    w.scores = align_up((size_t)rows * c.N * sizeof(float), 256);
+    w.topk = align_up(topk_workspace_bytes(rows, c.N, a->k), 256);
+    w.attend = plan_attend(c, fused_scores_supported(c) ? kIdxDenseScored : kIdxDense, 0, 0).ws_bytes;
   } else {
     const sa_index_kind ik = index_kind_of(a->score_kind);
     const int32_t bs = a->score_kind == SA_SCORE_BLOCK_MINMAX ? a->aux.block_size : 0;
@@ -241,6 +246,26 @@ LayerWs layer_ws(const Cache& c, const sa_layer_args* a, sa_layer_mode mode) {
   }
   w.total = w.scores + w.topk + align_up(w.attend, 256);
   return w;
+}
+
+// Dense decode plus the exact score of every token: one fused launch where
+// the gather kernel takes the shape, else the scoring kernel and then the
+// dense decode.
+sa_status run_dense_scored(const Cache& c, const void* q, const void* k, const void* v, float* out,
+                           float* scores, void* ws, hipStream_t s) {
+  if (fused_scores_supported(c)) {
+    const AttendPlan p = plan_attend(c, kIdxDenseScored, 0, 0);
+    return hip_status(launch_attend(c, p, q, k, v, nullptr, 0, 0, out, ws, s, scores),
+                      "dense decode (scored) launch");
+  }
+  sa_status st = hip_status(launch_score_exact(c, q, k, scores, s), "exact scoring launch");
+  if (st != SA_OK) return st;
+  const AttendPlan p = plan_attend(c, kIdxDense, 0, 0);
+  return hip_status(launch_attend(c, p, q, k, v, nullptr, 0, 0, out, ws, s), "dense decode launch");
+}
+
+size_t dense_scored_ws(const Cache& c) {
+  return plan_attend(c, fused_scores_supported(c) ? kIdxDenseScored : kIdxDense, 0, 0).ws_bytes;
 }
 
 __global__ void zero_kernel(uint4* p, size_t n16, uint8_t* tail, size_t ntail) {
@@ -377,6 +402,25 @@ sa_status sa_dense_decode(const sa_kv_desc* desc, const void* q, const void* k_c
                     "sa_dense_decode launch");
 }
 
+size_t sa_dense_scored_workspace_size(const sa_kv_desc* desc) {
+  Cache c;
+  if (check_desc(desc, &c) != SA_OK) return 0;
+  return align_up(dense_scored_ws(c), 256);
+}
+
+sa_status sa_dense_decode_scored(const sa_kv_desc* desc, const void* q, const void* k_cache,
+                                 const void* v_cache, float* out, float* scores, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  Cache c;
+  sa_status st;
+  if ((st = check_desc(desc, &c)) != SA_OK) return st;
+  if ((st = check_attend_args(c, q, k_cache, v_cache, out)) != SA_OK) return st;
+  if ((st = check_ptr(scores, "scores", 4)) != SA_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, dense_scored_ws(c), "sa_dense_decode_scored")) != SA_OK)
+    return st;
+  return run_dense_scored(c, q, k_cache, v_cache, out, scores, ws, stream);
+}
+
 size_t sa_layer_workspace_size(const sa_layer_args* a, sa_layer_mode mode) {
   Cache c;
   if (!a || check_desc(&a->desc, &c) != SA_OK) return 0;
@@ -393,7 +437,8 @@ sa_status sa_decode_layer(const sa_layer_args* a, sa_layer_mode mode, int32_t* i
   Cache c;
   sa_status st;
   if ((st = check_desc(&a->desc, &c)) != SA_OK) return st;
-  if (mode != SA_LAYER_DENSE && mode != SA_LAYER_SPARSE && mode != SA_LAYER_REUSE)
+  if (mode != SA_LAYER_DENSE && mode != SA_LAYER_SPARSE && mode != SA_LAYER_REUSE &&
+      mode != SA_LAYER_DENSE_SELECT)
     return fail(SA_ERR_SHAPE, "unknown layer mode %d", (int)mode);
   if ((st = check_attend_args(c, a->q, a->k_cache, a->v_cache, a->out)) != SA_OK) return st;
   if (mode == SA_LAYER_DENSE) {
@@ -407,6 +452,27 @@ sa_status sa_decode_layer(const sa_layer_args* a, sa_layer_mode mode, int32_t* i
   // selection-based modes
   if (!known_score_kind(a->score_kind))
     return fail(SA_ERR_SHAPE, "unknown score kind %d", (int)a->score_kind);
+  if (mode == SA_LAYER_DENSE_SELECT) {
+    if (a->score_kind != SA_SCORE_EXACT)
+      return fail(SA_ERR_UNSUPPORTED, "DENSE_SELECT selects on exact scores only (score kind %d)",
+                  (int)a->score_kind);
+    if (a->k < 1 || a->k > c.N)
+      return fail(SA_ERR_SHAPE, "k %d outside [1, %lld]", a->k, (long long)c.N);
+    if ((st = check_sparse_idx(c, SA_IDX_TOKEN_PER_KV_HEAD, idx, a->k, 0)) != SA_OK) return st;
+    const LayerWs w = layer_ws(c, a, mode);
+    if ((st = check_ws(a->ws, a->ws_bytes, w.total, "sa_decode_layer(DENSE_SELECT)")) != SA_OK)
+      return st;
+    uint8_t* base = static_cast<uint8_t*>(a->ws);
+    float* scores = reinterpret_cast<float*>(base);
+    void* topk_ws = base + w.scores;
+    void* att_ws = base + w.scores + w.topk;
+    if ((st = run_dense_scored(c, a->q, a->k_cache, a->v_cache, a->out, scores, att_ws, stream)) !=
+        SA_OK)
+      return st;
+    const int64_t rows = (int64_t)c.B * c.Hkv;
+    return hip_status(launch_topk(scores, rows, c.N, c.N, a->k, idx, topk_ws, stream),
+                      "sa_decode_layer(DENSE_SELECT) top-k launch");
+  }
   const sa_index_kind ik = index_kind_of(a->score_kind);
   const int32_t bs = a->score_kind == SA_SCORE_BLOCK_MINMAX ? a->aux.block_size : 0;
   if (a->score_kind == SA_SCORE_BLOCK_MINMAX) {
@@ -445,7 +511,8 @@ sa_status sa_plan_validate(const int32_t* modes, const int32_t* src, int32_t n_l
   bool has_idx[4096];
   for (int32_t l = 0; l < n_layers; ++l) {
     const int32_t m = modes[l];
-    if (m != SA_LAYER_DENSE && m != SA_LAYER_SPARSE && m != SA_LAYER_REUSE)
+    if (m != SA_LAYER_DENSE && m != SA_LAYER_SPARSE && m != SA_LAYER_REUSE &&
+        m != SA_LAYER_DENSE_SELECT)
       return fail(SA_ERR_SHAPE, "layer %d: unknown mode %d", l, m);
     if (m == SA_LAYER_REUSE) {
       const int32_t s = src[l];
@@ -454,6 +521,103 @@ sa_status sa_plan_validate(const int32_t* modes, const int32_t* src, int32_t n_l
       if (!has_idx[s]) return fail(SA_ERR_SHAPE, "layer %d: reuse source %d holds no index set", l, s);
     }
     has_idx[l] = (m != SA_LAYER_DENSE);
+  }
+  return ok();
+}
+
+sa_status sa_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t n_rows, int32_t k,
+                           int32_t* counts, hipStream_t stream) {
+  sa_status st;
+  if ((st = check_ptr(idx_a, "idx_a", 4)) != SA_OK) return st;
+  if ((st = check_ptr(idx_b, "idx_b", 4)) != SA_OK) return st;
+  if ((st = check_ptr(counts, "counts", 4)) != SA_OK) return st;
+  if (n_rows < 1 || n_rows > INT32_MAX)
+    return fail(SA_ERR_SHAPE, "n_rows %lld outside [1, 2^31)", (long long)n_rows);
+  if (k < 1) return fail(SA_ERR_SHAPE, "k %d must be >= 1", k);
+  return hip_status(launch_index_overlap(idx_a, idx_b, n_rows, k, counts, stream),
+                    "sa_index_overlap launch");
+}
+
+sa_status sa_plan_reuse(const int64_t* overlap, int64_t total, int32_t n_layers, double theta,
+                        const int32_t* sensitive, int32_t* modes, int32_t* src) {
+  constexpr int kMaxLayers = 256;
+  if (!overlap || !modes || !src) return fail(SA_ERR_NULL, "overlap, modes or src is null");
+  if (n_layers < 1 || n_layers > kMaxLayers)
+    return fail(SA_ERR_SHAPE, "n_layers %d outside [1, %d]", n_layers, kMaxLayers);
+  if (total < 1) return fail(SA_ERR_SHAPE, "total %lld must be >= 1", (long long)total);
+  if (isnan(theta)) return fail(SA_ERR_SHAPE, "theta is NaN");
+  const int L = n_layers;
+  for (int i = 0; i < L; ++i)
+    for (int j = i + 1; j < L; ++j) {
+      const int64_t o = overlap[(int64_t)i * L + j];
+      if (o < 0 || o > total)
+        return fail(SA_ERR_SHAPE, "overlap[%d][%d] = %lld outside [0, total]", i, j, (long long)o);
+    }
+  // reuse[i][j]: layer j may reuse the set of layer i (vertical move allowed)
+  auto may_reuse = [&](int i, int j) {
+    if (sensitive && sensitive[j]) return false;
+    return (double)overlap[(int64_t)i * L + j] / (double)total > theta;
+  };
+  // Suffix dynamic programme over reset layers: best[j] = (full layers,
+  // summed overlap) of layers j..L-1 given that layer j resets; next[j] = the
+  // following reset layer (L: none).  The reused run after reset j is
+  // j+1..j'-1, so the policy's path is (j, j) -> (j, j+1) -> ... -> (j, j'-1)
+  // -> (j', j').
+  int32_t fulls[kMaxLayers + 1];
+  int64_t sim[kMaxLayers + 1];
+  int32_t next[kMaxLayers + 1];
+  fulls[L] = 0;
+  sim[L] = 0;
+  for (int j = L - 1; j >= 0; --j) {
+    int32_t bf = INT32_MAX;
+    int64_t bs = -1;
+    int32_t bn = -1;
+    int64_t run = 0;  // summed overlap of layers j+1 .. jn-1 reusing layer j
+    for (int jn = j + 1; jn <= L; ++jn) {
+      // candidate: layers j+1 .. jn-1 reuse j (checked below on the way),
+      // jn resets (jn == L: no further reset); on a tie the later jn wins
+      const int32_t f = 1 + fulls[jn];
+      const int64_t sv = run + sim[jn];
+      if (f < bf || (f == bf && sv >= bs)) {
+        bf = f;
+        bs = sv;
+        bn = jn;
+      }
+      if (jn == L || !may_reuse(j, jn)) break;  // layer jn cannot join the run
+      run += overlap[(int64_t)j * L + jn];
+    }
+    fulls[j] = bf;
+    sim[j] = bs;
+    next[j] = bn;
+  }
+  for (int l = 0; l < L; ++l) src[l] = -1;
+  int j = 0;
+  while (j < L) {
+    const int jn = next[j];
+    modes[j] = jn > j + 1 ? SA_LAYER_DENSE_SELECT : SA_LAYER_DENSE;
+    for (int t = j + 1; t < jn; ++t) {
+      modes[t] = SA_LAYER_REUSE;
+      src[t] = j;
+    }
+    j = jn;
+  }
+  return ok();
+}
+
+sa_status sa_plan_fixed_jump(int32_t n_layers, int32_t step, int32_t* modes, int32_t* src) {
+  if (!modes || !src) return fail(SA_ERR_NULL, "modes or src is null");
+  if (n_layers < 1 || n_layers > 256)
+    return fail(SA_ERR_SHAPE, "n_layers %d outside [1, 256]", n_layers);
+  if (step < 1) return fail(SA_ERR_SHAPE, "step %d must be >= 1", step);
+  for (int32_t l = 0; l < n_layers; ++l) {
+    if (l % step == 0) {
+      const bool reused = step > 1 && l + 1 < n_layers;
+      modes[l] = reused ? SA_LAYER_DENSE_SELECT : SA_LAYER_DENSE;
+      src[l] = -1;
+    } else {
+      modes[l] = SA_LAYER_REUSE;
+      src[l] = l - l % step;
+    }
   }
   return ok();
 }

@@ -64,6 +64,8 @@ struct AttendArgs {
   int32_t chunk;
   int32_t nsplit;
   int32_t rounds;  // gather kernel: slot rounds per wave
+  float* scores;   // kIdxDenseScored: [rows, N] exact scores
+  float sscale;    // softmax scale (the exact score's scale)
   float* out;
   float* part;  // [rows, nsplit, G, D + 2]: o[G][D], m[G], l[G]
 };
@@ -261,7 +263,7 @@ __device__ __forceinline__ int32_t slot_token(const AttendArgs& a, int row, int 
                                               int64_t s1, bool& ok) {
   ok = j < s1;
   const int64_t jj = ok ? j : s1 - 1;
-  if constexpr (MODE == kIdxDense) {
+  if constexpr (MODE == kIdxDense || MODE == kIdxDenseScored) {
     return (int32_t)jj;
   } else if constexpr (MODE == kIdxTokenPerHead) {
     return a.idx[(int64_t)row * a.n_idx + jj];
@@ -278,7 +280,7 @@ __device__ __forceinline__ int32_t slot_token(const AttendArgs& a, int row, int 
 // nontemporal (streaming); gathered rows use ordinary loads.
 template <int MODE>
 __device__ __forceinline__ uint4 ld_kv(const uint8_t* p) {
-  if constexpr (MODE == kIdxDense) return ld16_nt(p);
+  if constexpr (MODE == kIdxDense || MODE == kIdxDenseScored) return ld16_nt(p);
   else return ld16(p);
 }
 
@@ -384,6 +386,16 @@ __global__ __launch_bounds__(64 * kMaxSparseWaves) void attend_sparse_kernel(Att
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) lg[i][h] = (rq == 0 && ok[i]) ? acc[h] * a.qscale : -INFINITY;
+      if constexpr (MODE == kIdxDenseScored) {
+        // the token's exact score from the same logits; a lane past the end
+        // holds the last token (slot_token clamps) and rewrites its score
+        if (rq == 0) {
+          float sc = 0.0f;
+#pragma unroll
+          for (int h = 0; h < G; ++h) sc += acc[h];
+          a.scores[(int64_t)row * a.N + tok[i]] = sc * a.sscale;
+        }
+      }
     }
     // 4. one max per head over the wave's tokens (valid in lanes 0..15), then
     //    p = 2^(logit - max) and its sum
@@ -657,6 +669,9 @@ hipError_t dispatch_sparse(int waves, int mode, dim3 grid, const AttendArgs& a, 
     case kIdxBlockPerHead:
       hipLaunchKernelGGL((attend_sparse_kernel<G, kIdxBlockPerHead, TILES>), grid, block, 0, s, a);
       break;
+    case kIdxDenseScored:
+      hipLaunchKernelGGL((attend_sparse_kernel<G, kIdxDenseScored, TILES>), grid, block, 0, s, a);
+      break;
     default:
       hipLaunchKernelGGL((attend_sparse_kernel<G, kIdxDense, TILES>), grid, block, 0, s, a);
       break;
@@ -720,7 +735,7 @@ int lanes_per_row(const Cache& c) { return c.D * (c.kv_dtype == SA_BF16 ? 2 : 4)
 AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs) {
   AttendPlan p{};
   p.mode = mode;
-  if (mode == kIdxDense) {
+  if (is_dense_mode(mode)) {
     p.n_slots = c.N;
   } else if (mode == kIdxBlockPerHead) {
     p.n_slots = (int64_t)n_idx * bs;
@@ -750,7 +765,7 @@ AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs) {
         }
       }
       waves = (int)((p.n_slots + per_wave - 1) / per_wave);
-    } else if (mode == kIdxDense) {
+    } else if (is_dense_mode(mode)) {
       // long contiguous scans: several rounds per wave merged online, so a
       // workgroup covers waves * rounds * 64 tokens and few split partials
       // are written (on 128 rows of 32768 tokens, 4 waves x 8 rounds: 323 us
@@ -769,7 +784,7 @@ AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs) {
       if (waves == 1)
         while (per_wave > 16 && rows * ((p.n_slots + per_wave - 1) / per_wave) < 512) per_wave /= 2;
     }
-    if (mode != kIdxDense) {
+    if (!is_dense_mode(mode)) {
       if (sparse_waves_override()) waves = sparse_waves_override();
       if (sparse_chunk_override()) per_wave = sparse_chunk_override();
     }
@@ -791,10 +806,14 @@ AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs) {
   return p;
 }
 
+bool fused_scores_supported(const Cache& c) { return use_wave_kernel(c); }
+
 hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, const void* k,
                          const void* v, const int32_t* idx, int32_t n_idx, int32_t bs, float* out,
-                         void* ws, hipStream_t s) {
+                         void* ws, hipStream_t s, float* scores) {
   AttendArgs a{};
+  a.scores = scores;
+  a.sscale = c.scale;
   a.q = q;
   a.q_dtype = c.q_dtype;
   a.k = static_cast<const uint8_t*>(k);

@@ -32,9 +32,22 @@ hipError_t launch_score_indexer(int32_t B, int64_t N, int32_t H, int32_t Di, con
 size_t topk_workspace_bytes(int64_t n_rows, int64_t n, int32_t k);
 hipError_t launch_topk(const float* scores, int64_t n_rows, int64_t n, int64_t row_stride, int32_t k,
                        int32_t* idx, void* ws, hipStream_t s);
+// counts[r] = |idx_a[r, :] intersect idx_b[r, :]|, rows of k ascending indices.
+hipError_t launch_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t n_rows, int32_t k,
+                                int32_t* counts, hipStream_t s);
 
 // ----------------------------------------------------------- attention
-enum IndexMode : int { kIdxTokenPerHead = 0, kIdxTokenShared = 1, kIdxBlockPerHead = 2, kIdxDense = 3 };
+// kIdxDenseScored: dense decode that also writes each token's exact score
+// (scale * sum_g q_g . k_t) from the logits it computes anyway.
+enum IndexMode : int {
+  kIdxTokenPerHead = 0,
+  kIdxTokenShared = 1,
+  kIdxBlockPerHead = 2,
+  kIdxDense = 3,
+  kIdxDenseScored = 4
+};
+
+inline bool is_dense_mode(int mode) { return mode == kIdxDense || mode == kIdxDenseScored; }
 
 struct AttendPlan {
   int mode;
@@ -47,9 +60,11 @@ struct AttendPlan {
 };
 
 AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs);
+// scores: kIdxDenseScored only, [B, Hkv, N] fp32.
 hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, const void* k,
                          const void* v, const int32_t* idx, int32_t n_idx, int32_t bs, float* out,
-                         void* ws, hipStream_t s);
+                         void* ws, hipStream_t s, float* scores = nullptr);
+bool fused_scores_supported(const Cache& c);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 

@@ -582,6 +582,61 @@ bool use_mw(int64_t n_rows, int64_t n, int32_t k) {
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Overlap of two ascending index sets per row: each thread takes entries of
+// row b and binary-searches them in row a (staged in LDS when it fits).
+constexpr int kOverlapThreads = 256;
+constexpr int kOverlapLds = 8192;
+
+__device__ __forceinline__ bool sorted_contains(const int32_t* a, int32_t k, int32_t x) {
+  int32_t lo = 0, hi = k;  // search [lo, hi)
+  while (lo < hi) {
+    const int32_t mid = (lo + hi) >> 1;
+    const int32_t v = a[mid];
+    if (v == x) return true;
+    if (v < x) lo = mid + 1;
+    else hi = mid;
+  }
+  return false;
+}
+
+__global__ __launch_bounds__(kOverlapThreads) void index_overlap_kernel(const int32_t* __restrict__ ia,
+                                                                        const int32_t* __restrict__ ib,
+                                                                        int32_t k,
+                                                                        int32_t* __restrict__ counts) {
+  __shared__ int32_t s_a[kOverlapLds];
+  __shared__ int32_t s_cnt[kOverlapThreads / 64];
+  const int64_t row = blockIdx.x;
+  const int32_t* a = ia + row * k;
+  const int32_t* b = ib + row * k;
+  const bool in_lds = k <= kOverlapLds;
+  if (in_lds) {
+    for (int32_t i = threadIdx.x; i < k; i += kOverlapThreads) s_a[i] = a[i];
+    __syncthreads();
+  }
+  int32_t c = 0;
+  for (int32_t i = threadIdx.x; i < k; i += kOverlapThreads) {
+    const int32_t x = b[i];
+    c += (in_lds ? sorted_contains(s_a, k, x) : sorted_contains(a, k, x)) ? 1 : 0;
+  }
+  // wave sum, then the workgroup's waves
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
+  if ((threadIdx.x & 63) == 0) s_cnt[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t t = 0;
+    for (int w = 0; w < kOverlapThreads / 64; ++w) t += s_cnt[w];
+    counts[row] = t;
+  }
+}
+
+hipError_t launch_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t n_rows, int32_t k,
+                                int32_t* counts, hipStream_t s) {
+  hipLaunchKernelGGL(index_overlap_kernel, dim3((unsigned)n_rows), dim3(kOverlapThreads), 0, s,
+                     idx_a, idx_b, k, counts);
+  return hipGetLastError();
+}
+
 size_t topk_workspace_bytes(int64_t n_rows, int64_t n, int32_t k) {
   return use_mw(n_rows, n, k) ? (size_t)n_rows * sizeof(MwRow) : 0;
 }
