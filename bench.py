@@ -63,6 +63,13 @@ def parse():
                         "per-KV-head low-dim indexer, then top-k and attend) against dense decode "
                         "at 2x-500x sparsity on the llama32k and batch128k shapes; prints a table "
                         "and one JSON line")
+    p.add_argument("--hylra", action="store_true",
+                   help="layer-reuse policy: an 8-layer llama32k-shaped decode whose queries and "
+                        "keys correlate across layers; profiles every layer, plans with the DP "
+                        "planner and times all-dense, all-sparse, the fixed-jump baseline and the "
+                        "planned policy; prints one JSON line")
+    p.add_argument("--theta", type=float, default=0.35,
+                   help="overlap threshold of the layer-reuse planner (--hylra)")
     p.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                    help="print the calibrated HBM traffic per dispatch from two rocprofv3 --pmc "
                         "runs of `bench.py --profile` (FETCH_SIZE, then WRITE_SIZE) and exit")
@@ -369,6 +376,130 @@ def sweep(args):
                       "rows": results, "device": torch.cuda.get_device_name(0)}), flush=True)
 
 
+def hylra(args):
+    """Layer-reuse policy on 8 layers of the llama32k shape.
+
+    Queries and keys of layer l follow x_l = rho_l x_{l-1} + sqrt(1 - rho_l^2) z_l
+    with the hylra32k schedule (a weakly correlated layer 4), drawn on the
+    device (timings depend on the shapes and the plan, not on the values).
+    Offline: every layer runs DENSE_SELECT, sa_index_overlap gives the
+    overlap matrix, sa_plan_reuse the policy.  Then one 8-layer decode step is
+    timed under each plan."""
+    import torch
+    import sa_synth as S
+    import top_sparse_decode_sa_amd as T
+
+    T.lib()
+    dev = torch.device("cuda", 0)
+    c = S.CONFIGS["hylra32k"]
+    B, Hq, Hkv, d, N, k, L = c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.ctx_len, c.k, c.n_layers
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    log("hylra: drawing %d layers (%.1f GB of KV)" % (L, L * c.kv_bytes() / 1e9))
+    qs, ks, vs = [], [], []
+    xq = torch.randn((B, Hq, d), generator=gen, device=dev)
+    xk = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=dev)
+    for l in range(L):
+        if l > 0:
+            r = c.rho_sched[l]
+            xq = r * xq + (1 - r * r) ** 0.5 * torch.randn(xq.shape, generator=gen, device=dev)
+        qs.append(xq.to(torch.bfloat16).contiguous())
+        kl = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=dev)
+        for b in range(B):     # the fp32 latent chain one sequence at a time
+            z = torch.randn((Hkv, N, d), generator=gen, device=dev)
+            if l > 0:
+                r = c.rho_sched[l]
+                z = r * xk[b].float() + (1 - r * r) ** 0.5 * z
+            xk[b] = z.to(torch.bfloat16)
+            kl[b] = xk[b]
+        ks.append(kl)
+        vs.append(torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=dev).normal_(generator=gen))
+    del xk
+    torch.cuda.synchronize()
+    outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(L)]
+    largs = []
+    for l in range(L):
+        a, _, _ = T.layer_args(qs[l], ks[l], vs[l], T.SA_SCORE_EXACT, k, out=outs[l])
+        largs.append(a)
+    ws = {}
+    for mode in (T.SA_LAYER_DENSE, T.SA_LAYER_SPARSE, T.SA_LAYER_REUSE, T.SA_LAYER_DENSE_SELECT):
+        ws[mode] = T.WORKSPACES.get(dev, ("hylra", mode), T.sa_layer_workspace_size(largs[0], mode))
+    idx = [torch.empty((B, Hkv, k), dtype=torch.int32, device=dev) for _ in range(L)]
+
+    def run(modes, src):
+        for l in range(L):
+            m = modes[l]
+            i = idx[src[l]] if m == T.SA_LAYER_REUSE else (None if m == T.SA_LAYER_DENSE else idx[l])
+            T.sa_decode_layer(largs[l], m, i, dev, ws[m])
+
+    # offline profiling: every layer full attention + its top-k, then overlaps
+    run([T.SA_LAYER_DENSE_SELECT] * L, [-1] * L)
+    M = np.zeros((L, L), dtype=np.int64)
+    for i in range(L):
+        for j in range(i + 1, L):
+            M[i, j] = int(T.sa_index_overlap(idx[i], idx[j]).sum().item())
+    total = B * Hkv * k
+    ratio = M / total
+    plans = {
+        "all_dense": ([T.SA_LAYER_DENSE] * L, [-1] * L),
+        "all_sparse_exact": ([T.SA_LAYER_SPARSE] * L, [-1] * L),
+        "fixed_jump3": T.sa_plan_fixed_jump(L, 3),
+        "hylra_dp": T.sa_plan_reuse(M, total, args.theta),
+    }
+    reps = max(3, min(args.steps, 20))
+    res = {}
+    for name, (modes, src) in plans.items():
+        T.sa_plan_validate(modes, src)
+        for _ in range(2):
+            run(modes, src)
+        torch.cuda.synchronize()
+        # a long launch ahead of the timed region lets the host queue every
+        # layer before the GPU reaches it
+        T.sa_decode_layer(largs[0], T.SA_LAYER_DENSE, None, dev, ws[T.SA_LAYER_DENSE])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run(modes, src)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        reused = [ratio[src[l], l] for l in range(L) if modes[l] == T.SA_LAYER_REUSE]
+        res[name] = {"modes": modes, "src": src, "us_per_step": round(us, 1),
+                     "full_layers": sum(m in (T.SA_LAYER_DENSE, T.SA_LAYER_DENSE_SELECT)
+                                        for m in modes),
+                     "min_reused_overlap": round(min(reused), 4) if reused else None,
+                     "mean_reused_overlap": round(float(np.mean(reused)), 4) if reused else None}
+        log("hylra: %s %.1f us" % (name, us))
+    # one layer per mode (layer 0; REUSE over layer 0's own set)
+    per_layer = {}
+    for name, m in (("dense", T.SA_LAYER_DENSE), ("dense_select", T.SA_LAYER_DENSE_SELECT),
+                    ("sparse_exact", T.SA_LAYER_SPARSE), ("reuse", T.SA_LAYER_REUSE)):
+        i = None if m == T.SA_LAYER_DENSE else idx[0]
+        for _ in range(2):
+            T.sa_decode_layer(largs[0], m, i, dev, ws[m])
+        T.sa_decode_layer(largs[1], T.SA_LAYER_DENSE, None, dev, ws[T.SA_LAYER_DENSE])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            T.sa_decode_layer(largs[0], m, i, dev, ws[m])
+        e1.record()
+        torch.cuda.synchronize()
+        per_layer[name] = round(e0.elapsed_time(e1) / reps * 1e3, 1)
+    log("hylra: per layer %s" % per_layer)
+    base = res["all_dense"]["us_per_step"]
+    for r in res.values():
+        r["speedup_vs_dense"] = round(base / r["us_per_step"], 3)
+    print(json.dumps({
+        "bench": "layer-reuse policy, 8-layer decode step", "unit": "us per 8-layer step (HIP events)",
+        "config": {"workload": "hylra32k: llama32k shape x 8 layers, per-layer correlated q and K",
+                   "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d, "ctx_len": N,
+                   "k": k, "rho_sched": list(c.rho_sched), "theta": args.theta},
+        "overlap_ratio": [[round(float(x), 4) for x in row] for row in ratio],
+        "plans": res, "us_per_layer": per_layer,
+        "data": "drawn on the device (torch generator, seed %d)" % args.seed,
+        "device": torch.cuda.get_device_name(0)}), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -379,6 +510,9 @@ def main():
         return
     if args.gpus == 1 and args.sweep:
         sweep(args)
+        return
+    if args.gpus == 1 and args.hylra:
+        hylra(args)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

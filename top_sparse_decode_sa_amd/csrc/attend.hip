@@ -295,9 +295,17 @@ __device__ __forceinline__ uint4 ld_kv(const uint8_t* p) {
 // rounds merge into a running (max, sum, o) per head.  The waves of a
 // workgroup merge in LDS and write one result.
 constexpr int kMaxSparseWaves = 12;
+// The scored dense scan keeps a few more values live per round; at most 4
+// waves per workgroup give it the registers to do so without spilling.
+constexpr int kMaxScoredWaves = 4;
+
+template <int MODE>
+constexpr int max_waves() {
+  return MODE == kIdxDenseScored ? kMaxScoredWaves : kMaxSparseWaves;
+}
 
 template <int G, int MODE, int TILES>
-__global__ __launch_bounds__(64 * kMaxSparseWaves) void attend_sparse_kernel(AttendArgs a) {
+__global__ __launch_bounds__(64 * max_waves<MODE>()) void attend_sparse_kernel(AttendArgs a) {
   static_assert(G >= 1 && G <= 4, "query heads of a group fit MFMA rows 0..3");
   constexpr int D = 128;
   constexpr int W = kMaxSparseWaves;
@@ -387,13 +395,14 @@ __global__ __launch_bounds__(64 * kMaxSparseWaves) void attend_sparse_kernel(Att
 #pragma unroll
       for (int h = 0; h < G; ++h) lg[i][h] = (rq == 0 && ok[i]) ? acc[h] * a.qscale : -INFINITY;
       if constexpr (MODE == kIdxDenseScored) {
-        // the token's exact score from the same logits; a lane past the end
-        // holds the last token (slot_token clamps) and rewrites its score
-        if (rq == 0) {
+        // the token's exact score from the same logits; in a dense scan slot
+        // j is token j (recomputed here, so the token ids need not stay live
+        // in registers)
+        if (rq == 0 && ok[i]) {
           float sc = 0.0f;
 #pragma unroll
           for (int h = 0; h < G; ++h) sc += acc[h];
-          a.scores[(int64_t)row * a.N + tok[i]] = sc * a.sscale;
+          a.scores[(int64_t)row * a.N + s0 + 16 * i + n] = sc * a.sscale;
         }
       }
     }
@@ -750,7 +759,7 @@ AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs) {
     const int64_t wn = (p.n_slots + 63) / 64;
     int waves = 1, rounds = 1;
     int64_t per_wave = 64;
-    if (rows >= 128 && wn <= kMaxSparseWaves) {
+    if (rows >= 128 && wn <= kMaxSparseWaves && mode != kIdxDenseScored) {
       // At least 128 rows (half the chip's CUs at one workgroup each) and at
       // most 12 waves' worth of slots: one workgroup takes a whole row in one
       // round, so no split partials and no combine launch (on 128 rows of
@@ -772,6 +781,7 @@ AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs) {
       // + 6 us combine, against 328-340 us for 4 x 4, 8 x 4 and 8 x 8)
       waves = dense_waves_override() ? dense_waves_override() : 4;
       rounds = dense_rounds_override() ? dense_rounds_override() : 8;
+      if (mode == kIdxDenseScored) waves = std::min(waves, kMaxScoredWaves);
     } else {
       // selections split so that about 512 workgroups (two per CU) run; a
       // combine pass merges the splits
