@@ -112,7 +112,13 @@ typedef enum {
    * q_idx [batch, n_kv_heads, n_idx_heads, idx_dim] bf16, k_idx [batch,
    * n_kv_heads, ctx_len, idx_dim] bf16, w [batch, n_kv_heads, n_idx_heads]
    * fp32, all contiguous.  Output [batch, n_kv_heads, ctx_len] fp32. */
-  SA_SCORE_INDEXER_PER_KV_HEAD = 3
+  SA_SCORE_INDEXER_PER_KV_HEAD = 3,
+  /* Exact score per QUERY head, for selection that differs between the query
+   * heads of a group ([P3] section 2: the sparse decode kernel takes
+   * irregular patterns per token, per query and per head):
+   *   scores[b, h, t] = scale * q[b, h, :] . K[b, h / G, t, :]
+   * Output [batch, n_q_heads, ctx_len] fp32; batch * n_q_heads <= 65535. */
+  SA_SCORE_EXACT_PER_Q_HEAD = 4
 } sa_score_kind;
 
 typedef struct {
@@ -166,13 +172,18 @@ typedef enum {
   SA_IDX_TOKEN_SHARED = 1,
   /* idx [batch, n_idx_rows=n_kv_heads, n_idx] ids of block_size-token blocks;
    * a block covers tokens [j*block_size, min((j+1)*block_size, ctx_len)). */
-  SA_IDX_BLOCK_PER_KV_HEAD = 2
+  SA_IDX_BLOCK_PER_KV_HEAD = 2,
+  /* idx [batch, n_q_heads, n_idx] token positions, one set per QUERY head
+   * ([P3] section 2); query head h reads its own tokens of KV head h / G.
+   * batch * n_q_heads <= 65535. */
+  SA_IDX_TOKEN_PER_Q_HEAD = 3
 } sa_index_kind;
 
 /* Attention of every query head over the selected set of its row only:
  * [P5] DSA Stage 2 and [P3] section 3.C (a decode kernel for irregular
  * token-level sparsity that reads O(k*d) of the cache).  For query head h of
- * sequence b, with S the selected tokens of row (b, h / G):
+ * sequence b, with S the selected tokens of row (b, h / G) (of row (b, h)
+ * for SA_IDX_TOKEN_PER_Q_HEAD):
  *   out[b, h, :] = sum_{t in S} softmax_S(scale * q[b,h,:] . K[b,h/G,t,:]) * V[b,h/G,t,:]
  * out: [batch, n_q_heads, head_dim] fp32.  Preconditions: every index in
  * range and the indices of one row distinct (not checked); 1 <= n_idx.
@@ -219,7 +230,7 @@ typedef enum {
 /* Everything one layer's decode step needs.  The score kind fixes the index
  * kind: EXACT and INDEXER_PER_KV_HEAD -> SA_IDX_TOKEN_PER_KV_HEAD,
  * BLOCK_MINMAX -> SA_IDX_BLOCK_PER_KV_HEAD (aux.block_size), INDEXER ->
- * SA_IDX_TOKEN_SHARED.
+ * SA_IDX_TOKEN_SHARED, EXACT_PER_Q_HEAD -> SA_IDX_TOKEN_PER_Q_HEAD.
  * k is the number of tokens (blocks for BLOCK_MINMAX) kept per row. */
 typedef struct {
   sa_kv_desc desc;
@@ -239,7 +250,8 @@ typedef struct {
  * reuse the top-k index set an earlier layer produced, unchanged.
  *   DENSE:  sa_dense_decode.
  *   SPARSE: sa_score -> sa_topk -> sa_sparse_decode, the index set written to
- *           idx ([batch, n_kv_heads, k] or [batch, k] for INDEXER).
+ *           idx ([batch, n_kv_heads, k]; [batch, k] for INDEXER; [batch,
+ *           n_q_heads, k] for EXACT_PER_Q_HEAD).
  *   REUSE:  sa_sparse_decode over idx exactly as given (no scoring, no top-k);
  *           idx must hold the set of an earlier SPARSE or DENSE_SELECT layer
  *           with the same score kind and k.

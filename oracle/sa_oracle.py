@@ -81,6 +81,18 @@ def scores_exact(q_group: np.ndarray, k_row: np.ndarray, scale: float) -> np.nda
     return s
 
 
+def scores_per_query_head(q_head: np.ndarray, k_row: np.ndarray, scale: float) -> np.ndarray:
+    """Exact token scores of ONE query head, for selection that differs
+    between the query heads of a group.
+
+    [P3] section 2 (hardware implementation): the sparse decode kernel takes
+    irregular sparsity per token, per query and per head.  Query head h scores
+    the keys of its KV head on its own:  s_t = (q_h . K_t) * scale.
+    q_head: [d]; k_row: [N, d] -> [N] float64.
+    """
+    return (k_row @ q_head) * scale
+
+
 def block_summaries(k_row: np.ndarray, block_size: int):
     """Elementwise min and max of the keys of each fixed-size token block.
 

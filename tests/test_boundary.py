@@ -259,3 +259,14 @@ def test_dense_scored_and_dense_select_errors():
                              None) == Bn.SA_ERR_UNSUPPORTED
     assert L.sa_decode_layer(ctypes.byref(a), 4, FAKE, None) == Bn.SA_ERR_SHAPE
     T.sa_plan_validate([Bn.SA_LAYER_DENSE_SELECT, Bn.SA_LAYER_REUSE], [-1, 0])
+
+
+def test_per_query_head_row_limit():
+    """Per-query-head rows are batch * n_q_heads grid rows: above 65535 the
+    calls refuse on the host."""
+    L = T.lib()
+    d = _desc(batch=2049, n_q_heads=32, n_kv_heads=8)     # 16392 KV rows, 65568 query rows
+    assert _sparse(d, ik=Bn.SA_IDX_TOKEN_PER_Q_HEAD) == Bn.SA_ERR_SHAPE
+    assert L.sa_score(ctypes.byref(d), Bn.SA_SCORE_EXACT_PER_Q_HEAD, FAKE, FAKE, None, FAKE,
+                      None) == Bn.SA_ERR_SHAPE
+    assert _sparse(_desc(), ik=4) == Bn.SA_ERR_SHAPE        # unknown index kind

@@ -117,6 +117,40 @@ def test_llama32k_exact_topk_at_50x(seed):
     rows = _sample_rows(c, 12, seed)
     _check_exact_layer(w, 0, qd, kd, vd, rows, "llama32k/%d" % seed)
     _check_dense(w, 0, qd, kd, vd, rows[:4], "llama32k/%d" % seed)
+    if seed == 0:
+        _check_per_q_head(w, qd, kd, vd, rows[:4], "llama32k/%d per-q-head" % seed)
+
+
+def _check_per_q_head(w, qd, kd, vd, rows, label):
+    """The same cache with one selection per query head (512 rows of 655):
+    sa_topk bit-exact on the GPU's scores for every row, and on sampled
+    (sequence, KV head) rows every grouped head's scores, set and output
+    against the oracle."""
+    c = w.cfg
+    scale = O.default_scale(c.head_dim)
+    args, out, d_ = T.layer_args(qd, kd, vd, T.SA_SCORE_EXACT_PER_Q_HEAD, c.k)
+    idx = torch.empty((c.batch, c.n_q_heads, c.k), dtype=torch.int32, device=dev())
+    T.sa_decode_layer(args, T.SA_LAYER_SPARSE, idx, d_)
+    scores = T.sa_score(qd, kd, T.SA_SCORE_EXACT_PER_Q_HEAD)
+    torch.cuda.synchronize()
+    idx_h, out_h, s_gpu = idx.cpu().numpy(), out.cpu().numpy(), scores.cpu().numpy()
+    for b in range(c.batch):
+        for h in range(c.n_q_heads):
+            assert np.array_equal(idx_h[b, h], O.topk(s_gpu[b, h].astype(np.float64), c.k)), (b, h)
+    q_h = O.widen(qd.cpu().view(torch.uint16).numpy())
+    counts = {"exact": 0, "excused": 0}
+    for b, r in rows:
+        kf = O.widen(w.k_row(0, b, r))
+        vf = O.widen(w.v_row(0, b, r))
+        for h in range(r * c.group, (r + 1) * c.group):
+            s64 = O.scores_per_query_head(q_h[b, h], kf, scale)
+            assert np.max(np.abs(s_gpu[b, h] - s64)) <= score_tol(s64), (label, b, h)
+            v = O.index_set_verdict(s64, idx_h[b, h], c.k)
+            assert not v.startswith("failed"), (label, b, h, v)
+            counts[v] += 1
+            want = O.attend(q_h[b, h][None], kf, vf, idx_h[b, h], scale)
+            check_out(out_h[b, h][None], want, c.dtype, "%s %d,%d" % (label, b, h))
+    say("%s: index sets %s" % (label, counts))
 
 
 @pytest.mark.timeout(600)

@@ -329,3 +329,55 @@ def test_tiny_config_end_to_end():
     full = T.sa_sparse_decode(qd, kd, vd, idx_all).cpu().numpy()
     check_out(full, wantd, "f32", "tiny k=N")
     assert np.max(np.abs(full - dense)) <= 1e-5
+
+
+# ---------------------------------------------------- per-query-head index sets
+
+@pytest.mark.parametrize("dtype,d,G,B,N,k", [
+    ("bf16", 128, 4, 2, 3000, 61), ("bf16", 128, 4, 40, 2000, 40), ("bf16", 128, 1, 2, 777, 100),
+    ("f32", 64, 8, 1, 1500, 33), ("bf16", 64, 2, 2, 999, 999)])
+def test_per_query_head_selection(dtype, d, G, B, N, k):
+    """Every query head scores, selects and attends on its own: scores
+    against the oracle, sa_topk bit-exact on the GPU's scores, outputs
+    against oracle attention of each head over its own set; the layer entry
+    point equals the single calls."""
+    say("per-q-head %s d=%d G=%d B=%d N=%d k=%d" % (dtype, d, G, B, N, k))
+    Hkv = 2
+    q, kc, vc = _rand_cache(B, Hkv * G, Hkv, N, d, dtype, N + k)
+    q, kc, vc = q.to(dev()), kc.to(dev()), vc.to(dev())
+    scores = T.sa_score(q, kc, T.SA_SCORE_EXACT_PER_Q_HEAD)
+    idx = T.sa_topk(scores, k)
+    out = T.sa_sparse_decode(q, kc, vc, idx, T.SA_IDX_TOKEN_PER_Q_HEAD)
+    args, out2, d_ = T.layer_args(q, kc, vc, T.SA_SCORE_EXACT_PER_Q_HEAD, k)
+    idx2 = torch.empty((B, Hkv * G, k), dtype=torch.int32, device=dev())
+    T.sa_decode_layer(args, T.SA_LAYER_SPARSE, idx2, d_)
+    torch.cuda.synchronize()
+    assert tuple(scores.shape) == (B, Hkv * G, N)
+    assert torch.equal(idx, idx2) and torch.equal(out, out2)
+    qf, kf, vf = _f64(q), _f64(kc), _f64(vc)
+    s, ih, o = scores.cpu().numpy(), idx.cpu().numpy(), out.cpu().numpy()
+    scale = O.default_scale(d)
+    for b in range(min(B, 3)):
+        for h in range(Hkv * G):
+            r = h // G
+            s64 = O.scores_per_query_head(qf[b, h], kf[b, r], scale)
+            assert np.max(np.abs(s[b, h] - s64)) <= score_tol(s64), (b, h)
+            assert np.array_equal(ih[b, h], O.topk(s[b, h].astype(np.float64), k)), (b, h)
+            v = O.index_set_verdict(s64, ih[b, h], k)
+            assert not v.startswith("failed"), (b, h, v)
+            want = O.attend(qf[b, h][None], kf[b, r], vf[b, r], ih[b, h], scale)
+            check_out(o[b, h][None], want, dtype, "per-q-head %d,%d" % (b, h))
+
+
+def test_per_query_head_with_shared_sets_equals_per_kv_head():
+    """When the G query heads of a group hold the same set, per-query-head
+    decode is per-KV-head decode (to fp32 rounding)."""
+    say("per-q-head == per-kv-head on shared sets")
+    B, Hkv, G, N, d, k = 3, 8, 4, 5000, 128, 100
+    q, kc, vc = _rand_cache(B, Hkv * G, Hkv, N, d, "bf16", 23)
+    q, kc, vc = q.to(dev()), kc.to(dev()), vc.to(dev())
+    idx = T.sa_topk(T.sa_score(q, kc), k)
+    per_q = idx.repeat_interleave(G, dim=1).contiguous()
+    a = T.sa_sparse_decode(q, kc, vc, idx).cpu().numpy()
+    b = T.sa_sparse_decode(q, kc, vc, per_q, T.SA_IDX_TOKEN_PER_Q_HEAD).cpu().numpy()
+    assert np.max(np.abs(a - b)) <= 1e-5

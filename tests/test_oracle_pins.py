@@ -342,6 +342,18 @@ def test_plan_dense_select_hands_its_topk_on():
     assert O.plan_check([O.DENSE_SELECT, O.REUSE], [-1, 0]) is None
 
 
+def test_per_query_head_scores():
+    # basis query: the score is the matching key coordinate times the scale
+    k = _rand(9, 8)
+    q = np.zeros(8)
+    q[3] = 2.0
+    np.testing.assert_allclose(O.scores_per_query_head(q, k, 0.5), k[:, 3], rtol=0, atol=1e-15)
+    # a group of G copies of one head selects what that head selects alone
+    qg = np.stack([_rand(8)] * 4)
+    np.testing.assert_array_equal(O.topk(O.scores_per_query_head(qg[0], k, 0.5), 3),
+                                  O.topk(O.scores_exact(qg, k, 0.5), 3))
+
+
 # ---------------------------------------------------------------------------
 # layer-reuse policy (HyLRA, section 2.2)
 # ---------------------------------------------------------------------------

@@ -23,8 +23,10 @@ SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_ALIGN, SA_ERR_DTYPE, SA_ERR_WORKSPACE, 
 SA_F32, SA_BF16 = 0, 1
 # sa_score_kind
 SA_SCORE_EXACT, SA_SCORE_BLOCK_MINMAX, SA_SCORE_INDEXER, SA_SCORE_INDEXER_PER_KV_HEAD = 0, 1, 2, 3
+SA_SCORE_EXACT_PER_Q_HEAD = 4
 # sa_index_kind
 SA_IDX_TOKEN_PER_KV_HEAD, SA_IDX_TOKEN_SHARED, SA_IDX_BLOCK_PER_KV_HEAD = 0, 1, 2
+SA_IDX_TOKEN_PER_Q_HEAD = 3
 # sa_layer_mode
 SA_LAYER_DENSE, SA_LAYER_SPARSE, SA_LAYER_REUSE, SA_LAYER_DENSE_SELECT = 0, 1, 2, 3
 
@@ -228,6 +230,8 @@ def sa_score(q, k_cache, kind=SA_SCORE_EXACT, *, kmin=None, kmax=None, block_siz
             if not t.is_contiguous():
                 raise ValueError("indexer tensors must be contiguous")
         shape = lead + (N,)
+    elif kind == SA_SCORE_EXACT_PER_Q_HEAD:
+        shape = (B, desc.n_q_heads, N)
     else:
         shape = (B, Hkv, N)
     if scores is None:

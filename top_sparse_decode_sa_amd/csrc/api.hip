@@ -106,8 +106,22 @@ int mode_of(sa_index_kind ik) {
     case SA_IDX_TOKEN_PER_KV_HEAD: return kIdxTokenPerHead;
     case SA_IDX_TOKEN_SHARED: return kIdxTokenShared;
     case SA_IDX_BLOCK_PER_KV_HEAD: return kIdxBlockPerHead;
+    case SA_IDX_TOKEN_PER_Q_HEAD: return kIdxTokenPerHead;  // on the per-query-head view
   }
   return -1;
+}
+
+// The cache as the attention kernels see it for an index kind: per-query-head
+// sets run on the view with one row per query head.
+Cache attend_view(const Cache& c, sa_index_kind ik) {
+  return ik == SA_IDX_TOKEN_PER_Q_HEAD ? per_q_head_view(c) : c;
+}
+
+// grid rows of the per-query-head view
+sa_status check_q_rows(const Cache& c) {
+  if ((int64_t)c.B * c.Hq > 65535)
+    return fail(SA_ERR_SHAPE, "per-query-head rows: batch * n_q_heads above 65535");
+  return SA_OK;
 }
 
 sa_status check_indexer_aux(const Cache& c, const sa_score_aux* aux) {
@@ -141,12 +155,14 @@ int64_t score_row_len(const Cache& c, sa_score_kind kind, const sa_score_aux* au
 }
 
 int64_t score_rows(const Cache& c, sa_score_kind kind) {
-  return kind == SA_SCORE_INDEXER ? (int64_t)c.B : (int64_t)c.B * c.Hkv;
+  if (kind == SA_SCORE_INDEXER) return c.B;
+  if (kind == SA_SCORE_EXACT_PER_Q_HEAD) return (int64_t)c.B * c.Hq;
+  return (int64_t)c.B * c.Hkv;
 }
 
 bool known_score_kind(sa_score_kind kind) {
   return kind == SA_SCORE_EXACT || kind == SA_SCORE_BLOCK_MINMAX || kind == SA_SCORE_INDEXER ||
-         kind == SA_SCORE_INDEXER_PER_KV_HEAD;
+         kind == SA_SCORE_INDEXER_PER_KV_HEAD || kind == SA_SCORE_EXACT_PER_Q_HEAD;
 }
 
 bool is_indexer(sa_score_kind kind) {
@@ -158,6 +174,7 @@ sa_index_kind index_kind_of(sa_score_kind kind) {
   switch (kind) {
     case SA_SCORE_BLOCK_MINMAX: return SA_IDX_BLOCK_PER_KV_HEAD;
     case SA_SCORE_INDEXER: return SA_IDX_TOKEN_SHARED;
+    case SA_SCORE_EXACT_PER_Q_HEAD: return SA_IDX_TOKEN_PER_Q_HEAD;
     default: return SA_IDX_TOKEN_PER_KV_HEAD;
   }
 }
@@ -167,6 +184,7 @@ sa_status do_score(const Cache& c, sa_score_kind kind, const void* q, const void
   hipError_t e;
   switch (kind) {
     case SA_SCORE_EXACT: e = launch_score_exact(c, q, k, scores, s); break;
+    case SA_SCORE_EXACT_PER_Q_HEAD: e = launch_score_exact(per_q_head_view(c), q, k, scores, s); break;
     case SA_SCORE_BLOCK_MINMAX:
       e = launch_score_block(c, aux->block_size, q, aux->kmin, aux->kmax, scores, s);
       break;
@@ -191,6 +209,7 @@ sa_status check_score_args(const sa_kv_desc* desc, sa_score_kind kind, const voi
   if (is_indexer(kind)) return check_indexer_aux(*c, aux);
   if ((st = check_ptr(q, "q", 16)) != SA_OK) return st;
   if (kind == SA_SCORE_BLOCK_MINMAX) return check_block_aux(*c, aux);
+  if (kind == SA_SCORE_EXACT_PER_Q_HEAD && (st = check_q_rows(*c)) != SA_OK) return st;
   return check_ptr(k_cache, "k_cache", 16);
 }
 
@@ -209,6 +228,7 @@ sa_status check_sparse_idx(const Cache& c, sa_index_kind ik, const int32_t* idx,
                            int32_t bs) {
   if (mode_of(ik) < 0) return fail(SA_ERR_SHAPE, "unknown index kind %d", (int)ik);
   sa_status st;
+  if (ik == SA_IDX_TOKEN_PER_Q_HEAD && (st = check_q_rows(c)) != SA_OK) return st;
   if ((st = check_ptr(idx, "idx", 4)) != SA_OK) return st;
   if (n_idx < 1) return fail(SA_ERR_SHAPE, "n_idx %d must be >= 1", n_idx);
   if (ik == SA_IDX_BLOCK_PER_KV_HEAD) {
@@ -236,7 +256,7 @@ LayerWs layer_ws(const Cache& c, const sa_layer_args* a, sa_layer_mode mode) {
   } else {
     const sa_index_kind ik = index_kind_of(a->score_kind);
     const int32_t bs = a->score_kind == SA_SCORE_BLOCK_MINMAX ? a->aux.block_size : 0;
-    w.attend = plan_attend(c, mode_of(ik), a->k, bs).ws_bytes;
+    w.attend = plan_attend(attend_view(c, ik), mode_of(ik), a->k, bs).ws_bytes;
     if (mode == SA_LAYER_SPARSE) {
       const int64_t rows = score_rows(c, a->score_kind);
       const int64_t len = score_row_len(c, a->score_kind, &a->aux);
@@ -364,7 +384,7 @@ size_t sa_sparse_workspace_size(const sa_kv_desc* desc, sa_index_kind ik, int32_
   Cache c;
   if (check_desc(desc, &c) != SA_OK || mode_of(ik) < 0 || n_idx < 1) return 0;
   if (ik == SA_IDX_BLOCK_PER_KV_HEAD && (block_size < 1 || block_size > 4096)) return 0;
-  return align_up(plan_attend(c, mode_of(ik), n_idx, block_size).ws_bytes, 256);
+  return align_up(plan_attend(attend_view(c, ik), mode_of(ik), n_idx, block_size).ws_bytes, 256);
 }
 
 sa_status sa_sparse_decode(const sa_kv_desc* desc, const void* q, const void* k_cache,
@@ -376,10 +396,11 @@ sa_status sa_sparse_decode(const sa_kv_desc* desc, const void* q, const void* k_
   if ((st = check_desc(desc, &c)) != SA_OK) return st;
   if ((st = check_attend_args(c, q, k_cache, v_cache, out)) != SA_OK) return st;
   if ((st = check_sparse_idx(c, ik, idx, n_idx, block_size)) != SA_OK) return st;
-  const AttendPlan p = plan_attend(c, mode_of(ik), n_idx, block_size);
+  const Cache v = attend_view(c, ik);
+  const AttendPlan p = plan_attend(v, mode_of(ik), n_idx, block_size);
   if ((st = check_ws(ws, ws_bytes, p.ws_bytes, "sa_sparse_decode")) != SA_OK) return st;
   return hip_status(
-      launch_attend(c, p, q, k_cache, v_cache, idx, n_idx, block_size, out, ws, stream),
+      launch_attend(v, p, q, k_cache, v_cache, idx, n_idx, block_size, out, ws, stream),
       "sa_sparse_decode launch");
 }
 
@@ -490,7 +511,8 @@ sa_status sa_decode_layer(const sa_layer_args* a, sa_layer_mode mode, int32_t* i
   float* scores = reinterpret_cast<float*>(base);
   void* topk_ws = base + w.scores;
   void* att_ws = base + w.scores + w.topk;
-  const AttendPlan p = plan_attend(c, mode_of(ik), a->k, bs);
+  const Cache v = attend_view(c, ik);
+  const AttendPlan p = plan_attend(v, mode_of(ik), a->k, bs);
   if (mode == SA_LAYER_SPARSE) {
     if ((st = do_score(c, a->score_kind, a->q, a->k_cache, &a->aux, scores, stream)) != SA_OK)
       return st;
@@ -500,7 +522,7 @@ sa_status sa_decode_layer(const sa_layer_args* a, sa_layer_mode mode, int32_t* i
       return st;
   }
   return hip_status(
-      launch_attend(c, p, a->q, a->k_cache, a->v_cache, idx, a->k, bs, a->out, att_ws, stream),
+      launch_attend(v, p, a->q, a->k_cache, a->v_cache, idx, a->k, bs, a->out, att_ws, stream),
       "sa_decode_layer attention launch");
 }
 

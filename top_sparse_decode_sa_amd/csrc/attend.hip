@@ -55,6 +55,7 @@ struct AttendArgs {
   const uint8_t* v;
   int64_t sb, sh, st;  // element strides
   int32_t Hq, Hkv;
+  int32_t kv_div;  // row r reads KV head r / kv_div (1, or G for per-query-head rows)
   int64_t N;
   float qscale;  // softmax scale * log2(e)
   const int32_t* idx;
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
       for (int e = 0; e < E; ++e) qv[g][e] = q8[g][e] * a.qscale;
   }
 
-  const int64_t kv_off = ((int64_t)b * a.sb + (int64_t)r * a.sh) * EB + sl * 16;
+  const int64_t kv_off = ((int64_t)b * a.sb + (int64_t)(r / a.kv_div) * a.sh) * EB + sl * 16;
   const uint8_t* kbase = a.k + kv_off;
   const uint8_t* vbase = a.v + kv_off;
   const int64_t row_bytes = a.st * EB;
@@ -339,7 +340,7 @@ __global__ __launch_bounds__(64 * max_waves<MODE>()) void attend_sparse_kernel(A
     }
   }
 
-  const int64_t kv_off = ((int64_t)b * a.sb + (int64_t)r * a.sh) * 2;
+  const int64_t kv_off = ((int64_t)b * a.sb + (int64_t)(r / a.kv_div) * a.sh) * 2;
   const uint8_t* kbase = a.k + kv_off + 16 * rq;
   const uint8_t* vbase = a.v + kv_off + 16 * n;
   const int64_t row_bytes = a.st * 2;
@@ -833,6 +834,7 @@ hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, con
   a.st = c.st;
   a.Hq = c.Hq;
   a.Hkv = c.Hkv;
+  a.kv_div = c.kv_div;
   a.N = c.N;
   a.qscale = c.scale * kLog2e;
   a.idx = idx;

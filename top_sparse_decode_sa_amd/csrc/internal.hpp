@@ -9,14 +9,28 @@
 
 namespace sa {
 
-// Validated view of one layer's KV cache (strides in elements).
+// Validated view of one layer's KV cache (strides in elements).  A "row" is
+// (sequence, r) for r < Hkv; row r reads KV head r / kv_div and query heads
+// r*G .. r*G + G - 1.
 struct Cache {
   int32_t B, Hq, Hkv, G, D;
   int64_t N;
   sa_dtype q_dtype, kv_dtype;
   int64_t sb, sh, st;
   float scale;  // softmax scale (already defaulted)
+  int32_t kv_div = 1;
 };
+
+// The same cache seen with one row per (sequence, QUERY head): G = 1 and row
+// h reads KV head h / G of the real cache, so every query head scores and
+// selects on its own.
+inline Cache per_q_head_view(const Cache& c) {
+  Cache v = c;
+  v.Hkv = c.Hq;
+  v.G = 1;
+  v.kv_div = c.G * c.kv_div;
+  return v;
+}
 
 // ------------------------------------------------------------- scoring
 hipError_t launch_score_exact(const Cache& c, const void* q, const void* k, float* scores,

@@ -39,6 +39,7 @@ struct ExactArgs {
   const uint8_t* k;
   int64_t sb, sh, st;
   int32_t Hq, Hkv, G;
+  int32_t kv_div;  // row r reads KV head r / kv_div (1, or G for per-query-head rows)
   int64_t N;
   float scale;
   float* scores;
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void score_exact_kernel(ExactArgs a) {
     }
   }
 
-  const uint8_t* kbase = a.k + ((int64_t)b * a.sb + (int64_t)r * a.sh) * EB + sl * 16;
+  const uint8_t* kbase = a.k + ((int64_t)b * a.sb + (int64_t)(r / a.kv_div) * a.sh) * EB + sl * 16;
   const int64_t row_bytes = a.st * EB;
   float* srow = a.scores + (int64_t)row * a.N;
 
@@ -395,6 +396,7 @@ hipError_t launch_score_exact(const Cache& c, const void* q, const void* k, floa
   a.Hq = c.Hq;
   a.Hkv = c.Hkv;
   a.G = c.G;
+  a.kv_div = c.kv_div;
   a.N = c.N;
   a.scale = c.scale;
   a.scores = scores;
