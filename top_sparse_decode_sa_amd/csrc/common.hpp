@@ -156,14 +156,26 @@ __device__ __forceinline__ float group_max(float x) {
   return x;
 }
 
-// Wave-wide inclusive prefix sum of a uint32 (64 lanes).
+// DPP move of a uint32 across lanes; lanes whose source lies outside the row
+// read 0 (bound_ctrl), lanes of rows outside ROW_MASK get 0.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xf, true);
+}
+
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142;  // lane 15 of each row into the next row
+constexpr int kRowBcast31 = 0x143;  // lane 31 into rows 2 and 3
+
+// Wave-wide inclusive prefix sum of a uint32 (64 lanes): shifted adds inside
+// each 16-lane row, then the row totals carried across rows by broadcasts.
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
+  v += dpp_u32<kRowShr1>(v);
+  v += dpp_u32<kRowShr2>(v);
+  v += dpp_u32<kRowShr4>(v);
+  v += dpp_u32<kRowShr8>(v);
+  v += dpp_u32<kRowBcast15, 0xa>(v);
+  v += dpp_u32<kRowBcast31, 0xc>(v);
   return v;
 }
 

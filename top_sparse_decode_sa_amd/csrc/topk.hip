@@ -296,13 +296,14 @@ __device__ void resolve_row(KeyAt key_at, int64_t n, uint32_t kleft, uint32_t pr
 
 // Ordered write of one LDS tile (positions tile0 + [0, n_valid), E per
 // thread): every key above T, and keys equal to T while fewer than `need`
-// came before, go to out at slot = kept keys at lower positions.  run_gt /
-// run_eq carry the counts of earlier tiles.  Contains barriers.
+// came before, go to out at slot = kept keys at lower positions (slots at or
+// beyond k are never written).  run_gt / run_eq carry the counts of earlier
+// tiles.  Contains barriers.
 template <int E>
 __device__ __forceinline__ void write_tile(const uint32_t* keys, int64_t tile0, int n_valid,
                                            uint32_t T, uint32_t need, uint32_t& run_gt,
                                            uint32_t& run_eq, int32_t* __restrict__ out,
-                                           Shared& sh) {
+                                           uint32_t k, Shared& sh) {
   static_assert(E % 4 == 0 && E <= 32, "E keys per thread in groups of four");
   constexpr int G = E / 4;
   constexpr int SW = G >= 8 ? 7 : G - 1;
@@ -337,10 +338,11 @@ __device__ __forceinline__ void write_tile(const uint32_t* keys, int64_t tile0, 
     m &= m - 1u;
     const int32_t pos = (int32_t)(tile0 + E * t + j);
     if ((mg >> j) & 1u) {
-      out[gb + std::min(eb, need)] = pos;
+      const uint32_t slot = gb + std::min(eb, need);
+      if (slot < k) out[slot] = pos;
       ++gb;
     } else {
-      if (eb < need) out[gb + eb] = pos;
+      if (eb < need && gb + eb < k) out[gb + eb] = pos;
       ++eb;
     }
   }
@@ -378,7 +380,44 @@ __device__ void topk_row(const float* __restrict__ s, int64_t n, int32_t k,
 
   // ---- 2-3. candidates of bin d1, resolved to T and need
   uint32_t T, need;
-  if (c1 <= cap) {
+  if (RES && c1 <= cap) {
+    // thread t owns keys [E t, E t + E): read them as the ordered write does
+    // (16-byte groups), count this thread's candidates, place them with one
+    // LDS atomic per wave (wave prefix sum of the counts)
+    if (tid == 0) sh.count = 0;
+    __syncthreads();
+    constexpr int G4 = E / 4;
+    constexpr int SW = G4 >= 8 ? 7 : G4 - 1;
+    uint32_t kk[E];
+#pragma unroll
+    for (int g = 0; g < G4; ++g) {
+      const uint4 v = *reinterpret_cast<const uint4*>(&keys[E * tid + 4 * (g ^ (tid & SW))]);
+      kk[4 * g + 0] = v.x;
+      kk[4 * g + 1] = v.y;
+      kk[4 * g + 2] = v.z;
+      kk[4 * g + 3] = v.w;
+    }
+    uint32_t mine = 0, cnt = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const bool c = (int64_t)E * tid + j < n && (kk[j] >> 20) == d1;
+      mine |= (c ? 1u : 0u) << j;
+      cnt += c ? 1u : 0u;
+    }
+    const uint32_t incl = wave_inclusive_scan(cnt);
+    uint32_t base = 0;
+    if ((tid & 63) == 63 && incl) base = atomicAdd(&sh.count, incl);
+    base = __builtin_amdgcn_readlane(base, 63) + incl - cnt;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      if ((mine >> j) & 1u) {
+        if (base < cap) cand[base] = make_uint2(kk[j], (uint32_t)(E * tid + j));
+        ++base;
+      }
+    }
+    __syncthreads();
+    resolve(cand, c1, kleft, prefix, mask, sh, T, need);
+  } else if (c1 <= cap) {
     if (tid == 0) sh.count = 0;
     __syncthreads();
     constexpr int U = 8;
@@ -404,14 +443,14 @@ __device__ void topk_row(const float* __restrict__ s, int64_t n, int32_t k,
   // ---- 4. ordered write
   uint32_t run_gt = 0, run_eq = 0;
   if constexpr (RES) {
-    write_tile<E>(keys, 0, (int)n, T, need, run_gt, run_eq, out, sh);
+    write_tile<E>(keys, 0, (int)n, T, need, run_gt, run_eq, out, (uint32_t)k, sh);
   } else {
     for (int64_t tile0 = 0; tile0 < n; tile0 += kTile) {
       const int nv = (int)std::min<int64_t>(kTile, n - tile0);
       __syncthreads();  // the previous tile is consumed
       load_tile<E>(s + tile0, nv, vec4, keys, nullptr);
       __syncthreads();
-      write_tile<E>(keys, tile0, nv, T, need, run_gt, run_eq, out, sh);
+      write_tile<E>(keys, tile0, nv, T, need, run_gt, run_eq, out, (uint32_t)k, sh);
     }
   }
 }
@@ -572,7 +611,7 @@ __global__ __launch_bounds__(kThreads) void topk_mw_write(const float* __restric
   __syncthreads();
   uint32_t run_gt = w.base_gt[blockIdx.x], run_eq = w.base_eq[blockIdx.x];
   write_tile<kMwChunk / kThreads>(keys, c0, nv, w.T, w.need, run_gt, run_eq,
-                                  idx_out + (int64_t)blockIdx.y * k, sh);
+                                  idx_out + (int64_t)blockIdx.y * k, (uint32_t)k, sh);
 }
 
 bool use_mw(int64_t n_rows, int64_t n, int32_t k) {
