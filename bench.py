@@ -9,8 +9,12 @@ Queries rotate over 8 pre-generated variants so consecutive steps select
 different tokens; the cache (2.15 GB) is resident in HBM before timing starts.
 
 Timing: W untimed warmup steps, then K timed steps bracketed by
-torch.cuda.synchronize(); HIP events recorded on the launch stream between
-the three calls give each kernel's average duration over the same region.
+torch.cuda.synchronize().  Each step is captured once per query variant as a
+HIP graph of its three launches and replayed (a serving loop's form; --eager
+times plain launches instead); the bench checks that a replay selects and
+attends exactly as an eager step.  A separate pass of eager steps with HIP
+events recorded on the launch stream between the three calls gives each
+kernel's average duration.
 
 Prints ONE JSON line.  `value` is the step's achieved HBM bandwidth
 (algorithmic bytes of score + top-k + attend per step / time per step);
@@ -51,6 +55,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bound on the oracle's CPU time for cpu_baseline (0 disables)")
     p.add_argument("--dense-steps", type=int, default=20)
+    p.add_argument("--eager", action="store_true",
+                   help="time eager launches instead of replaying each step as a HIP graph")
     p.add_argument("--profile", action="store_true",
                    help="short run for a profiler: few steps, no dense, no cpu baseline, plus "
                         "three 1 GiB device-to-device copies that calibrate HBM byte counters")
@@ -68,6 +74,11 @@ def parse():
                         "keys correlate across layers; profiles every layer, plans with the DP "
                         "planner and times all-dense, all-sparse, the fixed-jump baseline and the "
                         "planned policy; prints one JSON line")
+    p.add_argument("--offload", action="store_true",
+                   help="index-guided offload: block61k-shaped layers whose caches sit in pinned "
+                        "host memory; times the gather of the 24 selected blocks per row over the "
+                        "host link against copying the whole layer, and a 3-layer reuse pipeline "
+                        "that prefetches the next layer's blocks on a second stream; one JSON line")
     p.add_argument("--theta", type=float, default=0.35,
                    help="overlap threshold of the layer-reuse planner (--hylra)")
     p.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -500,6 +511,117 @@ def hylra(args):
         "device": torch.cuda.get_device_name(0)}), flush=True)
 
 
+def offload(args):
+    """Index-guided offload on the block61k shape (batch 8, 32/8 heads, d 128,
+    bf16, 61440 tokens = 480 blocks of 128, 24 blocks kept per row).
+
+    Layer 0's cache is on the device; it selects blocks from min/max
+    summaries.  Layers 1-3 keep their caches in pinned host memory and reuse
+    layer 0's blocks: sa_gather_blocks fetches only those blocks, and dense
+    decode over the gathered rows is their attention.  Values are drawn on
+    the device; timings depend on the sizes only."""
+    import torch
+    import sa_synth as S
+    import top_sparse_decode_sa_amd as T
+
+    T.lib()
+    dev = torch.device("cuda", 0)
+    c = S.CONFIGS["block61k"]
+    B, Hq, Hkv, d, N, bs, nblk = (c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.ctx_len,
+                                  c.block_size, c.k)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    shape = (B, Hkv, N, d)
+    log("offload: drawing 4 layers (%.1f GB of KV, 3 layers in pinned host memory)" % (
+        4 * c.kv_bytes() / 1e9))
+    qs = [torch.randn((B, Hq, d), generator=gen, device=dev).to(torch.bfloat16) for _ in range(4)]
+    k0 = torch.empty(shape, dtype=torch.bfloat16, device=dev).normal_(generator=gen)
+    v0 = torch.empty(shape, dtype=torch.bfloat16, device=dev).normal_(generator=gen)
+    host = []
+    for _ in range(3):
+        kh = torch.empty(shape, dtype=torch.bfloat16, pin_memory=True)
+        vh = torch.empty(shape, dtype=torch.bfloat16, pin_memory=True)
+        for t in (kh, vh):
+            t.copy_(torch.empty(shape, dtype=torch.bfloat16, device=dev).normal_(generator=gen))
+        host.append((kh, vh))
+    torch.cuda.synchronize()
+    # layer 0: block selection on the device
+    kmin, kmax = T.sa_block_summarize(k0, bs, q_like=qs[0])
+    args0, out0, _ = T.layer_args(qs[0], k0, v0, T.SA_SCORE_BLOCK_MINMAX, nblk, kmin=kmin,
+                                  kmax=kmax, block_size=bs)
+    idx = torch.empty((B, Hkv, nblk), dtype=torch.int32, device=dev)
+    T.sa_decode_layer(args0, T.SA_LAYER_SPARSE, idx, dev)
+    torch.cuda.synchronize()
+    sel_shape = (B, Hkv, nblk * bs, d)
+    stage = [(torch.empty(sel_shape, dtype=torch.bfloat16, device=dev),
+              torch.empty(sel_shape, dtype=torch.bfloat16, device=dev)) for _ in range(2)]
+    outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(3)]
+    reps = max(3, min(args.steps, 10))
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    kh, vh = host[0]
+    us_gather = timed(lambda: T.sa_gather_blocks(kh, vh, idx, bs, *stage[0]), reps)
+    us_attend = timed(lambda: T.sa_dense_decode(qs[1], *stage[0], out=outs[0]), reps)
+    full_k = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    full_v = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    us_full = timed(lambda: (full_k.copy_(kh, non_blocking=True),
+                             full_v.copy_(vh, non_blocking=True)), 2)
+    # reuse layers 1-3: layer l attends while layer l+1's blocks are fetched
+    # on a second stream (default priority)
+    side = torch.cuda.Stream(device=dev)
+    main_s = torch.cuda.current_stream(dev)
+
+    def pipeline():
+        done = [torch.cuda.Event() for _ in range(3)]
+        with torch.cuda.stream(side):
+            T.sa_gather_blocks(*host[0], idx, bs, *stage[0])
+            done[0].record(side)
+        for l in range(3):
+            if l + 1 < 3:
+                with torch.cuda.stream(side):
+                    if l >= 1:
+                        side.wait_event(used[l - 1])
+                    T.sa_gather_blocks(*host[l + 1], idx, bs, *stage[(l + 1) % 2])
+                    done[l + 1].record(side)
+            main_s.wait_event(done[l])
+            T.sa_dense_decode(qs[l + 1], *stage[l % 2], out=outs[l])
+            used[l].record(main_s)
+
+    used = [torch.cuda.Event() for _ in range(3)]
+    us_pipe = timed(pipeline, reps)
+    sel_bytes = 2 * B * Hkv * nblk * bs * d * 2
+    full_bytes = 2 * B * Hkv * N * d * 2
+    res = {
+        "bench": "index-guided offload (HyLRA section 2.4)", "unit": "us (HIP events)",
+        "config": {"workload": "block61k: batch 8, 32/8 heads, d 128, bf16, 61440 tokens, "
+                               "24 of 480 blocks of 128 per row; layers 1-3 in pinned host memory",
+                   "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d, "ctx_len": N,
+                   "block_size": bs, "blocks_kept": nblk},
+        "gather_selected_us": round(us_gather, 1), "gather_bytes": sel_bytes,
+        "gather_host_link_gbps": round(sel_bytes / us_gather / 1e3, 1),
+        "attend_gathered_us": round(us_attend, 1),
+        "full_layer_copy_us": round(us_full, 1), "full_layer_bytes": full_bytes,
+        "full_copy_host_link_gbps": round(full_bytes / us_full / 1e3, 1),
+        "per_layer_speedup_vs_full_copy": round(us_full / (us_gather + us_attend), 2),
+        "reuse_pipeline_3_layers_us": round(us_pipe, 1),
+        "data": "drawn on the device (torch generator, seed %d)" % args.seed,
+        "device": torch.cuda.get_device_name(0)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -513,6 +635,9 @@ def main():
         return
     if args.gpus == 1 and args.hylra:
         hylra(args)
+        return
+    if args.gpus == 1 and args.offload:
+        offload(args)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -568,18 +693,51 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    log("bench: timing %d steps" % args.steps)
+    # the timed steps: each step captured once per query variant as a HIP
+    # graph (the three launches of one decode step), replayed in turn
+    graphs = []
+    if not args.eager:
+        for v in range(N_QVAR):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(v)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % N_QVAR].replay()
+        torch.cuda.synchronize()
+        # a replayed step selects and attends exactly as the eager one
+        graphs[0].replay()
+        g_idx, g_out = idx.clone(), out.clone()
+        step(0)
+        torch.cuda.synchronize()
+        assert torch.equal(g_idx, idx) and torch.equal(g_out, out), "graph replay differs from eager"
+
+    log("bench: timing %d steps (%s)" % (args.steps, "eager" if args.eager else "graph replay"))
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
-        step(i, events[i])
+        if args.eager:
+            step(i)
+        else:
+            graphs[i % N_QVAR].replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    ms_score = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
-    ms_topk = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
-    ms_attend = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
     ms_step = wall * 1e3 / args.steps
+
+    # per-kernel durations: eager steps with HIP events between the calls, on
+    # the launch stream (a separate pass, so the events do not slow the
+    # timed steps)
+    n_ev = min(args.steps, 100)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
+    torch.cuda.synchronize()
+    t_ev = time.perf_counter()
+    for i in range(n_ev):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    ms_step_eager = (time.perf_counter() - t_ev) * 1e3 / n_ev
+    ms_score = sum(e[0].elapsed_time(e[1]) for e in events) / n_ev
+    ms_topk = sum(e[1].elapsed_time(e[2]) for e in events) / n_ev
+    ms_attend = sum(e[2].elapsed_time(e[3]) for e in events) / n_ev
 
     if args.profile:
         # plain device-to-device copies of known size: the byte counters of
@@ -677,6 +835,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "timing": "eager launches" if args.eager else "each step a replayed HIP graph (3 launches)",
+        "ms_per_step_eager_with_events": round(ms_step_eager, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

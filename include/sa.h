@@ -25,7 +25,8 @@
  *
  * Conventions shared by every call
  *   - Every pointer argument named *_cache, q, out, scores, idx*, kmin, kmax,
- *     ws is a DEVICE pointer; descriptors and plan arrays are HOST pointers.
+ *     ws is a DEVICE pointer; descriptors and plan arrays are HOST pointers;
+ *     *_host (sa_gather_blocks) point to pinned host memory.
  *   - The caller owns every buffer.  No call allocates or frees device memory
  *     or keeps state between calls.
  *   - Every call validates its arguments on the host first.  On an invalid
@@ -63,7 +64,8 @@ typedef enum {
   SA_ERR_DTYPE = 4,       /* unknown dtype, or a dtype the call does not take */
   SA_ERR_WORKSPACE = 5,   /* workspace missing or too small */
   SA_ERR_UNSUPPORTED = 6, /* valid but not built (e.g. head_dim 96, group size 3) */
-  SA_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed */
+  SA_ERR_HIP = 7,         /* a HIP runtime call or kernel launch failed */
+  SA_ERR_MEMORY = 8       /* a buffer is not the kind of memory the call needs */
 } sa_status;
 
 typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
@@ -307,6 +309,28 @@ sa_status sa_plan_reuse(const int64_t* overlap, int64_t total, int32_t n_layers,
  * set of the full layer before it.  modes/src as in sa_plan_reuse.  Limits:
  * 1 <= n_layers <= 256, step >= 1. */
 sa_status sa_plan_fixed_jump(int32_t n_layers, int32_t step, int32_t* modes, int32_t* src);
+
+/* ------------------------------------------------------------- offload */
+
+/* Index-guided offload: [P2] section 2.4, when the KV cache exceeds device
+ * memory the (reused) index set decides which blocks are fetched from host
+ * memory.  Copies the selected blocks of one layer's K and V, held in PINNED
+ * HOST memory (k_host, v_host: host pointers of one pinned allocation each,
+ * laid out as desc says), into device buffers:
+ *   k_out[b, r, j*block_size + i, :] = K[b, r, idx[b, r, j]*block_size + i, :]
+ * (same for V), k_out/v_out [batch, n_kv_heads, n_blk*block_size, head_dim]
+ * contiguous, kv_dtype, 16-byte aligned (device).  idx [batch, n_kv_heads,
+ * n_blk] int32 block ids (device); an id outside [0, ctx_len/block_size) is
+ * clamped into it (the kernel never reads outside the cache).  The GPU reads
+ * the host cache directly over the host link.  Full decode attention over the
+ * gathered buffers (sa_dense_decode with ctx_len = n_blk*block_size) is then
+ * the selected-block attention of SA_IDX_BLOCK_PER_KV_HEAD.
+ * Limits: ctx_len a multiple of block_size (blocks are whole); 1 <=
+ * block_size <= 4096; 1 <= n_blk <= ctx_len/block_size.  A host pointer that
+ * is not pinned, device-accessible memory gives SA_ERR_MEMORY. */
+sa_status sa_gather_blocks(const sa_kv_desc* desc, const void* k_host, const void* v_host,
+                           const int32_t* idx, int32_t n_blk, int32_t block_size, void* k_out,
+                           void* v_out, hipStream_t stream);
 
 /* ----------------------------------------------------------------- misc */
 

@@ -206,6 +206,25 @@ def test_block61k_block_selection_and_reuse():
             check_out(out_h[b, r * c.group:(r + 1) * c.group], want, "bf16", "block61k L%d %d,%d" % (layer, b, r))
         if layer == 0:
             _check_dense(w, 0, qd, kd, vd, rows[:3], "block61k L0")
+        if layer == 1:
+            # index-guided offload: the same layer with its cache in pinned
+            # host memory; only the 24 reused blocks per row cross the host
+            # link, and attention over them equals the device-resident reuse
+            kh = torch.empty(kd.shape, dtype=kd.dtype, pin_memory=True)
+            vh = torch.empty(vd.shape, dtype=vd.dtype, pin_memory=True)
+            kh.copy_(kd)
+            vh.copy_(vd)
+            ko, vo = T.sa_gather_blocks(kh, vh, idx, bs)
+            off = T.sa_dense_decode(qd, ko, vo)
+            torch.cuda.synchronize()
+            assert ko.shape == (c.batch, c.n_kv_heads, c.k * bs, c.head_dim)
+            assert np.max(np.abs(off.cpu().numpy() - out_h)) <= 1e-5, "offload differs from reuse"
+            for b, r in rows[:2]:
+                toks = torch.from_numpy(O.block_tokens(idx_h[b, r], bs, c.ctx_len))
+                assert torch.equal(ko[b, r].cpu(), kh[b, r][toks]), ("offload K", b, r)
+                assert torch.equal(vo[b, r].cpu(), vh[b, r][toks]), ("offload V", b, r)
+            say("block61k L1: offload gather of %d blocks per row equals the reuse decode" % c.k)
+            del kh, vh, ko, vo
         del kd, vd, kmin, kmax
         torch.cuda.empty_cache()
     say("block61k: layer-0 block sets %s over %d sampled rows; layers 1-3 reused them" % (counts, len(rows)))

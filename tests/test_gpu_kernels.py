@@ -381,3 +381,120 @@ def test_per_query_head_with_shared_sets_equals_per_kv_head():
     a = T.sa_sparse_decode(q, kc, vc, idx).cpu().numpy()
     b = T.sa_sparse_decode(q, kc, vc, per_q, T.SA_IDX_TOKEN_PER_Q_HEAD).cpu().numpy()
     assert np.max(np.abs(a - b)) <= 1e-5
+
+
+# ------------------------------------------------------------ graph replay
+
+@pytest.mark.parametrize("B,Hkv,N,k", [(2, 4, 5000, 61), (1, 2, 40000, 300)])
+def test_step_graph_replay(B, Hkv, N, k):
+    """A decode step (score -> top-k -> gather-attend) captured as a HIP graph
+    and replayed several times, with new queries copied in eagerly and the
+    stream synchronised between replays: every replay equals the eager step.
+    The shapes take the split attend plan with its combine launch and the
+    multi-workgroup top-k with its zeroing kernel."""
+    say("graph replay B=%d Hkv=%d N=%d k=%d" % (B, Hkv, N, k))
+    G, d = 4, 128
+    q, kc, vc = _rand_cache(B, Hkv * G, Hkv, N, d, "bf16", N)
+    q, kc, vc = q.to(dev()), kc.to(dev()), vc.to(dev())
+    scores = torch.empty((B, Hkv, N), dtype=torch.float32, device=dev())
+    idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev())
+    out = torch.empty((B, Hkv * G, d), dtype=torch.float32, device=dev())
+
+    def step():
+        T.sa_score(q, kc, T.SA_SCORE_EXACT, scores=scores)
+        T.sa_topk(scores, k, idx_out=idx)
+        T.sa_sparse_decode(q, kc, vc, idx, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    rng = np.random.default_rng(N + 1)
+    for rep in range(4):
+        q.copy_(torch.from_numpy(rng.standard_normal(tuple(q.shape)).astype(np.float32)).to(torch.bfloat16))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        gi, go = idx.clone(), out.clone()
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(gi, idx), "replay %d selects differently" % rep
+        assert torch.equal(go, out), "replay %d attends differently" % rep
+
+
+# ------------------------------------------------------- index-guided offload
+
+@pytest.mark.parametrize("dtype,d,B,Hkv,N,bs,n_blk,token_major", [
+    ("bf16", 128, 2, 4, 4096, 128, 5, False), ("f32", 64, 1, 2, 2048, 64, 7, True),
+    ("bf16", 64, 3, 2, 1000, 8, 60, False)])
+def test_gather_blocks_from_pinned_host(dtype, d, B, Hkv, N, bs, n_blk, token_major):
+    """Selected blocks copied from a pinned host cache are bit-exact; dense
+    decode over them equals block-sparse decode of the device-resident cache
+    and the oracle's attention over the blocks' tokens."""
+    say("gather blocks %s d=%d B=%d Hkv=%d N=%d bs=%d n_blk=%d tm=%s" % (
+        dtype, d, B, Hkv, N, bs, n_blk, token_major))
+    G = 4
+    q, kc, vc = _rand_cache(B, Hkv * G, Hkv, N, d, dtype, N + bs)
+    if token_major:   # [B, N, Hkv, d] storage seen as [B, Hkv, N, d]
+        kc = kc.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+        vc = vc.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    kh = torch.empty_strided(kc.shape, kc.stride(), dtype=kc.dtype, pin_memory=True)
+    vh = torch.empty_strided(vc.shape, vc.stride(), dtype=vc.dtype, pin_memory=True)
+    kh.copy_(kc)
+    vh.copy_(vc)
+    rng = np.random.default_rng(n_blk)
+    nb = N // bs
+    blocks = np.stack([rng.choice(nb, n_blk, replace=False) for _ in range(B * Hkv)])
+    blocks = blocks.reshape(B, Hkv, n_blk).astype(np.int32)       # unsorted ids
+    idx = torch.from_numpy(blocks).to(dev())
+    ko, vo = T.sa_gather_blocks(kh, vh, idx, bs)
+    qd, kd, vd = q.to(dev()), kc.to(dev()), vc.to(dev())
+    dense = T.sa_dense_decode(qd, ko, vo)
+    ref = T.sa_sparse_decode(qd, kd, vd, idx, T.SA_IDX_BLOCK_PER_KV_HEAD, block_size=bs)
+    torch.cuda.synchronize()
+    kg, vg = ko.cpu(), vo.cpu()
+    for b in range(B):
+        for r in range(Hkv):
+            want_k = torch.cat([kc[b, r, j * bs:(j + 1) * bs] for j in blocks[b, r]])
+            want_v = torch.cat([vc[b, r, j * bs:(j + 1) * bs] for j in blocks[b, r]])
+            assert torch.equal(kg[b, r], want_k) and torch.equal(vg[b, r], want_v), (b, r)
+    o, rf = dense.cpu().numpy(), ref.cpu().numpy()
+    assert np.max(np.abs(o - rf)) <= 1e-5
+    qf, kf, vf = _f64(q), _f64(kc), _f64(vc)
+    scale = O.default_scale(d)
+    for b in range(B):
+        for r in range(Hkv):
+            toks = O.block_tokens(blocks[b, r], bs, N)
+            want = O.attend(qf[b, r * G:(r + 1) * G], kf[b, r], vf[b, r], toks, scale)
+            check_out(o[b, r * G:(r + 1) * G], want, dtype, "offload %d,%d" % (b, r))
+
+
+def test_gather_blocks_refuses_pageable_memory_and_clamps_ids():
+    """The C call refuses host memory that is not pinned (nothing is
+    launched), and clamps block ids outside the cache into it."""
+    import ctypes
+    from top_sparse_decode_sa_amd import _binding as Bn
+    say("gather blocks: pageable memory refused; out-of-range ids clamped")
+    B, Hkv, N, d, bs = 1, 2, 1024, 128, 128
+    kc = torch.randn((B, Hkv, N, d)).to(torch.bfloat16)          # pageable
+    ids = [[-3, 2, 8], [7, 100, 0]]
+    idx = torch.tensor([ids], dtype=torch.int32, device=dev())
+    out = torch.empty((B, Hkv, 3 * bs, d), dtype=torch.bfloat16, device=dev())
+    desc = T.KVDesc(B, Hkv, Hkv, d, N, T.SA_BF16, T.SA_BF16, kc.stride(0), kc.stride(1),
+                    kc.stride(2), 0.0)
+    p = ctypes.c_void_p
+    st = T.lib().sa_gather_blocks(ctypes.byref(desc), p(kc.data_ptr()), p(kc.data_ptr()),
+                                  p(idx.data_ptr()), 3, bs, p(out.data_ptr()), p(out.data_ptr()),
+                                  None)
+    assert st == Bn.SA_ERR_MEMORY
+    kh = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, pin_memory=True)
+    kh.copy_(kc)
+    ko, _ = T.sa_gather_blocks(kh, kh, idx, bs)
+    torch.cuda.synchronize()
+    kg = ko.cpu()
+    nb = N // bs
+    for r in range(Hkv):
+        want = torch.cat([kc[0, r, min(max(j, 0), nb - 1) * bs:(min(max(j, 0), nb - 1) + 1) * bs]
+                          for j in ids[r]])
+        assert torch.equal(kg[0, r], want)

@@ -10,7 +10,7 @@ from ._binding import (  # noqa: F401
     SA_IDX_TOKEN_PER_Q_HEAD, SA_IDX_TOKEN_SHARED, SA_LAYER_DENSE, SA_LAYER_DENSE_SELECT, SA_LAYER_REUSE, SA_LAYER_SPARSE,
     SA_SCORE_BLOCK_MINMAX, SA_SCORE_EXACT, SA_SCORE_EXACT_PER_Q_HEAD, SA_SCORE_INDEXER, SA_SCORE_INDEXER_PER_KV_HEAD,
     WORKSPACES, KVDesc, LayerArgs, SAError, ScoreAux, layer_args, lib, make_desc,
-    sa_block_summarize, sa_decode_layer, sa_dense_decode, sa_dense_decode_scored,
+    sa_block_summarize, sa_decode_layer, sa_dense_decode, sa_dense_decode_scored, sa_gather_blocks,
     sa_index_overlap, sa_layer_workspace_size, sa_plan_fixed_jump, sa_plan_reuse,
     sa_plan_validate, sa_score, sa_sparse_decode, sa_topk, sa_version, sa_workspace_init)
 

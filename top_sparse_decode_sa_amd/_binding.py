@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libsa.so")
 
 # sa_status
 SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_ALIGN, SA_ERR_DTYPE, SA_ERR_WORKSPACE, \
-    SA_ERR_UNSUPPORTED, SA_ERR_HIP = range(8)
+    SA_ERR_UNSUPPORTED, SA_ERR_HIP, SA_ERR_MEMORY = range(9)
 # sa_dtype
 SA_F32, SA_BF16 = 0, 1
 # sa_score_kind
@@ -35,7 +35,7 @@ EXPORTED = [
     "sa_sparse_workspace_size", "sa_dense_decode", "sa_dense_workspace_size",
     "sa_dense_decode_scored", "sa_dense_scored_workspace_size", "sa_decode_layer",
     "sa_layer_workspace_size", "sa_plan_validate", "sa_index_overlap", "sa_plan_reuse",
-    "sa_plan_fixed_jump", "sa_workspace_init", "sa_status_string", "sa_last_error", "sa_version",
+    "sa_plan_fixed_jump", "sa_gather_blocks", "sa_workspace_init", "sa_status_string", "sa_last_error", "sa_version",
 ]
 
 
@@ -94,6 +94,7 @@ def lib() -> ctypes.CDLL:
     L.sa_index_overlap.argtypes = [vp, vp, i64, i32, vp, vp]
     L.sa_plan_reuse.argtypes = [vp, i64, i32, ctypes.c_double, vp, vp, vp]
     L.sa_plan_fixed_jump.argtypes = [i32, i32, vp, vp]
+    L.sa_gather_blocks.argtypes = [P(KVDesc), vp, vp, vp, i32, i32, vp, vp, vp]
     L.sa_decode_layer.argtypes = [P(LayerArgs), st, vp, vp]
     L.sa_layer_workspace_size.argtypes = [P(LayerArgs), st]
     L.sa_layer_workspace_size.restype = sz
@@ -106,7 +107,8 @@ def lib() -> ctypes.CDLL:
     L.sa_version.restype = ctypes.c_char_p
     for name in ["sa_score", "sa_block_summarize", "sa_topk", "sa_sparse_decode", "sa_dense_decode",
                  "sa_dense_decode_scored", "sa_decode_layer", "sa_plan_validate",
-                 "sa_index_overlap", "sa_plan_reuse", "sa_plan_fixed_jump", "sa_workspace_init"]:
+                 "sa_index_overlap", "sa_plan_reuse", "sa_plan_fixed_jump", "sa_gather_blocks",
+                 "sa_workspace_init"]:
         getattr(L, name).restype = st
     _lib = L
     return L
@@ -351,6 +353,38 @@ def sa_index_overlap(idx_a, idx_b, counts=None):
     check(lib().sa_index_overlap(_ptr(idx_a), _ptr(idx_b), rows, k, _ptr(counts),
                                  ctypes.c_void_p(_stream(dev))))
     return counts
+
+
+def sa_gather_blocks(k_host, v_host, idx, block_size, k_out=None, v_out=None):
+    """sa_gather_blocks: K/V caches [B, Hkv, N, d] in pinned host memory, idx [B, Hkv, n_blk]
+    int32 on the device; returns (k_out, v_out) [B, Hkv, n_blk * block_size, d] on idx's device."""
+    for t in (k_host, v_host):
+        if t.is_cuda or not t.is_pinned():
+            raise ValueError("the host caches must be pinned CPU tensors (pin_memory=True)")
+        if t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError("host caches must be [B, Hkv, N, d] with a contiguous last dimension")
+    if v_host.shape != k_host.shape or v_host.stride() != k_host.stride():
+        raise ValueError("K and V caches must share shape and strides")
+    dev = _dev(idx)
+    if idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be a contiguous int32 tensor")
+    B, Hkv, N, d = k_host.shape
+    n_blk = idx.shape[-1]
+    if tuple(idx.shape) != (B, Hkv, n_blk):
+        raise ValueError("idx must be [B, Hkv, n_blk]")
+    dt = _dtype(k_host)
+    desc = KVDesc(B, Hkv, Hkv, d, N, dt, dt, k_host.stride(0), k_host.stride(1), k_host.stride(2), 0.0)
+    shape = (B, Hkv, n_blk * block_size, d)
+    if k_out is None:
+        k_out = torch.empty(shape, dtype=k_host.dtype, device=dev)
+    if v_out is None:
+        v_out = torch.empty(shape, dtype=k_host.dtype, device=dev)
+    for t in (k_out, v_out):
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError("outputs must be contiguous %s" % (shape,))
+    check(lib().sa_gather_blocks(ctypes.byref(desc), _ptr(k_host), _ptr(v_host), _ptr(idx), n_blk,
+                                 block_size, _ptr(k_out), _ptr(v_out), ctypes.c_void_p(_stream(dev))))
+    return k_out, v_out
 
 
 def _plan_out(n):

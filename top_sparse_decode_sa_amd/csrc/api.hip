@@ -324,6 +324,7 @@ const char* sa_status_string(sa_status s) {
     case SA_ERR_WORKSPACE: return "SA_ERR_WORKSPACE: workspace missing or too small";
     case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED: configuration not built";
     case SA_ERR_HIP: return "SA_ERR_HIP: HIP runtime error";
+    case SA_ERR_MEMORY: return "SA_ERR_MEMORY: a buffer is not the kind of memory the call needs";
   }
   return "unknown sa_status";
 }
@@ -545,6 +546,41 @@ sa_status sa_plan_validate(const int32_t* modes, const int32_t* src, int32_t n_l
     has_idx[l] = (m != SA_LAYER_DENSE);
   }
   return ok();
+}
+
+sa_status sa_gather_blocks(const sa_kv_desc* desc, const void* k_host, const void* v_host,
+                           const int32_t* idx, int32_t n_blk, int32_t block_size, void* k_out,
+                           void* v_out, hipStream_t stream) {
+  Cache c;
+  sa_status st;
+  if ((st = check_desc(desc, &c)) != SA_OK) return st;
+  if (block_size < 1 || block_size > 4096)
+    return fail(SA_ERR_SHAPE, "block_size %d outside [1, 4096]", block_size);
+  if (c.N % block_size != 0)
+    return fail(SA_ERR_SHAPE, "ctx_len %lld is not a multiple of block_size %d", (long long)c.N,
+                block_size);
+  if (n_blk < 1 || n_blk > c.N / block_size)
+    return fail(SA_ERR_SHAPE, "n_blk %d outside [1, %lld]", n_blk, (long long)(c.N / block_size));
+  if ((st = check_ptr(k_host, "k_host", 16)) != SA_OK) return st;
+  if ((st = check_ptr(v_host, "v_host", 16)) != SA_OK) return st;
+  if ((st = check_ptr(idx, "idx", 4)) != SA_OK) return st;
+  if ((st = check_ptr(k_out, "k_out", 16)) != SA_OK) return st;
+  if ((st = check_ptr(v_out, "v_out", 16)) != SA_OK) return st;
+  // the device address of each pinned host allocation; fails for memory the
+  // runtime does not know as pinned host memory
+  void* kd = nullptr;
+  void* vd = nullptr;
+  if (hipHostGetDevicePointer(&kd, const_cast<void*>(k_host), 0) != hipSuccess || !kd) {
+    (void)hipGetLastError();
+    return fail(SA_ERR_MEMORY, "k_host is not pinned host memory the device can read");
+  }
+  if (hipHostGetDevicePointer(&vd, const_cast<void*>(v_host), 0) != hipSuccess || !vd) {
+    (void)hipGetLastError();
+    return fail(SA_ERR_MEMORY, "v_host is not pinned host memory the device can read");
+  }
+  return hip_status(
+      launch_gather_blocks(c, kd, vd, idx, n_blk, block_size, k_out, v_out, stream),
+      "sa_gather_blocks launch");
 }
 
 sa_status sa_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t n_rows, int32_t k,

@@ -783,6 +783,11 @@ AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs) {
       waves = dense_waves_override() ? dense_waves_override() : 4;
       rounds = dense_rounds_override() ? dense_rounds_override() : 8;
       if (mode == kIdxDenseScored) waves = std::min(waves, kMaxScoredWaves);
+      // short contexts: fewer rounds per wave until about 512 workgroups run
+      // (64 rows of 3072 tokens: 12 splits of 256 instead of 2 of 2048)
+      if (!dense_rounds_override())
+        while (rounds > 1 && rows * ((p.n_slots + 64 * waves * rounds - 1) / (64 * waves * rounds)) < 512)
+          rounds /= 2;
     } else {
       // selections split so that about 512 workgroups (two per CU) run; a
       // combine pass merges the splits

@@ -82,6 +82,13 @@ bool fused_scores_supported(const Cache& c);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
+// ------------------------------------------------------------- offload
+// k_dev / v_dev: device addresses of a cache in pinned host memory; c.N is a
+// multiple of bs.  Out: [B, Hkv, n_blk * bs, D] contiguous.
+hipError_t launch_gather_blocks(const Cache& c, const void* k_dev, const void* v_dev,
+                                const int32_t* idx, int32_t n_blk, int32_t bs, void* k_out,
+                                void* v_out, hipStream_t s);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace sa
