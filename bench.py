@@ -644,8 +644,9 @@ def main():
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     if args.profile:
+        # plain launches (no graph capture) under the profiler
         args.steps, args.warmup, args.cpu_seconds, args.dense_steps = 20, 5, 0.0, 0
-        args.cold_iters = 0
+        args.cold_iters, args.eager = 0, True
 
     import torch
     import sa_synth as S

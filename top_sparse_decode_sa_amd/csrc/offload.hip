@@ -9,9 +9,13 @@
 // is then attention restricted to the selected blocks (softmax does not
 // depend on the order of its tokens).
 //
-// One workgroup per (row, block): its tokens' rows are read in 16-byte pieces,
-// eight pieces per thread in flight before any is stored, since every read
-// crosses the host link and waits on its latency.
+// A fixed grid of at most kGatherGroups workgroups walks the (row, block)
+// items: a block's token rows are read in 16-byte pieces, eight pieces of K
+// and eight of V per thread in flight before any is stored, since every read
+// crosses the host link and waits on its latency.  64 workgroups keep about
+// 8 MB of reads in flight -- far more than the link's bandwidth-latency
+// product -- while leaving most compute units free for the attention that
+// runs beside a prefetch.
 #include <algorithm>
 
 #include "common.hpp"
@@ -22,6 +26,7 @@ namespace {
 
 constexpr int kGatherThreads = 256;
 constexpr int kGatherUnroll = 8;
+constexpr int kGatherGroups = 64;
 
 struct GatherArgs {
   const uint8_t* k;  // device address of the pinned host cache
@@ -37,34 +42,36 @@ struct GatherArgs {
   uint8_t* v_out;
 };
 
-__global__ __launch_bounds__(kGatherThreads) void gather_blocks_kernel(GatherArgs a) {
-  const int64_t row = blockIdx.y;
-  const int j = blockIdx.x;
-  const int64_t b = row / a.Hkv;
-  const int64_t r = row % a.Hkv;
-  // an out-of-range id is clamped: the kernel never reads outside the cache
-  const int64_t blk = min(max((int64_t)a.idx[row * a.n_blk + j], (int64_t)0), a.nb - 1);
-  const int pieces = a.row_bytes / 16;        // per token row
-  const int total = a.bs * pieces;            // per block
-  const int64_t src0 = (b * a.sb + r * a.sh + blk * a.bs * a.st) * a.elt;
-  const int64_t dst0 = ((row * a.n_blk + j) * (int64_t)a.bs) * a.row_bytes;
+__global__ __launch_bounds__(kGatherThreads) void gather_blocks_kernel(GatherArgs a, int64_t items) {
+  const int pieces = a.row_bytes / 16;  // per token row
+  const int total = a.bs * pieces;      // per block
   const int64_t st_bytes = a.st * a.elt;
-  for (int base = 0; base < total; base += kGatherThreads * kGatherUnroll) {
-    uint4 kw[kGatherUnroll], vw[kGatherUnroll];
+  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+    const int64_t row = item / a.n_blk;
+    const int j = (int)(item % a.n_blk);
+    const int64_t b = row / a.Hkv;
+    const int64_t r = row % a.Hkv;
+    // an out-of-range id is clamped: the kernel never reads outside the cache
+    const int64_t blk = min(max((int64_t)a.idx[row * a.n_blk + j], (int64_t)0), a.nb - 1);
+    const int64_t src0 = (b * a.sb + r * a.sh + blk * a.bs * a.st) * a.elt;
+    const int64_t dst0 = ((row * a.n_blk + j) * (int64_t)a.bs) * a.row_bytes;
+    for (int base = 0; base < total; base += kGatherThreads * kGatherUnroll) {
+      uint4 kw[kGatherUnroll], vw[kGatherUnroll];
 #pragma unroll
-    for (int u = 0; u < kGatherUnroll; ++u) {
-      const int i = min(base + u * kGatherThreads + (int)threadIdx.x, total - 1);
-      const int64_t off = src0 + (int64_t)(i / pieces) * st_bytes + (i % pieces) * 16;
-      kw[u] = ld16(a.k + off);
-      vw[u] = ld16(a.v + off);
-    }
+      for (int u = 0; u < kGatherUnroll; ++u) {
+        const int i = min(base + u * kGatherThreads + (int)threadIdx.x, total - 1);
+        const int64_t off = src0 + (int64_t)(i / pieces) * st_bytes + (i % pieces) * 16;
+        kw[u] = ld16(a.k + off);
+        vw[u] = ld16(a.v + off);
+      }
 #pragma unroll
-    for (int u = 0; u < kGatherUnroll; ++u) {
-      const int i = base + u * kGatherThreads + (int)threadIdx.x;
-      if (i < total) {
-        const int64_t off = dst0 + (int64_t)i * 16;
-        *reinterpret_cast<uint4*>(a.k_out + off) = kw[u];
-        *reinterpret_cast<uint4*>(a.v_out + off) = vw[u];
+      for (int u = 0; u < kGatherUnroll; ++u) {
+        const int i = base + u * kGatherThreads + (int)threadIdx.x;
+        if (i < total) {
+          const int64_t off = dst0 + (int64_t)i * 16;
+          *reinterpret_cast<uint4*>(a.k_out + off) = kw[u];
+          *reinterpret_cast<uint4*>(a.v_out + off) = vw[u];
+        }
       }
     }
   }
@@ -90,8 +97,9 @@ hipError_t launch_gather_blocks(const Cache& c, const void* k_dev, const void* v
   a.nb = c.N / bs;
   a.k_out = static_cast<uint8_t*>(k_out);
   a.v_out = static_cast<uint8_t*>(v_out);
-  const dim3 grid((unsigned)n_blk, (unsigned)((int64_t)c.B * c.Hkv));
-  hipLaunchKernelGGL(gather_blocks_kernel, grid, dim3(kGatherThreads), 0, s, a);
+  const int64_t items = (int64_t)c.B * c.Hkv * n_blk;
+  const unsigned groups = (unsigned)std::min<int64_t>(items, kGatherGroups);
+  hipLaunchKernelGGL(gather_blocks_kernel, dim3(groups), dim3(kGatherThreads), 0, s, a, items);
   return hipGetLastError();
 }
 
