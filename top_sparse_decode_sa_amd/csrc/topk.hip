@@ -7,27 +7,26 @@
 //
 // Method: radix select on order-preserving uint32 keys (score_key).
 //
-// Row path, one 1024-thread workgroup per row:
-//   1. One pass over the row (16-byte loads, many in flight) builds a
-//      histogram of the top 12 key bits (4096 bins); rows of up to kResident
-//      keys are kept in LDS at the same time.  A prefix sum over the bins
-//      gives d1, the bin of the k-th largest key, and kleft, how many result
-//      elements lie inside that bin.
-//   2. Each wave owns a contiguous, 64-aligned range of positions.  One pass
-//      in that order counts, per wave, the keys in bins above d1 (all of them
-//      are in the result) and collects the keys of bin d1 (the candidates)
-//      with their positions into LDS.
+// Row paths, one 1024-thread workgroup per row:
+//   1. A histogram of the top 12 key bits (4096 bins).  A prefix sum over the
+//      bins gives d1, the bin of the k-th largest key, and kleft, how many
+//      result elements lie inside that bin.
+//   2. The keys of bin d1 (the candidates) are collected with their positions
+//      into LDS; the keys of higher bins are all in the result.
 //   3. The candidates are resolved into T, the key of the last result element
 //      in selection order, and `need`, how many keys equal to T belong to the
 //      result: up to kRankCap candidates by pairwise ranking (rank = number of
 //      candidates with a larger key or an equal key at a lower position; rank
 //      < kleft is kept), more by 8- and 4-bit digit passes over the list.  If
 //      the list overflows, digit passes run over the whole row instead.
-//   4. Ordered write: each wave walks its range in position order; ballots
-//      give every kept element its output slot, the number of kept elements
-//      at lower positions = (keys above T before it) + min(keys equal to T
-//      before it, need).  One block-wide sum of the per-wave counts is the
-//      only cross-wave step.
+//   4. Ordered write: every kept element's output slot is the number of kept
+//      elements at lower positions = (keys above T before it) + min(keys
+//      equal to T before it, need).
+// Rows of at most kResident keys (topk_reg_kernel) keep every key in the
+// registers of the thread that loaded it, 32 per thread, and work on per-
+// thread bit masks after the histogram; longer rows (topk_long_kernel) are
+// read from global memory once per phase, the ordered write through LDS
+// tiles.
 //
 // Multi-workgroup path, for few rows longer than kResident (a single 1M-token
 // sequence): (a) zero a per-row histogram; (b) workgroups of kMwChunk keys add
@@ -350,29 +349,23 @@ __device__ __forceinline__ void write_tile(const uint32_t* keys, int64_t tile0, 
   run_eq += total & 0xffffu;
 }
 
-// The row path for one row, by the whole workgroup.  RES: the row is kept in
-// LDS (n <= kResident); otherwise it is read from global memory again for the
-// candidates and, tile by tile, for the ordered write.
-// buf: RES: kResident keys + kCandRes pairs; otherwise kTile keys + kCandGlob
-// pairs.
-template <bool RES>
-__device__ void topk_row(const float* __restrict__ s, int64_t n, int32_t k,
-                         int32_t* __restrict__ out, bool vec4, Shared& sh, uint32_t* buf) {
-  constexpr int E = RES ? kResident / kThreads : kTile / kThreads;
+// The row path for a row longer than kResident, by the whole workgroup: the
+// row is read from global memory for the histogram, again for the candidates
+// and, tile by tile through LDS, for the ordered write.
+// buf: kTile keys + kCandGlob (key, position) pairs.
+__device__ void topk_row_long(const float* __restrict__ s, int64_t n, int32_t k,
+                              int32_t* __restrict__ out, bool vec4, Shared& sh, uint32_t* buf) {
+  constexpr int E = kTile / kThreads;
   uint32_t* keys = buf;
-  uint2* cand = reinterpret_cast<uint2*>(buf + (RES ? kResident : kTile));
-  constexpr uint32_t cap = RES ? kCandRes : kCandGlob;
+  uint2* cand = reinterpret_cast<uint2*>(buf + kTile);
+  constexpr uint32_t cap = kCandGlob;
   const int tid = threadIdx.x;
-  auto key_at = [&](int64_t i) -> uint32_t {
-    if constexpr (RES) return keys[swz<E>((uint32_t)i)];
-    else return score_key(s[i]);
-  };
+  auto key_at = [&](int64_t i) -> uint32_t { return score_key(s[i]); };
 
   // ---- 1. histogram of the top 12 bits
   zero_hist(sh, kBins);
   __syncthreads();
-  if constexpr (RES) load_tile<E>(s, (int)n, vec4, keys, &sh);
-  else hist_global(s, n, vec4, sh);
+  hist_global(s, n, vec4, sh);
   __syncthreads();
   uint32_t prefix = 0, mask = 0, kleft = (uint32_t)k;
   const uint32_t c1 = select_digit(sh, 20, 12, prefix, mask, kleft);
@@ -380,44 +373,7 @@ __device__ void topk_row(const float* __restrict__ s, int64_t n, int32_t k,
 
   // ---- 2-3. candidates of bin d1, resolved to T and need
   uint32_t T, need;
-  if (RES && c1 <= cap) {
-    // thread t owns keys [E t, E t + E): read them as the ordered write does
-    // (16-byte groups), count this thread's candidates, place them with one
-    // LDS atomic per wave (wave prefix sum of the counts)
-    if (tid == 0) sh.count = 0;
-    __syncthreads();
-    constexpr int G4 = E / 4;
-    constexpr int SW = G4 >= 8 ? 7 : G4 - 1;
-    uint32_t kk[E];
-#pragma unroll
-    for (int g = 0; g < G4; ++g) {
-      const uint4 v = *reinterpret_cast<const uint4*>(&keys[E * tid + 4 * (g ^ (tid & SW))]);
-      kk[4 * g + 0] = v.x;
-      kk[4 * g + 1] = v.y;
-      kk[4 * g + 2] = v.z;
-      kk[4 * g + 3] = v.w;
-    }
-    uint32_t mine = 0, cnt = 0;
-#pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const bool c = (int64_t)E * tid + j < n && (kk[j] >> 20) == d1;
-      mine |= (c ? 1u : 0u) << j;
-      cnt += c ? 1u : 0u;
-    }
-    const uint32_t incl = wave_inclusive_scan(cnt);
-    uint32_t base = 0;
-    if ((tid & 63) == 63 && incl) base = atomicAdd(&sh.count, incl);
-    base = __builtin_amdgcn_readlane(base, 63) + incl - cnt;
-#pragma unroll
-    for (int j = 0; j < E; ++j) {
-      if ((mine >> j) & 1u) {
-        if (base < cap) cand[base] = make_uint2(kk[j], (uint32_t)(E * tid + j));
-        ++base;
-      }
-    }
-    __syncthreads();
-    resolve(cand, c1, kleft, prefix, mask, sh, T, need);
-  } else if (c1 <= cap) {
+  if (c1 <= cap) {
     if (tid == 0) sh.count = 0;
     __syncthreads();
     constexpr int U = 8;
@@ -431,7 +387,10 @@ __device__ void topk_row(const float* __restrict__ s, int64_t n, int32_t k,
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t i = base + (int64_t)u * kThreads + tid;
-        if (i < n && (kk[u] >> 20) == d1) cand[atomicAdd(&sh.count, 1u)] = make_uint2(kk[u], (uint32_t)i);
+        if (i < n && (kk[u] >> 20) == d1) {
+          const uint32_t at = atomicAdd(&sh.count, 1u);
+          if (at < cap) cand[at] = make_uint2(kk[u], (uint32_t)i);
+        }
       }
     }
     __syncthreads();
@@ -440,28 +399,206 @@ __device__ void topk_row(const float* __restrict__ s, int64_t n, int32_t k,
     resolve_row(key_at, n, kleft, prefix, mask, sh, T, need);
   }
 
-  // ---- 4. ordered write
+  // ---- 4. ordered write, one LDS tile at a time
   uint32_t run_gt = 0, run_eq = 0;
-  if constexpr (RES) {
-    write_tile<E>(keys, 0, (int)n, T, need, run_gt, run_eq, out, (uint32_t)k, sh);
+  for (int64_t tile0 = 0; tile0 < n; tile0 += kTile) {
+    const int nv = (int)std::min<int64_t>(kTile, n - tile0);
+    __syncthreads();  // the previous tile is consumed
+    load_tile<E>(s + tile0, nv, vec4, keys, nullptr);
+    __syncthreads();
+    write_tile<E>(keys, tile0, nv, T, need, run_gt, run_eq, out, (uint32_t)k, sh);
+  }
+}
+
+// ------------------------------------------------- register-resident rows
+// Rows of at most kResident keys: every key stays in the registers of the
+// thread that loaded it, so no phase after the load touches the row in
+// memory.  Wave w holds positions [2048 w, 2048 w + 2048); in group j
+// (0..7) lane l holds the four positions 2048 w + 256 j + 4 l + e (one
+// coalesced 16-byte load), so positions run in (j, lane, e) order inside a
+// wave.  Phases: histogram of the top 12 bits; digit select; the candidates
+// of the threshold bin placed in LDS (one atomic per wave) and resolved; the
+// ordered write, where a key's slot is (kept keys of earlier waves) + (of
+// earlier groups of its wave) + (of lower lanes in its group, a DPP prefix
+// sum) + (of lower e in its lane).  Candidate overflow runs the 8/8/4-bit
+// digit passes over the registers.
+constexpr int kRegGroups = kResident / kThreads / 4;  // 8 float4 groups per thread
+
+__global__ __launch_bounds__(kThreads) void topk_reg_kernel(const float* __restrict__ scores,
+                                                            int64_t n64, int64_t row_stride,
+                                                            int32_t k, int32_t* __restrict__ idx_out,
+                                                            bool vec4) {
+  __shared__ Shared sh;
+  __shared__ __align__(16) uint2 cand[kCandRes];
+  __shared__ uint32_t s_wave[kWaves];
+  const int n = (int)n64;  // <= kResident
+  const float* __restrict__ s = scores + (int64_t)blockIdx.x * row_stride;
+  int32_t* __restrict__ out = idx_out + (int64_t)blockIdx.x * k;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int p0 = wave * (kRegGroups * 256) + 4 * lane;  // position of (j = 0, e = 0)
+  auto pos = [&](int j, int e) { return p0 + 256 * j + e; };
+
+  // ---- 1. load (every load issued first) and the 12-bit histogram, each
+  // group counted as soon as its load arrives
+  zero_hist(sh, kBins);
+  __syncthreads();
+  uint32_t key[kRegGroups][4];
+  {
+    float v[kRegGroups][4];
+    if (vec4 && n % 4 == 0) {
+      // a group lies wholly inside or wholly outside the row
+      const float4* s4 = reinterpret_cast<const float4*>(s + p0);
+#pragma unroll
+      for (int j = 0; j < kRegGroups; ++j) {
+        const float4 f = pos(j, 0) < n ? s4[64 * j] : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[j][0] = f.x;
+        v[j][1] = f.y;
+        v[j][2] = f.z;
+        v[j][3] = f.w;
+      }
+    } else {
+      const float* s1 = s + p0;
+#pragma unroll
+      for (int j = 0; j < kRegGroups; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[j][e] = pos(j, e) < n ? s1[256 * j + e] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < kRegGroups; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        key[j][e] = score_key(v[j][e]);
+        if (pos(j, e) < n) atomicAdd(&sh.hist[key[j][e] >> 20], 1u);
+      }
+  }
+  __syncthreads();
+  uint32_t prefix = 0, mask = 0, kleft = (uint32_t)k;
+  const uint32_t c1 = select_digit(sh, 20, 12, prefix, mask, kleft);
+  const uint32_t d1 = prefix >> 20;
+
+  // ---- 2-3. per-thread bit masks over its keys (bit 4j + e): m_above =
+  // keys in bins above d1 (all kept), m_cand = keys of bin d1 (the
+  // candidates); then T (key of the last kept element) and need (kept keys
+  // equal to T)
+  const uint32_t lo = d1 << 20;                  // smallest key of bin d1
+  const bool top_bin = d1 == (uint32_t)(kBins - 1);
+  const uint32_t hi = top_bin ? 0u : (d1 + 1) << 20;  // smallest key above bin d1
+  uint32_t m_ge = 0, m_above = 0;
+#pragma unroll
+  for (int j = 0; j < kRegGroups; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool ok = pos(j, e) < n;
+      m_ge |= (ok && key[j][e] >= lo) ? 1u << (4 * j + e) : 0u;
+      m_above |= (ok && !top_bin && key[j][e] >= hi) ? 1u << (4 * j + e) : 0u;
+    }
+  const uint32_t m_cand = m_ge & ~m_above;
+  uint32_t T, need;
+  uint32_t m_gt = m_above, m_eq = 0;  // kept above T, equal to T
+  if (c1 <= (uint32_t)kCandRes) {
+    if (tid == 0) sh.count = 0;
+    __syncthreads();
+    const uint32_t cnt = __builtin_popcount(m_cand);
+    const uint32_t incl = wave_inclusive_scan(cnt);
+    uint32_t base = 0;
+    if (lane == 63 && incl) base = atomicAdd(&sh.count, incl);
+    base = __builtin_amdgcn_readlane(base, 63) + incl - cnt;
+    // few candidates per wave: a bit no lane holds is skipped as a whole
+#pragma unroll
+    for (int j = 0; j < kRegGroups; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((m_cand >> (4 * j + e)) & 1u) {
+          if (base < (uint32_t)kCandRes) cand[base] = make_uint2(key[j][e], (uint32_t)pos(j, e));
+          ++base;
+        }
+    __syncthreads();
+    resolve(cand, c1, kleft, prefix, mask, sh, T, need);
+#pragma unroll
+    for (int j = 0; j < kRegGroups; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((m_cand >> (4 * j + e)) & 1u) {
+          m_gt |= key[j][e] > T ? 1u << (4 * j + e) : 0u;
+          m_eq |= key[j][e] == T ? 1u << (4 * j + e) : 0u;
+        }
   } else {
-    for (int64_t tile0 = 0; tile0 < n; tile0 += kTile) {
-      const int nv = (int)std::min<int64_t>(kTile, n - tile0);
-      __syncthreads();  // the previous tile is consumed
-      load_tile<E>(s + tile0, nv, vec4, keys, nullptr);
+    constexpr int kShift[3] = {12, 4, 0};
+    constexpr int kWidth[3] = {8, 8, 4};
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+      zero_hist(sh, 1 << kWidth[d]);
       __syncthreads();
-      write_tile<E>(keys, tile0, nv, T, need, run_gt, run_eq, out, (uint32_t)k, sh);
+#pragma unroll
+      for (int j = 0; j < kRegGroups; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (pos(j, e) < n && (key[j][e] & mask) == prefix)
+            atomicAdd(&sh.hist[(key[j][e] >> kShift[d]) & ((1u << kWidth[d]) - 1u)], 1u);
+      __syncthreads();
+      select_digit(sh, kShift[d], kWidth[d], prefix, mask, kleft);
+    }
+    T = prefix;
+    need = kleft;
+#pragma unroll
+    for (int j = 0; j < kRegGroups; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = pos(j, e) < n;
+        m_gt |= (ok && key[j][e] > T) ? 1u << (4 * j + e) : 0u;
+        m_eq |= (ok && key[j][e] == T) ? 1u << (4 * j + e) : 0u;
+      }
+  }
+
+  // ---- 4. ordered write.  Group j's counts, packed (above T) << 16 |
+  // (equal to T), are prefix-summed over the wave's lanes; the groups of a
+  // wave follow each other, the waves follow each other.
+  uint32_t gbase[kRegGroups];  // kept keys before this lane's group j (packed)
+  uint32_t run = 0;
+#pragma unroll
+  for (int j = 0; j < kRegGroups; ++j) {
+    const uint32_t c = (__builtin_popcount((m_gt >> (4 * j)) & 0xfu) << 16) |
+                       __builtin_popcount((m_eq >> (4 * j)) & 0xfu);
+    const uint32_t incl = wave_inclusive_scan(c);
+    gbase[j] = run + incl - c;
+    run += __builtin_amdgcn_readlane(incl, 63);
+  }
+  if (lane == 0) s_wave[wave] = run;
+  __syncthreads();
+  uint32_t before = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) before += w < wave ? s_wave[w] : 0u;
+  uint32_t m_keep = m_gt | m_eq;
+  while (m_keep) {
+    const int bit = __builtin_ctz(m_keep);
+    m_keep &= m_keep - 1u;
+    const int j = bit >> 2;
+    uint32_t gb = gbase[0];
+#pragma unroll
+    for (int t = 1; t < kRegGroups; ++t) gb = j == t ? gbase[t] : gb;
+    const uint32_t lower = ((1u << bit) - 1u) & (0xfu << (4 * j));  // same group, lower e
+    gb += before;
+    const uint32_t g = (gb >> 16) + __builtin_popcount(m_gt & lower);
+    const uint32_t q = (gb & 0xffffu) + __builtin_popcount(m_eq & lower);
+    const int32_t p = pos(j, bit & 3);
+    if ((m_gt >> bit) & 1u) {
+      const uint32_t slot = g + std::min(q, need);
+      if (slot < (uint32_t)k) out[slot] = p;
+    } else if (q < need && g + q < (uint32_t)k) {
+      out[g + q] = p;
     }
   }
 }
 
-template <bool RES>
-__global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores, int64_t n,
-                                                        int64_t row_stride, int32_t k,
-                                                        int32_t* __restrict__ idx_out, bool vec4) {
+__global__ __launch_bounds__(kThreads) void topk_long_kernel(const float* __restrict__ scores,
+                                                             int64_t n, int64_t row_stride,
+                                                             int32_t k, int32_t* __restrict__ idx_out,
+                                                             bool vec4) {
   __shared__ Shared sh;
-  __shared__ __align__(16) uint32_t buf[RES ? kResident + 2 * kCandRes : kTile + 2 * kCandGlob];
-  topk_row<RES>(scores + (int64_t)blockIdx.x * row_stride, n, k,
+  __shared__ __align__(16) uint32_t buf[kTile + 2 * kCandGlob];
+  topk_row_long(scores + (int64_t)blockIdx.x * row_stride, n, k,
                 idx_out + (int64_t)blockIdx.x * k, vec4, sh, buf);
 }
 
@@ -559,8 +696,8 @@ __global__ __launch_bounds__(kThreads) void topk_mw_resolve(const float* __restr
   const uint32_t c1 = mw_select(w, k, sh, prefix, mask, kleft);
   if (c1 > (uint32_t)kMwCand) {
     if (threadIdx.x == 0) w.fallback = 1u;
-    topk_row<false>(scores + (int64_t)blockIdx.x * row_stride, n, k,
-                    idx_out + (int64_t)blockIdx.x * k, vec4, sh, buf);
+    topk_row_long(scores + (int64_t)blockIdx.x * row_stride, n, k,
+                  idx_out + (int64_t)blockIdx.x * k, vec4, sh, buf);
     return;
   }
   uint2* cand = reinterpret_cast<uint2*>(buf + kTile);
@@ -685,7 +822,7 @@ hipError_t launch_topk(const float* scores, int64_t n_rows, int64_t n, int64_t r
   // 16-byte loads when every row starts 16-byte aligned
   const bool vec4 = (reinterpret_cast<uintptr_t>(scores) % 16 == 0) && (row_stride % 4 == 0);
   if (n <= kResident) {
-    hipLaunchKernelGGL(topk_kernel<true>, dim3((unsigned)n_rows), dim3(kThreads), 0, s, scores, n,
+    hipLaunchKernelGGL(topk_reg_kernel, dim3((unsigned)n_rows), dim3(kThreads), 0, s, scores, n,
                        row_stride, k, idx, vec4);
   } else if (use_mw(n_rows, n, k)) {
     MwRow* rows = static_cast<MwRow*>(ws);
@@ -698,7 +835,7 @@ hipError_t launch_topk(const float* scores, int64_t n_rows, int64_t n, int64_t r
     hipLaunchKernelGGL(topk_mw_write, grid, dim3(kThreads), 0, s, scores, n, row_stride, k, vec4,
                        rows, idx);
   } else {
-    hipLaunchKernelGGL(topk_kernel<false>, dim3((unsigned)n_rows), dim3(kThreads), 0, s, scores, n,
+    hipLaunchKernelGGL(topk_long_kernel, dim3((unsigned)n_rows), dim3(kThreads), 0, s, scores, n,
                        row_stride, k, idx, vec4);
   }
   return hipGetLastError();
