@@ -376,20 +376,60 @@ __device__ void topk_row_long(const float* __restrict__ s, int64_t n, int32_t k,
   if (c1 <= cap) {
     if (tid == 0) sh.count = 0;
     __syncthreads();
-    constexpr int U = 8;
-    for (int64_t base = 0; base < n; base += (int64_t)kThreads * U) {
-      uint32_t kk[U];
+    if (vec4 && n % 4 == 0) {
+      // 16-byte loads, 32 keys per thread in flight; one LDS atomic per wave
+      // places the wave's candidates
+      constexpr int U = 8;
+      const float4* s4 = reinterpret_cast<const float4*>(s);
+      const int64_t n4 = n / 4;
+      for (int64_t base = 0; base < n4; base += (int64_t)kThreads * U) {
+        uint32_t kk[U][4];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t i = base + (int64_t)u * kThreads + tid;
-        kk[u] = i < n ? key_at(i) : 0u;
+        for (int u = 0; u < U; ++u) {
+          const int64_t i = base + (int64_t)u * kThreads + tid;
+          const float4 v = i < n4 ? s4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+          kk[u][0] = score_key(v.x);
+          kk[u][1] = score_key(v.y);
+          kk[u][2] = score_key(v.z);
+          kk[u][3] = score_key(v.w);
+        }
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            cnt += (base + (int64_t)u * kThreads + tid < n4 && (kk[u][e] >> 20) == d1) ? 1u : 0u;
+        const uint32_t incl = wave_inclusive_scan(cnt);
+        uint32_t at = 0;
+        if ((tid & 63) == 63 && incl) at = atomicAdd(&sh.count, incl);
+        at = __builtin_amdgcn_readlane(at, 63) + incl - cnt;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t i = base + (int64_t)u * kThreads + tid;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (i < n4 && (kk[u][e] >> 20) == d1) {
+              if (at < cap) cand[at] = make_uint2(kk[u][e], (uint32_t)(4 * i + e));
+              ++at;
+            }
+        }
       }
+    } else {
+      constexpr int U = 8;
+      for (int64_t base = 0; base < n; base += (int64_t)kThreads * U) {
+        uint32_t kk[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t i = base + (int64_t)u * kThreads + tid;
-        if (i < n && (kk[u] >> 20) == d1) {
-          const uint32_t at = atomicAdd(&sh.count, 1u);
-          if (at < cap) cand[at] = make_uint2(kk[u], (uint32_t)i);
+        for (int u = 0; u < U; ++u) {
+          const int64_t i = base + (int64_t)u * kThreads + tid;
+          kk[u] = i < n ? key_at(i) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t i = base + (int64_t)u * kThreads + tid;
+          if (i < n && (kk[u] >> 20) == d1) {
+            const uint32_t at = atomicAdd(&sh.count, 1u);
+            if (at < cap) cand[at] = make_uint2(kk[u], (uint32_t)i);
+          }
         }
       }
     }
@@ -401,12 +441,46 @@ __device__ void topk_row_long(const float* __restrict__ s, int64_t n, int32_t k,
 
   // ---- 4. ordered write, one LDS tile at a time
   uint32_t run_gt = 0, run_eq = 0;
-  for (int64_t tile0 = 0; tile0 < n; tile0 += kTile) {
-    const int nv = (int)std::min<int64_t>(kTile, n - tile0);
-    __syncthreads();  // the previous tile is consumed
-    load_tile<E>(s + tile0, nv, vec4, keys, nullptr);
-    __syncthreads();
-    write_tile<E>(keys, tile0, nv, T, need, run_gt, run_eq, out, (uint32_t)k, sh);
+  if (vec4 && n % 4 == 0) {
+    // two LDS tiles (the candidate list is no longer needed): the next
+    // tile's 16-byte loads are in flight while the current tile is written
+    constexpr int U4 = E / 4;  // float4 per thread per tile
+    const float4* s4 = reinterpret_cast<const float4*>(s);
+    const int64_t n4 = n / 4;
+    uint32_t* tiles[2] = {keys, buf + kTile};
+    float4 v[U4];
+    auto fetch = [&](int64_t tile0) {
+#pragma unroll
+      for (int u = 0; u < U4; ++u) {
+        const int64_t i = tile0 / 4 + u * kThreads + tid;
+        v[u] = i < n4 ? s4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    };
+    __syncthreads();  // the candidate list is consumed
+    fetch(0);
+    int cur = 0;
+    for (int64_t tile0 = 0; tile0 < n; tile0 += kTile) {
+      const int nv = (int)std::min<int64_t>(kTile, n - tile0);
+#pragma unroll
+      for (int u = 0; u < U4; ++u) {
+        const int i = u * kThreads + tid;  // float4 index inside the tile
+        if (4 * i < nv)
+          *reinterpret_cast<uint4*>(&tiles[cur][swz<E>(4 * i)]) =
+              make_uint4(score_key(v[u].x), score_key(v[u].y), score_key(v[u].z), score_key(v[u].w));
+      }
+      __syncthreads();
+      if (tile0 + kTile < n) fetch(tile0 + kTile);
+      write_tile<E>(tiles[cur], tile0, nv, T, need, run_gt, run_eq, out, (uint32_t)k, sh);
+      cur ^= 1;
+    }
+  } else {
+    for (int64_t tile0 = 0; tile0 < n; tile0 += kTile) {
+      const int nv = (int)std::min<int64_t>(kTile, n - tile0);
+      __syncthreads();  // the previous tile is consumed
+      load_tile<E>(s + tile0, nv, vec4, keys, nullptr);
+      __syncthreads();
+      write_tile<E>(keys, tile0, nv, T, need, run_gt, run_eq, out, (uint32_t)k, sh);
+    }
   }
 }
 
