@@ -51,11 +51,14 @@ def test_topk_bit_exact(n):
 
 
 @pytest.mark.parametrize("rows,n,k", [(3, 40000, 1), (3, 200003, 2048), (2, 200003, 8192),
-                                       (2, 100000, 9000), (1, 1048576, 2048)])
+                                       (2, 100000, 9000), (1, 1048576, 2048), (70, 40004, 300),
+                                       (66, 65536, 5000), (65, 131072, 12000)])
 def test_topk_long_rows(rows, n, k):
-    """Rows longer than the LDS-resident limit: few rows take the
-    multi-workgroup path (k <= 8192), larger k the row path; tied rows whose
-    candidate bin overflows exercise the in-kernel fallback."""
+    """Rows longer than the register-resident limit: few rows take the
+    multi-workgroup path (k <= 8192), more rows or larger k the row path --
+    its short-list finish when the keys of the threshold bin and above fit in
+    LDS (with a partial last chunk), its LDS tiles otherwise; tied rows whose
+    candidate bin overflows exercise the in-kernel fallbacks."""
     say("topk long rows=%d n=%d k=%d" % (rows, n, k))
     rng = np.random.default_rng(n + k)
     vals = rng.standard_normal((rows, n)).astype(np.float32)

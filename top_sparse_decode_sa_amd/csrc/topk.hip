@@ -349,6 +349,99 @@ __device__ __forceinline__ void write_tile(const uint32_t* keys, int64_t tile0, 
   run_eq += total & 0xffffu;
 }
 
+// Short-list finish of a long row (16-byte aligned rows, n % 4 == 0): one
+// ordered pass over the row collects every key of bin d1 or above, with its
+// position, into list (in position order; a workgroup prefix sum per chunk of
+// 16384 keys, the next chunk's loads in flight meanwhile) and the keys of bin
+// d1 into cand; the candidates are resolved, and the ordered write walks the
+// list.  buf holds kListCap list pairs and kListCand candidate pairs.
+constexpr int kListCap = 12288;
+constexpr int kListCand = 4096;
+
+__device__ void long_row_short_list(const float* __restrict__ s, int64_t n, int32_t k, uint32_t d1,
+                                    uint32_t c1, uint32_t kleft, uint32_t prefix, uint32_t mask,
+                                    int32_t* __restrict__ out, Shared& sh, uint32_t* buf) {
+  uint2* list = reinterpret_cast<uint2*>(buf);
+  uint2* cand = list + kListCap;
+  const int tid = threadIdx.x;
+  constexpr int KPT = 16;                  // keys per thread per chunk
+  constexpr int CHUNK = KPT * kThreads;    // 16384
+  const float4* s4 = reinterpret_cast<const float4*>(s);
+  const int64_t n4 = n / 4;
+  float4 v[KPT / 4];
+  auto fetch = [&](int64_t c0) {
+#pragma unroll
+    for (int u = 0; u < KPT / 4; ++u) {
+      const int64_t i = c0 / 4 + (int64_t)(KPT / 4) * tid + u;  // thread t: positions c0 + 16t ..
+      v[u] = i < n4 ? s4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  uint32_t list_base = 0, cand_base = 0;
+  fetch(0);
+  for (int64_t c0 = 0; c0 < n; c0 += CHUNK) {
+    uint32_t key[KPT];
+#pragma unroll
+    for (int u = 0; u < KPT / 4; ++u) {
+      key[4 * u + 0] = score_key(v[u].x);
+      key[4 * u + 1] = score_key(v[u].y);
+      key[4 * u + 2] = score_key(v[u].z);
+      key[4 * u + 3] = score_key(v[u].w);
+    }
+    const int64_t p0 = c0 + (int64_t)KPT * tid;
+    uint32_t n_ge = 0, n_c = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const bool ok = p0 + j < n;
+      n_ge += (ok && (key[j] >> 20) >= d1) ? 1u : 0u;
+      n_c += (ok && (key[j] >> 20) == d1) ? 1u : 0u;
+    }
+    if (c0 + CHUNK < n) fetch(c0 + CHUNK);  // in flight during the scan and the stores
+    uint32_t total;
+    const uint32_t excl = block_exclusive_scan((n_ge << 16) | n_c, sh.tot, total);
+    uint32_t at_l = list_base + (excl >> 16), at_c = cand_base + (excl & 0xffffu);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if (p0 + j < n && (key[j] >> 20) >= d1) {
+        const uint2 e = make_uint2(key[j], (uint32_t)(p0 + j));
+        if (at_l < (uint32_t)kListCap) list[at_l] = e;
+        ++at_l;
+        if ((key[j] >> 20) == d1) {
+          if (at_c < (uint32_t)kListCand) cand[at_c] = e;
+          ++at_c;
+        }
+      }
+    }
+    list_base += total >> 16;
+    cand_base += total & 0xffffu;
+  }
+  __syncthreads();
+  uint32_t T, need;
+  resolve(cand, c1, kleft, prefix, mask, sh, T, need);
+  // ordered write over the list: thread t takes entries [E t, E t + E)
+  const uint32_t L = min(list_base, (uint32_t)kListCap);
+  const uint32_t E = (L + kThreads - 1) / kThreads;
+  const uint32_t e0 = min(E * tid, L), e1 = min(e0 + E, L);
+  uint32_t cg = 0, ce = 0;
+  for (uint32_t i = e0; i < e1; ++i) {
+    cg += list[i].x > T ? 1u : 0u;
+    ce += list[i].x == T ? 1u : 0u;
+  }
+  uint32_t total;
+  const uint32_t excl = block_exclusive_scan((cg << 16) | ce, sh.tot, total);
+  uint32_t gb = excl >> 16, eb = excl & 0xffffu;
+  for (uint32_t i = e0; i < e1; ++i) {
+    const uint2 e = list[i];
+    if (e.x > T) {
+      const uint32_t slot = gb + std::min(eb, need);
+      if (slot < (uint32_t)k) out[slot] = (int32_t)e.y;
+      ++gb;
+    } else if (e.x == T) {
+      if (eb < need && gb + eb < (uint32_t)k) out[gb + eb] = (int32_t)e.y;
+      ++eb;
+    }
+  }
+}
+
 // The row path for a row longer than kResident, by the whole workgroup: the
 // row is read from global memory for the histogram, again for the candidates
 // and, tile by tile through LDS, for the ordered write.
@@ -370,6 +463,15 @@ __device__ void topk_row_long(const float* __restrict__ s, int64_t n, int32_t k,
   uint32_t prefix = 0, mask = 0, kleft = (uint32_t)k;
   const uint32_t c1 = select_digit(sh, 20, 12, prefix, mask, kleft);
   const uint32_t d1 = prefix >> 20;
+
+  // ---- short-list path: every key in bin d1 or above (k - kleft + c1 of
+  // them) is collected in position order in one pass, and the ordered write
+  // walks that list instead of the row
+  if (vec4 && n % 4 == 0 && (uint64_t)(k - kleft) + c1 <= (uint64_t)kListCap &&
+      c1 <= (uint32_t)kListCand) {
+    long_row_short_list(s, n, k, d1, c1, kleft, prefix, mask, out, sh, buf);
+    return;
+  }
 
   // ---- 2-3. candidates of bin d1, resolved to T and need
   uint32_t T, need;
