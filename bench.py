@@ -99,7 +99,7 @@ TRAFFIC_KERNELS = {
                                            "top_sparse_decode_sa_amd/csrc/common.hpp"]),
     "sparse_attend": ("attend_sparse_kernel", ["top_sparse_decode_sa_amd/csrc/attend.hip",
                                                "top_sparse_decode_sa_amd/csrc/common.hpp"]),
-    "topk": ("topk_kernel", ["top_sparse_decode_sa_amd/csrc/topk.hip",
+    "topk": ("topk_reg_kernel", ["top_sparse_decode_sa_amd/csrc/topk.hip",
                              "top_sparse_decode_sa_amd/csrc/common.hpp"]),
 }
 
