@@ -611,14 +611,16 @@ sa_status sa_plan_reuse(const int64_t* overlap, int64_t total, int32_t n_layers,
       if (o < 0 || o > total)
         return fail(SA_ERR_SHAPE, "overlap[%d][%d] = %lld outside [0, total]", i, j, (long long)o);
     }
-  // reuse[i][j]: layer j may reuse the set of layer i (vertical move allowed)
+  // may_reuse(i, j): layer j may reuse the set of layer i (the vertical move
+  // into (i, j) is allowed)
   auto may_reuse = [&](int i, int j) {
     if (sensitive && sensitive[j]) return false;
     return (double)overlap[(int64_t)i * L + j] / (double)total > theta;
   };
-  // Suffix dynamic programme over reset layers: best[j] = (full layers,
-  // summed overlap) of layers j..L-1 given that layer j resets; next[j] = the
-  // following reset layer (L: none).  The reused run after reset j is
+  // Suffix dynamic programme over reset layers: (fulls[j], sim[j]) = the
+  // best (full layers, summed overlap) of layers j..L-1 given that layer j
+  // resets; next[j] = the following reset layer (L: none).  The reused run
+  // after reset j is
   // j+1..j'-1, so the policy's path is (j, j) -> (j, j+1) -> ... -> (j, j'-1)
   // -> (j', j').
   int32_t fulls[kMaxLayers + 1];
