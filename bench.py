@@ -100,7 +100,7 @@ TRAFFIC_KERNELS = {
     "sparse_attend": ("attend_sparse_kernel", ["top_sparse_decode_sa_amd/csrc/attend.hip",
                                                "top_sparse_decode_sa_amd/csrc/common.hpp"]),
     "topk": ("topk_reg_kernel", ["top_sparse_decode_sa_amd/csrc/topk.hip",
-                             "top_sparse_decode_sa_amd/csrc/common.hpp"]),
+                                 "top_sparse_decode_sa_amd/csrc/common.hpp"]),
 }
 
 
@@ -147,6 +147,12 @@ def pmc_means(db_path, counter):
     return {name: (val, n) for name, val, n in rows}
 
 
+def db_dir_name(db_path):
+    """The rocprofv3 -d folder and -o name that wrote `db_path`."""
+    base = os.path.basename(db_path)
+    return os.path.dirname(db_path), base[:-len("_results.db")] if base.endswith("_results.db") else base
+
+
 def traffic_report(fetch_db, write_db):
     """HBM bytes per dispatch of the step's kernels.  FETCH_SIZE and
     WRITE_SIZE are scaled by what they read for the calibration copies that
@@ -168,12 +174,11 @@ def traffic_report(fetch_db, write_db):
     lines = ["# HBM traffic per dispatch, calibrated byte counters",
              "#",
              "# commands (one counter per run, then this report):",
-             "#   rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof_fetch -o fetch -- "
-             "python -u bench.py --profile",
-             "#   rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof_write -o write -- "
-             "python -u bench.py --profile",
-             "#   python bench.py --traffic gpurun_out/prof_fetch/fetch_results.db "
-             "gpurun_out/prof_write/write_results.db",
+             "#   rocprofv3 --pmc FETCH_SIZE -d %s -o %s -- python -u bench.py --profile"
+             % db_dir_name(fetch_db),
+             "#   rocprofv3 --pmc WRITE_SIZE -d %s -o %s -- python -u bench.py --profile"
+             % db_dir_name(write_db),
+             "#   python bench.py --traffic %s %s" % (fetch_db, write_db),
              "# bench.py --profile runs three 1 GiB device-to-device copies that read and write",
              "# exactly 1073741824 bytes each; factor = 1073741824 / (counter KiB of a copy * 1024)",
              "#",
