@@ -4,7 +4,8 @@ Workload (default): the Llama-3.1-8B-shaped decode step -- batch 16, 32 query
 / 8 KV heads, head_dim 128, bf16 KV cache of 32768 tokens per sequence, exact
 top-k per (sequence, KV head) at 50x sparsity (k = 655).  One step is one pass
 of the whole hot path through the C ABI:
-    sa_score (exact) -> sa_topk -> sa_sparse_decode (gather + split-K attend).
+    sa_select (exact scoring fused with a per-part top-k, then the merge)
+    -> sa_sparse_decode (gather + split-K attend).
 Queries rotate over 8 pre-generated variants so consecutive steps select
 different tokens; the cache (2.15 GB) is resident in HBM before timing starts.
 
@@ -13,16 +14,18 @@ torch.cuda.synchronize().  Each step is captured once per query variant as a
 HIP graph of its three launches and replayed (a serving loop's form; --eager
 times plain launches instead); the bench checks that a replay selects and
 attends exactly as an eager step.  A separate pass of eager steps with HIP
-events recorded on the launch stream between the three calls gives each
-kernel's average duration.
+events recorded on the launch stream between the two calls gives each call's
+average duration.
 
 Prints ONE JSON line.  `value` is the step's achieved HBM bandwidth
-(algorithmic bytes of score + top-k + attend per step / time per step);
-`steps_per_s` is the decode-step rate; `roofline` is the dominant kernel
-(exact scoring); `kernels` holds every kernel's bytes, time and fraction of
-the 8 TB/s peak, including the gather-attend kernel alone and a dense decode
-over the same cache for comparison.  `cpu_baseline` times the CPU oracle on a
-bounded sample of the same step (rows of the batch), scaled to a full step.
+(algorithmic bytes of selection + attend per step / time per step);
+`steps_per_s` is the decode-step rate; `roofline` is the dominant unit (the
+sa_select call: its fused kernel and merge); `kernels` holds each unit's
+bytes, time and fraction of the 8 TB/s peak, including the gather-attend
+alone, the unfused selection (sa_score then sa_topk on the same inputs) and a
+dense decode over the same cache for comparison.  `cpu_baseline` times the
+CPU oracle on a bounded sample of the same step (rows of the batch), scaled
+to a full step.
 """
 from __future__ import annotations
 
@@ -94,13 +97,19 @@ def parse():
 COPY_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "llama32k_hbm_traffic.txt")
 # kernel -> (name fragment in the trace, sources whose hash the counters belong to)
+# kernel -> (name fragments of its launches in the trace -- their bytes per
+# dispatch add up --, sources whose hash the counters belong to)
+_SEL_SRC = ["top_sparse_decode_sa_amd/csrc/select.hip", "top_sparse_decode_sa_amd/csrc/topk.hip",
+            "top_sparse_decode_sa_amd/csrc/topk_core.hpp", "top_sparse_decode_sa_amd/csrc/common.hpp"]
 TRAFFIC_KERNELS = {
-    "score_exact": ("score_exact_kernel", ["top_sparse_decode_sa_amd/csrc/score.hip",
-                                           "top_sparse_decode_sa_amd/csrc/common.hpp"]),
-    "sparse_attend": ("attend_sparse_kernel", ["top_sparse_decode_sa_amd/csrc/attend.hip",
-                                               "top_sparse_decode_sa_amd/csrc/common.hpp"]),
-    "topk": ("topk_reg_kernel", ["top_sparse_decode_sa_amd/csrc/topk.hip",
-                                 "top_sparse_decode_sa_amd/csrc/common.hpp"]),
+    "select": (["select_part_kernel", "topk_reg_kernel<512, 2, true>"], _SEL_SRC),
+    "sparse_attend": (["attend_sparse_kernel"], ["top_sparse_decode_sa_amd/csrc/attend.hip",
+                                                 "top_sparse_decode_sa_amd/csrc/common.hpp"]),
+    "score_exact": (["score_exact_kernel"], ["top_sparse_decode_sa_amd/csrc/score.hip",
+                                             "top_sparse_decode_sa_amd/csrc/common.hpp"]),
+    "topk": (["topk_reg_kernel<1024, 8, false>"], ["top_sparse_decode_sa_amd/csrc/topk.hip",
+                                                "top_sparse_decode_sa_amd/csrc/topk_core.hpp",
+                                                "top_sparse_decode_sa_amd/csrc/common.hpp"]),
 }
 
 
@@ -189,12 +198,17 @@ def traffic_report(fetch_db, write_db):
         lines.append("%-70s %6d %14.1f %14.1f %14d" % (name[:70], n, fk, wk,
                                                         round(fk * 1024 * ff + wk * 1024 * wf)))
     lines += ["", "fetch_factor: %.6f" % ff, "write_factor: %.6f" % wf]
-    for key, (frag, srcs) in TRAFFIC_KERNELS.items():
-        names = [n for n in fetch if frag in n]
-        if not names:
+    for key, (frags, srcs) in TRAFFIC_KERNELS.items():
+        t, found = 0, True
+        for frag in frags:
+            names = [n for n in fetch if frag in n]
+            if not names:
+                found = False
+                break
+            name = max(names, key=lambda n: fetch[n][1])
+            t += round(fetch[name][0] * 1024 * ff + write.get(name, (0.0, 0))[0] * 1024 * wf)
+        if not found:
             continue
-        name = max(names, key=lambda n: fetch[n][1])
-        t = round(fetch[name][0] * 1024 * ff + write.get(name, (0.0, 0))[0] * 1024 * wf)
         lines.append("%s.traffic_bytes_per_launch: %d" % (key, t))
         if key in alg:
             lines.append("%s.algorithmic_bytes_per_launch: %d" % (key, alg[key]))
@@ -221,6 +235,22 @@ def read_traffic(kernel):
         return None
 
 
+def select_candidates(rows, n, k):
+    """Candidates per row of the fused exact selection (sa_select): parts of
+    8192 tokens, halved (down to 256) while the grid has fewer than 512
+    workgroups and the candidates stay under half the row; each part keeps
+    min(k, its length).  Returns (candidates, fused)."""
+    def cands(L):
+        P = -(-n // L)
+        return (P - 1) * min(k, L) + min(k, n - (P - 1) * L)
+
+    L = 8192
+    while L > 256 and rows * -(-n // L) < 512 and 2 * cands(L // 2) <= n:
+        L //= 2
+    C = cands(L)
+    return C, (-(-n // L) == 1 or (C <= 32768 and 2 * C <= n))
+
+
 def step_bytes(cfg):
     """Algorithmic HBM bytes of one step's kernels (each input read once,
     each output written once)."""
@@ -231,10 +261,15 @@ def step_bytes(cfg):
     scores = rows * N * 4
     idx = rows * k * 4
     out = B * Hq * d * 4
+    C, fused = select_candidates(rows, N, k)
+    assert fused, "the step's selection takes the fused path"
     return {
+        # sa_select: keys and queries read, (score, position) candidates
+        # written and read back by the merge, the index list written
+        "select": rows * N * d * e + q_bytes + 2 * rows * C * 8 + idx,
+        "sparse_attend": 2 * rows * k * d * e + idx + q_bytes + out,
         "score_exact": rows * N * d * e + q_bytes + scores,
         "topk": scores + idx,
-        "sparse_attend": 2 * rows * k * d * e + idx + q_bytes + out,
         "dense_decode": 2 * rows * N * d * e + q_bytes + out,
     }
 
@@ -681,18 +716,17 @@ def main():
     torch.cuda.synchronize()
 
     def step(i, ev=None):
+        # exact selection (fused scoring + part top-k, then the merge), then
+        # the gather-attend
         q = qd[i % N_QVAR]
         if ev is not None:
             ev[0].record()
-        T.sa_score(q, kd, T.SA_SCORE_EXACT, scores=scores)
+        T.sa_select(q, kd, c.k, idx_out=idx)
         if ev is not None:
             ev[1].record()
-        T.sa_topk(scores, c.k, idx_out=idx)
-        if ev is not None:
-            ev[2].record()
         T.sa_sparse_decode(q, kd, vd, idx, out=out)
         if ev is not None:
-            ev[3].record()
+            ev[2].record()
 
     log("bench: warmup %d steps" % args.warmup)
     for i in range(args.warmup):
@@ -734,16 +768,29 @@ def main():
     # the launch stream (a separate pass, so the events do not slow the
     # timed steps)
     n_ev = min(args.steps, 100)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
     torch.cuda.synchronize()
     t_ev = time.perf_counter()
     for i in range(n_ev):
         step(i, events[i])
     torch.cuda.synchronize()
     ms_step_eager = (time.perf_counter() - t_ev) * 1e3 / n_ev
-    ms_score = sum(e[0].elapsed_time(e[1]) for e in events) / n_ev
-    ms_topk = sum(e[1].elapsed_time(e[2]) for e in events) / n_ev
-    ms_attend = sum(e[2].elapsed_time(e[3]) for e in events) / n_ev
+    ms_select = sum(e[0].elapsed_time(e[1]) for e in events) / n_ev
+    ms_attend = sum(e[1].elapsed_time(e[2]) for e in events) / n_ev
+
+    # the unfused selection on the same inputs, for comparison: every score
+    # written by sa_score, then sa_topk over them (same index list)
+    n_un = min(n_ev, 20)
+    ev_un = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_un)]
+    for i in range(n_un):
+        ev_un[i][0].record()
+        T.sa_score(qd[i % N_QVAR], kd, T.SA_SCORE_EXACT, scores=scores)
+        ev_un[i][1].record()
+        T.sa_topk(scores, c.k, idx_out=idx)
+        ev_un[i][2].record()
+    torch.cuda.synchronize()
+    ms_score = sum(e[0].elapsed_time(e[1]) for e in ev_un) / n_un
+    ms_topk = sum(e[1].elapsed_time(e[2]) for e in ev_un) / n_un
 
     if args.profile:
         # plain device-to-device copies of known size: the byte counters of
@@ -798,7 +845,7 @@ def main():
         cold = {name: float(np.median(v)) for name, v in times.items()}
 
     nbytes = step_bytes(c)
-    step_total = nbytes["score_exact"] + nbytes["topk"] + nbytes["sparse_attend"]
+    step_total = nbytes["select"] + nbytes["sparse_attend"]
     gbps = step_total / (ms_step * 1e-3) / 1e9
 
     def kern(name, ms):
@@ -808,14 +855,15 @@ def main():
         return {"bytes": nbytes[name], "us": round(ms * 1e3, 3), "gbps": round(g, 1),
                 "frac": round(g / HBM_PEAK_GBPS, 4)}
 
-    kernels = {"score_exact": kern("score_exact", ms_score), "topk": kern("topk", ms_topk),
+    kernels = {"select": kern("select", ms_select),
                "sparse_attend": kern("sparse_attend", ms_attend),
+               "score_exact": kern("score_exact", ms_score), "topk": kern("topk", ms_topk),
                "dense_decode": kern("dense_decode", ms_dense)}
     if cold:
         kernels["sparse_attend_cold"] = kern("sparse_attend", cold["sparse"])
         kernels["contiguous_same_bytes_cold"] = kern("sparse_attend", cold["contig"])
     # dominant kernel of the step: the one with the largest share of its time
-    dom = max(["score_exact", "topk", "sparse_attend"], key=lambda n: kernels[n]["us"])
+    dom = max(["select", "sparse_attend"], key=lambda n: kernels[n]["us"])
     roof = {"bound": "hbm", "achieved": kernels[dom]["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": kernels[dom]["frac"],
             "traffic": read_traffic(dom), "kernel": dom,
@@ -842,6 +890,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "timing": "eager launches" if args.eager else "each step a replayed HIP graph (3 launches)",
+        "step": "sa_select (fused exact scoring + part top-k, merge) -> sa_sparse_decode",
         "ms_per_step_eager_with_events": round(ms_step_eager, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -165,6 +165,26 @@ sa_status sa_topk(const float* scores, int64_t n_rows, int64_t n, int64_t row_st
                   int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
 size_t sa_topk_workspace_size(int64_t n_rows, int64_t n, int32_t k);
 
+/* Exact selection in one pass over the key cache: the index list that
+ * sa_score(kind) followed by sa_topk(k) writes ([P3] section 2, oracle top-k;
+ * [P5] DSA Stage 1, a top-K index list), identical position for position,
+ * without writing the scores.  kind: SA_SCORE_EXACT (idx_out [batch,
+ * n_kv_heads, k]) or SA_SCORE_EXACT_PER_Q_HEAD (idx_out [batch, n_q_heads,
+ * k], batch * n_q_heads <= 65535).
+ * Method: each row is cut into parts of at most 8192 tokens; a workgroup
+ * scores its part into on-chip memory and keeps the part's top-k as (score,
+ * position) candidates; a merge selects the row's top-k among them (every
+ * element of the row's top-k is in its part's top-k).  When the candidates
+ * would not be fewer than half the row it runs sa_score and sa_topk instead
+ * (same result).  ws: sa_select_workspace_size bytes (may be 0), 256-byte
+ * aligned; no state is kept in it between calls.
+ * Errors: SA_ERR_NULL / SA_ERR_ALIGN for q, k_cache (16 bytes), idx_out;
+ * SA_ERR_SHAPE for another kind or k outside [1, ctx_len];
+ * SA_ERR_WORKSPACE when ws_bytes is short. */
+sa_status sa_select(const sa_kv_desc* desc, sa_score_kind kind, const void* q, const void* k_cache,
+                    int32_t k, int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t sa_select_workspace_size(const sa_kv_desc* desc, sa_score_kind kind, int32_t k);
+
 /* ------------------------------------------------------------ attention */
 
 typedef enum {

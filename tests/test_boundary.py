@@ -100,6 +100,55 @@ def test_topk_errors():
     assert L.sa_topk_workspace_size(1, 10, 11) == 0
 
 
+def test_select_errors_and_sizes():
+    """sa_select rejects every bad argument before anything is enqueued
+    (every pointer here is fake: a call that got as far as a launch would
+    return SA_ERR_HIP on this machine)."""
+    L = T.lib()
+    d = _desc()  # 4 rows of 1000 tokens: parts of 256 tokens, 8192 workspace bytes at k = 64
+    E, Q = Bn.SA_SCORE_EXACT, Bn.SA_SCORE_EXACT_PER_Q_HEAD
+    mis = ctypes.c_void_p((1 << 20) + 2)
+    ws_mis = ctypes.c_void_p((1 << 20) + 16)
+
+    def sel(desc=d, kind=E, q=FAKE, k=FAKE, kk=64, idx=FAKE, ws=None, nbytes=0):
+        return L.sa_select(ctypes.byref(desc) if desc is not None else None, kind, q, k, kk, idx,
+                           ws, nbytes, None)
+
+    assert sel(desc=None) == Bn.SA_ERR_NULL
+    for kind in (Bn.SA_SCORE_BLOCK_MINMAX, Bn.SA_SCORE_INDEXER, Bn.SA_SCORE_INDEXER_PER_KV_HEAD, 9):
+        assert sel(kind=kind) == Bn.SA_ERR_SHAPE
+    assert sel(q=None) == Bn.SA_ERR_NULL
+    assert sel(q=mis) == Bn.SA_ERR_ALIGN
+    assert sel(k=None) == Bn.SA_ERR_NULL
+    assert sel(k=mis) == Bn.SA_ERR_ALIGN
+    assert sel(idx=None) == Bn.SA_ERR_NULL
+    assert sel(kk=0) == Bn.SA_ERR_SHAPE
+    assert sel(kk=1001) == Bn.SA_ERR_SHAPE
+    need = L.sa_select_workspace_size(ctypes.byref(d), E, 64)
+    assert need == 8192
+    assert sel() == Bn.SA_ERR_WORKSPACE
+    assert sel(ws=ws_mis, nbytes=need) == Bn.SA_ERR_ALIGN
+    assert sel(ws=FAKE, nbytes=need - 1) == Bn.SA_ERR_WORKSPACE
+    big = _desc(batch=4096, n_q_heads=32, n_kv_heads=8, kv_stride_b=8 * 1000 * 128)
+    assert sel(desc=big, kind=Q) == Bn.SA_ERR_SHAPE  # batch * n_q_heads > 65535
+    # sizes: 0 for an invalid request
+    assert L.sa_select_workspace_size(ctypes.byref(d), Bn.SA_SCORE_BLOCK_MINMAX, 64) == 0
+    assert L.sa_select_workspace_size(ctypes.byref(d), E, 0) == 0
+    assert L.sa_select_workspace_size(ctypes.byref(d), E, 1001) == 0
+    # llama-shaped rows (128 rows of 32768): four 8192-token parts, k = 655:
+    # 2620 candidates per row, a score and a position each
+    ll = _desc(batch=16, n_q_heads=32, n_kv_heads=8, ctx_len=32768, kv_stride_b=8 * 32768 * 128,
+               kv_stride_h=32768 * 128)
+    assert L.sa_select_workspace_size(ctypes.byref(ll), E, 655) == 2 * 128 * 2620 * 4
+    # candidates not fewer than half the row: scores plus a register top-k
+    assert L.sa_select_workspace_size(ctypes.byref(ll), E, 12000) == 128 * 32768 * 4
+    # one part per row (512 rows of 4096): the index list is written directly
+    one = _desc(batch=64, n_q_heads=8, n_kv_heads=8, ctx_len=4096, kv_stride_b=8 * 4096 * 128,
+                kv_stride_h=4096 * 128)
+    assert L.sa_select_workspace_size(ctypes.byref(one), E, 100) == 0
+    assert sel(desc=one, kk=100, idx=None) == Bn.SA_ERR_NULL
+
+
 def test_score_and_summary_errors():
     L = T.lib()
     d = _desc()
@@ -137,8 +186,9 @@ def test_layer_errors_and_sizes():
     assert L.sa_decode_layer(ctypes.byref(a), Bn.SA_LAYER_SPARSE, FAKE, None) == Bn.SA_ERR_WORKSPACE
     s_sparse = L.sa_layer_workspace_size(ctypes.byref(a), Bn.SA_LAYER_SPARSE)
     s_reuse = L.sa_layer_workspace_size(ctypes.byref(a), Bn.SA_LAYER_REUSE)
-    # SPARSE holds the [B, Hkv, N] fp32 scores on top of what REUSE needs
-    assert s_sparse >= s_reuse + 2 * 2 * 1000 * 4
+    # SPARSE holds the exact selection's workspace on top of what REUSE needs
+    s_select = L.sa_select_workspace_size(ctypes.byref(a.desc), Bn.SA_SCORE_EXACT, 64)
+    assert s_select > 0 and s_sparse == s_reuse + s_select
     a.score_kind = Bn.SA_SCORE_BLOCK_MINMAX
     a.aux.block_size = 128
     a.k = 9   # 8 blocks of 128 cover 1000 tokens
@@ -301,3 +351,33 @@ def test_gather_blocks_errors():
         p = ctypes.c_void_p((plain.ctypes.data + 255) // 256 * 256)
         assert call(kh=p, vh=p) == Bn.SA_ERR_MEMORY
         assert "pinned" in T.lib().sa_last_error().decode()
+
+
+def test_bench_select_bytes_follow_the_library_plan():
+    """bench.py prices the fused selection by its candidate count; that count
+    must be the library's: the workspace is a score and a position per
+    candidate slot (rows rounded to 4 slots, 256-byte aligned halves), none
+    for one part, the score array when the candidates fill half the row."""
+    import importlib.util
+    import os
+    spec = importlib.util.spec_from_file_location(
+        "bench_mod", os.path.join(os.path.dirname(__file__), "..", "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    L = T.lib()
+    for B, Hkv, N, k in [(16, 8, 32768, 655), (2, 2, 32768, 655), (1, 8, 65536, 1500),
+                         (32, 8, 17152, 300), (1, 1, 20000, 300), (3, 3, 100, 10),
+                         (2, 2, 32768, 12000), (64, 8, 4096, 100), (16, 8, 131072, 2621),
+                         (16, 8, 32768, 3276), (16, 8, 32768, 6553)]:
+        d = _desc(batch=B, n_q_heads=Hkv, n_kv_heads=Hkv, ctx_len=N, kv_stride_b=Hkv * N * 128,
+                  kv_stride_h=N * 128)
+        rows = B * Hkv
+        C, fused = bench.select_candidates(rows, N, k)
+        got = L.sa_select_workspace_size(ctypes.byref(d), Bn.SA_SCORE_EXACT, k)
+        if not fused:
+            want = -(-rows * N * 4 // 256) * 256 + L.sa_topk_workspace_size(rows, N, k)
+        elif C == min(k, N) and got == 0:
+            want = 0  # one part per row
+        else:
+            want = 2 * (-(-rows * (-(-C // 4) * 4) * 4 // 256) * 256)
+        assert got == want, (B, Hkv, N, k, C, fused, got, want)

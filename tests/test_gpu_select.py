@@ -1,0 +1,109 @@
+"""GPU parity of sa_select, exact selection without the score array.
+
+Every case must give, position for position, the index list of sa_score
+(exact) followed by sa_topk on the same device inputs.  That chain is itself
+pinned to the oracle elsewhere; one ragged case here is also checked against
+the oracle's fp64 scores directly.  The cases cover the fused path (parts of
+8192 tokens, parts shortened for few rows, a ragged last part, an odd and an
+even iteration count, the 256- and 1024-thread merges), the one-part path
+(which writes the index list itself), the fallback when the candidates would
+not be fewer than half the row, both dtypes and head sizes, per-query-head
+rows, and ties, NaN and -0.0 across part boundaries."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import top_sparse_decode_sa_amd as T
+from gpu_util import dev, say, verdicts
+
+pytestmark = pytest.mark.gpu
+
+
+def _cache(B, Hq, Hkv, N, d, dtype, seed):
+    """q and K drawn N(0, 1) on the device (large caches stay off the host)."""
+    g = torch.Generator(device=dev()).manual_seed(seed)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = torch.randn((B, Hq, d), generator=g, device=dev(), dtype=torch.float32).to(tdt)
+    k = torch.randn((B, Hkv, N, d), generator=g, device=dev(), dtype=torch.float32).to(tdt)
+    return q, k
+
+
+def _reference(q, k, kk, kind=T.SA_SCORE_EXACT):
+    return T.sa_topk(T.sa_score(q, k, kind), kk)
+
+
+CASES = [
+    # B, Hq, Hkv, N, d, dtype, k, what
+    (16, 32, 8, 32768, 128, "bf16", 655, "llama-shaped rows: four 8192-token parts"),
+    (2, 8, 2, 32768, 128, "bf16", 655, "few rows: 2048-token parts, 1024-thread merge"),
+    (32, 64, 8, 2 * 8192 + 768, 128, "bf16", 300, "parts of 32, 32 and 3 iterations"),
+    (1, 4, 1, 20000, 128, "bf16", 300, "ragged last part"),
+    (3, 6, 3, 100, 128, "bf16", 10, "one part shorter than one iteration"),
+    (1, 2, 2, 1, 128, "bf16", 1, "one token"),
+    (2, 4, 2, 300, 64, "bf16", 300, "k = N"),
+    (2, 4, 2, 5000, 64, "f32", 37, "f32, head_dim 64"),
+    (2, 8, 4, 9000, 128, "f32", 500, "f32, head_dim 128"),
+    (2, 4, 2, 3000, 64, "bf16", 64, "bf16, head_dim 64"),
+    (1, 8, 8, 65536, 128, "bf16", 1500, "24000 candidates: 1024-thread merge"),
+    (2, 8, 2, 32768, 128, "bf16", 12000, "fallback: candidates not fewer than half the row"),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,dtype,k,what", CASES)
+def test_select_matches_score_then_topk(B, Hq, Hkv, N, d, dtype, k, what):
+    say("select B=%d Hq=%d Hkv=%d N=%d d=%d %s k=%d (%s)" % (B, Hq, Hkv, N, d, dtype, k, what))
+    q, kc = _cache(B, Hq, Hkv, N, d, dtype, seed=N + k)
+    got = T.sa_select(q, kc, k)
+    want = _reference(q, kc, k)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want), what
+    del q, kc
+    torch.cuda.empty_cache()
+
+
+def test_select_per_query_head():
+    say("select per query head")
+    q, kc = _cache(2, 8, 2, 20000, 128, "bf16", seed=3)
+    got = T.sa_select(q, kc, 300, kind=T.SA_SCORE_EXACT_PER_Q_HEAD)
+    assert tuple(got.shape) == (2, 8, 300)
+    assert torch.equal(got, _reference(q, kc, 300, T.SA_SCORE_EXACT_PER_Q_HEAD))
+
+
+def test_select_against_oracle():
+    """Ragged parts, checked against fp64 scores: the selected set is the
+    exact top-k up to fp32 near-ties, in ascending order."""
+    say("select vs oracle")
+    B, Hq, Hkv, N, d, k = 1, 8, 2, 20000, 128, 300
+    q, kc = _cache(B, Hq, Hkv, N, d, "bf16", seed=11)
+    got = T.sa_select(q, kc, k).cpu().numpy()
+    qf = q.cpu().to(torch.float64).numpy()
+    kf = kc.cpu().to(torch.float64).numpy()
+    G = Hq // Hkv
+    s64 = [O.scores_exact(qf[0, r * G:(r + 1) * G], kf[0, r], O.default_scale(d)) for r in range(Hkv)]
+    counts, fails = verdicts(s64, [got[0, r] for r in range(Hkv)], k)
+    assert counts["failed"] == 0, fails
+
+
+@pytest.mark.parametrize("pattern", ["zero query", "integer scores", "nan and signed zero"])
+def test_select_ties_and_specials(pattern):
+    """Equal scores across part boundaries go to the lower position; NaN
+    ranks below every number; -0.0 equals +0.0."""
+    say("select specials: %s" % pattern)
+    B, Hq, Hkv, N, d, k = 2, 8, 2, 20000, 128, 300
+    q, kc = _cache(B, Hq, Hkv, N, d, "bf16", seed=5)
+    if pattern == "zero query":
+        q.zero_()
+    elif pattern == "integer scores":
+        q = torch.round(q.float()).to(q.dtype)
+        kc = torch.round(kc.float().clamp(-1, 1)).to(kc.dtype)
+    else:
+        kc[:, :, 17::97, :] = float("nan")
+        q[:, :, 0] = 0.0
+        kc[:, :, 5::13, :] = 0.0
+        kc[:, :, 6::13, :] = -0.0
+    got = T.sa_select(q, kc, k)
+    want = _reference(q, kc, k)
+    assert torch.equal(got, want), pattern
+    if pattern == "zero query":
+        assert torch.equal(got.cpu(), torch.arange(k, dtype=torch.int32).expand(B, Hkv, k))

@@ -31,7 +31,8 @@ SA_IDX_TOKEN_PER_Q_HEAD = 3
 SA_LAYER_DENSE, SA_LAYER_SPARSE, SA_LAYER_REUSE, SA_LAYER_DENSE_SELECT = 0, 1, 2, 3
 
 EXPORTED = [
-    "sa_score", "sa_block_summarize", "sa_topk", "sa_topk_workspace_size", "sa_sparse_decode",
+    "sa_score", "sa_block_summarize", "sa_topk", "sa_topk_workspace_size", "sa_select",
+    "sa_select_workspace_size", "sa_sparse_decode",
     "sa_sparse_workspace_size", "sa_dense_decode", "sa_dense_workspace_size",
     "sa_dense_decode_scored", "sa_dense_scored_workspace_size", "sa_decode_layer",
     "sa_layer_workspace_size", "sa_plan_validate", "sa_index_overlap", "sa_plan_reuse",
@@ -82,6 +83,9 @@ def lib() -> ctypes.CDLL:
     L.sa_topk.argtypes = [vp, i64, i64, i64, i32, vp, vp, sz, vp]
     L.sa_topk_workspace_size.argtypes = [i64, i64, i32]
     L.sa_topk_workspace_size.restype = sz
+    L.sa_select.argtypes = [P(KVDesc), st, vp, vp, i32, vp, vp, sz, vp]
+    L.sa_select_workspace_size.argtypes = [P(KVDesc), st, i32]
+    L.sa_select_workspace_size.restype = sz
     L.sa_sparse_decode.argtypes = [P(KVDesc), vp, vp, vp, st, vp, i32, i32, vp, vp, sz, vp]
     L.sa_sparse_workspace_size.argtypes = [P(KVDesc), st, i32, i32]
     L.sa_sparse_workspace_size.restype = sz
@@ -105,7 +109,8 @@ def lib() -> ctypes.CDLL:
     L.sa_last_error.argtypes = []
     L.sa_last_error.restype = ctypes.c_char_p
     L.sa_version.restype = ctypes.c_char_p
-    for name in ["sa_score", "sa_block_summarize", "sa_topk", "sa_sparse_decode", "sa_dense_decode",
+    for name in ["sa_score", "sa_block_summarize", "sa_topk", "sa_select", "sa_sparse_decode",
+                 "sa_dense_decode",
                  "sa_dense_decode_scored", "sa_decode_layer", "sa_plan_validate",
                  "sa_index_overlap", "sa_plan_reuse", "sa_plan_fixed_jump", "sa_gather_blocks",
                  "sa_workspace_init"]:
@@ -255,6 +260,22 @@ def sa_block_summarize(k_cache, block_size, q_like=None):
     check(lib().sa_block_summarize(ctypes.byref(desc), block_size, _ptr(k_cache), _ptr(kmin),
                                    _ptr(kmax), ctypes.c_void_p(_stream(dev))))
     return kmin, kmax
+
+
+def sa_select(q, k_cache, k, kind=SA_SCORE_EXACT, idx_out=None, softmax_scale=0.0):
+    """sa_select: the exact top-k positions without the score array; int32
+    [B, Hkv, k] (EXACT) or [B, Hq, k] (EXACT_PER_Q_HEAD)."""
+    dev = _dev(q, k_cache)
+    desc = make_desc(q, k_cache, softmax_scale)
+    rows = desc.n_q_heads if kind == SA_SCORE_EXACT_PER_Q_HEAD else desc.n_kv_heads
+    if idx_out is None:
+        idx_out = torch.empty((desc.batch, rows, k), dtype=torch.int32, device=dev)
+    L = lib()
+    nbytes = L.sa_select_workspace_size(ctypes.byref(desc), kind, k)
+    ws = WORKSPACES.get(dev, ("select", kind, k) + _desc_key(desc), nbytes)
+    check(L.sa_select(ctypes.byref(desc), kind, _ptr(q), _ptr(k_cache), k, _ptr(idx_out), _ptr(ws),
+                      nbytes, ctypes.c_void_p(_stream(dev))))
+    return idx_out
 
 
 def sa_topk(scores, k, idx_out=None):

@@ -156,6 +156,36 @@ __device__ __forceinline__ float group_max(float x) {
   return x;
 }
 
+// Exact token score pieces shared by every kernel that scores tokens one by
+// one (so their fp32 results agree bit for bit):
+//  * group_query_sum: lane's E values of (sum over the G <= 8 query heads of
+//    the group) * scale, all G loads issued before any add;
+//  * row_dot: one 16-byte piece of a cache row dotted with those values (fma
+//    chain from 0 in element order), summed over the row's LPR lanes.
+template <int E, int D>
+__device__ __forceinline__ void group_query_sum(const void* q, sa_dtype dt, int64_t g0, int G,
+                                                int off, float scale, float (&qs)[E]) {
+  float qv[8][E];
+  load_q_group<E, D>(q, dt, g0, G, off, qv);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) acc += g < G ? qv[g][e] : 0.0f;
+    qs[e] = acc * scale;
+  }
+}
+
+template <typename KT, int LPR, int E>
+__device__ __forceinline__ float row_dot(const uint4& w, const float (&qs)[E]) {
+  float kf[E];
+  unpack16<KT>(w, kf);
+  float acc = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc = fmaf(qs[e], kf[e], acc);
+  return group_sum<LPR>(acc);
+}
+
 // DPP move of a uint32 across lanes; lanes whose source lies outside the row
 // read 0 (bound_ctrl), lanes of rows outside ROW_MASK get 0.
 template <int CTRL, int ROW_MASK = 0xf>

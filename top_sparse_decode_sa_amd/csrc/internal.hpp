@@ -46,9 +46,33 @@ hipError_t launch_score_indexer(int32_t B, int64_t N, int32_t H, int32_t Di, con
 size_t topk_workspace_bytes(int64_t n_rows, int64_t n, int32_t k);
 hipError_t launch_topk(const float* scores, int64_t n_rows, int64_t n, int64_t row_stride, int32_t k,
                        int32_t* idx, void* ws, hipStream_t s);
+// Top-k of candidate rows (n <= 32768 values each, row stride cstride) whose
+// element i stands for position pos[i]: idx gets the k selected positions in
+// ascending candidate order.
+hipError_t launch_topk_merge(const float* cand_val, const int32_t* cand_pos, int64_t n_rows,
+                             int64_t n, int64_t cstride, int32_t k, int32_t* idx, hipStream_t s);
 // counts[r] = |idx_a[r, :] intersect idx_b[r, :]|, rows of k ascending indices.
 hipError_t launch_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t n_rows, int32_t k,
                                 int32_t* counts, hipStream_t s);
+
+// ------------------------------------------------------- fused select
+// Exact top-k of every row of c (B * Hkv rows; per_q_head_view for one row
+// per query head) without writing the scores: rows are cut into parts of L
+// tokens scored and pre-selected in LDS, then merged.  Falls back to exact
+// scoring plus top-k when the part candidates would not be fewer than half
+// the row.
+struct SelectPlan {
+  int32_t L = 0;        // tokens per part (a multiple of 256, at most 8192)
+  int32_t P = 0;        // parts per row
+  int32_t kcap = 0;     // candidate slots per part: min(k, L)
+  int64_t C = 0;        // candidates per row
+  int64_t cstride = 0;  // candidate row stride (C rounded up to 4)
+  bool fused = false;
+  size_t ws_bytes = 0;  // workspace of the chosen path
+};
+SelectPlan plan_select(const Cache& c, int32_t k);
+hipError_t launch_select(const Cache& c, const SelectPlan& p, const void* q, const void* k,
+                         int32_t kk, int32_t* idx, void* ws, hipStream_t s);
 
 // ----------------------------------------------------------- attention
 // kIdxDenseScored: dense decode that also writes each token's exact score

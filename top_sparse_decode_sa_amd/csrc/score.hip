@@ -61,19 +61,10 @@ __global__ __launch_bounds__(kThreads) void score_exact_kernel(ExactArgs a) {
   const int b = row / a.Hkv;
   const int r = row % a.Hkv;
 
-  // sum of the group's queries (G <= 8): all loads issued before any add
+  // sum of the group's queries (G <= 8)
   float qs[E];
-  {
-    float qv[8][E];
-    load_q_group<E, D>(a.q, a.q_dtype, (int64_t)b * a.Hq + (int64_t)r * a.G, a.G, sl * E, qv);
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int g = 0; g < 8; ++g) acc += g < a.G ? qv[g][e] : 0.0f;
-      qs[e] = acc * a.scale;
-    }
-  }
+  group_query_sum<E, D>(a.q, a.q_dtype, (int64_t)b * a.Hq + (int64_t)r * a.G, a.G, sl * E, a.scale,
+                        qs);
 
   const uint8_t* kbase = a.k + ((int64_t)b * a.sb + (int64_t)(r / a.kv_div) * a.sh) * EB + sl * 16;
   const int64_t row_bytes = a.st * EB;
@@ -99,12 +90,7 @@ __global__ __launch_bounds__(kThreads) void score_exact_kernel(ExactArgs a) {
     float mine = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float kf[E];
-      unpack16<KT>(kw[u], kf);
-      float acc = 0.0f;
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc = fmaf(qs[e], kf[e], acc);
-      acc = group_sum<LPR>(acc);
+      const float acc = row_dot<KT, LPR, E>(kw[u], qs);
       if (sl == u) mine = acc;
     }
     const int64_t t = base + wave * per_wave_iter + sl * RPW + lg;

@@ -1,0 +1,284 @@
+// Exact top-k selection without the score array.
+//
+// What is computed: the same index list as exact scoring followed by top-k
+// ("Inference-time context sparsity: illusion or opportunity?", section 2:
+// oracle top-k over the exact scores q . k_t, the group's query heads summed;
+// "Flash Attention vs Sparse Attention", DSA Stage 1: the top-K index list)
+// -- the k positions with the largest scores, equal scores taken from the
+// lower position, in ascending position order.
+//
+// Why fused: streaming the key cache is the whole cost of exact selection,
+// and writing the fp32 score of every token back to HBM in the middle of that
+// stream costs far more than its bytes (the writes interleave with the reads).
+// Here the scores never leave the chip:
+//
+//  1. select_part_kernel: a row is cut into parts of L <= 8192 tokens; one
+//     256-thread workgroup streams its part's keys (the score kernel's
+//     arithmetic, bit for bit: group_query_sum, row_dot), keeps the part's
+//     scores in LDS, then runs the register-resident radix select
+//     (reg_row_topk) on them and writes the part's top-min(k, part length)
+//     as (score, position) candidates, in position order.
+//  2. Merge: the row's candidates, concatenated in part order (so in
+//     position order), go through the same top-k with the candidate index
+//     mapped back to its position.  Every element of the row's top-k is in
+//     its part's top-k (fewer than k elements of its part precede it), so the
+//     merge returns exactly the row's top-k.
+//  A row of one part writes its index list from step 1 directly.
+#include <algorithm>
+
+#include "common.hpp"
+#include "internal.hpp"
+#include "topk_core.hpp"
+
+#ifndef SEL_HIST
+#define SEL_HIST 1
+#endif
+
+
+namespace sa {
+namespace {
+
+constexpr int kSelThreads = 256;
+constexpr int kSelGroups = 8;               // register select: 4 * 8 keys per thread
+constexpr int kPartMax = 4 * kSelGroups * kSelThreads;  // 8192: the register select's capacity
+constexpr int kPartAlign = 256;             // a multiple of every layout's tokens per iteration
+constexpr int kSelCand = kRankMax + 8;      // threshold-bin candidates ranked in LDS
+constexpr int kMinGroups = 512;             // parts shrink (to 256 tokens) until the grid has this many
+constexpr int64_t kMergeMax = 32768;        // candidates per row the merge holds in registers
+
+struct SelArgs {
+  const void* q;
+  sa_dtype q_dtype;
+  const uint8_t* k;
+  int64_t sb, sh, st;
+  int32_t Hq, Hkv, G;
+  int32_t kv_div;  // row r reads KV head r / kv_div
+  int64_t N;
+  float scale;
+  int32_t L;        // tokens per part
+  int32_t k_sel;    // k
+  int32_t kcap;     // candidate slots per part
+  int64_t cstride;  // candidate row stride
+  float* cand_val;  // [rows, cstride]: candidate scores
+  int32_t* cand_pos;
+  int32_t* idx;  // one part per row: the final list [rows, k], else null
+};
+
+template <typename KT, int D, int U>
+__global__ __launch_bounds__(kSelThreads) void select_part_kernel(SelArgs a) {
+  constexpr int EB = Elt<KT>::kBytes;
+  constexpr int E = Elt<KT>::kPer16B;
+  constexpr int LPR = D * EB / 16;
+  constexpr int RPW = 64 / LPR;  // rows per wave load
+  constexpr int per_wave_iter = RPW * U;
+  constexpr int per_iter = 4 * per_wave_iter;
+  static_assert(U <= LPR, "one storing lane per unrolled token");
+  static_assert(kSelThreads == 256 && kPartAlign % per_iter == 0, "whole iterations per part");
+
+  __shared__ __align__(16) float s_sc[kPartMax];
+  __shared__ SharedT<kSelThreads> sh;
+  __shared__ __align__(16) uint2 cand[kSelCand];
+  __shared__ uint32_t s_wave[kSelThreads / 64];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lg = (tid & 63) / LPR;
+  const int sl = tid % LPR;
+  const int part = blockIdx.x;
+  const int row = blockIdx.y;
+  const int b = row / a.Hkv;
+  const int r = row % a.Hkv;
+  const int64_t t0 = (int64_t)part * a.L;
+  const int n = (int)std::min<int64_t>(a.L, a.N - t0);  // tokens of this part
+
+  float qs[E];
+  group_query_sum<E, D>(a.q, a.q_dtype, (int64_t)b * a.Hq + (int64_t)r * a.G, a.G, sl * E, a.scale,
+                        qs);
+  const uint8_t* kbase =
+      a.k + ((int64_t)b * a.sb + (int64_t)(r / a.kv_div) * a.sh + t0 * a.st) * EB + sl * 16;
+#if SEL_HIST
+  // the selection's 12-bit histogram is counted as the scores are produced
+  zero_hist(sh, kBins);
+  __syncthreads();
+#endif
+  const int64_t row_bytes = a.st * EB;
+
+  // ---- 1. scores of the part into LDS.  Each wave covers per_wave_iter
+  // consecutive tokens per iteration; the next iteration's keys are
+  // requested before this one's are reduced.
+  const uint8_t* kwave = kbase + (int64_t)(wave * per_wave_iter + lg) * row_bytes;
+  auto load = [&](int base, uint4 (&kw)[U], bool clamp) {
+    if (clamp) {
+      const int wbase = base + wave * per_wave_iter + lg;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        kw[u] = ld16_nt(kbase + (int64_t)std::min(wbase + u * RPW, n - 1) * row_bytes);
+    } else {
+      const uint8_t* p = kwave + (int64_t)base * row_bytes;
+#pragma unroll
+      for (int u = 0; u < U; ++u) kw[u] = ld16_nt(p + (int64_t)(u * RPW) * row_bytes);
+    }
+  };
+  auto reduce = [&](int base, const uint4 (&kw)[U], bool check) {
+    float mine = 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float acc = row_dot<KT, LPR, E>(kw[u], qs);
+      if (sl == u) mine = acc;
+    }
+    const int t = base + wave * per_wave_iter + sl * RPW + lg;
+    if (sl < U && (!check || t < n)) {
+      s_sc[t] = mine;
+#if SEL_HIST
+      atomicAdd(&sh.hist[score_key(mine) >> 20], 1u);
+#endif
+    }
+  };
+  const int nf = n / per_iter;  // whole iterations
+  int i0 = 0;
+  if (nf & 1) {
+    // an odd count: one iteration on its own, so the pipelined run is even
+    uint4 kw[U];
+    load(0, kw, false);
+    reduce(0, kw, false);
+    i0 = 1;
+  }
+  if (i0 < nf) {
+    uint4 ka[U], kb[U];
+    load(i0 * per_iter, ka, false);
+    int i = i0;
+    for (; i + 2 < nf; i += 2) {
+      load((i + 1) * per_iter, kb, false);
+      __builtin_amdgcn_sched_barrier(0);
+      reduce(i * per_iter, ka, false);
+      load((i + 2) * per_iter, ka, false);
+      __builtin_amdgcn_sched_barrier(0);
+      reduce((i + 1) * per_iter, kb, false);
+    }
+    load((i + 1) * per_iter, kb, false);
+    __builtin_amdgcn_sched_barrier(0);
+    reduce(i * per_iter, ka, false);
+    reduce((i + 1) * per_iter, kb, false);
+  }
+  if (nf * per_iter < n) {
+    // the part's ragged end: loads clamped to its last token
+    uint4 kw[U];
+    load(nf * per_iter, kw, true);
+    reduce(nf * per_iter, kw, true);
+  }
+  __syncthreads();
+
+  // ---- 2. top-min(k, n) of the part, from LDS into registers
+  auto lds_load = [&](int p0, float (&v)[kSelGroups][4]) {
+#pragma unroll
+    for (int j = 0; j < kSelGroups; ++j) {
+      const float4 f = *reinterpret_cast<const float4*>(&s_sc[p0 + 256 * j]);
+      v[j][0] = f.x;
+      v[j][1] = f.y;
+      v[j][2] = f.z;
+      v[j][3] = f.w;
+    }
+  };
+  const int32_t kk = std::min(a.k_sel, n);
+  if (a.idx) {
+    int32_t* out = a.idx + (int64_t)row * a.k_sel;
+    reg_row_topk<kSelThreads, kSelGroups, SEL_HIST>(
+        lds_load, n, kk, [&](uint32_t slot, int32_t p) { out[slot] = p; }, sh, cand, s_wave);
+  } else {
+    const int64_t c0 = (int64_t)row * a.cstride + (int64_t)part * a.kcap;
+    float* cv = a.cand_val + c0;
+    int32_t* cp = a.cand_pos + c0;
+    reg_row_topk<kSelThreads, kSelGroups, SEL_HIST>(
+        lds_load, n, kk,
+        [&](uint32_t slot, int32_t p) {
+          cv[slot] = s_sc[p];
+          cp[slot] = (int32_t)t0 + p;
+        },
+        sh, cand, s_wave);
+  }
+}
+
+}  // namespace
+
+SelectPlan plan_select(const Cache& c, int32_t k) {
+  SelectPlan p;
+  const int64_t rows = (int64_t)c.B * c.Hkv;
+  // candidates per row for parts of L tokens
+  auto cands = [&](int64_t L) {
+    const int64_t P = (c.N + L - 1) / L;
+    return (P - 1) * std::min<int64_t>(k, L) + std::min<int64_t>(k, c.N - (P - 1) * L);
+  };
+  // the longest parts, shortened while the grid is small and the candidates
+  // stay under half the row
+  int64_t L = kPartMax;
+  while (L > kPartAlign && rows * ((c.N + L - 1) / L) < kMinGroups && 2 * cands(L / 2) <= c.N)
+    L /= 2;
+  p.L = (int32_t)L;
+  p.P = (int32_t)((c.N + L - 1) / L);
+  p.kcap = (int32_t)std::min<int64_t>(k, L);
+  p.C = cands(L);
+  p.cstride = (p.C + 3) / 4 * 4;
+  // fused when the candidates are fewer than half the row (8 bytes each
+  // against 4 per score) and fit the merge; one part needs no merge
+  p.fused = p.P == 1 || (p.C <= kMergeMax && 2 * p.C <= c.N);
+  if (!p.fused) {
+    p.ws_bytes = align_up((size_t)rows * c.N * sizeof(float), 256) +
+                 align_up(topk_workspace_bytes(rows, c.N, k), 256);
+  } else if (p.P > 1) {
+    p.ws_bytes = 2 * align_up((size_t)rows * p.cstride * sizeof(float), 256);
+  }
+  return p;
+}
+
+hipError_t launch_select(const Cache& c, const SelectPlan& p, const void* q, const void* k,
+                         int32_t kk, int32_t* idx, void* ws, hipStream_t s) {
+  const int64_t rows = (int64_t)c.B * c.Hkv;
+  if (!p.fused) {
+    float* scores = static_cast<float*>(ws);
+    void* topk_ws = static_cast<uint8_t*>(ws) + align_up((size_t)rows * c.N * sizeof(float), 256);
+    hipError_t e = launch_score_exact(c, q, k, scores, s);
+    if (e != hipSuccess) return e;
+    return launch_topk(scores, rows, c.N, c.N, kk, idx, topk_ws, s);
+  }
+  SelArgs a{};
+  a.q = q;
+  a.q_dtype = c.q_dtype;
+  a.k = static_cast<const uint8_t*>(k);
+  a.sb = c.sb;
+  a.sh = c.sh;
+  a.st = c.st;
+  a.Hq = c.Hq;
+  a.Hkv = c.Hkv;
+  a.G = c.G;
+  a.kv_div = c.kv_div;
+  a.N = c.N;
+  a.scale = c.scale;
+  a.L = p.L;
+  a.k_sel = kk;
+  a.kcap = p.kcap;
+  a.cstride = p.cstride;
+  if (p.P == 1) {
+    a.idx = idx;
+  } else {
+    a.cand_val = static_cast<float*>(ws);
+    a.cand_pos = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) +
+                                            align_up((size_t)rows * p.cstride * sizeof(float), 256));
+  }
+  const dim3 grid((unsigned)p.P, (unsigned)rows);
+  if (c.kv_dtype == SA_BF16) {
+    if (c.D == 64)
+      hipLaunchKernelGGL((select_part_kernel<bf16_t, 64, 8>), grid, dim3(kSelThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((select_part_kernel<bf16_t, 128, 16>), grid, dim3(kSelThreads), 0, s, a);
+  } else {
+    if (c.D == 64)
+      hipLaunchKernelGGL((select_part_kernel<float, 64, 16>), grid, dim3(kSelThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((select_part_kernel<float, 128, 16>), grid, dim3(kSelThreads), 0, s, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.P == 1) return e;
+  return launch_topk_merge(a.cand_val, a.cand_pos, rows, p.C, p.cstride, kk, idx, s);
+}
+
+}  // namespace sa

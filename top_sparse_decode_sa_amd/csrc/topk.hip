@@ -40,6 +40,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "topk_core.hpp"
 
 namespace sa {
 namespace {
@@ -48,81 +49,15 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kResident = 32768;  // keys kept in LDS (128 KB)
 constexpr int kTile = 16384;      // keys per LDS tile of the ordered write, other rows
-constexpr int kBins = 4096;       // first digit: 12 bits
 constexpr int kCandRes = 1024;    // candidate (key, position) pairs, resident rows
 constexpr int kCandGlob = 8192;   // candidate pairs, other rows
-constexpr int kRankCap = 256;     // candidates resolved by pairwise ranking
 
 constexpr int kMwChunk = 8192;       // keys per workgroup, multi-workgroup path
 constexpr int kMwCand = 8192;        // candidate capacity per row
 constexpr int kMwMaxRows = 64;       // rows at most, multi-workgroup path
 constexpr int kMwMaxChunks = 1024;   // chunks per row at most (n <= 8M)
 
-struct Shared {
-  uint32_t hist[kBins];
-  uint32_t tot[kWaves];
-  uint32_t digit, above, count, T, cgt, base;
-};
-
-// Workgroup-wide exclusive prefix sum; also returns the total.  Uses s_tot
-// (kWaves entries) as scratch; contains two barriers.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_tot,
-                                                         uint32_t& total) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const uint32_t incl = wave_inclusive_scan(v);
-  if (lane == 63) s_tot[wave] = incl;
-  __syncthreads();
-  uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const uint32_t t = s_tot[w];
-    before += (w < wave) ? t : 0u;
-    all += t;
-  }
-  __syncthreads();
-  total = all;
-  return before + incl - v;
-}
-
-__device__ __forceinline__ void zero_hist(Shared& sh, int bins) {
-  for (int i = threadIdx.x; i < bins; i += kThreads) sh.hist[i] = 0u;
-}
-
-// Pick the digit (of `width` bits at `shift`) of the kleft-th largest key among
-// those counted in sh.hist; updates prefix/mask/kleft and returns the count of
-// keys with that digit.  Called by every thread; contains barriers.
-__device__ __forceinline__ uint32_t select_digit(Shared& sh, int shift, int width, uint32_t& prefix,
-                                                 uint32_t& mask, uint32_t& kleft) {
-  const int tid = threadIdx.x;
-  const int bins = 1 << width;
-  const int per = (bins + kThreads - 1) / kThreads;  // bins per thread, descending
-  uint32_t c[4] = {0u, 0u, 0u, 0u};
-  uint32_t csum = 0;
-  for (int j = 0; j < per; ++j) {
-    const int d = bins - 1 - (tid * per + j);
-    c[j] = d >= 0 ? sh.hist[d] : 0u;
-    csum += c[j];
-  }
-  uint32_t total;
-  uint32_t excl = block_exclusive_scan(csum, sh.tot, total);
-  for (int j = 0; j < per; ++j) {
-    const int d = bins - 1 - (tid * per + j);
-    if (d >= 0 && excl < kleft && kleft <= excl + c[j]) {
-      sh.digit = (uint32_t)d;
-      sh.above = excl;
-      sh.count = c[j];
-    }
-    excl += c[j];
-  }
-  __syncthreads();
-  prefix |= sh.digit << shift;
-  mask |= (uint32_t)(bins - 1) << shift;
-  kleft -= sh.above;
-  const uint32_t cnt = sh.count;
-  __syncthreads();
-  return cnt;
-}
+using Shared = SharedT<kThreads>;
 
 // LDS key layout for a tile in which thread t owns the E keys at positions
 // [E*t, E*t + E): groups of four keys stay together and group g of thread t
@@ -212,65 +147,6 @@ __device__ __forceinline__ void hist_global(const float* __restrict__ s, int64_t
   for (int64_t i = done + tid; i < n; i += kThreads) atomicAdd(&sh.hist[score_key(s[i]) >> 20], 1u);
 }
 
-// Resolve the candidates cand[0, c1) (key, position) of the bin fixed by
-// (prefix, mask), of which kleft1 belong to the result: T, the key of the
-// last kept candidate in selection order, and `need`, the kept candidates
-// equal to T.  cand must have room for c1 rounded up to 32.
-__device__ void resolve(uint2* cand, uint32_t c1, uint32_t kleft1, uint32_t prefix, uint32_t mask,
-                        Shared& sh, uint32_t& T, uint32_t& need) {
-  const int tid = threadIdx.x;
-  if (c1 <= (uint32_t)kRankCap) {
-    // rank = candidates with a larger key or an equal key at a lower
-    // position; four threads per candidate, each over a quarter of the list
-    const uint32_t c1p = (c1 + 31u) & ~31u;
-    for (uint32_t c = c1 + tid; c < c1p; c += kThreads) cand[c] = make_uint2(0u, 0xffffffffu);
-    __syncthreads();
-    const uint32_t ci = tid >> 2, part = tid & 3;
-    const uint2 me = cand[ci < c1 ? ci : 0];
-    uint32_t rank = 0;
-    if (ci < c1) {
-      const uint32_t q = c1p / 4;
-      for (uint32_t j0 = part * q; j0 < (part + 1) * q; j0 += 8) {
-        uint2 o[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) o[u] = cand[j0 + u];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          rank += (o[u].x > me.x || (o[u].x == me.x && o[u].y < me.y)) ? 1u : 0u;
-      }
-    }
-    rank += __shfl_xor(rank, 1, 64);
-    rank += __shfl_xor(rank, 2, 64);
-    if (ci < c1 && part == 0 && rank == kleft1 - 1) sh.T = me.x;
-    __syncthreads();
-    T = sh.T;
-  } else {
-    constexpr int kShift[3] = {12, 4, 0};
-    constexpr int kWidth[3] = {8, 8, 4};
-    uint32_t kleft = kleft1;
-#pragma unroll
-    for (int d = 0; d < 3; ++d) {
-      zero_hist(sh, 1 << kWidth[d]);
-      __syncthreads();
-      for (uint32_t c = tid; c < c1; c += kThreads) {
-        const uint32_t key = cand[c].x;
-        if ((key & mask) == prefix)
-          atomicAdd(&sh.hist[(key >> kShift[d]) & ((1u << kWidth[d]) - 1u)], 1u);
-      }
-      __syncthreads();
-      select_digit(sh, kShift[d], kWidth[d], prefix, mask, kleft);
-    }
-    T = prefix;
-  }
-  if (tid == 0) sh.cgt = 0;
-  __syncthreads();
-  uint32_t g = 0;
-  for (uint32_t c = tid; c < c1; c += kThreads) g += cand[c].x > T ? 1u : 0u;
-  if (g) atomicAdd(&sh.cgt, g);
-  __syncthreads();
-  need = kleft1 - sh.cgt;  // kept candidates: those above T and `need` equal to T
-}
-
 // Digit passes over a whole row when the candidates overflow: T and need.
 template <typename KeyAt>
 __device__ void resolve_row(KeyAt key_at, int64_t n, uint32_t kleft, uint32_t prefix, uint32_t mask,
@@ -328,7 +204,7 @@ __device__ __forceinline__ void write_tile(const uint32_t* keys, int64_t tile0, 
     me |= (eq ? 1u : 0u) << j;
   }
   uint32_t total;
-  const uint32_t excl = block_exclusive_scan((cg << 16) | ce, sh.tot, total);
+  const uint32_t excl = block_exclusive_scan((cg << 16) | ce, sh, total);
   uint32_t gb = run_gt + (excl >> 16);
   uint32_t eb = run_eq + (excl & 0xffffu);
   uint32_t m = mg | me;
@@ -397,7 +273,7 @@ __device__ void long_row_short_list(const float* __restrict__ s, int64_t n, int3
     }
     if (c0 + CHUNK < n) fetch(c0 + CHUNK);  // in flight during the scan and the stores
     uint32_t total;
-    const uint32_t excl = block_exclusive_scan((n_ge << 16) | n_c, sh.tot, total);
+    const uint32_t excl = block_exclusive_scan((n_ge << 16) | n_c, sh, total);
     uint32_t at_l = list_base + (excl >> 16), at_c = cand_base + (excl & 0xffffu);
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
@@ -427,7 +303,7 @@ __device__ void long_row_short_list(const float* __restrict__ s, int64_t n, int3
     ce += list[i].x == T ? 1u : 0u;
   }
   uint32_t total;
-  const uint32_t excl = block_exclusive_scan((cg << 16) | ce, sh.tot, total);
+  const uint32_t excl = block_exclusive_scan((cg << 16) | ce, sh, total);
   uint32_t gb = excl >> 16, eb = excl & 0xffffu;
   for (uint32_t i = e0; i < e1; ++i) {
     const uint2 e = list[i];
@@ -587,185 +463,60 @@ __device__ void topk_row_long(const float* __restrict__ s, int64_t n, int32_t k,
 }
 
 // ------------------------------------------------- register-resident rows
-// Rows of at most kResident keys: every key stays in the registers of the
-// thread that loaded it, so no phase after the load touches the row in
-// memory.  Wave w holds positions [2048 w, 2048 w + 2048); in group j
-// (0..7) lane l holds the four positions 2048 w + 256 j + 4 l + e (one
-// coalesced 16-byte load), so positions run in (j, lane, e) order inside a
-// wave.  Phases: histogram of the top 12 bits; digit select; the candidates
-// of the threshold bin placed in LDS (one atomic per wave) and resolved; the
-// ordered write, where a key's slot is (kept keys of earlier waves) + (of
-// earlier groups of its wave) + (of lower lanes in its group, a DPP prefix
-// sum) + (of lower e in its lane).  Candidate overflow runs the 8/8/4-bit
-// digit passes over the registers.
-constexpr int kRegGroups = kResident / kThreads / 4;  // 8 float4 groups per thread
-
-__global__ __launch_bounds__(kThreads) void topk_reg_kernel(const float* __restrict__ scores,
-                                                            int64_t n64, int64_t row_stride,
-                                                            int32_t k, int32_t* __restrict__ idx_out,
-                                                            bool vec4) {
-  __shared__ Shared sh;
-  __shared__ __align__(16) uint2 cand[kCandRes];
-  __shared__ uint32_t s_wave[kWaves];
-  const int n = (int)n64;  // <= kResident
+// Rows of at most 4 * G * NT keys: the register-resident row path of
+// reg_row_topk, one workgroup per row.  With MAP the row is a candidate list
+// and position p is reported as pos_map[p] (the merge of the fused
+// score-and-select path); the map is staged in LDS next to the keys, so the
+// ordered write does not wait on a global load per kept element.
+template <int NT, int G, bool MAP>
+__global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ scores, int64_t n64,
+                                                      int64_t row_stride, int32_t k,
+                                                      int32_t* __restrict__ idx_out, bool vec4,
+                                                      const int32_t* __restrict__ pos_map) {
+  __shared__ SharedT<NT> sh;
+  __shared__ __align__(16) uint2 cand[kRankMax + 8];
+  __shared__ uint32_t s_wave[NT / 64];
+  __shared__ __align__(16) int32_t s_map[MAP ? 4 * G * NT : 4];
+  const int n = (int)n64;  // <= 4 * G * NT
   const float* __restrict__ s = scores + (int64_t)blockIdx.x * row_stride;
   int32_t* __restrict__ out = idx_out + (int64_t)blockIdx.x * k;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int p0 = wave * (kRegGroups * 256) + 4 * lane;  // position of (j = 0, e = 0)
-  auto pos = [&](int j, int e) { return p0 + 256 * j + e; };
-
-  // ---- 1. load (every load issued first) and the 12-bit histogram, each
-  // group counted as soon as its load arrives
-  zero_hist(sh, kBins);
-  __syncthreads();
-  uint32_t key[kRegGroups][4];
-  {
-    float v[kRegGroups][4];
+  const int32_t* __restrict__ map = MAP ? pos_map + (int64_t)blockIdx.x * row_stride : nullptr;
+  auto load = [&](int p0, float (&v)[G][4]) {
     if (vec4 && n % 4 == 0) {
       // a group lies wholly inside or wholly outside the row
       const float4* s4 = reinterpret_cast<const float4*>(s + p0);
+      int4 m[G];
 #pragma unroll
-      for (int j = 0; j < kRegGroups; ++j) {
-        const float4 f = pos(j, 0) < n ? s4[64 * j] : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int j = 0; j < G; ++j) {
+        const bool in = p0 + 256 * j < n;
+        const float4 f = in ? s4[64 * j] : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (MAP) m[j] = in ? reinterpret_cast<const int4*>(map + p0)[64 * j] : make_int4(0, 0, 0, 0);
         v[j][0] = f.x;
         v[j][1] = f.y;
         v[j][2] = f.z;
         v[j][3] = f.w;
       }
+      if (MAP) {
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+          *reinterpret_cast<int4*>(&s_map[p0 + 256 * j]) = m[j];
+      }
     } else {
       const float* s1 = s + p0;
 #pragma unroll
-      for (int j = 0; j < kRegGroups; ++j)
+      for (int j = 0; j < G; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[j][e] = pos(j, e) < n ? s1[256 * j + e] : 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < kRegGroups; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        key[j][e] = score_key(v[j][e]);
-        if (pos(j, e) < n) atomicAdd(&sh.hist[key[j][e] >> 20], 1u);
-      }
-  }
-  __syncthreads();
-  uint32_t prefix = 0, mask = 0, kleft = (uint32_t)k;
-  const uint32_t c1 = select_digit(sh, 20, 12, prefix, mask, kleft);
-  const uint32_t d1 = prefix >> 20;
-
-  // ---- 2-3. per-thread bit masks over its keys (bit 4j + e): m_above =
-  // keys in bins above d1 (all kept), m_cand = keys of bin d1 (the
-  // candidates); then T (key of the last kept element) and need (kept keys
-  // equal to T)
-  const uint32_t lo = d1 << 20;                  // smallest key of bin d1
-  const bool top_bin = d1 == (uint32_t)(kBins - 1);
-  const uint32_t hi = top_bin ? 0u : (d1 + 1) << 20;  // smallest key above bin d1
-  uint32_t m_ge = 0, m_above = 0;
-#pragma unroll
-  for (int j = 0; j < kRegGroups; ++j)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool ok = pos(j, e) < n;
-      m_ge |= (ok && key[j][e] >= lo) ? 1u << (4 * j + e) : 0u;
-      m_above |= (ok && !top_bin && key[j][e] >= hi) ? 1u << (4 * j + e) : 0u;
-    }
-  const uint32_t m_cand = m_ge & ~m_above;
-  uint32_t T, need;
-  uint32_t m_gt = m_above, m_eq = 0;  // kept above T, equal to T
-  if (c1 <= (uint32_t)kCandRes) {
-    if (tid == 0) sh.count = 0;
-    __syncthreads();
-    const uint32_t cnt = __builtin_popcount(m_cand);
-    const uint32_t incl = wave_inclusive_scan(cnt);
-    uint32_t base = 0;
-    if (lane == 63 && incl) base = atomicAdd(&sh.count, incl);
-    base = __builtin_amdgcn_readlane(base, 63) + incl - cnt;
-    // few candidates per wave: a bit no lane holds is skipped as a whole
-#pragma unroll
-    for (int j = 0; j < kRegGroups; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((m_cand >> (4 * j + e)) & 1u) {
-          if (base < (uint32_t)kCandRes) cand[base] = make_uint2(key[j][e], (uint32_t)pos(j, e));
-          ++base;
+        for (int e = 0; e < 4; ++e) {
+          const bool in = p0 + 256 * j + e < n;
+          v[j][e] = in ? s1[256 * j + e] : 0.0f;
+          if (MAP && in) s_map[p0 + 256 * j + e] = map[p0 + 256 * j + e];
         }
-    __syncthreads();
-    resolve(cand, c1, kleft, prefix, mask, sh, T, need);
-#pragma unroll
-    for (int j = 0; j < kRegGroups; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((m_cand >> (4 * j + e)) & 1u) {
-          m_gt |= key[j][e] > T ? 1u << (4 * j + e) : 0u;
-          m_eq |= key[j][e] == T ? 1u << (4 * j + e) : 0u;
-        }
-  } else {
-    constexpr int kShift[3] = {12, 4, 0};
-    constexpr int kWidth[3] = {8, 8, 4};
-#pragma unroll
-    for (int d = 0; d < 3; ++d) {
-      zero_hist(sh, 1 << kWidth[d]);
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < kRegGroups; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (pos(j, e) < n && (key[j][e] & mask) == prefix)
-            atomicAdd(&sh.hist[(key[j][e] >> kShift[d]) & ((1u << kWidth[d]) - 1u)], 1u);
-      __syncthreads();
-      select_digit(sh, kShift[d], kWidth[d], prefix, mask, kleft);
     }
-    T = prefix;
-    need = kleft;
-#pragma unroll
-    for (int j = 0; j < kRegGroups; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool ok = pos(j, e) < n;
-        m_gt |= (ok && key[j][e] > T) ? 1u << (4 * j + e) : 0u;
-        m_eq |= (ok && key[j][e] == T) ? 1u << (4 * j + e) : 0u;
-      }
-  }
-
-  // ---- 4. ordered write.  Group j's counts, packed (above T) << 16 |
-  // (equal to T), are prefix-summed over the wave's lanes; the groups of a
-  // wave follow each other, the waves follow each other.
-  uint32_t gbase[kRegGroups];  // kept keys before this lane's group j (packed)
-  uint32_t run = 0;
-#pragma unroll
-  for (int j = 0; j < kRegGroups; ++j) {
-    const uint32_t c = (__builtin_popcount((m_gt >> (4 * j)) & 0xfu) << 16) |
-                       __builtin_popcount((m_eq >> (4 * j)) & 0xfu);
-    const uint32_t incl = wave_inclusive_scan(c);
-    gbase[j] = run + incl - c;
-    run += __builtin_amdgcn_readlane(incl, 63);
-  }
-  if (lane == 0) s_wave[wave] = run;
-  __syncthreads();
-  uint32_t before = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) before += w < wave ? s_wave[w] : 0u;
-  uint32_t m_keep = m_gt | m_eq;
-  while (m_keep) {
-    const int bit = __builtin_ctz(m_keep);
-    m_keep &= m_keep - 1u;
-    const int j = bit >> 2;
-    uint32_t gb = gbase[0];
-#pragma unroll
-    for (int t = 1; t < kRegGroups; ++t) gb = j == t ? gbase[t] : gb;
-    const uint32_t lower = ((1u << bit) - 1u) & (0xfu << (4 * j));  // same group, lower e
-    gb += before;
-    const uint32_t g = (gb >> 16) + __builtin_popcount(m_gt & lower);
-    const uint32_t q = (gb & 0xffffu) + __builtin_popcount(m_eq & lower);
-    const int32_t p = pos(j, bit & 3);
-    if ((m_gt >> bit) & 1u) {
-      const uint32_t slot = g + std::min(q, need);
-      if (slot < (uint32_t)k) out[slot] = p;
-    } else if (q < need && g + q < (uint32_t)k) {
-      out[g + q] = p;
-    }
-  }
+  };
+  // s_map is complete before the ordered write: reg_row_topk passes several
+  // barriers between the load and the write
+  auto emit = [&](uint32_t slot, int32_t p) { out[slot] = MAP ? s_map[p] : p; };
+  reg_row_topk<NT, G, false>(load, n, k, emit, sh, cand, s_wave);
 }
 
 __global__ __launch_bounds__(kThreads) void topk_long_kernel(const float* __restrict__ scores,
@@ -844,7 +595,7 @@ __global__ __launch_bounds__(kThreads) void topk_mw_collect(const float* __restr
     n_cand += (valid && (key[e] >> 20) == d1) ? 1u : 0u;
   }
   uint32_t total;
-  const uint32_t excl = block_exclusive_scan((n_above << 16) | n_cand, sh.tot, total);
+  const uint32_t excl = block_exclusive_scan((n_above << 16) | n_cand, sh, total);
   if (threadIdx.x == 0) {
     w.n_above[blockIdx.x] = total >> 16;
     sh.base = 0;
@@ -897,7 +648,7 @@ __global__ __launch_bounds__(kThreads) void topk_mw_resolve(const float* __restr
   const int c = threadIdx.x;
   const uint32_t v = c < n_chunks ? (s_gt[c] << 16) | s_eq[c] : 0u;
   uint32_t total;
-  const uint32_t excl = block_exclusive_scan(v, sh.tot, total);
+  const uint32_t excl = block_exclusive_scan(v, sh, total);
   if (c < n_chunks) {
     w.base_gt[c] = excl >> 16;
     w.base_eq[c] = excl & 0xffffu;
@@ -993,13 +744,29 @@ size_t topk_workspace_bytes(int64_t n_rows, int64_t n, int32_t k) {
   return use_mw(n_rows, n, k) ? (size_t)n_rows * sizeof(MwRow) : 0;
 }
 
+hipError_t launch_topk_merge(const float* cand_val, const int32_t* cand_pos, int64_t n_rows,
+                             int64_t n, int64_t cstride, int32_t k, int32_t* idx, hipStream_t s) {
+  const bool vec4 = (reinterpret_cast<uintptr_t>(cand_val) % 16 == 0) && (cstride % 4 == 0);
+  // the fewest keys per thread that hold the row
+  if (n <= 4 * 2 * 512)
+    hipLaunchKernelGGL((topk_reg_kernel<512, 2, true>), dim3((unsigned)n_rows), dim3(512), 0, s,
+                       cand_val, n, cstride, k, idx, vec4, cand_pos);
+  else if (n <= 4 * 4 * 512)
+    hipLaunchKernelGGL((topk_reg_kernel<512, 4, true>), dim3((unsigned)n_rows), dim3(512), 0, s,
+                       cand_val, n, cstride, k, idx, vec4, cand_pos);
+  else
+    hipLaunchKernelGGL((topk_reg_kernel<kThreads, 8, true>), dim3((unsigned)n_rows), dim3(kThreads),
+                       0, s, cand_val, n, cstride, k, idx, vec4, cand_pos);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const float* scores, int64_t n_rows, int64_t n, int64_t row_stride, int32_t k,
                        int32_t* idx, void* ws, hipStream_t s) {
   // 16-byte loads when every row starts 16-byte aligned
   const bool vec4 = (reinterpret_cast<uintptr_t>(scores) % 16 == 0) && (row_stride % 4 == 0);
   if (n <= kResident) {
-    hipLaunchKernelGGL(topk_reg_kernel, dim3((unsigned)n_rows), dim3(kThreads), 0, s, scores, n,
-                       row_stride, k, idx, vec4);
+    hipLaunchKernelGGL((topk_reg_kernel<kThreads, 8, false>), dim3((unsigned)n_rows), dim3(kThreads),
+                       0, s, scores, n, row_stride, k, idx, vec4, nullptr);
   } else if (use_mw(n_rows, n, k)) {
     MwRow* rows = static_cast<MwRow*>(ws);
     const dim3 grid((unsigned)((n + kMwChunk - 1) / kMwChunk), (unsigned)n_rows);
