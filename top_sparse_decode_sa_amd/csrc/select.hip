@@ -39,8 +39,7 @@ namespace sa {
 namespace {
 
 constexpr int kSelThreads = 256;
-constexpr int kSelGroups = 8;               // register select: 4 * 8 keys per thread
-constexpr int kPartMax = 4 * kSelGroups * kSelThreads;  // 8192: the register select's capacity
+constexpr int kPartMax = 8192;  // longest part: the register select at 4 * 8 keys per thread
 constexpr int kPartAlign = 256;             // a multiple of every layout's tokens per iteration
 constexpr int kSelCand = kRankMax + 8;      // threshold-bin candidates ranked in LDS
 constexpr int kMinGroups = 512;             // parts shrink (to 256 tokens) until the grid has this many
@@ -64,7 +63,9 @@ struct SelArgs {
   int32_t* idx;  // one part per row: the final list [rows, k], else null
 };
 
-template <typename KT, int D, int U>
+// Parts of at most 4 * G * 256 tokens (the register select holds 4 G keys
+// per thread).
+template <typename KT, int D, int U, int G>
 __global__ __launch_bounds__(kSelThreads) void select_part_kernel(SelArgs a) {
   constexpr int EB = Elt<KT>::kBytes;
   constexpr int E = Elt<KT>::kPer16B;
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(kSelThreads) void select_part_kernel(SelArgs a) {
   static_assert(U <= LPR, "one storing lane per unrolled token");
   static_assert(kSelThreads == 256 && kPartAlign % per_iter == 0, "whole iterations per part");
 
-  __shared__ __align__(16) float s_sc[kPartMax];
+  __shared__ __align__(16) float s_sc[4 * G * kSelThreads];
   __shared__ SharedT<kSelThreads> sh;
   __shared__ __align__(16) uint2 cand[kSelCand];
   __shared__ uint32_t s_wave[kSelThreads / 64];
@@ -169,9 +170,9 @@ __global__ __launch_bounds__(kSelThreads) void select_part_kernel(SelArgs a) {
   __syncthreads();
 
   // ---- 2. top-min(k, n) of the part, from LDS into registers
-  auto lds_load = [&](int p0, float (&v)[kSelGroups][4]) {
+  auto lds_load = [&](int p0, float (&v)[G][4]) {
 #pragma unroll
-    for (int j = 0; j < kSelGroups; ++j) {
+    for (int j = 0; j < G; ++j) {
       const float4 f = *reinterpret_cast<const float4*>(&s_sc[p0 + 256 * j]);
       v[j][0] = f.x;
       v[j][1] = f.y;
@@ -182,13 +183,13 @@ __global__ __launch_bounds__(kSelThreads) void select_part_kernel(SelArgs a) {
   const int32_t kk = std::min(a.k_sel, n);
   if (a.idx) {
     int32_t* out = a.idx + (int64_t)row * a.k_sel;
-    reg_row_topk<kSelThreads, kSelGroups, SEL_HIST>(
+    reg_row_topk<kSelThreads, G, SEL_HIST>(
         lds_load, n, kk, [&](uint32_t slot, int32_t p) { out[slot] = p; }, sh, cand, s_wave);
   } else {
     const int64_t c0 = (int64_t)row * a.cstride + (int64_t)part * a.kcap;
     float* cv = a.cand_val + c0;
     int32_t* cp = a.cand_pos + c0;
-    reg_row_topk<kSelThreads, kSelGroups, SEL_HIST>(
+    reg_row_topk<kSelThreads, G, SEL_HIST>(
         lds_load, n, kk,
         [&](uint32_t slot, int32_t p) {
           cv[slot] = s_sc[p];
@@ -265,16 +266,30 @@ hipError_t launch_select(const Cache& c, const SelectPlan& p, const void* q, con
                                             align_up((size_t)rows * p.cstride * sizeof(float), 256));
   }
   const dim3 grid((unsigned)p.P, (unsigned)rows);
-  if (c.kv_dtype == SA_BF16) {
-    if (c.D == 64)
-      hipLaunchKernelGGL((select_part_kernel<bf16_t, 64, 8>), grid, dim3(kSelThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((select_part_kernel<bf16_t, 128, 16>), grid, dim3(kSelThreads), 0, s, a);
+  if (p.L > 4096) {
+    if (c.kv_dtype == SA_BF16) {
+      if (c.D == 64)
+        hipLaunchKernelGGL((select_part_kernel<bf16_t, 64, 8, 8>), grid, dim3(kSelThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((select_part_kernel<bf16_t, 128, 16, 8>), grid, dim3(kSelThreads), 0, s, a);
+    } else {
+      if (c.D == 64)
+        hipLaunchKernelGGL((select_part_kernel<float, 64, 16, 8>), grid, dim3(kSelThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((select_part_kernel<float, 128, 16, 8>), grid, dim3(kSelThreads), 0, s, a);
+    }
   } else {
-    if (c.D == 64)
-      hipLaunchKernelGGL((select_part_kernel<float, 64, 16>), grid, dim3(kSelThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((select_part_kernel<float, 128, 16>), grid, dim3(kSelThreads), 0, s, a);
+    if (c.kv_dtype == SA_BF16) {
+      if (c.D == 64)
+        hipLaunchKernelGGL((select_part_kernel<bf16_t, 64, 8, 4>), grid, dim3(kSelThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((select_part_kernel<bf16_t, 128, 16, 4>), grid, dim3(kSelThreads), 0, s, a);
+    } else {
+      if (c.D == 64)
+        hipLaunchKernelGGL((select_part_kernel<float, 64, 16, 4>), grid, dim3(kSelThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((select_part_kernel<float, 128, 16, 4>), grid, dim3(kSelThreads), 0, s, a);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.P == 1) return e;
