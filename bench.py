@@ -238,17 +238,17 @@ def read_traffic(kernel):
 def select_candidates(rows, n, k):
     """Candidates per row of the fused exact selection (sa_select): parts of
     8192 tokens, halved (down to 256) while the grid has fewer than 512
-    workgroups and the candidates stay under half the row; each part keeps
-    min(k, its length).  Returns (candidates, fused)."""
+    workgroups and the candidates stay within a quarter of the row; each part
+    keeps min(k, its length).  Returns (candidates, fused)."""
     def cands(L):
         P = -(-n // L)
         return (P - 1) * min(k, L) + min(k, n - (P - 1) * L)
 
     L = 8192
-    while L > 256 and rows * -(-n // L) < 512 and 2 * cands(L // 2) <= n:
+    while L > 256 and rows * -(-n // L) < 512 and 4 * cands(L // 2) <= n:
         L //= 2
     C = cands(L)
-    return C, (-(-n // L) == 1 or (C <= 32768 and 2 * C <= n))
+    return C, (-(-n // L) == 1 or (C <= 32768 and 4 * C <= n))
 
 
 def step_bytes(cfg):
@@ -305,11 +305,20 @@ SWEEP_X = (2, 5, 10, 20, 50, 100, 200, 500)
 IDX_HEADS, IDX_DIM = 4, 64
 
 
+def select_fused(rows, n, k):
+    """Whether sa_select takes its fused path on this shape (else it scores
+    every token and runs sa_topk)."""
+    return select_candidates(rows, n, k)[1]
+
+
 def sweep(args):
     """Full decode step against dense decode across sparsity.
 
-    Two selection front ends feed the same top-k and gather-attend: exact
-    scores (every key row read) and a per-KV-head lightning indexer (keys
+    Selection front ends feeding the same gather-attend: exact scores (every
+    key row read) then sa_topk; sa_select, the same exact selection with the
+    scores kept on chip (fused where the part candidates are at most a
+    quarter of the row, column select_fused); and a per-KV-head lightning
+    indexer (keys
     projected to 64 dims, 4 indexer heads = the KV head's 4 grouped queries
     projected the same way, weights U(0,1)), which reads a quarter of the
     key bytes.  The llama32k shape uses the seeded workload; batch128k (68.7
@@ -397,6 +406,9 @@ def sweep(args):
             def attend():
                 T.sa_sparse_decode(q, kd, vd, idx, out=out)
 
+            def fused_select():
+                T.sa_select(q, kd, k, idx_out=idx)
+
             row = {"shape": shape, "x": x, "k": k, "dense_us": round(us_dense, 1)}
             row["exact_score_us"] = round(timed(exact_score, reps, dense), 1)
             row["indexer_us"] = round(timed(idx_score, reps, dense), 1)
@@ -406,9 +418,13 @@ def sweep(args):
                                                dense), 1)
             row["indexer_step_us"] = round(timed(lambda: (idx_score(), select(), attend()), reps,
                                                  dense), 1)
+            row["select_us"] = round(timed(fused_select, reps, dense), 1)
+            row["select_step_us"] = round(timed(lambda: (fused_select(), attend()), reps, dense), 1)
+            row["select_fused"] = select_fused(B * Hkv, N, k)
             row["attend_only_speedup"] = round(us_dense / row["attend_us"], 2)
             row["exact_step_speedup"] = round(us_dense / row["exact_step_us"], 2)
             row["indexer_step_speedup"] = round(us_dense / row["indexer_step_us"], 2)
+            row["select_step_speedup"] = round(us_dense / row["select_step_us"], 2)
             row["attend_gbps"] = round((2 * B * Hkv * k * d * 2) / row["attend_us"] / 1e3, 1)
             row["data"] = data
             results.append(row)
@@ -418,7 +434,8 @@ def sweep(args):
         torch.cuda.empty_cache()
 
     cols = ["shape", "x", "k", "dense_us", "exact_score_us", "indexer_us", "topk_us", "attend_us",
-            "exact_step_us", "indexer_step_us", "attend_only_speedup", "exact_step_speedup",
+            "select_us", "select_fused", "exact_step_us", "select_step_us", "indexer_step_us",
+            "attend_only_speedup", "exact_step_speedup", "select_step_speedup",
             "indexer_step_speedup", "attend_gbps"]
     print("  ".join("%12s" % c_ for c_ in cols))
     for r in results:

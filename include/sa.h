@@ -5,6 +5,8 @@
  * and values sit in a device-resident KV cache:
  *   1. score every cached token against the current query   (sa_score)
  *   2. keep the top-k tokens or token blocks per row          (sa_topk)
+ *      -- for exact scores, steps 1 and 2 in one pass that
+ *      keeps the scores on chip                               (sa_select)
  *   3. gather only those K/V rows and run a split-K
  *      online-softmax decode over them                        (sa_sparse_decode)
  * plus full-attention decode for layers routed dense (sa_dense_decode) and a
@@ -175,8 +177,8 @@ size_t sa_topk_workspace_size(int64_t n_rows, int64_t n, int32_t k);
  * scores its part into on-chip memory and keeps the part's top-k as (score,
  * position) candidates; a merge selects the row's top-k among them (every
  * element of the row's top-k is in its part's top-k).  When the candidates
- * would not be fewer than half the row it runs sa_score and sa_topk instead
- * (same result).  ws: sa_select_workspace_size bytes (may be 0), 256-byte
+ * would be more than a quarter of the row it runs sa_score and sa_topk
+ * instead (same result).  ws: sa_select_workspace_size bytes (may be 0), 256-byte
  * aligned; no state is kept in it between calls.
  * Errors: SA_ERR_NULL / SA_ERR_ALIGN for q, k_cache (16 bytes), idx_out;
  * SA_ERR_SHAPE for another kind or k outside [1, ctx_len];
@@ -271,7 +273,8 @@ typedef struct {
  * and sparse attention; [P2] sections 2.2-2.3 and [P5] IndexCache: a layer may
  * reuse the top-k index set an earlier layer produced, unchanged.
  *   DENSE:  sa_dense_decode.
- *   SPARSE: sa_score -> sa_topk -> sa_sparse_decode, the index set written to
+ *   SPARSE: sa_score -> sa_topk -> sa_sparse_decode (sa_select for the exact
+ *           score kinds, the same index set), the index set written to
  *           idx ([batch, n_kv_heads, k]; [batch, k] for INDEXER; [batch,
  *           n_q_heads, k] for EXACT_PER_Q_HEAD).
  *   REUSE:  sa_sparse_decode over idx exactly as given (no scoring, no top-k);

@@ -105,7 +105,7 @@ def test_select_errors_and_sizes():
     (every pointer here is fake: a call that got as far as a launch would
     return SA_ERR_HIP on this machine)."""
     L = T.lib()
-    d = _desc()  # 4 rows of 1000 tokens: parts of 256 tokens, 8192 workspace bytes at k = 64
+    d = _desc()  # 4 rows of 1000 tokens: two parts of 512, 4096 workspace bytes at k = 64
     E, Q = Bn.SA_SCORE_EXACT, Bn.SA_SCORE_EXACT_PER_Q_HEAD
     mis = ctypes.c_void_p((1 << 20) + 2)
     ws_mis = ctypes.c_void_p((1 << 20) + 16)
@@ -125,7 +125,7 @@ def test_select_errors_and_sizes():
     assert sel(kk=0) == Bn.SA_ERR_SHAPE
     assert sel(kk=1001) == Bn.SA_ERR_SHAPE
     need = L.sa_select_workspace_size(ctypes.byref(d), E, 64)
-    assert need == 8192
+    assert need == 2 * 4 * 128 * 4
     assert sel() == Bn.SA_ERR_WORKSPACE
     assert sel(ws=ws_mis, nbytes=need) == Bn.SA_ERR_ALIGN
     assert sel(ws=FAKE, nbytes=need - 1) == Bn.SA_ERR_WORKSPACE
@@ -140,7 +140,7 @@ def test_select_errors_and_sizes():
     ll = _desc(batch=16, n_q_heads=32, n_kv_heads=8, ctx_len=32768, kv_stride_b=8 * 32768 * 128,
                kv_stride_h=32768 * 128)
     assert L.sa_select_workspace_size(ctypes.byref(ll), E, 655) == 2 * 128 * 2620 * 4
-    # candidates not fewer than half the row: scores plus a register top-k
+    # candidates more than a quarter of the row: scores plus a register top-k
     assert L.sa_select_workspace_size(ctypes.byref(ll), E, 12000) == 128 * 32768 * 4
     # one part per row (512 rows of 4096): the index list is written directly
     one = _desc(batch=64, n_q_heads=8, n_kv_heads=8, ctx_len=4096, kv_stride_b=8 * 4096 * 128,
@@ -357,7 +357,8 @@ def test_bench_select_bytes_follow_the_library_plan():
     """bench.py prices the fused selection by its candidate count; that count
     must be the library's: the workspace is a score and a position per
     candidate slot (rows rounded to 4 slots, 256-byte aligned halves), none
-    for one part, the score array when the candidates fill half the row."""
+    for one part, the score array when the candidates exceed a quarter of
+    the row."""
     import importlib.util
     import os
     spec = importlib.util.spec_from_file_location(

@@ -5,10 +5,10 @@ Every case must give, position for position, the index list of sa_score
 pinned to the oracle elsewhere; one ragged case here is also checked against
 the oracle's fp64 scores directly.  The cases cover the fused path (parts of
 8192 tokens, parts shortened for few rows, a ragged last part, an odd and an
-even iteration count, the 256- and 1024-thread merges), the one-part path
-(which writes the index list itself), the fallback when the candidates would
-not be fewer than half the row, both dtypes and head sizes, per-query-head
-rows, and ties, NaN and -0.0 across part boundaries."""
+even iteration count, each merge variant), the one-part path (which writes
+the index list itself), the fallback when the candidates would be more than
+a quarter of the row, both dtypes and head sizes, per-query-head rows, and
+ties, NaN and -0.0 across part boundaries."""
 import numpy as np
 import pytest
 import torch
@@ -35,8 +35,8 @@ def _reference(q, k, kk, kind=T.SA_SCORE_EXACT):
 
 CASES = [
     # B, Hq, Hkv, N, d, dtype, k, what
-    (16, 32, 8, 32768, 128, "bf16", 655, "llama-shaped rows: four 8192-token parts"),
-    (2, 8, 2, 32768, 128, "bf16", 655, "few rows: 2048-token parts, 1024-thread merge"),
+    (16, 32, 8, 32768, 128, "bf16", 655, "llama-shaped rows: four 8192-token parts, 2620-key merge"),
+    (2, 8, 2, 32768, 128, "bf16", 655, "few rows: 4096-token parts, 5240-key merge"),
     (32, 64, 8, 2 * 8192 + 768, 128, "bf16", 300, "parts of 32, 32 and 3 iterations"),
     (1, 4, 1, 20000, 128, "bf16", 300, "ragged last part"),
     (3, 6, 3, 100, 128, "bf16", 10, "one part shorter than one iteration"),
@@ -45,8 +45,9 @@ CASES = [
     (2, 4, 2, 5000, 64, "f32", 37, "f32, head_dim 64"),
     (2, 8, 4, 9000, 128, "f32", 500, "f32, head_dim 128"),
     (2, 4, 2, 3000, 64, "bf16", 64, "bf16, head_dim 64"),
-    (1, 8, 8, 65536, 128, "bf16", 1500, "24000 candidates: 1024-thread merge"),
-    (2, 8, 2, 32768, 128, "bf16", 12000, "fallback: candidates not fewer than half the row"),
+    (1, 8, 8, 65536, 128, "bf16", 1500, "12000 candidates: 1024-thread merge"),
+    (2, 8, 2, 32768, 128, "bf16", 12000, "fallback: candidates more than a quarter of the row"),
+    (16, 32, 8, 32768, 128, "bf16", 3276, "fallback at 10x sparsity"),
 ]
 
 

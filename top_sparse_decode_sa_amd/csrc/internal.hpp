@@ -59,8 +59,8 @@ hipError_t launch_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int6
 // Exact top-k of every row of c (B * Hkv rows; per_q_head_view for one row
 // per query head) without writing the scores: rows are cut into parts of L
 // tokens scored and pre-selected in LDS, then merged.  Falls back to exact
-// scoring plus top-k when the part candidates would not be fewer than half
-// the row.
+// scoring plus top-k when the part candidates would be more than a quarter
+// of the row.
 struct SelectPlan {
   int32_t L = 0;        // tokens per part (a multiple of 256, at most 8192)
   int32_t P = 0;        // parts per row

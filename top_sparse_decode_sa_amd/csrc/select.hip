@@ -210,18 +210,20 @@ SelectPlan plan_select(const Cache& c, int32_t k) {
     return (P - 1) * std::min<int64_t>(k, L) + std::min<int64_t>(k, c.N - (P - 1) * L);
   };
   // the longest parts, shortened while the grid is small and the candidates
-  // stay under half the row
+  // stay within a quarter of the row
   int64_t L = kPartMax;
-  while (L > kPartAlign && rows * ((c.N + L - 1) / L) < kMinGroups && 2 * cands(L / 2) <= c.N)
+  while (L > kPartAlign && rows * ((c.N + L - 1) / L) < kMinGroups && 4 * cands(L / 2) <= c.N)
     L /= 2;
   p.L = (int32_t)L;
   p.P = (int32_t)((c.N + L - 1) / L);
   p.kcap = (int32_t)std::min<int64_t>(k, L);
   p.C = cands(L);
   p.cstride = (p.C + 3) / 4 * 4;
-  // fused when the candidates are fewer than half the row (8 bytes each
-  // against 4 per score) and fit the merge; one part needs no merge
-  p.fused = p.P == 1 || (p.C <= kMergeMax && 2 * p.C <= c.N);
+  // fused when the candidates are at most a quarter of the row and fit the
+  // merge (measured: at 4 parts of 8192 tokens the fused path is faster
+  // from 20x sparsity on, slower at 10x, where each part keeps 40% of its
+  // tokens); one part needs no merge
+  p.fused = p.P == 1 || (p.C <= kMergeMax && 4 * p.C <= c.N);
   if (!p.fused) {
     p.ws_bytes = align_up((size_t)rows * c.N * sizeof(float), 256) +
                  align_up(topk_workspace_bytes(rows, c.N, k), 256);
