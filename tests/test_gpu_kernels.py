@@ -388,14 +388,16 @@ def test_per_query_head_with_shared_sets_equals_per_kv_head():
 
 # ------------------------------------------------------------ graph replay
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("B,Hkv,N,k", [(2, 4, 5000, 61), (1, 2, 40000, 300)])
-def test_step_graph_replay(B, Hkv, N, k):
-    """A decode step (score -> top-k -> gather-attend) captured as a HIP graph
-    and replayed several times, with new queries copied in eagerly and the
-    stream synchronised between replays: every replay equals the eager step.
-    The shapes take the split attend plan with its combine launch and the
-    multi-workgroup top-k with its zeroing kernel."""
-    say("graph replay B=%d Hkv=%d N=%d k=%d" % (B, Hkv, N, k))
+def test_step_graph_replay(B, Hkv, N, k, fused):
+    """A decode step (score -> top-k, or the fused sa_select, -> gather-attend)
+    captured as a HIP graph and replayed several times, with new queries
+    copied in eagerly and the stream synchronised between replays: every
+    replay equals the eager step.  The shapes take the split attend plan with
+    its combine launch, the multi-workgroup top-k with its zeroing kernel, and
+    the fused selection's part and merge launches."""
+    say("graph replay B=%d Hkv=%d N=%d k=%d fused=%s" % (B, Hkv, N, k, fused))
     G, d = 4, 128
     q, kc, vc = _rand_cache(B, Hkv * G, Hkv, N, d, "bf16", N)
     q, kc, vc = q.to(dev()), kc.to(dev()), vc.to(dev())
@@ -404,8 +406,11 @@ def test_step_graph_replay(B, Hkv, N, k):
     out = torch.empty((B, Hkv * G, d), dtype=torch.float32, device=dev())
 
     def step():
-        T.sa_score(q, kc, T.SA_SCORE_EXACT, scores=scores)
-        T.sa_topk(scores, k, idx_out=idx)
+        if fused:
+            T.sa_select(q, kc, k, idx_out=idx)
+        else:
+            T.sa_score(q, kc, T.SA_SCORE_EXACT, scores=scores)
+            T.sa_topk(scores, k, idx_out=idx)
         T.sa_sparse_decode(q, kc, vc, idx, out=out)
 
     step()
