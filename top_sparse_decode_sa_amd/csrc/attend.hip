@@ -403,7 +403,7 @@ __global__ __launch_bounds__(64 * max_waves<MODE>()) void attend_sparse_kernel(A
           float sc = 0.0f;
 #pragma unroll
           for (int h = 0; h < G; ++h) sc += acc[h];
-          a.scores[(int64_t)row * a.N + s0 + 16 * i + n] = sc * a.sscale;
+          __builtin_nontemporal_store(sc * a.sscale, a.scores + (int64_t)row * a.N + s0 + 16 * i + n);
         }
       }
     }

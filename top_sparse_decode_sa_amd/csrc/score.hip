@@ -17,7 +17,8 @@
 // All kernels are HBM-streaming: a lane group of LPR lanes reads one cache row
 // with 16-byte loads, reduces its dot product with DPP inside the group, and
 // each wave covers a contiguous run of tokens so both loads and score stores
-// are coalesced.
+// are coalesced.  Score stores are nontemporal: stores mixed into the key
+// stream cost far more than their bytes, less so when they bypass the caches.
 #include <math.h>
 
 #include <algorithm>
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void score_exact_kernel(ExactArgs a) {
       if (sl == u) mine = acc;
     }
     const int64_t t = base + wave * per_wave_iter + sl * RPW + lg;
-    if (sl < U && (!check || t < t_end)) srow[t] = mine;
+    if (sl < U && (!check || t < t_end)) __builtin_nontemporal_store(mine, srow + t);
   };
   if (t_end - t_tile == kScoreTile) {
     // whole tile: a fixed number of iterations, fully unrolled, so every
@@ -333,7 +334,7 @@ __global__ __launch_bounds__(kThreads) void score_indexer_kernel(IndexerArgs a) 
       if (sl == u) mine = sc;
     }
     const int64_t t = base + wave * per_wave_iter + sl * RPW + lg;
-    if (sl < U && (!check || t < t_end)) srow[t] = mine;
+    if (sl < U && (!check || t < t_end)) __builtin_nontemporal_store(mine, srow + t);
   };
   if (t_end - t_tile == kScoreTile) {
     uint4 kb[2][U];
