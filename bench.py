@@ -320,8 +320,8 @@ def sweep(args):
     quarter of the row, column select_fused); and a per-KV-head lightning
     indexer (keys
     projected to 64 dims, 4 indexer heads = the KV head's 4 grouped queries
-    projected the same way, weights U(0,1)), which reads a quarter of the
-    key bytes.  The llama32k shape uses the seeded workload; batch128k (68.7
+    projected the same way, weights U(0,1)), which reads half the key bytes.
+    The llama32k shape uses the seeded workload; batch128k (68.7
     GB of K/V) is drawn N(0,1) on the device, since only the selection sizes,
     not the values, drive the timings there."""
     import torch

@@ -30,20 +30,15 @@
 #include "internal.hpp"
 #include "topk_core.hpp"
 
-#ifndef SEL_HIST
-#define SEL_HIST 1
-#endif
-
-
 namespace sa {
 namespace {
 
 constexpr int kSelThreads = 256;
-constexpr int kPartMax = 8192;  // longest part: the register select at 4 * 8 keys per thread
-constexpr int kPartAlign = 256;             // a multiple of every layout's tokens per iteration
-constexpr int kSelCand = kRankMax + 8;      // threshold-bin candidates ranked in LDS
-constexpr int kMinGroups = 512;             // parts shrink (to 256 tokens) until the grid has this many
-constexpr int64_t kMergeMax = 32768;        // candidates per row the merge holds in registers
+constexpr int kPartMax = 8192;         // longest part: the register select at 4 * 8 keys per thread
+constexpr int kPartAlign = 256;        // a multiple of every layout's tokens per iteration
+constexpr int kSelCand = kRankMax + 8; // threshold-bin candidates ranked in LDS
+constexpr int kMinGroups = 512;        // parts shrink (to 256 tokens) until the grid has this many
+constexpr int64_t kMergeMax = 32768;   // candidates per row the merge holds in registers
 
 struct SelArgs {
   const void* q;
@@ -97,11 +92,9 @@ __global__ __launch_bounds__(kSelThreads) void select_part_kernel(SelArgs a) {
                         qs);
   const uint8_t* kbase =
       a.k + ((int64_t)b * a.sb + (int64_t)(r / a.kv_div) * a.sh + t0 * a.st) * EB + sl * 16;
-#if SEL_HIST
   // the selection's 12-bit histogram is counted as the scores are produced
   zero_hist(sh, kBins);
   __syncthreads();
-#endif
   const int64_t row_bytes = a.st * EB;
 
   // ---- 1. scores of the part into LDS.  Each wave covers per_wave_iter
@@ -130,9 +123,7 @@ __global__ __launch_bounds__(kSelThreads) void select_part_kernel(SelArgs a) {
     const int t = base + wave * per_wave_iter + sl * RPW + lg;
     if (sl < U && (!check || t < n)) {
       s_sc[t] = mine;
-#if SEL_HIST
       atomicAdd(&sh.hist[score_key(mine) >> 20], 1u);
-#endif
     }
   };
   const int nf = n / per_iter;  // whole iterations
@@ -183,13 +174,13 @@ __global__ __launch_bounds__(kSelThreads) void select_part_kernel(SelArgs a) {
   const int32_t kk = std::min(a.k_sel, n);
   if (a.idx) {
     int32_t* out = a.idx + (int64_t)row * a.k_sel;
-    reg_row_topk<kSelThreads, G, SEL_HIST>(
+    reg_row_topk<kSelThreads, G, true>(
         lds_load, n, kk, [&](uint32_t slot, int32_t p) { out[slot] = p; }, sh, cand, s_wave);
   } else {
     const int64_t c0 = (int64_t)row * a.cstride + (int64_t)part * a.kcap;
     float* cv = a.cand_val + c0;
     int32_t* cp = a.cand_pos + c0;
-    reg_row_topk<kSelThreads, G, SEL_HIST>(
+    reg_row_topk<kSelThreads, G, true>(
         lds_load, n, kk,
         [&](uint32_t slot, int32_t p) {
           cv[slot] = s_sc[p];
