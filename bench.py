@@ -318,7 +318,7 @@ def sweep(args):
     key row read) then sa_topk; sa_select, the same exact selection with the
     scores kept on chip (fused where the part candidates are at most a
     quarter of the row, column select_fused); and a per-KV-head lightning
-    indexer (keys
+    indexer, scored then sa_topk or through sa_select (keys
     projected to 64 dims, 4 indexer heads = the KV head's 4 grouped queries
     projected the same way, weights U(0,1)), which reads half the key bytes.
     The llama32k shape uses the seeded workload; batch128k (68.7
@@ -409,6 +409,10 @@ def sweep(args):
             def fused_select():
                 T.sa_select(q, kd, k, idx_out=idx)
 
+            def fused_idx_select():
+                T.sa_select(q, kd, k, T.SA_SCORE_INDEXER_PER_KV_HEAD, idx_out=idx, q_idx=q_idx,
+                            k_idx=k_idx, idx_w=idx_w)
+
             row = {"shape": shape, "x": x, "k": k, "dense_us": round(us_dense, 1)}
             row["exact_score_us"] = round(timed(exact_score, reps, dense), 1)
             row["indexer_us"] = round(timed(idx_score, reps, dense), 1)
@@ -421,10 +425,13 @@ def sweep(args):
             row["select_us"] = round(timed(fused_select, reps, dense), 1)
             row["select_step_us"] = round(timed(lambda: (fused_select(), attend()), reps, dense), 1)
             row["select_fused"] = select_fused(B * Hkv, N, k)
+            row["indexer_select_step_us"] = round(timed(lambda: (fused_idx_select(), attend()), reps,
+                                                        dense), 1)
             row["attend_only_speedup"] = round(us_dense / row["attend_us"], 2)
             row["exact_step_speedup"] = round(us_dense / row["exact_step_us"], 2)
             row["indexer_step_speedup"] = round(us_dense / row["indexer_step_us"], 2)
             row["select_step_speedup"] = round(us_dense / row["select_step_us"], 2)
+            row["indexer_select_step_speedup"] = round(us_dense / row["indexer_select_step_us"], 2)
             row["attend_gbps"] = round((2 * B * Hkv * k * d * 2) / row["attend_us"] / 1e3, 1)
             row["data"] = data
             results.append(row)
@@ -435,8 +442,9 @@ def sweep(args):
 
     cols = ["shape", "x", "k", "dense_us", "exact_score_us", "indexer_us", "topk_us", "attend_us",
             "select_us", "select_fused", "exact_step_us", "select_step_us", "indexer_step_us",
-            "attend_only_speedup", "exact_step_speedup", "select_step_speedup",
-            "indexer_step_speedup", "attend_gbps"]
+            "indexer_select_step_us", "attend_only_speedup", "exact_step_speedup",
+            "select_step_speedup", "indexer_step_speedup", "indexer_select_step_speedup",
+            "attend_gbps"]
     print("  ".join("%12s" % c_ for c_ in cols))
     for r in results:
         print("  ".join("%12s" % r[c_] for c_ in cols))

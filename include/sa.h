@@ -5,8 +5,8 @@
  * and values sit in a device-resident KV cache:
  *   1. score every cached token against the current query   (sa_score)
  *   2. keep the top-k tokens or token blocks per row          (sa_topk)
- *      -- for exact scores, steps 1 and 2 in one pass that
- *      keeps the scores on chip                               (sa_select)
+ *      -- for exact or indexer scores, steps 1 and 2 in one
+ *      pass that keeps the scores on chip                     (sa_select)
  *   3. gather only those K/V rows and run a split-K
  *      online-softmax decode over them                        (sa_sparse_decode)
  * plus full-attention decode for layers routed dense (sa_dense_decode) and a
@@ -167,24 +167,29 @@ sa_status sa_topk(const float* scores, int64_t n_rows, int64_t n, int64_t row_st
                   int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
 size_t sa_topk_workspace_size(int64_t n_rows, int64_t n, int32_t k);
 
-/* Exact selection in one pass over the key cache: the index list that
- * sa_score(kind) followed by sa_topk(k) writes ([P3] section 2, oracle top-k;
- * [P5] DSA Stage 1, a top-K index list), identical position for position,
- * without writing the scores.  kind: SA_SCORE_EXACT (idx_out [batch,
- * n_kv_heads, k]) or SA_SCORE_EXACT_PER_Q_HEAD (idx_out [batch, n_q_heads,
- * k], batch * n_q_heads <= 65535).
+/* Selection in one pass over the keys: the index list that sa_score(kind)
+ * followed by sa_topk(k) writes ([P3] section 2, oracle top-k; [P5] DSA
+ * Stage 1, a top-K index list from the indexer), identical position for
+ * position, without writing the scores.  kind and idx_out:
+ *   SA_SCORE_EXACT                [batch, n_kv_heads, k]
+ *   SA_SCORE_EXACT_PER_Q_HEAD     [batch, n_q_heads, k]  (batch * n_q_heads <= 65535)
+ *   SA_SCORE_INDEXER              [batch, k]            (aux as for sa_score)
+ *   SA_SCORE_INDEXER_PER_KV_HEAD  [batch, n_kv_heads, k] (aux as for sa_score)
+ * q and k_cache are read for the exact kinds, aux for the indexers (q and
+ * k_cache may then be null).
  * Method: each row is cut into parts of at most 8192 tokens; a workgroup
  * scores its part into on-chip memory and keeps the part's top-k as (score,
  * position) candidates; a merge selects the row's top-k among them (every
  * element of the row's top-k is in its part's top-k).  When the candidates
  * would be more than a quarter of the row it runs sa_score and sa_topk
- * instead (same result).  ws: sa_select_workspace_size bytes (may be 0), 256-byte
- * aligned; no state is kept in it between calls.
- * Errors: SA_ERR_NULL / SA_ERR_ALIGN for q, k_cache (16 bytes), idx_out;
- * SA_ERR_SHAPE for another kind or k outside [1, ctx_len];
- * SA_ERR_WORKSPACE when ws_bytes is short. */
+ * instead (same result).  ws: sa_select_workspace_size bytes (may be 0),
+ * 256-byte aligned; no state is kept in it between calls.
+ * Errors: SA_ERR_NULL / SA_ERR_ALIGN for q, k_cache (16 bytes), idx_out or
+ * the indexer tensors; SA_ERR_SHAPE for another kind, bad indexer sizes or k
+ * outside [1, ctx_len]; SA_ERR_WORKSPACE when ws_bytes is short. */
 sa_status sa_select(const sa_kv_desc* desc, sa_score_kind kind, const void* q, const void* k_cache,
-                    int32_t k, int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
+                    const sa_score_aux* aux, int32_t k, int32_t* idx_out, void* ws,
+                    size_t ws_bytes, hipStream_t stream);
 size_t sa_select_workspace_size(const sa_kv_desc* desc, sa_score_kind kind, int32_t k);
 
 /* ------------------------------------------------------------ attention */
@@ -274,7 +279,7 @@ typedef struct {
  * reuse the top-k index set an earlier layer produced, unchanged.
  *   DENSE:  sa_dense_decode.
  *   SPARSE: sa_score -> sa_topk -> sa_sparse_decode (sa_select for the exact
- *           score kinds, the same index set), the index set written to
+ *           and indexer score kinds, the same index set), the index set written to
  *           idx ([batch, n_kv_heads, k]; [batch, k] for INDEXER; [batch,
  *           n_q_heads, k] for EXACT_PER_Q_HEAD).
  *   REUSE:  sa_sparse_decode over idx exactly as given (no scoring, no top-k);

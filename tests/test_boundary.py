@@ -110,13 +110,34 @@ def test_select_errors_and_sizes():
     mis = ctypes.c_void_p((1 << 20) + 2)
     ws_mis = ctypes.c_void_p((1 << 20) + 16)
 
-    def sel(desc=d, kind=E, q=FAKE, k=FAKE, kk=64, idx=FAKE, ws=None, nbytes=0):
-        return L.sa_select(ctypes.byref(desc) if desc is not None else None, kind, q, k, kk, idx,
-                           ws, nbytes, None)
+    def sel(desc=d, kind=E, q=FAKE, k=FAKE, aux=None, kk=64, idx=FAKE, ws=None, nbytes=0):
+        return L.sa_select(ctypes.byref(desc) if desc is not None else None, kind, q, k,
+                           ctypes.byref(aux) if aux is not None else None, kk, idx, ws, nbytes,
+                           None)
 
     assert sel(desc=None) == Bn.SA_ERR_NULL
-    for kind in (Bn.SA_SCORE_BLOCK_MINMAX, Bn.SA_SCORE_INDEXER, Bn.SA_SCORE_INDEXER_PER_KV_HEAD, 9):
+    for kind in (Bn.SA_SCORE_BLOCK_MINMAX, 9):
         assert sel(kind=kind) == Bn.SA_ERR_SHAPE
+    # the indexer kinds: aux checked as for sa_score, q and k_cache unused
+    IX, IXK = Bn.SA_SCORE_INDEXER, Bn.SA_SCORE_INDEXER_PER_KV_HEAD
+    for kind in (IX, IXK):
+        assert sel(kind=kind) == Bn.SA_ERR_NULL
+        aux = Bn.ScoreAux()
+        aux.q_idx = aux.k_idx = 1 << 20
+        aux.idx_w = 1 << 20
+        aux.n_idx_heads, aux.idx_dim = 17, 64
+        assert sel(kind=kind, aux=aux, q=None, k=None) == Bn.SA_ERR_SHAPE
+        aux.n_idx_heads, aux.idx_dim = 4, 48
+        assert sel(kind=kind, aux=aux, q=None, k=None) == Bn.SA_ERR_UNSUPPORTED
+        aux.idx_dim = 64
+        assert sel(kind=kind, aux=aux, q=None, k=None, idx=None) == Bn.SA_ERR_NULL
+        assert sel(kind=kind, aux=aux, q=None, k=None, kk=1001) == Bn.SA_ERR_SHAPE
+        assert sel(kind=kind, aux=aux, q=None, k=None) == Bn.SA_ERR_WORKSPACE
+        aux.q_idx = (1 << 20) + 2
+        assert sel(kind=kind, aux=aux, q=None, k=None) == Bn.SA_ERR_ALIGN
+    # rows: one per sequence (shared indexer) or per (sequence, KV head)
+    assert L.sa_select_workspace_size(ctypes.byref(d), IX, 64) == 2 * 2 * 128 * 4
+    assert L.sa_select_workspace_size(ctypes.byref(d), IXK, 64) == 2 * 4 * 128 * 4
     assert sel(q=None) == Bn.SA_ERR_NULL
     assert sel(q=mis) == Bn.SA_ERR_ALIGN
     assert sel(k=None) == Bn.SA_ERR_NULL

@@ -108,3 +108,59 @@ def test_select_ties_and_specials(pattern):
     assert torch.equal(got, want), pattern
     if pattern == "zero query":
         assert torch.equal(got.cpu(), torch.arange(k, dtype=torch.int32).expand(B, Hkv, k))
+
+
+# ------------------------------------------------------------ indexer kinds
+
+IDX_CASES = [
+    # B, Hkv, N, H, Di, k, shared, what
+    (16, 8, 32768, 4, 64, 655, False, "llama-shaped per-KV-head indexer, four 8192-token parts"),
+    (2, 2, 20000, 4, 64, 300, False, "ragged last part"),
+    (3, 2, 9000, 16, 128, 200, True, "shared indexer, 16 heads of 128 dims"),
+    (2, 4, 5000, 3, 32, 40, False, "3 heads of 32 dims"),
+    (4, 2, 100, 8, 64, 10, True, "one part shorter than one iteration"),
+    (2, 2, 32768, 4, 64, 12000, False, "fallback: candidates more than a quarter of the row"),
+]
+
+
+def _indexer_inputs(B, Hkv, N, H, Di, shared, seed):
+    """Indexer tensors drawn on the device; q and a cache view that only give
+    the call its shapes (the indexer kinds read neither)."""
+    g = torch.Generator(device=dev()).manual_seed(seed)
+    lead = (B,) if shared else (B, Hkv)
+    qi = torch.randn(lead + (H, Di), generator=g, device=dev()).to(torch.bfloat16)
+    ki = torch.randn(lead + (N, Di), generator=g, device=dev()).to(torch.bfloat16)
+    w = torch.rand(lead + (H,), generator=g, device=dev())
+    q = torch.zeros((B, Hkv * 4, 128), dtype=torch.bfloat16, device=dev())
+    kc = torch.zeros((N, 128), dtype=torch.bfloat16, device=dev()).as_strided(
+        (B, Hkv, N, 128), (0, 0, 128, 1))
+    return q, kc, qi, ki, w
+
+
+@pytest.mark.parametrize("B,Hkv,N,H,Di,k,shared,what", IDX_CASES)
+def test_select_indexer_matches_score_then_topk(B, Hkv, N, H, Di, k, shared, what):
+    say("select indexer B=%d Hkv=%d N=%d H=%d Di=%d k=%d shared=%s (%s)" % (
+        B, Hkv, N, H, Di, k, shared, what))
+    kind = T.SA_SCORE_INDEXER if shared else T.SA_SCORE_INDEXER_PER_KV_HEAD
+    q, kc, qi, ki, w = _indexer_inputs(B, Hkv, N, H, Di, shared, seed=N + H)
+    got = T.sa_select(q, kc, k, kind, q_idx=qi, k_idx=ki, idx_w=w)
+    want = T.sa_topk(T.sa_score(q, kc, kind, q_idx=qi, k_idx=ki, idx_w=w), k)
+    torch.cuda.synchronize()
+    assert tuple(got.shape) == ((B, k) if shared else (B, Hkv, k))
+    assert torch.equal(got, want), what
+
+
+def test_select_indexer_against_oracle():
+    """Indexer selection checked against the oracle's fp64 indexer scores:
+    the exact top-k up to fp32 near-ties, in ascending order."""
+    say("select indexer vs oracle")
+    B, Hkv, N, H, Di, k = 1, 2, 20000, 4, 64, 300
+    q, kc, qi, ki, w = _indexer_inputs(B, Hkv, N, H, Di, False, seed=21)
+    got = T.sa_select(q, kc, k, T.SA_SCORE_INDEXER_PER_KV_HEAD, q_idx=qi, k_idx=ki, idx_w=w)
+    got = got.cpu().numpy()
+    qf = qi.cpu().to(torch.float64).numpy()
+    kf = ki.cpu().to(torch.float64).numpy()
+    wf = w.cpu().to(torch.float64).numpy()
+    s64 = [O.scores_indexer(qf[0, r], kf[0, r], wf[0, r]) for r in range(Hkv)]
+    counts, fails = verdicts(s64, [got[0, r] for r in range(Hkv)], k)
+    assert counts["failed"] == 0, fails

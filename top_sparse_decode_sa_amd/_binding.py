@@ -83,7 +83,7 @@ def lib() -> ctypes.CDLL:
     L.sa_topk.argtypes = [vp, i64, i64, i64, i32, vp, vp, sz, vp]
     L.sa_topk_workspace_size.argtypes = [i64, i64, i32]
     L.sa_topk_workspace_size.restype = sz
-    L.sa_select.argtypes = [P(KVDesc), st, vp, vp, i32, vp, vp, sz, vp]
+    L.sa_select.argtypes = [P(KVDesc), st, vp, vp, P(ScoreAux), i32, vp, vp, sz, vp]
     L.sa_select_workspace_size.argtypes = [P(KVDesc), st, i32]
     L.sa_select_workspace_size.restype = sz
     L.sa_sparse_decode.argtypes = [P(KVDesc), vp, vp, vp, st, vp, i32, i32, vp, vp, sz, vp]
@@ -262,19 +262,34 @@ def sa_block_summarize(k_cache, block_size, q_like=None):
     return kmin, kmax
 
 
-def sa_select(q, k_cache, k, kind=SA_SCORE_EXACT, idx_out=None, softmax_scale=0.0):
-    """sa_select: the exact top-k positions without the score array; int32
-    [B, Hkv, k] (EXACT) or [B, Hq, k] (EXACT_PER_Q_HEAD)."""
-    dev = _dev(q, k_cache)
+def sa_select(q, k_cache, k, kind=SA_SCORE_EXACT, idx_out=None, softmax_scale=0.0, *, q_idx=None,
+              k_idx=None, idx_w=None):
+    """sa_select: the top-k positions without the score array; int32
+    [B, Hkv, k] (EXACT, INDEXER_PER_KV_HEAD), [B, Hq, k] (EXACT_PER_Q_HEAD)
+    or [B, k] (INDEXER).  The indexer kinds take q_idx / k_idx / idx_w as
+    sa_score does (q and k_cache give the shapes)."""
+    dev = _dev(q, k_cache, q_idx, k_idx, idx_w)
     desc = make_desc(q, k_cache, softmax_scale)
-    rows = desc.n_q_heads if kind == SA_SCORE_EXACT_PER_Q_HEAD else desc.n_kv_heads
+    aux = ScoreAux()
+    if kind in (SA_SCORE_INDEXER, SA_SCORE_INDEXER_PER_KV_HEAD):
+        aux.q_idx, aux.k_idx, aux.idx_w = q_idx.data_ptr(), k_idx.data_ptr(), idx_w.data_ptr()
+        aux.n_idx_heads, aux.idx_dim = q_idx.shape[-2], q_idx.shape[-1]
+        for t in (q_idx, k_idx, idx_w):
+            if not t.is_contiguous():
+                raise ValueError("indexer tensors must be contiguous")
+    if kind == SA_SCORE_EXACT_PER_Q_HEAD:
+        shape = (desc.batch, desc.n_q_heads, k)
+    elif kind == SA_SCORE_INDEXER:
+        shape = (desc.batch, k)
+    else:
+        shape = (desc.batch, desc.n_kv_heads, k)
     if idx_out is None:
-        idx_out = torch.empty((desc.batch, rows, k), dtype=torch.int32, device=dev)
+        idx_out = torch.empty(shape, dtype=torch.int32, device=dev)
     L = lib()
     nbytes = L.sa_select_workspace_size(ctypes.byref(desc), kind, k)
     ws = WORKSPACES.get(dev, ("select", kind, k) + _desc_key(desc), nbytes)
-    check(L.sa_select(ctypes.byref(desc), kind, _ptr(q), _ptr(k_cache), k, _ptr(idx_out), _ptr(ws),
-                      nbytes, ctypes.c_void_p(_stream(dev))))
+    check(L.sa_select(ctypes.byref(desc), kind, _ptr(q), _ptr(k_cache), ctypes.byref(aux), k,
+                      _ptr(idx_out), _ptr(ws), nbytes, ctypes.c_void_p(_stream(dev))))
     return idx_out
 
 

@@ -179,13 +179,30 @@ sa_index_kind index_kind_of(sa_score_kind kind) {
   }
 }
 
-bool is_exact(sa_score_kind kind) {
-  return kind == SA_SCORE_EXACT || kind == SA_SCORE_EXACT_PER_Q_HEAD;
+// Score kinds that sa_select takes: the exact ones and the indexers.
+bool selectable(sa_score_kind kind) {
+  return kind == SA_SCORE_EXACT || kind == SA_SCORE_EXACT_PER_Q_HEAD || is_indexer(kind);
 }
 
-// Rows of an exact selection: one per KV head, or one per query head.
+// Rows of a selection: one per KV head, per query head, or per sequence
+// (shared indexer).
 Cache select_view(const Cache& c, sa_score_kind kind) {
-  return kind == SA_SCORE_EXACT_PER_Q_HEAD ? per_q_head_view(c) : c;
+  if (kind == SA_SCORE_EXACT_PER_Q_HEAD) return per_q_head_view(c);
+  Cache v = c;
+  if (kind == SA_SCORE_INDEXER) v.Hkv = 1;
+  return v;
+}
+
+// The indexer inputs of a selection (null for the exact kinds).
+const SelectIndexer* select_indexer(sa_score_kind kind, const sa_score_aux* aux,
+                                    SelectIndexer* buf) {
+  if (!is_indexer(kind)) return nullptr;
+  buf->q_idx = aux->q_idx;
+  buf->k_idx = aux->k_idx;
+  buf->w = aux->idx_w;
+  buf->H = aux->n_idx_heads;
+  buf->Di = aux->idx_dim;
+  return buf;
 }
 
 sa_status do_score(const Cache& c, sa_score_kind kind, const void* q, const void* k,
@@ -266,7 +283,7 @@ LayerWs layer_ws(const Cache& c, const sa_layer_args* a, sa_layer_mode mode) {
     const sa_index_kind ik = index_kind_of(a->score_kind);
     const int32_t bs = a->score_kind == SA_SCORE_BLOCK_MINMAX ? a->aux.block_size : 0;
     w.attend = plan_attend(attend_view(c, ik), mode_of(ik), a->k, bs).ws_bytes;
-    if (mode == SA_LAYER_SPARSE && is_exact(a->score_kind)) {
+    if (mode == SA_LAYER_SPARSE && selectable(a->score_kind)) {
       // the fused selection's candidates (or its scores and top-k fallback)
       w.scores = align_up(plan_select(select_view(c, a->score_kind), a->k).ws_bytes, 256);
     } else if (mode == SA_LAYER_SPARSE) {
@@ -394,26 +411,35 @@ sa_status sa_topk(const float* scores, int64_t n_rows, int64_t n, int64_t row_st
 
 size_t sa_select_workspace_size(const sa_kv_desc* desc, sa_score_kind kind, int32_t k) {
   Cache c;
-  if (check_desc(desc, &c) != SA_OK || !is_exact(kind) || k < 1 || k > c.N) return 0;
+  if (check_desc(desc, &c) != SA_OK || !selectable(kind) || k < 1 || k > c.N) return 0;
   return align_up(plan_select(select_view(c, kind), k).ws_bytes, 256);
 }
 
 sa_status sa_select(const sa_kv_desc* desc, sa_score_kind kind, const void* q, const void* k_cache,
-                    int32_t k, int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+                    const sa_score_aux* aux, int32_t k, int32_t* idx_out, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
   Cache c;
   sa_status st;
   if ((st = check_desc(desc, &c)) != SA_OK) return st;
-  if (!is_exact(kind))
-    return fail(SA_ERR_SHAPE, "sa_select takes the exact score kinds only (kind %d)", (int)kind);
-  if ((st = check_ptr(q, "q", 16)) != SA_OK) return st;
-  if ((st = check_ptr(k_cache, "k_cache", 16)) != SA_OK) return st;
+  if (!selectable(kind))
+    return fail(SA_ERR_SHAPE, "sa_select takes the exact and indexer score kinds (kind %d)",
+                (int)kind);
+  if (is_indexer(kind)) {
+    if ((st = check_indexer_aux(c, aux)) != SA_OK) return st;
+  } else {
+    if ((st = check_ptr(q, "q", 16)) != SA_OK) return st;
+    if ((st = check_ptr(k_cache, "k_cache", 16)) != SA_OK) return st;
+  }
   if ((st = check_ptr(idx_out, "idx_out", 4)) != SA_OK) return st;
   if (kind == SA_SCORE_EXACT_PER_Q_HEAD && (st = check_q_rows(c)) != SA_OK) return st;
   if (k < 1 || k > c.N) return fail(SA_ERR_SHAPE, "k %d outside [1, %lld]", k, (long long)c.N);
   const Cache v = select_view(c, kind);
   const SelectPlan p = plan_select(v, k);
   if ((st = check_ws(ws, ws_bytes, align_up(p.ws_bytes, 256), "sa_select")) != SA_OK) return st;
-  return hip_status(launch_select(v, p, q, k_cache, k, idx_out, ws, stream), "sa_select launch");
+  SelectIndexer ixb;
+  return hip_status(
+      launch_select(v, p, q, k_cache, select_indexer(kind, aux, &ixb), k, idx_out, ws, stream),
+      "sa_select launch");
 }
 
 size_t sa_sparse_workspace_size(const sa_kv_desc* desc, sa_index_kind ik, int32_t n_idx,
@@ -550,10 +576,12 @@ sa_status sa_decode_layer(const sa_layer_args* a, sa_layer_mode mode, int32_t* i
   void* att_ws = base + w.scores + w.topk;
   const Cache v = attend_view(c, ik);
   const AttendPlan p = plan_attend(v, mode_of(ik), a->k, bs);
-  if (mode == SA_LAYER_SPARSE && is_exact(a->score_kind)) {
+  if (mode == SA_LAYER_SPARSE && selectable(a->score_kind)) {
     const Cache sv = select_view(c, a->score_kind);
-    if ((st = hip_status(launch_select(sv, plan_select(sv, a->k), a->q, a->k_cache, a->k, idx, base,
-                                       stream),
+    SelectIndexer ixb;
+    if ((st = hip_status(launch_select(sv, plan_select(sv, a->k), a->q, a->k_cache,
+                                       select_indexer(a->score_kind, &a->aux, &ixb), a->k, idx,
+                                       base, stream),
                          "sa_decode_layer selection launch")) != SA_OK)
       return st;
   } else if (mode == SA_LAYER_SPARSE) {

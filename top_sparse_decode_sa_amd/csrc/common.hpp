@@ -186,6 +186,54 @@ __device__ __forceinline__ float row_dot(const uint4& w, const float (&qs)[E]) {
   return group_sum<LPR>(acc);
 }
 
+// Indexer score of one token ("Flash Attention vs Sparse Attention", DSA
+// Stage 1): sum_h w_h max(0, q_h . k), with the key's DI bf16 values spread
+// over LPR lanes (16 bytes each) and this lane's 16 bytes of every indexer
+// query packed in qv.  Each lane dots its 8 dims with v_dot2_f32_bf16 (both
+// operands bf16, so the products are exact and the sums fp32), the head
+// sums close over the lane group with DPP.  Shared by every kernel that
+// scores with the indexer, so their fp32 results agree bit for bit.
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
+__device__ __forceinline__ float dot8_bf16(const uint4& k, const uint4& q, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.x),
+                                        __builtin_bit_cast(bf16x2_t, q.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.y),
+                                        __builtin_bit_cast(bf16x2_t, q.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.z),
+                                        __builtin_bit_cast(bf16x2_t, q.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.w),
+                                        __builtin_bit_cast(bf16x2_t, q.w), acc, false);
+  return acc;
+}
+
+template <int LPR, int HP>
+__device__ __forceinline__ float indexer_token(const uint4& kw, const uint4 (&qv)[HP],
+                                               const float (&wv)[HP]) {
+  float sc = 0.0f;
+#pragma unroll
+  for (int h = 0; h < HP; ++h) {
+    const float acc = group_sum<LPR>(dot8_bf16(kw, qv[h], 0.0f));
+    sc = fmaf(wv[h], fmaxf(acc, 0.0f), sc);
+  }
+  return sc;
+}
+
+// This lane's 16 bytes (dims [8 sl, 8 sl + 8)) of the H <= HP indexer queries
+// of row `b` and their weights; heads >= H are zero.
+template <int DI, int HP>
+__device__ __forceinline__ void load_indexer_queries(const uint8_t* q_idx, const float* w, int64_t b,
+                                                     int H, int sl, uint4 (&qv)[HP],
+                                                     float (&wv)[HP]) {
+#pragma unroll
+  for (int h = 0; h < HP; ++h) {
+    const bool live = h < H;
+    wv[h] = live ? w[b * H + h] : 0.0f;
+    qv[h] = live ? *reinterpret_cast<const uint4*>(q_idx + ((b * H + h) * DI) * 2 + sl * 16)
+                 : make_uint4(0, 0, 0, 0);
+  }
+}
+
 // DPP move of a uint32 across lanes; lanes whose source lies outside the row
 // read 0 (bound_ctrl), lanes of rows outside ROW_MASK get 0.
 template <int CTRL, int ROW_MASK = 0xf>

@@ -56,11 +56,11 @@ hipError_t launch_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int6
                                 int32_t* counts, hipStream_t s);
 
 // ------------------------------------------------------- fused select
-// Exact top-k of every row of c (B * Hkv rows; per_q_head_view for one row
-// per query head) without writing the scores: rows are cut into parts of L
-// tokens scored and pre-selected in LDS, then merged.  Falls back to exact
-// scoring plus top-k when the part candidates would be more than a quarter
-// of the row.
+// Top-k of every row of c (B * Hkv rows; per_q_head_view for one row per
+// query head) by exact or indexer scores, without writing the scores: rows
+// are cut into parts of L tokens scored and pre-selected in LDS, then merged.
+// Falls back to scoring plus top-k when the part candidates would be more
+// than a quarter of the row.
 struct SelectPlan {
   int32_t L = 0;        // tokens per part (a multiple of 256, at most 8192)
   int32_t P = 0;        // parts per row
@@ -70,9 +70,19 @@ struct SelectPlan {
   bool fused = false;
   size_t ws_bytes = 0;  // workspace of the chosen path
 };
+// Indexer scoring instead of exact scores: rows of c (B * Hkv) are the
+// indexer's rows; q_idx [rows, H, Di] bf16, k_idx [rows, N, Di] bf16,
+// w [rows, H] fp32.
+struct SelectIndexer {
+  const void* q_idx;
+  const void* k_idx;
+  const float* w;
+  int32_t H, Di;
+};
 SelectPlan plan_select(const Cache& c, int32_t k);
 hipError_t launch_select(const Cache& c, const SelectPlan& p, const void* q, const void* k,
-                         int32_t kk, int32_t* idx, void* ws, hipStream_t s);
+                         const SelectIndexer* ix, int32_t kk, int32_t* idx, void* ws,
+                         hipStream_t s);
 
 // ----------------------------------------------------------- attention
 // kIdxDenseScored: dense decode that also writes each token's exact score

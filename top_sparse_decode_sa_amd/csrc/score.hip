@@ -268,28 +268,11 @@ struct IndexerArgs {
   float* scores;         // [B, N]
 };
 
-// One lane group of LPR = DI/8 lanes holds a token's indexer key (16 bytes,
-// 8 bf16, per lane); each lane dots its 8 dims with the matching 8 dims of
-// every indexer query with v_dot2_f32_bf16 (both operands are bf16, so each
-// product is exact and the sum is fp32, as the fma form), four per head
-// without unpacking the key, then the head sums close over the group with
-// DPP.  (The unpack-and-fma form needed 2.5x the VALU instructions per byte
-// and capped the kernel well below the HBM rate; matrix-core tiles need a
-// 16-token by 16-byte load pattern that streams worse.)
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_i;
-
-__device__ __forceinline__ float dot8_bf16(const uint4& k, const uint4& q, float acc) {
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_i, k.x),
-                                        __builtin_bit_cast(bf16x2_i, q.x), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_i, k.y),
-                                        __builtin_bit_cast(bf16x2_i, q.y), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_i, k.z),
-                                        __builtin_bit_cast(bf16x2_i, q.z), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_i, k.w),
-                                        __builtin_bit_cast(bf16x2_i, q.w), acc, false);
-  return acc;
-}
-
+// One lane group of LPR = DI/8 lanes holds a token's indexer key (16 bytes
+// per lane); indexer_token (v_dot2_f32_bf16 on the packed bf16 values, DPP
+// head sums) gives its score.  (The unpack-and-fma form needed 2.5x the VALU
+// instructions per byte; matrix-core tiles need a 16-token by 16-byte load
+// pattern that streams worse.)
 template <int DI, int HP, int U>
 __global__ __launch_bounds__(kThreads) void score_indexer_kernel(IndexerArgs a) {
   constexpr int LPR = DI * 2 / 16;
@@ -303,12 +286,7 @@ __global__ __launch_bounds__(kThreads) void score_indexer_kernel(IndexerArgs a) 
 
   uint4 qv[HP];  // this lane's 8 dims of every indexer query, packed bf16
   float wv[HP];
-#pragma unroll
-  for (int h = 0; h < HP; ++h) {
-    const bool live = h < a.H;
-    wv[h] = live ? a.w[(int64_t)b * a.H + h] : 0.0f;
-    qv[h] = live ? ld16(a.q_idx + (((int64_t)b * a.H + h) * DI) * 2 + sl * 16) : make_uint4(0, 0, 0, 0);
-  }
+  load_indexer_queries<DI, HP>(a.q_idx, a.w, b, a.H, sl, qv, wv);
 
   const uint8_t* kbase = a.k_idx + (int64_t)b * a.N * DI * 2 + sl * 16;
   float* srow = a.scores + (int64_t)b * a.N;
@@ -333,12 +311,7 @@ __global__ __launch_bounds__(kThreads) void score_indexer_kernel(IndexerArgs a) 
     float mine = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float sc = 0.0f;
-#pragma unroll
-      for (int h = 0; h < HP; ++h) {
-        const float acc = group_sum<LPR>(dot8_bf16(kw[u], qv[h], 0.0f));
-        sc = fmaf(wv[h], fmaxf(acc, 0.0f), sc);
-      }
+      const float sc = indexer_token<LPR, HP>(kw[u], qv, wv);
       if (sl == u) mine = sc;
     }
     const int64_t t = base + wave * per_wave_iter + sl * RPW + lg;

@@ -56,7 +56,93 @@ struct SelArgs {
   float* cand_val;  // [rows, cstride]: candidate scores
   int32_t* cand_pos;
   int32_t* idx;  // one part per row: the final list [rows, k], else null
+  // indexer scoring: queries [rows, H, DI] bf16, keys [rows, N, DI] bf16,
+  // weights [rows, H]
+  const uint8_t* q_idx;
+  const uint8_t* k_idx;
+  const float* w_idx;
+  int32_t H_idx;
 };
+
+// Streams a part's n tokens in iterations of PER tokens: whole iterations
+// through a 2-deep ping-pong (the next iteration's loads requested before
+// this one's are reduced; an odd count peels one first so the pipelined run
+// is even), then the ragged end with loads clamped to the last token.
+template <int PER, int U, typename Load, typename Reduce>
+__device__ __forceinline__ void stream_part(int n, Load load, Reduce reduce) {
+  const int nf = n / PER;  // whole iterations
+  int i0 = 0;
+  if (nf & 1) {
+    uint4 kw[U];
+    load(0, kw, false);
+    reduce(0, kw, false);
+    i0 = 1;
+  }
+  if (i0 < nf) {
+    uint4 ka[U], kb[U];
+    load(i0 * PER, ka, false);
+    int i = i0;
+    for (; i + 2 < nf; i += 2) {
+      load((i + 1) * PER, kb, false);
+      __builtin_amdgcn_sched_barrier(0);
+      reduce(i * PER, ka, false);
+      load((i + 2) * PER, ka, false);
+      __builtin_amdgcn_sched_barrier(0);
+      reduce((i + 1) * PER, kb, false);
+    }
+    load((i + 1) * PER, kb, false);
+    __builtin_amdgcn_sched_barrier(0);
+    reduce(i * PER, ka, false);
+    reduce((i + 1) * PER, kb, false);
+  }
+  if (nf * PER < n) {
+    uint4 kw[U];
+    load(nf * PER, kw, true);
+    reduce(nf * PER, kw, true);
+  }
+}
+
+struct PartLds {
+  SharedT<kSelThreads> sh;
+  uint2 cand[kSelCand];
+  uint32_t s_wave[kSelThreads / 64];
+};
+
+// The part's top-min(k, n) from its LDS scores (histogram already counted):
+// the index list itself for a one-part row, else (score, position)
+// candidates in position order.
+template <int G>
+__device__ __forceinline__ void part_select(const SelArgs& a, const float* s_sc, int n, int row,
+                                            int part, int64_t t0, PartLds& l) {
+  auto lds_load = [&](int p0, float (&v)[G][4]) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float4 f = *reinterpret_cast<const float4*>(&s_sc[p0 + 256 * j]);
+      v[j][0] = f.x;
+      v[j][1] = f.y;
+      v[j][2] = f.z;
+      v[j][3] = f.w;
+    }
+  };
+  const int32_t kk = std::min(a.k_sel, n);
+  if (a.idx) {
+    int32_t* out = a.idx + (int64_t)row * a.k_sel;
+    reg_row_topk<kSelThreads, G, true>(
+        lds_load, n, kk, [&](uint32_t slot, int32_t p) { out[slot] = p; }, l.sh, l.cand,
+        l.s_wave);
+  } else {
+    const int64_t c0 = (int64_t)row * a.cstride + (int64_t)part * a.kcap;
+    float* cv = a.cand_val + c0;
+    int32_t* cp = a.cand_pos + c0;
+    reg_row_topk<kSelThreads, G, true>(
+        lds_load, n, kk,
+        [&](uint32_t slot, int32_t p) {
+          cv[slot] = s_sc[p];
+          cp[slot] = (int32_t)t0 + p;
+        },
+        l.sh, l.cand, l.s_wave);
+  }
+}
 
 // Parts of at most 4 * G * 256 tokens (the register select holds 4 G keys
 // per thread).
@@ -72,9 +158,7 @@ __global__ __launch_bounds__(kSelThreads) void select_part_kernel(SelArgs a) {
   static_assert(kSelThreads == 256 && kPartAlign % per_iter == 0, "whole iterations per part");
 
   __shared__ __align__(16) float s_sc[4 * G * kSelThreads];
-  __shared__ SharedT<kSelThreads> sh;
-  __shared__ __align__(16) uint2 cand[kSelCand];
-  __shared__ uint32_t s_wave[kSelThreads / 64];
+  __shared__ PartLds l;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -93,13 +177,12 @@ __global__ __launch_bounds__(kSelThreads) void select_part_kernel(SelArgs a) {
   const uint8_t* kbase =
       a.k + ((int64_t)b * a.sb + (int64_t)(r / a.kv_div) * a.sh + t0 * a.st) * EB + sl * 16;
   // the selection's 12-bit histogram is counted as the scores are produced
-  zero_hist(sh, kBins);
+  zero_hist(l.sh, kBins);
   __syncthreads();
   const int64_t row_bytes = a.st * EB;
 
   // ---- 1. scores of the part into LDS.  Each wave covers per_wave_iter
-  // consecutive tokens per iteration; the next iteration's keys are
-  // requested before this one's are reduced.
+  // consecutive tokens per iteration.
   const uint8_t* kwave = kbase + (int64_t)(wave * per_wave_iter + lg) * row_bytes;
   auto load = [&](int base, uint4 (&kw)[U], bool clamp) {
     if (clamp) {
@@ -123,71 +206,73 @@ __global__ __launch_bounds__(kSelThreads) void select_part_kernel(SelArgs a) {
     const int t = base + wave * per_wave_iter + sl * RPW + lg;
     if (sl < U && (!check || t < n)) {
       s_sc[t] = mine;
-      atomicAdd(&sh.hist[score_key(mine) >> 20], 1u);
+      atomicAdd(&l.sh.hist[score_key(mine) >> 20], 1u);
     }
   };
-  const int nf = n / per_iter;  // whole iterations
-  int i0 = 0;
-  if (nf & 1) {
-    // an odd count: one iteration on its own, so the pipelined run is even
-    uint4 kw[U];
-    load(0, kw, false);
-    reduce(0, kw, false);
-    i0 = 1;
-  }
-  if (i0 < nf) {
-    uint4 ka[U], kb[U];
-    load(i0 * per_iter, ka, false);
-    int i = i0;
-    for (; i + 2 < nf; i += 2) {
-      load((i + 1) * per_iter, kb, false);
-      __builtin_amdgcn_sched_barrier(0);
-      reduce(i * per_iter, ka, false);
-      load((i + 2) * per_iter, ka, false);
-      __builtin_amdgcn_sched_barrier(0);
-      reduce((i + 1) * per_iter, kb, false);
-    }
-    load((i + 1) * per_iter, kb, false);
-    __builtin_amdgcn_sched_barrier(0);
-    reduce(i * per_iter, ka, false);
-    reduce((i + 1) * per_iter, kb, false);
-  }
-  if (nf * per_iter < n) {
-    // the part's ragged end: loads clamped to its last token
-    uint4 kw[U];
-    load(nf * per_iter, kw, true);
-    reduce(nf * per_iter, kw, true);
-  }
+  stream_part<per_iter, U>(n, load, reduce);
   __syncthreads();
 
-  // ---- 2. top-min(k, n) of the part, from LDS into registers
-  auto lds_load = [&](int p0, float (&v)[G][4]) {
+  // ---- 2. top-min(k, n) of the part
+  part_select<G>(a, s_sc, n, row, part, t0, l);
+}
+
+// The same part selection on indexer scores ("Flash Attention vs Sparse
+// Attention", DSA Stage 1): row `row` of the indexer tensors, its keys read
+// by lane groups of DI/8 lanes, each token scored by indexer_token (the same
+// arithmetic as the indexer scoring kernel).
+template <int DI, int HP, int U, int G>
+__global__ __launch_bounds__(kSelThreads) void select_indexer_kernel(SelArgs a) {
+  constexpr int LPR = DI * 2 / 16;
+  constexpr int RPW = 64 / LPR;
+  constexpr int per_wave_iter = RPW * U;
+  constexpr int per_iter = 4 * per_wave_iter;
+  static_assert(U <= LPR, "one storing lane per unrolled token");
+  static_assert(kSelThreads == 256 && kPartAlign % per_iter == 0, "whole iterations per part");
+
+  __shared__ __align__(16) float s_sc[4 * G * kSelThreads];
+  __shared__ PartLds l;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lg = (tid & 63) / LPR;
+  const int sl = tid % LPR;
+  const int part = blockIdx.x;
+  const int row = blockIdx.y;
+  const int64_t t0 = (int64_t)part * a.L;
+  const int n = (int)std::min<int64_t>(a.L, a.N - t0);
+
+  uint4 qv[HP];
+  float wv[HP];
+  load_indexer_queries<DI, HP>(a.q_idx, a.w_idx, row, a.H_idx, sl, qv, wv);
+  const uint8_t* kbase = a.k_idx + ((int64_t)row * a.N + t0) * DI * 2 + sl * 16;
+  zero_hist(l.sh, kBins);
+  __syncthreads();
+
+  auto load = [&](int base, uint4 (&kw)[U], bool clamp) {
+    const int wbase = base + wave * per_wave_iter + lg;
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float4 f = *reinterpret_cast<const float4*>(&s_sc[p0 + 256 * j]);
-      v[j][0] = f.x;
-      v[j][1] = f.y;
-      v[j][2] = f.z;
-      v[j][3] = f.w;
+    for (int u = 0; u < U; ++u) {
+      int t = wbase + u * RPW;
+      if (clamp) t = std::min(t, n - 1);
+      kw[u] = ld16_nt(kbase + (int64_t)t * (DI * 2));
     }
   };
-  const int32_t kk = std::min(a.k_sel, n);
-  if (a.idx) {
-    int32_t* out = a.idx + (int64_t)row * a.k_sel;
-    reg_row_topk<kSelThreads, G, true>(
-        lds_load, n, kk, [&](uint32_t slot, int32_t p) { out[slot] = p; }, sh, cand, s_wave);
-  } else {
-    const int64_t c0 = (int64_t)row * a.cstride + (int64_t)part * a.kcap;
-    float* cv = a.cand_val + c0;
-    int32_t* cp = a.cand_pos + c0;
-    reg_row_topk<kSelThreads, G, true>(
-        lds_load, n, kk,
-        [&](uint32_t slot, int32_t p) {
-          cv[slot] = s_sc[p];
-          cp[slot] = (int32_t)t0 + p;
-        },
-        sh, cand, s_wave);
-  }
+  auto reduce = [&](int base, const uint4 (&kw)[U], bool check) {
+    float mine = 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float sc = indexer_token<LPR, HP>(kw[u], qv, wv);
+      if (sl == u) mine = sc;
+    }
+    const int t = base + wave * per_wave_iter + sl * RPW + lg;
+    if (sl < U && (!check || t < n)) {
+      s_sc[t] = mine;
+      atomicAdd(&l.sh.hist[score_key(mine) >> 20], 1u);
+    }
+  };
+  stream_part<per_iter, U>(n, load, reduce);
+  __syncthreads();
+  part_select<G>(a, s_sc, n, row, part, t0, l);
 }
 
 }  // namespace
@@ -224,13 +309,63 @@ SelectPlan plan_select(const Cache& c, int32_t k) {
   return p;
 }
 
+namespace {
+
+template <int G, int DI, int HP>
+void launch_indexer_part(const SelArgs& a, dim3 grid, hipStream_t s) {
+  constexpr int LPR = DI * 2 / 16;
+  constexpr int U = HP >= 16 ? (LPR < 4 ? LPR : 4) : (LPR < 8 ? LPR : 8);
+  hipLaunchKernelGGL((select_indexer_kernel<DI, HP, U, G>), grid, dim3(kSelThreads), 0, s, a);
+}
+
+template <int G, int DI>
+void launch_indexer_part_h(const SelArgs& a, dim3 grid, hipStream_t s) {
+  if (a.H_idx <= 4) launch_indexer_part<G, DI, 4>(a, grid, s);
+  else if (a.H_idx <= 8) launch_indexer_part<G, DI, 8>(a, grid, s);
+  else launch_indexer_part<G, DI, 16>(a, grid, s);
+}
+
+template <int G>
+void launch_exact_part(const Cache& c, const SelArgs& a, dim3 grid, hipStream_t s) {
+  if (c.kv_dtype == SA_BF16) {
+    if (c.D == 64)
+      hipLaunchKernelGGL((select_part_kernel<bf16_t, 64, 8, G>), grid, dim3(kSelThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((select_part_kernel<bf16_t, 128, 16, G>), grid, dim3(kSelThreads), 0, s, a);
+  } else {
+    if (c.D == 64)
+      hipLaunchKernelGGL((select_part_kernel<float, 64, 16, G>), grid, dim3(kSelThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((select_part_kernel<float, 128, 16, G>), grid, dim3(kSelThreads), 0, s, a);
+  }
+}
+
+template <int G>
+void launch_part(const Cache& c, const SelectIndexer* ix, const SelArgs& a, dim3 grid,
+                 hipStream_t s) {
+  if (!ix) {
+    launch_exact_part<G>(c, a, grid, s);
+  } else if (ix->Di == 32) {
+    launch_indexer_part_h<G, 32>(a, grid, s);
+  } else if (ix->Di == 64) {
+    launch_indexer_part_h<G, 64>(a, grid, s);
+  } else {
+    launch_indexer_part_h<G, 128>(a, grid, s);
+  }
+}
+
+}  // namespace
+
 hipError_t launch_select(const Cache& c, const SelectPlan& p, const void* q, const void* k,
-                         int32_t kk, int32_t* idx, void* ws, hipStream_t s) {
+                         const SelectIndexer* ix, int32_t kk, int32_t* idx, void* ws,
+                         hipStream_t s) {
   const int64_t rows = (int64_t)c.B * c.Hkv;
   if (!p.fused) {
     float* scores = static_cast<float*>(ws);
     void* topk_ws = static_cast<uint8_t*>(ws) + align_up((size_t)rows * c.N * sizeof(float), 256);
-    hipError_t e = launch_score_exact(c, q, k, scores, s);
+    hipError_t e = ix ? launch_score_indexer((int32_t)rows, c.N, ix->H, ix->Di, ix->q_idx,
+                                             ix->k_idx, ix->w, scores, s)
+                      : launch_score_exact(c, q, k, scores, s);
     if (e != hipSuccess) return e;
     return launch_topk(scores, rows, c.N, c.N, kk, idx, topk_ws, s);
   }
@@ -251,6 +386,12 @@ hipError_t launch_select(const Cache& c, const SelectPlan& p, const void* q, con
   a.k_sel = kk;
   a.kcap = p.kcap;
   a.cstride = p.cstride;
+  if (ix) {
+    a.q_idx = static_cast<const uint8_t*>(ix->q_idx);
+    a.k_idx = static_cast<const uint8_t*>(ix->k_idx);
+    a.w_idx = ix->w;
+    a.H_idx = ix->H;
+  }
   if (p.P == 1) {
     a.idx = idx;
   } else {
@@ -259,31 +400,10 @@ hipError_t launch_select(const Cache& c, const SelectPlan& p, const void* q, con
                                             align_up((size_t)rows * p.cstride * sizeof(float), 256));
   }
   const dim3 grid((unsigned)p.P, (unsigned)rows);
-  if (p.L > 4096) {
-    if (c.kv_dtype == SA_BF16) {
-      if (c.D == 64)
-        hipLaunchKernelGGL((select_part_kernel<bf16_t, 64, 8, 8>), grid, dim3(kSelThreads), 0, s, a);
-      else
-        hipLaunchKernelGGL((select_part_kernel<bf16_t, 128, 16, 8>), grid, dim3(kSelThreads), 0, s, a);
-    } else {
-      if (c.D == 64)
-        hipLaunchKernelGGL((select_part_kernel<float, 64, 16, 8>), grid, dim3(kSelThreads), 0, s, a);
-      else
-        hipLaunchKernelGGL((select_part_kernel<float, 128, 16, 8>), grid, dim3(kSelThreads), 0, s, a);
-    }
-  } else {
-    if (c.kv_dtype == SA_BF16) {
-      if (c.D == 64)
-        hipLaunchKernelGGL((select_part_kernel<bf16_t, 64, 8, 4>), grid, dim3(kSelThreads), 0, s, a);
-      else
-        hipLaunchKernelGGL((select_part_kernel<bf16_t, 128, 16, 4>), grid, dim3(kSelThreads), 0, s, a);
-    } else {
-      if (c.D == 64)
-        hipLaunchKernelGGL((select_part_kernel<float, 64, 16, 4>), grid, dim3(kSelThreads), 0, s, a);
-      else
-        hipLaunchKernelGGL((select_part_kernel<float, 128, 16, 4>), grid, dim3(kSelThreads), 0, s, a);
-    }
-  }
+  if (p.L > 4096)
+    launch_part<8>(c, ix, a, grid, s);
+  else
+    launch_part<4>(c, ix, a, grid, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.P == 1) return e;
   return launch_topk_merge(a.cand_val, a.cand_pos, rows, p.C, p.cstride, kk, idx, s);
