@@ -23,7 +23,9 @@ Prints ONE JSON line.  `value` is the step's achieved HBM bandwidth
 sa_select call: its fused kernel and merge); `kernels` holds each unit's
 bytes, time and fraction of the 8 TB/s peak, including the gather-attend
 alone, the unfused selection (sa_score then sa_topk on the same inputs) and a
-dense decode over the same cache for comparison.  `cpu_baseline` times the
+dense decode over the same cache for comparison; `stream_read` is the
+device's streaming read rate (sa_stream_read over 8 GiB), and the step's and
+the dominant unit's rates are also given as fractions of it.  `cpu_baseline` times the
 CPU oracle on a bounded sample of the same step (rows of the batch), scaled
 to a full step.
 """
@@ -58,6 +60,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bound on the oracle's CPU time for cpu_baseline (0 disables)")
     p.add_argument("--dense-steps", type=int, default=20)
+    p.add_argument("--stream-gib", type=int, default=8,
+                   help="GiB read by sa_stream_read for the device's streaming read rate (0: skip)")
     p.add_argument("--eager", action="store_true",
                    help="time eager launches instead of replaying each step as a HIP graph")
     p.add_argument("--profile", action="store_true",
@@ -82,6 +86,11 @@ def parse():
                         "host memory; times the gather of the 24 selected blocks per row over the "
                         "host link against copying the whole layer, and a 3-layer reuse pipeline "
                         "that prefetches the next layer's blocks on a second stream; one JSON line")
+    p.add_argument("--nscale", action="store_true",
+                   help="context-length scaling at fixed k: the llama32k shape at 32K, 64K and "
+                        "128K tokens with k = 655; the gather-attend moves the same bytes at every "
+                        "N while selection and dense decode grow with N; prints a table and one "
+                        "JSON line")
     p.add_argument("--theta", type=float, default=0.35,
                    help="overlap threshold of the layer-reuse planner (--hylra)")
     p.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -452,6 +461,89 @@ def sweep(args):
                       "rows": results, "device": torch.cuda.get_device_name(0)}), flush=True)
 
 
+NSCALE_N = (32768, 65536, 131072)
+
+
+def nscale(args):
+    """Decode step at a fixed number of selected tokens as the context grows.
+
+    The llama32k shape (batch 16, 32/8 heads, d 128, bf16) with k = 655 at
+    N = 32K, 64K and 128K.  The gather-attend reads 2*B*Hkv*k*d*2 bytes at
+    every N (the sparse method's traffic does not grow with the context);
+    the exact selection reads every key once and dense decode every key and
+    value, so both grow linearly.  Values are N(0,1) drawn on the device:
+    only the sizes drive these timings."""
+    import torch
+    import top_sparse_decode_sa_amd as T
+
+    T.lib()
+    dev = torch.device("cuda", 0)
+    reps = max(3, min(args.steps, 10))
+    B, Hq, Hkv, d, k = 16, 32, 8, 128, 655
+    rows = []
+
+    def timed(fn, n, blocker=None):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        if blocker is not None:
+            blocker()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3  # us
+
+    for N in NSCALE_N:
+        log("nscale: N=%d" % N)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed)
+        q = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev).normal_(generator=gen)
+        kd = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=dev).normal_(generator=gen)
+        vd = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=dev).normal_(generator=gen)
+        idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+
+        def dense():
+            T.sa_dense_decode(q, kd, vd, out=out)
+
+        def select():
+            T.sa_select(q, kd, k, idx_out=idx)
+
+        def attend():
+            T.sa_sparse_decode(q, kd, vd, idx, out=out)
+
+        us_dense = timed(dense, reps)
+        us_sel = timed(select, reps, dense)
+        us_att = timed(attend, reps, dense)
+        us_step = timed(lambda: (select(), attend()), reps, dense)
+        att_bytes = 2 * B * Hkv * k * d * 2
+        key_bytes = B * Hkv * N * d * 2
+        rows.append({
+            "N": N, "k": k, "dense_us": round(us_dense, 1), "select_us": round(us_sel, 1),
+            "attend_us": round(us_att, 1), "step_us": round(us_step, 1),
+            "attend_bytes": att_bytes, "attend_gbps": round(att_bytes / us_att / 1e3, 1),
+            "select_key_bytes": key_bytes, "select_gbps": round(key_bytes / us_sel / 1e3, 1),
+            "select_fused": select_fused(B * Hkv, N, k),
+            "dense_gbps": round(2 * key_bytes / us_dense / 1e3, 1),
+            "step_speedup": round(us_dense / us_step, 2)})
+        del q, kd, vd, idx, out
+        torch.cuda.empty_cache()
+
+    cols = ["N", "k", "dense_us", "select_us", "attend_us", "step_us", "attend_gbps",
+            "select_gbps", "dense_gbps", "select_fused", "step_speedup"]
+    print("  ".join("%12s" % c_ for c_ in cols))
+    for r in rows:
+        print("  ".join("%12s" % r[c_] for c_ in cols))
+    print(json.dumps({"bench": "context-length scaling at fixed k", "unit": "us (HIP events)",
+                      "config": {"workload": "llama32k shape at N = 32K, 64K, 128K, k = 655",
+                                 "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d},
+                      "rows": rows, "data": "N(0,1) drawn on the device (seed %d)" % args.seed,
+                      "device": torch.cuda.get_device_name(0)}), flush=True)
+
+
 def hylra(args):
     """Layer-reuse policy on 8 layers of the llama32k shape.
 
@@ -698,6 +790,9 @@ def main():
     if args.gpus == 1 and args.sweep:
         sweep(args)
         return
+    if args.gpus == 1 and args.nscale:
+        nscale(args)
+        return
     if args.gpus == 1 and args.hylra:
         hylra(args)
         return
@@ -711,7 +806,7 @@ def main():
     if args.profile:
         # plain launches (no graph capture) under the profiler
         args.steps, args.warmup, args.cpu_seconds, args.dense_steps = 20, 5, 0.0, 0
-        args.cold_iters, args.eager = 0, True
+        args.cold_iters, args.eager, args.stream_gib = 0, True, 0
 
     import torch
     import sa_synth as S
@@ -846,6 +941,28 @@ def main():
         torch.cuda.synchronize()
         ms_dense = e0.elapsed_time(e1) / args.dense_steps
 
+    # the device's streaming read rate (sa_stream_read over 8 GiB): the
+    # reference the rates above are also read against
+    stream = None
+    if args.stream_gib > 0:
+        nbytes_s = args.stream_gib << 30
+        buf = torch.empty(nbytes_s, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        for _ in range(2):
+            T.sa_stream_read(buf, sink)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            T.sa_stream_read(buf, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        us_s = e0.elapsed_time(e1) / 5 * 1e3
+        stream = {"bytes": nbytes_s, "us": round(us_s, 1), "gbps": round(nbytes_s / us_s / 1e3, 1),
+                  "frac": round(nbytes_s / us_s / 1e3 / HBM_PEAK_GBPS, 4)}
+        del buf, sink
+        torch.cuda.empty_cache()
+
     # cache-cold gather-attend: before each launch a 1 GiB read evicts L2 and
     # the 256 MB last-level cache, as other layers' traffic would between
     # decode steps; beside it, the same kernel over the same number of bytes
@@ -897,6 +1014,8 @@ def main():
             "frac": kernels[dom]["frac"],
             "traffic": read_traffic(dom), "kernel": dom,
             "bytes_per_launch": nbytes[dom]}
+    if stream:
+        roof["frac_of_stream_read"] = round(kernels[dom]["gbps"] / stream["gbps"], 4)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -933,6 +1052,8 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "sparse_over_dense_speedup": (round(ms_dense / ms_attend, 2) if ms_dense else None),
+        "stream_read": stream,
+        "value_frac_of_stream_read": (round(gbps / stream["gbps"], 4) if stream else None),
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0),
         "hip": torch.version.hip,

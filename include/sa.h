@@ -375,6 +375,17 @@ const char* sa_last_error(void);
 /* Library version string. */
 const char* sa_version(void);
 
+/* ------------------------------------------------------------ measurement */
+
+/* Not a step of the method: a plain streaming read of `bytes` (a positive
+ * multiple of 16) of device memory at `data` (16-byte aligned), 16-byte
+ * nontemporal loads from 4096 workgroups reading contiguous chunks, folded
+ * so they cannot be removed (`sink`, one uint32, is written only if the fold
+ * hits a fixed constant).  Its duration gives the HBM read rate this device
+ * reaches, the reference the kernels' rates are compared with.
+ * Errors: SA_ERR_NULL / SA_ERR_ALIGN for data, sink; SA_ERR_SHAPE for bytes. */
+sa_status sa_stream_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -170,6 +170,16 @@ def test_select_errors_and_sizes():
     assert sel(desc=one, kk=100, idx=None) == Bn.SA_ERR_NULL
 
 
+def test_stream_read_errors():
+    L = T.lib()
+    sink = FAKE
+    assert L.sa_stream_read(None, 4096, sink, None) == Bn.SA_ERR_NULL
+    assert L.sa_stream_read(ctypes.c_void_p((1 << 20) + 8), 4096, sink, None) == Bn.SA_ERR_ALIGN
+    assert L.sa_stream_read(FAKE, 4096, None, None) == Bn.SA_ERR_NULL
+    assert L.sa_stream_read(FAKE, 0, sink, None) == Bn.SA_ERR_SHAPE
+    assert L.sa_stream_read(FAKE, 4100, sink, None) == Bn.SA_ERR_SHAPE
+
+
 def test_score_and_summary_errors():
     L = T.lib()
     d = _desc()

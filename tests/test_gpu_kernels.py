@@ -506,3 +506,23 @@ def test_gather_blocks_refuses_pageable_memory_and_clamps_ids():
         want = torch.cat([kc[0, r, min(max(j, 0), nb - 1) * bs:(min(max(j, 0), nb - 1) + 1) * bs]
                           for j in ids[r]])
         assert torch.equal(kg[0, r], want)
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, (1 << 20) + 48, 64 << 20])
+def test_stream_read_covers_every_word(nbytes):
+    """The streaming read folds every 32-bit word it loads and writes the
+    fold only when it equals 0x9e3779b9; with one such word in a zero buffer
+    the sink is written wherever the word sits (first, middle, last), so no
+    part of the buffer goes unread, and a zero buffer leaves it alone."""
+    say("stream read %d bytes" % nbytes)
+    marker = np.uint32(0x9E3779B9).view(np.int32)
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device=dev())
+    sink = torch.zeros(1, dtype=torch.int32, device=dev())
+    T.sa_stream_read(buf, sink)
+    assert int(sink.item()) == 0
+    for w in sorted({0, nbytes // 8, nbytes // 4 - 1}):
+        buf.zero_()
+        buf[w] = int(marker)
+        sink.zero_()
+        T.sa_stream_read(buf, sink)
+        assert int(sink.item()) == int(marker), w

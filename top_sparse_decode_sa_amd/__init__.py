@@ -12,7 +12,7 @@ from ._binding import (  # noqa: F401
     WORKSPACES, KVDesc, LayerArgs, SAError, ScoreAux, layer_args, lib, make_desc,
     sa_block_summarize, sa_decode_layer, sa_dense_decode, sa_dense_decode_scored, sa_gather_blocks,
     sa_index_overlap, sa_layer_workspace_size, sa_plan_fixed_jump, sa_plan_reuse,
-    sa_plan_validate, sa_score, sa_select, sa_sparse_decode, sa_topk, sa_version,
-    sa_workspace_init)
+    sa_plan_validate, sa_score, sa_select, sa_sparse_decode, sa_stream_read, sa_topk,
+    sa_version, sa_workspace_init)
 
 __version__ = "0.1.0"

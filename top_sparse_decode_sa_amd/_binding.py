@@ -36,7 +36,8 @@ EXPORTED = [
     "sa_sparse_workspace_size", "sa_dense_decode", "sa_dense_workspace_size",
     "sa_dense_decode_scored", "sa_dense_scored_workspace_size", "sa_decode_layer",
     "sa_layer_workspace_size", "sa_plan_validate", "sa_index_overlap", "sa_plan_reuse",
-    "sa_plan_fixed_jump", "sa_gather_blocks", "sa_workspace_init", "sa_status_string", "sa_last_error", "sa_version",
+    "sa_plan_fixed_jump", "sa_gather_blocks", "sa_workspace_init", "sa_stream_read",
+    "sa_status_string", "sa_last_error", "sa_version",
 ]
 
 
@@ -86,6 +87,7 @@ def lib() -> ctypes.CDLL:
     L.sa_select.argtypes = [P(KVDesc), st, vp, vp, P(ScoreAux), i32, vp, vp, sz, vp]
     L.sa_select_workspace_size.argtypes = [P(KVDesc), st, i32]
     L.sa_select_workspace_size.restype = sz
+    L.sa_stream_read.argtypes = [vp, sz, vp, vp]
     L.sa_sparse_decode.argtypes = [P(KVDesc), vp, vp, vp, st, vp, i32, i32, vp, vp, sz, vp]
     L.sa_sparse_workspace_size.argtypes = [P(KVDesc), st, i32, i32]
     L.sa_sparse_workspace_size.restype = sz
@@ -113,7 +115,7 @@ def lib() -> ctypes.CDLL:
                  "sa_dense_decode",
                  "sa_dense_decode_scored", "sa_decode_layer", "sa_plan_validate",
                  "sa_index_overlap", "sa_plan_reuse", "sa_plan_fixed_jump", "sa_gather_blocks",
-                 "sa_workspace_init"]:
+                 "sa_workspace_init", "sa_stream_read"]:
         getattr(L, name).restype = st
     _lib = L
     return L
@@ -291,6 +293,14 @@ def sa_select(q, k_cache, k, kind=SA_SCORE_EXACT, idx_out=None, softmax_scale=0.
     check(L.sa_select(ctypes.byref(desc), kind, _ptr(q), _ptr(k_cache), ctypes.byref(aux), k,
                       _ptr(idx_out), _ptr(ws), nbytes, ctypes.c_void_p(_stream(dev))))
     return idx_out
+
+
+def sa_stream_read(data, sink):
+    """sa_stream_read: a plain streaming read of a device tensor (measurement
+    reference, not a step of the method)."""
+    dev = _dev(data, sink)
+    check(lib().sa_stream_read(_ptr(data), data.numel() * data.element_size(), _ptr(sink),
+                               ctypes.c_void_p(_stream(dev))))
 
 
 def sa_topk(scores, k, idx_out=None):

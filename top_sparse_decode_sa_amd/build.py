@@ -17,7 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsa.so")
-SOURCES = ["api.hip", "attend.hip", "offload.hip", "score.hip", "select.hip", "topk.hip"]
+SOURCES = ["api.hip", "attend.hip", "offload.hip", "score.hip", "select.hip", "stream.hip",
+           "topk.hip"]
 ARCH = "gfx950"
 
 

@@ -653,6 +653,15 @@ sa_status sa_gather_blocks(const sa_kv_desc* desc, const void* k_host, const voi
       "sa_gather_blocks launch");
 }
 
+sa_status sa_stream_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  sa_status st;
+  if ((st = check_ptr(data, "data", 16)) != SA_OK) return st;
+  if ((st = check_ptr(sink, "sink", 4)) != SA_OK) return st;
+  if (bytes == 0 || bytes % 16)
+    return fail(SA_ERR_SHAPE, "bytes %zu must be a positive multiple of 16", bytes);
+  return hip_status(launch_stream_read(data, bytes, sink, stream), "sa_stream_read launch");
+}
+
 sa_status sa_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t n_rows, int32_t k,
                            int32_t* counts, hipStream_t stream) {
   sa_status st;

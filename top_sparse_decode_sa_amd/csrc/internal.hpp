@@ -123,6 +123,10 @@ hipError_t launch_gather_blocks(const Cache& c, const void* k_dev, const void* v
                                 const int32_t* idx, int32_t n_blk, int32_t bs, void* k_out,
                                 void* v_out, hipStream_t s);
 
+// --------------------------------------------------------- measurement
+// A plain streaming read of `bytes` (a multiple of 16) of device memory.
+hipError_t launch_stream_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t s);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace sa
