@@ -91,6 +91,11 @@ def parse():
                         "128K tokens with k = 655; the gather-attend moves the same bytes at every "
                         "N while selection and dense decode grow with N; prints a table and one "
                         "JSON line")
+    p.add_argument("--indexer1m", action="store_true",
+                   help="one 1M-token sequence over 8 layers (32/8 heads, d 128, bf16): layers 0-1 "
+                        "dense, layers 2-7 select 2048 tokens shared by the KV heads with a 4-head "
+                        "64-dim indexer; times the mixed 8-layer step against all-dense and each "
+                        "sparse layer's launches; prints a table and one JSON line")
     p.add_argument("--theta", type=float, default=0.35,
                    help="overlap threshold of the layer-reuse planner (--hylra)")
     p.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -544,6 +549,104 @@ def nscale(args):
                       "device": torch.cuda.get_device_name(0)}), flush=True)
 
 
+def indexer1m(args):
+    """The indexer1m workload: batch 1, 32/8 heads, d 128, bf16, 1048576
+    tokens, 8 layers; layers 0-1 DENSE, layers 2-7 SPARSE with the shared
+    lightning indexer (4 heads of 64 dims, top-2048 shared by the 8 KV
+    heads).  One 8-layer step is timed under the mixed plan and all-dense;
+    one sparse layer is timed whole and call by call (indexer scores, top-k
+    of the one 1M-score row, gather-attend).  Values are N(0,1) (weights
+    U(0,1)) drawn on the device: the timings depend on the sizes."""
+    import torch
+    import sa_synth as S
+    import top_sparse_decode_sa_amd as T
+
+    T.lib()
+    dev = torch.device("cuda", 0)
+    c = S.CONFIGS["indexer1m"]
+    B, Hq, Hkv, d, N, k, L = c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.ctx_len, c.k, c.n_layers
+    H, Di = c.indexer_heads, c.indexer_dim
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    log("indexer1m: drawing %d layers (%.1f GB of KV)" % (L, L * c.kv_bytes() / 1e9))
+
+    def bf(shape):
+        return torch.empty(shape, dtype=torch.bfloat16, device=dev).normal_(generator=gen)
+
+    qs = [bf((B, Hq, d)) for _ in range(L)]
+    ks = [bf((B, Hkv, N, d)) for _ in range(L)]
+    vs = [bf((B, Hkv, N, d)) for _ in range(L)]
+    qi = [bf((B, H, Di)) for _ in range(L)]
+    ki = [bf((B, N, Di)) for _ in range(L)]
+    wi = [torch.rand((B, H), generator=gen, device=dev) for _ in range(L)]
+    outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(L)]
+    largs = [T.layer_args(qs[l], ks[l], vs[l], T.SA_SCORE_INDEXER, k, q_idx=qi[l], k_idx=ki[l],
+                          idx_w=wi[l], out=outs[l])[0] for l in range(L)]
+    ws = {m: T.WORKSPACES.get(dev, ("indexer1m", m), T.sa_layer_workspace_size(largs[0], m))
+          for m in (T.SA_LAYER_DENSE, T.SA_LAYER_SPARSE)}
+    idx = [torch.empty((B, k), dtype=torch.int32, device=dev) for _ in range(L)]
+    mixed = [T.SA_LAYER_DENSE if m == "dense" else T.SA_LAYER_SPARSE for m in c.modes]
+    T.sa_plan_validate(mixed, list(c.src))
+    reps = max(3, min(args.steps, 10))
+
+    def layer(l, m):
+        T.sa_decode_layer(largs[l], m, None if m == T.SA_LAYER_DENSE else idx[l], dev, ws[m])
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        layer(0, T.SA_LAYER_DENSE)  # queued ahead, so the host enqueues the rest in time
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3  # us
+
+    us_mixed = timed(lambda: [layer(l, mixed[l]) for l in range(L)], reps)
+    us_dense8 = timed(lambda: [layer(l, T.SA_LAYER_DENSE) for l in range(L)], reps)
+    us_dense = timed(lambda: layer(2, T.SA_LAYER_DENSE), reps)
+    us_sparse = timed(lambda: layer(2, T.SA_LAYER_SPARSE), reps)
+    scores = torch.empty((B, N), dtype=torch.float32, device=dev)
+    sel = torch.empty((B, k), dtype=torch.int32, device=dev)
+    us_score = timed(lambda: T.sa_score(qs[2], ks[2], T.SA_SCORE_INDEXER, q_idx=qi[2], k_idx=ki[2],
+                                        idx_w=wi[2], scores=scores), reps)
+    us_topk = timed(lambda: T.sa_topk(scores, k, idx_out=sel), reps)
+    us_attend = timed(lambda: T.sa_sparse_decode(qs[2], ks[2], vs[2], sel, out=outs[2],
+                                                 index_kind=T.SA_IDX_TOKEN_SHARED), reps)
+    # the layer's own selection equals the calls' one
+    layer(2, T.SA_LAYER_SPARSE)
+    torch.cuda.synchronize()
+    assert torch.equal(idx[2], sel), "sparse layer and its calls selected differently"
+    dense_bytes = 2 * B * Hkv * N * d * 2
+    score_bytes = B * N * Di * 2 + B * N * 4
+    gather_bytes = 2 * B * Hkv * k * d * 2
+    res = {
+        "bench": "indexer1m: mixed 8-layer decode step", "unit": "us (HIP events)",
+        "config": {"workload": "indexer1m: batch 1, 32/8 heads, d 128, bf16, 1048576 tokens, 8 layers "
+                               "(2 dense, 6 sparse with a 4x64 shared indexer, top-2048)",
+                   "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d, "ctx_len": N,
+                   "k": k, "indexer_heads": H, "indexer_dim": Di, "modes": list(c.modes)},
+        "mixed_step_us": round(us_mixed, 1), "all_dense_step_us": round(us_dense8, 1),
+        "mixed_speedup_vs_all_dense": round(us_dense8 / us_mixed, 2),
+        "dense_layer_us": round(us_dense, 1), "dense_layer_bytes": dense_bytes,
+        "dense_layer_gbps": round(dense_bytes / us_dense / 1e3, 1),
+        "sparse_layer_us": round(us_sparse, 1),
+        "indexer_score_us": round(us_score, 1), "indexer_score_bytes": score_bytes,
+        "indexer_score_gbps": round(score_bytes / us_score / 1e3, 1),
+        "topk_us": round(us_topk, 1), "attend_us": round(us_attend, 1),
+        "attend_bytes": gather_bytes, "attend_gbps": round(gather_bytes / us_attend / 1e3, 1),
+        "data": "N(0,1) drawn on the device (seed %d)" % args.seed,
+        "device": torch.cuda.get_device_name(0)}
+    for key in ("mixed_step_us", "all_dense_step_us", "mixed_speedup_vs_all_dense", "dense_layer_us",
+                "dense_layer_gbps", "sparse_layer_us", "indexer_score_us", "indexer_score_gbps",
+                "topk_us", "attend_us", "attend_gbps"):
+        print("%28s  %s" % (key, res[key]))
+    print(json.dumps(res), flush=True)
+
+
 def hylra(args):
     """Layer-reuse policy on 8 layers of the llama32k shape.
 
@@ -789,6 +892,9 @@ def main():
         return
     if args.gpus == 1 and args.sweep:
         sweep(args)
+        return
+    if args.gpus == 1 and args.indexer1m:
+        indexer1m(args)
         return
     if args.gpus == 1 and args.nscale:
         nscale(args)

@@ -526,3 +526,38 @@ def test_stream_read_covers_every_word(nbytes):
         sink.zero_()
         T.sa_stream_read(buf, sink)
         assert int(sink.item()) == int(marker), w
+
+
+@pytest.mark.parametrize("N,dtype,want_splits,want_sparse",
+                         [(25677, "bf16", 101, 313), (51277, "bf16", 201, 313),
+                          (153677, "bf16", 301, 313), (40000, "f32", 625, 625)])
+def test_combine_across_split_counts(N, dtype, want_splits, want_sparse):
+    """Few rows over a long context split into 101, 201, 301 and 625
+    partials per row (the combine's 8-, 16- and 32-lane variants, the last in
+    two rounds of loads, each with a ragged last split); dense decode and a
+    20000-token selection (bf16: 313 one-wave partials in the interleaved
+    layout) against the oracle."""
+    from top_sparse_decode_sa_amd import _binding as Bn
+    import ctypes
+    say("combine N=%d %s" % (N, dtype))
+    B, Hkv, G, d = 1, 2, 4, 128
+    q, k, v = _rand_cache(B, Hkv * G, Hkv, N, d, dtype, N)
+    qd, kd, vd = q.to(dev()), k.to(dev()), v.to(dev())
+    desc = Bn.make_desc(qd, kd)
+    ws = int(T.lib().sa_dense_workspace_size(ctypes.byref(desc)))
+    def padded(splits):  # partials [rows, nsplit, G, d + 2] fp32, in 256-byte units
+        return -(-B * Hkv * splits * G * (d + 2) * 4 // 256) * 256
+
+    assert ws == padded(want_splits)
+    qf, kf, vf = _f64(q), _f64(k), _f64(v)
+    scale = O.default_scale(d)
+    dense = T.sa_dense_decode(qd, kd, vd).cpu().numpy()
+    check_out(dense, _oracle_out(qf, kf, vf, [[np.arange(N)] * Hkv], G, scale), dtype, "dense")
+    rng = np.random.default_rng(N + 1)
+    sets = [np.sort(rng.choice(N, 20000, replace=False)).astype(np.int32) for _ in range(Hkv)]
+    idx = torch.from_numpy(np.stack(sets)[None]).to(dev())
+    ws_s = int(T.lib().sa_sparse_workspace_size(ctypes.byref(desc), T.SA_IDX_TOKEN_PER_KV_HEAD,
+                                                20000, 0))
+    assert ws_s == padded(want_sparse)
+    sparse = T.sa_sparse_decode(qd, kd, vd, idx).cpu().numpy()
+    check_out(sparse, _oracle_out(qf, kf, vf, [sets], G, scale), dtype, "sparse 20000")

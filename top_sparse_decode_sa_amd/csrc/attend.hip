@@ -589,29 +589,36 @@ __global__ __launch_bounds__(64 * max_waves<MODE>()) void attend_sparse_kernel(A
 
 
 // ---------------------------------------------------------------------------
-// Combine: one workgroup of D threads per (row, query head); thread = one
-// output dimension.  Sixteen splits' (o, m, l) are loaded at a time, all
-// independent, and merged with a running log-sum-exp.
-template <int D>
-__global__ __launch_bounds__(D) void combine_kernel(const float* __restrict__ part, int nsplit,
-                                                    int G, int Hq, int Hkv, float* __restrict__ out,
-                                                    bool vec_layout) {
+// Combine: the nsplit partials (o, m, l) of one (row, query head) merged
+// with a log-sum-exp.  A workgroup covers 32 output dimensions of one
+// (row, head) with SL lanes per dimension: lane j merges splits j, j + SL,
+// j + 2 SL, ..., sixteen at a time with all their loads independent, so a
+// row of 512 splits is one round of loads at SL = 32 instead of 32 rounds
+// one after another; the SL running (m, l, o) are then merged in LDS.
+template <int SL>
+__global__ __launch_bounds__(32 * SL) void combine_kernel(const float* __restrict__ part, int nsplit,
+                                                         int G, int D, int Hq, int Hkv,
+                                                         float* __restrict__ out, bool vec_layout) {
   constexpr int K = 16;
+  __shared__ float s_m[SL][32], s_l[SL][32], s_o[SL][32];
   const int row = blockIdx.x;
   const int h = blockIdx.y;
-  const int dim = threadIdx.x;
+  const int lane = threadIdx.x & 31;
+  const int j = threadIdx.x >> 5;
+  const int dim = blockIdx.z * 32 + lane;
   const int PS = G * (D + 2);
   const float* pr = part + (int64_t)row * nsplit * PS;
   // where dim lives inside a partial's head block: dim itself, or (sparse
   // one-wave kernel) [half][n][4] with dim = 8n + 4 half + j
   const int pos = vec_layout ? ((dim & 7) >> 2) * 64 + (dim >> 3) * 4 + (dim & 3) : dim;
   float M = -INFINITY, L = 0.0f, O = 0.0f;
-  for (int s0 = 0; s0 < nsplit; s0 += K) {
+  for (int s0 = j; s0 < nsplit; s0 += K * SL) {
     float ov[K], mv[K], lv[K];
 #pragma unroll
     for (int u = 0; u < K; ++u) {
-      const bool ok = s0 + u < nsplit;
-      const float* ps = pr + (int64_t)(s0 + u) * PS;
+      const int sp = s0 + u * SL;
+      const bool ok = sp < nsplit;
+      const float* ps = pr + (int64_t)sp * PS;
       ov[u] = ok ? ps[h * D + pos] : 0.0f;
       mv[u] = ok ? ps[G * D + h] : -INFINITY;
       lv[u] = ok ? ps[G * D + G + h] : 0.0f;
@@ -631,9 +638,26 @@ __global__ __launch_bounds__(D) void combine_kernel(const float* __restrict__ pa
     }
     M = mn;
   }
+  s_m[j][lane] = M;
+  s_l[j][lane] = L;
+  s_o[j][lane] = O;
+  __syncthreads();
+  if (j != 0) return;
+  float mn = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < SL; ++i) mn = fmaxf(mn, s_m[i][lane]);
+  float Lt = 0.0f, Ot = 0.0f;
+  if (mn != -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < SL; ++i) {
+      const float w = exp2f(s_m[i][lane] - mn);
+      Lt = fmaf(s_l[i][lane], w, Lt);
+      Ot = fmaf(s_o[i][lane], w, Ot);
+    }
+  }
   const int b = row / Hkv;
   const int r = row % Hkv;
-  out[((int64_t)b * Hq + (int64_t)r * G + h) * D + dim] = O / L;
+  out[((int64_t)b * Hq + (int64_t)r * G + h) * D + dim] = Ot / Lt;
 }
 
 // ---------------------------------------------------------------------------
@@ -868,15 +892,23 @@ hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, con
                   : dispatch_group<float, 128>(c.G, p.mode, grid, a, s);
   }
   if (e != hipSuccess || p.nsplit == 1) return e;
-  const dim3 cgrid((unsigned)rows, (unsigned)c.G);
+  const dim3 cgrid((unsigned)rows, (unsigned)c.G, (unsigned)(c.D / 32));
   // one-wave selected-set workgroups write the interleaved partial layout
   const bool vec_layout = use_wave_kernel(c) && p.waves == 1;
-  if (c.D == 64)
-    hipLaunchKernelGGL(combine_kernel<64>, cgrid, dim3(64), 0, s, a.part, p.nsplit, c.G, c.Hq, c.Hkv,
-                       out, vec_layout);
-  else
-    hipLaunchKernelGGL(combine_kernel<128>, cgrid, dim3(128), 0, s, a.part, p.nsplit, c.G, c.Hq,
+  // the fewest lanes per dimension that cover the splits in one round of
+  // sixteen loads (at most 32)
+  if (p.nsplit <= 64)
+    hipLaunchKernelGGL(combine_kernel<4>, cgrid, dim3(128), 0, s, a.part, p.nsplit, c.G, c.D, c.Hq,
                        c.Hkv, out, vec_layout);
+  else if (p.nsplit <= 128)
+    hipLaunchKernelGGL(combine_kernel<8>, cgrid, dim3(256), 0, s, a.part, p.nsplit, c.G, c.D, c.Hq,
+                       c.Hkv, out, vec_layout);
+  else if (p.nsplit <= 256)
+    hipLaunchKernelGGL(combine_kernel<16>, cgrid, dim3(512), 0, s, a.part, p.nsplit, c.G, c.D, c.Hq,
+                       c.Hkv, out, vec_layout);
+  else
+    hipLaunchKernelGGL(combine_kernel<32>, cgrid, dim3(1024), 0, s, a.part, p.nsplit, c.G, c.D,
+                       c.Hq, c.Hkv, out, vec_layout);
   return hipGetLastError();
 }
 
