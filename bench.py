@@ -136,15 +136,21 @@ def source_hash(paths):
 
 
 def summarize(db_path):
-    """Per-kernel dispatch count and duration stats; with counter data, the
-    per-dispatch mean of each counter."""
+    """Per-kernel dispatch count and duration stats (mean, min, max, median,
+    p10, p90); with counter data, the per-dispatch mean of each counter."""
     import sqlite3
     db = sqlite3.connect(db_path)
     rows = db.execute("select name, count(*), avg(end-start), min(end-start), max(end-start) "
                       "from kernels group by name order by sum(end-start) desc").fetchall()
-    lines = ["%-70s %6s %10s %10s %10s" % ("kernel", "calls", "avg_us", "min_us", "max_us")]
+    durs = {}
+    for name, dt in db.execute("select name, end-start from kernels"):
+        durs.setdefault(name, []).append(dt)
+    lines = ["%-70s %6s %10s %10s %10s %10s %10s %10s" % (
+        "kernel", "calls", "avg_us", "min_us", "max_us", "median_us", "p10_us", "p90_us")]
     for name, n, avg, mn, mx in rows:
-        lines.append("%-70s %6d %10.2f %10.2f %10.2f" % (name[:70], n, avg / 1e3, mn / 1e3, mx / 1e3))
+        med, p10, p90 = np.percentile(np.asarray(durs[name], dtype=np.float64), [50, 10, 90])
+        lines.append("%-70s %6d %10.2f %10.2f %10.2f %10.2f %10.2f %10.2f" % (
+            name[:70], n, avg / 1e3, mn / 1e3, mx / 1e3, med / 1e3, p10 / 1e3, p90 / 1e3))
     try:
         pmc = db.execute("select kernel_name, counter_name, avg(value), count(*) "
                          "from counters_collection group by kernel_name, counter_name").fetchall()
@@ -158,6 +164,41 @@ def summarize(db_path):
             lines.append("%-70s %-14s %16.1f %6d" % (name[:70], cname, val, n))
             counters[(name, cname)] = val
     return "\n".join(lines), rows, counters
+
+
+def provenance(clocks=False):
+    """What the numbers were measured on: device name, gfx target, compute
+    units, HBM size, HIP version and, if asked, the current clocks as
+    rocm-smi reports them (best effort: absent if the tool is not there)."""
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    out = {"device": torch.cuda.get_device_name(0), "gfx": getattr(pr, "gcnArchName", None),
+           "compute_units": pr.multi_processor_count,
+           "hbm_gib": round(pr.total_memory / 2 ** 30, 1), "hip": torch.version.hip}
+    if clocks:
+        import subprocess
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                               text=True, timeout=30)
+            card = next(iter(json.loads(r.stdout).values()))
+            out["clocks"] = {k_: v_ for k_, v_ in card.items() if "clk" in k_.lower()}
+        except Exception as e:  # the tool is absent or printed no JSON
+            out["clocks"] = "unavailable (%s)" % type(e).__name__
+    return out
+
+
+def host_cpu():
+    """Host CPU model name and logical CPU count."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "host_cpus": os.cpu_count()}
 
 
 def pmc_means(db_path, counter):
@@ -463,7 +504,7 @@ def sweep(args):
     for r in results:
         print("  ".join("%12s" % r[c_] for c_ in cols))
     print(json.dumps({"sweep": "indexer-inclusive break-even", "unit": "us per step (HIP events)",
-                      "rows": results, "device": torch.cuda.get_device_name(0)}), flush=True)
+                      "rows": results, "provenance": provenance()}), flush=True)
 
 
 NSCALE_N = (32768, 65536, 131072)
@@ -546,7 +587,7 @@ def nscale(args):
                       "config": {"workload": "llama32k shape at N = 32K, 64K, 128K, k = 655",
                                  "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d},
                       "rows": rows, "data": "N(0,1) drawn on the device (seed %d)" % args.seed,
-                      "device": torch.cuda.get_device_name(0)}), flush=True)
+                      "provenance": provenance()}), flush=True)
 
 
 def indexer1m(args):
@@ -639,7 +680,7 @@ def indexer1m(args):
         "topk_us": round(us_topk, 1), "attend_us": round(us_attend, 1),
         "attend_bytes": gather_bytes, "attend_gbps": round(gather_bytes / us_attend / 1e3, 1),
         "data": "N(0,1) drawn on the device (seed %d)" % args.seed,
-        "device": torch.cuda.get_device_name(0)}
+        "provenance": provenance()}
     for key in ("mixed_step_us", "all_dense_step_us", "mixed_speedup_vs_all_dense", "dense_layer_us",
                 "dense_layer_gbps", "sparse_layer_us", "indexer_score_us", "indexer_score_gbps",
                 "topk_us", "attend_us", "attend_gbps"):
@@ -768,7 +809,7 @@ def hylra(args):
         "overlap_ratio": [[round(float(x), 4) for x in row] for row in ratio],
         "plans": res, "us_per_layer": per_layer,
         "data": "drawn on the device (torch generator, seed %d)" % args.seed,
-        "device": torch.cuda.get_device_name(0)}), flush=True)
+        "provenance": provenance()}), flush=True)
 
 
 def offload(args):
@@ -878,7 +919,7 @@ def offload(args):
         "per_layer_speedup_vs_full_copy": round(us_full / (us_gather + us_attend), 2),
         "reuse_pipeline_3_layers_us": round(us_pipe, 1),
         "data": "drawn on the device (torch generator, seed %d)" % args.seed,
-        "device": torch.cuda.get_device_name(0)}
+        "provenance": provenance()}
     print(json.dumps(res), flush=True)
 
 
@@ -1132,6 +1173,7 @@ def main():
                "sample": "fp64 numpy oracle, one thread: score+top-k+attend of %d of the %d "
                          "(sequence, KV head) rows of one step, scaled by %d/%d" % (
                              done, total, total, done)}
+        cpu.update(host_cpu())
 
     line = {
         "metric": "sparse-decode attn: achieved HBM GB/s (% of peak) + decode steps/s at 50x",
@@ -1161,8 +1203,7 @@ def main():
         "stream_read": stream,
         "value_frac_of_stream_read": (round(gbps / stream["gbps"], 4) if stream else None),
         "cpu_baseline": cpu,
-        "device": torch.cuda.get_device_name(0),
-        "hip": torch.version.hip,
+        "provenance": provenance(clocks=not args.profile),
     }
     print(json.dumps(line), flush=True)
 

@@ -251,7 +251,12 @@ size_t sa_dense_scored_workspace_size(const sa_kv_desc* desc);
 
 typedef enum {
   SA_LAYER_DENSE = 0,  /* full attention; idx untouched */
-  SA_LAYER_SPARSE = 1, /* score -> top-k -> selected-set attention; WRITES idx */
+  SA_LAYER_SPARSE = 1, /* score -> top-k -> selected-set attention; WRITES idx.
+                        * With exact or per-KV-head indexer scores the
+                        * selection is sa_select's; when its candidates are
+                        * merged and a row's attention fits one workgroup the
+                        * merge and the attention run in one launch (the same
+                        * idx and out as the separate calls). */
   SA_LAYER_REUSE = 2,  /* selected-set attention over idx as given; READS idx */
   SA_LAYER_DENSE_SELECT = 3 /* full attention + top-k of its exact scores; WRITES idx */
 } sa_layer_mode;

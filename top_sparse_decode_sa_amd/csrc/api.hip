@@ -577,13 +577,18 @@ sa_status sa_decode_layer(const sa_layer_args* a, sa_layer_mode mode, int32_t* i
   const Cache v = attend_view(c, ik);
   const AttendPlan p = plan_attend(v, mode_of(ik), a->k, bs);
   if (mode == SA_LAYER_SPARSE && selectable(a->score_kind)) {
+    // the gather-attend runs in the selection's merge launch when the plans
+    // allow it (merge_attend_ok), else after it
     const Cache sv = select_view(c, a->score_kind);
     SelectIndexer ixb;
+    const MergeAttend ma{v, p, a->q, a->k_cache, a->v_cache, a->out};
+    bool attended = false;
     if ((st = hip_status(launch_select(sv, plan_select(sv, a->k), a->q, a->k_cache,
                                        select_indexer(a->score_kind, &a->aux, &ixb), a->k, idx,
-                                       base, stream),
+                                       base, stream, &ma, &attended),
                          "sa_decode_layer selection launch")) != SA_OK)
       return st;
+    if (attended) return SA_OK;
   } else if (mode == SA_LAYER_SPARSE) {
     if ((st = do_score(c, a->score_kind, a->q, a->k_cache, &a->aux, scores, stream)) != SA_OK)
       return st;

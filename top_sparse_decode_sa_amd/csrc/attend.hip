@@ -41,6 +41,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "topk_core.hpp"
 
 namespace sa {
 namespace {
@@ -259,12 +260,14 @@ __device__ __forceinline__ float wave_bcast0(float x) {
 // past the selection: the load is always made at an in-range position (the
 // last slot, the last token) and `ok` reports whether the slot is real.  No
 // load sits under a branch, so the wave's loads stay in flight together.
-template <int MODE>
+template <int MODE, bool LIDX = false>
 __device__ __forceinline__ int32_t slot_token(const AttendArgs& a, int row, int b, int64_t j,
-                                              int64_t s1, bool& ok) {
+                                              int64_t s1, bool& ok, const int32_t* lidx = nullptr) {
   ok = j < s1;
   const int64_t jj = ok ? j : s1 - 1;
-  if constexpr (MODE == kIdxDense || MODE == kIdxDenseScored) {
+  if constexpr (LIDX) {
+    return lidx[jj];  // the row's index list, already in LDS
+  } else if constexpr (MODE == kIdxDense || MODE == kIdxDenseScored) {
     return (int32_t)jj;
   } else if constexpr (MODE == kIdxTokenPerHead) {
     return a.idx[(int64_t)row * a.n_idx + jj];
@@ -305,16 +308,27 @@ constexpr int max_waves() {
   return MODE == kIdxDenseScored ? kMaxScoredWaves : kMaxSparseWaves;
 }
 
-template <int G, int MODE, int TILES>
-__global__ __launch_bounds__(64 * max_waves<MODE>()) void attend_sparse_kernel(AttendArgs a) {
+// LDS of one gather-attend workgroup: p of slot 16i + 4u + g for head h at
+// s_pa[wave][h][i][g][u] (the MFMA A-fragment order of the P.V product), and
+// each wave's (o, m, l) for the merge of the waves.
+template <int G, int TILES>
+struct AttendLds {
+  alignas(16) float s_pa[kMaxSparseWaves][G][TILES][4][4];
+  alignas(16) float s_o[kMaxSparseWaves][G][128];
+  float s_ml[kMaxSparseWaves][2][G];
+};
+
+// The workgroup's share of the gather-attend (the kernel below, and the
+// merge-then-attend kernel, which passes the row's index list in LDS as
+// `lidx` with LIDX set).
+template <int G, int MODE, int TILES, bool LIDX>
+__device__ __forceinline__ void attend_sparse_body(const AttendArgs& a, const int32_t* lidx,
+                                                   AttendLds<G, TILES>& lds) {
   static_assert(G >= 1 && G <= 4, "query heads of a group fit MFMA rows 0..3");
   constexpr int D = 128;
-  constexpr int W = kMaxSparseWaves;
-  // p of slot 16i + 4u + g for head h at s_pa[wave][h][i][g][u]: the MFMA
-  // A-fragment order of the P.V product
-  __shared__ __align__(16) float s_pa[W][G][TILES][4][4];
-  __shared__ __align__(16) float s_o[W][G][D];
-  __shared__ float s_ml[W][2][G];
+  auto& s_pa = lds.s_pa;
+  auto& s_o = lds.s_o;
+  auto& s_ml = lds.s_ml;
   const int nw = blockDim.x >> 6;  // waves in this workgroup
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -361,7 +375,7 @@ __global__ __launch_bounds__(64 * max_waves<MODE>()) void attend_sparse_kernel(A
     bool ok[TILES];
 #pragma unroll
     for (int i = 0; i < TILES; ++i)
-      tok[i] = slot_token<MODE>(a, row, b, s0 + 16 * i + n, s1, ok[i]);
+      tok[i] = slot_token<MODE, LIDX>(a, row, b, s0 + 16 * i + n, s1, ok[i], lidx);
 
     // 2. key pieces of every tile, then value rows (token 4u + rq of each tile)
     uint4 kw[TILES][4], vw[TILES][4];
@@ -587,6 +601,77 @@ __global__ __launch_bounds__(64 * max_waves<MODE>()) void attend_sparse_kernel(A
   }
 }
 
+
+template <int G, int MODE, int TILES>
+__global__ __launch_bounds__(64 * max_waves<MODE>()) void attend_sparse_kernel(AttendArgs a) {
+  __shared__ __align__(16) AttendLds<G, TILES> lds;
+  attend_sparse_body<G, MODE, TILES, false>(a, nullptr, lds);
+}
+
+// Merge, then gather-attend, in one workgroup of kMaxSparseWaves waves per
+// row: the register top-k of the selection's merge picks the row's k tokens
+// from its parts' (score, position) candidates, writes them to the index
+// list and to LDS, and the waves attend over them from LDS -- the same
+// index list and the same per-wave work as the merge launch followed by the
+// whole-row gather-attend launch, without the launch between them and
+// without reading the index list back from memory.
+template <int G, int TILES, int GK>
+__global__ __launch_bounds__(64 * kMaxSparseWaves) void merge_attend_kernel(
+    AttendArgs a, const float* __restrict__ cand_val, const int32_t* __restrict__ cand_pos,
+    int n_cand, int64_t cstride, bool vec4, int32_t* __restrict__ idx_out) {
+  constexpr int NT = 64 * kMaxSparseWaves;
+  __shared__ SharedT<NT> sh;
+  __shared__ __align__(16) uint2 cand[kRankMax + 8];
+  __shared__ uint32_t s_wave[NT / 64];
+  __shared__ __align__(16) int32_t s_map[4 * GK * NT];
+  __shared__ int32_t s_idx[64 * kMaxSparseWaves];
+  __shared__ __align__(16) AttendLds<G, TILES> lds;
+  const int row = blockIdx.y;
+  const int n = n_cand;  // <= 4 * GK * NT
+  const int32_t k = a.n_idx;
+  const float* __restrict__ sv = cand_val + (int64_t)row * cstride;
+  const int32_t* __restrict__ map = cand_pos + (int64_t)row * cstride;
+  int32_t* __restrict__ out = idx_out + (int64_t)row * k;
+  auto load = [&](int p0, float (&v)[GK][4]) {
+    if (vec4 && n % 4 == 0) {
+      // a group of four lies wholly inside or wholly outside the row
+      const float4* s4 = reinterpret_cast<const float4*>(sv + p0);
+      int4 m[GK];
+#pragma unroll
+      for (int j = 0; j < GK; ++j) {
+        const bool in = p0 + 256 * j < n;
+        const float4 f = in ? s4[64 * j] : make_float4(0.f, 0.f, 0.f, 0.f);
+        m[j] = in ? reinterpret_cast<const int4*>(map + p0)[64 * j] : make_int4(0, 0, 0, 0);
+        v[j][0] = f.x;
+        v[j][1] = f.y;
+        v[j][2] = f.z;
+        v[j][3] = f.w;
+      }
+#pragma unroll
+      for (int j = 0; j < GK; ++j) *reinterpret_cast<int4*>(&s_map[p0 + 256 * j]) = m[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < GK; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = p0 + 256 * j + e;
+          const bool in = i < n;
+          v[j][e] = in ? sv[i] : 0.0f;
+          if (in) s_map[i] = map[i];
+        }
+    }
+  };
+  // s_map is complete before the ordered write: reg_row_topk passes several
+  // barriers between the load and the write
+  auto emit = [&](uint32_t slot, int32_t p) {
+    const int32_t t = s_map[p];
+    out[slot] = t;
+    s_idx[slot] = t;
+  };
+  reg_row_topk<NT, GK, false>(load, n, k, emit, sh, cand, s_wave);
+  __syncthreads();
+  attend_sparse_body<G, kIdxTokenPerHead, TILES, true>(a, s_idx, lds);
+}
 
 // ---------------------------------------------------------------------------
 // Combine: the nsplit partials (o, m, l) of one (row, query head) merged
@@ -848,9 +933,11 @@ AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs) {
 
 bool fused_scores_supported(const Cache& c) { return use_wave_kernel(c); }
 
-hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, const void* k,
-                         const void* v, const int32_t* idx, int32_t n_idx, int32_t bs, float* out,
-                         void* ws, hipStream_t s, float* scores) {
+namespace {
+
+AttendArgs attend_args(const Cache& c, const AttendPlan& p, const void* q, const void* k,
+                       const void* v, const int32_t* idx, int32_t n_idx, int32_t bs, float* out,
+                       void* ws, float* scores) {
   AttendArgs a{};
   a.scores = scores;
   a.sscale = c.scale;
@@ -875,6 +962,15 @@ hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, con
   a.rounds = p.rounds;
   a.out = out;
   a.part = static_cast<float*>(ws);
+  return a;
+}
+
+}  // namespace
+
+hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, const void* k,
+                         const void* v, const int32_t* idx, int32_t n_idx, int32_t bs, float* out,
+                         void* ws, hipStream_t s, float* scores) {
+  const AttendArgs a = attend_args(c, p, q, k, v, idx, n_idx, bs, out, ws, scores);
   const int64_t rows = (int64_t)c.B * c.Hkv;
   const dim3 grid(p.nsplit, (unsigned)rows);
   hipError_t e;
@@ -910,6 +1006,61 @@ hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, con
     hipLaunchKernelGGL(combine_kernel<32>, cgrid, dim3(1024), 0, s, a.part, p.nsplit, c.G, c.D,
                        c.Hq, c.Hkv, out, vec_layout);
   return hipGetLastError();
+}
+
+namespace {
+
+template <int G, int TILES>
+hipError_t launch_merge_attend_g(const AttendArgs& a, int64_t rows, const float* cand_val,
+                                 const int32_t* cand_pos, int64_t n_cand, int64_t cstride,
+                                 bool vec4, int32_t* idx, hipStream_t s) {
+  const dim3 grid(1, (unsigned)rows), block(64 * kMaxSparseWaves);
+  if (n_cand <= 4 * 64 * kMaxSparseWaves)
+    hipLaunchKernelGGL((merge_attend_kernel<G, TILES, 1>), grid, block, 0, s, a, cand_val, cand_pos,
+                       (int)n_cand, cstride, vec4, idx);
+  else
+    hipLaunchKernelGGL((merge_attend_kernel<G, TILES, 2>), grid, block, 0, s, a, cand_val, cand_pos,
+                       (int)n_cand, cstride, vec4, idx);
+  return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_merge_attend_t(int tiles, const AttendArgs& a, int64_t rows,
+                                 const float* cand_val, const int32_t* cand_pos, int64_t n_cand,
+                                 int64_t cstride, bool vec4, int32_t* idx, hipStream_t s) {
+  if (tiles == 2) return launch_merge_attend_g<G, 2>(a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
+  if (tiles == 3) return launch_merge_attend_g<G, 3>(a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
+  return launch_merge_attend_g<G, 4>(a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
+}
+
+// slots per wave of a whole-row plan (one round, one split)
+int whole_row_tiles(const AttendPlan& p) { return p.chunk / (p.waves * 16); }
+
+}  // namespace
+
+bool merge_attend_ok(const Cache& c, const AttendPlan& p, int64_t n_cand, int32_t k) {
+  if (!use_wave_kernel(c) || p.mode != kIdxTokenPerHead || p.nsplit != 1 || p.rounds != 1 ||
+      p.waves > kMaxSparseWaves || p.n_slots != k)
+    return false;
+  const int tiles = whole_row_tiles(p);
+  return p.chunk == p.waves * 16 * tiles && tiles >= 2 && tiles <= 4 && k >= 1 && n_cand >= k &&
+         n_cand <= 2 * 4 * 64 * kMaxSparseWaves;
+}
+
+hipError_t launch_merge_attend(const Cache& c, const AttendPlan& p, const void* q, const void* k,
+                               const void* v, float* out, const float* cand_val,
+                               const int32_t* cand_pos, int64_t n_cand, int64_t cstride, int32_t kk,
+                               int32_t* idx, hipStream_t s) {
+  const AttendArgs a = attend_args(c, p, q, k, v, nullptr, kk, 0, out, nullptr, nullptr);
+  const int64_t rows = (int64_t)c.B * c.Hkv;
+  const bool vec4 = (reinterpret_cast<uintptr_t>(cand_val) % 16 == 0) && (cstride % 4 == 0) &&
+                    (reinterpret_cast<uintptr_t>(cand_pos) % 16 == 0);
+  const int tiles = whole_row_tiles(p);
+  switch (c.G) {
+    case 1: return launch_merge_attend_t<1>(tiles, a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
+    case 2: return launch_merge_attend_t<2>(tiles, a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
+    default: return launch_merge_attend_t<4>(tiles, a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
+  }
 }
 
 }  // namespace sa

@@ -80,9 +80,12 @@ struct SelectIndexer {
   int32_t H, Di;
 };
 SelectPlan plan_select(const Cache& c, int32_t k);
+struct MergeAttend;
+// With `ma`, the gather-attend that follows may run in the merge's launch
+// (merge_attend_ok); *attended then says whether it did.
 hipError_t launch_select(const Cache& c, const SelectPlan& p, const void* q, const void* k,
                          const SelectIndexer* ix, int32_t kk, int32_t* idx, void* ws,
-                         hipStream_t s);
+                         hipStream_t s, const MergeAttend* ma = nullptr, bool* attended = nullptr);
 
 // ----------------------------------------------------------- attention
 // kIdxDenseScored: dense decode that also writes each token's exact score
@@ -113,6 +116,26 @@ hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, con
                          const void* v, const int32_t* idx, int32_t n_idx, int32_t bs, float* out,
                          void* ws, hipStream_t s, float* scores = nullptr);
 bool fused_scores_supported(const Cache& c);
+
+// The gather-attend over a selection's index list: cache view, plan, q,
+// K/V and the output.
+struct MergeAttend {
+  Cache c;
+  AttendPlan p;
+  const void* q;
+  const void* k;
+  const void* v;
+  float* out;
+};
+
+// Merge-then-attend (the selection's merge and a whole-row gather-attend in
+// one launch): whether plan p over n_cand candidates per row allows it, and
+// the launch, which writes idx [rows, kk] and out.
+bool merge_attend_ok(const Cache& c, const AttendPlan& p, int64_t n_cand, int32_t k);
+hipError_t launch_merge_attend(const Cache& c, const AttendPlan& p, const void* q, const void* k,
+                               const void* v, float* out, const float* cand_val,
+                               const int32_t* cand_pos, int64_t n_cand, int64_t cstride, int32_t kk,
+                               int32_t* idx, hipStream_t s);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 

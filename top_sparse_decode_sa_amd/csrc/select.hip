@@ -358,8 +358,9 @@ void launch_part(const Cache& c, const SelectIndexer* ix, const SelArgs& a, dim3
 
 hipError_t launch_select(const Cache& c, const SelectPlan& p, const void* q, const void* k,
                          const SelectIndexer* ix, int32_t kk, int32_t* idx, void* ws,
-                         hipStream_t s) {
+                         hipStream_t s, const MergeAttend* ma, bool* attended) {
   const int64_t rows = (int64_t)c.B * c.Hkv;
+  if (attended) *attended = false;
   if (!p.fused) {
     float* scores = static_cast<float*>(ws);
     void* topk_ws = static_cast<uint8_t*>(ws) + align_up((size_t)rows * c.N * sizeof(float), 256);
@@ -406,6 +407,12 @@ hipError_t launch_select(const Cache& c, const SelectPlan& p, const void* q, con
     launch_part<4>(c, ix, a, grid, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.P == 1) return e;
+  if (ma && attended && (int64_t)ma->c.B * ma->c.Hkv == rows &&
+      merge_attend_ok(ma->c, ma->p, p.C, kk)) {
+    *attended = true;
+    return launch_merge_attend(ma->c, ma->p, ma->q, ma->k, ma->v, ma->out, a.cand_val, a.cand_pos,
+                               p.C, p.cstride, kk, idx, s);
+  }
   return launch_topk_merge(a.cand_val, a.cand_pos, rows, p.C, p.cstride, kk, idx, s);
 }
 
