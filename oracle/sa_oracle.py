@@ -379,7 +379,7 @@ def fixed_jump_plan(n_layers: int, step: int):
 # ---------------------------------------------------------------------------
 
 def index_set_verdict(s: np.ndarray, got, k: int, rel: float = 1e-4):
-    """Judge a selected set against the fp64 scores of its row.
+    """Classify a selected set against the fp64 scores of its row.
 
     Let s_(1) >= s_(2) >= ... be the sorted scores and tau = rel * max(|s_(k)|,
     |s_(k+1)|, 1e-30).  If s_(k) - s_(k+1) > tau the set must equal the exact
