@@ -96,6 +96,11 @@ def parse():
                         "dense, layers 2-7 select 2048 tokens shared by the KV heads with a 4-head "
                         "64-dim indexer; times the mixed 8-layer step against all-dense and each "
                         "sparse layer's launches; prints a table and one JSON line")
+    p.add_argument("--block61k", action="store_true",
+                   help="block selection on the block61k workload (batch 8, 32/8 heads, d 128, bf16, "
+                        "61440 tokens, 24 of 480 blocks of 128 kept): block summaries, block scores, "
+                        "block top-k and the block gather-attend timed call by call, and the 4-layer "
+                        "plan (SPARSE, then 3 REUSE layers) against all-dense; one JSON line")
     p.add_argument("--theta", type=float, default=0.35,
                    help="overlap threshold of the layer-reuse planner (--hylra)")
     p.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -688,6 +693,110 @@ def indexer1m(args):
     print(json.dumps(res), flush=True)
 
 
+def block61k(args):
+    """The block61k workload on the device: batch 8, 32/8 heads, d 128, bf16,
+    61440 tokens = 480 blocks of 128, 24 blocks kept per (sequence, KV head),
+    4 layers planned [SPARSE, REUSE 0, REUSE 0, REUSE 0].  Per call: the
+    per-block key summaries (built once per cache, read K, write min/max),
+    the block scores from the summaries, the top-24 of 480 and the gather-
+    attend of the 3072 tokens of the kept blocks; then the 4-layer step
+    against 4 dense layers.  Values are N(0,1) drawn on the device."""
+    import torch
+    import sa_synth as S
+    import top_sparse_decode_sa_amd as T
+
+    T.lib()
+    dev = torch.device("cuda", 0)
+    c = S.CONFIGS["block61k"]
+    B, Hq, Hkv, d, N, bs, nblk, L = (c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.ctx_len,
+                                     c.block_size, c.k, c.n_layers)
+    nb = N // bs
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    log("block61k: drawing %d layers (%.1f GB of KV)" % (L, L * c.kv_bytes() / 1e9))
+
+    def bf(shape):
+        return torch.empty(shape, dtype=torch.bfloat16, device=dev).normal_(generator=gen)
+
+    qs = [bf((B, Hq, d)) for _ in range(L)]
+    ks = [bf((B, Hkv, N, d)) for _ in range(L)]
+    vs = [bf((B, Hkv, N, d)) for _ in range(L)]
+    kmin, kmax = T.sa_block_summarize(ks[0], bs, q_like=qs[0])
+    scores = torch.empty((B, Hkv, nb), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, Hkv, nblk), dtype=torch.int32, device=dev)
+    outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(L)]
+    largs = [T.layer_args(qs[l], ks[l], vs[l], T.SA_SCORE_BLOCK_MINMAX, nblk, kmin=kmin, kmax=kmax,
+                          block_size=bs, out=outs[l])[0] for l in range(L)]
+    modes = [T.SA_LAYER_DENSE if m == "dense" else T.SA_LAYER_SPARSE if m == "sparse" else
+             T.SA_LAYER_REUSE for m in c.modes]
+    T.sa_plan_validate(modes, list(c.src))
+    ws = {m: T.WORKSPACES.get(dev, ("block61k", m), T.sa_layer_workspace_size(largs[0], m))
+          for m in (T.SA_LAYER_DENSE, T.SA_LAYER_SPARSE, T.SA_LAYER_REUSE)}
+    reps = max(3, min(args.steps, 10))
+
+    def layer(l, m):
+        T.sa_decode_layer(largs[l], m, None if m == T.SA_LAYER_DENSE else idx, dev, ws[m])
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        layer(0, T.SA_LAYER_DENSE)  # queued ahead, so the host enqueues the rest in time
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3  # us
+
+    us_summ = timed(lambda: T.sa_block_summarize(ks[0], bs, q_like=qs[0], kmin=kmin, kmax=kmax), reps)
+    us_score = timed(lambda: T.sa_score(qs[0], ks[0], T.SA_SCORE_BLOCK_MINMAX, kmin=kmin, kmax=kmax,
+                                        block_size=bs, scores=scores), reps)
+    us_topk = timed(lambda: T.sa_topk(scores, nblk, idx_out=idx), reps)
+    us_attend = timed(lambda: T.sa_sparse_decode(qs[0], ks[0], vs[0], idx, out=outs[0],
+                                                 index_kind=T.SA_IDX_BLOCK_PER_KV_HEAD,
+                                                 block_size=bs), reps)
+    us_sparse = timed(lambda: layer(0, T.SA_LAYER_SPARSE), reps)
+    us_reuse = timed(lambda: layer(1, T.SA_LAYER_REUSE), reps)
+    us_dense = timed(lambda: layer(0, T.SA_LAYER_DENSE), reps)
+    us_plan = timed(lambda: [layer(l, modes[l]) for l in range(L)], reps)
+    us_dense4 = timed(lambda: [layer(l, T.SA_LAYER_DENSE) for l in range(L)], reps)
+    rows = B * Hkv
+    summ_bytes = rows * N * d * 2 + 2 * rows * nb * d * 2
+    score_bytes = 2 * rows * nb * d * 2 + B * Hq * d * 2 + rows * nb * 4
+    topk_bytes = rows * nb * 4 + rows * nblk * 4
+    attend_bytes = 2 * rows * nblk * bs * d * 2 + rows * nblk * 4 + 2 * B * Hq * d * 2 + B * Hq * d * 4
+    dense_bytes = 2 * rows * N * d * 2
+
+    def rate(nbytes, us):
+        return {"us": round(us, 1), "bytes": nbytes, "gbps": round(nbytes / us / 1e3, 1),
+                "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
+
+    res = {
+        "bench": "block61k: block selection and reuse on the device", "unit": "us (HIP events)",
+        "config": {"workload": "block61k: batch 8, 32/8 heads, d 128, bf16, 61440 tokens = 480 "
+                               "blocks of 128, 24 blocks kept; 4 layers [SPARSE, REUSE x3]",
+                   "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d, "ctx_len": N,
+                   "block_size": bs, "blocks_kept": nblk, "modes": list(c.modes)},
+        "block_summarize": rate(summ_bytes, us_summ),
+        "block_score": rate(score_bytes, us_score),
+        "block_topk": rate(topk_bytes, us_topk),
+        "block_attend": rate(attend_bytes, us_attend),
+        "sparse_layer_us": round(us_sparse, 1), "reuse_layer_us": round(us_reuse, 1),
+        "dense_layer": rate(dense_bytes, us_dense),
+        "plan_4_layers_us": round(us_plan, 1), "all_dense_4_layers_us": round(us_dense4, 1),
+        "plan_speedup_vs_all_dense": round(us_dense4 / us_plan, 2),
+        "data": "N(0,1) drawn on the device (seed %d)" % args.seed,
+        "provenance": provenance()}
+    for key in ("block_summarize", "block_score", "block_topk", "block_attend", "dense_layer"):
+        print("%18s  %s" % (key, res[key]))
+    for key in ("sparse_layer_us", "reuse_layer_us", "plan_4_layers_us", "all_dense_4_layers_us",
+                "plan_speedup_vs_all_dense"):
+        print("%18s  %s" % (key, res[key]))
+    print(json.dumps(res), flush=True)
+
+
 def hylra(args):
     """Layer-reuse policy on 8 layers of the llama32k shape.
 
@@ -933,6 +1042,9 @@ def main():
         return
     if args.gpus == 1 and args.sweep:
         sweep(args)
+        return
+    if args.gpus == 1 and args.block61k:
+        block61k(args)
         return
     if args.gpus == 1 and args.indexer1m:
         indexer1m(args)

@@ -31,7 +31,7 @@ def _f64(t):
 
 # --------------------------------------------------------------------- top-k
 
-@pytest.mark.parametrize("n", [1, 2, 7, 100, 1000, 4097, 32773])
+@pytest.mark.parametrize("n", [1, 2, 7, 100, 480, 1000, 1025, 3000, 4097, 8192, 8193, 32768, 32773])
 def test_topk_bit_exact(n):
     say("topk n=%d" % n)
     rows = 5

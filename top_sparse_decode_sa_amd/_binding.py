@@ -250,15 +250,21 @@ def sa_score(q, k_cache, kind=SA_SCORE_EXACT, *, kmin=None, kmax=None, block_siz
     return scores
 
 
-def sa_block_summarize(k_cache, block_size, q_like=None):
-    """sa_block_summarize: returns (kmin, kmax) [B, Hkv, nb, d] in the cache dtype."""
-    dev = _dev(k_cache)
+def sa_block_summarize(k_cache, block_size, q_like=None, kmin=None, kmax=None):
+    """sa_block_summarize: returns (kmin, kmax) [B, Hkv, nb, d] in the cache dtype
+    (written into kmin / kmax when given)."""
+    dev = _dev(k_cache, kmin, kmax)
     B, Hkv, N, d = k_cache.shape
     q = q_like if q_like is not None else torch.empty((B, Hkv, d), dtype=k_cache.dtype, device=dev)
     desc = make_desc(q, k_cache)
     nb = (N + block_size - 1) // block_size
-    kmin = torch.empty((B, Hkv, nb, d), dtype=k_cache.dtype, device=dev)
-    kmax = torch.empty_like(kmin)
+    if kmin is None:
+        kmin = torch.empty((B, Hkv, nb, d), dtype=k_cache.dtype, device=dev)
+    if kmax is None:
+        kmax = torch.empty_like(kmin)
+    for t in (kmin, kmax):
+        if t.shape != (B, Hkv, nb, d) or t.dtype != k_cache.dtype or not t.is_contiguous():
+            raise ValueError("kmin / kmax must be contiguous [B, Hkv, nb, d] in the cache dtype")
     check(lib().sa_block_summarize(ctypes.byref(desc), block_size, _ptr(k_cache), _ptr(kmin),
                                    _ptr(kmax), ctypes.c_void_p(_stream(dev))))
     return kmin, kmax

@@ -765,8 +765,20 @@ hipError_t launch_topk(const float* scores, int64_t n_rows, int64_t n, int64_t r
   // 16-byte loads when every row starts 16-byte aligned
   const bool vec4 = (reinterpret_cast<uintptr_t>(scores) % 16 == 0) && (row_stride % 4 == 0);
   if (n <= kResident) {
-    hipLaunchKernelGGL((topk_reg_kernel<kThreads, 8, false>), dim3((unsigned)n_rows), dim3(kThreads),
-                       0, s, scores, n, row_stride, k, idx, vec4, nullptr);
+    // the fewest keys per thread that hold the row: short rows (block scores,
+    // merges) do not pay for 32 keys per thread on 16 waves
+    if (n <= 4 * 1 * 256)
+      hipLaunchKernelGGL((topk_reg_kernel<256, 1, false>), dim3((unsigned)n_rows), dim3(256), 0, s,
+                         scores, n, row_stride, k, idx, vec4, nullptr);
+    else if (n <= 4 * 2 * 512)
+      hipLaunchKernelGGL((topk_reg_kernel<512, 2, false>), dim3((unsigned)n_rows), dim3(512), 0, s,
+                         scores, n, row_stride, k, idx, vec4, nullptr);
+    else if (n <= 4 * 4 * 512)
+      hipLaunchKernelGGL((topk_reg_kernel<512, 4, false>), dim3((unsigned)n_rows), dim3(512), 0, s,
+                         scores, n, row_stride, k, idx, vec4, nullptr);
+    else
+      hipLaunchKernelGGL((topk_reg_kernel<kThreads, 8, false>), dim3((unsigned)n_rows),
+                         dim3(kThreads), 0, s, scores, n, row_stride, k, idx, vec4, nullptr);
   } else if (use_mw(n_rows, n, k)) {
     MwRow* rows = static_cast<MwRow*>(ws);
     const dim3 grid((unsigned)((n + kMwChunk - 1) / kMwChunk), (unsigned)n_rows);
