@@ -280,11 +280,13 @@ __device__ __forceinline__ int32_t slot_token(const AttendArgs& a, int row, int 
   }
 }
 
-// K/V row pieces: a dense scan reads every row once, so its loads are
-// nontemporal (streaming); gathered rows use ordinary loads.
+// K/V row pieces: a dense scan, and the 128-token runs of selected blocks,
+// read every row once in long contiguous runs, so their loads are
+// nontemporal (streaming); gathered token rows use ordinary loads.
 template <int MODE>
 __device__ __forceinline__ uint4 ld_kv(const uint8_t* p) {
-  if constexpr (MODE == kIdxDense || MODE == kIdxDenseScored) return ld16_nt(p);
+  if constexpr (MODE == kIdxDense || MODE == kIdxDenseScored || MODE == kIdxBlockPerHead)
+    return ld16_nt(p);
   else return ld16(p);
 }
 

@@ -228,7 +228,18 @@ __global__ __launch_bounds__(kThreads) void score_block_kernel(BlockArgs a) {
   const int row = blockIdx.y;
   const int b = row / a.Hkv;
   const int r = row % a.Hkv;
+  const int stride = gridDim.x * NG;
+  auto off_of = [&](int j) { return (((int64_t)row * a.nb + j) * D) * EB + sl * 16; };
 
+  // the first block's summaries are requested before the queries, so the
+  // two loads' latencies overlap; each later block's load is issued one
+  // iteration ahead
+  int j = blockIdx.x * NG + grp;
+  uint4 lmn = make_uint4(0u, 0u, 0u, 0u), lmx = make_uint4(0u, 0u, 0u, 0u);
+  if (j < a.nb) {
+    lmn = ld16(a.kmin + off_of(j));
+    lmx = ld16(a.kmax + off_of(j));
+  }
   float qp[E], qn[E];
   float qv[8][E];
   load_q_group<E, D>(a.q, a.q_dtype, (int64_t)b * a.Hq + (int64_t)r * a.G, a.G, sl * E, qv);
@@ -244,11 +255,14 @@ __global__ __launch_bounds__(kThreads) void score_block_kernel(BlockArgs a) {
     qp[e] = p;
     qn[e] = n;
   }
-  for (int j = blockIdx.x * NG + grp; j < a.nb; j += gridDim.x * NG) {
-    const int64_t off = (((int64_t)row * a.nb + j) * D) * EB + sl * 16;
+  for (; j < a.nb; j += stride) {
     float mn[E], mx[E];
-    unpack16<KT>(ld16(a.kmin + off), mn);
-    unpack16<KT>(ld16(a.kmax + off), mx);
+    unpack16<KT>(lmn, mn);
+    unpack16<KT>(lmx, mx);
+    if (j + stride < a.nb) {
+      lmn = ld16(a.kmin + off_of(j + stride));
+      lmx = ld16(a.kmax + off_of(j + stride));
+    }
     float acc = 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) acc = fmaf(qp[e], mx[e], fmaf(qn[e], mn[e], acc));
