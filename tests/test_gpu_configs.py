@@ -302,7 +302,8 @@ def test_indexer1m_mixed_plan():
 def test_split_counts_agree():
     """The same selection decoded with different split counts -- one sequence
     versus the sequence repeated 64 times, which changes the planned chunking
-    (41 vs 11 splits per row sparse, 16 vs 4 dense) -- agrees within fp32
+    (41 splits per row vs one whole-row workgroup sparse, 16 vs 2 splits
+    dense) -- agrees within fp32
     rounding: the split-K log-sum-exp combine gives the same result."""
     say("split invariance")
     rng = np.random.default_rng(5)

@@ -530,11 +530,11 @@ def test_stream_read_covers_every_word(nbytes):
 
 @pytest.mark.parametrize("N,dtype,want_splits,want_sparse",
                          [(25677, "bf16", 101, 313), (51277, "bf16", 201, 313),
-                          (153677, "bf16", 301, 313), (40000, "f32", 625, 625)])
+                          (153677, "bf16", 601, 313), (40000, "f32", 625, 625)])
 def test_combine_across_split_counts(N, dtype, want_splits, want_sparse):
-    """Few rows over a long context split into 101, 201, 301 and 625
-    partials per row (the combine's 8-, 16- and 32-lane variants, the last in
-    two rounds of loads, each with a ragged last split); dense decode and a
+    """Few rows over a long context split into 101, 201, 601 and 625
+    partials per row (the combine's 8-, 16- and 32-lane variants, the last
+    two in two rounds of loads, each with a ragged last split); dense decode and a
     20000-token selection (bf16: 313 one-wave partials in the interleaved
     layout) against the oracle."""
     from top_sparse_decode_sa_amd import _binding as Bn

@@ -889,15 +889,18 @@ AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs) {
     } else if (is_dense_mode(mode)) {
       // long contiguous scans: several rounds per wave merged online, so a
       // workgroup covers waves * rounds * 64 tokens and few split partials
-      // are written (on 128 rows of 32768 tokens, 4 waves x 8 rounds: 323 us
-      // + 6 us combine, against 328-340 us for 4 x 4, 8 x 4 and 8 x 8)
+      // are written.  4 waves, and the most rounds (at most 32) that still
+      // give about 1024 workgroups: on 128 rows of 32768 tokens 16 rounds
+      // (8 splits) take 320 us against 324.5 us for 8 rounds; on 8 rows of
+      // 1M tokens 32 rounds (128 splits) 626 us against 649 us for 8 rounds
+      // and 638 us for 64; 8 waves were no faster on either
       waves = dense_waves_override() ? dense_waves_override() : 4;
-      rounds = dense_rounds_override() ? dense_rounds_override() : 8;
+      rounds = dense_rounds_override() ? dense_rounds_override() : 32;
       if (mode == kIdxDenseScored) waves = std::min(waves, kMaxScoredWaves);
-      // short contexts: fewer rounds per wave until about 512 workgroups run
-      // (64 rows of 3072 tokens: 12 splits of 256 instead of 2 of 2048)
+      // fewer rounds per wave until about 1024 workgroups run (64 rows of
+      // 3072 tokens: 12 splits of 256 tokens, not 1 of 3072)
       if (!dense_rounds_override())
-        while (rounds > 1 && rows * ((p.n_slots + 64 * waves * rounds - 1) / (64 * waves * rounds)) < 512)
+        while (rounds > 1 && rows * ((p.n_slots + 64 * waves * rounds - 1) / (64 * waves * rounds)) < 1024)
           rounds /= 2;
     } else {
       // selections split so that about 512 workgroups (two per CU) run; a
