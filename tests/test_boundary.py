@@ -413,3 +413,40 @@ def test_bench_select_bytes_follow_the_library_plan():
         else:
             want = 2 * (-(-rows * (-(-C // 4) * 4) * 4 // 256) * 256)
         assert got == want, (B, Hkv, N, k, C, fused, got, want)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus 2 exits with status 2 and says why,
+    before touching a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(os.path.dirname(__file__), "..", "bench.py"),
+                        "--gpus", "2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and "--gpus 2" in r.stderr
+
+
+def test_bench_summarize_percentiles(tmp_path):
+    """The kernel-trace summary gives count, mean, min, max, median, p10 and
+    p90 per kernel name (durations in ns in, microseconds out)."""
+    import importlib.util
+    import sqlite3
+    spec = importlib.util.spec_from_file_location(
+        "bench_mod", os.path.join(os.path.dirname(__file__), "..", "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    db = tmp_path / "t_results.db"
+    con = sqlite3.connect(str(db))
+    con.execute("create table kernels (name text, start integer, end integer)")
+    for i in range(1, 11):  # 1..10 us
+        con.execute("insert into kernels values (?, ?, ?)", ("k_a", 0, i * 1000))
+    con.execute("insert into kernels values (?, ?, ?)", ("k_b", 0, 500))
+    con.commit()
+    con.close()
+    text, rows, counters = bench.summarize(str(db))
+    lines = {l.split()[0]: l.split()[1:] for l in text.splitlines()[1:]}
+    n, avg, mn, mx, med, p10, p90 = lines["k_a"]
+    assert int(n) == 10 and float(avg) == 5.5 and float(mn) == 1.0 and float(mx) == 10.0
+    assert float(med) == 5.5 and abs(float(p10) - 1.9) < 1e-9 and abs(float(p90) - 9.1) < 1e-9
+    assert lines["k_b"][0] == "1" and float(lines["k_b"][4]) == 0.5
+    assert counters == {}
