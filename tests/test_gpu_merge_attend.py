@@ -27,6 +27,8 @@ CASES = [
     (32, 16, 8, 32768, 655, EX, "groups of 2 query heads"),
     (4, 32, 8, 32768, 655, EXQ, "per query head: 128 rows of one head"),
     (16, 32, 8, 32768, 655, IXK, "per-KV-head indexer"),
+    (16, 32, 8, 32768, 1, EX, "k = 1: one wave with slots, eleven idle"),
+    (16, 32, 8, 32768, 768, EX, "k = 768: twelve full waves, 3072 candidates (register capacity)"),
 ]
 
 
@@ -69,13 +71,16 @@ def test_layer_merge_attend_equals_select_then_decode(B, Hq, Hkv, N, k, kind, wh
     torch.cuda.empty_cache()
 
 
-def test_layer_without_whole_row_plan_keeps_two_launches():
-    """Few rows (the gather-attend splits each row over several workgroups):
-    the layer runs the merge and the split gather-attend as before, with the
-    same results as the two calls."""
-    say("merge-attend fallback: 2 x 2 rows")
-    g = torch.Generator(device=dev()).manual_seed(3)
-    B, Hq, Hkv, N, k = 2, 8, 2, 32768, 655
+@pytest.mark.parametrize("B,Hq,Hkv,N,k,what", [
+    (2, 8, 2, 32768, 655, "4 rows: the gather-attend splits each row"),
+    (16, 32, 8, 32768, 769, "k = 769: more slots than twelve waves of 64"),
+])
+def test_layer_without_whole_row_plan_keeps_two_launches(B, Hq, Hkv, N, k, what):
+    """When a row's gather-attend does not fit one workgroup, the layer runs
+    the merge and the split gather-attend as before, with the same results
+    as the two calls."""
+    say("merge-attend fallback: %s" % what)
+    g = torch.Generator(device=dev()).manual_seed(3 + k)
     q = torch.randn((B, Hq, 128), generator=g, device=dev()).to(torch.bfloat16)
     kc = torch.randn((B, Hkv, N, 128), generator=g, device=dev()).to(torch.bfloat16)
     vc = torch.randn((B, Hkv, N, 128), generator=g, device=dev()).to(torch.bfloat16)
