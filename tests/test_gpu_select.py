@@ -120,6 +120,7 @@ IDX_CASES = [
     (2, 4, 5000, 3, 32, 40, False, "3 heads of 32 dims"),
     (4, 2, 100, 8, 64, 10, True, "one part shorter than one iteration"),
     (2, 2, 32768, 4, 64, 12000, False, "fallback: candidates more than a quarter of the row"),
+    (128, 8, 131072, 4, 64, 262, False, "batch128k shape at 500x: 1024 rows of sixteen 8192-token parts"),
 ]
 
 
@@ -148,6 +149,8 @@ def test_select_indexer_matches_score_then_topk(B, Hkv, N, H, Di, k, shared, wha
     torch.cuda.synchronize()
     assert tuple(got.shape) == ((B, k) if shared else (B, Hkv, k))
     assert torch.equal(got, want), what
+    del q, kc, qi, ki, w, got, want
+    torch.cuda.empty_cache()
 
 
 def test_select_indexer_against_oracle():
