@@ -431,6 +431,43 @@ def test_step_graph_replay(B, Hkv, N, k, fused):
         assert torch.equal(go, out), "replay %d attends differently" % rep
 
 
+def test_layer_graph_replay_with_merge_attend():
+    """A SPARSE layer whose merge and gather-attend share one launch (128
+    rows of 32768 tokens, k = 655) captured as a HIP graph and replayed four
+    times with new queries copied in eagerly between replays: every replay
+    selects and attends as the eager layer call."""
+    say("graph replay: SPARSE layer with merge-attend")
+    B, Hkv, G, N, d, k = 16, 8, 4, 32768, 128, 655
+    gen = torch.Generator(device=dev()).manual_seed(7)
+    q = torch.randn((B, Hkv * G, d), generator=gen, device=dev()).to(torch.bfloat16)
+    kc = torch.randn((B, Hkv, N, d), generator=gen, device=dev()).to(torch.bfloat16)
+    vc = torch.randn((B, Hkv, N, d), generator=gen, device=dev()).to(torch.bfloat16)
+    args, out, d_ = T.layer_args(q, kc, vc, T.SA_SCORE_EXACT, k)
+    ws = T.WORKSPACES.get(d_, ("graph-layer", T.SA_LAYER_SPARSE),
+                          T.sa_layer_workspace_size(args, T.SA_LAYER_SPARSE))
+    idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev())
+
+    def layer():
+        T.sa_decode_layer(args, T.SA_LAYER_SPARSE, idx, d_, ws)
+
+    layer()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer()
+    for rep in range(4):
+        q.copy_(torch.randn(tuple(q.shape), generator=gen, device=dev()).to(torch.bfloat16))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        gi, go = idx.clone(), out.clone()
+        layer()
+        torch.cuda.synchronize()
+        assert torch.equal(gi, idx), "replay %d selects differently" % rep
+        assert torch.equal(go, out), "replay %d attends differently" % rep
+        assert torch.equal(gi, T.sa_select(q, kc, k)), "replay %d differs from sa_select" % rep
+
+
 # ------------------------------------------------------- index-guided offload
 
 @pytest.mark.parametrize("dtype,d,B,Hkv,N,bs,n_blk,token_major", [
