@@ -28,6 +28,14 @@ device's streaming read rate (sa_stream_read over 8 GiB), and the step's and
 the dominant unit's rates are also given as fractions of it.  `cpu_baseline` times the
 CPU oracle on a bounded sample of the same step (rows of the batch), scaled
 to a full step.
+
+Other modes (each prints its own JSON line): --sweep (full step with four
+selection front ends against dense decode at 2x-500x on the llama32k and
+batch128k shapes), --hylra (layer-reuse plans over 8 layers), --offload
+(selected blocks fetched from a pinned host cache), --nscale (32K-128K
+tokens at fixed k), --indexer1m (the 1M-token 8-layer mixed plan),
+--block61k (block selection and reuse on the device); --profile (a short
+run for rocprofv3), --traffic and --summarize (reports from its results).
 """
 from __future__ import annotations
 
