@@ -6,8 +6,10 @@ top-k per (sequence, KV head) at 50x sparsity (k = 655).  One step is one pass
 of the whole hot path through the C ABI:
     sa_select (exact scoring fused with a per-part top-k, then the merge)
     -> sa_sparse_decode (gather + split-K attend).
-Queries rotate over 8 pre-generated variants so consecutive steps select
-different tokens; the cache (2.15 GB) is resident in HBM before timing starts.
+Queries rotate over 8 pre-generated variants and the steps over 8 device
+copies of the cache (2.15 GB each, all resident in HBM before timing starts;
+--kv-replicas), so consecutive steps select different tokens and no step
+finds the previous step's rows in cache.
 
 Timing: W untimed warmup steps, then K timed steps bracketed by
 torch.cuda.synchronize().  Each step is captured once per query variant as a
@@ -41,6 +43,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -68,6 +71,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bound on the oracle's CPU time for cpu_baseline (0 disables)")
     p.add_argument("--dense-steps", type=int, default=20)
+    p.add_argument("--kv-replicas", type=int, default=8,
+                   help="copies of the K/V cache the timed steps rotate through (step i uses "
+                        "copy i mod R), so a step never finds the previous step's rows in cache")
     p.add_argument("--stream-gib", type=int, default=8,
                    help="GiB read by sa_stream_read for the device's streaming read rate (0: skip)")
     p.add_argument("--eager", action="store_true",
@@ -1095,6 +1101,10 @@ def main():
         return (t.view(torch.bfloat16) if t.dtype == torch.uint16 else t).to(dev)
 
     kd, vd = up(k_host), up(v_host)
+    # R replicas of the cache (device copies), rotated with the queries
+    n_rep = max(1, args.kv_replicas)
+    kds = [kd] + [kd.clone() for _ in range(n_rep - 1)]
+    vds = [vd] + [vd.clone() for _ in range(n_rep - 1)]
     qd = [up(q) for q in q_host]
     rows = c.batch * c.n_kv_heads
     scores = torch.empty((c.batch, c.n_kv_heads, c.ctx_len), dtype=torch.float32, device=dev)
@@ -1106,12 +1116,13 @@ def main():
         # exact selection (fused scoring + part top-k, then the merge), then
         # the gather-attend
         q = qd[i % N_QVAR]
+        kr, vr = kds[i % n_rep], vds[i % n_rep]
         if ev is not None:
             ev[0].record()
-        T.sa_select(q, kd, c.k, idx_out=idx)
+        T.sa_select(q, kr, c.k, idx_out=idx)
         if ev is not None:
             ev[1].record()
-        T.sa_sparse_decode(q, kd, vd, idx, out=out)
+        T.sa_sparse_decode(q, kr, vr, idx, out=out)
         if ev is not None:
             ev[2].record()
 
@@ -1123,14 +1134,15 @@ def main():
     # the timed steps: each step captured once per query variant as a HIP
     # graph (the three launches of one decode step), replayed in turn
     graphs = []
+    n_graph = N_QVAR * n_rep // math.gcd(N_QVAR, n_rep)
     if not args.eager:
-        for v in range(N_QVAR):
+        for v in range(n_graph):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 step(v)
             graphs.append(g)
         for i in range(args.warmup):
-            graphs[i % N_QVAR].replay()
+            graphs[i % n_graph].replay()
         torch.cuda.synchronize()
         # a replayed step selects and attends exactly as the eager one
         graphs[0].replay()
@@ -1146,7 +1158,7 @@ def main():
         if args.eager:
             step(i)
         else:
-            graphs[i % N_QVAR].replay()
+            graphs[i % n_graph].replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_step = wall * 1e3 / args.steps
@@ -1316,7 +1328,7 @@ def main():
         "config": {"workload": "llama3.1-8b-shaped decode, exact top-k at 50x sparsity",
                    "batch": c.batch, "n_q_heads": c.n_q_heads, "n_kv_heads": c.n_kv_heads,
                    "head_dim": c.head_dim, "ctx_len": c.ctx_len, "k": c.k,
-                   "kv_dtype": c.dtype, "parallelism": "single GPU"},
+                   "kv_dtype": c.dtype, "kv_replicas": n_rep, "parallelism": "single GPU"},
         "roofline": roof,
         "kernels": kernels,
         "sparse_over_dense_speedup": (round(ms_dense / ms_attend, 2) if ms_dense else None),
