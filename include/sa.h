@@ -58,6 +58,10 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden symbol visibility: the functions declared
+ * here are its only exports. */
+#pragma GCC visibility push(default)
+
 typedef enum {
   SA_OK = 0,
   SA_ERR_NULL = 1,        /* a required pointer is null */
@@ -390,6 +394,8 @@ const char* sa_version(void);
  * reaches, the reference the kernels' rates are compared with.
  * Errors: SA_ERR_NULL / SA_ERR_ALIGN for data, sink; SA_ERR_SHAPE for bytes. */
 sa_status sa_stream_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t stream);
+
+#pragma GCC visibility pop
 
 #ifdef __cplusplus
 }

@@ -31,6 +31,8 @@ def hipcc() -> str:
 
 def common_flags():
     return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+            # only the C ABI of include/sa.h is exported
+            "-fvisibility=hidden",
             "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
             # no packed fp32 instructions in any kernel
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -34,7 +34,6 @@
 //   * attend_kernel (any other dtype / head_dim / group): lane groups of LPR
 //     lanes hold whole cache rows; logits reduce with DPP inside the group.
 #include <math.h>
-#include <stdlib.h>
 
 #include <algorithm>
 #include <initializer_list>
@@ -70,7 +69,22 @@ struct AttendArgs {
   float sscale;    // softmax scale (the exact score's scale)
   float* out;
   float* part;  // [rows, nsplit, G, D + 2]: o[G][D], m[G], l[G]
+  uint32_t row_span;  // pair kernel: bytes of one row's cache, N * st * 2 (< 2^32)
 };
+
+// Buffer resource word 3 of a raw (stride 0) buffer of 32-bit data; loads
+// past num_records return zeros.
+constexpr int kBufferFlags = 0x00020000;
+// Cache-policy operand of a buffer load: nontemporal.
+constexpr int kBufferNT = 2;
+
+// 16-byte nontemporal buffer load: a gathered row is read once, so it is
+// fetched without displacing reusable lines (on a cold cache this also keeps
+// the gather from evicting, and writing back, other data).
+__device__ __forceinline__ uint4 ld16_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kBufferNT);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 template <int MODE>
 __device__ __forceinline__ int64_t resolve_slot(const AttendArgs& a, int row, int b, int64_t j,
@@ -610,14 +624,387 @@ __global__ __launch_bounds__(64 * max_waves<MODE>()) void attend_sparse_kernel(A
   attend_sparse_body<G, MODE, TILES, false>(a, nullptr, lds);
 }
 
+// ---------------------------------------------------------------------------
+// Selected-token gather-attend, pipelined by pairs of 16-slot tiles.
+//
+// A wave owns up to 32 * PAIRS consecutive slots.  It requests every index,
+// key and value row of its slots at once, in pair order (indices; then per
+// pair: keys of both tiles, values of both tiles), and then consumes the
+// pairs in that order, so the work on a pair's rows overlaps the arrival of
+// the later pairs' rows and only the last pair's work follows the last row.
+//
+// Per pair, Q.K gives each tile's logits in MFMA rows 0..3 (lanes 0..15);
+// one lane-row swap then puts the second tile's in lanes 16..31, so the
+// softmax of a pair runs on 32 lanes.  The softmax keeps one reference per head for the whole wave
+// (the first pair's maximum), raised only when a later logit exceeds it by
+// more than 2^kLazyLog2 -- so exp2(logit - reference) never exceeds 2^8 and
+// the running sums and the P.V accumulators are rescaled only then.  Row
+// sums accumulate per lane and are reduced once at the end.  P.V runs on
+// MFMA as in the kernel above (P as a truncated bf16 pair hi + lo, V columns
+// assembled from the lane's own value rows by byte permutes).
+constexpr int kMaxPairWaves = 12;
+constexpr float kLazyLog2 = 8.0f;
+
+// Position of 16-byte chunk x (dims [8x, 8x + 8)) of token t in a wave's
+// key tile: one row of the 16 tokens per chunk, rows padded to 272 bytes, so
+// the 16 lanes that store chunk n of one token each (row stride 272 = 16 mod
+// 256) and the 16 lanes that load one chunk of 16 tokens (consecutive) both
+// touch 16 different bank groups, and every store and load of a lane is one
+// base address plus a constant.
+constexpr int kKtRow = 16 * 16 + 16;
+__device__ __forceinline__ int kt_pos(int t, int x) { return x * kKtRow + 16 * t; }
+
+template <int G>
+struct PairLds {
+  // per wave: one tile of keys on its way to the MFMA layout (kt_pos),
+  // later the wave's O rows for the merge of the waves
+  union Wave {
+    alignas(16) uint8_t kt[16 * kKtRow];
+    alignas(16) float o[G][128];
+  };
+  Wave w[kMaxPairWaves];
+  alignas(16) uint8_t q[4 * 256];                     // the row's G query heads, bf16
+  alignas(16) float s_p[kMaxPairWaves][G][2][4][4];  // p of head h, tile, g, u (token 4u + g)
+  alignas(16) float s_zero[8];                        // A rows that carry no head
+  float s_ml[kMaxPairWaves][2][G];
+};
+
+
+__device__ __forceinline__ float lane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+template <int G, int MODE, int PAIRS, bool LIDX>
+__device__ __forceinline__ void attend_pairs_body(const AttendArgs& a, const int32_t* lidx,
+                                                  PairLds<G>& lds) {
+  static_assert(G >= 1 && G <= 4, "query heads of a group fit MFMA rows 0..3");
+  constexpr int D = 128;
+  constexpr int TILES = 2 * PAIRS;
+  const int nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n = lane & 15;
+  const int rq = lane >> 4;
+  const int row = blockIdx.y;
+  const int split = blockIdx.x;
+  const int b = row / a.Hkv;
+  const int r = row % a.Hkv;
+  const int64_t wg0 = (int64_t)split * a.chunk;
+  const int64_t wg1 = min(wg0 + (int64_t)a.chunk, a.n_slots);
+  const int64_t s0 = wg0 + (int64_t)wave * 32 * PAIRS;
+  const int64_t s1 = min(s0 + 32 * PAIRS, wg1);
+
+  float m_me = -INFINITY, l_me = 0.0f;
+  float mine[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  if (lane < 8) lds.s_zero[lane] = 0.0f;
+  // Where this workgroup writes its result; a word of it is read early (see
+  // below), so the page's address translation is in place when the result
+  // is stored at the very end (a translation miss there would follow the
+  // last row's arrival).  The value read is never used.
+  float* const dst_row = a.nsplit == 1
+                             ? a.out + ((int64_t)b * a.Hq + (int64_t)r * G) * D
+                             : a.part + ((int64_t)row * a.nsplit + split) * (G * (D + 2));
+  float touch = 0.0f;
+  if (s0 < wg1) {  // uniform: the wave has slots
+    // the row's G query heads (G * 256 bytes) straight into LDS, first of
+    // all loads, so any later wait for key rows covers it; every wave of the
+    // workgroup writes the same bytes.  Lane l copies bytes [16l, +16)
+    // (lanes past the heads copy the last 16 bytes again).
+    {
+      const int qb = min(16 * lane, G * 256 - 16);
+      __builtin_amdgcn_global_load_lds(
+          static_cast<const uint8_t*>(a.q) + ((int64_t)b * a.Hq + (int64_t)r * G) * D * 2 + qb,
+          reinterpret_cast<__attribute__((address_space(3))) void*>(
+              reinterpret_cast<uintptr_t>(lds.q)),
+          16, 0, 0);
+    }
+    // the row's keys and values as buffer resources over its N tokens: a
+    // token's rows sit at byte offset token * row_bytes, and an offset past
+    // the row reads zeros instead of leaving the cache
+    const int64_t kv_off = ((int64_t)b * a.sb + (int64_t)(r / a.kv_div) * a.sh) * 2;
+    const uint32_t row_bytes = (uint32_t)(a.st * 2);
+    const uint32_t nrec = a.row_span;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.k + kv_off), (short)0, nrec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.v + kv_off), (short)0, nrec, kBufferFlags);
+
+    // 1. token of slot 16i + n of every tile, as a byte offset
+    uint32_t toff[TILES];
+#pragma unroll
+    for (int i = 0; i < TILES; ++i) {
+      bool ok_unused;
+      toff[i] = (uint32_t)slot_token<MODE, LIDX>(a, row, b, s0 + 16 * i + n, s1, ok_unused, lidx) *
+                row_bytes;
+    }
+    // 2. tile by tile (so pair by pair), the key and the value row pieces of
+    //    each token: lane (n, rq) reads bytes [16n, +16) of token 4u + rq of
+    //    the tile (load u), so every 8 lanes read one whole 128-byte line.
+    uint4 kl[TILES][4], vw[TILES][4];
+#pragma unroll
+    for (int i = 0; i < TILES; ++i)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t off = (uint32_t)__shfl((int)toff[i], 4 * u + rq) + 16 * n;
+        kl[i][u] = ld16_buf(rk, off);
+        vw[i][u] = ld16_buf(rv, off);
+      }
+    // after the rows, so no wait for a row waits for it (a per-lane address:
+    // a vector load, counted with the rows)
+    touch = dst_row[lane];
+    __builtin_amdgcn_sched_barrier(0);
+    uint8_t* const kt = lds.w[wave].kt;
+
+    float mref[G], lsum[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      mref[h] = 0.0f;
+      lsum[h] = 0.0f;
+    }
+    f32x4_t oacc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) oacc[e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const int ha = n >> 2;  // A row n of P.V: head n / 4, part n % 4 (0 hi, 1 lo)
+    const bool arow = (n & 3) < 2 && ha < G;
+    const uint32_t lo_mask = (n & 3) == 1 ? 0xffff0000u : 0u;
+    const float* pa0 = arow ? &lds.s_p[wave][ha < G ? ha : 0][0][rq][0] : lds.s_zero;
+    const float* pa1 = arow ? pa0 + 16 : lds.s_zero + 4;
+
+#pragma unroll
+    for (int p = 0; p < PAIRS; ++p) {
+      // each pair's work stays after the previous pair's (it waits only for
+      // its own rows)
+      __builtin_amdgcn_sched_barrier(0);
+      // 3. logits of both tiles (rows 0..G-1, lanes 0..15 of each result),
+      //    then the second tile's rows moved to lanes 16..31: lanes 0..15
+      //    hold tile 2p, lanes 16..31 tile 2p + 1
+      //    Each tile goes through the wave's LDS tile: stored as loaded,
+      //    read back as MFMA B fragments (lane (n, rq) of fragment c: token n,
+      //    dims [32c + 8rq, +8), i.e. chunk 4c + rq).
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          *reinterpret_cast<uint4*>(kt + kt_pos(4 * u + rq, n)) = kl[2 * p + i][u];
+        __builtin_amdgcn_wave_barrier();
+        // A fragments: q of head n % G, dims [32c + 8rq, +8) (lanes n >= G
+        // repeat a head; the result rows they produce, G..15, are never
+        // read); B fragments from the key tile
+        bf16x8_t kf[4], qa[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint4 w = *reinterpret_cast<const uint4*>(kt + kt_pos(n, 4 * c + rq));
+          __builtin_memcpy(&kf[c], &w, 16);
+          const uint4 x = *reinterpret_cast<const uint4*>(lds.q + (n % G) * 256 + 64 * c + 16 * rq);
+          __builtin_memcpy(&qa[c], &x, 16);
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (i == 0)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[c], kf[c], acc, 0, 0, 0);
+          else
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[c], kf[c], acc1, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        // odd 16-lane rows of the first operand trade with even rows of the second
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[h]),
+                                                         __float_as_uint(acc1[h]), false, false);
+        acc[h] = __uint_as_float(sw[0]);
+      }
+      // lane (n, rq < 2) holds slot 32p + 16rq + n of the wave
+      const bool vld = rq < 2 && s0 + 32 * p + 16 * rq + n < s1;
+      // 4. exponents against the wave's reference (set by the first pair)
+      float t[G];
+      if (p == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float x = vld ? acc[h] * a.qscale : -INFINITY;
+          const float mx = group_max<16>(x);
+          mref[h] = fmaxf(lane_f(mx, 0), lane_f(mx, 16));
+          t[h] = x - mref[h];
+        }
+      } else {
+        float tm = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          t[h] = vld ? fmaf(acc[h], a.qscale, -mref[h]) : -INFINITY;
+          tm = fmaxf(tm, t[h]);
+        }
+        if (__any(tm > kLazyLog2)) {
+          // a logit above the reference by more than 2^8: raise the
+          // references of the heads that grew and rescale what they summed
+          float alpha_me = 1.0f;
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float mx = group_max<16>(t[h]);
+            const float pm = fmaxf(lane_f(mx, 0), lane_f(mx, 16));
+            if (pm > 0.0f) {
+              const float al = __builtin_amdgcn_exp2f(-pm);
+              mref[h] += pm;
+              t[h] -= pm;
+              lsum[h] *= al;
+              if (rq == h) alpha_me = al;
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            oacc[e][0] *= alpha_me;
+            oacc[e][1] *= alpha_me;
+          }
+        }
+      }
+      float pv[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        pv[h] = __builtin_amdgcn_exp2f(t[h]);  // exp2(-inf) = 0 for empty slots
+        lsum[h] += pv[h];
+      }
+      // 5. P to the A fragments of P.V: slot 4u + g of tile j/4 is k index
+      //    8g + 4(j/4) + u
+      if (rq < 2) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) lds.s_p[wave][h][rq][n & 3][n >> 2] = pv[h];
+      }
+      __builtin_amdgcn_wave_barrier();
+      const float4 x0 = *reinterpret_cast<const float4*>(pa0);
+      const float4 x1 = *reinterpret_cast<const float4*>(pa1);
+      const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      uint32_t af[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        // hi rows: p truncated to bf16; lo rows: the rest, truncated
+        const uint32_t u0 = __float_as_uint(xs[2 * d]), u1 = __float_as_uint(xs[2 * d + 1]);
+        const float w0 = xs[2 * d] - __uint_as_float(u0 & lo_mask);
+        const float w1 = xs[2 * d + 1] - __uint_as_float(u1 & lo_mask);
+        af[d] = __builtin_amdgcn_perm(__float_as_uint(w1), __float_as_uint(w0), 0x07060302u);
+      }
+      bf16x8_t a_p;
+      __builtin_memcpy(&a_p, af, 16);
+      // 6. O += P.V: B fragment of lane (n, g) = value dim 8n + e of the
+      //    pair's slots 4u + g of both tiles, from this lane's own rows
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        auto word = [&](const uint4& x) -> uint32_t {
+          return (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
+        };
+        uint32_t bw[4];
+        bw[0] = __builtin_amdgcn_perm(word(vw[2 * p][1]), word(vw[2 * p][0]), sel);
+        bw[1] = __builtin_amdgcn_perm(word(vw[2 * p][3]), word(vw[2 * p][2]), sel);
+        bw[2] = __builtin_amdgcn_perm(word(vw[2 * p + 1][1]), word(vw[2 * p + 1][0]), sel);
+        bw[3] = __builtin_amdgcn_perm(word(vw[2 * p + 1][3]), word(vw[2 * p + 1][2]), sel);
+        bf16x8_t bv;
+        __builtin_memcpy(&bv, bw, 16);
+        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_p, bv, oacc[e], 0, 0, 0);
+      }
+    }
+    // the wave's (reference, sum) of head rq and its O rows
+    float m_r = mref[0], l_r = 0.0f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float s = group_sum<16>(lsum[h]);
+      const float lh = lane_f(s, 0) + lane_f(s, 16);
+      if (h == 0) l_r = lh;
+      if (rq == h) {
+        m_r = mref[h];
+        l_r = lh;
+      }
+    }
+    m_me = m_r;
+    l_me = l_r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mine[e] = oacc[e][0] + oacc[e][1];
+  }
+  if (nw > 1) {
+    __builtin_amdgcn_wave_barrier();  // the wave's key-tile reads are done
+    if (rq < G) {
+      float* so = &lds.w[wave].o[rq][8 * n];
+      *reinterpret_cast<float4*>(so) = make_float4(mine[0], mine[1], mine[2], mine[3]);
+      *reinterpret_cast<float4*>(so + 4) = make_float4(mine[4], mine[5], mine[6], mine[7]);
+      if (n == 0) {
+        lds.s_ml[wave][0][rq] = m_me;
+        lds.s_ml[wave][1][rq] = l_me;
+      }
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < G * D; t += 64 * nw) {
+      const int h = t / D;
+      const int dim = t % D;
+      // unrolled over the largest workgroup so all LDS reads issue together
+      float mw[kMaxPairWaves], lw[kMaxPairWaves], ow[kMaxPairWaves];
+#pragma unroll
+      for (int w = 0; w < kMaxPairWaves; ++w) {
+        const bool in = w < nw;
+        mw[w] = in ? lds.s_ml[w][0][h] : -INFINITY;
+        lw[w] = in ? lds.s_ml[w][1][h] : 0.0f;
+        ow[w] = in ? lds.w[w].o[h][dim] : 0.0f;
+      }
+      float Mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kMaxPairWaves; ++w) Mx = fmaxf(Mx, mw[w]);
+      float Lx = 0.0f, Ox = 0.0f;
+      if (Mx != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < kMaxPairWaves; ++w) {
+          const float wt = __builtin_amdgcn_exp2f(mw[w] - Mx);
+          Lx = fmaf(lw[w], wt, Lx);
+          Ox = fmaf(ow[w], wt, Ox);
+        }
+      }
+      if (a.nsplit == 1) {
+        a.out[((int64_t)b * a.Hq + (int64_t)r * G + h) * D + dim] = Ox / Lx;
+      } else {
+        float* pp = a.part + ((int64_t)row * a.nsplit + split) * (G * (D + 2));
+        pp[h * D + dim] = Ox;
+        if (dim == 0) {
+          pp[G * D + h] = Mx;
+          pp[G * D + G + h] = Lx;
+        }
+      }
+    }
+    if (touch == 1.0f && a.n_slots < 0) dst_row[1] = 0.0f;  // never true: keeps the read
+    return;
+  }
+  if (rq < G) {
+    if (a.nsplit == 1) {
+      float* dst = a.out + ((int64_t)b * a.Hq + (int64_t)r * G + rq) * D + 8 * n;
+      const float inv = 1.0f / l_me;
+      *reinterpret_cast<float4*>(dst) =
+          make_float4(mine[0] * inv, mine[1] * inv, mine[2] * inv, mine[3] * inv);
+      *reinterpret_cast<float4*>(dst + 4) =
+          make_float4(mine[4] * inv, mine[5] * inv, mine[6] * inv, mine[7] * inv);
+    } else {
+      float* pp = a.part + ((int64_t)row * a.nsplit + split) * (G * (D + 2));
+      float* ph = pp + rq * D + 8 * n;
+      *reinterpret_cast<float4*>(ph) = make_float4(mine[0], mine[1], mine[2], mine[3]);
+      *reinterpret_cast<float4*>(ph + 4) = make_float4(mine[4], mine[5], mine[6], mine[7]);
+      if (n == 0) {
+        pp[G * D + rq] = m_me;
+        pp[G * D + G + rq] = l_me;
+      }
+    }
+  }
+  if (touch == 1.0f && a.n_slots < 0) dst_row[1] = 0.0f;  // never true: keeps the read
+}
+
+template <int G, int MODE, int PAIRS>
+__global__ __launch_bounds__(64 * kMaxPairWaves) void attend_pairs_kernel(AttendArgs a) {
+  __shared__ __align__(16) PairLds<G> lds;
+  attend_pairs_body<G, MODE, PAIRS, false>(a, nullptr, lds);
+}
+
 // Merge, then gather-attend, in one workgroup of kMaxSparseWaves waves per
 // row: the register top-k of the selection's merge picks the row's k tokens
 // from its parts' (score, position) candidates, writes them to the index
 // list and to LDS, and the waves attend over them from LDS -- the same
 // index list and the same per-wave work as the merge launch followed by the
-// whole-row gather-attend launch, without the launch between them and
-// without reading the index list back from memory.
-template <int G, int TILES, int GK>
+// whole-row pair-pipelined gather-attend launch, without the launch between
+// them and without reading the index list back from memory.
+template <int G, int PAIRS, int GK>
 __global__ __launch_bounds__(64 * kMaxSparseWaves) void merge_attend_kernel(
     AttendArgs a, const float* __restrict__ cand_val, const int32_t* __restrict__ cand_pos,
     int n_cand, int64_t cstride, bool vec4, int32_t* __restrict__ idx_out) {
@@ -627,7 +1014,7 @@ __global__ __launch_bounds__(64 * kMaxSparseWaves) void merge_attend_kernel(
   __shared__ uint32_t s_wave[NT / 64];
   __shared__ __align__(16) int32_t s_map[4 * GK * NT];
   __shared__ int32_t s_idx[64 * kMaxSparseWaves];
-  __shared__ __align__(16) AttendLds<G, TILES> lds;
+  __shared__ __align__(16) PairLds<G> lds;
   const int row = blockIdx.y;
   const int n = n_cand;  // <= 4 * GK * NT
   const int32_t k = a.n_idx;
@@ -672,7 +1059,7 @@ __global__ __launch_bounds__(64 * kMaxSparseWaves) void merge_attend_kernel(
   };
   reg_row_topk<NT, GK, false>(load, n, k, emit, sh, cand, s_wave);
   __syncthreads();
-  attend_sparse_body<G, kIdxTokenPerHead, TILES, true>(a, s_idx, lds);
+  attend_pairs_body<G, kIdxTokenPerHead, PAIRS, true>(a, s_idx, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -812,41 +1199,32 @@ hipError_t dispatch_wave(int waves, int rounds, int chunk, int mode, dim3 grid,
   return dispatch_sparse<G, 4>(waves, mode, grid, a, s);
 }
 
+template <int G, int PAIRS>
+hipError_t dispatch_pairs_mode(int mode, dim3 grid, dim3 block, const AttendArgs& a,
+                               hipStream_t s) {
+  if (mode == kIdxTokenShared)
+    hipLaunchKernelGGL((attend_pairs_kernel<G, kIdxTokenShared, PAIRS>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((attend_pairs_kernel<G, kIdxTokenPerHead, PAIRS>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <int G>
+hipError_t dispatch_pairs(int pairs, int waves, int mode, dim3 grid, const AttendArgs& a,
+                          hipStream_t s) {
+  const dim3 block(64 * waves);
+  return pairs == 1 ? dispatch_pairs_mode<G, 1>(mode, grid, block, a, s)
+                    : dispatch_pairs_mode<G, 2>(mode, grid, block, a, s);
+}
+
 bool use_wave_kernel(const Cache& c) {
   return c.kv_dtype == SA_BF16 && c.q_dtype == SA_BF16 && c.D == 128 && c.G <= 4;
 }
 
-// Tuning overrides for selected-set decode: SA_SPARSE_CHUNK fixes the slots
-// per wave (16, 32, 48 or 64), SA_SPARSE_WAVES the waves per workgroup (1 to
-// 12); 0 (unset) leaves the choice to plan_attend.
-int env_choice(const char* name, std::initializer_list<int> allowed) {
-  const char* e = getenv(name);
-  if (!e) return 0;
-  const int x = atoi(e);
-  for (int v : allowed)
-    if (v == x) return x;
-  return 0;
-}
-
-int sparse_chunk_override() {
-  static const int v = env_choice("SA_SPARSE_CHUNK", {16, 32, 48, 64});
-  return v;
-}
-
-int sparse_waves_override() {
-  static const int v = env_choice("SA_SPARSE_WAVES", {1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12});
-  return v;
-}
-
-// Dense decode: SA_DENSE_WAVES (1 to 12) and SA_DENSE_ROUNDS (1 to 64).
-int dense_waves_override() {
-  static const int v = env_choice("SA_DENSE_WAVES", {1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12});
-  return v;
-}
-
-int dense_rounds_override() {
-  static const int v = env_choice("SA_DENSE_ROUNDS", {1, 2, 4, 8, 16, 32, 64});
-  return v;
+// Bytes from a row's first token to the end of its last one: the range its
+// gathered K/V rows lie in.
+int64_t row_span_bytes(const Cache& c) {
+  return ((c.N - 1) * c.st + c.D) * (c.kv_dtype == SA_BF16 ? 2 : 4);
 }
 
 int lanes_per_row(const Cache& c) { return c.D * (c.kv_dtype == SA_BF16 ? 2 : 4) / 16; }
@@ -865,7 +1243,43 @@ AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs) {
   }
   const int64_t rows = (int64_t)c.B * c.Hkv;
   int64_t chunk;
-  if (use_wave_kernel(c)) {
+  p.pairs = 0;
+  if (use_wave_kernel(c) && (mode == kIdxTokenPerHead || mode == kIdxTokenShared) &&
+      row_span_bytes(c) < (int64_t(1) << 32)) {
+    // Selected tokens: waves of one or two pairs of 16-slot tiles.  At least
+    // 128 rows (half the chip's CUs at one workgroup each) and at most 24
+    // pairs: one workgroup takes a whole row, so no split partials and no
+    // combine launch; one pair per wave while 12 waves hold the row, else
+    // two.  Otherwise rows split so that about 512 workgroups run, and a
+    // combine launch merges the splits.
+    p.kernel = kKernPairs;
+    p.rounds = 1;
+    const int64_t np = (p.n_slots + 31) / 32;
+    int waves, pairs;
+    if (rows >= 128 && np <= 2 * kMaxPairWaves) {
+      pairs = np <= kMaxPairWaves ? 1 : 2;
+      waves = (int)((np + pairs - 1) / pairs);
+    } else {
+      pairs = 2;
+      waves = 0;
+      for (int w : {12, 8, 4, 2, 1}) {
+        if (rows * ((np + 2 * w - 1) / (2 * w)) >= 512) {
+          waves = w;
+          break;
+        }
+      }
+      if (waves == 0) {
+        waves = 1;
+        pairs = 1;
+      }
+      // no more waves than the row has pairs for
+      while (waves > 1 && (int64_t)(waves - 1) * pairs >= np) --waves;
+    }
+    p.waves = waves;
+    p.pairs = pairs;
+    chunk = (int64_t)waves * pairs * 32;
+  } else if (use_wave_kernel(c)) {
+    p.kernel = kKernWave;
     // Each wave takes rounds of up to 64 slots with every load of a round in
     // flight at once; the waves of a workgroup merge in LDS.
     const int64_t wn = (p.n_slots + 63) / 64;
@@ -894,14 +1308,12 @@ AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs) {
       // (8 splits) take 320 us against 324.5 us for 8 rounds; on 8 rows of
       // 1M tokens 32 rounds (128 splits) 626 us against 649 us for 8 rounds
       // and 638 us for 64; 8 waves were no faster on either
-      waves = dense_waves_override() ? dense_waves_override() : 4;
-      rounds = dense_rounds_override() ? dense_rounds_override() : 32;
-      if (mode == kIdxDenseScored) waves = std::min(waves, kMaxScoredWaves);
+      waves = 4;
+      rounds = 32;
       // fewer rounds per wave until about 1024 workgroups run (64 rows of
       // 3072 tokens: 12 splits of 256 tokens, not 1 of 3072)
-      if (!dense_rounds_override())
-        while (rounds > 1 && rows * ((p.n_slots + 64 * waves * rounds - 1) / (64 * waves * rounds)) < 1024)
-          rounds /= 2;
+      while (rounds > 1 && rows * ((p.n_slots + 64 * waves * rounds - 1) / (64 * waves * rounds)) < 1024)
+        rounds /= 2;
     } else {
       // selections split so that about 512 workgroups (two per CU) run; a
       // combine pass merges the splits
@@ -914,14 +1326,11 @@ AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs) {
       if (waves == 1)
         while (per_wave > 16 && rows * ((p.n_slots + per_wave - 1) / per_wave) < 512) per_wave /= 2;
     }
-    if (!is_dense_mode(mode)) {
-      if (sparse_waves_override()) waves = sparse_waves_override();
-      if (sparse_chunk_override()) per_wave = sparse_chunk_override();
-    }
     p.waves = waves;
     p.rounds = rounds;
     chunk = per_wave * waves * rounds;
   } else {
+    p.kernel = kKernGeneric;
     p.waves = 4;
     p.rounds = 1;
     const int64_t unit = (int64_t)(kThreads / lanes_per_row(c)) * kUnroll;
@@ -967,6 +1376,7 @@ AttendArgs attend_args(const Cache& c, const AttendPlan& p, const void* q, const
   a.rounds = p.rounds;
   a.out = out;
   a.part = static_cast<float*>(ws);
+  a.row_span = p.kernel == kKernPairs ? (uint32_t)row_span_bytes(c) : 0u;
   return a;
 }
 
@@ -979,7 +1389,13 @@ hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, con
   const int64_t rows = (int64_t)c.B * c.Hkv;
   const dim3 grid(p.nsplit, (unsigned)rows);
   hipError_t e;
-  if (use_wave_kernel(c)) {
+  if (p.kernel == kKernPairs) {
+    switch (c.G) {
+      case 1: e = dispatch_pairs<1>(p.pairs, p.waves, p.mode, grid, a, s); break;
+      case 2: e = dispatch_pairs<2>(p.pairs, p.waves, p.mode, grid, a, s); break;
+      default: e = dispatch_pairs<4>(p.pairs, p.waves, p.mode, grid, a, s); break;
+    }
+  } else if (p.kernel == kKernWave) {
     switch (c.G) {
       case 1: e = dispatch_wave<1>(p.waves, p.rounds, p.chunk, p.mode, grid, a, s); break;
       case 2: e = dispatch_wave<2>(p.waves, p.rounds, p.chunk, p.mode, grid, a, s); break;
@@ -994,8 +1410,9 @@ hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, con
   }
   if (e != hipSuccess || p.nsplit == 1) return e;
   const dim3 cgrid((unsigned)rows, (unsigned)c.G, (unsigned)(c.D / 32));
-  // one-wave selected-set workgroups write the interleaved partial layout
-  const bool vec_layout = use_wave_kernel(c) && p.waves == 1;
+  // one-wave workgroups of the round kernel write the interleaved partial
+  // layout
+  const bool vec_layout = p.kernel == kKernWave && p.waves == 1;
   // the fewest lanes per dimension that cover the splits in one round of
   // sixteen loads (at most 32)
   if (p.nsplit <= 64)
@@ -1015,41 +1432,37 @@ hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, con
 
 namespace {
 
-template <int G, int TILES>
+template <int G, int PAIRS>
 hipError_t launch_merge_attend_g(const AttendArgs& a, int64_t rows, const float* cand_val,
                                  const int32_t* cand_pos, int64_t n_cand, int64_t cstride,
                                  bool vec4, int32_t* idx, hipStream_t s) {
   const dim3 grid(1, (unsigned)rows), block(64 * kMaxSparseWaves);
   if (n_cand <= 4 * 64 * kMaxSparseWaves)
-    hipLaunchKernelGGL((merge_attend_kernel<G, TILES, 1>), grid, block, 0, s, a, cand_val, cand_pos,
+    hipLaunchKernelGGL((merge_attend_kernel<G, PAIRS, 1>), grid, block, 0, s, a, cand_val, cand_pos,
                        (int)n_cand, cstride, vec4, idx);
   else
-    hipLaunchKernelGGL((merge_attend_kernel<G, TILES, 2>), grid, block, 0, s, a, cand_val, cand_pos,
+    hipLaunchKernelGGL((merge_attend_kernel<G, PAIRS, 2>), grid, block, 0, s, a, cand_val, cand_pos,
                        (int)n_cand, cstride, vec4, idx);
   return hipGetLastError();
 }
 
 template <int G>
-hipError_t launch_merge_attend_t(int tiles, const AttendArgs& a, int64_t rows,
+hipError_t launch_merge_attend_t(int pairs, const AttendArgs& a, int64_t rows,
                                  const float* cand_val, const int32_t* cand_pos, int64_t n_cand,
                                  int64_t cstride, bool vec4, int32_t* idx, hipStream_t s) {
-  if (tiles == 2) return launch_merge_attend_g<G, 2>(a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
-  if (tiles == 3) return launch_merge_attend_g<G, 3>(a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
-  return launch_merge_attend_g<G, 4>(a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
+  if (pairs == 1) return launch_merge_attend_g<G, 1>(a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
+  return launch_merge_attend_g<G, 2>(a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
 }
-
-// slots per wave of a whole-row plan (one round, one split)
-int whole_row_tiles(const AttendPlan& p) { return p.chunk / (p.waves * 16); }
 
 }  // namespace
 
 bool merge_attend_ok(const Cache& c, const AttendPlan& p, int64_t n_cand, int32_t k) {
-  if (!use_wave_kernel(c) || p.mode != kIdxTokenPerHead || p.nsplit != 1 || p.rounds != 1 ||
-      p.waves > kMaxSparseWaves || p.n_slots != k)
-    return false;
-  const int tiles = whole_row_tiles(p);
-  return p.chunk == p.waves * 16 * tiles && tiles >= 2 && tiles <= 4 && k >= 1 && n_cand >= k &&
-         n_cand <= 2 * 4 * 64 * kMaxSparseWaves;
+  // the merge's workgroup (kMaxSparseWaves waves) attends over the row as one
+  // whole-row pair plan
+  static_assert(kMaxSparseWaves == kMaxPairWaves, "merge and attend share the workgroup");
+  return p.kernel == kKernPairs && p.mode == kIdxTokenPerHead && p.nsplit == 1 &&
+         p.waves <= kMaxPairWaves && p.n_slots == k && k >= 1 && n_cand >= k &&
+         n_cand <= 2 * 4 * 64 * kMaxSparseWaves && c.G <= 4;
 }
 
 hipError_t launch_merge_attend(const Cache& c, const AttendPlan& p, const void* q, const void* k,
@@ -1060,11 +1473,10 @@ hipError_t launch_merge_attend(const Cache& c, const AttendPlan& p, const void* 
   const int64_t rows = (int64_t)c.B * c.Hkv;
   const bool vec4 = (reinterpret_cast<uintptr_t>(cand_val) % 16 == 0) && (cstride % 4 == 0) &&
                     (reinterpret_cast<uintptr_t>(cand_pos) % 16 == 0);
-  const int tiles = whole_row_tiles(p);
   switch (c.G) {
-    case 1: return launch_merge_attend_t<1>(tiles, a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
-    case 2: return launch_merge_attend_t<2>(tiles, a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
-    default: return launch_merge_attend_t<4>(tiles, a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
+    case 1: return launch_merge_attend_t<1>(p.pairs, a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
+    case 2: return launch_merge_attend_t<2>(p.pairs, a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
+    default: return launch_merge_attend_t<4>(p.pairs, a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
   }
 }
 

@@ -100,13 +100,21 @@ enum IndexMode : int {
 
 inline bool is_dense_mode(int mode) { return mode == kIdxDense || mode == kIdxDenseScored; }
 
+// Which gather-attend kernel a plan runs: lane groups holding whole rows (any
+// dtype and head size), MFMA waves over rounds of tiles (bf16, head_dim 128,
+// dense scans and blocks), or MFMA waves pipelined by pairs of tiles (bf16,
+// head_dim 128, selected tokens).
+enum AttendKernel : int { kKernGeneric = 0, kKernWave = 1, kKernPairs = 2 };
+
 struct AttendPlan {
   int mode;
+  int kernel;       // AttendKernel
   int64_t n_slots;  // selected slots per row (tokens, or block slots)
   int32_t chunk;    // slots per workgroup
   int32_t nsplit;   // workgroups per row
   int32_t waves;    // waves per workgroup
-  int32_t rounds;   // slot rounds per wave (gather kernel)
+  int32_t rounds;   // slot rounds per wave (kKernWave)
+  int32_t pairs;    // pairs of 16-slot tiles per wave (kKernPairs)
   size_t ws_bytes;  // split partials (0 when nsplit == 1)
 };
 
