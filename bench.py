@@ -12,24 +12,27 @@ copies of the cache (2.15 GB each, all resident in HBM before timing starts;
 finds the previous step's rows in cache.
 
 Timing: W untimed warmup steps, then K timed steps bracketed by
-torch.cuda.synchronize().  Each step is captured once per query variant as a
-HIP graph of its three launches and replayed (a serving loop's form; --eager
-times plain launches instead); the bench checks that a replay selects and
-attends exactly as an eager step.  A separate pass of eager steps with HIP
-events recorded on the launch stream between the two calls gives each call's
-average duration.
+torch.cuda.synchronize().  Each step is captured once per (query variant,
+cache copy) as a HIP graph of its three launches and replayed (a serving
+loop's form; --eager times plain launches instead); the bench checks that a
+replay selects and attends exactly as an eager step.
 
-Prints ONE JSON line.  `value` is the step's achieved HBM bandwidth
-(algorithmic bytes of selection + attend per step / time per step);
-`steps_per_s` is the decode-step rate; `roofline` is the dominant unit (the
-sa_select call: its fused kernel and merge); `kernels` holds each unit's
-bytes, time and fraction of the 8 TB/s peak, including the gather-attend
-alone, the unfused selection (sa_score then sa_topk on the same inputs) and a
-dense decode over the same cache for comparison; `stream_read` is the
-device's streaming read rate (sa_stream_read over 8 GiB), and the step's and
-the dominant unit's rates are also given as fractions of it.  `cpu_baseline` times the
-CPU oracle on a bounded sample of the same step (rows of the batch), scaled
-to a full step.
+Prints ONE JSON line.  `value` is the gather-attend's achieved HBM bandwidth
+(its algorithmic bytes, 43.65 MB per call, over its time per call): each
+(query variant, cache copy) pair's index set is selected once, the 8
+sa_sparse_decode calls over the 8 copies are captured back to back in one
+HIP graph, and its replays are timed with HIP events on the launch stream
+(consecutive calls read different copies, 8 x 43.65 MB exceeding the 256 MB
+last-level cache).  `roofline` is that kernel against the 8 TB/s peak;
+`ms_per_step` / `steps_per_s` are the K timed full decode steps (selection +
+gather-attend) and `step` their bandwidth; `kernels` holds per-call times:
+the same attend timed inside eager steps, the selection, the unfused
+selection (sa_score then sa_topk) and a dense decode for comparison, and two
+cache-cold single launches after a 1 GiB read -- the gather-attend and
+sa_stream_read over the same number of bytes (the floor for one launch of
+that size).  `stream_read` is sa_stream_read over 8 GiB.  `cpu_baseline`
+times the CPU oracle's selected-set attention (and its full step) on whole
+rows of one step, scaled to a step.
 
 Other modes (each prints its own JSON line): --sweep (full step with four
 selection front ends against dense decode at 2x-500x on the llama32k and
@@ -136,8 +139,8 @@ _SEL_SRC = ["top_sparse_decode_sa_amd/csrc/select.hip", "top_sparse_decode_sa_am
             "top_sparse_decode_sa_amd/csrc/topk_core.hpp", "top_sparse_decode_sa_amd/csrc/common.hpp"]
 TRAFFIC_KERNELS = {
     "select": (["select_part_kernel", "topk_reg_kernel<512, 2, true>"], _SEL_SRC),
-    "sparse_attend": (["attend_sparse_kernel"], ["top_sparse_decode_sa_amd/csrc/attend.hip",
-                                                 "top_sparse_decode_sa_amd/csrc/common.hpp"]),
+    "sparse_attend": (["attend_pairs_kernel"], ["top_sparse_decode_sa_amd/csrc/attend.hip",
+                                                "top_sparse_decode_sa_amd/csrc/common.hpp"]),
     "score_exact": (["score_exact_kernel"], ["top_sparse_decode_sa_amd/csrc/score.hip",
                                              "top_sparse_decode_sa_amd/csrc/common.hpp"]),
     "topk": (["topk_reg_kernel<1024, 8, false>"], ["top_sparse_decode_sa_amd/csrc/topk.hip",
@@ -348,9 +351,12 @@ def step_bytes(cfg):
     }
 
 
-def cpu_baseline(w, q_host, k_host, v_host, seconds):
-    """Time the oracle, one BLAS thread, on whole rows of the step until
-    `seconds` elapse; returns (seconds per full step, rows timed, rows)."""
+def cpu_baseline(w, q_host, k_host, v_host, idx_host, seconds):
+    """Time the oracle, one BLAS thread, on whole (sequence, KV head) rows of
+    one step until `seconds` elapse: its selected-set attention over the
+    GPU's index set of the row (the headline's unit) and its full step
+    (exact scores, top-k, attention).  Returns (seconds of attention per
+    step, seconds of the full step per step, rows timed, rows)."""
     import oracle as O
     from threadpoolctl import threadpool_limits
 
@@ -358,21 +364,30 @@ def cpu_baseline(w, q_host, k_host, v_host, seconds):
     scale = O.default_scale(c.head_dim)
     rows = c.batch * c.n_kv_heads
     rows_done = 0
+    t_att = t_step = 0.0
     with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
         qf = O.widen(q_host[0])
+        t_all = time.perf_counter()
         for row in range(rows):
             b, r = divmod(row, c.n_kv_heads)
             qg = qf[b, r * c.group:(r + 1) * c.group]
+            t0 = time.perf_counter()
             kf = O.widen(k_host[b, r])
+            vf = O.widen(v_host[b, r])
+            t1 = time.perf_counter()
+            O.attend(qg, kf, vf, idx_host[b, r], scale)
+            t2 = time.perf_counter()
             s = O.scores_exact(qg, kf, scale)
             sel = O.topk(s, c.k)
-            O.attend(qg, kf, O.widen(v_host[b, r]), sel, scale)
+            O.attend(qg, kf, vf, sel, scale)
+            t3 = time.perf_counter()
+            # the rows' widening to fp64 is part of both
+            t_att += (t1 - t0) + (t2 - t1)
+            t_step += (t1 - t0) + (t3 - t2)
             rows_done += 1
-            if time.perf_counter() - t0 >= seconds:
+            if time.perf_counter() - t_all >= seconds:
                 break
-        dt = time.perf_counter() - t0
-    return dt * rows / rows_done, rows_done, rows
+    return t_att * rows / rows_done, t_step * rows / rows_done, rows_done, rows
 
 
 SWEEP_X = (2, 5, 10, 20, 50, 100, 200, 500)
@@ -1131,8 +1146,9 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # the timed steps: each step captured once per query variant as a HIP
-    # graph (the three launches of one decode step), replayed in turn
+    # the timed steps: each step captured once per (query variant, cache
+    # copy) as a HIP graph (the three launches of one decode step), replayed
+    # in turn
     graphs = []
     n_graph = N_QVAR * n_rep // math.gcd(N_QVAR, n_rep)
     if not args.eager:
@@ -1163,9 +1179,48 @@ def main():
     wall = time.perf_counter() - t_start
     ms_step = wall * 1e3 / args.steps
 
-    # per-kernel durations: eager steps with HIP events between the calls, on
-    # the launch stream (a separate pass, so the events do not slow the
-    # timed steps)
+    # The gather-attend alone (the headline): every (query variant, cache
+    # copy) pair's own index set, selected once, then the n_graph attends
+    # captured back to back in one graph whose replays are timed with events
+    # on the launch stream.  Consecutive attends read different copies
+    # (n_graph x 43.65 MB > the 256 MB last-level cache), so each finds its
+    # rows evicted, as in the step.
+    idx_v = [torch.empty_like(idx) for _ in range(n_graph)]
+    out_v = [torch.empty_like(out) for _ in range(n_graph)]
+    for v in range(n_graph):
+        T.sa_select(qd[v % N_QVAR], kds[v % n_rep], c.k, idx_out=idx_v[v])
+
+    def attends():
+        for v in range(n_graph):
+            T.sa_sparse_decode(qd[v % N_QVAR], kds[v % n_rep], vds[v % n_rep], idx_v[v], out=out_v[v])
+
+    attends()
+    torch.cuda.synchronize()
+    eager_out = [o.clone() for o in out_v]
+    g_att = None
+    if not args.eager:
+        g_att = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_att):
+            attends()
+        g_att.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a_, b_) for a_, b_ in zip(out_v, eager_out)), \
+            "attend graph replay differs from eager"
+    n_att_rep = max(25, args.steps // n_graph)
+    for _ in range(3):
+        g_att.replay() if g_att else attends()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n_att_rep):
+        g_att.replay() if g_att else attends()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_attend = e0.elapsed_time(e1) / (n_att_rep * n_graph)
+
+    # per-call durations inside eager steps: HIP events on the launch stream
+    # between the two calls (each event pair also holds its launch's
+    # dispatch, a few us)
     n_ev = min(args.steps, 100)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
     torch.cuda.synchronize()
@@ -1175,7 +1230,7 @@ def main():
     torch.cuda.synchronize()
     ms_step_eager = (time.perf_counter() - t_ev) * 1e3 / n_ev
     ms_select = sum(e[0].elapsed_time(e[1]) for e in events) / n_ev
-    ms_attend = sum(e[1].elapsed_time(e[2]) for e in events) / n_ev
+    ms_attend_in_step = sum(e[1].elapsed_time(e[2]) for e in events) / n_ev
 
     # the unfused selection on the same inputs, for comparison: every score
     # written by sa_score, then sa_topk over them (same index list)
@@ -1220,8 +1275,7 @@ def main():
         torch.cuda.synchronize()
         ms_dense = e0.elapsed_time(e1) / args.dense_steps
 
-    # the device's streaming read rate (sa_stream_read over 8 GiB): the
-    # reference the rates above are also read against
+    # the device's streaming read rate (sa_stream_read over 8 GiB)
     stream = None
     if args.stream_gib > 0:
         nbytes_s = args.stream_gib << 30
@@ -1242,84 +1296,97 @@ def main():
         del buf, sink
         torch.cuda.empty_cache()
 
-    # cache-cold gather-attend: before each launch a 1 GiB read evicts L2 and
-    # the 256 MB last-level cache, as other layers' traffic would between
-    # decode steps; beside it, the same kernel over the same number of bytes
-    # read contiguously (a dense decode of the first k tokens of every row),
-    # the cold-read floor at this size
+    nbytes = step_bytes(c)
+    att_bytes = nbytes["sparse_attend"]
+
+    # cache-cold single launches: before each, a 1 GiB read evicts L2 and the
+    # 256 MB last-level cache; the gather-attend, and beside it the same
+    # number of bytes read by the library's streaming read (the floor a
+    # single launch of this size can reach on this device)
     cold = None
     if args.cold_iters > 0:
         flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
-        kpre, vpre = kd[:, :, :c.k], vd[:, :, :c.k]
+        sbuf = torch.empty(att_bytes // 16 * 16, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
         cout = torch.empty_like(out)
-        times = {"sparse": [], "contig": []}
+        times = {"sparse": [], "stream": []}
         for i in range(args.cold_iters + 2):
-            for name in ("sparse", "contig"):
+            for name in ("sparse", "stream"):
                 flush.sum()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
                 if name == "sparse":
-                    T.sa_sparse_decode(qd[0], kd, vd, idx, out=cout)
+                    T.sa_sparse_decode(qd[0], kd, vd, idx_v[0], out=cout)
                 else:
-                    T.sa_dense_decode(qd[0], kpre, vpre, out=cout)
+                    T.sa_stream_read(sbuf, sink)
                 e1.record()
                 torch.cuda.synchronize()
                 if i >= 2:
                     times[name].append(e0.elapsed_time(e1))
-        del flush
+        del flush, sbuf
         cold = {name: float(np.median(v)) for name, v in times.items()}
 
-    nbytes = step_bytes(c)
-    step_total = nbytes["select"] + nbytes["sparse_attend"]
-    gbps = step_total / (ms_step * 1e-3) / 1e9
+    step_total = nbytes["select"] + att_bytes
 
-    def kern(name, ms):
+    def kern(name, ms, nb=None):
         if ms is None:
             return None
-        g = nbytes[name] / (ms * 1e-3) / 1e9
-        return {"bytes": nbytes[name], "us": round(ms * 1e3, 3), "gbps": round(g, 1),
+        nb = nbytes[name] if nb is None else nb
+        g = nb / (ms * 1e-3) / 1e9
+        return {"bytes": nb, "us": round(ms * 1e3, 3), "gbps": round(g, 1),
                 "frac": round(g / HBM_PEAK_GBPS, 4)}
 
-    kernels = {"select": kern("select", ms_select),
-               "sparse_attend": kern("sparse_attend", ms_attend),
+    att = kern("sparse_attend", ms_attend)
+    kernels = {"sparse_attend": att,
+               "sparse_attend_in_step": kern("sparse_attend", ms_attend_in_step),
+               "select": kern("select", ms_select),
                "score_exact": kern("score_exact", ms_score), "topk": kern("topk", ms_topk),
                "dense_decode": kern("dense_decode", ms_dense)}
+    floor = None
     if cold:
         kernels["sparse_attend_cold"] = kern("sparse_attend", cold["sparse"])
-        kernels["contiguous_same_bytes_cold"] = kern("sparse_attend", cold["contig"])
-    # dominant kernel of the step: the one with the largest share of its time
-    dom = max(["select", "sparse_attend"], key=lambda n: kernels[n]["us"])
-    roof = {"bound": "hbm", "achieved": kernels[dom]["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": kernels[dom]["frac"],
-            "traffic": read_traffic(dom), "kernel": dom,
-            "bytes_per_launch": nbytes[dom]}
+        floor = kern("sparse_attend", cold["stream"], nb=att_bytes // 16 * 16)
+        kernels["stream_read_same_bytes_cold"] = floor
+    roof = {"bound": "hbm", "achieved": att["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": att["frac"], "traffic": read_traffic("sparse_attend"),
+            "kernel": "sparse_attend", "bytes_per_launch": att_bytes}
     if stream:
-        roof["frac_of_stream_read"] = round(kernels[dom]["gbps"] / stream["gbps"], 4)
+        roof["frac_of_stream_read"] = round(att["gbps"] / stream["gbps"], 4)
+    if cold:
+        # the cold single launch against a cold streaming read of its bytes
+        roof["cold_frac_of_same_bytes_stream"] = round(cold["stream"] / cold["sparse"], 4)
 
     cpu = None
     if args.cpu_seconds > 0:
         log("bench: oracle cpu baseline (bounded to %.0f s)" % args.cpu_seconds)
-        step_s, done, total = cpu_baseline(w, q_host, k_host, v_host, args.cpu_seconds)
-        cpu = {"value": round(step_total / step_s / 1e9, 4), "unit": "GB/s", "cores": 1,
-               "kind": "oracle", "steps_per_s": round(1.0 / step_s, 4),
-               "sample": "fp64 numpy oracle, one thread: score+top-k+attend of %d of the %d "
-                         "(sequence, KV head) rows of one step, scaled by %d/%d" % (
+        idx_host = idx_v[0].cpu().numpy()
+        att_s, step_s, done, total = cpu_baseline(w, q_host, k_host, v_host, idx_host,
+                                                  args.cpu_seconds)
+        cpu = {"value": round(att_bytes / att_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle", "steps_per_s": round(1.0 / att_s, 4),
+               "full_step_steps_per_s": round(1.0 / step_s, 4),
+               "sample": "fp64 numpy oracle, one thread: selected-set attention over the GPU's "
+                         "index sets of %d of the %d (sequence, KV head) rows of one step, scaled "
+                         "by %d/%d; full_step adds the oracle's exact scores and top-k" % (
                              done, total, total, done)}
         cpu.update(host_cpu())
 
     line = {
         "metric": "sparse-decode attn: achieved HBM GB/s (% of peak) + decode steps/s at 50x",
-        "value": round(gbps, 1),
+        "value": att["gbps"],
         "unit": "GB/s",
-        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "hbm_frac": att["frac"],
+        "attend_us": att["us"],
+        "attend_steps_per_s": round(1e3 / ms_attend, 1),
         "steps_per_s": round(1e3 / ms_step, 1),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
-        "timing": "eager launches" if args.eager else "each step a replayed HIP graph (3 launches)",
-        "step": "sa_select (fused exact scoring + part top-k, merge) -> sa_sparse_decode",
-        "ms_per_step_eager_with_events": round(ms_step_eager, 4),
+        "timing": ("value: the gather-attend alone, %d attends over %d cache copies captured back "
+                   "to back in a HIP graph, replayed %d times between HIP events; ms_per_step and "
+                   "steps_per_s: the K timed decode steps (selection + gather-attend), each a "
+                   "replayed HIP graph" % (n_graph, n_rep, n_att_rep)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -1330,10 +1397,16 @@ def main():
                    "head_dim": c.head_dim, "ctx_len": c.ctx_len, "k": c.k,
                    "kv_dtype": c.dtype, "kv_replicas": n_rep, "parallelism": "single GPU"},
         "roofline": roof,
+        "step": {"what": "sa_select (fused exact scoring + part top-k, merge) -> sa_sparse_decode",
+                 "ms_per_step": round(ms_step, 4), "steps_per_s": round(1e3 / ms_step, 1),
+                 "gbps": round(step_total / (ms_step * 1e-3) / 1e9, 1),
+                 "frac": round(step_total / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                 "bytes": step_total,
+                 "timing": "eager launches" if args.eager else "each step a replayed HIP graph",
+                 "ms_per_step_eager_with_events": round(ms_step_eager, 4)},
         "kernels": kernels,
         "sparse_over_dense_speedup": (round(ms_dense / ms_attend, 2) if ms_dense else None),
         "stream_read": stream,
-        "value_frac_of_stream_read": (round(gbps / stream["gbps"], 4) if stream else None),
         "cpu_baseline": cpu,
         "provenance": provenance(clocks=not args.profile),
     }

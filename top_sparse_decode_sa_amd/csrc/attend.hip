@@ -70,6 +70,7 @@ struct AttendArgs {
   float* out;
   float* part;  // [rows, nsplit, G, D + 2]: o[G][D], m[G], l[G]
   uint32_t row_span;  // pair kernel: bytes of one row's cache, N * st * 2 (< 2^32)
+  int32_t rows;       // B * Hkv
 };
 
 // Buffer resource word 3 of a raw (stride 0) buffer of 32-bit data; loads
@@ -84,6 +85,12 @@ constexpr int kBufferNT = 2;
 __device__ __forceinline__ uint4 ld16_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kBufferNT);
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 ld8_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kBufferNT);
+  return make_uint2(v.x, v.y);
 }
 
 template <int MODE>
@@ -674,19 +681,27 @@ __device__ __forceinline__ float lane_f(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
 
-template <int G, int MODE, int PAIRS, bool LIDX>
+// VH = 1: the workgroup computes all head_dim output dimensions of its slot
+// range.  VH = 2: two workgroups share a whole row, each computing the
+// output of one half of the value dimensions over all of the row's slots:
+// both read every selected key row and the half of every value row they
+// need, compute the same softmax, and write disjoint halves of the output --
+// no partial results cross workgroups.
+template <int G, int MODE, int PAIRS, bool LIDX, int VH>
 __device__ __forceinline__ void attend_pairs_body(const AttendArgs& a, const int32_t* lidx,
-                                                  PairLds<G>& lds) {
+                                                  PairLds<G>& lds, int row, int split, int half) {
   static_assert(G >= 1 && G <= 4, "query heads of a group fit MFMA rows 0..3");
+  static_assert(VH == 1 || VH == 2, "whole rows or value halves");
   constexpr int D = 128;
+  constexpr int DV = D / VH;    // value dimensions of this workgroup
+  constexpr int NE = 8 / VH;    // P.V MFMAs per pair (16 dimensions each)
+  constexpr int VW = 4 / VH;    // 32-bit words of a lane's value piece
   constexpr int TILES = 2 * PAIRS;
   const int nw = blockDim.x >> 6;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int n = lane & 15;
   const int rq = lane >> 4;
-  const int row = blockIdx.y;
-  const int split = blockIdx.x;
   const int b = row / a.Hkv;
   const int r = row % a.Hkv;
   const int64_t wg0 = (int64_t)split * a.chunk;
@@ -695,14 +710,16 @@ __device__ __forceinline__ void attend_pairs_body(const AttendArgs& a, const int
   const int64_t s1 = min(s0 + 32 * PAIRS, wg1);
 
   float m_me = -INFINITY, l_me = 0.0f;
-  float mine[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  float mine[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) mine[e] = 0.0f;
   if (lane < 8) lds.s_zero[lane] = 0.0f;
-  // Where this workgroup writes its result; a word of it is read early (see
-  // below), so the page's address translation is in place when the result
-  // is stored at the very end (a translation miss there would follow the
-  // last row's arrival).  The value read is never used.
+  // Where this workgroup writes its result (head 0); a word of it is read
+  // early (see below), so the page's address translation is in place when
+  // the result is stored at the very end (a translation miss there would
+  // follow the last row's arrival).  The value read is never used.
   float* const dst_row = a.nsplit == 1
-                             ? a.out + ((int64_t)b * a.Hq + (int64_t)r * G) * D
+                             ? a.out + ((int64_t)b * a.Hq + (int64_t)r * G) * D + half * DV
                              : a.part + ((int64_t)row * a.nsplit + split) * (G * (D + 2));
   float touch = 0.0f;
   if (s0 < wg1) {  // uniform: the wave has slots
@@ -738,16 +755,28 @@ __device__ __forceinline__ void attend_pairs_body(const AttendArgs& a, const int
                 row_bytes;
     }
     // 2. tile by tile (so pair by pair), the key and the value row pieces of
-    //    each token: lane (n, rq) reads bytes [16n, +16) of token 4u + rq of
-    //    the tile (load u), so every 8 lanes read one whole 128-byte line.
-    uint4 kl[TILES][4], vw[TILES][4];
+    //    token 4u + rq of the tile (load u): lane (n, rq) reads key bytes
+    //    [16n, +16) and value bytes [DV*2*half + 16n/VH, +16/VH), so every
+    //    8 (values of a half: 16) lanes read one whole 128-byte line.
+    uint4 kl[TILES][4];
+    uint32_t vw[TILES][4][VW];
 #pragma unroll
     for (int i = 0; i < TILES; ++i)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint32_t off = (uint32_t)__shfl((int)toff[i], 4 * u + rq) + 16 * n;
-        kl[i][u] = ld16_buf(rk, off);
-        vw[i][u] = ld16_buf(rv, off);
+        const uint32_t base = (uint32_t)__shfl((int)toff[i], 4 * u + rq);
+        kl[i][u] = ld16_buf(rk, base + 16 * n);
+        if constexpr (VH == 1) {
+          const uint4 x = ld16_buf(rv, base + 16 * n);
+          vw[i][u][0] = x.x;
+          vw[i][u][1] = x.y;
+          vw[i][u][2] = x.z;
+          vw[i][u][3] = x.w;
+        } else {
+          const uint2 x = ld8_buf(rv, base + DV * 2 * half + 8 * n);
+          vw[i][u][0] = x.x;
+          vw[i][u][1] = x.y;
+        }
       }
     // after the rows, so no wait for a row waits for it (a per-lane address:
     // a vector load, counted with the rows)
@@ -761,9 +790,9 @@ __device__ __forceinline__ void attend_pairs_body(const AttendArgs& a, const int
       mref[h] = 0.0f;
       lsum[h] = 0.0f;
     }
-    f32x4_t oacc[8];
+    f32x4_t oacc[NE];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) oacc[e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int e = 0; e < NE; ++e) oacc[e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     const int ha = n >> 2;  // A row n of P.V: head n / 4, part n % 4 (0 hi, 1 lo)
     const bool arow = (n & 3) < 2 && ha < G;
     const uint32_t lo_mask = (n & 3) == 1 ? 0xffff0000u : 0u;
@@ -777,7 +806,7 @@ __device__ __forceinline__ void attend_pairs_body(const AttendArgs& a, const int
       __builtin_amdgcn_sched_barrier(0);
       // 3. logits of both tiles (rows 0..G-1, lanes 0..15 of each result),
       //    then the second tile's rows moved to lanes 16..31: lanes 0..15
-      //    hold tile 2p, lanes 16..31 tile 2p + 1
+      //    hold tile 2p, lanes 16..31 tile 2p + 1.
       //    Each tile goes through the wave's LDS tile: stored as loaded,
       //    read back as MFMA B fragments (lane (n, rq) of fragment c: token n,
       //    dims [32c + 8rq, +8), i.e. chunk 4c + rq).
@@ -851,7 +880,7 @@ __device__ __forceinline__ void attend_pairs_body(const AttendArgs& a, const int
             }
           }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
+          for (int e = 0; e < NE; ++e) {
             oacc[e][0] *= alpha_me;
             oacc[e][1] *= alpha_me;
           }
@@ -884,19 +913,17 @@ __device__ __forceinline__ void attend_pairs_body(const AttendArgs& a, const int
       }
       bf16x8_t a_p;
       __builtin_memcpy(&a_p, af, 16);
-      // 6. O += P.V: B fragment of lane (n, g) = value dim 8n + e of the
+      // 6. O += P.V: B fragment of lane (n, g) = value dim NE*n + e of the
       //    pair's slots 4u + g of both tiles, from this lane's own rows
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < NE; ++e) {
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        auto word = [&](const uint4& x) -> uint32_t {
-          return (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
-        };
+        const int wi = e >> 1;
         uint32_t bw[4];
-        bw[0] = __builtin_amdgcn_perm(word(vw[2 * p][1]), word(vw[2 * p][0]), sel);
-        bw[1] = __builtin_amdgcn_perm(word(vw[2 * p][3]), word(vw[2 * p][2]), sel);
-        bw[2] = __builtin_amdgcn_perm(word(vw[2 * p + 1][1]), word(vw[2 * p + 1][0]), sel);
-        bw[3] = __builtin_amdgcn_perm(word(vw[2 * p + 1][3]), word(vw[2 * p + 1][2]), sel);
+        bw[0] = __builtin_amdgcn_perm(vw[2 * p][1][wi], vw[2 * p][0][wi], sel);
+        bw[1] = __builtin_amdgcn_perm(vw[2 * p][3][wi], vw[2 * p][2][wi], sel);
+        bw[2] = __builtin_amdgcn_perm(vw[2 * p + 1][1][wi], vw[2 * p + 1][0][wi], sel);
+        bw[3] = __builtin_amdgcn_perm(vw[2 * p + 1][3][wi], vw[2 * p + 1][2][wi], sel);
         bf16x8_t bv;
         __builtin_memcpy(&bv, bw, 16);
         oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_p, bv, oacc[e], 0, 0, 0);
@@ -917,23 +944,24 @@ __device__ __forceinline__ void attend_pairs_body(const AttendArgs& a, const int
     m_me = m_r;
     l_me = l_r;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) mine[e] = oacc[e][0] + oacc[e][1];
+    for (int e = 0; e < NE; ++e) mine[e] = oacc[e][0] + oacc[e][1];
   }
   if (nw > 1) {
     __builtin_amdgcn_wave_barrier();  // the wave's key-tile reads are done
     if (rq < G) {
-      float* so = &lds.w[wave].o[rq][8 * n];
-      *reinterpret_cast<float4*>(so) = make_float4(mine[0], mine[1], mine[2], mine[3]);
-      *reinterpret_cast<float4*>(so + 4) = make_float4(mine[4], mine[5], mine[6], mine[7]);
+      float* so = &lds.w[wave].o[rq][NE * n];
+#pragma unroll
+      for (int e = 0; e < NE; e += 4)
+        *reinterpret_cast<float4*>(so + e) = make_float4(mine[e], mine[e + 1], mine[e + 2], mine[e + 3]);
       if (n == 0) {
         lds.s_ml[wave][0][rq] = m_me;
         lds.s_ml[wave][1][rq] = l_me;
       }
     }
     __syncthreads();
-    for (int t = threadIdx.x; t < G * D; t += 64 * nw) {
-      const int h = t / D;
-      const int dim = t % D;
+    for (int t = threadIdx.x; t < G * DV; t += 64 * nw) {
+      const int h = t / DV;
+      const int dim = t % DV;
       // unrolled over the largest workgroup so all LDS reads issue together
       float mw[kMaxPairWaves], lw[kMaxPairWaves], ow[kMaxPairWaves];
 #pragma unroll
@@ -956,9 +984,9 @@ __device__ __forceinline__ void attend_pairs_body(const AttendArgs& a, const int
         }
       }
       if (a.nsplit == 1) {
-        a.out[((int64_t)b * a.Hq + (int64_t)r * G + h) * D + dim] = Ox / Lx;
+        dst_row[h * D + dim] = Ox / Lx;
       } else {
-        float* pp = a.part + ((int64_t)row * a.nsplit + split) * (G * (D + 2));
+        float* pp = dst_row;
         pp[h * D + dim] = Ox;
         if (dim == 0) {
           pp[G * D + h] = Mx;
@@ -970,31 +998,53 @@ __device__ __forceinline__ void attend_pairs_body(const AttendArgs& a, const int
     return;
   }
   if (rq < G) {
+    float* dst = dst_row + rq * D + NE * n;
     if (a.nsplit == 1) {
-      float* dst = a.out + ((int64_t)b * a.Hq + (int64_t)r * G + rq) * D + 8 * n;
       const float inv = 1.0f / l_me;
-      *reinterpret_cast<float4*>(dst) =
-          make_float4(mine[0] * inv, mine[1] * inv, mine[2] * inv, mine[3] * inv);
-      *reinterpret_cast<float4*>(dst + 4) =
-          make_float4(mine[4] * inv, mine[5] * inv, mine[6] * inv, mine[7] * inv);
+#pragma unroll
+      for (int e = 0; e < NE; e += 4)
+        *reinterpret_cast<float4*>(dst + e) =
+            make_float4(mine[e] * inv, mine[e + 1] * inv, mine[e + 2] * inv, mine[e + 3] * inv);
     } else {
-      float* pp = a.part + ((int64_t)row * a.nsplit + split) * (G * (D + 2));
-      float* ph = pp + rq * D + 8 * n;
-      *reinterpret_cast<float4*>(ph) = make_float4(mine[0], mine[1], mine[2], mine[3]);
-      *reinterpret_cast<float4*>(ph + 4) = make_float4(mine[4], mine[5], mine[6], mine[7]);
+#pragma unroll
+      for (int e = 0; e < NE; e += 4)
+        *reinterpret_cast<float4*>(dst + e) = make_float4(mine[e], mine[e + 1], mine[e + 2], mine[e + 3]);
       if (n == 0) {
-        pp[G * D + rq] = m_me;
-        pp[G * D + G + rq] = l_me;
+        dst_row[G * D + rq] = m_me;
+        dst_row[G * D + G + rq] = l_me;
       }
     }
   }
   if (touch == 1.0f && a.n_slots < 0) dst_row[1] = 0.0f;  // never true: keeps the read
 }
 
-template <int G, int MODE, int PAIRS>
+// Workgroup -> (row, split, value half).  With value halves the grid is 1-D
+// and the two halves of a row are workgroups id and id + 8 of each group of
+// 16: workgroups are dispatched to the chip's 8 XCDs in turn, so both land on
+// the same XCD and the second reading of a key row finds it in that XCD's L2
+// (only a matter of speed: the halves exchange nothing).
+template <int VH>
+__device__ __forceinline__ bool pairs_coords(const AttendArgs& a, int& row, int& split, int& half) {
+  if constexpr (VH == 2) {
+    const int id = blockIdx.x;
+    half = (id >> 3) & 1;
+    row = (id >> 4) * 8 + (id & 7);
+    split = 0;
+    return row < a.rows;
+  } else {
+    row = blockIdx.y;
+    split = blockIdx.x;
+    half = 0;
+    return true;
+  }
+}
+
+template <int G, int MODE, int PAIRS, int VH>
 __global__ __launch_bounds__(64 * kMaxPairWaves) void attend_pairs_kernel(AttendArgs a) {
   __shared__ __align__(16) PairLds<G> lds;
-  attend_pairs_body<G, MODE, PAIRS, false>(a, nullptr, lds);
+  int row, split, half;
+  if (!pairs_coords<VH>(a, row, split, half)) return;
+  attend_pairs_body<G, MODE, PAIRS, false, VH>(a, nullptr, lds, row, split, half);
 }
 
 // Merge, then gather-attend, in one workgroup of kMaxSparseWaves waves per
@@ -1004,7 +1054,7 @@ __global__ __launch_bounds__(64 * kMaxPairWaves) void attend_pairs_kernel(Attend
 // index list and the same per-wave work as the merge launch followed by the
 // whole-row pair-pipelined gather-attend launch, without the launch between
 // them and without reading the index list back from memory.
-template <int G, int PAIRS, int GK>
+template <int G, int PAIRS, int GK, int VH>
 __global__ __launch_bounds__(64 * kMaxSparseWaves) void merge_attend_kernel(
     AttendArgs a, const float* __restrict__ cand_val, const int32_t* __restrict__ cand_pos,
     int n_cand, int64_t cstride, bool vec4, int32_t* __restrict__ idx_out) {
@@ -1015,7 +1065,8 @@ __global__ __launch_bounds__(64 * kMaxSparseWaves) void merge_attend_kernel(
   __shared__ __align__(16) int32_t s_map[4 * GK * NT];
   __shared__ int32_t s_idx[64 * kMaxSparseWaves];
   __shared__ __align__(16) PairLds<G> lds;
-  const int row = blockIdx.y;
+  int row, split, half;
+  if (!pairs_coords<VH>(a, row, split, half)) return;
   const int n = n_cand;  // <= 4 * GK * NT
   const int32_t k = a.n_idx;
   const float* __restrict__ sv = cand_val + (int64_t)row * cstride;
@@ -1052,14 +1103,16 @@ __global__ __launch_bounds__(64 * kMaxSparseWaves) void merge_attend_kernel(
   };
   // s_map is complete before the ordered write: reg_row_topk passes several
   // barriers between the load and the write
+  // with value halves both workgroups of a row select (the same list);
+  // half 0 writes it
   auto emit = [&](uint32_t slot, int32_t p) {
     const int32_t t = s_map[p];
-    out[slot] = t;
+    if (half == 0) out[slot] = t;
     s_idx[slot] = t;
   };
   reg_row_topk<NT, GK, false>(load, n, k, emit, sh, cand, s_wave);
   __syncthreads();
-  attend_pairs_body<G, kIdxTokenPerHead, PAIRS, true>(a, s_idx, lds);
+  attend_pairs_body<G, kIdxTokenPerHead, PAIRS, true, VH>(a, s_idx, lds, row, split, half);
 }
 
 // ---------------------------------------------------------------------------
@@ -1199,22 +1252,31 @@ hipError_t dispatch_wave(int waves, int rounds, int chunk, int mode, dim3 grid,
   return dispatch_sparse<G, 4>(waves, mode, grid, a, s);
 }
 
-template <int G, int PAIRS>
+template <int G, int PAIRS, int VH>
 hipError_t dispatch_pairs_mode(int mode, dim3 grid, dim3 block, const AttendArgs& a,
                                hipStream_t s) {
   if (mode == kIdxTokenShared)
-    hipLaunchKernelGGL((attend_pairs_kernel<G, kIdxTokenShared, PAIRS>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((attend_pairs_kernel<G, kIdxTokenShared, PAIRS, VH>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((attend_pairs_kernel<G, kIdxTokenPerHead, PAIRS>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((attend_pairs_kernel<G, kIdxTokenPerHead, PAIRS, VH>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
+// Grid of a pair plan: (nsplit, rows), or with value halves one workgroup
+// per (row, half) in groups of 16 (8 rows, both halves; pairs_coords).
+dim3 pairs_grid(const AttendPlan& p, int64_t rows) {
+  if (p.vhalves == 2) return dim3((unsigned)(16 * ((rows + 7) / 8)));
+  return dim3((unsigned)p.nsplit, (unsigned)rows);
+}
+
 template <int G>
-hipError_t dispatch_pairs(int pairs, int waves, int mode, dim3 grid, const AttendArgs& a,
-                          hipStream_t s) {
-  const dim3 block(64 * waves);
-  return pairs == 1 ? dispatch_pairs_mode<G, 1>(mode, grid, block, a, s)
-                    : dispatch_pairs_mode<G, 2>(mode, grid, block, a, s);
+hipError_t dispatch_pairs(const AttendPlan& p, int64_t rows, const AttendArgs& a, hipStream_t s) {
+  const dim3 block(64 * p.waves), grid = pairs_grid(p, rows);
+  if (p.vhalves == 2)
+    return p.pairs == 1 ? dispatch_pairs_mode<G, 1, 2>(p.mode, grid, block, a, s)
+                        : dispatch_pairs_mode<G, 2, 2>(p.mode, grid, block, a, s);
+  return p.pairs == 1 ? dispatch_pairs_mode<G, 1, 1>(p.mode, grid, block, a, s)
+                      : dispatch_pairs_mode<G, 2, 1>(p.mode, grid, block, a, s);
 }
 
 bool use_wave_kernel(const Cache& c) {
@@ -1278,6 +1340,12 @@ AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs) {
     p.waves = waves;
     p.pairs = pairs;
     chunk = (int64_t)waves * pairs * 32;
+    // Fewer whole rows than the chip has CUs: two workgroups per row, each
+    // reading all the row's keys and half of each value row (the keys' second
+    // reading is served by the XCD's L2), so twice as many CUs request the
+    // rows.  On 128 rows of 655 slots the gather alone takes 9.0 us against
+    // 9.7 us with one workgroup per row (cache-cold).
+    p.vhalves = (chunk >= p.n_slots && rows < 256) ? 2 : 1;
   } else if (use_wave_kernel(c)) {
     p.kernel = kKernWave;
     // Each wave takes rounds of up to 64 slots with every load of a round in
@@ -1377,6 +1445,7 @@ AttendArgs attend_args(const Cache& c, const AttendPlan& p, const void* q, const
   a.out = out;
   a.part = static_cast<float*>(ws);
   a.row_span = p.kernel == kKernPairs ? (uint32_t)row_span_bytes(c) : 0u;
+  a.rows = c.B * c.Hkv;
   return a;
 }
 
@@ -1391,9 +1460,9 @@ hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, con
   hipError_t e;
   if (p.kernel == kKernPairs) {
     switch (c.G) {
-      case 1: e = dispatch_pairs<1>(p.pairs, p.waves, p.mode, grid, a, s); break;
-      case 2: e = dispatch_pairs<2>(p.pairs, p.waves, p.mode, grid, a, s); break;
-      default: e = dispatch_pairs<4>(p.pairs, p.waves, p.mode, grid, a, s); break;
+      case 1: e = dispatch_pairs<1>(p, rows, a, s); break;
+      case 2: e = dispatch_pairs<2>(p, rows, a, s); break;
+      default: e = dispatch_pairs<4>(p, rows, a, s); break;
     }
   } else if (p.kernel == kKernWave) {
     switch (c.G) {
@@ -1432,26 +1501,31 @@ hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, con
 
 namespace {
 
-template <int G, int PAIRS>
-hipError_t launch_merge_attend_g(const AttendArgs& a, int64_t rows, const float* cand_val,
-                                 const int32_t* cand_pos, int64_t n_cand, int64_t cstride,
-                                 bool vec4, int32_t* idx, hipStream_t s) {
-  const dim3 grid(1, (unsigned)rows), block(64 * kMaxSparseWaves);
+template <int G, int PAIRS, int VH>
+hipError_t launch_merge_attend_g(const AttendArgs& a, const AttendPlan& p, int64_t rows,
+                                 const float* cand_val, const int32_t* cand_pos, int64_t n_cand,
+                                 int64_t cstride, bool vec4, int32_t* idx, hipStream_t s) {
+  const dim3 grid = pairs_grid(p, rows), block(64 * kMaxSparseWaves);
   if (n_cand <= 4 * 64 * kMaxSparseWaves)
-    hipLaunchKernelGGL((merge_attend_kernel<G, PAIRS, 1>), grid, block, 0, s, a, cand_val, cand_pos,
-                       (int)n_cand, cstride, vec4, idx);
+    hipLaunchKernelGGL((merge_attend_kernel<G, PAIRS, 1, VH>), grid, block, 0, s, a, cand_val,
+                       cand_pos, (int)n_cand, cstride, vec4, idx);
   else
-    hipLaunchKernelGGL((merge_attend_kernel<G, PAIRS, 2>), grid, block, 0, s, a, cand_val, cand_pos,
-                       (int)n_cand, cstride, vec4, idx);
+    hipLaunchKernelGGL((merge_attend_kernel<G, PAIRS, 2, VH>), grid, block, 0, s, a, cand_val,
+                       cand_pos, (int)n_cand, cstride, vec4, idx);
   return hipGetLastError();
 }
 
 template <int G>
-hipError_t launch_merge_attend_t(int pairs, const AttendArgs& a, int64_t rows,
+hipError_t launch_merge_attend_t(const AttendPlan& p, const AttendArgs& a, int64_t rows,
                                  const float* cand_val, const int32_t* cand_pos, int64_t n_cand,
                                  int64_t cstride, bool vec4, int32_t* idx, hipStream_t s) {
-  if (pairs == 1) return launch_merge_attend_g<G, 1>(a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
-  return launch_merge_attend_g<G, 2>(a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
+  if (p.vhalves == 2)
+    return p.pairs == 1
+               ? launch_merge_attend_g<G, 1, 2>(a, p, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s)
+               : launch_merge_attend_g<G, 2, 2>(a, p, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
+  return p.pairs == 1
+             ? launch_merge_attend_g<G, 1, 1>(a, p, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s)
+             : launch_merge_attend_g<G, 2, 1>(a, p, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
 }
 
 }  // namespace
@@ -1474,9 +1548,9 @@ hipError_t launch_merge_attend(const Cache& c, const AttendPlan& p, const void* 
   const bool vec4 = (reinterpret_cast<uintptr_t>(cand_val) % 16 == 0) && (cstride % 4 == 0) &&
                     (reinterpret_cast<uintptr_t>(cand_pos) % 16 == 0);
   switch (c.G) {
-    case 1: return launch_merge_attend_t<1>(p.pairs, a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
-    case 2: return launch_merge_attend_t<2>(p.pairs, a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
-    default: return launch_merge_attend_t<4>(p.pairs, a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
+    case 1: return launch_merge_attend_t<1>(p, a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
+    case 2: return launch_merge_attend_t<2>(p, a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
+    default: return launch_merge_attend_t<4>(p, a, rows, cand_val, cand_pos, n_cand, cstride, vec4, idx, s);
   }
 }
 

@@ -115,6 +115,7 @@ struct AttendPlan {
   int32_t waves;    // waves per workgroup
   int32_t rounds;   // slot rounds per wave (kKernWave)
   int32_t pairs;    // pairs of 16-slot tiles per wave (kKernPairs)
+  int32_t vhalves;  // kKernPairs: 2 = two workgroups per row, one per half of the value dims
   size_t ws_bytes;  // split partials (0 when nsplit == 1)
 };
 
