@@ -173,6 +173,22 @@ def summarize(db_path):
         med, p10, p90 = np.percentile(np.asarray(durs[name], dtype=np.float64), [50, 10, 90])
         lines.append("%-70s %6d %10.2f %10.2f %10.2f %10.2f %10.2f %10.2f" % (
             name[:70], n, avg / 1e3, mn / 1e3, mx / 1e3, med / 1e3, p10 / 1e3, p90 / 1e3))
+    # launches of the method's kernels split by the kernel that ran just
+    # before each (e.g. a gather-attend inside a step follows the selection,
+    # one of a back-to-back series follows another gather-attend)
+    seq = db.execute("select name, start, end from kernels order by start").fetchall()
+    by_prev = {}
+    for (pname, _, _), (name, st, en) in zip(seq, seq[1:]):
+        if "sa::" in name:
+            by_prev.setdefault((name, pname), []).append(en - st)
+    if by_prev:
+        lines.append("")
+        lines.append("%-58s %-40s %6s %10s %10s" % ("kernel", "after", "calls", "avg_us",
+                                                    "median_us"))
+        for (name, pname), d in sorted(by_prev.items(), key=lambda kv: (kv[0][0], -len(kv[1]))):
+            d = np.asarray(d, dtype=np.float64)
+            lines.append("%-58s %-40s %6d %10.2f %10.2f" % (name[:58], pname[:40], len(d),
+                                                            d.mean() / 1e3, np.median(d) / 1e3))
     try:
         pmc = db.execute("select kernel_name, counter_name, avg(value), count(*) "
                          "from counters_collection group by kernel_name, counter_name").fetchall()
@@ -233,6 +249,22 @@ def pmc_means(db_path, counter):
     return {name: (val, n) for name, val, n in rows}
 
 
+def pmc_copy_kib(db_path, counter):
+    """The counter's value for the 1 GiB calibration copies: the mean over the
+    copy dispatches within half of the largest one (the cache copies and the
+    calibration copies move 1 GiB each; smaller copies of outputs are left
+    out)."""
+    import sqlite3
+    db = sqlite3.connect(db_path)
+    vals = [v for (v,) in db.execute(
+        "select value from counters_collection where counter_name = ? and "
+        "kernel_name like '%copyBuffer%'", (counter,)).fetchall()]
+    if not vals:
+        raise SystemExit("no calibration copy in %s" % db_path)
+    big = [v for v in vals if v >= 0.5 * max(vals)]
+    return sum(big) / len(big), len(big)
+
+
 def db_dir_name(db_path):
     """The rocprofv3 -d folder and -o name that wrote `db_path`."""
     base = os.path.basename(db_path)
@@ -245,11 +277,10 @@ def traffic_report(fetch_db, write_db):
     `bench.py --profile` runs (1 GiB read and 1 GiB written each)."""
     fetch = pmc_means(fetch_db, "FETCH_SIZE")
     write = pmc_means(write_db, "WRITE_SIZE")
-    copy = [n for n in fetch if "copyBuffer" in n]
-    if not copy:
-        raise SystemExit("no calibration copy in %s" % fetch_db)
-    ff = COPY_BYTES / (fetch[copy[0]][0] * 1024.0)
-    wf = COPY_BYTES / (write[copy[0]][0] * 1024.0)
+    fk_copy, n_copy = pmc_copy_kib(fetch_db, "FETCH_SIZE")
+    wk_copy, _ = pmc_copy_kib(write_db, "WRITE_SIZE")
+    ff = COPY_BYTES / (fk_copy * 1024.0)
+    wf = COPY_BYTES / (wk_copy * 1024.0)
     c = None
     try:
         import sa_synth as S
@@ -265,8 +296,10 @@ def traffic_report(fetch_db, write_db):
              "#   rocprofv3 --pmc WRITE_SIZE -d %s -o %s -- python -u bench.py --profile"
              % db_dir_name(write_db),
              "#   python bench.py --traffic %s %s" % (fetch_db, write_db),
-             "# bench.py --profile runs three 1 GiB device-to-device copies that read and write",
-             "# exactly 1073741824 bytes each; factor = 1073741824 / (counter KiB of a copy * 1024)",
+             "# bench.py --profile runs three 1 GiB device-to-device copies (and 14 more make the",
+             "# cache copies) that read and write exactly 1073741824 bytes each; factor =",
+             "# 1073741824 / (mean counter KiB of those copies * 1024); smaller copies of outputs",
+             "# are left out of the mean",
              "#",
              "%-70s %6s %14s %14s %14s" % ("kernel", "n", "FETCH_KiB", "WRITE_KiB", "bytes(calib.)")]
     for name in sorted(fetch, key=lambda n: -fetch[n][0]):
