@@ -229,6 +229,23 @@ sa_status sa_sparse_decode(const sa_kv_desc* desc, const void* q, const void* k_
 size_t sa_sparse_workspace_size(const sa_kv_desc* desc, sa_index_kind ik, int32_t n_idx,
                                 int32_t block_size);
 
+/* sa_sparse_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments, kernels and results, without (ws,
+ * ws_bytes).  The split partials that sa_sparse_decode keeps in the caller's
+ * workspace go to a static device array of the library instead, 16 MiB
+ * (16777216 bytes), which every GPU the library runs on holds until the
+ * process ends; a call whose plan needs more (sa_sparse_workspace_size above
+ * 16 MiB) returns SA_ERR_WORKSPACE with nothing enqueued.  The call allocates
+ * nothing; the first call on a device looks the array's address up on that
+ * device (the device of `stream`).  Every call on one GPU shares that GPU's
+ * array: calls that may overlap on one GPU (different streams, or different
+ * threads) race on it and must be serialised by the caller. */
+sa_status sa_sparse_decode_noalloc(const sa_kv_desc* desc, const void* q, const void* k_cache,
+                                   const void* v_cache, sa_index_kind ik, const int32_t* idx,
+                                   int32_t n_idx, int32_t block_size, float* out,
+                                   hipStream_t stream);
+
 /* Full decode attention over all ctx_len tokens (layers routed to full
  * attention, [P1]; the dense baseline of [P3] section 3.C).  Same output as
  * sa_sparse_decode with S = [0, ctx_len). */

@@ -450,3 +450,26 @@ def test_bench_summarize_percentiles(tmp_path):
     assert float(med) == 5.5 and abs(float(p10) - 1.9) < 1e-9 and abs(float(p90) - 9.1) < 1e-9
     assert lines["k_b"][0] == "1" and float(lines["k_b"][4]) == 0.5
     assert counters == {}
+
+
+def test_noalloc_rejects_plans_beyond_its_scratch():
+    """sa_sparse_decode_noalloc: the same argument checks as sa_sparse_decode,
+    and a plan whose split partials exceed the 16 MiB static scratch is
+    refused on the host with SA_ERR_WORKSPACE (every pointer is fake)."""
+    L = T.lib()
+    d = _desc()
+
+    def na(desc, q=FAKE, n_idx=10, ik=0):
+        return L.sa_sparse_decode_noalloc(ctypes.byref(desc) if desc is not None else None, q,
+                                          FAKE, FAKE, ik, FAKE, n_idx, 0, FAKE, None)
+
+    assert na(None) == Bn.SA_ERR_NULL
+    assert na(d, q=None) == Bn.SA_ERR_NULL
+    assert na(d, q=MIS) == Bn.SA_ERR_ALIGN
+    assert na(d, n_idx=0) == Bn.SA_ERR_SHAPE
+    big = _desc(batch=128, n_q_heads=32, n_kv_heads=8, ctx_len=65536,
+                kv_stride_b=8 * 65536 * 128, kv_stride_h=65536 * 128)
+    need = L.sa_sparse_workspace_size(ctypes.byref(big), 0, 16384, 0)
+    assert need > 16 << 20
+    assert na(big, n_idx=16384) == Bn.SA_ERR_WORKSPACE
+    assert "16777216" in L.sa_last_error().decode()

@@ -32,7 +32,7 @@ SA_LAYER_DENSE, SA_LAYER_SPARSE, SA_LAYER_REUSE, SA_LAYER_DENSE_SELECT = 0, 1, 2
 
 EXPORTED = [
     "sa_score", "sa_block_summarize", "sa_topk", "sa_topk_workspace_size", "sa_select",
-    "sa_select_workspace_size", "sa_sparse_decode",
+    "sa_select_workspace_size", "sa_sparse_decode", "sa_sparse_decode_noalloc",
     "sa_sparse_workspace_size", "sa_dense_decode", "sa_dense_workspace_size",
     "sa_dense_decode_scored", "sa_dense_scored_workspace_size", "sa_decode_layer",
     "sa_layer_workspace_size", "sa_plan_validate", "sa_index_overlap", "sa_plan_reuse",
@@ -89,6 +89,7 @@ def lib() -> ctypes.CDLL:
     L.sa_select_workspace_size.restype = sz
     L.sa_stream_read.argtypes = [vp, sz, vp, vp]
     L.sa_sparse_decode.argtypes = [P(KVDesc), vp, vp, vp, st, vp, i32, i32, vp, vp, sz, vp]
+    L.sa_sparse_decode_noalloc.argtypes = [P(KVDesc), vp, vp, vp, st, vp, i32, i32, vp, vp]
     L.sa_sparse_workspace_size.argtypes = [P(KVDesc), st, i32, i32]
     L.sa_sparse_workspace_size.restype = sz
     L.sa_dense_decode.argtypes = [P(KVDesc), vp, vp, vp, vp, vp, sz, vp]
@@ -112,6 +113,7 @@ def lib() -> ctypes.CDLL:
     L.sa_last_error.restype = ctypes.c_char_p
     L.sa_version.restype = ctypes.c_char_p
     for name in ["sa_score", "sa_block_summarize", "sa_topk", "sa_select", "sa_sparse_decode",
+                 "sa_sparse_decode_noalloc",
                  "sa_dense_decode",
                  "sa_dense_decode_scored", "sa_decode_layer", "sa_plan_validate",
                  "sa_index_overlap", "sa_plan_reuse", "sa_plan_fixed_jump", "sa_gather_blocks",
@@ -349,6 +351,24 @@ def sa_sparse_decode(q, k_cache, v_cache, idx, index_kind=SA_IDX_TOKEN_PER_KV_HE
     check(L.sa_sparse_decode(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), index_kind,
                              _ptr(idx), n_idx, block_size, _ptr(out), _ptr(ws), nbytes,
                              ctypes.c_void_p(_stream(dev))))
+    return out
+
+
+def sa_sparse_decode_noalloc(q, k_cache, v_cache, idx, index_kind=SA_IDX_TOKEN_PER_KV_HEAD,
+                             block_size=0, out=None, softmax_scale=0.0):
+    """sa_sparse_decode_noalloc (no workspace: the library's static scratch).
+    `out` must be given for a call that may not allocate; returns out."""
+    dev = _dev(q, k_cache, v_cache, idx)
+    if v_cache.shape != k_cache.shape or v_cache.stride() != k_cache.stride():
+        raise ValueError("K and V caches must share shape and strides")
+    if idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be a contiguous int32 tensor")
+    desc = make_desc(q, k_cache, softmax_scale)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    check(lib().sa_sparse_decode_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                         index_kind, _ptr(idx), idx.shape[-1], block_size,
+                                         _ptr(out), ctypes.c_void_p(_stream(dev))))
     return out
 
 

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "common.hpp"
@@ -339,6 +340,55 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
 
 using namespace sa;
 
+// ---------------------------------------------------------------------------
+// The allocation-free entry point's scratch: a file-scope device array that
+// every GPU the library runs on holds until the process ends.  Host code uses
+// it only through the address hipGetSymbolAddress returns on each device
+// (the array's name in host code is a host-side stand-in, not a device
+// address).
+static __device__ __align__(256) uint8_t scratch[sa::kNoAllocScratchBytes];
+
+namespace sa {
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+// The scratch's device address on the device `stream` belongs to, looked up
+// once per device with that device current.
+sa_status noalloc_scratch(hipStream_t stream, void** out) {
+  int cur = 0, dev = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return fail(SA_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(SA_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                kMaxScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(SA_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess && e2 != hipSuccess) e = e2;
+    }
+    if (e != hipSuccess || !p)
+      return fail(SA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  e != hipSuccess ? hipGetErrorString(e) : "null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SA_OK;
+}
+}  // namespace sa
+
 extern "C" {
 
 const char* sa_version(void) { return "sa 0.1.0 (gfx950)"; }
@@ -465,6 +515,31 @@ sa_status sa_sparse_decode(const sa_kv_desc* desc, const void* q, const void* k_
   return hip_status(
       launch_attend(v, p, q, k_cache, v_cache, idx, n_idx, block_size, out, ws, stream),
       "sa_sparse_decode launch");
+}
+
+sa_status sa_sparse_decode_noalloc(const sa_kv_desc* desc, const void* q, const void* k_cache,
+                                   const void* v_cache, sa_index_kind ik, const int32_t* idx,
+                                   int32_t n_idx, int32_t block_size, float* out,
+                                   hipStream_t stream) {
+  Cache c;
+  sa_status st;
+  if ((st = check_desc(desc, &c)) != SA_OK) return st;
+  if ((st = check_attend_args(c, q, k_cache, v_cache, out)) != SA_OK) return st;
+  if ((st = check_sparse_idx(c, ik, idx, n_idx, block_size)) != SA_OK) return st;
+  const Cache v = attend_view(c, ik);
+  const AttendPlan p = plan_attend(v, mode_of(ik), n_idx, block_size);
+  void* ws = nullptr;
+  if (p.ws_bytes > 0) {
+    if (p.ws_bytes > sa::kNoAllocScratchBytes)
+      return fail(SA_ERR_WORKSPACE,
+                  "sa_sparse_decode_noalloc: this call needs %zu bytes of scratch, the static "
+                  "scratch holds %zu",
+                  p.ws_bytes, sa::kNoAllocScratchBytes);
+    if ((st = sa::noalloc_scratch(stream, &ws)) != SA_OK) return st;
+  }
+  return hip_status(
+      launch_attend(v, p, q, k_cache, v_cache, idx, n_idx, block_size, out, ws, stream),
+      "sa_sparse_decode_noalloc launch");
 }
 
 size_t sa_dense_workspace_size(const sa_kv_desc* desc) {

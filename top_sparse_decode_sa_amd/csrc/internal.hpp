@@ -161,4 +161,10 @@ hipError_t launch_stream_read(const void* data, size_t bytes, uint32_t* sink, hi
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// ------------------------------------------------ allocation-free calls
+// Bytes of the static device scratch of sa_sparse_decode_noalloc (16 MiB).
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+// Its device address on the device of `stream` (looked up once per device).
+sa_status noalloc_scratch(hipStream_t stream, void** out);
+
 }  // namespace sa
