@@ -54,6 +54,16 @@
 
 #include <hip/hip_runtime_api.h>
 
+/* The enumerations are 32-bit integers on both sides of the ABI.  C++ gets
+ * the fixed underlying type written out, so that a value outside the listed
+ * ones (which a C caller may pass, and which the calls reject) is still a
+ * valid value of the type. */
+#ifdef __cplusplus
+#define SA_ENUM enum : int32_t
+#else
+#define SA_ENUM enum
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -62,7 +72,7 @@ extern "C" {
  * here are its only exports. */
 #pragma GCC visibility push(default)
 
-typedef enum {
+typedef SA_ENUM {
   SA_OK = 0,
   SA_ERR_NULL = 1,        /* a required pointer is null */
   SA_ERR_SHAPE = 2,       /* a size, count, stride or k is out of range */
@@ -74,7 +84,7 @@ typedef enum {
   SA_ERR_MEMORY = 8       /* a buffer is not the kind of memory the call needs */
 } sa_status;
 
-typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+typedef SA_ENUM { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
 
 /* One layer's KV cache and query shape.
  *   K and V: element (b, h, t, i) at base + b*kv_stride_b + h*kv_stride_h
@@ -100,7 +110,7 @@ typedef struct {
 
 /* ---------------------------------------------------------------- scoring */
 
-typedef enum {
+typedef SA_ENUM {
   /* Exact score of every token of every row: [P3] section 2 (oracle top-k).
    *   scores[b, r, t] = scale * sum_{g < G} q[b, r*G + g, :] . K[b, r, t, :]
    * Output [batch, n_kv_heads, ctx_len] fp32. */
@@ -198,7 +208,7 @@ size_t sa_select_workspace_size(const sa_kv_desc* desc, sa_score_kind kind, int3
 
 /* ------------------------------------------------------------ attention */
 
-typedef enum {
+typedef SA_ENUM {
   /* idx [batch, n_kv_heads, n_idx] token positions, one set per row. */
   SA_IDX_TOKEN_PER_KV_HEAD = 0,
   /* idx [batch, n_idx] token positions shared by every KV head of a sequence. */
@@ -219,15 +229,33 @@ typedef enum {
  * for SA_IDX_TOKEN_PER_Q_HEAD):
  *   out[b, h, :] = sum_{t in S} softmax_S(scale * q[b,h,:] . K[b,h/G,t,:]) * V[b,h/G,t,:]
  * out: [batch, n_q_heads, head_dim] fp32.  Preconditions: every index in
- * range and the indices of one row distinct (not checked); 1 <= n_idx.
- * Computed as a split-K online softmax whose partial results are merged with
- * a log-sum-exp combine inside the same launch ([P5] tiling + online softmax). */
+ * range and the indices of one row distinct (not checked here; see
+ * sa_check_indices); 1 <= n_idx.  For bf16 caches with head_dim 128 and
+ * token indices, an index outside the row reads zeros or another token of the
+ * row, never memory outside the row's cache.
+ * Computed as a split-K online softmax ([P5] tiling + online softmax): each
+ * workgroup attends a run of a row's slots; when a row is split over several
+ * workgroups their partial results (o, max, sum) are merged by a log-sum-exp
+ * combine in a second launch (the workspace holds them in between). */
 sa_status sa_sparse_decode(const sa_kv_desc* desc, const void* q, const void* k_cache,
                            const void* v_cache, sa_index_kind ik, const int32_t* idx, int32_t n_idx,
                            int32_t block_size, float* out, void* ws, size_t ws_bytes,
                            hipStream_t stream);
 size_t sa_sparse_workspace_size(const sa_kv_desc* desc, sa_index_kind ik, int32_t n_idx,
                                 int32_t block_size);
+
+/* Check an index list before sa_sparse_decode (or before a REUSE layer reads
+ * it): [P3] section 3.C attends over a set of tokens, so each row's indices
+ * must name distinct tokens (blocks) inside the cache.  One launch writes
+ *   counts[0] = number of rows holding an index outside [0, ctx_len)
+ *               (block kind: outside [0, ceil(ctx_len / block_size)))
+ *   counts[1] = number of rows in which some index appears more than once
+ * (counts: int32[2], device, overwritten).  Rows and layout as for
+ * sa_sparse_decode with the same index kind.  Indices are only read as data.
+ * Limits: 1 <= n_idx <= 8192 (larger: SA_ERR_UNSUPPORTED). */
+sa_status sa_check_indices(const sa_kv_desc* desc, sa_index_kind ik, const int32_t* idx,
+                           int32_t n_idx, int32_t block_size, int32_t* counts,
+                           hipStream_t stream);
 
 /* sa_sparse_decode for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
@@ -270,7 +298,7 @@ size_t sa_dense_scored_workspace_size(const sa_kv_desc* desc);
 
 /* ----------------------------------------------------- per-layer mode flag */
 
-typedef enum {
+typedef SA_ENUM {
   SA_LAYER_DENSE = 0,  /* full attention; idx untouched */
   SA_LAYER_SPARSE = 1, /* score -> top-k -> selected-set attention; WRITES idx.
                         * With exact or per-KV-head indexer scores the

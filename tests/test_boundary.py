@@ -473,3 +473,118 @@ def test_noalloc_rejects_plans_beyond_its_scratch():
     assert need > 16 << 20
     assert na(big, n_idx=16384) == Bn.SA_ERR_WORKSPACE
     assert "16777216" in L.sa_last_error().decode()
+
+
+def test_check_indices_errors():
+    """sa_check_indices: index-kind, pointer and size checks on the host."""
+    L = T.lib()
+    d = _desc()
+
+    def ci(desc, idx=FAKE, n_idx=10, ik=0, bs=0, counts=FAKE):
+        return L.sa_check_indices(ctypes.byref(desc) if desc is not None else None, ik, idx,
+                                  n_idx, bs, counts, None)
+
+    assert ci(None) == Bn.SA_ERR_NULL
+    assert ci(d, idx=None) == Bn.SA_ERR_NULL
+    assert ci(d, counts=None) == Bn.SA_ERR_NULL
+    assert ci(d, n_idx=0) == Bn.SA_ERR_SHAPE
+    assert ci(d, ik=9) == Bn.SA_ERR_SHAPE
+    assert ci(d, ik=Bn.SA_IDX_BLOCK_PER_KV_HEAD, bs=0) == Bn.SA_ERR_SHAPE
+    assert ci(d, n_idx=8193) == Bn.SA_ERR_UNSUPPORTED
+    assert "8192" in L.sa_last_error().decode()
+
+
+_PLAN_PROBE = r"""
+import ctypes, json, sys
+sys.path.insert(0, %r)
+import top_sparse_decode_sa_amd as T
+from top_sparse_decode_sa_amd import _binding as Bn
+L = T.lib()
+out = []
+for B, Hkv, N, k in [(1, 8, 32768, 655), (16, 8, 32768, 655), (128, 8, 131072, 262),
+                     (1, 1, 1048576, 2048), (4, 2, 5000, 61)]:
+    d = Bn.KVDesc(batch=B, n_q_heads=4 * Hkv, n_kv_heads=Hkv, head_dim=128, ctx_len=N,
+                  q_dtype=Bn.SA_BF16, kv_dtype=Bn.SA_BF16, kv_stride_b=Hkv * N * 128,
+                  kv_stride_h=N * 128, kv_stride_t=128)
+    out.append([L.sa_sparse_workspace_size(ctypes.byref(d), 0, k, 0),
+                L.sa_dense_workspace_size(ctypes.byref(d))])
+print(json.dumps(out))
+"""
+
+
+def test_launch_plans_ignore_the_environment():
+    """The library is stateless: no environment variable steers its launch
+    plans (the workspace sizes follow from the plan's split counts), and its
+    sources read none."""
+    import subprocess
+    import sys
+    src = os.path.join(ROOT, "top_sparse_decode_sa_amd", "csrc")
+    for f in os.listdir(src):
+        assert "getenv" not in open(os.path.join(src, f)).read(), f
+    probe = _PLAN_PROBE % ROOT
+
+    def run(env):
+        e = dict(os.environ)
+        e.update(env)
+        return subprocess.run([sys.executable, "-c", probe], env=e, check=True,
+                              capture_output=True, text=True).stdout
+    knobs = {"SA_SPARSE_CHUNK": "64", "SA_SPARSE_WAVES": "1", "SA_DENSE_WAVES": "2",
+             "SA_DENSE_ROUNDS": "7"}
+    assert run({}) == run(knobs)
+
+
+def test_bench_oracle_baseline_on_small_workloads(tmp_path):
+    """The per-workload cpu_baseline leg of bench.py (oracle worker processes
+    behind a barrier, makespans scaled to a step) on shrunken copies of the
+    three workloads: every figure is positive and finite, and the units
+    reported are the ones dealt out."""
+    import dataclasses
+    import math
+
+    import numpy as np
+
+    import bench
+    import sa_synth as S
+    C = S.CONFIGS
+    small = {
+        "batch128k": dataclasses.replace(C["batch128k"], batch=4, ctx_len=2048, k=8, n_planted=8),
+        "block61k": dataclasses.replace(C["block61k"], batch=2, ctx_len=1024, k=3),
+        "indexer1m": dataclasses.replace(C["indexer1m"], ctx_len=4096, k=64),
+    }
+    for name, c in small.items():
+        shm = None
+        if name == "indexer1m":
+            w = S.Workload(c, 0)
+            shm = str(tmp_path)
+            for l in range(c.n_layers):
+                if c.modes[l] == "sparse":
+                    k, q = w.k(l), w.q(l)
+                    np.savez(os.path.join(shm, "layer%d.npz" % l), qi=w.indexer_q(l, q),
+                             ki=w.indexer_k(l, k), wi=w.indexer_w(l), q=q)
+        cpu = bench.config_cpu_baseline(name, 0, 10 ** 6, shm=shm, cfg=c, workers=2)
+        assert cpu["cores"] == 2 and cpu["kind"] == "oracle"
+        for v in (cpu["value"], cpu["steps_per_s"], cpu["one_thread"]["steps_per_s"],
+                  cpu["one_thread"]["attend_gbps"]):
+            assert v > 0 and math.isfinite(v), (name, cpu)
+        want = {"batch128k": 2 * max(1, 64 // 2), "block61k": c.batch * c.n_kv_heads,
+                "indexer1m": 6 + 2 * c.n_kv_heads}[name]
+        assert "%d units" % want in cpu["sample"], (name, cpu["sample"])
+
+
+@pytest.mark.parametrize("lang,compiler", [("c", "gcc"), ("c++", "g++")])
+def test_header_compiles_as_c_and_cxx(tmp_path, lang, compiler):
+    """include/sa.h is a C header usable from C and C++, and its enumerations
+    have the size of int32_t in both."""
+    import shutil
+    import subprocess
+    if shutil.which(compiler) is None:
+        pytest.skip(compiler + " missing")
+    src = tmp_path / "t.c"
+    src.write_text('#include "sa.h"\n'
+                   'typedef char enum_is_32_bit[sizeof(sa_dtype) == 4 && sizeof(sa_status) == 4 '
+                   '? 1 : -1];\n'
+                   'int main(void) { sa_kv_desc d; d.q_dtype = SA_BF16; return (int)d.q_dtype; }\n')
+    r = subprocess.run([compiler, "-fsyntax-only", "-Wall", "-D__HIP_PLATFORM_AMD__",
+                        "-I/opt/rocm/include", "-I" + os.path.join(ROOT, "include"), "-x", lang,
+                        str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr

@@ -235,6 +235,51 @@ def test_sparse_shared_and_unsorted_indices():
     check_out(out, want, "bf16", "sparse shared")
 
 
+def _bad_rows(idx, limit):
+    """Rows with an index outside [0, limit), rows with a repeated index."""
+    rows = idx.reshape(-1, idx.shape[-1])
+    return [int(sum(((r < 0) | (r >= limit)).any() for r in rows)),
+            int(sum(len(set(r.tolist())) < len(r) for r in rows))]
+
+
+@pytest.mark.parametrize("kind,n_idx", [(T.SA_IDX_TOKEN_PER_KV_HEAD, 1), (T.SA_IDX_TOKEN_PER_KV_HEAD, 700),
+                                        (T.SA_IDX_TOKEN_PER_KV_HEAD, 8192), (T.SA_IDX_TOKEN_SHARED, 33),
+                                        (T.SA_IDX_TOKEN_PER_Q_HEAD, 2048), (T.SA_IDX_BLOCK_PER_KV_HEAD, 24)])
+def test_check_indices_counts_bad_rows(kind, n_idx):
+    """sa_check_indices counts rows with an out-of-range index and rows with a
+    repeat, on clean index sets and with mistakes planted at the row ends,
+    in the middle, at -1, at the limit and as INT32 extremes."""
+    say("check indices", kind, n_idx)
+    B, Hkv, G, N, d, bs = 2, 4, 2, 9000, 64, 128
+    q, k, _ = _rand_cache(B, Hkv * G, Hkv, N, d, "f32", 41)
+    qd, kd = q.to(dev()), k.to(dev())
+    limit = -(-N // bs) if kind == T.SA_IDX_BLOCK_PER_KV_HEAD else N
+    rows = {T.SA_IDX_TOKEN_SHARED: B, T.SA_IDX_TOKEN_PER_Q_HEAD: B * Hkv * G}.get(kind, B * Hkv)
+    rng = np.random.default_rng(n_idx)
+    idx = np.stack([rng.choice(limit, n_idx, replace=False) for _ in range(rows)]).astype(np.int32)
+    bsz = bs if kind == T.SA_IDX_BLOCK_PER_KV_HEAD else 0
+
+    def run(x):
+        got = T.sa_check_indices(qd, kd, torch.from_numpy(x).to(dev()), kind, bsz).cpu().tolist()
+        assert got == _bad_rows(x, limit), (got, _bad_rows(x, limit))
+        return got
+
+    assert run(idx) == [0, 0]
+    bad = idx.copy()
+    bad[0, -1] = limit
+    bad[rows - 1, 0] = -1
+    if rows > 2:
+        bad[1, n_idx // 2] = np.iinfo(np.int32).min
+    if n_idx > 2:
+        bad[rows - 1, -1] = bad[rows - 1, n_idx // 2]       # repeat in a row already out of range
+    if n_idx > 3:
+        bad[rows // 2, 1] = bad[rows // 2, 2]
+    if rows > 3 and n_idx > 1:
+        bad[2, 0] = bad[2, 1] = np.iinfo(np.int32).max       # out of range and repeated
+    got = run(bad)
+    assert got[0] >= 1 and (n_idx < 3 or got[1] >= 1)
+
+
 @pytest.mark.parametrize("N,bs,n_blk", [(1000, 128, 3), (61440, 128, 24), (300, 16, 19)])
 def test_sparse_blocks_with_partial_last_block(N, bs, n_blk):
     say("sparse blocks", N, bs, n_blk)

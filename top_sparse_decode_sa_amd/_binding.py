@@ -14,7 +14,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsa.so")
+# SA_LIBRARY names another build of the same library to load instead (the
+# host-sanitized one: build.build_sanitized()).
+LIB_PATH = os.environ.get("SA_LIBRARY") or os.path.join(_HERE, "libsa.so")
 
 # sa_status
 SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_ALIGN, SA_ERR_DTYPE, SA_ERR_WORKSPACE, \
@@ -33,6 +35,7 @@ SA_LAYER_DENSE, SA_LAYER_SPARSE, SA_LAYER_REUSE, SA_LAYER_DENSE_SELECT = 0, 1, 2
 EXPORTED = [
     "sa_score", "sa_block_summarize", "sa_topk", "sa_topk_workspace_size", "sa_select",
     "sa_select_workspace_size", "sa_sparse_decode", "sa_sparse_decode_noalloc",
+    "sa_check_indices",
     "sa_sparse_workspace_size", "sa_dense_decode", "sa_dense_workspace_size",
     "sa_dense_decode_scored", "sa_dense_scored_workspace_size", "sa_decode_layer",
     "sa_layer_workspace_size", "sa_plan_validate", "sa_index_overlap", "sa_plan_reuse",
@@ -90,6 +93,7 @@ def lib() -> ctypes.CDLL:
     L.sa_stream_read.argtypes = [vp, sz, vp, vp]
     L.sa_sparse_decode.argtypes = [P(KVDesc), vp, vp, vp, st, vp, i32, i32, vp, vp, sz, vp]
     L.sa_sparse_decode_noalloc.argtypes = [P(KVDesc), vp, vp, vp, st, vp, i32, i32, vp, vp]
+    L.sa_check_indices.argtypes = [P(KVDesc), st, vp, i32, i32, vp, vp]
     L.sa_sparse_workspace_size.argtypes = [P(KVDesc), st, i32, i32]
     L.sa_sparse_workspace_size.restype = sz
     L.sa_dense_decode.argtypes = [P(KVDesc), vp, vp, vp, vp, vp, sz, vp]
@@ -113,7 +117,7 @@ def lib() -> ctypes.CDLL:
     L.sa_last_error.restype = ctypes.c_char_p
     L.sa_version.restype = ctypes.c_char_p
     for name in ["sa_score", "sa_block_summarize", "sa_topk", "sa_select", "sa_sparse_decode",
-                 "sa_sparse_decode_noalloc",
+                 "sa_sparse_decode_noalloc", "sa_check_indices",
                  "sa_dense_decode",
                  "sa_dense_decode_scored", "sa_decode_layer", "sa_plan_validate",
                  "sa_index_overlap", "sa_plan_reuse", "sa_plan_fixed_jump", "sa_gather_blocks",
@@ -370,6 +374,21 @@ def sa_sparse_decode_noalloc(q, k_cache, v_cache, idx, index_kind=SA_IDX_TOKEN_P
                                          index_kind, _ptr(idx), idx.shape[-1], block_size,
                                          _ptr(out), ctypes.c_void_p(_stream(dev))))
     return out
+
+
+def sa_check_indices(q, k_cache, idx, index_kind=SA_IDX_TOKEN_PER_KV_HEAD, block_size=0,
+                     counts=None):
+    """sa_check_indices: returns counts (int32[2] on the device): rows with an
+    out-of-range index, rows with a repeated index."""
+    dev = _dev(q, k_cache, idx)
+    if idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be a contiguous int32 tensor")
+    desc = make_desc(q, k_cache)
+    if counts is None:
+        counts = torch.empty(2, dtype=torch.int32, device=dev)
+    check(lib().sa_check_indices(ctypes.byref(desc), index_kind, _ptr(idx), idx.shape[-1],
+                                 block_size, _ptr(counts), ctypes.c_void_p(_stream(dev))))
+    return counts
 
 
 def sa_dense_decode(q, k_cache, v_cache, out=None, softmax_scale=0.0, ws=None):

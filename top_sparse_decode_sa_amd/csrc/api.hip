@@ -542,6 +542,25 @@ sa_status sa_sparse_decode_noalloc(const sa_kv_desc* desc, const void* q, const 
       "sa_sparse_decode_noalloc launch");
 }
 
+sa_status sa_check_indices(const sa_kv_desc* desc, sa_index_kind ik, const int32_t* idx,
+                           int32_t n_idx, int32_t block_size, int32_t* counts,
+                           hipStream_t stream) {
+  Cache c;
+  sa_status st;
+  if ((st = check_desc(desc, &c)) != SA_OK) return st;
+  if ((st = check_sparse_idx(c, ik, idx, n_idx, block_size)) != SA_OK) return st;
+  if ((st = check_ptr(counts, "counts", 4)) != SA_OK) return st;
+  if (n_idx > kCheckMaxIdx)
+    return fail(SA_ERR_UNSUPPORTED, "n_idx %d above %d", n_idx, kCheckMaxIdx);
+  int64_t rows = (int64_t)c.B * c.Hkv;
+  if (ik == SA_IDX_TOKEN_SHARED) rows = c.B;
+  if (ik == SA_IDX_TOKEN_PER_Q_HEAD) rows = (int64_t)c.B * c.Hq;
+  const int64_t limit =
+      ik == SA_IDX_BLOCK_PER_KV_HEAD ? (c.N + block_size - 1) / block_size : c.N;
+  return hip_status(launch_check_indices(idx, rows, n_idx, limit, counts, stream),
+                    "sa_check_indices launch");
+}
+
 size_t sa_dense_workspace_size(const sa_kv_desc* desc) {
   Cache c;
   if (check_desc(desc, &c) != SA_OK) return 0;

@@ -96,17 +96,20 @@ __device__ __forceinline__ uint2 ld8_buf(__amdgpu_buffer_rsrc_t r, uint32_t off)
 template <int MODE>
 __device__ __forceinline__ int64_t resolve_slot(const AttendArgs& a, int row, int b, int64_t j,
                                                 bool& ok) {
+  // Out-of-range indices as in slot_token below: token N - 1, or masked.
+  const uint32_t last = (uint32_t)(a.N - 1);
   if constexpr (MODE == kIdxDense) {
     return j;
   } else if constexpr (MODE == kIdxTokenPerHead) {
-    return a.idx[(int64_t)row * a.n_idx + j];
+    return min((uint32_t)a.idx[(int64_t)row * a.n_idx + j], last);
   } else if constexpr (MODE == kIdxTokenShared) {
-    return a.idx[(int64_t)b * a.n_idx + j];
+    return min((uint32_t)a.idx[(int64_t)b * a.n_idx + j], last);
   } else {
     const int64_t blk = a.idx[(int64_t)row * a.n_idx + j / a.bs];
     const int64_t t = blk * a.bs + j % a.bs;
-    ok = ok && (t < a.N);
-    return t;
+    const bool in = t >= 0 && t < a.N;
+    ok = ok && in;
+    return in ? t : a.N - 1;
   }
 }
 
@@ -286,18 +289,23 @@ __device__ __forceinline__ int32_t slot_token(const AttendArgs& a, int row, int 
                                               int64_t s1, bool& ok, const int32_t* lidx = nullptr) {
   ok = j < s1;
   const int64_t jj = ok ? j : s1 - 1;
+  // A token index outside [0, N) (a broken precondition) is read as token
+  // N - 1, so no load leaves the row's cache; block tokens past the end are
+  // masked out.
+  const uint32_t last = (uint32_t)(a.N - 1);
   if constexpr (LIDX) {
-    return lidx[jj];  // the row's index list, already in LDS
+    return (int32_t)min((uint32_t)lidx[jj], last);  // the row's index list, already in LDS
   } else if constexpr (MODE == kIdxDense || MODE == kIdxDenseScored) {
     return (int32_t)jj;
   } else if constexpr (MODE == kIdxTokenPerHead) {
-    return a.idx[(int64_t)row * a.n_idx + jj];
+    return (int32_t)min((uint32_t)a.idx[(int64_t)row * a.n_idx + jj], last);
   } else if constexpr (MODE == kIdxTokenShared) {
-    return a.idx[(int64_t)b * a.n_idx + jj];
+    return (int32_t)min((uint32_t)a.idx[(int64_t)b * a.n_idx + jj], last);
   } else {
     const int64_t t = (int64_t)a.idx[(int64_t)row * a.n_idx + jj / a.bs] * a.bs + jj % a.bs;
-    ok = ok && t < a.N;
-    return (int32_t)(t < a.N ? t : a.N - 1);
+    const bool in = t >= 0 && t < a.N;
+    ok = ok && in;
+    return (int32_t)(in ? t : a.N - 1);
   }
 }
 

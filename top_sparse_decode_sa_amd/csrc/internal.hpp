@@ -148,6 +148,13 @@ hipError_t launch_merge_attend(const Cache& c, const AttendPlan& p, const void* 
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
+// ------------------------------------------------------- index checks
+// counts[0] = rows of `rows` x n indices with one outside [0, limit);
+// counts[1] = rows with a repeated index.  n <= kCheckMaxIdx.
+constexpr int32_t kCheckMaxIdx = 8192;
+hipError_t launch_check_indices(const int32_t* idx, int64_t rows, int32_t n, int64_t limit,
+                                int32_t* counts, hipStream_t s);
+
 // ------------------------------------------------------------- offload
 // k_dev / v_dev: device addresses of a cache in pinned host memory; c.N is a
 // multiple of bs.  Out: [B, Hkv, n_blk * bs, D] contiguous.
