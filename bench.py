@@ -69,7 +69,11 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="llama32k")
+    p.add_argument("--workload", default="llama32k",
+                   choices=["llama32k", "block61k", "batch128k", "indexer1m"],
+                   help="llama32k: the default line; the others time that workload on its seeded "
+                        "inputs and print one JSON line of their own (attend GB/s, step rate, "
+                        "kernels, dense comparison, an all-core oracle cpu_baseline)")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bound on the oracle's CPU time for cpu_baseline (0 disables)")
@@ -108,16 +112,8 @@ def parse():
                         "128K tokens with k = 655; the gather-attend moves the same bytes at every "
                         "N while selection and dense decode grow with N; prints a table and one "
                         "JSON line")
-    p.add_argument("--indexer1m", action="store_true",
-                   help="one 1M-token sequence over 8 layers (32/8 heads, d 128, bf16): layers 0-1 "
-                        "dense, layers 2-7 select 2048 tokens shared by the KV heads with a 4-head "
-                        "64-dim indexer; times the mixed 8-layer step against all-dense and each "
-                        "sparse layer's launches; prints a table and one JSON line")
-    p.add_argument("--block61k", action="store_true",
-                   help="block selection on the block61k workload (batch 8, 32/8 heads, d 128, bf16, "
-                        "61440 tokens, 24 of 480 blocks of 128 kept): block summaries, block scores, "
-                        "block top-k and the block gather-attend timed call by call, and the 4-layer "
-                        "plan (SPARSE, then 3 REUSE layers) against all-dense; one JSON line")
+    p.add_argument("--indexer1m", action="store_true", help="same as --workload indexer1m")
+    p.add_argument("--block61k", action="store_true", help="same as --workload block61k")
     p.add_argument("--theta", type=float, default=0.35,
                    help="overlap threshold of the layer-reuse planner (--hylra)")
     p.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -657,206 +653,692 @@ def nscale(args):
                       "provenance": provenance()}), flush=True)
 
 
-def indexer1m(args):
-    """The indexer1m workload: batch 1, 32/8 heads, d 128, bf16, 1048576
-    tokens, 8 layers; layers 0-1 DENSE, layers 2-7 SPARSE with the shared
-    lightning indexer (4 heads of 64 dims, top-2048 shared by the 8 KV
-    heads).  One 8-layer step is timed under the mixed plan and all-dense;
-    one sparse layer is timed whole and call by call (indexer scores, top-k
-    of the one 1M-score row, gather-attend).  Values are N(0,1) (weights
-    U(0,1)) drawn on the device: the timings depend on the sizes."""
-    import torch
+# ---------------------------------------------------------------------------
+# The three other workloads on their seeded inputs (--workload NAME)
+# ---------------------------------------------------------------------------
+
+CPU_SHARE = 16   # oracle worker processes at most: one GPU's share of the host's cores
+
+
+def cpu_workers():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(CPU_SHARE, n))
+
+
+def _oracle_prepare(cfg, seed, task, shm):
+    """Generate (untimed) the inputs of one unit of the oracle's work and
+    return a function that runs the unit and gives its seconds per part."""
+    import oracle as O
     import sa_synth as S
-    import top_sparse_decode_sa_amd as T
 
-    T.lib()
-    dev = torch.device("cuda", 0)
-    c = S.CONFIGS["indexer1m"]
-    B, Hq, Hkv, d, N, k, L = c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.ctx_len, c.k, c.n_layers
-    H, Di = c.indexer_heads, c.indexer_dim
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(args.seed)
-    log("indexer1m: drawing %d layers (%.1f GB of KV)" % (L, L * c.kv_bytes() / 1e9))
+    w = S.Workload(cfg, seed)
+    c = w.cfg
+    G, scale = c.group, O.default_scale(c.head_dim)
+    clock = time.perf_counter
+    kind = task[0]
+    if kind == "row":          # one (sequence, KV head) row of an exact top-k layer
+        _, b, r = task
+        q = w.q(0, batch=(b, b + 1))[0, r * G:(r + 1) * G]
+        k, v = w.k_row(0, b, r), w.v_row(0, b, r)
 
-    def bf(shape):
-        return torch.empty(shape, dtype=torch.bfloat16, device=dev).normal_(generator=gen)
+        def run():
+            t0 = clock()
+            qg, kf = O.widen(q), O.widen(k)
+            t1 = clock()
+            sel = O.topk(O.scores_exact(qg, kf, scale), c.k)
+            t2 = clock()
+            O.attend(qg, O.widen(k[sel]), O.widen(v[sel]), np.arange(c.k), scale)
+            t3 = clock()
+            O.dense(qg, kf, O.widen(v), scale)
+            t4 = clock()
+            return {"select": t2 - t0, "attend": t3 - t2, "dense": (t1 - t0) + (t4 - t3)}
+        return run
+    if kind == "block_row":    # one row of the 4-layer block plan
+        _, b, r = task
+        qs = [w.q(l, batch=(b, b + 1))[0, r * G:(r + 1) * G] for l in range(c.n_layers)]
+        ks = [w.k_row(l, b, r) for l in range(c.n_layers)]
+        vs = [w.v_row(l, b, r) for l in range(c.n_layers)]
 
-    qs = [bf((B, Hq, d)) for _ in range(L)]
-    ks = [bf((B, Hkv, N, d)) for _ in range(L)]
-    vs = [bf((B, Hkv, N, d)) for _ in range(L)]
-    qi = [bf((B, H, Di)) for _ in range(L)]
-    ki = [bf((B, N, Di)) for _ in range(L)]
-    wi = [torch.rand((B, H), generator=gen, device=dev) for _ in range(L)]
-    outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(L)]
-    largs = [T.layer_args(qs[l], ks[l], vs[l], T.SA_SCORE_INDEXER, k, q_idx=qi[l], k_idx=ki[l],
-                          idx_w=wi[l], out=outs[l])[0] for l in range(L)]
-    ws = {m: T.WORKSPACES.get(dev, ("indexer1m", m), T.sa_layer_workspace_size(largs[0], m))
-          for m in (T.SA_LAYER_DENSE, T.SA_LAYER_SPARSE)}
-    idx = [torch.empty((B, k), dtype=torch.int32, device=dev) for _ in range(L)]
-    mixed = [T.SA_LAYER_DENSE if m == "dense" else T.SA_LAYER_SPARSE for m in c.modes]
-    T.sa_plan_validate(mixed, list(c.src))
-    reps = max(3, min(args.steps, 10))
+        def run():
+            t0 = clock()
+            kf = O.widen(ks[0])
+            kmin, kmax = O.block_summaries(kf, c.block_size)
+            t1 = clock()
+            q0 = O.widen(qs[0])
+            blocks = O.topk(O.scores_block(q0, kmin, kmax), c.k)
+            toks = O.block_tokens(blocks, c.block_size, c.ctx_len)
+            t2 = clock()
+            for l in range(c.n_layers):   # layer 0 SPARSE, layers 1-3 REUSE its blocks
+                O.attend(O.widen(qs[l]), O.widen(ks[l][toks]), O.widen(vs[l][toks]),
+                         np.arange(len(toks)), scale)
+            t3 = clock()
+            O.dense(q0, kf, O.widen(vs[0]), scale)
+            t4 = clock()
+            return {"summaries": t1 - t0, "select": t2 - t1, "attend": t3 - t2,
+                    "dense": (t4 - t3) + (t1 - t0)}
+        return run
+    if kind == "dense_row":    # one row of a DENSE layer of the 1M-token plan
+        _, layer, r = task
+        q = w.q(layer)[0, r * G:(r + 1) * G]
+        k, v = w.k_row(layer, 0, r), w.v_row(layer, 0, r)
 
-    def layer(l, m):
-        T.sa_decode_layer(largs[l], m, None if m == T.SA_LAYER_DENSE else idx[l], dev, ws[m])
+        def run():
+            t0 = clock()
+            O.dense(O.widen(q), O.widen(k), O.widen(v), scale)
+            return {"dense": clock() - t0}
+        return run
+    if kind == "indexer_layer":   # one SPARSE layer of the 1M-token plan (all 8 KV heads)
+        _, layer = task
+        z = np.load(os.path.join(shm, "layer%d.npz" % layer))
+        qi, ki, wi, q = z["qi"], z["ki"], z["wi"], z["q"]
 
-    def timed(fn, n):
-        for _ in range(2):
-            fn()
-        torch.cuda.synchronize()
-        layer(0, T.SA_LAYER_DENSE)  # queued ahead, so the host enqueues the rest in time
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(n):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n * 1e3  # us
+        def run():
+            t0 = clock()
+            sel = O.topk(O.scores_indexer(O.widen(qi[0]), O.widen(ki[0]), wi.astype(np.float64)),
+                         c.k)
+            t1 = clock()
+            # the selected rows are drawn from the generator's counters (untimed)
+            rows = [(w.kv_tokens("k", layer, 0, r, sel), w.kv_tokens("v", layer, 0, r, sel))
+                    for r in range(c.n_kv_heads)]
+            t2 = clock()
+            for r, (kr, vr) in enumerate(rows):
+                O.attend(O.widen(q[0, r * G:(r + 1) * G]), O.widen(kr), O.widen(vr),
+                         np.arange(c.k), scale)
+            t3 = clock()
+            return {"select": t1 - t0, "attend": t3 - t2}
+        return run
+    raise ValueError(kind)
 
-    us_mixed = timed(lambda: [layer(l, mixed[l]) for l in range(L)], reps)
-    us_dense8 = timed(lambda: [layer(l, T.SA_LAYER_DENSE) for l in range(L)], reps)
-    us_dense = timed(lambda: layer(2, T.SA_LAYER_DENSE), reps)
-    us_sparse = timed(lambda: layer(2, T.SA_LAYER_SPARSE), reps)
-    scores = torch.empty((B, N), dtype=torch.float32, device=dev)
-    sel = torch.empty((B, k), dtype=torch.int32, device=dev)
-    us_score = timed(lambda: T.sa_score(qs[2], ks[2], T.SA_SCORE_INDEXER, q_idx=qi[2], k_idx=ki[2],
-                                        idx_w=wi[2], scores=scores), reps)
-    us_topk = timed(lambda: T.sa_topk(scores, k, idx_out=sel), reps)
-    us_attend = timed(lambda: T.sa_sparse_decode(qs[2], ks[2], vs[2], sel, out=outs[2],
-                                                 index_kind=T.SA_IDX_TOKEN_SHARED), reps)
-    # the layer's own selection equals the calls' one
-    layer(2, T.SA_LAYER_SPARSE)
+
+def _oracle_worker(cfg, seed, tasks, shm, barrier, results):
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1):
+        runs = [_oracle_prepare(cfg, seed, t, shm) for t in tasks]
+        barrier.wait()
+        out = [fn() for fn in runs]
+    results.put(out)
+
+
+def oracle_pool(cfg, seed, task_lists, shm=None):
+    """Run the oracle's units in len(task_lists) worker processes, one BLAS /
+    OpenMP thread each: every worker generates its inputs, all start the
+    timed work together (a barrier), and each reports its units' seconds.
+    Returns (per-part makespan: the largest per-worker sum, units done)."""
+    import multiprocessing as mp
+
+    ctx = mp.get_context("spawn")
+    n = len(task_lists)
+    barrier, results = ctx.Barrier(n), ctx.Queue()
+    saved = {v: os.environ.get(v) for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                            "MKL_NUM_THREADS")}
+    os.environ.update({v: "1" for v in saved})
+    try:
+        procs = [ctx.Process(target=_oracle_worker, args=(cfg, seed, tl, shm, barrier, results))
+                 for tl in task_lists]
+        for p in procs:
+            p.start()
+        got = [results.get() for _ in procs]
+        for p in procs:
+            p.join()
+    finally:
+        for v, x in saved.items():
+            if x is None:
+                os.environ.pop(v, None)
+            else:
+                os.environ[v] = x
+    sums = [{} for _ in got]
+    for acc, worker in zip(sums, got):
+        for unit in worker:
+            for part, sec in unit.items():
+                acc[part] = acc.get(part, 0.0) + sec
+
+    def span(*parts):
+        return max(sum(acc.get(p_, 0.0) for p_ in parts) for acc in sums)
+    return span, sum(len(worker) for worker in got)
+
+
+def _spread(tasks, n):
+    """Deal tasks to n workers in turn."""
+    return [tasks[i::n] for i in range(n) if tasks[i::n]]
+
+
+def config_cpu_baseline(name, seed, attend_bytes, shm=None, cfg=None, workers=None):
+    """The oracle on the host: one thread on a stated subset, then all the
+    workers over a larger sample, each scaled to one step of the workload
+    `name` (cfg: the same workload at other sizes)."""
+    import sa_synth as S
+
+    c = S.CONFIGS[name] if cfg is None else cfg
+    W = workers or cpu_workers()
+    if name == "batch128k":
+        rows = c.batch * c.n_kv_heads
+        one = [("row", 0, r) for r in range(c.n_kv_heads)]
+        per = max(1, 64 // W)
+        sample = [("row", (i * 37) % c.batch, i % c.n_kv_heads) for i in range(W * per)]
+        one_unit, all_unit = rows / len(one), rows / len(sample)
+        what = ("exact scores, top-%d and selected-set attention of (sequence, KV head) rows; "
+                "dense: full attention of the same rows" % c.k)
+    elif name == "block61k":
+        rows = c.batch * c.n_kv_heads
+        one = [("block_row", 0, r) for r in range(c.n_kv_heads)]
+        sample = [("block_row", b, r) for b in range(c.batch) for r in range(c.n_kv_heads)]
+        one_unit, all_unit = rows / len(one), rows / len(sample)
+        what = ("per row: block scores from the layer-0 summaries, top-%d blocks, attention over "
+                "their tokens at all %d layers (SPARSE + REUSE); summaries (once per cache) and "
+                "dense layer 0 apart" % (c.k, c.n_layers))
+    else:
+        one = [("dense_row", 0, 0), ("indexer_layer", 2)]
+        sample = [("indexer_layer", l) for l in range(c.n_layers) if c.modes[l] == "sparse"] + \
+                 [("dense_row", l, r) for l in range(c.n_layers) if c.modes[l] == "dense"
+                  for r in range(c.n_kv_heads)]
+        one_unit = all_unit = None
+        what = ("the 8-layer plan: dense rows of layers 0-1, and for layers 2-7 the indexer "
+                "scores of all 1048576 tokens, the top-%d and the attention of the 8 KV heads "
+                "over it" % c.k)
+    log("%s: oracle on one thread (%d units)" % (name, len(one)))
+    t0 = time.perf_counter()
+    span1, n1 = oracle_pool(c, seed, [one], shm)
+    log("%s: oracle on %d workers (%d units)" % (name, W, len(sample)))
+    spanW, nW = oracle_pool(c, seed, _spread(sample, W), shm)
+    wall = time.perf_counter() - t0
+    if name == "indexer1m":
+        n_dense = sum(1 for m in c.modes if m == "dense") * c.n_kv_heads
+        n_sparse = sum(1 for m in c.modes if m == "sparse")
+        # one thread: one dense row and one sparse layer, scaled to the plan
+        step1 = n_dense * span1("dense") + n_sparse * span1("select", "attend")
+        att1 = n_sparse * span1("attend")
+        # all workers: the whole plan's units, so no scaling
+        stepW, attW = spanW("dense", "select", "attend"), spanW("attend")
+        dense1 = denseW = None
+    else:
+        step1 = span1("select", "attend") * one_unit
+        att1 = span1("attend") * one_unit
+        dense1 = span1("dense") * one_unit
+        stepW = spanW("select", "attend") * all_unit
+        attW = spanW("attend") * all_unit
+        denseW = spanW("dense") * all_unit
+    cpu = {"value": round(attend_bytes / attW / 1e9, 4), "unit": "GB/s", "cores": W,
+           "kind": "oracle", "steps_per_s": round(1.0 / stepW, 4),
+           "sample": "fp64 numpy oracle on %d worker processes of one thread (%s), %d units, "
+                     "scaled to one step; value: its selected-set attention's algorithmic bytes "
+                     "per step over its attention time" % (W, what, nW),
+           "one_thread": {"steps_per_s": round(1.0 / step1, 4),
+                          "attend_gbps": round(attend_bytes / att1 / 1e9, 4),
+                          "sample": "units %s, scaled to one step" % (one,)},
+           "wall_s": round(wall, 1)}
+    if dense1 is not None:
+        cpu["dense_steps_per_s"] = round(1.0 / denseW, 4)
+        cpu["one_thread"]["dense_steps_per_s"] = round(1.0 / dense1, 4)
+    cpu.update(host_cpu())
+    return cpu
+
+
+def _ev_us(fn, n, warm=2):
+    """Mean microseconds per call over n back-to-back calls (HIP events on
+    the current stream)."""
+    import torch
+
+    for _ in range(warm):
+        fn()
     torch.cuda.synchronize()
-    assert torch.equal(idx[2], sel), "sparse layer and its calls selected differently"
-    dense_bytes = 2 * B * Hkv * N * d * 2
-    score_bytes = B * N * Di * 2 + B * N * 4
-    gather_bytes = 2 * B * Hkv * k * d * 2
-    res = {
-        "bench": "indexer1m: mixed 8-layer decode step", "unit": "us (HIP events)",
-        "config": {"workload": "indexer1m: batch 1, 32/8 heads, d 128, bf16, 1048576 tokens, 8 layers "
-                               "(2 dense, 6 sparse with a 4x64 shared indexer, top-2048)",
-                   "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d, "ctx_len": N,
-                   "k": k, "indexer_heads": H, "indexer_dim": Di, "modes": list(c.modes)},
-        "mixed_step_us": round(us_mixed, 1), "all_dense_step_us": round(us_dense8, 1),
-        "mixed_speedup_vs_all_dense": round(us_dense8 / us_mixed, 2),
-        "dense_layer_us": round(us_dense, 1), "dense_layer_bytes": dense_bytes,
-        "dense_layer_gbps": round(dense_bytes / us_dense / 1e3, 1),
-        "sparse_layer_us": round(us_sparse, 1),
-        "indexer_score_us": round(us_score, 1), "indexer_score_bytes": score_bytes,
-        "indexer_score_gbps": round(score_bytes / us_score / 1e3, 1),
-        "topk_us": round(us_topk, 1), "attend_us": round(us_attend, 1),
-        "attend_bytes": gather_bytes, "attend_gbps": round(gather_bytes / us_attend / 1e3, 1),
-        "data": "N(0,1) drawn on the device (seed %d)" % args.seed,
-        "provenance": provenance()}
-    for key in ("mixed_step_us", "all_dense_step_us", "mixed_speedup_vs_all_dense", "dense_layer_us",
-                "dense_layer_gbps", "sparse_layer_us", "indexer_score_us", "indexer_score_gbps",
-                "topk_us", "attend_us", "attend_gbps"):
-        print("%28s  %s" % (key, res[key]))
-    print(json.dumps(res), flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n * 1e3
 
 
-def block61k(args):
-    """The block61k workload on the device: batch 8, 32/8 heads, d 128, bf16,
-    61440 tokens = 480 blocks of 128, 24 blocks kept per (sequence, KV head),
-    4 layers planned [SPARSE, REUSE 0, REUSE 0, REUSE 0].  Per call: the
-    per-block key summaries (built once per cache, read K, write min/max),
-    the block scores from the summaries, the top-24 of 480 and the gather-
-    attend of the 3072 tokens of the kept blocks; then the 4-layer step
-    against 4 dense layers.  Values are N(0,1) drawn on the device."""
+def _graph_us(fns, n):
+    """Microseconds per call of the calls fns captured back to back in one
+    HIP graph, replayed n times between HIP events."""
     import torch
+
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    return _ev_us(g.replay, n, warm=3) / len(fns)
+
+
+def _cold_us(fns, iters, dev):
+    """Cache-cold single launches: before each, a 1 GiB read evicts L2 and the
+    256 MB last-level cache.  Returns {name: median us} over `iters` rounds."""
+    import torch
+
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    times = {name: [] for name in fns}
+    for i in range(iters + 2):
+        for name, fn in fns.items():
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                times[name].append(e0.elapsed_time(e1) * 1e3)
+    del flush
+    return {name: float(np.median(v)) for name, v in times.items()}
+
+
+def _rate(nbytes, us):
+    if us is None:
+        return None
+    g = nbytes / us / 1e3
+    return {"bytes": int(nbytes), "us": round(us, 3), "gbps": round(g, 1),
+            "frac": round(g / HBM_PEAK_GBPS, 4)}
+
+
+def _stream_floor(nbytes, dev):
+    """sa_stream_read over nbytes (rounded down to 16 B) as a cold single launch."""
+    import torch
+    import top_sparse_decode_sa_amd as T
+
+    sbuf = torch.empty(nbytes // 16 * 16, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    return sbuf, (lambda: T.sa_stream_read(sbuf, sink))
+
+
+def _line(name, c, args, value_kernel, timing, extra):
+    """One JSON line of a seeded-workload run."""
+    at = value_kernel
+    line = {
+        "metric": "sparse-decode attn: achieved HBM GB/s (% of peak) + decode steps/s",
+        "value": at["gbps"], "unit": "GB/s", "hbm_frac": at["frac"], "attend_us": at["us"],
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "timing": timing,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: the seeded %s workload (counter-based generator; generation and "
+                "upload untimed)" % name,
+        "roofline": {"bound": "hbm", "achieved": at["gbps"], "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": at["frac"], "traffic": None,
+                     "kernel": "sparse_attend", "bytes_per_launch": at["bytes"]},
+    }
+    line.update(extra)
+    line["provenance"] = provenance()
+    return line
+
+
+def bench_batch128k(args):
+    """batch 128, 32/8 heads, d 128, bf16, 131072 tokens (68.7 GB of KV), exact
+    top-262 per (sequence, KV head) at 500x, the 262 planted heavy keys of each
+    row.  The step: sa_select then sa_sparse_decode.  The gather-attend
+    (137.4 MB) fits the 256 MB last-level cache, so back-to-back repeats would
+    be cache hits: `value` is the median cache-cold single launch after a
+    1 GiB read, beside a cold sa_stream_read of the same byte count."""
     import sa_synth as S
+
+    name = "batch128k"
+    c = S.CONFIGS[name]
+    att_bytes = step_bytes(c)["sparse_attend"]
+    cpu = config_cpu_baseline(name, args.seed, att_bytes) if args.cpu_seconds > 0 else None
+
+    import torch
     import top_sparse_decode_sa_amd as T
 
     T.lib()
     dev = torch.device("cuda", 0)
-    c = S.CONFIGS["block61k"]
-    B, Hq, Hkv, d, N, bs, nblk, L = (c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.ctx_len,
-                                     c.block_size, c.k, c.n_layers)
-    nb = N // bs
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(args.seed)
-    log("block61k: drawing %d layers (%.1f GB of KV)" % (L, L * c.kv_bytes() / 1e9))
+    w = S.Workload(name, args.seed)
+    log("%s: generating %.1f GB of KV" % (name, c.kv_bytes() / 1e9))
+    gen_s = up_s = 0.0
+    kd = torch.empty((c.batch, c.n_kv_heads, c.ctx_len, c.head_dim), dtype=torch.bfloat16,
+                     device=dev)
+    vd = torch.empty_like(kd)
+    for b0 in range(0, c.batch, 4):
+        for which, dst in (("k", kd), ("v", vd)):
+            t0 = time.perf_counter()
+            host = w.k(0, batch=(b0, b0 + 4)) if which == "k" else w.v(0, batch=(b0, b0 + 4))
+            t1 = time.perf_counter()
+            dst[b0:b0 + 4].copy_(torch.from_numpy(host).view(torch.bfloat16))
+            torch.cuda.synchronize()
+            gen_s += t1 - t0
+            up_s += time.perf_counter() - t1
+            del host
+    qd = [torch.from_numpy(w.q(0, qvar=v)).view(torch.bfloat16).to(dev) for v in range(2)]
+    idx = torch.empty((c.batch, c.n_kv_heads, c.k), dtype=torch.int32, device=dev)
+    out = torch.empty((c.batch, c.n_q_heads, c.head_dim), dtype=torch.float32, device=dev)
+    n_steps, n_warm = max(3, min(args.steps, 20)), max(1, min(args.warmup, 3))
 
-    def bf(shape):
-        return torch.empty(shape, dtype=torch.bfloat16, device=dev).normal_(generator=gen)
+    def select(i=0):
+        T.sa_select(qd[i % 2], kd, c.k, idx_out=idx)
 
-    qs = [bf((B, Hq, d)) for _ in range(L)]
-    ks = [bf((B, Hkv, N, d)) for _ in range(L)]
-    vs = [bf((B, Hkv, N, d)) for _ in range(L)]
+    def attend(i=0):
+        T.sa_sparse_decode(qd[i % 2], kd, vd, idx, out=out)
+
+    for i in range(n_warm):
+        select(i)
+        attend(i)
+    torch.cuda.synchronize()
+    # the selection is the planted set of every row
+    planted = np.stack([[w.planted(0, b, r) for r in range(c.n_kv_heads)] for b in range(c.batch)])
+    assert np.array_equal(idx.cpu().numpy(), planted), "selection differs from the planted sets"
+    assert T.sa_check_indices(qd[0], kd, idx).tolist() == [0, 0]
+    log("%s: timing %d steps" % (name, n_steps))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n_steps):
+        ev[i][0].record()
+        select(i)
+        ev[i][1].record()
+        attend(i)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / n_steps
+    us_sel = sum(e[0].elapsed_time(e[1]) for e in ev) / n_steps * 1e3
+    us_att_step = sum(e[1].elapsed_time(e[2]) for e in ev) / n_steps * 1e3
+    sbuf, stream = _stream_floor(att_bytes, dev)
+    cold = _cold_us({"attend": attend, "stream": stream}, max(5, args.cold_iters), dev)
+    del sbuf
+    dout = torch.empty_like(out)
+    us_dense = _ev_us(lambda: T.sa_dense_decode(qd[0], kd, vd, out=dout), 3, warm=1)
+    nb = step_bytes(c)
+    att = _rate(att_bytes, cold["attend"])
+    kernels = {"sparse_attend_cold": att,
+               "stream_read_same_bytes_cold": _rate(att_bytes // 16 * 16, cold["stream"]),
+               "sparse_attend_in_step": _rate(att_bytes, us_att_step),
+               "select": _rate(nb["select"], us_sel),
+               "dense_decode": _rate(nb["dense_decode"], us_dense)}
+    line = _line(name, c, args, att,
+                 "value: median of %d cache-cold single gather-attend launches (HIP events), "
+                 "each after a 1 GiB read; steps: %d eager steps (select + gather-attend) after "
+                 "%d warmup" % (max(5, args.cold_iters), n_steps, n_warm),
+                 {"ms_per_step": round(ms_step, 4), "steps_per_s": round(1e3 / ms_step, 2),
+                  "config": {"workload": "batch128k: large batch at 500x sparsity, exact top-k",
+                             "batch": c.batch, "n_q_heads": c.n_q_heads,
+                             "n_kv_heads": c.n_kv_heads, "head_dim": c.head_dim,
+                             "ctx_len": c.ctx_len, "k": c.k, "kv_dtype": c.dtype,
+                             "parallelism": "single GPU"},
+                  "kernels": kernels,
+                  "sparse_over_dense_speedup": round(us_dense / cold["attend"], 2),
+                  "step_over_dense_speedup": round(us_dense / (ms_step * 1e3), 3),
+                  "generation_s": round(gen_s, 1), "upload_s": round(up_s, 1),
+                  "cpu_baseline": cpu})
+    line["roofline"]["cold_frac_of_same_bytes_stream"] = round(cold["stream"] / cold["attend"], 4)
+    print(json.dumps(line), flush=True)
+
+
+def bench_block61k(args):
+    """batch 8, 32/8 heads, d 128, bf16, 61440 tokens = 480 blocks of 128, the
+    top 24 blocks per (sequence, KV head) from per-block key min/max
+    summaries, 4 layers planned [SPARSE, REUSE 0 x 3] over keys correlated
+    0.9 from layer to layer.  `value`: the block gather-attend (3072 tokens a
+    row, 100.9 MB a layer), the four layers' attends over their own caches
+    back to back in a HIP graph (403 MB, more than the last-level cache)."""
+    import sa_synth as S
+
+    name = "block61k"
+    c = S.CONFIGS[name]
+    bs, L = c.block_size, c.n_layers
+    rows, nb = c.batch * c.n_kv_heads, c.ctx_len // c.block_size
+    att_bytes = (2 * rows * c.k * bs * c.head_dim * 2 + rows * c.k * 4 + c.batch * c.n_q_heads *
+                 c.head_dim * (2 + 4))
+    cpu = config_cpu_baseline(name, args.seed, att_bytes * L) if args.cpu_seconds > 0 else None
+
+    import torch
+    import top_sparse_decode_sa_amd as T
+
+    T.lib()
+    dev = torch.device("cuda", 0)
+    w = S.Workload(name, args.seed)
+    log("%s: generating %d layers (%.1f GB of KV)" % (name, L, L * c.kv_bytes() / 1e9))
+    gen_s = up_s = 0.0
+    qs, ks, vs = [], [], []
+    for l in range(L):
+        t0 = time.perf_counter()
+        kh, vh, qh = w.k(l), w.v(l), w.q(l)
+        t1 = time.perf_counter()
+        for h, lst in ((kh, ks), (vh, vs), (qh, qs)):
+            lst.append(torch.from_numpy(h).view(torch.bfloat16).to(dev))
+        torch.cuda.synchronize()
+        gen_s += t1 - t0
+        up_s += time.perf_counter() - t1
+        del kh, vh, qh
     kmin, kmax = T.sa_block_summarize(ks[0], bs, q_like=qs[0])
-    scores = torch.empty((B, Hkv, nb), dtype=torch.float32, device=dev)
-    idx = torch.empty((B, Hkv, nblk), dtype=torch.int32, device=dev)
-    outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(L)]
-    largs = [T.layer_args(qs[l], ks[l], vs[l], T.SA_SCORE_BLOCK_MINMAX, nblk, kmin=kmin, kmax=kmax,
+    scores = torch.empty((c.batch, c.n_kv_heads, nb), dtype=torch.float32, device=dev)
+    idx = torch.empty((c.batch, c.n_kv_heads, c.k), dtype=torch.int32, device=dev)
+    outs = [torch.empty((c.batch, c.n_q_heads, c.head_dim), dtype=torch.float32, device=dev)
+            for _ in range(L)]
+    largs = [T.layer_args(qs[l], ks[l], vs[l], T.SA_SCORE_BLOCK_MINMAX, c.k, kmin=kmin, kmax=kmax,
                           block_size=bs, out=outs[l])[0] for l in range(L)]
-    modes = [T.SA_LAYER_DENSE if m == "dense" else T.SA_LAYER_SPARSE if m == "sparse" else
-             T.SA_LAYER_REUSE for m in c.modes]
+    modes = [T.SA_LAYER_SPARSE if m == "sparse" else T.SA_LAYER_REUSE for m in c.modes]
     T.sa_plan_validate(modes, list(c.src))
-    ws = {m: T.WORKSPACES.get(dev, ("block61k", m), T.sa_layer_workspace_size(largs[0], m))
+    ws = {m: T.WORKSPACES.get(dev, (name, m), T.sa_layer_workspace_size(largs[0], m))
           for m in (T.SA_LAYER_DENSE, T.SA_LAYER_SPARSE, T.SA_LAYER_REUSE)}
-    reps = max(3, min(args.steps, 10))
 
     def layer(l, m):
         T.sa_decode_layer(largs[l], m, None if m == T.SA_LAYER_DENSE else idx, dev, ws[m])
 
-    def timed(fn, n):
-        for _ in range(2):
-            fn()
-        torch.cuda.synchronize()
-        layer(0, T.SA_LAYER_DENSE)  # queued ahead, so the host enqueues the rest in time
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(n):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n * 1e3  # us
+    def plan():
+        for l in range(L):
+            layer(l, modes[l])
 
-    us_summ = timed(lambda: T.sa_block_summarize(ks[0], bs, q_like=qs[0], kmin=kmin, kmax=kmax), reps)
-    us_score = timed(lambda: T.sa_score(qs[0], ks[0], T.SA_SCORE_BLOCK_MINMAX, kmin=kmin, kmax=kmax,
-                                        block_size=bs, scores=scores), reps)
-    us_topk = timed(lambda: T.sa_topk(scores, nblk, idx_out=idx), reps)
-    us_attend = timed(lambda: T.sa_sparse_decode(qs[0], ks[0], vs[0], idx, out=outs[0],
-                                                 index_kind=T.SA_IDX_BLOCK_PER_KV_HEAD,
-                                                 block_size=bs), reps)
-    us_sparse = timed(lambda: layer(0, T.SA_LAYER_SPARSE), reps)
-    us_reuse = timed(lambda: layer(1, T.SA_LAYER_REUSE), reps)
-    us_dense = timed(lambda: layer(0, T.SA_LAYER_DENSE), reps)
-    us_plan = timed(lambda: [layer(l, modes[l]) for l in range(L)], reps)
-    us_dense4 = timed(lambda: [layer(l, T.SA_LAYER_DENSE) for l in range(L)], reps)
-    rows = B * Hkv
-    summ_bytes = rows * N * d * 2 + 2 * rows * nb * d * 2
-    score_bytes = 2 * rows * nb * d * 2 + B * Hq * d * 2 + rows * nb * 4
-    topk_bytes = rows * nb * 4 + rows * nblk * 4
-    attend_bytes = 2 * rows * nblk * bs * d * 2 + rows * nblk * 4 + 2 * B * Hq * d * 2 + B * Hq * d * 4
-    dense_bytes = 2 * rows * N * d * 2
+    n_steps, n_warm = max(3, min(args.steps, 50)), max(1, min(args.warmup, 5))
+    for _ in range(n_warm):
+        plan()
+    torch.cuda.synchronize()
+    assert T.sa_check_indices(qs[0], ks[0], idx, T.SA_IDX_BLOCK_PER_KV_HEAD, bs).tolist() == [0, 0]
+    log("%s: timing %d 4-layer steps" % (name, n_steps))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(L + 1)] for _ in range(n_steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n_steps):
+        for l in range(L):
+            ev[i][l].record()
+            layer(l, modes[l])
+        ev[i][L].record()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / n_steps
+    us_layer = [sum(e[l].elapsed_time(e[l + 1]) for e in ev) / n_steps * 1e3 for l in range(L)]
 
-    def rate(nbytes, us):
-        return {"us": round(us, 1), "bytes": nbytes, "gbps": round(nbytes / us / 1e3, 1),
-                "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
+    def attend(l):
+        return lambda: T.sa_sparse_decode(qs[l], ks[l], vs[l], idx, out=outs[l],
+                                          index_kind=T.SA_IDX_BLOCK_PER_KV_HEAD, block_size=bs)
 
-    res = {
-        "bench": "block61k: block selection and reuse on the device", "unit": "us (HIP events)",
-        "config": {"workload": "block61k: batch 8, 32/8 heads, d 128, bf16, 61440 tokens = 480 "
-                               "blocks of 128, 24 blocks kept; 4 layers [SPARSE, REUSE x3]",
-                   "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d, "ctx_len": N,
-                   "block_size": bs, "blocks_kept": nblk, "modes": list(c.modes)},
-        "block_summarize": rate(summ_bytes, us_summ),
-        "block_score": rate(score_bytes, us_score),
-        "block_topk": rate(topk_bytes, us_topk),
-        "block_attend": rate(attend_bytes, us_attend),
-        "sparse_layer_us": round(us_sparse, 1), "reuse_layer_us": round(us_reuse, 1),
-        "dense_layer": rate(dense_bytes, us_dense),
-        "plan_4_layers_us": round(us_plan, 1), "all_dense_4_layers_us": round(us_dense4, 1),
-        "plan_speedup_vs_all_dense": round(us_dense4 / us_plan, 2),
-        "data": "N(0,1) drawn on the device (seed %d)" % args.seed,
-        "provenance": provenance()}
-    for key in ("block_summarize", "block_score", "block_topk", "block_attend", "dense_layer"):
-        print("%18s  %s" % (key, res[key]))
-    for key in ("sparse_layer_us", "reuse_layer_us", "plan_4_layers_us", "all_dense_4_layers_us",
-                "plan_speedup_vs_all_dense"):
-        print("%18s  %s" % (key, res[key]))
-    print(json.dumps(res), flush=True)
+    reps = max(10, min(args.steps, 50))
+    us_att = _graph_us([attend(l) for l in range(L)], reps)
+    us_summ = _ev_us(lambda: T.sa_block_summarize(ks[0], bs, q_like=qs[0], kmin=kmin, kmax=kmax), 5)
+    us_score = _ev_us(lambda: T.sa_score(qs[0], ks[0], T.SA_SCORE_BLOCK_MINMAX, kmin=kmin,
+                                         kmax=kmax, block_size=bs, scores=scores), reps)
+    us_topk = _ev_us(lambda: T.sa_topk(scores, c.k, idx_out=idx), reps)
+    sbuf, stream = _stream_floor(att_bytes, dev)
+    cold = _cold_us({"attend": attend(0), "stream": stream,
+                     "sparse_layer": lambda: layer(0, T.SA_LAYER_SPARSE)},
+                    max(5, args.cold_iters), dev)
+    del sbuf
+    us_dense = _ev_us(lambda: layer(0, T.SA_LAYER_DENSE), 5)
+    us_dense4 = _ev_us(lambda: [layer(l, T.SA_LAYER_DENSE) for l in range(L)], 3)
+    summ_bytes = rows * c.ctx_len * c.head_dim * 2 + 2 * rows * nb * c.head_dim * 2
+    score_bytes = 2 * rows * nb * c.head_dim * 2 + c.batch * c.n_q_heads * c.head_dim * 2 + rows * nb * 4
+    topk_bytes = rows * nb * 4 + rows * c.k * 4
+    dense_bytes = 2 * rows * c.ctx_len * c.head_dim * 2
+    att = _rate(att_bytes, us_att)
+    kernels = {"sparse_attend": att, "sparse_attend_cold": _rate(att_bytes, cold["attend"]),
+               "stream_read_same_bytes_cold": _rate(att_bytes // 16 * 16, cold["stream"]),
+               "block_summarize": _rate(summ_bytes, us_summ),
+               "block_score": _rate(score_bytes, us_score),
+               "block_topk": _rate(topk_bytes, us_topk),
+               "dense_layer": _rate(dense_bytes, us_dense)}
+    line = _line(name, c, args, att,
+                 "value: the %d layers' block gather-attends captured back to back in a HIP "
+                 "graph, replayed %d times (HIP events); steps: %d eager 4-layer plan steps after "
+                 "%d warmup, per-layer HIP events" % (L, reps, n_steps, n_warm),
+                 {"ms_per_step": round(ms_step, 4), "steps_per_s": round(1e3 / ms_step, 1),
+                  "config": {"workload": "block61k: 128-token block selection, 4 layers "
+                                         "[SPARSE, REUSE 0 x3]",
+                             "batch": c.batch, "n_q_heads": c.n_q_heads,
+                             "n_kv_heads": c.n_kv_heads, "head_dim": c.head_dim,
+                             "ctx_len": c.ctx_len, "block_size": bs, "blocks_kept": c.k,
+                             "modes": list(c.modes), "kv_dtype": c.dtype,
+                             "parallelism": "single GPU"},
+                  "kernels": kernels,
+                  "layers_us": {"sparse": round(us_layer[0], 1),
+                                "reuse": round(sum(us_layer[1:]) / (L - 1), 1),
+                                "sparse_cold": round(cold["sparse_layer"], 1),
+                                "dense": round(us_dense, 1)},
+                  "plan_step_us": round(ms_step * 1e3, 1),
+                  "all_dense_step_us": round(us_dense4, 1),
+                  "plan_speedup_vs_all_dense": round(us_dense4 / (ms_step * 1e3), 2),
+                  "omega_msr": 1.0,
+                  "generation_s": round(gen_s, 1), "upload_s": round(up_s, 1),
+                  "cpu_baseline": cpu})
+    line["roofline"]["cold_frac_of_same_bytes_stream"] = round(cold["stream"] / cold["attend"], 4)
+    print(json.dumps(line), flush=True)
+
+
+def bench_indexer1m(args):
+    """One sequence of 1048576 tokens, 32/8 heads, d 128, bf16, 8 layers:
+    layers 0-1 DENSE, layers 2-7 SPARSE, each with its own lightning indexer
+    (4 heads x 64 dims, keys projected from the layer's keys) and a top-2048
+    shared by the 8 KV heads.  `value`: the gather-attend of the six sparse
+    layers (8.39 MB each) captured back to back in a HIP graph; beside it
+    the 8-layer mixed step against 8 dense layers, and Omega_MSR (the share
+    of layers attending sparsely)."""
+    import shutil
+    import tempfile
+    import sa_synth as S
+
+    name = "indexer1m"
+    c = S.CONFIGS[name]
+    L = c.n_layers
+    sparse_l = [l for l in range(L) if c.modes[l] == "sparse"]
+    att_bytes = 2 * c.n_kv_heads * c.k * c.head_dim * 2 + c.k * 4 + c.n_q_heads * c.head_dim * 6
+    w = S.Workload(name, args.seed)
+    log("%s: generating %d layers (%.1f GB of KV)" % (name, L, L * c.kv_bytes() / 1e9))
+    t0 = time.perf_counter()
+    host = []
+    for l in range(L):
+        kh, vh, qh = w.k(l), w.v(l), w.q(l)
+        ind = None
+        if c.modes[l] == "sparse":
+            ind = (w.indexer_q(l, qh), w.indexer_k(l, kh), w.indexer_w(l))
+        host.append((kh, vh, qh, ind))
+    gen_s = time.perf_counter() - t0
+    cpu = None
+    if args.cpu_seconds > 0:
+        shm = tempfile.mkdtemp(prefix="sa_oracle_", dir="/dev/shm" if os.path.isdir("/dev/shm")
+                               else None)
+        try:
+            for l in sparse_l:
+                qi, ki, wi = host[l][3]
+                np.savez(os.path.join(shm, "layer%d.npz" % l), qi=qi, ki=ki, wi=wi, q=host[l][2])
+            cpu = config_cpu_baseline(name, args.seed, att_bytes * len(sparse_l), shm)
+        finally:
+            shutil.rmtree(shm, ignore_errors=True)
+
+    import torch
+    import top_sparse_decode_sa_amd as T
+
+    T.lib()
+    dev = torch.device("cuda", 0)
+
+    def up(x):
+        t = torch.from_numpy(np.ascontiguousarray(x))
+        return (t.view(torch.bfloat16) if t.dtype == torch.uint16 else t).to(dev)
+
+    t0 = time.perf_counter()
+    qs, ks, vs, qi, ki, wi = [], [], [], {}, {}, {}
+    for l in range(L):
+        kh, vh, qh, ind = host[l]
+        ks.append(up(kh))
+        vs.append(up(vh))
+        qs.append(up(qh))
+        if ind is not None:
+            qi[l], ki[l], wi[l] = up(ind[0]), up(ind[1]), up(ind[2][None, :].copy())
+        host[l] = None
+    torch.cuda.synchronize()
+    up_s = time.perf_counter() - t0
+    del host
+    outs = [torch.empty((c.batch, c.n_q_heads, c.head_dim), dtype=torch.float32, device=dev)
+            for _ in range(L)]
+    largs = [T.layer_args(qs[l], ks[l], vs[l], T.SA_SCORE_INDEXER, c.k, q_idx=qi.get(l),
+                          k_idx=ki.get(l), idx_w=wi.get(l), out=outs[l])[0]
+             if l in qi else T.layer_args(qs[l], ks[l], vs[l], T.SA_SCORE_EXACT, c.k,
+                                          out=outs[l])[0] for l in range(L)]
+    idx = [torch.empty((c.batch, c.k), dtype=torch.int32, device=dev) for _ in range(L)]
+    mixed = [T.SA_LAYER_DENSE if m == "dense" else T.SA_LAYER_SPARSE for m in c.modes]
+    T.sa_plan_validate(mixed, list(c.src))
+    ws = {m: T.WORKSPACES.get(dev, (name, m), max(T.sa_layer_workspace_size(largs[l], m)
+                                                  for l in sparse_l))
+          for m in (T.SA_LAYER_DENSE, T.SA_LAYER_SPARSE)}
+
+    def layer(l, m):
+        T.sa_decode_layer(largs[l], m, None if m == T.SA_LAYER_DENSE else idx[l], dev, ws[m])
+
+    n_steps, n_warm = max(3, min(args.steps, 20)), max(1, min(args.warmup, 3))
+    for _ in range(n_warm):
+        for l in range(L):
+            layer(l, mixed[l])
+    torch.cuda.synchronize()
+    for l in sparse_l:
+        assert T.sa_check_indices(qs[l], ks[l], idx[l], T.SA_IDX_TOKEN_SHARED).tolist() == [0, 0]
+    log("%s: timing %d 8-layer steps" % (name, n_steps))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(L + 1)] for _ in range(n_steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n_steps):
+        for l in range(L):
+            ev[i][l].record()
+            layer(l, mixed[l])
+        ev[i][L].record()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / n_steps
+    us_layer = [sum(e[l].elapsed_time(e[l + 1]) for e in ev) / n_steps * 1e3 for l in range(L)]
+    us_dense8 = _ev_us(lambda: [layer(l, T.SA_LAYER_DENSE) for l in range(L)], 3, warm=1)
+    reps = max(10, min(args.steps, 50))
+
+    def attend(l):
+        return lambda: T.sa_sparse_decode(qs[l], ks[l], vs[l], idx[l], out=outs[l],
+                                          index_kind=T.SA_IDX_TOKEN_SHARED)
+
+    us_att = _graph_us([attend(l) for l in sparse_l], reps)
+    scores = [torch.empty((c.batch, c.ctx_len), dtype=torch.float32, device=dev) for _ in sparse_l]
+    sel = torch.empty((c.batch, c.k), dtype=torch.int32, device=dev)
+    n_sp = len(sparse_l)
+    us_score = _ev_us(lambda: [T.sa_score(qs[l], ks[l], T.SA_SCORE_INDEXER, q_idx=qi[l],
+                                          k_idx=ki[l], idx_w=wi[l], scores=scores[j])
+                               for j, l in enumerate(sparse_l)], max(3, reps // n_sp)) / n_sp
+    us_topk = _ev_us(lambda: [T.sa_topk(scores[j], c.k, idx_out=sel) for j in range(n_sp)],
+                     max(3, reps // n_sp)) / n_sp
+    torch.cuda.synchronize()
+    score_bytes = c.ctx_len * c.indexer_dim * 2 + c.ctx_len * 4
+    dense_bytes = 2 * c.n_kv_heads * c.ctx_len * c.head_dim * 2
+    us_sparse = sum(us_layer[l] for l in sparse_l) / n_sp
+    us_dense = sum(us_layer[l] for l in range(L) if l not in sparse_l) / (L - n_sp)
+    att = _rate(att_bytes, us_att)
+    kernels = {"sparse_attend": att, "indexer_score": _rate(score_bytes, us_score),
+               "topk_1m": _rate(c.ctx_len * 4 + c.k * 4, us_topk),
+               "dense_layer": _rate(dense_bytes, us_dense)}
+    line = _line(name, c, args, att,
+                 "value: the %d sparse layers' gather-attends captured back to back in a HIP "
+                 "graph, replayed %d times (HIP events); steps: %d eager 8-layer steps after %d "
+                 "warmup, per-layer HIP events" % (n_sp, reps, n_steps, n_warm),
+                 {"ms_per_step": round(ms_step, 4), "steps_per_s": round(1e3 / ms_step, 2),
+                  "config": {"workload": "indexer1m: one 1M-token sequence, 8 layers (2 dense, "
+                                         "6 sparse with a 4x64 lightning indexer, top-2048 "
+                                         "shared by the KV heads)",
+                             "batch": c.batch, "n_q_heads": c.n_q_heads,
+                             "n_kv_heads": c.n_kv_heads, "head_dim": c.head_dim,
+                             "ctx_len": c.ctx_len, "k": c.k, "indexer_heads": c.indexer_heads,
+                             "indexer_dim": c.indexer_dim, "modes": list(c.modes),
+                             "kv_dtype": c.dtype, "parallelism": "single GPU"},
+                  "kernels": kernels,
+                  "layers_us": {"sparse": round(us_sparse, 1), "dense": round(us_dense, 1)},
+                  "mixed_step_us": round(ms_step * 1e3, 1),
+                  "all_dense_step_us": round(us_dense8, 1),
+                  "mixed_speedup_vs_all_dense": round(us_dense8 / (ms_step * 1e3), 2),
+                  "omega_msr": round(n_sp / L, 4),
+                  "generation_s": round(gen_s, 1), "upload_s": round(up_s, 1),
+                  "cpu_baseline": cpu})
+    print(json.dumps(line), flush=True)
 
 
 def hylra(args):
@@ -1105,11 +1587,14 @@ def main():
     if args.gpus == 1 and args.sweep:
         sweep(args)
         return
-    if args.gpus == 1 and args.block61k:
-        block61k(args)
-        return
-    if args.gpus == 1 and args.indexer1m:
-        indexer1m(args)
+    if args.block61k:
+        args.workload = "block61k"
+    if args.indexer1m:
+        args.workload = "indexer1m"
+    seeded = {"block61k": bench_block61k, "batch128k": bench_batch128k,
+              "indexer1m": bench_indexer1m}
+    if args.gpus == 1 and args.workload in seeded:
+        seeded[args.workload](args)
         return
     if args.gpus == 1 and args.nscale:
         nscale(args)

@@ -27,6 +27,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "csrc", "synth.c")
 _LIB_PATH = os.path.join(_HERE, "libsa_synth.so")
+# the same generator built with ASan + UBSan (build_lib_sanitized); selected
+# by SA_SYNTH_LIBRARY, loaded with the sanitizer runtime preloaded
+_SAN_LIB_PATH = os.path.join(_HERE, "_build", "sanitized", "libsa_synth.so")
 
 OUT_F64, OUT_F32, OUT_BF16 = 0, 1, 2
 
@@ -45,15 +48,29 @@ def build_lib(force: bool = False) -> str:
     return _LIB_PATH
 
 
+def build_lib_sanitized(clang: str) -> str:
+    """Compile the generator with clang under ASan + UBSan (no OpenMP)."""
+    os.makedirs(os.path.dirname(_SAN_LIB_PATH), exist_ok=True)
+    tmp = _SAN_LIB_PATH + ".tmp%d" % os.getpid()
+    subprocess.check_call([clang, "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                           "-fno-sanitize-recover=undefined", "-shared-libsan", "-fPIC", "-shared",
+                           "-Wno-unknown-pragmas", "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _SAN_LIB_PATH)
+    return _SAN_LIB_PATH
+
+
 _lib = None
 
 
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            build_lib()
-        L = ctypes.CDLL(_LIB_PATH)
+        path = os.environ.get("SA_SYNTH_LIBRARY")
+        if not path:
+            path = _LIB_PATH
+            if not os.path.exists(path):
+                build_lib()
+        L = ctypes.CDLL(path)
         u64, i64, u32, dbl, vp = (ctypes.c_uint64, ctypes.c_int64, ctypes.c_uint32,
                                   ctypes.c_double, ctypes.c_void_p)
         L.synth_stream_id.argtypes = [u32, u32, u32, u32]
@@ -320,6 +337,22 @@ class Workload:
             lib().synth_normal(self.seed, stream_id(TAG_K, layer, b, r), 0, per, 0.0, 1.0, c.kind,
                                _ptr(out))
             self._plant(out, layer, b, r)
+        return out
+
+    def kv_tokens(self, which: str, layer: int, b: int, r: int, toks) -> np.ndarray:
+        """K ("k") or V ("v") of the listed tokens of one (sequence, KV head)
+        row, [len(toks), d], storage format: the same values as k_row / v_row
+        at those rows, drawn from the counters alone.  Only for caches drawn
+        without planting or a layer chain (indexer1m's keys, every V)."""
+        c = self.cfg
+        if which == "k" and (c.planting != "none" or c.rho > 0.0 or c.rho_sched):
+            raise ValueError("kv_tokens: keys of %s are not plain draws" % c.name)
+        tag = TAG_K if which == "k" else TAG_V
+        sid = stream_id(tag, layer, b, r)
+        out = np.empty((len(toks), c.head_dim), dtype=c.np_dtype)
+        for i, t in enumerate(np.asarray(toks, dtype=np.int64)):
+            lib().synth_normal(self.seed, sid, int(t) * c.head_dim, c.head_dim, 0.0, 1.0, c.kind,
+                               _ptr(out[i]))
         return out
 
     def v_row(self, layer: int, b: int, r: int) -> np.ndarray:
