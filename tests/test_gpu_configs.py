@@ -48,7 +48,15 @@ def _sample_rows(c, n, seed=0):
     return sorted(rows)
 
 
-def _check_exact_layer(w, layer, qd, kd, vd, rows, label):
+def _report(capsys, msg):
+    """A summary line that shows in the test log even when output is captured."""
+    say(msg)
+    if capsys is not None:
+        with capsys.disabled():
+            print("\n" + msg, flush=True)
+
+
+def _check_exact_layer(w, layer, qd, kd, vd, rows, label, capsys=None):
     """SPARSE layer with exact scoring: decode_layer == score+topk+sparse, and
     every sampled row against the oracle."""
     c = w.cfg
@@ -62,6 +70,7 @@ def _check_exact_layer(w, layer, qd, kd, vd, rows, label):
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2), "%s: layer entry point and single calls select differently" % label
     assert torch.equal(out, out2), "%s: layer entry point and single calls differ" % label
+    assert T.sa_check_indices(qd, kd, idx).tolist() == [0, 0], label
     idx_h = idx.cpu().numpy()
     out_h = out.cpu().numpy()
     q_h = O.widen(qd.cpu().view(torch.uint16).numpy() if c.dtype == "bf16" else qd.cpu().numpy())
@@ -86,7 +95,9 @@ def _check_exact_layer(w, layer, qd, kd, vd, rows, label):
         want = O.attend(qg, kf, vf, idx_h[b, r], scale)
         mx, _ = check_out(out_h[b, r * c.group:(r + 1) * c.group], want, c.dtype, "%s row %d,%d" % (label, b, r))
         worst = max(worst, mx)
-    say("%s: index sets %s over %d sampled rows; worst output error %.2e" % (label, counts, len(rows), worst))
+    _report(capsys, "%s: %d/%d checked rows exact or excused %s (of %d rows); worst output "
+                    "error %.2e" % (label, counts["exact"] + counts["excused"], len(rows), counts,
+                                    c.batch * c.n_kv_heads, worst))
     return idx, out
 
 
@@ -107,15 +118,16 @@ def _check_dense(w, layer, qd, kd, vd, rows, label):
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("seed", [0, 1])
-def test_llama32k_exact_topk_at_50x(seed):
+def test_llama32k_exact_topk_at_50x(seed, capsys):
     """Batch 16, 32/8 heads, d 128, bf16 32K cache, k = 655 (50x)."""
     w = S.Workload("llama32k", seed)
     c = w.cfg
     say("llama32k seed %d: generating %.2f GB" % (seed, c.kv_bytes() / 1e9))
     kd, vd = _upload_cache(w, "k", 0), _upload_cache(w, "v", 0)
     qd = to_dev(w.q(0))
-    rows = _sample_rows(c, 12, seed)
-    _check_exact_layer(w, 0, qd, kd, vd, rows, "llama32k/%d" % seed)
+    # seed 0: every (sequence, KV head) row against the oracle
+    rows = _sample_rows(c, c.batch * c.n_kv_heads if seed == 0 else 12, seed)
+    _check_exact_layer(w, 0, qd, kd, vd, rows, "llama32k/%d" % seed, capsys)
     _check_dense(w, 0, qd, kd, vd, rows[:4], "llama32k/%d" % seed)
     if seed == 0:
         _check_per_q_head(w, qd, kd, vd, rows[:4], "llama32k/%d per-q-head" % seed)
@@ -132,6 +144,7 @@ def _check_per_q_head(w, qd, kd, vd, rows, label):
     idx = torch.empty((c.batch, c.n_q_heads, c.k), dtype=torch.int32, device=dev())
     T.sa_decode_layer(args, T.SA_LAYER_SPARSE, idx, d_)
     scores = T.sa_score(qd, kd, T.SA_SCORE_EXACT_PER_Q_HEAD)
+    assert T.sa_check_indices(qd, kd, idx, T.SA_IDX_TOKEN_PER_Q_HEAD).tolist() == [0, 0]
     torch.cuda.synchronize()
     idx_h, out_h, s_gpu = idx.cpu().numpy(), out.cpu().numpy(), scores.cpu().numpy()
     for b in range(c.batch):
@@ -178,6 +191,7 @@ def test_block61k_block_selection_and_reuse():
         args, out, d_ = T.layer_args(qd, kd, vd, T.SA_SCORE_BLOCK_MINMAX, c.k, kmin=kmin, kmax=kmax,
                                      block_size=bs)
         T.sa_decode_layer(args, modes[layer], idx, d_)
+        assert T.sa_check_indices(qd, kd, idx, T.SA_IDX_BLOCK_PER_KV_HEAD, bs).tolist() == [0, 0]
         torch.cuda.synchronize()
         idx_h = idx.cpu().numpy()
         if layer == 0:
@@ -231,7 +245,7 @@ def test_block61k_block_selection_and_reuse():
 
 
 @pytest.mark.timeout(900)
-def test_batch128k_exact_topk_at_500x():
+def test_batch128k_exact_topk_at_500x(capsys):
     """Batch 128, 131072 tokens (68.7 GB of KV), k = 262 (500x): the top-262 is
     exactly the planted set; dense decode on the same cache."""
     w = S.Workload("batch128k", 0)
@@ -240,8 +254,8 @@ def test_batch128k_exact_topk_at_500x():
     kd = _upload_cache(w, "k", 0, chunk=4)
     vd = _upload_cache(w, "v", 0, chunk=4)
     qd = to_dev(w.q(0))
-    rows = _sample_rows(c, 6)
-    idx, _ = _check_exact_layer(w, 0, qd, kd, vd, rows, "batch128k")
+    rows = _sample_rows(c, 32)
+    idx, _ = _check_exact_layer(w, 0, qd, kd, vd, rows, "batch128k", capsys)
     idx_h = idx.cpu().numpy()
     for b in range(c.batch):
         for r in range(c.n_kv_heads):
@@ -250,7 +264,7 @@ def test_batch128k_exact_topk_at_500x():
 
 
 @pytest.mark.timeout(900)
-def test_indexer1m_mixed_plan():
+def test_indexer1m_mixed_plan(capsys):
     """One 1M-token sequence, 8 layers: dense at layers 0-1, then indexer
     top-2048 shared by the 8 KV heads at layers 2-7."""
     w = S.Workload("indexer1m", 0)
@@ -258,7 +272,6 @@ def test_indexer1m_mixed_plan():
     modes = [T.SA_LAYER_DENSE if m == "dense" else T.SA_LAYER_SPARSE for m in c.modes]
     T.sa_plan_validate(modes, list(c.src))
     scale = O.default_scale(c.head_dim)
-    heads = [0, c.n_kv_heads - 1]
     counts = {"exact": 0, "excused": 0}
     for layer in range(c.n_layers):
         say("indexer1m layer %d (%s): generating" % (layer, c.modes[layer]))
@@ -269,7 +282,7 @@ def test_indexer1m_mixed_plan():
         qd = to_dev(q_h)
         qf = O.widen(q_h)
         if modes[layer] == T.SA_LAYER_DENSE:
-            _check_dense(w, layer, qd, kd, vd, [(0, r) for r in heads], "indexer1m L%d" % layer)
+            _check_dense(w, layer, qd, kd, vd, [(0, 0), (0, c.n_kv_heads - 1)], "indexer1m L%d" % layer)
         else:
             qi_h, ki_h, wi_h = w.indexer_q(layer, q_h), w.indexer_k(layer, k_h), w.indexer_w(layer)
             qi, ki = to_dev(qi_h), to_dev(ki_h)
@@ -278,6 +291,7 @@ def test_indexer1m_mixed_plan():
             idx = torch.empty((c.batch, c.k), dtype=torch.int32, device=dev())
             T.sa_decode_layer(args, T.SA_LAYER_SPARSE, idx, d_)
             si = T.sa_score(qd, kd, T.SA_SCORE_INDEXER, q_idx=qi, k_idx=ki, idx_w=wi).cpu().numpy()[0]
+            assert T.sa_check_indices(qd, kd, idx, T.SA_IDX_TOKEN_SHARED).tolist() == [0, 0]
             torch.cuda.synchronize()
             idx_h = idx.cpu().numpy()[0]
             assert np.array_equal(idx_h, O.topk(si.astype(np.float64), c.k))
@@ -288,15 +302,18 @@ def test_indexer1m_mixed_plan():
             counts[v] += 1
             out_h = out.cpu().numpy()
             sel = np.sort(idx_h)
+            # every KV head on the first sparse layer, the first and last on the others
+            heads = range(c.n_kv_heads) if layer == 2 else [0, c.n_kv_heads - 1]
             for r in heads:
                 qg = qf[0, r * c.group:(r + 1) * c.group]
                 # only the selected rows are widened; attention over them is the same
-                want = O.attend(qg, O.widen(k_h[0, r][sel]), O.widen(w.v_row(layer, 0, r)[sel]),
+                want = O.attend(qg, O.widen(k_h[0, r][sel]), O.widen(w.kv_tokens("v", layer, 0, r, sel)),
                                 np.arange(c.k), scale)
                 check_out(out_h[0, r * c.group:(r + 1) * c.group], want, "bf16", "indexer1m L%d head %d" % (layer, r))
         del kd, vd, k_h
         torch.cuda.empty_cache()
-    say("indexer1m: sparse-layer index sets %s" % counts)
+    _report(capsys, "indexer1m: sparse-layer index sets %s over the 6 sparse layers; outputs "
+                    "of all 8 KV heads at layer 2, heads 0 and 7 elsewhere" % counts)
 
 
 def test_split_counts_agree():

@@ -73,6 +73,24 @@ def test_topk_long_rows(rows, n, k):
         assert np.array_equal(got[r], want), (rows, n, k, r)
 
 
+@pytest.mark.parametrize("n,k", [(150001, 2048), (1048576, 2048), (40000, 8192)])
+def test_topk_long_rows_ties_at_the_threshold(n, k):
+    """Multi-workgroup rows whose k-th largest score is shared by a few
+    hundred positions spread over every chunk: only the lowest positions of
+    the tie are kept, and the kept set is written in ascending order."""
+    say("topk long rows, ties at the threshold n=%d k=%d" % (n, k))
+    rng = np.random.default_rng(n + 3 * k)
+    vals = rng.standard_normal((2, n)).astype(np.float32)
+    for r in range(2):
+        v = np.sort(vals[r])[::-1][k - 100 + 50 * r]
+        vals[r, rng.choice(n, 400, replace=False)] = v
+    vals[1, rng.choice(n, 50, replace=False)] = -0.0   # signed zeros tie with +0.0
+    vals[1, rng.choice(n, 50, replace=False)] = 0.0
+    got = T.sa_topk(torch.from_numpy(vals).to(dev()), k).cpu().numpy()
+    for r in range(2):
+        assert np.array_equal(got[r], O.topk(vals[r].astype(np.float64), k)), (n, k, r)
+
+
 def test_topk_row_stride():
     say("topk row_stride")
     base = RNG.standard_normal((6, 3000)).astype(np.float32)

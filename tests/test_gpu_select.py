@@ -121,6 +121,11 @@ IDX_CASES = [
     (4, 2, 100, 8, 64, 10, True, "one part shorter than one iteration"),
     (2, 2, 32768, 4, 64, 12000, False, "fallback: candidates more than a quarter of the row"),
     (128, 8, 131072, 4, 64, 262, False, "batch128k shape at 500x: 1024 rows of sixteen 8192-token parts"),
+    # few long rows: the scoring launch counts the top-k's histogram
+    (1, 8, 1 << 20, 4, 64, 2048, True, "indexer1m shape: one 1M-token row, histogram counted"),
+    (2, 2, 200003, 4, 64, 8192, True, "counted histogram, ragged last chunk, k = 8192"),
+    (3, 1, 65536 + 77, 4, 64, 1, True, "counted histogram, k = 1"),
+    (2, 2, 40000, 16, 128, 700, True, "counted histogram, 16 heads of 128 dims"),
 ]
 
 
@@ -167,3 +172,33 @@ def test_select_indexer_against_oracle():
     s64 = [O.scores_indexer(qf[0, r], kf[0, r], wf[0, r]) for r in range(Hkv)]
     counts, fails = verdicts(s64, [got[0, r] for r in range(Hkv)], k)
     assert counts["failed"] == 0, fails
+
+
+def test_select_indexer_long_row_against_oracle():
+    """One 200003-token row (the multi-workgroup top-k with its histogram
+    counted by the indexer launch) against the oracle's fp64 indexer scores."""
+    say("select indexer long row vs oracle")
+    B, Hkv, N, H, Di, k = 1, 2, 200003, 4, 64, 2048
+    q, kc, qi, ki, w = _indexer_inputs(B, Hkv, N, H, Di, True, seed=23)
+    got = T.sa_select(q, kc, k, T.SA_SCORE_INDEXER, q_idx=qi, k_idx=ki, idx_w=w).cpu().numpy()
+    s64 = O.scores_indexer(qi.cpu().to(torch.float64).numpy()[0], ki.cpu().to(torch.float64).numpy()[0],
+                           w.cpu().to(torch.float64).numpy()[0])
+    counts, fails = verdicts([s64], [got[0]], k)
+    assert counts["failed"] == 0, fails
+
+
+@pytest.mark.parametrize("what", ["zero weights", "all dots negative"])
+def test_select_indexer_long_row_all_ties(what):
+    """Every score equal (0): the top-k is the first k positions; bin d1 then
+    holds the whole row, more than the candidate list takes, so the last
+    launch runs the row path."""
+    say("select indexer long row ties: %s" % what)
+    B, Hkv, N, H, Di, k = 2, 2, 300001, 4, 64, 3000
+    q, kc, qi, ki, w = _indexer_inputs(B, Hkv, N, H, Di, True, seed=29)
+    if what == "zero weights":
+        w.zero_()
+    else:
+        ki = ki.abs()
+        qi = -qi.abs()
+    got = T.sa_select(q, kc, k, T.SA_SCORE_INDEXER, q_idx=qi, k_idx=ki, idx_w=w)
+    assert torch.equal(got.cpu(), torch.arange(k, dtype=torch.int32).expand(B, k))

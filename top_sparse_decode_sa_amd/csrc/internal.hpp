@@ -39,13 +39,26 @@ hipError_t launch_block_summarize(const Cache& c, int32_t bs, const void* k, voi
                                   hipStream_t s);
 hipError_t launch_score_block(const Cache& c, int32_t bs, const void* q, const void* kmin,
                               const void* kmax, float* scores, hipStream_t s);
+// With hist, the launch also adds the 12-bit key histogram of row b's scores
+// into hist + b * hist_stride (the counted top-k below).
 hipError_t launch_score_indexer(int32_t B, int64_t N, int32_t H, int32_t Di, const void* q_idx,
-                                const void* k_idx, const float* w, float* scores, hipStream_t s);
+                                const void* k_idx, const float* w, float* scores, hipStream_t s,
+                                uint32_t* hist = nullptr, int64_t hist_stride = 0);
 
 // --------------------------------------------------------------- top-k
 size_t topk_workspace_bytes(int64_t n_rows, int64_t n, int32_t k);
 hipError_t launch_topk(const float* scores, int64_t n_rows, int64_t n, int64_t row_stride, int32_t k,
                        int32_t* idx, void* ws, hipStream_t s);
+// The multi-workgroup top-k of few long rows with the histogram counted by the
+// launch that writes the scores: when topk_counted(rows, n, k), run
+// launch_topk_counted_zero, then the scoring launch adding into
+// topk_counted_hist(ws) (row r at + r * stride words), then
+// launch_topk_counted; same result and workspace as launch_topk.
+bool topk_counted(int64_t n_rows, int64_t n, int32_t k);
+uint32_t* topk_counted_hist(void* ws, int64_t* stride_words);
+hipError_t launch_topk_counted_zero(void* ws, int64_t n_rows, hipStream_t s);
+hipError_t launch_topk_counted(const float* scores, int64_t n_rows, int64_t n, int64_t row_stride,
+                               int32_t k, int32_t* idx, void* ws, hipStream_t s);
 // Top-k of candidate rows (n <= 32768 values each, row stride cstride) whose
 // element i stands for position pos[i]: idx gets the k selected positions in
 // ascending candidate order.

@@ -31,6 +31,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kScoreTile = 1024;  // tokens per workgroup of the exact score
+constexpr int kIndexerHistTile = 4096;  // tokens per workgroup, indexer scores counting a histogram
 
 // ------------------------------------------------------------ exact score
 
@@ -280,14 +281,22 @@ struct IndexerArgs {
   int32_t H;
   int64_t N;
   float* scores;         // [B, N]
+  uint32_t* hist;        // optional: row b's 12-bit key histogram at hist + b * hist_stride
+  int64_t hist_stride;
 };
+
+constexpr int kKeyBins = 4096;  // histogram of the top 12 bits of score_key
 
 // One lane group of LPR = DI/8 lanes holds a token's indexer key (16 bytes
 // per lane); indexer_token (v_dot2_f32_bf16 on the packed bf16 values, DPP
 // head sums) gives its score.  (The unpack-and-fma form needed 2.5x the VALU
 // instructions per byte; matrix-core tiles need a 16-token by 16-byte load
 // pattern that streams worse.)
-template <int DI, int HP, int U>
+// With HIST the workgroup also counts the top 12 bits of its scores' keys in
+// LDS and adds the non-empty bins to the row's histogram (global atomics)
+// for the top-k that follows; its tile is then TILE tokens, larger than the
+// plain kernel's, so that fewer workgroups add into the same bins.
+template <int DI, int HP, int U, bool HIST, int TILE>
 __global__ __launch_bounds__(kThreads) void score_indexer_kernel(IndexerArgs a) {
   constexpr int LPR = DI * 2 / 16;
   constexpr int RPW = 64 / LPR;
@@ -302,14 +311,20 @@ __global__ __launch_bounds__(kThreads) void score_indexer_kernel(IndexerArgs a) 
   float wv[HP];
   load_indexer_queries<DI, HP>(a.q_idx, a.w, b, a.H, sl, qv, wv);
 
+  __shared__ uint32_t s_hist[HIST ? kKeyBins : 1];
+  if constexpr (HIST) {
+    for (int i = tid; i < kKeyBins; i += kThreads) s_hist[i] = 0u;
+    __syncthreads();
+  }
+
   const uint8_t* kbase = a.k_idx + (int64_t)b * a.N * DI * 2 + sl * 16;
   float* srow = a.scores + (int64_t)b * a.N;
   constexpr int per_wave_iter = RPW * U;
   constexpr int per_iter = 4 * per_wave_iter;
-  constexpr int kIters = kScoreTile / per_iter;
-  static_assert(kScoreTile % per_iter == 0, "whole iterations per tile");
-  const int64_t t_tile = (int64_t)blockIdx.x * kScoreTile;
-  const int64_t t_end = min(t_tile + (int64_t)kScoreTile, a.N);
+  constexpr int kIters = TILE / per_iter;
+  static_assert(TILE % per_iter == 0, "whole iterations per tile");
+  const int64_t t_tile = (int64_t)blockIdx.x * TILE;
+  const int64_t t_end = min(t_tile + (int64_t)TILE, a.N);
   // same load structure as the exact score: clamped, branch-free loads and a
   // ping-pong over two buffers on whole tiles
   auto load = [&](int64_t base, uint4 (&kw)[U], bool clamp) {
@@ -329,9 +344,12 @@ __global__ __launch_bounds__(kThreads) void score_indexer_kernel(IndexerArgs a) 
       if (sl == u) mine = sc;
     }
     const int64_t t = base + wave * per_wave_iter + sl * RPW + lg;
-    if (sl < U && (!check || t < t_end)) __builtin_nontemporal_store(mine, srow + t);
+    if (sl < U && (!check || t < t_end)) {
+      __builtin_nontemporal_store(mine, srow + t);
+      if constexpr (HIST) atomicAdd(&s_hist[score_key(mine) >> 20], 1u);
+    }
   };
-  if (t_end - t_tile == kScoreTile) {
+  if (t_end - t_tile == TILE) {
     uint4 kb[2][U];
     load(t_tile, kb[0], false);
 #pragma unroll
@@ -347,6 +365,12 @@ __global__ __launch_bounds__(kThreads) void score_indexer_kernel(IndexerArgs a) 
       reduce(base, kw, true);
     }
   }
+  if constexpr (HIST) {
+    __syncthreads();
+    uint32_t* g = a.hist + (int64_t)b * a.hist_stride;
+    for (int i = tid; i < kKeyBins; i += kThreads)
+      if (s_hist[i]) atomicAdd(&g[i], s_hist[i]);
+  }
 }
 
 template <int DI, int HP>
@@ -355,7 +379,14 @@ hipError_t launch_indexer_hp(const IndexerArgs& a, dim3 grid, hipStream_t s) {
   // tokens per lane group in flight: 8 (4 with 16 heads, whose queries fill
   // the registers)
   constexpr int U = HP >= 16 ? (LPR < 4 ? LPR : 4) : (LPR < 8 ? LPR : 8);
-  hipLaunchKernelGGL((score_indexer_kernel<DI, HP, U>), grid, dim3(kThreads), 0, s, a);
+  if (a.hist) {
+    const dim3 g((unsigned)((a.N + kIndexerHistTile - 1) / kIndexerHistTile), grid.y);
+    hipLaunchKernelGGL((score_indexer_kernel<DI, HP, U, true, kIndexerHistTile>), g, dim3(kThreads),
+                       0, s, a);
+  } else {
+    hipLaunchKernelGGL((score_indexer_kernel<DI, HP, U, false, kScoreTile>), grid, dim3(kThreads),
+                       0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -458,8 +489,11 @@ hipError_t launch_score_block(const Cache& c, int32_t bs, const void* q, const v
 }
 
 hipError_t launch_score_indexer(int32_t B, int64_t N, int32_t H, int32_t Di, const void* q_idx,
-                                const void* k_idx, const float* w, float* scores, hipStream_t s) {
+                                const void* k_idx, const float* w, float* scores, hipStream_t s,
+                                uint32_t* hist, int64_t hist_stride) {
   IndexerArgs a{};
+  a.hist = hist;
+  a.hist_stride = hist_stride;
   a.q_idx = static_cast<const uint8_t*>(q_idx);
   a.k_idx = static_cast<const uint8_t*>(k_idx);
   a.w = w;

@@ -364,6 +364,17 @@ hipError_t launch_select(const Cache& c, const SelectPlan& p, const void* q, con
   if (!p.fused) {
     float* scores = static_cast<float*>(ws);
     void* topk_ws = static_cast<uint8_t*>(ws) + align_up((size_t)rows * c.N * sizeof(float), 256);
+    if (ix && topk_counted(rows, c.N, kk)) {
+      // the indexer launch counts the top-k's histogram as it writes the scores
+      int64_t hs = 0;
+      uint32_t* hist = topk_counted_hist(topk_ws, &hs);
+      hipError_t e = launch_topk_counted_zero(topk_ws, rows, s);
+      if (e == hipSuccess)
+        e = launch_score_indexer((int32_t)rows, c.N, ix->H, ix->Di, ix->q_idx, ix->k_idx, ix->w,
+                                 scores, s, hist, hs);
+      if (e != hipSuccess) return e;
+      return launch_topk_counted(scores, rows, c.N, c.N, kk, idx, topk_ws, s);
+    }
     hipError_t e = ix ? launch_score_indexer((int32_t)rows, c.N, ix->H, ix->Di, ix->q_idx,
                                              ix->k_idx, ix->w, scores, s)
                       : launch_score_exact(c, q, k, scores, s);

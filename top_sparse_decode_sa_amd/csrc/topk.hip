@@ -30,12 +30,15 @@
 //
 // Multi-workgroup path, for few rows longer than kResident (a single 1M-token
 // sequence): (a) zero a per-row histogram; (b) workgroups of kMwChunk keys add
-// their 12-bit histograms with global atomics; (c) the same workgroups each
-// recompute d1 from the finished histogram and append the positions of keys
-// above bin d1 and the (key, position) candidates of bin d1 to per-row lists;
-// (d) one workgroup per row sorts the candidates by (key descending, position
-// ascending), keeps the first kleft, and sorts the k positions ascending.  If
-// the candidates overflow their list, (d) runs the row path on the row.
+// their 12-bit histograms with global atomics (or the scoring launch counts
+// the histogram as it writes the scores: launch_topk_counted); (c) the same
+// workgroups each recompute d1 from the finished histogram and append, in
+// position order within their chunk, the positions of keys above bin d1 and
+// the (key, position) candidates of bin d1 to per-row lists; (d) one
+// workgroup per row gathers both lists in chunk order, resolves the
+// candidates as in step 3 and writes each kept position to its slot (kept
+// positions of earlier chunks, then of its own chunk below it).  If the
+// candidates overflow their list, (d) runs the row path on the row.
 #include <algorithm>
 
 #include "common.hpp"
@@ -531,20 +534,36 @@ __global__ __launch_bounds__(kThreads) void topk_long_kernel(const float* __rest
 
 // ------------------------------------------------- multi-workgroup path
 
-// Per-row workspace.
+// Per-row workspace.  The two lists hold runs by chunk: a chunk's entries in
+// position order, the runs in whatever order the chunks arrived.
 struct MwRow {
-  uint32_t hist[kBins];            // 12-bit histogram of the row
-  uint32_t n_cand, T, need, fallback;
-  uint2 cand[kMwCand];             // (key, position) of bin d1, any order
-  uint32_t n_above[kMwMaxChunks];  // per chunk: keys above bin d1
-  uint32_t base_gt[kMwMaxChunks];  // per chunk: result keys above T before it
-  uint32_t base_eq[kMwMaxChunks];  // per chunk: keys equal to T before it
+  uint32_t hist[kBins];             // 12-bit histogram of the row's keys
+  uint32_t hist2[kBins];            // key bits 19..8 of the keys of bin d1
+  uint32_t n_above_all, n_cand_all;  // list fill counters
+  uint32_t sel_prefix, sel_kleft, sel_c1;  // bin d1 (as a key prefix), kleft, its count
+  uint32_t pad_[59];
+  uint32_t n_above[kMwMaxChunks];   // per chunk: keys above bin d1
+  uint32_t above_at[kMwMaxChunks];  // per chunk: start of its run in `above`
+  uint32_t n_cand[kMwMaxChunks];    // per chunk: keys of bin d1
+  uint32_t cand_at[kMwMaxChunks];   // per chunk: start of its run in `cand`
+  uint32_t above[kMwCand];          // positions of the keys above bin d1
+  uint2 cand[kMwCand];              // (key, position) of the keys of bin d1
 };
+
+constexpr int kMwPer = kMwChunk / kThreads;  // consecutive positions per thread
+static_assert(kMwChunk % (4 * kThreads) == 0, "whole float4 groups per thread");
+static_assert(kMwMaxChunks <= kThreads, "one chunk per thread in the final scan");
 
 __global__ __launch_bounds__(256) void topk_mw_zero(MwRow* rows) {
   MwRow& w = rows[blockIdx.x];
-  for (int i = threadIdx.x; i < kBins; i += 256) w.hist[i] = 0u;
-  if (threadIdx.x == 0) w.n_cand = 0u;
+  for (int i = threadIdx.x; i < kBins; i += 256) {
+    w.hist[i] = 0u;
+    w.hist2[i] = 0u;
+  }
+  if (threadIdx.x == 0) {
+    w.n_above_all = 0u;
+    w.n_cand_all = 0u;
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void topk_mw_hist(const float* __restrict__ scores, int64_t n,
@@ -573,109 +592,276 @@ __device__ __forceinline__ uint32_t mw_select(const MwRow& w, int32_t k, Shared&
   return select_digit(sh, 20, 12, prefix, mask, kleft);
 }
 
+// Every workgroup takes one chunk of kMwChunk positions, thread t the kMwPer
+// consecutive ones from kMwPer * t, so that a block scan of per-thread counts
+// lays the chunk's entries out in position order: the positions above bin d1
+// go to `above`, the (key, position) pairs of bin d1 to `cand` (unless they
+// overflow it: then the final launch runs the row path).
 __global__ __launch_bounds__(kThreads) void topk_mw_collect(const float* __restrict__ scores,
                                                             int64_t n, int64_t row_stride,
-                                                            int32_t k, MwRow* rows) {
+                                                            int32_t k, bool vec4, MwRow* rows) {
   __shared__ Shared sh;
   MwRow& w = rows[blockIdx.y];
+  const int ch = blockIdx.x;
+  const int64_t p0 = (int64_t)ch * kMwChunk + (int64_t)kMwPer * threadIdx.x;
+  const float* __restrict__ s = scores + (int64_t)blockIdx.y * row_stride;
+  // the chunk's scores are loaded first: they arrive while the histogram is
+  // read and scanned
+  float v[kMwPer];
+  if (vec4 && p0 + kMwPer <= n) {
+#pragma unroll
+    for (int e = 0; e < kMwPer; e += 4) {
+      const float4 f = *reinterpret_cast<const float4*>(s + p0 + e);
+      v[e] = f.x;
+      v[e + 1] = f.y;
+      v[e + 2] = f.z;
+      v[e + 3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kMwPer; ++e) v[e] = p0 + e < n ? s[p0 + e] : 0.0f;
+  }
   uint32_t prefix, mask, kleft;
   const uint32_t c1 = mw_select(w, k, sh, prefix, mask, kleft);
   const uint32_t d1 = prefix >> 20;
-  const int64_t c0 = (int64_t)blockIdx.x * kMwChunk;
-  const float* s = scores + (int64_t)blockIdx.y * row_stride;
-  constexpr int PER = kMwChunk / kThreads;
-  uint32_t key[PER];
-  uint32_t n_above = 0, n_cand = 0;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int64_t i = c0 + (int64_t)e * kThreads + threadIdx.x;
-    const bool valid = i < n;
-    key[e] = valid ? score_key(s[i]) : 0u;
-    n_above += (valid && (key[e] >> 20) > d1) ? 1u : 0u;
-    n_cand += (valid && (key[e] >> 20) == d1) ? 1u : 0u;
+  const bool keep = c1 <= (uint32_t)kMwCand;
+  if (ch == 0 && threadIdx.x == 0) {
+    w.sel_prefix = prefix;
+    w.sel_kleft = kleft;
+    w.sel_c1 = c1;
   }
-  uint32_t total;
-  const uint32_t excl = block_exclusive_scan((n_above << 16) | n_cand, sh, total);
+  uint32_t key[kMwPer];
+#pragma unroll
+  for (int e = 0; e < kMwPer; ++e) key[e] = score_key(v[e]);
+  uint32_t na = 0, nc = 0;
+#pragma unroll
+  for (int e = 0; e < kMwPer; ++e) {
+    const bool valid = p0 + e < n;
+    na += (valid && (key[e] >> 20) > d1) ? 1u : 0u;
+    nc += (valid && (key[e] >> 20) == d1) ? 1u : 0u;
+  }
+  uint32_t total;  // both halves stay below 2^16 (at most kMwChunk each)
+  const uint32_t excl = block_exclusive_scan((na << 16) | nc, sh, total);
   if (threadIdx.x == 0) {
-    w.n_above[blockIdx.x] = total >> 16;
-    sh.base = 0;
-    if (c1 <= (uint32_t)kMwCand && (total & 0xffffu)) sh.base = atomicAdd(&w.n_cand, total & 0xffffu);
+    const uint32_t ta = total >> 16, tc = keep ? (total & 0xffffu) : 0u;
+    const uint32_t at_a = ta ? atomicAdd(&w.n_above_all, ta) : 0u;
+    const uint32_t at_c = tc ? atomicAdd(&w.n_cand_all, tc) : 0u;
+    w.n_above[ch] = ta;
+    w.above_at[ch] = at_a;
+    w.n_cand[ch] = tc;
+    w.cand_at[ch] = at_c;
+    sh.base = at_a;
+    sh.cgt = at_c;
   }
   __syncthreads();
-  if (c1 > (uint32_t)kMwCand) return;  // the resolving kernel runs the row path
-  uint32_t pc = sh.base + (excl & 0xffffu);
+  uint32_t pa = sh.base + (excl >> 16), pc = sh.cgt + (excl & 0xffffu);
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int64_t i = c0 + (int64_t)e * kThreads + threadIdx.x;
-    if (i < n && (key[e] >> 20) == d1) w.cand[pc++] = make_uint2(key[e], (uint32_t)i);
+  for (int e = 0; e < kMwPer; ++e) {
+    if (p0 + e >= n) continue;
+    const uint32_t d = key[e] >> 20;
+    if (d > d1) {
+      w.above[pa++] = (uint32_t)(p0 + e);
+    } else if (keep && d == d1) {
+      w.cand[pc++] = make_uint2(key[e], (uint32_t)(p0 + e));
+      atomicAdd(&w.hist2[(key[e] >> 8) & (kBins - 1)], 1u);
+    }
   }
 }
 
-__global__ __launch_bounds__(kThreads) void topk_mw_resolve(const float* __restrict__ scores,
-                                                            int64_t n, int64_t row_stride,
-                                                            int32_t k, bool vec4, MwRow* rows,
-                                                            int32_t* __restrict__ idx_out) {
+// First index in [lo, hi) whose value is >= x (a[] ascending).
+__device__ __forceinline__ uint32_t lower_bound_u32(const uint32_t* a, uint32_t lo, uint32_t hi,
+                                                    uint32_t x) {
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// LDS of the final launch: the row path's buffers, or the lists in chunk order.
+constexpr int kMwArena = kTile + 2 * kCandGlob;
+static_assert(4 * (kMwMaxChunks + 1) + kMwCand + 2 * (kMwCand + 32) + 2 * (kRankCap + 32) <= kMwArena,
+              "the chunk tables, both lists and the sub-bin list fit the row path's LDS");
+
+// One workgroup per row: the lists are gathered into LDS in chunk order (so
+// both are in position order), the candidates resolved into T and `need`,
+// each candidate marked kept or not, and every kept position written to its
+// output slot = (kept positions of earlier chunks) + (earlier ones of its own
+// list in its chunk) + (those of the other list in its chunk below it, by
+// binary search).
+__global__ __launch_bounds__(kThreads) void topk_mw_finish(const float* __restrict__ scores,
+                                                           int64_t n, int64_t row_stride, int32_t k,
+                                                           bool vec4, MwRow* rows,
+                                                           int32_t* __restrict__ idx_out) {
   __shared__ Shared sh;
-  __shared__ __align__(16) uint32_t buf[kTile + 2 * kCandGlob];
-  __shared__ uint32_t s_gt[kMwMaxChunks], s_eq[kMwMaxChunks];
+  __shared__ __align__(16) uint32_t arena[kMwArena];
   MwRow& w = rows[blockIdx.x];
-  uint32_t prefix, mask, kleft;
-  const uint32_t c1 = mw_select(w, k, sh, prefix, mask, kleft);
+  int32_t* __restrict__ out = idx_out + (int64_t)blockIdx.x * k;
+  const int tid = threadIdx.x;
+  const int nch = (int)((n + kMwChunk - 1) / kMwChunk);
+  // the chunk table is loaded first: it arrives while the histogram is read
+  // and scanned
+  // the selection scalars, the chunk table and the second-level histogram
+  // are all loaded at once
+  uint32_t na = 0, nc = 0, at_a = 0, at_c = 0;
+  if (tid < nch) {
+    na = w.n_above[tid];
+    nc = w.n_cand[tid];
+    at_a = w.above_at[tid];
+    at_c = w.cand_at[tid];
+  }
+  const uint32_t prefix = w.sel_prefix, kleft = w.sel_kleft, c1 = w.sel_c1;
+  for (int b = tid; b < kBins; b += kThreads) sh.hist[b] = w.hist2[b];
   if (c1 > (uint32_t)kMwCand) {
-    if (threadIdx.x == 0) w.fallback = 1u;
-    topk_row_long(scores + (int64_t)blockIdx.x * row_stride, n, k,
-                  idx_out + (int64_t)blockIdx.x * k, vec4, sh, buf);
+    topk_row_long(scores + (int64_t)blockIdx.x * row_stride, n, k, out, vec4, sh, arena);
     return;
   }
-  uint2* cand = reinterpret_cast<uint2*>(buf + kTile);
-  for (uint32_t c = threadIdx.x; c < c1; c += kThreads) cand[c] = w.cand[c];
-  const int n_chunks = (int)((n + kMwChunk - 1) / kMwChunk);
-  for (int c = threadIdx.x; c < n_chunks; c += kThreads) {
-    s_gt[c] = w.n_above[c];
-    s_eq[c] = 0u;
+  uint32_t* a_off = arena;                              // [nch + 1]
+  uint32_t* c_off = arena + (kMwMaxChunks + 1);         // [nch + 1]
+  uint32_t* a_at = arena + 2 * (kMwMaxChunks + 1);      // [nch]
+  uint32_t* c_at = arena + 3 * (kMwMaxChunks + 1);      // [nch]
+  uint32_t* above = arena + 4 * (kMwMaxChunks + 1);     // [k - kleft]
+  uint2* cand = reinterpret_cast<uint2*>(above + kMwCand);  // [c1, padded]
+  const uint32_t v = (na << 16) | nc;
+  if (tid < nch) {
+    a_at[tid] = at_a;
+    c_at[tid] = at_c;
   }
-  __syncthreads();
-  uint32_t T, need;
-  resolve(cand, c1, kleft, prefix, mask, sh, T, need);
-  for (uint32_t c = threadIdx.x; c < c1; c += kThreads) {
-    const uint2 e = cand[c];
-    const int ch = (int)(e.y / kMwChunk);
-    if (e.x > T) atomicAdd(&s_gt[ch], 1u);
-    else if (e.x == T) atomicAdd(&s_eq[ch], 1u);
-  }
-  __syncthreads();
-  // per-chunk counts (each < 2^14) to exclusive prefix sums
-  const int c = threadIdx.x;
-  const uint32_t v = c < n_chunks ? (s_gt[c] << 16) | s_eq[c] : 0u;
   uint32_t total;
   const uint32_t excl = block_exclusive_scan(v, sh, total);
-  if (c < n_chunks) {
-    w.base_gt[c] = excl >> 16;
-    w.base_eq[c] = excl & 0xffffu;
+  if (tid < nch) {
+    a_off[tid] = excl >> 16;
+    c_off[tid] = excl & 0xffffu;
   }
-  if (c == 0) {
-    w.T = T;
-    w.need = need;
-    w.fallback = 0u;
+  if (tid == 0) {
+    a_off[nch] = total >> 16;
+    c_off[nch] = total & 0xffffu;
   }
-}
-
-__global__ __launch_bounds__(kThreads) void topk_mw_write(const float* __restrict__ scores,
-                                                          int64_t n, int64_t row_stride,
-                                                          int32_t k, bool vec4, MwRow* rows,
-                                                          int32_t* __restrict__ idx_out) {
-  __shared__ Shared sh;
-  __shared__ __align__(16) uint32_t keys[kMwChunk];
-  const MwRow& w = rows[blockIdx.y];
-  if (w.fallback) return;  // the resolving kernel wrote this row
-  const int64_t c0 = (int64_t)blockIdx.x * kMwChunk;
-  const int nv = (int)std::min<int64_t>(kMwChunk, n - c0);
-  load_tile<kMwChunk / kThreads>(scores + (int64_t)blockIdx.y * row_stride + c0, nv, vec4, keys,
-                                 nullptr);
   __syncthreads();
-  uint32_t run_gt = w.base_gt[blockIdx.x], run_eq = w.base_eq[blockIdx.x];
-  write_tile<kMwChunk / kThreads>(keys, c0, nv, w.T, w.need, run_gt, run_eq,
-                                  idx_out + (int64_t)blockIdx.y * k, (uint32_t)k, sh);
+  const uint32_t n_above = a_off[nch];  // = k - kleft
+  // gather both lists in chunk order: thread t takes entries [kG t, kG t +
+  // kG) of each, finds the chunk of its first entry by binary search and
+  // walks forward; every load is in flight before any is stored
+  constexpr int kG = kMwCand / kThreads;
+  uint32_t src_a[kG], src_c[kG];
+  {
+    const uint32_t i0 = (uint32_t)tid * kG;
+    uint32_t ca = i0 < n_above ? lower_bound_u32(a_off, 0, (uint32_t)nch + 1, i0 + 1) - 1 : 0u;
+    uint32_t cc = i0 < c1 ? lower_bound_u32(c_off, 0, (uint32_t)nch + 1, i0 + 1) - 1 : 0u;
+#pragma unroll
+    for (int u = 0; u < kG; ++u) {
+      const uint32_t i = i0 + u;
+      src_a[u] = src_c[u] = 0u;
+      if (i < n_above) {
+        while (a_off[ca + 1] <= i) ++ca;
+        src_a[u] = a_at[ca] + (i - a_off[ca]);
+      }
+      if (i < c1) {
+        while (c_off[cc + 1] <= i) ++cc;
+        src_c[u] = c_at[cc] + (i - c_off[cc]);
+      }
+    }
+  }
+  uint32_t ga[kG];
+  uint2 gc[kG];
+#pragma unroll
+  for (int u = 0; u < kG; ++u) {
+    ga[u] = w.above[src_a[u]];
+    gc[u] = w.cand[src_c[u]];
+  }
+#pragma unroll
+  for (int u = 0; u < kG; ++u) {
+    const uint32_t i = (uint32_t)tid * kG + u;
+    if (i < n_above) above[i] = ga[u];
+    if (i < c1) cand[i] = gc[u];
+  }
+  // the second digit (key bits 19..8) from the collected histogram of bin
+  // d1; its keys (the sub-bin) are copied to `sub` and resolved there
+  uint32_t above2, c2;
+  const uint32_t d2 = wave_select_bin<kBins>(sh.hist, kleft, &above2, &c2);
+  __syncthreads();  // every wave has read sh.hist before resolve may reuse it
+  const uint32_t kleft2 = kleft - above2;
+  const uint32_t prefix2 = prefix | (d2 << 8), mask2 = 0xffffff00u;
+  uint2* sub = cand + (kMwCand + 32);  // [c2 <= kRankCap, padded]
+  const bool small = c2 <= (uint32_t)kRankCap;
+  uint32_t T, need;
+  if (small) {
+    if (tid == 0) sh.count = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kG; ++u) {
+      const uint32_t i = (uint32_t)tid * kG + u;
+      if (i < c1 && (gc[u].x & mask2) == prefix2) sub[atomicAdd(&sh.count, 1u)] = gc[u];
+    }
+    __syncthreads();
+    resolve(sub, c2, kleft2, prefix2, mask2, sh, T, need);
+  } else {
+    // many keys share the second digit: resolve bin d1 as a whole
+    resolve(cand, c1, kleft, prefix, 0xfff00000u, sh, T, need);
+  }
+  // keep: key above T, or equal to T among the first `need` such in
+  // position order; cand[j].x becomes (kept candidates before j) << 1 | kept
+  constexpr uint32_t kPerC = (kMwCand + kThreads - 1) / kThreads;
+  const uint32_t j0 = tid * kPerC, j1 = std::min<uint32_t>(j0 + kPerC, c1);
+  uint32_t flags = 0, nk = 0;
+  if (small) {
+    // few keys share T's top 24 bits: a tied key's rank among them by a scan of `sub`
+    for (uint32_t j = j0; j < j1; ++j) {
+      const uint2 e = cand[j];
+      bool kept = e.x > T;
+      if (e.x == T) {
+        uint32_t r = 0;
+        for (uint32_t m = 0; m < c2; ++m) r += (sub[m].x == T && sub[m].y < e.y) ? 1u : 0u;
+        kept = r < need;
+      }
+      flags |= (kept ? 1u : 0u) << (j - j0);
+      nk += kept ? 1u : 0u;
+    }
+  } else {
+    uint32_t ne = 0;
+    for (uint32_t j = j0; j < j1; ++j) ne += cand[j].x == T ? 1u : 0u;
+    uint32_t eq_before = block_exclusive_scan(ne, sh, total);
+    for (uint32_t j = j0; j < j1; ++j) {
+      const uint32_t key = cand[j].x;
+      const bool kept = key > T || (key == T && eq_before++ < need);
+      flags |= (kept ? 1u : 0u) << (j - j0);
+      nk += kept ? 1u : 0u;
+    }
+  }
+  uint32_t kept_before = block_exclusive_scan(nk, sh, total);
+  for (uint32_t j = j0; j < j1; ++j) {
+    const uint32_t kept = (flags >> (j - j0)) & 1u;
+    cand[j].x = (kept_before << 1) | kept;
+    kept_before += kept;
+  }
+  __syncthreads();
+  auto kept_upto = [&](uint32_t j) { return j < c1 ? cand[j].x >> 1 : kleft; };
+  auto cand_pos_lb = [&](uint32_t lo, uint32_t hi, uint32_t x) {
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (cand[mid].y < x) lo = mid + 1;
+      else hi = mid;
+    }
+    return lo;
+  };
+  for (uint32_t i = tid; i < n_above; i += kThreads) {
+    const uint32_t p = above[i];
+    const uint32_t c = p / (uint32_t)kMwChunk;
+    const uint32_t before = a_off[c] + kept_upto(c_off[c]);
+    const uint32_t below = kept_upto(cand_pos_lb(c_off[c], c_off[c + 1], p)) - kept_upto(c_off[c]);
+    const uint32_t slot = before + (i - a_off[c]) + below;
+    if (slot < (uint32_t)k) out[slot] = (int32_t)p;
+  }
+  for (uint32_t j = tid; j < c1; j += kThreads) {
+    const uint2 e = cand[j];
+    if (!(e.x & 1u)) continue;
+    const uint32_t c = e.y / (uint32_t)kMwChunk;
+    const uint32_t before = a_off[c] + kept_upto(c_off[c]);
+    const uint32_t below = lower_bound_u32(above, a_off[c], a_off[c + 1], e.y) - a_off[c];
+    const uint32_t slot = before + ((e.x >> 1) - kept_upto(c_off[c])) + below;
+    if (slot < (uint32_t)k) out[slot] = (int32_t)e.y;
+  }
 }
 
 bool use_mw(int64_t n_rows, int64_t n, int32_t k) {
@@ -744,6 +930,30 @@ size_t topk_workspace_bytes(int64_t n_rows, int64_t n, int32_t k) {
   return use_mw(n_rows, n, k) ? (size_t)n_rows * sizeof(MwRow) : 0;
 }
 
+bool topk_counted(int64_t n_rows, int64_t n, int32_t k) { return use_mw(n_rows, n, k); }
+
+uint32_t* topk_counted_hist(void* ws, int64_t* stride_words) {
+  *stride_words = (int64_t)(sizeof(MwRow) / sizeof(uint32_t));
+  return static_cast<MwRow*>(ws)->hist;
+}
+
+hipError_t launch_topk_counted_zero(void* ws, int64_t n_rows, hipStream_t s) {
+  hipLaunchKernelGGL(topk_mw_zero, dim3((unsigned)n_rows), dim3(256), 0, s, static_cast<MwRow*>(ws));
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_counted(const float* scores, int64_t n_rows, int64_t n, int64_t row_stride,
+                               int32_t k, int32_t* idx, void* ws, hipStream_t s) {
+  const bool vec4 = (reinterpret_cast<uintptr_t>(scores) % 16 == 0) && (row_stride % 4 == 0);
+  MwRow* rows = static_cast<MwRow*>(ws);
+  const dim3 grid((unsigned)((n + kMwChunk - 1) / kMwChunk), (unsigned)n_rows);
+  hipLaunchKernelGGL(topk_mw_collect, grid, dim3(kThreads), 0, s, scores, n, row_stride, k, vec4,
+                     rows);
+  hipLaunchKernelGGL(topk_mw_finish, dim3((unsigned)n_rows), dim3(kThreads), 0, s, scores, n,
+                     row_stride, k, vec4, rows, idx);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk_merge(const float* cand_val, const int32_t* cand_pos, int64_t n_rows,
                              int64_t n, int64_t cstride, int32_t k, int32_t* idx, hipStream_t s) {
   const bool vec4 = (reinterpret_cast<uintptr_t>(cand_val) % 16 == 0) && (cstride % 4 == 0);
@@ -784,11 +994,7 @@ hipError_t launch_topk(const float* scores, int64_t n_rows, int64_t n, int64_t r
     const dim3 grid((unsigned)((n + kMwChunk - 1) / kMwChunk), (unsigned)n_rows);
     hipLaunchKernelGGL(topk_mw_zero, dim3((unsigned)n_rows), dim3(256), 0, s, rows);
     hipLaunchKernelGGL(topk_mw_hist, grid, dim3(kThreads), 0, s, scores, n, row_stride, vec4, rows);
-    hipLaunchKernelGGL(topk_mw_collect, grid, dim3(kThreads), 0, s, scores, n, row_stride, k, rows);
-    hipLaunchKernelGGL(topk_mw_resolve, dim3((unsigned)n_rows), dim3(kThreads), 0, s, scores, n,
-                       row_stride, k, vec4, rows, idx);
-    hipLaunchKernelGGL(topk_mw_write, grid, dim3(kThreads), 0, s, scores, n, row_stride, k, vec4,
-                       rows, idx);
+    return launch_topk_counted(scores, n_rows, n, row_stride, k, idx, ws, s);
   } else {
     hipLaunchKernelGGL(topk_long_kernel, dim3((unsigned)n_rows), dim3(kThreads), 0, s, scores, n,
                        row_stride, k, idx, vec4);
