@@ -298,7 +298,8 @@ def test_check_indices_counts_bad_rows(kind, n_idx):
     assert got[0] >= 1 and (n_idx < 3 or got[1] >= 1)
 
 
-@pytest.mark.parametrize("N,bs,n_blk", [(1000, 128, 3), (61440, 128, 24), (300, 16, 19)])
+@pytest.mark.parametrize("N,bs,n_blk", [(1000, 128, 3), (61440, 128, 24), (300, 16, 19),
+                                         (8192, 128, 64), (4096, 16, 256), (2048, 128, 16)])
 def test_sparse_blocks_with_partial_last_block(N, bs, n_blk):
     say("sparse blocks", N, bs, n_blk)
     B, Hkv, G, d = 2, 2, 4, 128
@@ -313,6 +314,38 @@ def test_sparse_blocks_with_partial_last_block(N, bs, n_blk):
     sets = [[O.block_tokens(idx[b, r], bs, N) for r in range(Hkv)] for b in range(B)]
     want = _oracle_out(_f64(q), _f64(k), _f64(v), sets, G, O.default_scale(d))
     check_out(out, want, "bf16", "sparse blocks")
+
+
+@pytest.mark.parametrize("dtype,d,G,B,Hkv,N,bs,k,zero_q", [
+    ("bf16", 128, 4, 2, 2, 61440, 128, 24, False),   # block61k rows
+    ("bf16", 128, 4, 1, 2, 1000, 128, 3, False),     # partial last block
+    ("f32", 64, 4, 2, 2, 5000, 16, 40, False),
+    ("bf16", 64, 2, 1, 1, 4096 * 128, 128, 100, False),  # 4096 blocks: the fused limit
+    ("bf16", 128, 4, 1, 1, 4097 * 16, 16, 50, False),    # one block more: score, then top-k
+    ("bf16", 128, 4, 2, 2, 8192, 128, 10, True),     # every score 0: the first k blocks
+])
+def test_block_layer_selection(dtype, d, G, B, Hkv, N, bs, k, zero_q):
+    """A SPARSE layer on block scores selects, in one launch where the row's
+    blocks fit it, the same blocks as sa_score followed by sa_topk, and
+    attends over them as sa_sparse_decode does."""
+    say("block layer selection", dtype, d, G, B, Hkv, N, bs, k, zero_q)
+    q, kc, vc = _rand_cache(B, Hkv * G, Hkv, N, d, dtype, 43)
+    if zero_q:
+        q.zero_()
+    qd, kd, vd = q.to(dev()), kc.to(dev()), vc.to(dev())
+    kmin, kmax = T.sa_block_summarize(kd, bs, q_like=qd)
+    args, out, d_ = T.layer_args(qd, kd, vd, T.SA_SCORE_BLOCK_MINMAX, k, kmin=kmin, kmax=kmax,
+                                 block_size=bs)
+    idx = torch.full((B, Hkv, k), -1, dtype=torch.int32, device=dev())
+    T.sa_decode_layer(args, T.SA_LAYER_SPARSE, idx, d_)
+    want = T.sa_topk(T.sa_score(qd, kd, T.SA_SCORE_BLOCK_MINMAX, kmin=kmin, kmax=kmax,
+                                block_size=bs), k)
+    ref = T.sa_sparse_decode(qd, kd, vd, want, T.SA_IDX_BLOCK_PER_KV_HEAD, block_size=bs)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, want)
+    assert torch.equal(out, ref)
+    if zero_q:
+        assert torch.equal(idx.cpu(), torch.arange(k, dtype=torch.int32).expand(B, Hkv, k))
 
 
 @pytest.mark.parametrize("dtype,d,G,N", [("f32", 64, 4, 1024), ("bf16", 128, 4, 20000),

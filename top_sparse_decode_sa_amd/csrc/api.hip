@@ -683,6 +683,13 @@ sa_status sa_decode_layer(const sa_layer_args* a, sa_layer_mode mode, int32_t* i
                          "sa_decode_layer selection launch")) != SA_OK)
       return st;
     if (attended) return SA_OK;
+  } else if (mode == SA_LAYER_SPARSE && a->score_kind == SA_SCORE_BLOCK_MINMAX &&
+             select_block_fits(c, bs)) {
+    // block scores and their top-k in one launch
+    if ((st = hip_status(launch_select_block(c, bs, a->q, a->aux.kmin, a->aux.kmax, a->k, idx,
+                                             stream),
+                         "sa_decode_layer block selection launch")) != SA_OK)
+      return st;
   } else if (mode == SA_LAYER_SPARSE) {
     if ((st = do_score(c, a->score_kind, a->q, a->k_cache, &a->aux, scores, stream)) != SA_OK)
       return st;

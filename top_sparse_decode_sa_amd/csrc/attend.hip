@@ -1265,6 +1265,8 @@ hipError_t dispatch_pairs_mode(int mode, dim3 grid, dim3 block, const AttendArgs
                                hipStream_t s) {
   if (mode == kIdxTokenShared)
     hipLaunchKernelGGL((attend_pairs_kernel<G, kIdxTokenShared, PAIRS, VH>), grid, block, 0, s, a);
+  else if (mode == kIdxBlockPerHead)
+    hipLaunchKernelGGL((attend_pairs_kernel<G, kIdxBlockPerHead, PAIRS, VH>), grid, block, 0, s, a);
   else
     hipLaunchKernelGGL((attend_pairs_kernel<G, kIdxTokenPerHead, PAIRS, VH>), grid, block, 0, s, a);
   return hipGetLastError();
@@ -1314,8 +1316,11 @@ AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs) {
   const int64_t rows = (int64_t)c.B * c.Hkv;
   int64_t chunk;
   p.pairs = 0;
-  if (use_wave_kernel(c) && (mode == kIdxTokenPerHead || mode == kIdxTokenShared) &&
-      row_span_bytes(c) < (int64_t(1) << 32)) {
+  // (selected blocks: only when every block is whole, as the pair kernel
+  // masks slots, not tokens past the end)
+  const bool pair_mode = mode == kIdxTokenPerHead || mode == kIdxTokenShared ||
+                         (mode == kIdxBlockPerHead && c.N % bs == 0);
+  if (use_wave_kernel(c) && pair_mode && row_span_bytes(c) < (int64_t(1) << 32)) {
     // Selected tokens: waves of one or two pairs of 16-slot tiles.  At least
     // 128 rows (half the chip's CUs at one workgroup each) and at most 24
     // pairs: one workgroup takes a whole row, so no split partials and no

@@ -39,6 +39,12 @@ hipError_t launch_block_summarize(const Cache& c, int32_t bs, const void* k, voi
                                   hipStream_t s);
 hipError_t launch_score_block(const Cache& c, int32_t bs, const void* q, const void* kmin,
                               const void* kmax, float* scores, hipStream_t s);
+// Block scores and their top-k in one launch (one workgroup per row), for
+// rows of at most 4096 blocks (select_block_fits): idx [rows, k] ascending,
+// the same list as launch_score_block followed by launch_topk.
+bool select_block_fits(const Cache& c, int32_t bs);
+hipError_t launch_select_block(const Cache& c, int32_t bs, const void* q, const void* kmin,
+                               const void* kmax, int32_t k, int32_t* idx, hipStream_t s);
 // With hist, the launch also adds the 12-bit key histogram of row b's scores
 // into hist + b * hist_stride (the counted top-k below).
 hipError_t launch_score_indexer(int32_t B, int64_t N, int32_t H, int32_t Di, const void* q_idx,

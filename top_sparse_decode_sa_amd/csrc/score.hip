@@ -25,6 +25,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "topk_core.hpp"
 
 namespace sa {
 namespace {
@@ -272,6 +273,87 @@ __global__ __launch_bounds__(kThreads) void score_block_kernel(BlockArgs a) {
   }
 }
 
+// ------------------------------------------------ block score + top-k
+// Block selection of a whole row in one workgroup: the row's block scores
+// (the same arithmetic as score_block_kernel, so the same fp32 values) from
+// its per-block key summaries, kSelBlkU passes of blocks with every summary
+// load of a pass group in flight, kept in LDS; then the register-resident
+// top-k of the row (reg_row_topk) writes the k best block ids, ascending --
+// one launch instead of a score launch and a top-k launch.
+constexpr int kSelBlkThreads = 1024;
+constexpr int kSelBlkMax = 4 * kSelBlkThreads;  // blocks per row at most
+constexpr int kSelBlkU = 4;
+
+template <typename KT, int D>
+__global__ __launch_bounds__(kSelBlkThreads) void select_block_kernel(BlockArgs a, int32_t k,
+                                                                     int32_t* __restrict__ idx) {
+  constexpr int EB = Elt<KT>::kBytes;
+  constexpr int E = Elt<KT>::kPer16B;
+  constexpr int LPR = D * EB / 16;
+  constexpr int NG = kSelBlkThreads / LPR;  // blocks per pass
+  __shared__ float s_sc[kSelBlkMax];
+  __shared__ SharedT<kSelBlkThreads> sh;
+  __shared__ __align__(16) uint2 cand[kRankMax + 8];
+  __shared__ uint32_t s_wave[kSelBlkThreads / 64];
+  const int tid = threadIdx.x;
+  const int grp = tid / LPR;
+  const int sl = tid % LPR;
+  const int row = blockIdx.x;
+  const int b = row / a.Hkv;
+  const int r = row % a.Hkv;
+  auto off_of = [&](int j) { return (((int64_t)row * a.nb + j) * D) * EB + sl * 16; };
+
+  uint4 lmn[kSelBlkU], lmx[kSelBlkU];
+#pragma unroll
+  for (int u = 0; u < kSelBlkU; ++u) {
+    const int j = u * NG + grp;
+    lmn[u] = j < a.nb ? ld16(a.kmin + off_of(j)) : make_uint4(0u, 0u, 0u, 0u);
+    lmx[u] = j < a.nb ? ld16(a.kmax + off_of(j)) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  float qp[E], qn[E];
+  float qv[8][E];
+  load_q_group<E, D>(a.q, a.q_dtype, (int64_t)b * a.Hq + (int64_t)r * a.G, a.G, sl * E, qv);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    float p = 0.0f, n = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const float v = g < a.G ? qv[g][e] : 0.0f;
+      p += fmaxf(v, 0.0f);
+      n += fminf(v, 0.0f);
+    }
+    qp[e] = p;
+    qn[e] = n;
+  }
+  for (int j0 = 0; j0 < a.nb; j0 += kSelBlkU * NG) {
+#pragma unroll
+    for (int u = 0; u < kSelBlkU; ++u) {
+      const int j = j0 + u * NG + grp;
+      float mn[E], mx[E];
+      unpack16<KT>(lmn[u], mn);
+      unpack16<KT>(lmx[u], mx);
+      const int jn = j + kSelBlkU * NG;  // the next group's block, loaded now
+      if (jn < a.nb) {
+        lmn[u] = ld16(a.kmin + off_of(jn));
+        lmx[u] = ld16(a.kmax + off_of(jn));
+      }
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc = fmaf(qp[e], mx[e], fmaf(qn[e], mn[e], acc));
+      acc = group_sum<LPR>(acc);
+      if (sl == 0 && j < a.nb) s_sc[j] = acc;
+    }
+  }
+  __syncthreads();
+  int32_t* __restrict__ out = idx + (int64_t)row * k;
+  auto load = [&](int p0, float (&v)[1][4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[0][e] = p0 + e < a.nb ? s_sc[p0 + e] : 0.0f;
+  };
+  auto emit = [&](uint32_t slot, int32_t p) { out[slot] = p; };
+  reg_row_topk<kSelBlkThreads, 1, false>(load, a.nb, k, emit, sh, cand, s_wave);
+}
+
 // --------------------------------------------------------------- indexer
 
 struct IndexerArgs {
@@ -484,6 +566,37 @@ hipError_t launch_score_block(const Cache& c, int32_t bs, const void* q, const v
       hipLaunchKernelGGL((score_block_kernel<float, 64>), grid, dim3(kThreads), 0, s, a);
     else
       hipLaunchKernelGGL((score_block_kernel<float, 128>), grid, dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+bool select_block_fits(const Cache& c, int32_t bs) {
+  return (c.N + bs - 1) / bs <= kSelBlkMax && c.G <= 8;
+}
+
+hipError_t launch_select_block(const Cache& c, int32_t bs, const void* q, const void* kmin,
+                               const void* kmax, int32_t k, int32_t* idx, hipStream_t s) {
+  BlockArgs a{};
+  a.q = q;
+  a.q_dtype = c.q_dtype;
+  a.kmin = static_cast<const uint8_t*>(kmin);
+  a.kmax = static_cast<const uint8_t*>(kmax);
+  a.Hq = c.Hq;
+  a.Hkv = c.Hkv;
+  a.G = c.G;
+  a.nb = (int32_t)((c.N + bs - 1) / bs);
+  a.scores = nullptr;
+  const dim3 grid((unsigned)(c.B * c.Hkv)), block(kSelBlkThreads);
+  if (c.kv_dtype == SA_BF16) {
+    if (c.D == 64)
+      hipLaunchKernelGGL((select_block_kernel<bf16_t, 64>), grid, block, 0, s, a, k, idx);
+    else
+      hipLaunchKernelGGL((select_block_kernel<bf16_t, 128>), grid, block, 0, s, a, k, idx);
+  } else {
+    if (c.D == 64)
+      hipLaunchKernelGGL((select_block_kernel<float, 64>), grid, block, 0, s, a, k, idx);
+    else
+      hipLaunchKernelGGL((select_block_kernel<float, 128>), grid, block, 0, s, a, k, idx);
   }
   return hipGetLastError();
 }
