@@ -439,9 +439,12 @@ def sweep(args):
     indexer, scored then sa_topk or through sa_select (keys
     projected to 64 dims, 4 indexer heads = the KV head's 4 grouped queries
     projected the same way, weights U(0,1)), which reads half the key bytes.
-    The llama32k shape uses the seeded workload; batch128k (68.7
-    GB of K/V) is drawn N(0,1) on the device, since only the selection sizes,
-    not the values, drive the timings there."""
+    Both shapes use their seeded workloads (batch128k: 68.7 GB of K/V, the
+    262 planted keys of each row).  attend_us is the median cache-cold
+    gather-attend launch (a 1 GiB read before each): timed back to back, the
+    batch128k gather (at most 137 MB) would find its rows in the 256 MB
+    last-level cache.  The step columns read every key (or indexer key) row
+    first, which evicts the gathered rows."""
     import torch
     import sa_synth as S
     import top_sparse_decode_sa_amd as T
@@ -475,20 +478,10 @@ def sweep(args):
         log("sweep: %s inputs" % shape)
         gen = torch.Generator(device=dev)
         gen.manual_seed(args.seed)
-        if shape == "llama32k":
-            w = S.Workload(shape, args.seed)
-
-            def up(x):
-                t = torch.from_numpy(x)
-                return (t.view(torch.bfloat16) if t.dtype == torch.uint16 else t).to(dev)
-
-            q, kd, vd = up(w.q()), up(w.k()), up(w.v())
-            data = "seeded workload (planted heavy keys)"
-        else:
-            q = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev).normal_(generator=gen)
-            kd = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=dev).normal_(generator=gen)
-            vd = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=dev).normal_(generator=gen)
-            data = "N(0,1) drawn on the device"
+        w = S.Workload(shape, args.seed)
+        kd, vd, _, _ = upload_kv(w, 0, dev)
+        q = torch.from_numpy(w.q()).view(torch.bfloat16).to(dev)
+        data = "seeded %s workload (planted heavy keys)" % shape
         # per-KV-head indexer inputs (projection P [64, d], N(0, 1/d) entries)
         P = torch.randn((IDX_DIM, d), generator=gen, device=dev) / d ** 0.5
         k_idx = torch.empty((B, Hkv, N, IDX_DIM), dtype=torch.bfloat16, device=dev)
@@ -535,7 +528,7 @@ def sweep(args):
             row["exact_score_us"] = round(timed(exact_score, reps, dense), 1)
             row["indexer_us"] = round(timed(idx_score, reps, dense), 1)
             row["topk_us"] = round(timed(select, reps, dense), 1)
-            row["attend_us"] = round(timed(attend, reps, dense), 1)
+            row["attend_us"] = round(_cold_us({"a": attend}, reps, dev)["a"], 1)
             row["exact_step_us"] = round(timed(lambda: (exact_score(), select(), attend()), reps,
                                                dense), 1)
             row["indexer_step_us"] = round(timed(lambda: (idx_score(), select(), attend()), reps,
@@ -948,6 +941,32 @@ def _stream_floor(nbytes, dev):
     return sbuf, (lambda: T.sa_stream_read(sbuf, sink))
 
 
+def upload_kv(w, layer, dev, chunk=4):
+    """K and V of one layer of a seeded workload, generated on the host in
+    batch slices of `chunk` sequences and copied into device memory; returns
+    (k, v, generation seconds, upload seconds)."""
+    import torch
+
+    c = w.cfg
+    gen_s = up_s = 0.0
+    tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+    kd = torch.empty((c.batch, c.n_kv_heads, c.ctx_len, c.head_dim), dtype=tdt, device=dev)
+    vd = torch.empty_like(kd)
+    for b0 in range(0, c.batch, chunk):
+        b1 = min(c.batch, b0 + chunk)
+        for which, dst in (("k", kd), ("v", vd)):
+            t0 = time.perf_counter()
+            host = w.k(layer, batch=(b0, b1)) if which == "k" else w.v(layer, batch=(b0, b1))
+            t1 = time.perf_counter()
+            t = torch.from_numpy(host)
+            dst[b0:b1].copy_(t.view(torch.bfloat16) if t.dtype == torch.uint16 else t)
+            torch.cuda.synchronize()
+            gen_s += t1 - t0
+            up_s += time.perf_counter() - t1
+            del host, t
+    return kd, vd, gen_s, up_s
+
+
 def _line(name, c, args, value_kernel, timing, extra):
     """One JSON line of a seeded-workload run."""
     at = value_kernel
@@ -988,20 +1007,7 @@ def bench_batch128k(args):
     dev = torch.device("cuda", 0)
     w = S.Workload(name, args.seed)
     log("%s: generating %.1f GB of KV" % (name, c.kv_bytes() / 1e9))
-    gen_s = up_s = 0.0
-    kd = torch.empty((c.batch, c.n_kv_heads, c.ctx_len, c.head_dim), dtype=torch.bfloat16,
-                     device=dev)
-    vd = torch.empty_like(kd)
-    for b0 in range(0, c.batch, 4):
-        for which, dst in (("k", kd), ("v", vd)):
-            t0 = time.perf_counter()
-            host = w.k(0, batch=(b0, b0 + 4)) if which == "k" else w.v(0, batch=(b0, b0 + 4))
-            t1 = time.perf_counter()
-            dst[b0:b0 + 4].copy_(torch.from_numpy(host).view(torch.bfloat16))
-            torch.cuda.synchronize()
-            gen_s += t1 - t0
-            up_s += time.perf_counter() - t1
-            del host
+    kd, vd, gen_s, up_s = upload_kv(w, 0, dev)
     qd = [torch.from_numpy(w.q(0, qvar=v)).view(torch.bfloat16).to(dev) for v in range(2)]
     idx = torch.empty((c.batch, c.n_kv_heads, c.k), dtype=torch.int32, device=dev)
     out = torch.empty((c.batch, c.n_q_heads, c.head_dim), dtype=torch.float32, device=dev)
