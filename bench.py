@@ -26,7 +26,10 @@ HIP graph, and its replays are timed with HIP events on the launch stream
 last-level cache).  `roofline` is that kernel against the 8 TB/s peak;
 `ms_per_step` / `steps_per_s` are the K timed full decode steps (selection +
 gather-attend) and `step` their bandwidth; `kernels` holds per-call times:
-the same attend timed inside eager steps, the selection, the unfused
+the same attend's reads alone (sa_gather_read: the same plan, index and row
+loads without the arithmetic, timed the same way; `roofline.frac_of_gather_read`
+is its time over the attend's), the same attend timed inside eager steps,
+the selection, the unfused
 selection (sa_score then sa_topk) and a dense decode for comparison, and two
 cache-cold single launches after a 1 GiB read -- the gather-attend and
 sa_stream_read over the same number of bytes (the floor for one launch of
@@ -34,13 +37,14 @@ that size).  `stream_read` is sa_stream_read over 8 GiB.  `cpu_baseline`
 times the CPU oracle's selected-set attention (and its full step) on whole
 rows of one step, scaled to a step.
 
-Other modes (each prints its own JSON line): --sweep (full step with four
-selection front ends against dense decode at 2x-500x on the llama32k and
-batch128k shapes), --hylra (layer-reuse plans over 8 layers), --offload
-(selected blocks fetched from a pinned host cache), --nscale (32K-128K
-tokens at fixed k), --indexer1m (the 1M-token 8-layer mixed plan),
---block61k (block selection and reuse on the device); --profile (a short
-run for rocprofv3), --traffic and --summarize (reports from its results).
+Other modes (each prints its own JSON line): --workload block61k |
+indexer1m | batch128k (those workloads on their seeded inputs, with an
+all-core oracle baseline; --block61k and --indexer1m are aliases), --sweep
+(full step with four selection front ends against dense decode at 2x-500x
+on the llama32k and batch128k shapes), --hylra (layer-reuse plans over 8
+layers), --offload (selected blocks fetched from a pinned host cache),
+--nscale (32K-128K tokens at fixed k); --profile (a short run for
+rocprofv3), --traffic and --summarize (reports from its results).
 """
 from __future__ import annotations
 
@@ -1742,6 +1746,32 @@ def main():
     torch.cuda.synchronize()
     ms_attend = e0.elapsed_time(e1) / (n_att_rep * n_graph)
 
+    # the same launches' reads without their arithmetic (sa_gather_read: the
+    # same plan, index loads and row loads), timed the same way: the floor
+    # for this gather-attend on these rows
+    gsink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def gathers():
+        for v in range(n_graph):
+            T.sa_gather_read(qd[v % N_QVAR], kds[v % n_rep], vds[v % n_rep], idx_v[v], gsink)
+
+    gathers()
+    torch.cuda.synchronize()
+    g_gat = None
+    if not args.eager:
+        g_gat = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_gat):
+            gathers()
+    for _ in range(3):
+        g_gat.replay() if g_gat else gathers()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n_att_rep):
+        g_gat.replay() if g_gat else gathers()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_gather = e0.elapsed_time(e1) / (n_att_rep * n_graph)
+
     # per-call durations inside eager steps: HIP events on the launch stream
     # between the two calls (each event pair also holds its launch's
     # dispatch, a few us)
@@ -1862,6 +1892,7 @@ def main():
 
     att = kern("sparse_attend", ms_attend)
     kernels = {"sparse_attend": att,
+               "gather_read_same_rows": kern("sparse_attend", ms_gather),
                "sparse_attend_in_step": kern("sparse_attend", ms_attend_in_step),
                "select": kern("select", ms_select),
                "score_exact": kern("score_exact", ms_score), "topk": kern("topk", ms_topk),
@@ -1876,6 +1907,8 @@ def main():
             "kernel": "sparse_attend", "bytes_per_launch": att_bytes}
     if stream:
         roof["frac_of_stream_read"] = round(att["gbps"] / stream["gbps"], 4)
+    # the gather-attend against its own reads alone (sa_gather_read)
+    roof["frac_of_gather_read"] = round(ms_gather / ms_attend, 4)
     if cold:
         # the cold single launch against a cold streaming read of its bytes
         roof["cold_frac_of_same_bytes_stream"] = round(cold["stream"] / cold["sparse"], 4)

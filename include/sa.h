@@ -440,6 +440,20 @@ const char* sa_version(void);
  * Errors: SA_ERR_NULL / SA_ERR_ALIGN for data, sink; SA_ERR_SHAPE for bytes. */
 sa_status sa_stream_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t stream);
 
+/* The reads of sa_sparse_decode without its arithmetic (a measurement
+ * reference, not a step of the method): for the same descriptor, index kind
+ * and index list, the same launch plan, index loads and key/value row loads
+ * as the pair-pipelined gather-attend, folded with XOR into *sink only if
+ * the fold hits a fixed constant.  Its duration is how long reading the
+ * selected rows alone takes, the floor for that gather-attend launch.
+ * Errors: as sa_sparse_decode for desc, k_cache, v_cache and the index
+ * arguments; SA_ERR_NULL / SA_ERR_ALIGN for sink; SA_ERR_UNSUPPORTED when
+ * sa_sparse_decode would not take the pair-pipelined kernel (fp32, head_dim
+ * 64, more than 4 query heads per KV head, partial last blocks). */
+sa_status sa_gather_read(const sa_kv_desc* desc, const void* k_cache, const void* v_cache,
+                         sa_index_kind ik, const int32_t* idx, int32_t n_idx, int32_t block_size,
+                         uint32_t* sink, hipStream_t stream);
+
 #pragma GCC visibility pop
 
 #ifdef __cplusplus

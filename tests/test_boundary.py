@@ -588,3 +588,24 @@ def test_header_compiles_as_c_and_cxx(tmp_path, lang, compiler):
                         "-I/opt/rocm/include", "-I" + os.path.join(ROOT, "include"), "-x", lang,
                         str(src)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_gather_read_errors():
+    """sa_gather_read: argument checks on the host, and SA_ERR_UNSUPPORTED
+    where sa_sparse_decode would not run the pair-pipelined gather-attend."""
+    L = T.lib()
+    d = _desc()
+
+    def gr(desc, k=FAKE, sink=FAKE, n_idx=10, ik=0, bs=0, idx=FAKE):
+        return L.sa_gather_read(ctypes.byref(desc) if desc is not None else None, k, FAKE, ik,
+                                idx, n_idx, bs, sink, None)
+
+    assert gr(None) == Bn.SA_ERR_NULL
+    assert gr(d, k=None) == Bn.SA_ERR_NULL
+    assert gr(d, sink=None) == Bn.SA_ERR_NULL
+    assert gr(d, k=MIS) == Bn.SA_ERR_ALIGN
+    assert gr(d, n_idx=0) == Bn.SA_ERR_SHAPE
+    assert gr(d, idx=None) == Bn.SA_ERR_NULL
+    f32 = _desc(q_dtype=Bn.SA_F32, kv_dtype=Bn.SA_F32)
+    assert gr(f32) == Bn.SA_ERR_UNSUPPORTED
+    assert "pair-pipelined" in L.sa_last_error().decode()

@@ -661,6 +661,43 @@ def test_stream_read_covers_every_word(nbytes):
         assert int(sink.item()) == int(marker), w
 
 
+@pytest.mark.parametrize("B,Hkv,N,k,kind,bs", [(16, 8, 32768, 655, T.SA_IDX_TOKEN_PER_KV_HEAD, 0),
+                                                (1, 8, 100000, 2048, T.SA_IDX_TOKEN_SHARED, 0),
+                                                (2, 2, 8192, 24, T.SA_IDX_BLOCK_PER_KV_HEAD, 128)])
+def test_gather_read_reads_the_selected_rows(B, Hkv, N, k, kind, bs):
+    """sa_gather_read folds every word of the selected key and value rows it
+    loads: with zero caches, a 0x9e3779b9 word in a selected row (the first
+    selected token of a row; any of the key's or the value's words) reaches
+    the sink, and the same word in a row that is not selected does not."""
+    say("gather read", B, Hkv, N, k, kind, bs)
+    marker = int(np.uint32(0x9E3779B9).view(np.int32))
+    G, d = 4, 128
+    q = torch.zeros((B, Hkv * G, d), dtype=torch.bfloat16, device=dev())
+    kc = torch.zeros((B, Hkv, N, d), dtype=torch.bfloat16, device=dev())
+    vc = torch.zeros_like(kc)
+    rng = np.random.default_rng(N + k)
+    nsel = N // bs if bs else N
+    rows = B if kind == T.SA_IDX_TOKEN_SHARED else B * Hkv
+    sel = np.stack([np.sort(rng.choice(np.arange(1, nsel), k, replace=False)) for _ in range(rows)])
+    idx = torch.from_numpy(sel.astype(np.int32).reshape((B, k) if kind == T.SA_IDX_TOKEN_SHARED
+                                                         else (B, Hkv, k))).to(dev())
+    sink = torch.zeros(1, dtype=torch.int32, device=dev())
+    T.sa_gather_read(q, kc, vc, idx, sink, kind, bs)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
+    b, r = B - 1, Hkv - 1
+    t = int(sel[b if kind == T.SA_IDX_TOKEN_SHARED else b * Hkv + r, 0]) * (bs or 1)
+    for cache, word, tok in [(kc, 0, t), (kc, 63, t), (vc, 5, t), (vc, 60, t), (kc, 0, 0)]:
+        kc.zero_()
+        vc.zero_()
+        cache.view(torch.int32)[b, r, tok, word] = marker
+        sink.zero_()
+        T.sa_gather_read(q, kc, vc, idx, sink, kind, bs)
+        torch.cuda.synchronize()
+        want = 0 if tok == 0 else marker   # token 0 is never selected
+        assert int(sink.item()) == want, (word, tok)
+
+
 @pytest.mark.parametrize("N,dtype,want_splits,want_sparse",
                          [(25677, "bf16", 101, 313), (51277, "bf16", 201, 313),
                           (153677, "bf16", 601, 313), (40000, "f32", 625, 625)])

@@ -14,7 +14,7 @@ from ._binding import (  # noqa: F401
     sa_index_overlap, sa_layer_workspace_size, sa_plan_fixed_jump, sa_plan_reuse,
     sa_check_indices, sa_plan_validate, sa_score, sa_select, sa_sparse_decode,
     sa_sparse_decode_noalloc,
-    sa_stream_read, sa_topk,
+    sa_gather_read, sa_stream_read, sa_topk,
     sa_version, sa_workspace_init)
 
 __version__ = "0.1.0"

@@ -39,7 +39,7 @@ EXPORTED = [
     "sa_sparse_workspace_size", "sa_dense_decode", "sa_dense_workspace_size",
     "sa_dense_decode_scored", "sa_dense_scored_workspace_size", "sa_decode_layer",
     "sa_layer_workspace_size", "sa_plan_validate", "sa_index_overlap", "sa_plan_reuse",
-    "sa_plan_fixed_jump", "sa_gather_blocks", "sa_workspace_init", "sa_stream_read",
+    "sa_plan_fixed_jump", "sa_gather_blocks", "sa_workspace_init", "sa_stream_read", "sa_gather_read",
     "sa_status_string", "sa_last_error", "sa_version",
 ]
 
@@ -91,6 +91,7 @@ def lib() -> ctypes.CDLL:
     L.sa_select_workspace_size.argtypes = [P(KVDesc), st, i32]
     L.sa_select_workspace_size.restype = sz
     L.sa_stream_read.argtypes = [vp, sz, vp, vp]
+    L.sa_gather_read.argtypes = [P(KVDesc), vp, vp, st, vp, i32, i32, vp, vp]
     L.sa_sparse_decode.argtypes = [P(KVDesc), vp, vp, vp, st, vp, i32, i32, vp, vp, sz, vp]
     L.sa_sparse_decode_noalloc.argtypes = [P(KVDesc), vp, vp, vp, st, vp, i32, i32, vp, vp]
     L.sa_check_indices.argtypes = [P(KVDesc), st, vp, i32, i32, vp, vp]
@@ -121,7 +122,7 @@ def lib() -> ctypes.CDLL:
                  "sa_dense_decode",
                  "sa_dense_decode_scored", "sa_decode_layer", "sa_plan_validate",
                  "sa_index_overlap", "sa_plan_reuse", "sa_plan_fixed_jump", "sa_gather_blocks",
-                 "sa_workspace_init", "sa_stream_read"]:
+                 "sa_workspace_init", "sa_stream_read", "sa_gather_read"]:
         getattr(L, name).restype = st
     _lib = L
     return L
@@ -312,6 +313,20 @@ def sa_stream_read(data, sink):
     reference, not a step of the method)."""
     dev = _dev(data, sink)
     check(lib().sa_stream_read(_ptr(data), data.numel() * data.element_size(), _ptr(sink),
+                               ctypes.c_void_p(_stream(dev))))
+
+
+def sa_gather_read(q, k_cache, v_cache, idx, sink, index_kind=SA_IDX_TOKEN_PER_KV_HEAD,
+                   block_size=0):
+    """sa_gather_read: the reads of sa_sparse_decode on the same arguments
+    without its arithmetic (measurement reference); q only gives the
+    descriptor its head counts."""
+    dev = _dev(q, k_cache, v_cache, idx, sink)
+    if idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be a contiguous int32 tensor")
+    desc = make_desc(q, k_cache)
+    check(lib().sa_gather_read(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), index_kind,
+                               _ptr(idx), idx.shape[-1], block_size, _ptr(sink),
                                ctypes.c_void_p(_stream(dev))))
 
 

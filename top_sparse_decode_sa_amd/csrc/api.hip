@@ -542,6 +542,26 @@ sa_status sa_sparse_decode_noalloc(const sa_kv_desc* desc, const void* q, const 
       "sa_sparse_decode_noalloc launch");
 }
 
+sa_status sa_gather_read(const sa_kv_desc* desc, const void* k_cache, const void* v_cache,
+                         sa_index_kind ik, const int32_t* idx, int32_t n_idx, int32_t block_size,
+                         uint32_t* sink, hipStream_t stream) {
+  Cache c;
+  sa_status st;
+  if ((st = check_desc(desc, &c)) != SA_OK) return st;
+  if ((st = check_ptr(k_cache, "k_cache", 16)) != SA_OK) return st;
+  if ((st = check_ptr(v_cache, "v_cache", 16)) != SA_OK) return st;
+  if ((st = check_ptr(sink, "sink", 4)) != SA_OK) return st;
+  if ((st = check_sparse_idx(c, ik, idx, n_idx, block_size)) != SA_OK) return st;
+  const Cache v = attend_view(c, ik);
+  const AttendPlan p = plan_attend(v, mode_of(ik), n_idx, block_size);
+  if (p.kernel != kKernPairs)
+    return fail(SA_ERR_UNSUPPORTED,
+                "sa_gather_read covers the pair-pipelined gather-attend only (bf16, head_dim 128, "
+                "at most 4 query heads per KV head, token indices or whole blocks)");
+  return hip_status(launch_gather_read(v, p, k_cache, v_cache, idx, n_idx, block_size, sink, stream),
+                    "sa_gather_read launch");
+}
+
 sa_status sa_check_indices(const sa_kv_desc* desc, sa_index_kind ik, const int32_t* idx,
                            int32_t n_idx, int32_t block_size, int32_t* counts,
                            hipStream_t stream) {

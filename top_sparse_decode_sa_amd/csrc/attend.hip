@@ -807,6 +807,7 @@ __device__ __forceinline__ void attend_pairs_body(const AttendArgs& a, const int
     const float* pa0 = arow ? &lds.s_p[wave][ha < G ? ha : 0][0][rq][0] : lds.s_zero;
     const float* pa1 = arow ? pa0 + 16 : lds.s_zero + 4;
 
+    bf16x8_t qa[4];  // A fragments: q of head n % G, dims [32c + 8rq, +8)
 #pragma unroll
     for (int p = 0; p < PAIRS; ++p) {
       // each pair's work stays after the previous pair's (it waits only for
@@ -828,13 +829,15 @@ __device__ __forceinline__ void attend_pairs_body(const AttendArgs& a, const int
         // A fragments: q of head n % G, dims [32c + 8rq, +8) (lanes n >= G
         // repeat a head; the result rows they produce, G..15, are never
         // read); B fragments from the key tile
-        bf16x8_t kf[4], qa[4];
+        bf16x8_t kf[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const uint4 w = *reinterpret_cast<const uint4*>(kt + kt_pos(n, 4 * c + rq));
           __builtin_memcpy(&kf[c], &w, 16);
-          const uint4 x = *reinterpret_cast<const uint4*>(lds.q + (n % G) * 256 + 64 * c + 16 * rq);
-          __builtin_memcpy(&qa[c], &x, 16);
+          if (p == 0 && i == 0) {  // the query fragments are the same for every tile
+            const uint4 x = *reinterpret_cast<const uint4*>(lds.q + (n % G) * 256 + 64 * c + 16 * rq);
+            __builtin_memcpy(&qa[c], &x, 16);
+          }
         }
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -1053,6 +1056,75 @@ __global__ __launch_bounds__(64 * kMaxPairWaves) void attend_pairs_kernel(Attend
   int row, split, half;
   if (!pairs_coords<VH>(a, row, split, half)) return;
   attend_pairs_body<G, MODE, PAIRS, false, VH>(a, nullptr, lds, row, split, half);
+}
+
+// The reads of attend_pairs_kernel without its arithmetic (a measurement
+// reference, not a step of the method): the same grid, the same slots per
+// wave, the same index loads and the same key and value row loads (whole
+// 128-byte lines, nontemporal buffer loads), folded with XOR; the fold is
+// stored only if it equals a constant it practically never equals.  Its
+// duration is what reading the selected rows alone takes on this device.
+template <int MODE, int PAIRS, int VH>
+__global__ __launch_bounds__(64 * kMaxPairWaves) void gather_read_kernel(AttendArgs a,
+                                                                         uint32_t* sink) {
+  constexpr int D = 128;
+  constexpr int DV = D / VH;
+  constexpr int TILES = 2 * PAIRS;
+  int row, split, half;
+  if (!pairs_coords<VH>(a, row, split, half)) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n = lane & 15;
+  const int rq = lane >> 4;
+  const int b = row / a.Hkv;
+  const int r = row % a.Hkv;
+  const int64_t wg0 = (int64_t)split * a.chunk;
+  const int64_t wg1 = min(wg0 + (int64_t)a.chunk, a.n_slots);
+  const int64_t s0 = wg0 + (int64_t)wave * 32 * PAIRS;
+  const int64_t s1 = min(s0 + 32 * PAIRS, wg1);
+  if (s0 >= wg1) return;
+  const int64_t kv_off = ((int64_t)b * a.sb + (int64_t)(r / a.kv_div) * a.sh) * 2;
+  const uint32_t row_bytes = (uint32_t)(a.st * 2);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.k + kv_off), (short)0, a.row_span, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.v + kv_off), (short)0, a.row_span, kBufferFlags);
+  uint32_t toff[TILES];
+#pragma unroll
+  for (int i = 0; i < TILES; ++i) {
+    bool ok_unused;
+    toff[i] = (uint32_t)slot_token<MODE, false>(a, row, b, s0 + 16 * i + n, s1, ok_unused) *
+              row_bytes;
+  }
+  uint32_t acc = 0;
+#pragma unroll
+  for (int i = 0; i < TILES; ++i)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t base = (uint32_t)__shfl((int)toff[i], 4 * u + rq);
+      const uint4 k = ld16_buf(rk, base + 16 * n);
+      acc ^= k.x ^ k.y ^ k.z ^ k.w;
+      if constexpr (VH == 1) {
+        const uint4 x = ld16_buf(rv, base + 16 * n);
+        acc ^= x.x ^ x.y ^ x.z ^ x.w;
+      } else {
+        const uint2 x = ld8_buf(rv, base + DV * 2 * half + 8 * n);
+        acc ^= x.x ^ x.y;
+      }
+    }
+  if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
+template <int PAIRS, int VH>
+hipError_t dispatch_gather_read(int mode, dim3 grid, dim3 block, const AttendArgs& a, uint32_t* sink,
+                                hipStream_t s) {
+  if (mode == kIdxTokenShared)
+    hipLaunchKernelGGL((gather_read_kernel<kIdxTokenShared, PAIRS, VH>), grid, block, 0, s, a, sink);
+  else if (mode == kIdxBlockPerHead)
+    hipLaunchKernelGGL((gather_read_kernel<kIdxBlockPerHead, PAIRS, VH>), grid, block, 0, s, a, sink);
+  else
+    hipLaunchKernelGGL((gather_read_kernel<kIdxTokenPerHead, PAIRS, VH>), grid, block, 0, s, a, sink);
+  return hipGetLastError();
 }
 
 // Merge, then gather-attend, in one workgroup of kMaxSparseWaves waves per
@@ -1463,6 +1535,19 @@ AttendArgs attend_args(const Cache& c, const AttendPlan& p, const void* q, const
 }
 
 }  // namespace
+
+hipError_t launch_gather_read(const Cache& c, const AttendPlan& p, const void* k, const void* v,
+                              const int32_t* idx, int32_t n_idx, int32_t bs, uint32_t* sink,
+                              hipStream_t s) {
+  const AttendArgs a = attend_args(c, p, nullptr, k, v, idx, n_idx, bs, nullptr, nullptr, nullptr);
+  const int64_t rows = (int64_t)c.B * c.Hkv;
+  const dim3 block(64 * p.waves), grid = pairs_grid(p, rows);
+  if (p.vhalves == 2)
+    return p.pairs == 1 ? dispatch_gather_read<1, 2>(p.mode, grid, block, a, sink, s)
+                        : dispatch_gather_read<2, 2>(p.mode, grid, block, a, sink, s);
+  return p.pairs == 1 ? dispatch_gather_read<1, 1>(p.mode, grid, block, a, sink, s)
+                      : dispatch_gather_read<2, 1>(p.mode, grid, block, a, sink, s);
+}
 
 hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, const void* k,
                          const void* v, const int32_t* idx, int32_t n_idx, int32_t bs, float* out,

@@ -140,6 +140,10 @@ struct AttendPlan {
 
 AttendPlan plan_attend(const Cache& c, int mode, int32_t n_idx, int32_t bs);
 // scores: kIdxDenseScored only, [B, Hkv, N] fp32.
+// The gather-attend's reads alone for a kKernPairs plan (measurement reference).
+hipError_t launch_gather_read(const Cache& c, const AttendPlan& p, const void* k, const void* v,
+                              const int32_t* idx, int32_t n_idx, int32_t bs, uint32_t* sink,
+                              hipStream_t s);
 hipError_t launch_attend(const Cache& c, const AttendPlan& p, const void* q, const void* k,
                          const void* v, const int32_t* idx, int32_t n_idx, int32_t bs, float* out,
                          void* ws, hipStream_t s, float* scores = nullptr);
