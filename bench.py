@@ -773,15 +773,31 @@ def oracle_pool(cfg, seed, task_lists, shm=None):
     saved = {v: os.environ.get(v) for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
                                             "MKL_NUM_THREADS")}
     os.environ.update({v: "1" for v in saved})
+    import queue
+
+    procs = []
     try:
         procs = [ctx.Process(target=_oracle_worker, args=(cfg, seed, tl, shm, barrier, results))
                  for tl in task_lists]
         for p in procs:
             p.start()
-        got = [results.get() for _ in procs]
+        got = []
+        while len(got) < len(procs):
+            try:
+                got.append(results.get(timeout=5.0))
+            except queue.Empty:
+                # a worker that died (out of memory, an exception) never reports
+                dead = [p.exitcode for p in procs if p.exitcode not in (None, 0)]
+                if dead:
+                    barrier.abort()
+                    raise RuntimeError("oracle worker failed (exit codes %s)" % dead)
         for p in procs:
             p.join()
     finally:
+        for p in procs:
+            if p.is_alive():
+                p.terminate()
+                p.join()
         for v, x in saved.items():
             if x is None:
                 os.environ.pop(v, None)

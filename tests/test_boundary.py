@@ -609,3 +609,12 @@ def test_gather_read_errors():
     f32 = _desc(q_dtype=Bn.SA_F32, kv_dtype=Bn.SA_F32)
     assert gr(f32) == Bn.SA_ERR_UNSUPPORTED
     assert "pair-pipelined" in L.sa_last_error().decode()
+
+
+def test_bench_oracle_pool_reports_a_failed_worker():
+    """A worker of the oracle baseline that fails (here: an unknown unit)
+    makes the pool raise instead of leaving the others at the barrier."""
+    import bench
+    import sa_synth as S
+    with pytest.raises(RuntimeError, match="oracle worker failed"):
+        bench.oracle_pool(S.CONFIGS["tiny"], 0, [[("no such unit",)], [("no such unit",)]])
