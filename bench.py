@@ -577,8 +577,8 @@ def nscale(args):
     N = 32K, 64K and 128K.  The gather-attend reads 2*B*Hkv*k*d*2 bytes at
     every N (the sparse method's traffic does not grow with the context);
     the exact selection reads every key once and dense decode every key and
-    value, so both grow linearly.  Values are N(0,1) drawn on the device:
-    only the sizes drive these timings."""
+    value, so both grow linearly.  The seeded llama32k workload at each
+    context length (1 % planted heavy keys), generated on the host."""
     import torch
     import top_sparse_decode_sa_amd as T
 
@@ -602,13 +602,16 @@ def nscale(args):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n * 1e3  # us
 
+    import dataclasses
+    import sa_synth as S
+
     for N in NSCALE_N:
         log("nscale: N=%d" % N)
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(args.seed)
-        q = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev).normal_(generator=gen)
-        kd = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=dev).normal_(generator=gen)
-        vd = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=dev).normal_(generator=gen)
+        cN = dataclasses.replace(S.CONFIGS["llama32k"], ctx_len=N, k=k,
+                                 n_planted=int(0.01 * N))
+        w = S.Workload(cN, args.seed)
+        kd, vd, _, _ = upload_kv(w, 0, dev)
+        q = torch.from_numpy(w.q()).view(torch.bfloat16).to(dev)
         idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
 
@@ -646,7 +649,8 @@ def nscale(args):
     print(json.dumps({"bench": "context-length scaling at fixed k", "unit": "us (HIP events)",
                       "config": {"workload": "llama32k shape at N = 32K, 64K, 128K, k = 655",
                                  "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d},
-                      "rows": rows, "data": "N(0,1) drawn on the device (seed %d)" % args.seed,
+                      "rows": rows, "data": "synthetic: the seeded llama32k workload at each "
+                                            "context length (seed %d)" % args.seed,
                       "provenance": provenance()}), flush=True)
 
 
@@ -1371,8 +1375,8 @@ def hylra(args):
     """Layer-reuse policy on 8 layers of the llama32k shape.
 
     Queries and keys of layer l follow x_l = rho_l x_{l-1} + sqrt(1 - rho_l^2) z_l
-    with the hylra32k schedule (a weakly correlated layer 4), drawn on the
-    device (timings depend on the shapes and the plan, not on the values).
+    with the hylra32k schedule (a weakly correlated layer 4): the seeded
+    hylra32k workload, generated on the host (untimed).
     Offline: every layer runs DENSE_SELECT, sa_index_overlap gives the
     overlap matrix, sa_plan_reuse the policy.  Then one 8-layer decode step is
     timed under each plan."""
@@ -1384,28 +1388,15 @@ def hylra(args):
     dev = torch.device("cuda", 0)
     c = S.CONFIGS["hylra32k"]
     B, Hq, Hkv, d, N, k, L = c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.ctx_len, c.k, c.n_layers
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(args.seed)
-    log("hylra: drawing %d layers (%.1f GB of KV)" % (L, L * c.kv_bytes() / 1e9))
+    w = S.Workload(c, args.seed)
+    log("hylra: generating %d layers (%.1f GB of KV)" % (L, L * c.kv_bytes() / 1e9))
     qs, ks, vs = [], [], []
-    xq = torch.randn((B, Hq, d), generator=gen, device=dev)
-    xk = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=dev)
     for l in range(L):
-        if l > 0:
-            r = c.rho_sched[l]
-            xq = r * xq + (1 - r * r) ** 0.5 * torch.randn(xq.shape, generator=gen, device=dev)
-        qs.append(xq.to(torch.bfloat16).contiguous())
-        kl = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=dev)
-        for b in range(B):     # the fp32 latent chain one sequence at a time
-            z = torch.randn((Hkv, N, d), generator=gen, device=dev)
-            if l > 0:
-                r = c.rho_sched[l]
-                z = r * xk[b].float() + (1 - r * r) ** 0.5 * z
-            xk[b] = z.to(torch.bfloat16)
-            kl[b] = xk[b]
-        ks.append(kl)
-        vs.append(torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=dev).normal_(generator=gen))
-    del xk
+        kd, vd, _, _ = upload_kv(w, l, dev)
+        ks.append(kd)
+        vs.append(vd)
+        qs.append(torch.from_numpy(w.q(l)).view(torch.bfloat16).to(dev))
+        log("hylra: layer %d generated" % l)
     torch.cuda.synchronize()
     outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(L)]
     largs = []
@@ -1487,7 +1478,7 @@ def hylra(args):
                    "k": k, "rho_sched": list(c.rho_sched), "theta": args.theta},
         "overlap_ratio": [[round(float(x), 4) for x in row] for row in ratio],
         "plans": res, "us_per_layer": per_layer,
-        "data": "drawn on the device (torch generator, seed %d)" % args.seed,
+        "data": "synthetic: the seeded hylra32k workload (seed %d)" % args.seed,
         "provenance": provenance()}), flush=True)
 
 
@@ -1498,8 +1489,8 @@ def offload(args):
     Layer 0's cache is on the device; it selects blocks from min/max
     summaries.  Layers 1-3 keep their caches in pinned host memory and reuse
     layer 0's blocks: sa_gather_blocks fetches only those blocks, and dense
-    decode over the gathered rows is their attention.  Values are drawn on
-    the device; timings depend on the sizes only."""
+    decode over the gathered rows is their attention.  The seeded block61k
+    workload (its four layers), generated on the host (untimed)."""
     import torch
     import sa_synth as S
     import top_sparse_decode_sa_amd as T
@@ -1509,20 +1500,18 @@ def offload(args):
     c = S.CONFIGS["block61k"]
     B, Hq, Hkv, d, N, bs, nblk = (c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.ctx_len,
                                   c.block_size, c.k)
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(args.seed)
+    w = S.Workload(c, args.seed)
     shape = (B, Hkv, N, d)
-    log("offload: drawing 4 layers (%.1f GB of KV, 3 layers in pinned host memory)" % (
+    log("offload: generating 4 layers (%.1f GB of KV, 3 layers in pinned host memory)" % (
         4 * c.kv_bytes() / 1e9))
-    qs = [torch.randn((B, Hq, d), generator=gen, device=dev).to(torch.bfloat16) for _ in range(4)]
-    k0 = torch.empty(shape, dtype=torch.bfloat16, device=dev).normal_(generator=gen)
-    v0 = torch.empty(shape, dtype=torch.bfloat16, device=dev).normal_(generator=gen)
+    qs = [torch.from_numpy(w.q(l)).view(torch.bfloat16).to(dev) for l in range(4)]
+    k0, v0, _, _ = upload_kv(w, 0, dev)
     host = []
-    for _ in range(3):
+    for l in range(1, 4):
         kh = torch.empty(shape, dtype=torch.bfloat16, pin_memory=True)
         vh = torch.empty(shape, dtype=torch.bfloat16, pin_memory=True)
-        for t in (kh, vh):
-            t.copy_(torch.empty(shape, dtype=torch.bfloat16, device=dev).normal_(generator=gen))
+        kh.copy_(torch.from_numpy(w.k(l)).view(torch.bfloat16))
+        vh.copy_(torch.from_numpy(w.v(l)).view(torch.bfloat16))
         host.append((kh, vh))
     torch.cuda.synchronize()
     # layer 0: block selection on the device
@@ -1597,7 +1586,7 @@ def offload(args):
         "full_copy_host_link_gbps": round(full_bytes / us_full / 1e3, 1),
         "per_layer_speedup_vs_full_copy": round(us_full / (us_gather + us_attend), 2),
         "reuse_pipeline_3_layers_us": round(us_pipe, 1),
-        "data": "drawn on the device (torch generator, seed %d)" % args.seed,
+        "data": "synthetic: the seeded block61k workload (seed %d)" % args.seed,
         "provenance": provenance()}
     print(json.dumps(res), flush=True)
 
