@@ -643,22 +643,19 @@ __global__ __launch_bounds__(64 * max_waves<MODE>()) void attend_sparse_kernel(A
 // Selected-token gather-attend, pipelined by pairs of 16-slot tiles.
 //
 // A wave owns up to 32 * PAIRS consecutive slots.  It requests every index,
-// key and value row of its slots at once, in pair order (indices; then per
-// pair: keys of both tiles, values of both tiles), and then consumes the
-// pairs in that order, so the work on a pair's rows overlaps the arrival of
-// the later pairs' rows and only the last pair's work follows the last row.
+// then the key rows of all its slots, then their value rows, all at once,
+// and consumes them in that order: the logits of every pair as its keys
+// arrive, one softmax over all of the wave's slots, then P.V pair by pair as
+// the values arrive -- so only P.V follows the last row's arrival.
 //
 // Per pair, Q.K gives each tile's logits in MFMA rows 0..3 (lanes 0..15);
 // one lane-row swap then puts the second tile's in lanes 16..31, so the
-// softmax of a pair runs on 32 lanes.  The softmax keeps one reference per head for the whole wave
-// (the first pair's maximum), raised only when a later logit exceeds it by
-// more than 2^kLazyLog2 -- so exp2(logit - reference) never exceeds 2^8 and
-// the running sums and the P.V accumulators are rescaled only then.  Row
-// sums accumulate per lane and are reduced once at the end.  P.V runs on
+// softmax runs on 32 lanes.  Its reference per head is the maximum of the
+// wave's logits, so exp2(logit - reference) <= 1 and nothing is rescaled;
+// row sums accumulate per lane and are reduced once at the end.  P.V runs on
 // MFMA as in the kernel above (P as a truncated bf16 pair hi + lo, V columns
 // assembled from the lane's own value rows by byte permutes).
 constexpr int kMaxPairWaves = 12;
-constexpr float kLazyLog2 = 8.0f;
 
 // Position of 16-byte chunk x (dims [8x, 8x + 8)) of token t in a wave's
 // key tile: one row of the 16 tokens per chunk, rows padded to 272 bytes, so
@@ -681,12 +678,37 @@ struct PairLds {
   alignas(16) uint8_t q[4 * 256];                     // the row's G query heads, bf16
   alignas(16) float s_p[kMaxPairWaves][G][2][4][4];  // p of head h, tile, g, u (token 4u + g)
   alignas(16) float s_zero[8];                        // A rows that carry no head
-  float s_ml[kMaxPairWaves][2][G];
+  float s_m[4][kMaxPairWaves];                        // merge: reference of head h, wave w
+  float s_l[4][kMaxPairWaves];                        // merge: sum of head h, wave w
 };
 
 
 __device__ __forceinline__ float lane_f(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// Order-preserving integer key of a float that is not NaN (a larger float
+// has a larger key, -0 just below +0), and back: a max over lanes then runs
+// as integer DPP maxes, which need no quieting of their float operands.
+__device__ __forceinline__ int ordered_key(float f) {
+  const int s = __float_as_int(f);
+  return s ^ ((s >> 31) & 0x7fffffff);
+}
+__device__ __forceinline__ float ordered_float(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7fffffff)); }
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+}
+
+// Maximum of x over lanes 0..31 (two rows of 16), x finite or -inf.
+__device__ __forceinline__ float max_lanes32(float x) {
+  int k = ordered_key(x);
+  k = max(k, dpp_i<kQuadXor1>(k));
+  k = max(k, dpp_i<kQuadXor2>(k));
+  k = max(k, dpp_i<kRowHalfMirror>(k));
+  k = max(k, dpp_i<kRowMirror>(k));
+  return ordered_float(max(__builtin_amdgcn_readlane(k, 0), __builtin_amdgcn_readlane(k, 16)));
 }
 
 // VH = 1: the workgroup computes all head_dim output dimensions of its slot
@@ -762,26 +784,35 @@ __device__ __forceinline__ void attend_pairs_body(const AttendArgs& a, const int
       toff[i] = (uint32_t)slot_token<MODE, LIDX>(a, row, b, s0 + 16 * i + n, s1, ok_unused, lidx) *
                 row_bytes;
     }
-    // 2. tile by tile (so pair by pair), the key and the value row pieces of
-    //    token 4u + rq of the tile (load u): lane (n, rq) reads key bytes
-    //    [16n, +16) and value bytes [DV*2*half + 16n/VH, +16/VH), so every
-    //    8 (values of a half: 16) lanes read one whole 128-byte line.
+    // 2. the key row pieces of every tile, then the value row pieces of every
+    //    tile, of token 4u + rq of the tile (load u): lane (n, rq) reads key
+    //    bytes [16n, +16) and value bytes [DV*2*half + 16n/VH, +16/VH), so
+    //    every 8 (values of a half: 16) lanes read one whole 128-byte line.
+    //    Keys first: the logits and the softmax of all pairs need only keys,
+    //    so they run while the values arrive, and only P.V follows them.
+    uint32_t base[TILES][4];
+#pragma unroll
+    for (int i = 0; i < TILES; ++i)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) base[i][u] = (uint32_t)__shfl((int)toff[i], 4 * u + rq);
     uint4 kl[TILES][4];
     uint32_t vw[TILES][4][VW];
 #pragma unroll
     for (int i = 0; i < TILES; ++i)
 #pragma unroll
+      for (int u = 0; u < 4; ++u) kl[i][u] = ld16_buf(rk, base[i][u] + 16 * n);
+#pragma unroll
+    for (int i = 0; i < TILES; ++i)
+#pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint32_t base = (uint32_t)__shfl((int)toff[i], 4 * u + rq);
-        kl[i][u] = ld16_buf(rk, base + 16 * n);
         if constexpr (VH == 1) {
-          const uint4 x = ld16_buf(rv, base + 16 * n);
+          const uint4 x = ld16_buf(rv, base[i][u] + 16 * n);
           vw[i][u][0] = x.x;
           vw[i][u][1] = x.y;
           vw[i][u][2] = x.z;
           vw[i][u][3] = x.w;
         } else {
-          const uint2 x = ld8_buf(rv, base + DV * 2 * half + 8 * n);
+          const uint2 x = ld8_buf(rv, base[i][u] + DV * 2 * half + 8 * n);
           vw[i][u][0] = x.x;
           vw[i][u][1] = x.y;
         }
@@ -792,13 +823,16 @@ __device__ __forceinline__ void attend_pairs_body(const AttendArgs& a, const int
     __builtin_amdgcn_sched_barrier(0);
     uint8_t* const kt = lds.w[wave].kt;
 
-    float mref[G], lsum[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      mref[h] = 0.0f;
-      lsum[h] = 0.0f;
-    }
+    float mref[G];
     f32x4_t oacc[NE];
+    // row sums on the matrix cores: P times a B of ones gives, in lane
+    // (n, rq), the sums of A rows 4rq (hi) and 4rq + 1 (lo) of head rq
+    f32x4_t lacc = {0.0f, 0.0f, 0.0f, 0.0f};
+    bf16x8_t ones;
+    {
+      const uint32_t o1[4] = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+      __builtin_memcpy(&ones, o1, 16);
+    }
 #pragma unroll
     for (int e = 0; e < NE; ++e) oacc[e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     const int ha = n >> 2;  // A row n of P.V: head n / 4, part n % 4 (0 hi, 1 lo)
@@ -807,18 +841,19 @@ __device__ __forceinline__ void attend_pairs_body(const AttendArgs& a, const int
     const float* pa0 = arow ? &lds.s_p[wave][ha < G ? ha : 0][0][rq][0] : lds.s_zero;
     const float* pa1 = arow ? pa0 + 16 : lds.s_zero + 4;
 
-    bf16x8_t qa[4];  // A fragments: q of head n % G, dims [32c + 8rq, +8)
+    // 3. logits of every pair: both tiles' (rows 0..G-1, lanes 0..15 of
+    //    each result), then the second tile's rows moved to lanes 16..31:
+    //    lanes 0..15 hold tile 2p, lanes 16..31 tile 2p + 1.
+    //    Each tile goes through the wave's LDS tile: stored as loaded, read
+    //    back as MFMA B fragments (lane (n, rq) of fragment c: token n, dims
+    //    [32c + 8rq, +8), i.e. chunk 4c + rq).
+    float xl[PAIRS][G];  // lane (n, rq < 2): logit of slot 32p + 16rq + n
+    bf16x8_t qa[4];      // A fragments: q of head n % G, dims [32c + 8rq, +8)
 #pragma unroll
     for (int p = 0; p < PAIRS; ++p) {
       // each pair's work stays after the previous pair's (it waits only for
-      // its own rows)
+      // its own keys)
       __builtin_amdgcn_sched_barrier(0);
-      // 3. logits of both tiles (rows 0..G-1, lanes 0..15 of each result),
-      //    then the second tile's rows moved to lanes 16..31: lanes 0..15
-      //    hold tile 2p, lanes 16..31 tile 2p + 1.
-      //    Each tile goes through the wave's LDS tile: stored as loaded,
-      //    read back as MFMA B fragments (lane (n, rq) of fragment c: token n,
-      //    dims [32c + 8rq, +8), i.e. chunk 4c + rq).
       f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -826,9 +861,8 @@ __device__ __forceinline__ void attend_pairs_body(const AttendArgs& a, const int
         for (int u = 0; u < 4; ++u)
           *reinterpret_cast<uint4*>(kt + kt_pos(4 * u + rq, n)) = kl[2 * p + i][u];
         __builtin_amdgcn_wave_barrier();
-        // A fragments: q of head n % G, dims [32c + 8rq, +8) (lanes n >= G
-        // repeat a head; the result rows they produce, G..15, are never
-        // read); B fragments from the key tile
+        // lanes n >= G repeat a head; the result rows they produce, G..15,
+        // are never read
         bf16x8_t kf[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -848,66 +882,37 @@ __device__ __forceinline__ void attend_pairs_body(const AttendArgs& a, const int
             acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[c], kf[c], acc1, 0, 0, 0);
         }
       }
+      const bool vld = rq < 2 && s0 + 32 * p + 16 * rq + n < s1;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         // odd 16-lane rows of the first operand trade with even rows of the second
         const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[h]),
                                                          __float_as_uint(acc1[h]), false, false);
-        acc[h] = __uint_as_float(sw[0]);
+        xl[p][h] = vld ? __uint_as_float(sw[0]) * a.qscale : -INFINITY;
       }
-      // lane (n, rq < 2) holds slot 32p + 16rq + n of the wave
-      const bool vld = rq < 2 && s0 + 32 * p + 16 * rq + n < s1;
-      // 4. exponents against the wave's reference (set by the first pair)
-      float t[G];
-      if (p == 0) {
+    }
+    // 4. the wave's reference per head: the maximum of its logits (finite:
+    //    the wave has at least one slot), and the exponents against it
+    float pv[PAIRS][G];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float x = vld ? acc[h] * a.qscale : -INFINITY;
-          const float mx = group_max<16>(x);
-          mref[h] = fmaxf(lane_f(mx, 0), lane_f(mx, 16));
-          t[h] = x - mref[h];
-        }
-      } else {
-        float tm = -INFINITY;
+    for (int h = 0; h < G; ++h) {
+      float x = xl[0][h];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          t[h] = vld ? fmaf(acc[h], a.qscale, -mref[h]) : -INFINITY;
-          tm = fmaxf(tm, t[h]);
-        }
-        if (__any(tm > kLazyLog2)) {
-          // a logit above the reference by more than 2^8: raise the
-          // references of the heads that grew and rescale what they summed
-          float alpha_me = 1.0f;
+      for (int p = 1; p < PAIRS; ++p) x = fmaxf(x, xl[p][h]);
+      mref[h] = max_lanes32(x);
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float mx = group_max<16>(t[h]);
-            const float pm = fmaxf(lane_f(mx, 0), lane_f(mx, 16));
-            if (pm > 0.0f) {
-              const float al = __builtin_amdgcn_exp2f(-pm);
-              mref[h] += pm;
-              t[h] -= pm;
-              lsum[h] *= al;
-              if (rq == h) alpha_me = al;
-            }
-          }
+      for (int p = 0; p < PAIRS; ++p)
+        pv[p][h] = __builtin_amdgcn_exp2f(xl[p][h] - mref[h]);  // exp2(-inf) = 0 for empty slots
+    }
+    // 5. P to the A fragments of P.V (slot 4u + g of tile j/4 is k index
+    //    8g + 4(j/4) + u), every pair's before any P.V, so that only the
+    //    value permutes and the P.V products wait for the values
+    bf16x8_t a_p[PAIRS];
 #pragma unroll
-          for (int e = 0; e < NE; ++e) {
-            oacc[e][0] *= alpha_me;
-            oacc[e][1] *= alpha_me;
-          }
-        }
-      }
-      float pv[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        pv[h] = __builtin_amdgcn_exp2f(t[h]);  // exp2(-inf) = 0 for empty slots
-        lsum[h] += pv[h];
-      }
-      // 5. P to the A fragments of P.V: slot 4u + g of tile j/4 is k index
-      //    8g + 4(j/4) + u
+    for (int p = 0; p < PAIRS; ++p) {
       if (rq < 2) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) lds.s_p[wave][h][rq][n & 3][n >> 2] = pv[h];
+        for (int h = 0; h < G; ++h) lds.s_p[wave][h][rq][n & 3][n >> 2] = pv[p][h];
       }
       __builtin_amdgcn_wave_barrier();
       const float4 x0 = *reinterpret_cast<const float4*>(pa0);
@@ -922,8 +927,16 @@ __device__ __forceinline__ void attend_pairs_body(const AttendArgs& a, const int
         const float w1 = xs[2 * d + 1] - __uint_as_float(u1 & lo_mask);
         af[d] = __builtin_amdgcn_perm(__float_as_uint(w1), __float_as_uint(w0), 0x07060302u);
       }
-      bf16x8_t a_p;
-      __builtin_memcpy(&a_p, af, 16);
+      __builtin_memcpy(&a_p[p], af, 16);
+      lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_p[p], ones, lacc, 0, 0, 0);
+      // the next pair's P overwrites s_p: every lane has read this pair's
+      __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int p = 0; p < PAIRS; ++p) {
+      // each pair's P.V stays after the previous pair's (it waits only for
+      // its own values)
+      __builtin_amdgcn_sched_barrier(0);
       // 6. O += P.V: B fragment of lane (n, g) = value dim NE*n + e of the
       //    pair's slots 4u + g of both tiles, from this lane's own rows
 #pragma unroll
@@ -937,27 +950,25 @@ __device__ __forceinline__ void attend_pairs_body(const AttendArgs& a, const int
         bw[3] = __builtin_amdgcn_perm(vw[2 * p + 1][3][wi], vw[2 * p + 1][2][wi], sel);
         bf16x8_t bv;
         __builtin_memcpy(&bv, bw, 16);
-        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_p, bv, oacc[e], 0, 0, 0);
+        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_p[p], bv, oacc[e], 0, 0, 0);
       }
     }
     // the wave's (reference, sum) of head rq and its O rows
-    float m_r = mref[0], l_r = 0.0f;
+    float m_r = mref[0];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float s = group_sum<16>(lsum[h]);
-      const float lh = lane_f(s, 0) + lane_f(s, 16);
-      if (h == 0) l_r = lh;
-      if (rq == h) {
-        m_r = mref[h];
-        l_r = lh;
-      }
-    }
+    for (int h = 1; h < G; ++h)
+      if (rq == h) m_r = mref[h];
     m_me = m_r;
-    l_me = l_r;
+    l_me = lacc[0] + lacc[1];
 #pragma unroll
     for (int e = 0; e < NE; ++e) mine[e] = oacc[e][0] + oacc[e][1];
   }
   if (nw > 1) {
+    // merge of the waves: every wave's O rows, reference and sum to LDS;
+    // then wave h merges head h: lane j < nw takes wave j's reference and
+    // sum, the head's reference M = their maximum, wave j's weight
+    // 2^(m_j - M) (over L = the weighted sum of the sums when the result is
+    // final), and lane d sums value dimension d of the rows, weighted
     __builtin_amdgcn_wave_barrier();  // the wave's key-tile reads are done
     if (rq < G) {
       float* so = &lds.w[wave].o[rq][NE * n];
@@ -965,44 +976,40 @@ __device__ __forceinline__ void attend_pairs_body(const AttendArgs& a, const int
       for (int e = 0; e < NE; e += 4)
         *reinterpret_cast<float4*>(so + e) = make_float4(mine[e], mine[e + 1], mine[e + 2], mine[e + 3]);
       if (n == 0) {
-        lds.s_ml[wave][0][rq] = m_me;
-        lds.s_ml[wave][1][rq] = l_me;
+        lds.s_m[rq][wave] = m_me;
+        lds.s_l[rq][wave] = l_me;
       }
     }
     __syncthreads();
-    for (int t = threadIdx.x; t < G * DV; t += 64 * nw) {
-      const int h = t / DV;
-      const int dim = t % DV;
-      // unrolled over the largest workgroup so all LDS reads issue together
-      float mw[kMaxPairWaves], lw[kMaxPairWaves], ow[kMaxPairWaves];
+    for (int h = wave; h < G; h += nw) {
+      const bool in = lane < nw;
+      const float mj = in ? lds.s_m[h][in ? lane : 0] : -INFINITY;
+      const float lj = in ? lds.s_l[h][in ? lane : 0] : 0.0f;
+      // lanes 0..15 hold every wave (nw <= 12): row 0's maximum and sum
+      int kx = ordered_key(mj);
+      kx = max(kx, dpp_i<kQuadXor1>(kx));
+      kx = max(kx, dpp_i<kQuadXor2>(kx));
+      kx = max(kx, dpp_i<kRowHalfMirror>(kx));
+      kx = max(kx, dpp_i<kRowMirror>(kx));
+      const float M = ordered_float(__builtin_amdgcn_readlane(kx, 0));  // finite: wave 0 has slots
+      const float wt = mj == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mj - M);
+      const float L = lane_f(group_sum<16>(wt * lj), 0);
+      const float wn = a.nsplit == 1 ? wt / L : wt;
+      float wj[kMaxPairWaves];
 #pragma unroll
-      for (int w = 0; w < kMaxPairWaves; ++w) {
-        const bool in = w < nw;
-        mw[w] = in ? lds.s_ml[w][0][h] : -INFINITY;
-        lw[w] = in ? lds.s_ml[w][1][h] : 0.0f;
-        ow[w] = in ? lds.w[w].o[h][dim] : 0.0f;
-      }
-      float Mx = -INFINITY;
+      for (int j = 0; j < kMaxPairWaves; ++j) wj[j] = lane_f(wn, j);
+      for (int d = lane; d < DV; d += 64) {
+        float Ox = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kMaxPairWaves; ++w) Mx = fmaxf(Mx, mw[w]);
-      float Lx = 0.0f, Ox = 0.0f;
-      if (Mx != -INFINITY) {
-#pragma unroll
-        for (int w = 0; w < kMaxPairWaves; ++w) {
-          const float wt = __builtin_amdgcn_exp2f(mw[w] - Mx);
-          Lx = fmaf(lw[w], wt, Lx);
-          Ox = fmaf(ow[w], wt, Ox);
+        for (int j = 0; j < kMaxPairWaves; ++j) {
+          const float o = lds.w[j].o[h][d];  // slots past the waves: dropped
+          Ox = fmaf(j < nw ? o : 0.0f, wj[j], Ox);
         }
+        dst_row[h * D + d] = Ox;
       }
-      if (a.nsplit == 1) {
-        dst_row[h * D + dim] = Ox / Lx;
-      } else {
-        float* pp = dst_row;
-        pp[h * D + dim] = Ox;
-        if (dim == 0) {
-          pp[G * D + h] = Mx;
-          pp[G * D + G + h] = Lx;
-        }
+      if (a.nsplit > 1 && lane == 0) {
+        dst_row[G * D + h] = M;
+        dst_row[G * D + G + h] = L;
       }
     }
     if (touch == 1.0f && a.n_slots < 0) dst_row[1] = 0.0f;  // never true: keeps the read
