@@ -1067,8 +1067,9 @@ __global__ __launch_bounds__(64 * kMaxPairWaves) void attend_pairs_kernel(Attend
 
 // The reads of attend_pairs_kernel without its arithmetic (a measurement
 // reference, not a step of the method): the same grid, the same slots per
-// wave, the same index loads and the same key and value row loads (whole
-// 128-byte lines, nontemporal buffer loads), folded with XOR; the fold is
+// wave, the same index loads and the same key and value row loads in the
+// same order (whole 128-byte lines, nontemporal buffer loads, every key row
+// before the value rows), folded with XOR; the fold is
 // stored only if it equals a constant it practically never equals.  Its
 // duration is what reading the selected rows alone takes on this device.
 template <int MODE, int PAIRS, int VH>
@@ -1103,19 +1104,29 @@ __global__ __launch_bounds__(64 * kMaxPairWaves) void gather_read_kernel(AttendA
     toff[i] = (uint32_t)slot_token<MODE, false>(a, row, b, s0 + 16 * i + n, s1, ok_unused) *
               row_bytes;
   }
+  // the key rows of every tile, then the value rows, as the attend requests them
+  uint32_t base[TILES][4];
+#pragma unroll
+  for (int i = 0; i < TILES; ++i)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) base[i][u] = (uint32_t)__shfl((int)toff[i], 4 * u + rq);
   uint32_t acc = 0;
 #pragma unroll
   for (int i = 0; i < TILES; ++i)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const uint32_t base = (uint32_t)__shfl((int)toff[i], 4 * u + rq);
-      const uint4 k = ld16_buf(rk, base + 16 * n);
+      const uint4 k = ld16_buf(rk, base[i][u] + 16 * n);
       acc ^= k.x ^ k.y ^ k.z ^ k.w;
+    }
+#pragma unroll
+  for (int i = 0; i < TILES; ++i)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
       if constexpr (VH == 1) {
-        const uint4 x = ld16_buf(rv, base + 16 * n);
+        const uint4 x = ld16_buf(rv, base[i][u] + 16 * n);
         acc ^= x.x ^ x.y ^ x.z ^ x.w;
       } else {
-        const uint2 x = ld8_buf(rv, base + DV * 2 * half + 8 * n);
+        const uint2 x = ld8_buf(rv, base[i][u] + DV * 2 * half + 8 * n);
         acc ^= x.x ^ x.y;
       }
     }
