@@ -651,10 +651,10 @@ __global__ __launch_bounds__(64 * max_waves<MODE>()) void attend_sparse_kernel(A
 // Per pair, Q.K gives each tile's logits in MFMA rows 0..3 (lanes 0..15);
 // one lane-row swap then puts the second tile's in lanes 16..31, so the
 // softmax runs on 32 lanes.  Its reference per head is the maximum of the
-// wave's logits, so exp2(logit - reference) <= 1 and nothing is rescaled;
-// row sums accumulate per lane and are reduced once at the end.  P.V runs on
-// MFMA as in the kernel above (P as a truncated bf16 pair hi + lo, V columns
-// assembled from the lane's own value rows by byte permutes).
+// wave's logits, so exp2(logit - reference) <= 1 and nothing is rescaled.
+// P.V runs on MFMA as in the kernel above (P as a truncated bf16 pair hi +
+// lo, V columns assembled from the lane's own value rows by byte permutes),
+// and the row sums are one more MFMA of the same P against a B of ones.
 constexpr int kMaxPairWaves = 12;
 
 // Position of 16-byte chunk x (dims [8x, 8x + 8)) of token t in a wave's
