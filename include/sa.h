@@ -443,7 +443,8 @@ sa_status sa_stream_read(const void* data, size_t bytes, uint32_t* sink, hipStre
 /* The reads of sa_sparse_decode without its arithmetic (a measurement
  * reference, not a step of the method): for the same descriptor, index kind
  * and index list, the same launch plan, index loads and key/value row loads
- * as the pair-pipelined gather-attend, folded with XOR into *sink only if
+ * as the pair-pipelined gather-attend, in the same order (every key row of a
+ * wave's slots before their value rows), folded with XOR into *sink only if
  * the fold hits a fixed constant.  Its duration is how long reading the
  * selected rows alone takes, the floor for that gather-attend launch.
  * Errors: as sa_sparse_decode for desc, k_cache, v_cache and the index
