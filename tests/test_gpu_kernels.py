@@ -240,6 +240,30 @@ def test_sparse_token_per_head(dtype, d, G, N, n_idx):
     check_out(out, want, dtype, "sparse per-head")
 
 
+@pytest.mark.parametrize("G,B,Hkv,N,n_idx,qmul", [
+    (1, 32, 4, 1024, 655, 1.0), (2, 32, 4, 1024, 655, 1.0), (4, 32, 4, 1024, 768, 1.0),
+    (2, 32, 4, 1024, 300, 8.0), (4, 32, 4, 1024, 33, 8.0), (2, 2, 4, 4096, 2048, 1.0),
+    (1, 2, 4, 4096, 1500, 8.0)])
+def test_pair_kernel_groups_and_plans(G, B, Hkv, N, n_idx, qmul):
+    """The pair-pipelined gather-attend at 1, 2 and 4 query heads per KV head,
+    in both of its plans: 128 whole rows with two workgroups per row (value
+    halves; one or two pairs per wave, a partial last wave, a full twelfth
+    wave) and 8 rows split over many workgroups with the combine; queries
+    scaled by 8 make most of a row's probabilities underflow against its
+    maximum."""
+    say("pair kernel", G, B, Hkv, N, n_idx, qmul)
+    q, k, v = _rand_cache(B, Hkv * G, Hkv, N, 128, "bf16", 50 + G + n_idx)
+    q = (q.to(torch.float32) * qmul).to(torch.bfloat16)
+    rng = np.random.default_rng(51 + n_idx)
+    idx = np.stack([np.stack([np.sort(rng.choice(N, n_idx, replace=False)) for _ in range(Hkv)])
+                    for _ in range(B)]).astype(np.int32)
+    out = T.sa_sparse_decode(q.to(dev()), k.to(dev()), v.to(dev()),
+                             torch.from_numpy(idx).to(dev())).cpu().numpy()
+    want = _oracle_out(_f64(q), _f64(k), _f64(v), [[idx[b, r] for r in range(Hkv)] for b in range(B)],
+                       G, O.default_scale(128))
+    check_out(out, want, "bf16", "pair kernel G=%d rows=%d n_idx=%d" % (G, B * Hkv, n_idx))
+
+
 def test_sparse_shared_and_unsorted_indices():
     say("sparse shared")
     B, Hkv, G, N, d, n_idx = 2, 4, 4, 4000, 128, 700
