@@ -33,7 +33,8 @@
 namespace sa {
 namespace {
 
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 256;  // indexer-score parts
+constexpr int kExactNT = 512;     // exact-score parts
 constexpr int kPartMax = 8192;         // longest part: the register select at 4 * 8 keys per thread
 constexpr int kPartAlign = 256;        // a multiple of every layout's tokens per iteration
 constexpr int kSelCand = kRankMax + 8; // threshold-bin candidates ranked in LDS
@@ -102,18 +103,19 @@ __device__ __forceinline__ void stream_part(int n, Load load, Reduce reduce) {
   }
 }
 
+template <int NT>
 struct PartLds {
-  SharedT<kSelThreads> sh;
+  SharedT<NT> sh;
   uint2 cand[kSelCand];
-  uint32_t s_wave[kSelThreads / 64];
+  uint32_t s_wave[NT / 64];
 };
 
 // The part's top-min(k, n) from its LDS scores (histogram already counted):
 // the index list itself for a one-part row, else (score, position)
 // candidates in position order.
-template <int G>
+template <int G, int NT>
 __device__ __forceinline__ void part_select(const SelArgs& a, const float* s_sc, int n, int row,
-                                            int part, int64_t t0, PartLds& l) {
+                                            int part, int64_t t0, PartLds<NT>& l) {
   auto lds_load = [&](int p0, float (&v)[G][4]) {
 #pragma unroll
     for (int j = 0; j < G; ++j) {
@@ -127,14 +129,14 @@ __device__ __forceinline__ void part_select(const SelArgs& a, const float* s_sc,
   const int32_t kk = std::min(a.k_sel, n);
   if (a.idx) {
     int32_t* out = a.idx + (int64_t)row * a.k_sel;
-    reg_row_topk<kSelThreads, G, true>(
+    reg_row_topk<NT, G, true>(
         lds_load, n, kk, [&](uint32_t slot, int32_t p) { out[slot] = p; }, l.sh, l.cand,
         l.s_wave);
   } else {
     const int64_t c0 = (int64_t)row * a.cstride + (int64_t)part * a.kcap;
     float* cv = a.cand_val + c0;
     int32_t* cp = a.cand_pos + c0;
-    reg_row_topk<kSelThreads, G, true>(
+    reg_row_topk<NT, G, true>(
         lds_load, n, kk,
         [&](uint32_t slot, int32_t p) {
           cv[slot] = s_sc[p];
@@ -144,21 +146,21 @@ __device__ __forceinline__ void part_select(const SelArgs& a, const float* s_sc,
   }
 }
 
-// Parts of at most 4 * G * 256 tokens (the register select holds 4 G keys
-// per thread).
-template <typename KT, int D, int U, int G>
-__global__ __launch_bounds__(kSelThreads) void select_part_kernel(SelArgs a) {
+// Parts of at most 4 * G * NT tokens (the register select holds 4 G keys
+// per thread) for workgroups of NT threads.
+template <typename KT, int D, int U, int G, int NT>
+__global__ __launch_bounds__(NT) void select_part_kernel(SelArgs a) {
   constexpr int EB = Elt<KT>::kBytes;
   constexpr int E = Elt<KT>::kPer16B;
   constexpr int LPR = D * EB / 16;
   constexpr int RPW = 64 / LPR;  // rows per wave load
   constexpr int per_wave_iter = RPW * U;
-  constexpr int per_iter = 4 * per_wave_iter;
+  constexpr int per_iter = (NT / 64) * per_wave_iter;
   static_assert(U <= LPR, "one storing lane per unrolled token");
-  static_assert(kSelThreads == 256 && kPartAlign % per_iter == 0, "whole iterations per part");
+  static_assert(kPartAlign % per_iter == 0, "whole iterations per part");
 
-  __shared__ __align__(16) float s_sc[4 * G * kSelThreads];
-  __shared__ PartLds l;
+  __shared__ __align__(16) float s_sc[4 * G * NT];
+  __shared__ PartLds<NT> l;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(kSelThreads) void select_part_kernel(SelArgs a) {
   __syncthreads();
 
   // ---- 2. top-min(k, n) of the part
-  part_select<G>(a, s_sc, n, row, part, t0, l);
+  part_select<G, NT>(a, s_sc, n, row, part, t0, l);
 }
 
 // The same part selection on indexer scores ("Flash Attention vs Sparse
@@ -225,12 +227,12 @@ __global__ __launch_bounds__(kSelThreads) void select_indexer_kernel(SelArgs a) 
   constexpr int LPR = DI * 2 / 16;
   constexpr int RPW = 64 / LPR;
   constexpr int per_wave_iter = RPW * U;
-  constexpr int per_iter = 4 * per_wave_iter;
+  constexpr int per_iter = (kSelThreads / 64) * per_wave_iter;
   static_assert(U <= LPR, "one storing lane per unrolled token");
-  static_assert(kSelThreads == 256 && kPartAlign % per_iter == 0, "whole iterations per part");
+  static_assert(kPartAlign % per_iter == 0, "whole iterations per part");
 
   __shared__ __align__(16) float s_sc[4 * G * kSelThreads];
-  __shared__ PartLds l;
+  __shared__ PartLds<kSelThreads> l;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -272,7 +274,7 @@ __global__ __launch_bounds__(kSelThreads) void select_indexer_kernel(SelArgs a) 
   };
   stream_part<per_iter, U>(n, load, reduce);
   __syncthreads();
-  part_select<G>(a, s_sc, n, row, part, t0, l);
+  part_select<G, kSelThreads>(a, s_sc, n, row, part, t0, l);
 }
 
 }  // namespace
@@ -325,26 +327,41 @@ void launch_indexer_part_h(const SelArgs& a, dim3 grid, hipStream_t s) {
   else launch_indexer_part<G, DI, 16>(a, grid, s);
 }
 
+// Exact-score parts: workgroups of kExactNT threads, each wave U token rows
+// per load (U scaled so that one iteration of the workgroup is kPartAlign
+// tokens or a divisor of it).
 template <int G>
-void launch_exact_part(const Cache& c, const SelArgs& a, dim3 grid, hipStream_t s) {
+void launch_exact_part_g(const Cache& c, const SelArgs& a, dim3 grid, hipStream_t s) {
+  constexpr int NT = kExactNT;
+  static_assert(NT == 256 || NT == 512, "four or eight waves");
+  const dim3 block(NT);
   if (c.kv_dtype == SA_BF16) {
     if (c.D == 64)
-      hipLaunchKernelGGL((select_part_kernel<bf16_t, 64, 8, G>), grid, dim3(kSelThreads), 0, s, a);
+      hipLaunchKernelGGL((select_part_kernel<bf16_t, 64, (NT == 256 ? 8 : 4), G, NT>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((select_part_kernel<bf16_t, 128, 16, G>), grid, dim3(kSelThreads), 0, s, a);
+      hipLaunchKernelGGL((select_part_kernel<bf16_t, 128, (NT == 256 ? 16 : 8), G, NT>), grid, block, 0, s, a);
   } else {
     if (c.D == 64)
-      hipLaunchKernelGGL((select_part_kernel<float, 64, 16, G>), grid, dim3(kSelThreads), 0, s, a);
+      hipLaunchKernelGGL((select_part_kernel<float, 64, (NT == 256 ? 16 : 8), G, NT>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((select_part_kernel<float, 128, 16, G>), grid, dim3(kSelThreads), 0, s, a);
+      hipLaunchKernelGGL((select_part_kernel<float, 128, 16, G, NT>), grid, block, 0, s, a);
   }
+}
+
+// Groups of four keys per thread that hold a part of L tokens: eight for
+// the longest parts, else the form that holds 4096 tokens.
+void launch_exact_part(const Cache& c, const SelArgs& a, dim3 grid, hipStream_t s) {
+  if (a.L > 4096)
+    launch_exact_part_g<8 * 256 / kExactNT>(c, a, grid, s);
+  else
+    launch_exact_part_g<4 * 256 / kExactNT>(c, a, grid, s);
 }
 
 template <int G>
 void launch_part(const Cache& c, const SelectIndexer* ix, const SelArgs& a, dim3 grid,
                  hipStream_t s) {
   if (!ix) {
-    launch_exact_part<G>(c, a, grid, s);
+    launch_exact_part(c, a, grid, s);
   } else if (ix->Di == 32) {
     launch_indexer_part_h<G, 32>(a, grid, s);
   } else if (ix->Di == 64) {
