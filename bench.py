@@ -3,9 +3,11 @@
 Workload (default): the Llama-3.1-8B-shaped decode step -- batch 16, 32 query
 / 8 KV heads, head_dim 128, bf16 KV cache of 32768 tokens per sequence, exact
 top-k per (sequence, KV head) at 50x sparsity (k = 655).  One step is one pass
-of the whole hot path through the C ABI:
-    sa_select (exact scoring fused with a per-part top-k, then the merge)
-    -> sa_sparse_decode (gather + split-K attend).
+of the whole hot path through the C ABI, the SPARSE layer call:
+    sa_decode_layer(SPARSE) = exact scoring fused with a per-part top-k, then
+    the merge of the parts' candidates and the gather-attend in one launch;
+the same step as two calls (sa_select -> sa_sparse_decode, the same index list
+and output) is timed beside it.
 Queries rotate over 8 pre-generated variants and the steps over 8 device
 copies of the cache (2.15 GB each, all resident in HBM before timing starts;
 --kv-replicas), so consecutive steps select different tokens and no step
@@ -13,7 +15,7 @@ finds the previous step's rows in cache.
 
 Timing: W untimed warmup steps, then K timed steps bracketed by
 torch.cuda.synchronize().  Each step is captured once per (query variant,
-cache copy) as a HIP graph of its three launches and replayed (a serving
+cache copy) as a HIP graph of its launches and replayed (a serving
 loop's form; --eager times plain launches instead); the bench checks that a
 replay selects and attends exactly as an eager step.
 
@@ -291,9 +293,9 @@ def traffic_report(fetch_db, write_db):
     lines = ["# HBM traffic per dispatch, calibrated byte counters",
              "#",
              "# commands (one counter per run, then this report):",
-             "#   rocprofv3 --pmc FETCH_SIZE -d %s -o %s -- python -u bench.py --profile"
+             "#   rocprofv3 --pmc FETCH_SIZE -d %s -o %s -- python3 bench.py --profile"
              % db_dir_name(fetch_db),
-             "#   rocprofv3 --pmc WRITE_SIZE -d %s -o %s -- python -u bench.py --profile"
+             "#   rocprofv3 --pmc WRITE_SIZE -d %s -o %s -- python3 bench.py --profile"
              % db_dir_name(write_db),
              "#   python bench.py --traffic %s %s" % (fetch_db, write_db),
              "# bench.py --profile runs three 1 GiB device-to-device copies (and 14 more make the",
@@ -1674,43 +1676,65 @@ def main():
         if ev is not None:
             ev[2].record()
 
+    # the same step as the library's SPARSE layer call: the fused selection's
+    # part kernel, then the merge of the parts' candidates and the
+    # gather-attend in one launch (merge_attend_kernel)
+    n_graph = N_QVAR * n_rep // math.gcd(N_QVAR, n_rep)
+    largs = [T.layer_args(qd[v % N_QVAR], kds[v % n_rep], vds[v % n_rep], T.SA_SCORE_EXACT, c.k,
+                          out=out)[0] for v in range(n_graph)]
+    lws = torch.empty(max(1, T.sa_layer_workspace_size(largs[0], T.SA_LAYER_SPARSE)),
+                      dtype=torch.uint8, device=dev)
+
+    def layer_step(i):
+        T.sa_decode_layer(largs[i % n_graph], T.SA_LAYER_SPARSE, idx, dev, lws)
+
     log("bench: warmup %d steps" % args.warmup)
     for i in range(args.warmup):
         step(i)
+        layer_step(i)
     torch.cuda.synchronize()
+    # the layer call selects and attends exactly as the two calls
+    step(0)
+    two_idx, two_out = idx.clone(), out.clone()
+    layer_step(0)
+    torch.cuda.synchronize()
+    assert torch.equal(two_idx, idx) and torch.equal(two_out, out), "layer call differs from the two calls"
 
     # the timed steps: each step captured once per (query variant, cache
-    # copy) as a HIP graph (the three launches of one decode step), replayed
-    # in turn
-    graphs = []
-    n_graph = N_QVAR * n_rep // math.gcd(N_QVAR, n_rep)
-    if not args.eager:
-        for v in range(n_graph):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(v)
-            graphs.append(g)
-        for i in range(args.warmup):
-            graphs[i % n_graph].replay()
+    # copy) as a HIP graph, replayed in turn; the layer call's graphs give
+    # ms_per_step, the two calls' graphs the two-call figure beside it
+    def timed(fn, name):
+        graphs = []
+        if not args.eager:
+            for v in range(n_graph):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    fn(v)
+                graphs.append(g)
+            for i in range(args.warmup):
+                graphs[i % n_graph].replay()
+            torch.cuda.synchronize()
+            # a replayed step selects and attends exactly as the eager one
+            graphs[0].replay()
+            g_idx, g_out = idx.clone(), out.clone()
+            fn(0)
+            torch.cuda.synchronize()
+            assert torch.equal(g_idx, idx) and torch.equal(g_out, out), \
+                "graph replay of the %s differs from eager" % name
+        log("bench: timing %d steps of the %s (%s)" % (args.steps, name,
+                                                      "eager" if args.eager else "graph replay"))
         torch.cuda.synchronize()
-        # a replayed step selects and attends exactly as the eager one
-        graphs[0].replay()
-        g_idx, g_out = idx.clone(), out.clone()
-        step(0)
+        t_start = time.perf_counter()
+        for i in range(args.steps):
+            if args.eager:
+                fn(i)
+            else:
+                graphs[i % n_graph].replay()
         torch.cuda.synchronize()
-        assert torch.equal(g_idx, idx) and torch.equal(g_out, out), "graph replay differs from eager"
+        return (time.perf_counter() - t_start) * 1e3 / args.steps
 
-    log("bench: timing %d steps (%s)" % (args.steps, "eager" if args.eager else "graph replay"))
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(args.steps):
-        if args.eager:
-            step(i)
-        else:
-            graphs[i % n_graph].replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    ms_step = wall * 1e3 / args.steps
+    ms_step = timed(layer_step, "SPARSE layer call")
+    ms_step_two = timed(step, "two calls")
 
     # The gather-attend alone (the headline): every (query variant, cache
     # copy) pair's own index set, selected once, then the n_graph attends
@@ -1947,8 +1971,8 @@ def main():
         "ms_per_step": round(ms_step, 4),
         "timing": ("value: the gather-attend alone, %d attends over %d cache copies captured back "
                    "to back in a HIP graph, replayed %d times between HIP events; ms_per_step and "
-                   "steps_per_s: the K timed decode steps (selection + gather-attend), each a "
-                   "replayed HIP graph" % (n_graph, n_rep, n_att_rep)),
+                   "steps_per_s: the K timed decode steps (the SPARSE layer call: exact selection "
+                   "+ gather-attend), each a replayed HIP graph" % (n_graph, n_rep, n_att_rep)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -1959,13 +1983,18 @@ def main():
                    "head_dim": c.head_dim, "ctx_len": c.ctx_len, "k": c.k,
                    "kv_dtype": c.dtype, "kv_replicas": n_rep, "parallelism": "single GPU"},
         "roofline": roof,
-        "step": {"what": "sa_select (fused exact scoring + part top-k, merge) -> sa_sparse_decode",
+        "step": {"what": "sa_decode_layer(SPARSE): the fused exact selection's part kernel "
+                         "(scores kept on chip, each part's top-k), then the merge of the parts' "
+                         "candidates and the gather-attend in one launch",
                  "ms_per_step": round(ms_step, 4), "steps_per_s": round(1e3 / ms_step, 1),
                  "gbps": round(step_total / (ms_step * 1e-3) / 1e9, 1),
                  "frac": round(step_total / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                  "bytes": step_total,
                  "timing": "eager launches" if args.eager else "each step a replayed HIP graph",
-                 "ms_per_step_eager_with_events": round(ms_step_eager, 4)},
+                 "two_calls": {"what": "sa_select -> sa_sparse_decode (the same index list and "
+                                       "output)", "ms_per_step": round(ms_step_two, 4),
+                               "steps_per_s": round(1e3 / ms_step_two, 1),
+                               "ms_per_step_eager_with_events": round(ms_step_eager, 4)}},
         "kernels": kernels,
         "sparse_over_dense_speedup": (round(ms_dense / ms_attend, 2) if ms_dense else None),
         "stream_read": stream,
