@@ -276,17 +276,15 @@ __global__ __launch_bounds__(kThreads) void score_block_kernel(BlockArgs a) {
 // ------------------------------------------------ block score + top-k
 // Block selection of a whole row in one workgroup: the row's block scores
 // (the same arithmetic as score_block_kernel, so the same fp32 values) from
-// its per-block key summaries, U passes of blocks with every summary load of
-// a pass group in flight, kept in LDS; then the register-resident top-k of
-// the row (reg_row_topk) writes the k best block ids, ascending -- one launch
-// instead of a score launch and a top-k launch.  With at most four query
-// heads per KV head (GM = 4) the query registers leave room for eight
-// passes in flight (U = 8: a row of up to 512 blocks of d = 128 in one round
-// of loads), else four.
+// its per-block key summaries, kSelBlkU passes of blocks with every summary
+// load of a pass group in flight, kept in LDS; then the register-resident
+// top-k of the row (reg_row_topk) writes the k best block ids, ascending --
+// one launch instead of a score launch and a top-k launch.
 constexpr int kSelBlkThreads = 1024;
 constexpr int kSelBlkMax = 4 * kSelBlkThreads;  // blocks per row at most
+constexpr int kSelBlkU = 4;
 
-template <typename KT, int D, int GM, int U>
+template <typename KT, int D>
 __global__ __launch_bounds__(kSelBlkThreads) void select_block_kernel(BlockArgs a, int32_t k,
                                                                      int32_t* __restrict__ idx) {
   constexpr int EB = Elt<KT>::kBytes;
@@ -305,31 +303,21 @@ __global__ __launch_bounds__(kSelBlkThreads) void select_block_kernel(BlockArgs 
   const int r = row % a.Hkv;
   auto off_of = [&](int j) { return (((int64_t)row * a.nb + j) * D) * EB + sl * 16; };
 
-  uint4 lmn[U], lmx[U];
+  uint4 lmn[kSelBlkU], lmx[kSelBlkU];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
+  for (int u = 0; u < kSelBlkU; ++u) {
     const int j = u * NG + grp;
     lmn[u] = j < a.nb ? ld16(a.kmin + off_of(j)) : make_uint4(0u, 0u, 0u, 0u);
     lmx[u] = j < a.nb ? ld16(a.kmax + off_of(j)) : make_uint4(0u, 0u, 0u, 0u);
   }
   float qp[E], qn[E];
-  float qv[GM][E];
-  {
-    const int64_t g0 = (int64_t)b * a.Hq + (int64_t)r * a.G;
-#pragma unroll
-    for (int g = 0; g < GM; ++g) {
-      const int64_t at = (g0 + (g < a.G ? g : 0)) * D + sl * E;
-      if (a.q_dtype == SA_BF16)
-        load_q_vec<E, true>(a.q, at, qv[g]);
-      else
-        load_q_vec<E, false>(a.q, at, qv[g]);
-    }
-  }
+  float qv[8][E];
+  load_q_group<E, D>(a.q, a.q_dtype, (int64_t)b * a.Hq + (int64_t)r * a.G, a.G, sl * E, qv);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     float p = 0.0f, n = 0.0f;
 #pragma unroll
-    for (int g = 0; g < GM; ++g) {
+    for (int g = 0; g < 8; ++g) {
       const float v = g < a.G ? qv[g][e] : 0.0f;
       p += fmaxf(v, 0.0f);
       n += fminf(v, 0.0f);
@@ -337,14 +325,14 @@ __global__ __launch_bounds__(kSelBlkThreads) void select_block_kernel(BlockArgs 
     qp[e] = p;
     qn[e] = n;
   }
-  for (int j0 = 0; j0 < a.nb; j0 += U * NG) {
+  for (int j0 = 0; j0 < a.nb; j0 += kSelBlkU * NG) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < kSelBlkU; ++u) {
       const int j = j0 + u * NG + grp;
       float mn[E], mx[E];
       unpack16<KT>(lmn[u], mn);
       unpack16<KT>(lmx[u], mx);
-      const int jn = j + U * NG;  // the next group's block, loaded now
+      const int jn = j + kSelBlkU * NG;  // the next group's block, loaded now
       if (jn < a.nb) {
         lmn[u] = ld16(a.kmin + off_of(jn));
         lmx[u] = ld16(a.kmax + off_of(jn));
@@ -582,23 +570,6 @@ hipError_t launch_score_block(const Cache& c, int32_t bs, const void* q, const v
   return hipGetLastError();
 }
 
-template <int GM, int U>
-void launch_select_block_g(const Cache& c, const BlockArgs& a, dim3 grid, int32_t k, int32_t* idx,
-                           hipStream_t s) {
-  const dim3 block(kSelBlkThreads);
-  if (c.kv_dtype == SA_BF16) {
-    if (c.D == 64)
-      hipLaunchKernelGGL((select_block_kernel<bf16_t, 64, GM, U>), grid, block, 0, s, a, k, idx);
-    else
-      hipLaunchKernelGGL((select_block_kernel<bf16_t, 128, GM, U>), grid, block, 0, s, a, k, idx);
-  } else {
-    if (c.D == 64)
-      hipLaunchKernelGGL((select_block_kernel<float, 64, GM, U>), grid, block, 0, s, a, k, idx);
-    else
-      hipLaunchKernelGGL((select_block_kernel<float, 128, GM, U>), grid, block, 0, s, a, k, idx);
-  }
-}
-
 bool select_block_fits(const Cache& c, int32_t bs) {
   return (c.N + bs - 1) / bs <= kSelBlkMax && c.G <= 8;
 }
@@ -615,11 +586,18 @@ hipError_t launch_select_block(const Cache& c, int32_t bs, const void* q, const 
   a.G = c.G;
   a.nb = (int32_t)((c.N + bs - 1) / bs);
   a.scores = nullptr;
-  const dim3 grid((unsigned)(c.B * c.Hkv));
-  if (c.G <= 4)
-    launch_select_block_g<4, 8>(c, a, grid, k, idx, s);
-  else
-    launch_select_block_g<8, 4>(c, a, grid, k, idx, s);
+  const dim3 grid((unsigned)(c.B * c.Hkv)), block(kSelBlkThreads);
+  if (c.kv_dtype == SA_BF16) {
+    if (c.D == 64)
+      hipLaunchKernelGGL((select_block_kernel<bf16_t, 64>), grid, block, 0, s, a, k, idx);
+    else
+      hipLaunchKernelGGL((select_block_kernel<bf16_t, 128>), grid, block, 0, s, a, k, idx);
+  } else {
+    if (c.D == 64)
+      hipLaunchKernelGGL((select_block_kernel<float, 64>), grid, block, 0, s, a, k, idx);
+    else
+      hipLaunchKernelGGL((select_block_kernel<float, 128>), grid, block, 0, s, a, k, idx);
+  }
   return hipGetLastError();
 }
 

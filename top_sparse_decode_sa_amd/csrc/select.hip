@@ -13,8 +13,8 @@
 // Here the scores never leave the chip:
 //
 //  1. select_part_kernel: a row is cut into parts of L <= 8192 tokens; one
-//     256-thread workgroup streams its part's keys (the score kernel's
-//     arithmetic, bit for bit: group_query_sum, row_dot), keeps the part's
+//     workgroup (256 or 512 threads) streams its part's keys (the score
+//     kernel's arithmetic, bit for bit: group_query_sum, row_dot), keeps the part's
 //     scores in LDS, then runs the register-resident radix select
 //     (reg_row_topk) on them and writes the part's top-min(k, part length)
 //     as (score, position) candidates, in position order.
@@ -33,8 +33,8 @@
 namespace sa {
 namespace {
 
-constexpr int kSelThreads = 256;  // indexer-score parts
-constexpr int kExactNT = 512;     // exact-score parts
+constexpr int kIndexerNT = 512;  // threads of an indexer-score part
+constexpr int kChipCUs = 256;    // MI355X compute units
 constexpr int kPartMax = 8192;         // longest part: the register select at 4 * 8 keys per thread
 constexpr int kPartAlign = 256;        // a multiple of every layout's tokens per iteration
 constexpr int kSelCand = kRankMax + 8; // threshold-bin candidates ranked in LDS
@@ -222,17 +222,17 @@ __global__ __launch_bounds__(NT) void select_part_kernel(SelArgs a) {
 // Attention", DSA Stage 1): row `row` of the indexer tensors, its keys read
 // by lane groups of DI/8 lanes, each token scored by indexer_token (the same
 // arithmetic as the indexer scoring kernel).
-template <int DI, int HP, int U, int G>
-__global__ __launch_bounds__(kSelThreads) void select_indexer_kernel(SelArgs a) {
+template <int DI, int HP, int U, int G, int NT>
+__global__ __launch_bounds__(NT) void select_indexer_kernel(SelArgs a) {
   constexpr int LPR = DI * 2 / 16;
   constexpr int RPW = 64 / LPR;
   constexpr int per_wave_iter = RPW * U;
-  constexpr int per_iter = (kSelThreads / 64) * per_wave_iter;
+  constexpr int per_iter = (NT / 64) * per_wave_iter;
   static_assert(U <= LPR, "one storing lane per unrolled token");
   static_assert(kPartAlign % per_iter == 0, "whole iterations per part");
 
-  __shared__ __align__(16) float s_sc[4 * G * kSelThreads];
-  __shared__ PartLds<kSelThreads> l;
+  __shared__ __align__(16) float s_sc[4 * G * NT];
+  __shared__ PartLds<NT> l;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kSelThreads) void select_indexer_kernel(SelArgs a) 
   };
   stream_part<per_iter, U>(n, load, reduce);
   __syncthreads();
-  part_select<G, kSelThreads>(a, s_sc, n, row, part, t0, l);
+  part_select<G, NT>(a, s_sc, n, row, part, t0, l);
 }
 
 }  // namespace
@@ -313,11 +313,16 @@ SelectPlan plan_select(const Cache& c, int32_t k) {
 
 namespace {
 
+// Indexer-score parts: workgroups of kIndexerNT threads; U as for 256
+// threads, halved per doubling of the waves (one workgroup iteration stays
+// within kPartAlign tokens), at least 1.
 template <int G, int DI, int HP>
 void launch_indexer_part(const SelArgs& a, dim3 grid, hipStream_t s) {
+  constexpr int NT = kIndexerNT;
   constexpr int LPR = DI * 2 / 16;
-  constexpr int U = HP >= 16 ? (LPR < 4 ? LPR : 4) : (LPR < 8 ? LPR : 8);
-  hipLaunchKernelGGL((select_indexer_kernel<DI, HP, U, G>), grid, dim3(kSelThreads), 0, s, a);
+  constexpr int U256 = HP >= 16 ? (LPR < 4 ? LPR : 4) : (LPR < 8 ? LPR : 8);
+  constexpr int U = U256 * 256 / NT > 0 ? U256 * 256 / NT : 1;
+  hipLaunchKernelGGL((select_indexer_kernel<DI, HP, U, G, NT>), grid, dim3(NT), 0, s, a);
 }
 
 template <int G, int DI>
@@ -327,12 +332,11 @@ void launch_indexer_part_h(const SelArgs& a, dim3 grid, hipStream_t s) {
   else launch_indexer_part<G, DI, 16>(a, grid, s);
 }
 
-// Exact-score parts: workgroups of kExactNT threads, each wave U token rows
-// per load (U scaled so that one iteration of the workgroup is kPartAlign
-// tokens or a divisor of it).
-template <int G>
+// Exact-score parts: workgroups of NT threads, each wave U token rows per
+// load (U scaled so that one iteration of the workgroup is kPartAlign tokens
+// or a divisor of it).
+template <int G, int NT>
 void launch_exact_part_g(const Cache& c, const SelArgs& a, dim3 grid, hipStream_t s) {
-  constexpr int NT = kExactNT;
   static_assert(NT == 256 || NT == 512, "four or eight waves");
   const dim3 block(NT);
   if (c.kv_dtype == SA_BF16) {
@@ -348,13 +352,27 @@ void launch_exact_part_g(const Cache& c, const SelArgs& a, dim3 grid, hipStream_
   }
 }
 
-// Groups of four keys per thread that hold a part of L tokens: eight for
-// the longest parts, else the form that holds 4096 tokens.
-void launch_exact_part(const Cache& c, const SelArgs& a, dim3 grid, hipStream_t s) {
+// Groups of four keys per thread that hold a part of L tokens: eight (at
+// 256 threads) for the longest parts, else the form that holds 4096 tokens.
+template <int NT>
+void launch_exact_part_nt(const Cache& c, const SelArgs& a, dim3 grid, hipStream_t s) {
   if (a.L > 4096)
-    launch_exact_part_g<8 * 256 / kExactNT>(c, a, grid, s);
+    launch_exact_part_g<8 * 256 / NT, NT>(c, a, grid, s);
   else
-    launch_exact_part_g<4 * 256 / kExactNT>(c, a, grid, s);
+    launch_exact_part_g<4 * 256 / NT, NT>(c, a, grid, s);
+}
+
+// Parts that all run at once (two 512-thread workgroups per CU) take eight
+// waves each, so the key stream has twice the waves and each part's top-k
+// half the keys per thread (llama32k, 512 parts: 176 against 181 us for
+// sa_select); grids of several rounds keep 256-thread workgroups, three per
+// CU, whose part top-k overlaps the other workgroups' streams (batch128k,
+// 16384 parts: 5.51 against 5.65 ms at 100x).
+void launch_exact_part(const Cache& c, const SelArgs& a, dim3 grid, hipStream_t s) {
+  if ((int64_t)grid.x * grid.y <= 2 * kChipCUs)
+    launch_exact_part_nt<512>(c, a, grid, s);
+  else
+    launch_exact_part_nt<256>(c, a, grid, s);
 }
 
 template <int G>
@@ -430,9 +448,9 @@ hipError_t launch_select(const Cache& c, const SelectPlan& p, const void* q, con
   }
   const dim3 grid((unsigned)p.P, (unsigned)rows);
   if (p.L > 4096)
-    launch_part<8>(c, ix, a, grid, s);
+    launch_part<8 * 256 / kIndexerNT>(c, ix, a, grid, s);
   else
-    launch_part<4>(c, ix, a, grid, s);
+    launch_part<4 * 256 / kIndexerNT>(c, ix, a, grid, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.P == 1) return e;
   if (ma && attended && (int64_t)ma->c.B * ma->c.Hkv == rows &&
