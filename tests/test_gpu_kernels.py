@@ -458,7 +458,8 @@ def test_tiny_config_end_to_end():
 
 @pytest.mark.parametrize("dtype,d,G,B,N,k", [
     ("bf16", 128, 4, 2, 3000, 61), ("bf16", 128, 4, 40, 2000, 40), ("bf16", 128, 1, 2, 777, 100),
-    ("f32", 64, 8, 1, 1500, 33), ("bf16", 64, 2, 2, 999, 999)])
+    ("f32", 64, 8, 1, 1500, 33), ("bf16", 64, 2, 2, 999, 999), ("f32", 128, 4, 2, 2500, 50),
+    ("f32", 64, 2, 3, 1300, 20)])
 def test_per_query_head_selection(dtype, d, G, B, N, k):
     """Every query head scores, selects and attends on its own: scores
     against the oracle, sa_topk bit-exact on the GPU's scores, outputs

@@ -32,6 +32,15 @@ inline Cache per_q_head_view(const Cache& c) {
   return v;
 }
 
+// Rows of the per-query-head view that read one KV row (its query heads:
+// kv_div), when 2 or 4: the exact scoring reads each key row once for all
+// of them.  1 otherwise (scored row by row; eight queries per key load
+// would not fit the registers).
+inline int per_q_head_shared_rows(const Cache& c) {
+  const bool view = c.G == 1 && c.kv_div > 1 && c.Hkv % c.kv_div == 0;
+  return view && (c.kv_div == 2 || c.kv_div == 4) ? c.kv_div : 1;
+}
+
 // ------------------------------------------------------------- scoring
 hipError_t launch_score_exact(const Cache& c, const void* q, const void* k, float* scores,
                               hipStream_t s);

@@ -122,6 +122,100 @@ __global__ __launch_bounds__(kThreads) void score_exact_kernel(ExactArgs a) {
   }
 }
 
+// Per-query-head scores of HM view rows that read the same KV row (the
+// per-query-head view: G = 1, rows r0 .. r0 + HM - 1 read KV head r0 /
+// kv_div): each loaded piece of a key row is dotted with the HM queries, so
+// the key cache is read once instead of HM times.  Row h's query values are
+// (0 + q_h) * scale and its dot products row_dot's, the arithmetic of
+// score_exact_kernel on one view row (group_query_sum of one head), so the
+// scores are the same fp32 values bit for bit.
+template <typename KT, int D, int U, int HM>
+__global__ __launch_bounds__(kThreads) void score_exact_heads_kernel(ExactArgs a) {
+  constexpr int EB = Elt<KT>::kBytes;
+  constexpr int E = Elt<KT>::kPer16B;
+  constexpr int LPR = D * EB / 16;
+  constexpr int RPW = 64 / LPR;  // rows per wave load
+  static_assert(U <= LPR, "one storing lane per unrolled token");
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lg = (tid & 63) / LPR;
+  const int sl = tid % LPR;
+  const int row0 = blockIdx.y * HM;  // first view row of the group
+  const int b = row0 / a.Hkv;
+  const int r0 = row0 % a.Hkv;
+
+  float qs[HM][E];
+#pragma unroll
+  for (int h = 0; h < HM; ++h) {
+    float qv[E];
+    const int64_t at = ((int64_t)b * a.Hq + r0 + h) * D + sl * E;
+    if (a.q_dtype == SA_BF16)
+      load_q_vec<E, true>(a.q, at, qv);
+    else
+      load_q_vec<E, false>(a.q, at, qv);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float acc = 0.0f;
+      acc += qv[e];
+      qs[h][e] = acc * a.scale;
+    }
+  }
+
+  const uint8_t* kbase = a.k + ((int64_t)b * a.sb + (int64_t)(r0 / a.kv_div) * a.sh) * EB + sl * 16;
+  const int64_t row_bytes = a.st * EB;
+  float* srow = a.scores + (int64_t)row0 * a.N;
+
+  constexpr int per_wave_iter = RPW * U;
+  constexpr int per_iter = 4 * per_wave_iter;
+  constexpr int kIters = kScoreTile / per_iter;
+  static_assert(kScoreTile % per_iter == 0, "whole iterations per tile");
+  const int64_t t_tile = (int64_t)blockIdx.x * kScoreTile;
+  const int64_t t_end = min(t_tile + (int64_t)kScoreTile, a.N);
+  auto load = [&](int64_t base, uint4 (&kw)[U], bool clamp) {
+    const int64_t wbase = base + wave * per_wave_iter + lg;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int64_t t = wbase + u * RPW;
+      if (clamp) t = std::min<int64_t>(t, t_end - 1);
+      kw[u] = ld16_nt(kbase + t * row_bytes);
+    }
+  };
+  auto reduce = [&](int64_t base, const uint4 (&kw)[U], bool check) {
+    float mine[HM];
+#pragma unroll
+    for (int h = 0; h < HM; ++h) mine[h] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int h = 0; h < HM; ++h) {
+        const float acc = row_dot<KT, LPR, E>(kw[u], qs[h]);
+        if (sl == u) mine[h] = acc;
+      }
+    const int64_t t = base + wave * per_wave_iter + sl * RPW + lg;
+    if (sl < U && (!check || t < t_end)) {
+#pragma unroll
+      for (int h = 0; h < HM; ++h) __builtin_nontemporal_store(mine[h], srow + (int64_t)h * a.N + t);
+    }
+  };
+  if (t_end - t_tile == kScoreTile) {
+    uint4 kb[2][U];
+    load(t_tile, kb[0], false);
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      if (i + 1 < kIters) load(t_tile + (i + 1) * per_iter, kb[(i + 1) & 1], false);
+      __builtin_amdgcn_sched_barrier(0);
+      reduce(t_tile + i * per_iter, kb[i & 1], false);
+    }
+  } else {
+    for (int64_t base = t_tile; base < t_end; base += per_iter) {
+      uint4 kw[U];
+      load(base, kw, true);
+      reduce(base, kw, true);
+    }
+  }
+}
+
 // -------------------------------------------------------- block summaries
 
 struct SumArgs {
@@ -479,6 +573,24 @@ hipError_t launch_indexer_di(const IndexerArgs& a, dim3 grid, hipStream_t s) {
   return launch_indexer_hp<DI, 16>(a, grid, s);
 }
 
+// HM view rows per workgroup row, each wave U token rows per load.
+template <int HM>
+hipError_t launch_score_heads(const Cache& c, const ExactArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((c.N + kScoreTile - 1) / kScoreTile), (unsigned)(c.B * c.Hkv / HM));
+  if (c.kv_dtype == SA_BF16) {
+    if (c.D == 64)
+      hipLaunchKernelGGL((score_exact_heads_kernel<bf16_t, 64, 4, HM>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((score_exact_heads_kernel<bf16_t, 128, 8, HM>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    if (c.D == 64)
+      hipLaunchKernelGGL((score_exact_heads_kernel<float, 64, 8, HM>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((score_exact_heads_kernel<float, 128, 8, HM>), grid, dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_score_exact(const Cache& c, const void* q, const void* k, float* scores,
@@ -497,6 +609,10 @@ hipError_t launch_score_exact(const Cache& c, const void* q, const void* k, floa
   a.N = c.N;
   a.scale = c.scale;
   a.scores = scores;
+  if (per_q_head_shared_rows(c) > 1) {
+    if (per_q_head_shared_rows(c) == 2) return launch_score_heads<2>(c, a, s);
+    return launch_score_heads<4>(c, a, s);
+  }
   const dim3 grid((unsigned)((c.N + kScoreTile - 1) / kScoreTile), (unsigned)(c.B * c.Hkv));
   if (c.kv_dtype == SA_BF16) {
     if (c.D == 64)

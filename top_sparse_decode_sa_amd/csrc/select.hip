@@ -300,8 +300,11 @@ SelectPlan plan_select(const Cache& c, int32_t k) {
   // fused when the candidates are at most a quarter of the row and fit the
   // merge (measured: at 4 parts of 8192 tokens the fused path is faster
   // from 20x sparsity on, slower at 10x, where each part keeps 40% of its
-  // tokens); one part needs no merge
-  p.fused = p.P == 1 || (p.C <= kMergeMax && 4 * p.C <= c.N);
+  // tokens); one part needs no merge.  Per-query-head rows (several view
+  // rows on one KV row) split into parts take the unfused path: their
+  // scoring reads each key row once for all of the KV head's query heads,
+  // where the part kernel would read it once per query head.
+  p.fused = p.P == 1 || (p.C <= kMergeMax && 4 * p.C <= c.N && per_q_head_shared_rows(c) == 1);
   if (!p.fused) {
     p.ws_bytes = align_up((size_t)rows * c.N * sizeof(float), 256) +
                  align_up(topk_workspace_bytes(rows, c.N, k), 256);
