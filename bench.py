@@ -45,8 +45,9 @@ all-core oracle baseline; --block61k and --indexer1m are aliases), --sweep
 (full step with four selection front ends against dense decode at 2x-500x
 on the llama32k and batch128k shapes), --hylra (layer-reuse plans over 8
 layers), --offload (selected blocks fetched from a pinned host cache),
---nscale (32K-128K tokens at fixed k); --profile (a short run for
-rocprofv3), --traffic and --summarize (reports from its results).
+--nscale (32K-128K tokens at fixed k), --perhead (per-query-head index
+sets); --profile (a short run for rocprofv3), --traffic and --summarize
+(reports from its results).
 """
 from __future__ import annotations
 
@@ -118,6 +119,11 @@ def parse():
                         "128K tokens with k = 655; the gather-attend moves the same bytes at every "
                         "N while selection and dense decode grow with N; prints a table and one "
                         "JSON line")
+    p.add_argument("--perhead", action="store_true",
+                   help="per-query-head index sets on the llama32k workload: each query head "
+                        "selects its own top-655 and attends over it ([B, Hq, k]); the cold "
+                        "gather-attend, the step, the SPARSE layer call, the per-KV-head step "
+                        "and dense decode; one JSON line")
     p.add_argument("--indexer1m", action="store_true", help="same as --workload indexer1m")
     p.add_argument("--block61k", action="store_true", help="same as --workload block61k")
     p.add_argument("--theta", type=float, default=0.35,
@@ -1098,6 +1104,169 @@ def bench_batch128k(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_perhead(args):
+    """Per-query-head index sets on the llama32k workload (batch 16, 32/8
+    heads, d 128, bf16, 32768 tokens, k = 655): every query head scores the
+    cache with its own query (SA_SCORE_EXACT_PER_Q_HEAD), keeps its own top-655
+    and attends over its own set (SA_IDX_TOKEN_PER_Q_HEAD, [B, Hq, k]); beside
+    it the per-KV-head step on the same inputs and dense decode.  A query
+    head's gather is 655 key and value rows, so one step gathers four times
+    the per-KV-head bytes (171.7 MB), which fits the 256 MB last-level cache:
+    `value` is the median cache-cold single launch after a 1 GiB read, beside
+    a cold streaming read of the same byte count."""
+    import sa_synth as S
+
+    name = "llama32k"
+    c = S.CONFIGS[name]
+    import torch
+    import top_sparse_decode_sa_amd as T
+
+    T.lib()
+    dev = torch.device("cuda", 0)
+    w = S.Workload(name, args.seed)
+    B, Hq, Hkv, d, k = c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.k
+    log("perhead: generating %s (%.2f GB of KV)" % (name, c.kv_bytes() / 1e9))
+    kd, vd, gen_s, up_s = upload_kv(w, 0, dev)
+    qd = [torch.from_numpy(w.q(0, qvar=v)).view(torch.bfloat16).to(dev) for v in range(2)]
+    idx_q = torch.empty((B, Hq, k), dtype=torch.int32, device=dev)
+    idx_kv = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    n_steps, n_warm = max(3, min(args.steps, 20)), max(1, min(args.warmup, 3))
+
+    def select(i=0):
+        T.sa_select(qd[i % 2], kd, k, T.SA_SCORE_EXACT_PER_Q_HEAD, idx_out=idx_q)
+
+    def attend(i=0):
+        T.sa_sparse_decode(qd[i % 2], kd, vd, idx_q, index_kind=T.SA_IDX_TOKEN_PER_Q_HEAD, out=out)
+
+    largs = [T.layer_args(qd[v], kd, vd, T.SA_SCORE_EXACT_PER_Q_HEAD, k, out=out)[0] for v in range(2)]
+    lws = torch.empty(max(1, T.sa_layer_workspace_size(largs[0], T.SA_LAYER_SPARSE)),
+                      dtype=torch.uint8, device=dev)
+
+    def layer(i=0):
+        T.sa_decode_layer(largs[i % 2], T.SA_LAYER_SPARSE, idx_q, dev, lws)
+
+    def kv_step(i=0):
+        T.sa_select(qd[i % 2], kd, k, idx_out=idx_kv)
+        T.sa_sparse_decode(qd[i % 2], kd, vd, idx_kv, out=out)
+
+    for i in range(n_warm):
+        select(i)
+        attend(i)
+        layer(i)
+        kv_step(i)
+    torch.cuda.synchronize()
+    # the layer call selects and attends exactly as the two calls
+    select(0)
+    attend(0)
+    two_idx, two_out = idx_q.clone(), out.clone()
+    layer(0)
+    torch.cuda.synchronize()
+    assert torch.equal(two_idx, idx_q) and torch.equal(two_out, out), "layer call differs"
+    assert T.sa_check_indices(qd[0], kd, idx_q, index_kind=T.SA_IDX_TOKEN_PER_Q_HEAD).tolist() == [0, 0]
+    log("perhead: timing %d steps" % n_steps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_steps)]
+    torch.cuda.synchronize()
+    for i in range(n_steps):
+        ev[i][0].record()
+        select(i)
+        ev[i][1].record()
+        attend(i)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    us_sel = sum(e[0].elapsed_time(e[1]) for e in ev) / n_steps * 1e3
+    us_att_step = sum(e[1].elapsed_time(e[2]) for e in ev) / n_steps * 1e3
+    us_layer = _ev_us(lambda: layer(1), n_steps, warm=2)
+    us_kv_step = _ev_us(lambda: kv_step(1), n_steps, warm=2)
+    att_bytes = 2 * B * Hq * k * d * c.elt + B * Hq * k * 4 + B * Hq * d * (c.elt + 4)
+    sbuf, stream = _stream_floor(att_bytes, dev)
+    cold = _cold_us({"attend": attend, "stream": stream}, max(5, args.cold_iters), dev)
+    del sbuf
+    dout = torch.empty_like(out)
+    us_dense = _ev_us(lambda: T.sa_dense_decode(qd[0], kd, vd, out=dout), 3, warm=1)
+    nb = step_bytes(c)
+    # the selection's algorithmic bytes: the keys read once (one scoring
+    # pass serves a KV head's query heads), the queries, every query head's
+    # scores written and read back by the top-k, the index lists written
+    sel_bytes = (B * Hkv * c.ctx_len * d * c.elt + B * Hq * d * c.elt + 2 * B * Hq * c.ctx_len * 4
+                 + B * Hq * k * 4)
+    att = _rate(att_bytes, cold["attend"])
+    kernels = {"sparse_attend_cold": att,
+               "stream_read_same_bytes_cold": _rate(att_bytes // 16 * 16, cold["stream"]),
+               "sparse_attend_in_step": _rate(att_bytes, us_att_step),
+               "select": _rate(sel_bytes, us_sel),
+               "dense_decode": _rate(nb["dense_decode"], us_dense)}
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = perhead_cpu_baseline(w, att_bytes, args.cpu_seconds)
+    line = _line("llama32k", c, args, att,
+                 "value: median of %d cache-cold single per-query-head gather-attend launches "
+                 "(HIP events), each after a 1 GiB read; steps: %d eager steps (sa_select per "
+                 "query head + gather-attend) after %d warmup; layer: the SPARSE layer call with "
+                 "per-query-head scores, back to back" % (max(5, args.cold_iters), n_steps, n_warm),
+                 {"ms_per_step": round((us_sel + us_att_step) / 1e3, 4),
+                  "steps_per_s": round(1e6 / (us_sel + us_att_step), 1),
+                  "config": {"workload": "llama32k with per-query-head index sets ([B, Hq, k])",
+                             "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d,
+                             "ctx_len": c.ctx_len, "k": k, "kv_dtype": c.dtype,
+                             "parallelism": "single GPU"},
+                  "kernels": kernels,
+                  "layer_us": round(us_layer, 1),
+                  "per_kv_head_step_us": round(us_kv_step, 1),
+                  "sparse_over_dense_speedup": round(us_dense / cold["attend"], 2),
+                  "layer_over_dense_speedup": round(us_dense / us_layer, 3),
+                  "generation_s": round(gen_s, 1), "upload_s": round(up_s, 1),
+                  "cpu_baseline": cpu})
+    line["roofline"]["cold_frac_of_same_bytes_stream"] = round(cold["stream"] / cold["attend"], 4)
+    print(json.dumps(line), flush=True)
+
+
+def perhead_cpu_baseline(w, att_bytes, seconds):
+    """The oracle, one BLAS thread, on whole query-head rows of one step until
+    `seconds` elapse: each head's exact scores over the cache, its top-k and
+    its attention over that set; scaled to the step's B * Hq rows."""
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+
+    c = w.cfg
+    scale = O.default_scale(c.head_dim)
+    rows = c.batch * c.n_q_heads
+    done = 0
+    t_att = t_step = 0.0
+    with threadpool_limits(limits=1):
+        t_all = time.perf_counter()
+        b_loaded = -1
+        for row in range(rows):
+            b, h = divmod(row, c.n_q_heads)
+            if b != b_loaded:
+                k_b, v_b = w.k(0, batch=(b, b + 1))[0], w.v(0, batch=(b, b + 1))[0]
+                qf = O.widen(w.q(0, batch=(b, b + 1))[0])
+                b_loaded = b
+            t0 = time.perf_counter()
+            kf = O.widen(k_b[h // c.group])
+            vf = O.widen(v_b[h // c.group])
+            qh = qf[h:h + 1]
+            t1 = time.perf_counter()
+            sel = O.topk(O.scores_exact(qh, kf, scale), c.k)
+            t2 = time.perf_counter()
+            O.attend(qh, kf, vf, sel, scale)
+            t3 = time.perf_counter()
+            t_att += (t1 - t0) + (t3 - t2)
+            t_step += t3 - t0
+            done += 1
+            if time.perf_counter() - t_all >= seconds:
+                break
+    att_s, step_s = t_att * rows / done, t_step * rows / done
+    cpu = {"value": round(att_bytes / att_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+           "kind": "oracle", "steps_per_s": round(1.0 / step_s, 4),
+           "attend_steps_per_s": round(1.0 / att_s, 4),
+           "sample": "fp64 numpy oracle, one thread: %d of the %d query-head rows of one step "
+                     "(exact scores, top-k, attention over the head's own set), scaled by %d/%d"
+                     % (done, rows, rows, done)}
+    cpu.update(host_cpu())
+    return cpu
+
+
 def bench_block61k(args):
     """batch 8, 32/8 heads, d 128, bf16, 61440 tokens = 480 blocks of 128, the
     top 24 blocks per (sequence, KV head) from per-block key min/max
@@ -1615,6 +1784,9 @@ def main():
         return
     if args.gpus == 1 and args.nscale:
         nscale(args)
+        return
+    if args.gpus == 1 and args.perhead:
+        bench_perhead(args)
         return
     if args.gpus == 1 and args.hylra:
         hylra(args)
