@@ -196,7 +196,9 @@ size_t sa_topk_workspace_size(int64_t n_rows, int64_t n, int32_t k);
  * position) candidates; a merge selects the row's top-k among them (every
  * element of the row's top-k is in its part's top-k).  When the candidates
  * would be more than a quarter of the row it runs sa_score and sa_topk
- * instead (same result).  ws: sa_select_workspace_size bytes (may be 0),
+ * instead (same result); so does SA_SCORE_EXACT_PER_Q_HEAD on rows longer
+ * than one part, whose scoring reads each key row once for the 2 or 4
+ * query heads of its KV head.  ws: sa_select_workspace_size bytes (may be 0),
  * 256-byte aligned; no state is kept in it between calls.
  * Errors: SA_ERR_NULL / SA_ERR_ALIGN for q, k_cache (16 bytes), idx_out or
  * the indexer tensors; SA_ERR_SHAPE for another kind, bad indexer sizes or k
