@@ -14,8 +14,8 @@
 //
 //  1. select_part_kernel: a row is cut into parts of L <= 8192 tokens; one
 //     workgroup (256 or 512 threads) streams its part's keys (the score
-//     kernel's arithmetic, bit for bit: group_query_sum, row_dot), keeps the part's
-//     scores in LDS, then runs the register-resident radix select
+//     kernel's arithmetic, bit for bit: group_query_sum, row_dot), keeps
+//     the part's scores in LDS, then runs the register-resident radix select
 //     (reg_row_topk) on them and writes the part's top-min(k, part length)
 //     as (score, position) candidates, in position order.
 //  2. Merge: the row's candidates, concatenated in part order (so in
@@ -35,7 +35,8 @@ namespace {
 
 constexpr int kIndexerNT = 512;  // threads of an indexer-score part
 constexpr int kChipCUs = 256;    // MI355X compute units
-constexpr int kPartMax = 8192;         // longest part: the register select at 4 * 8 keys per thread
+constexpr int kPartMax = 8192;         // longest part: what the register select holds (32 keys
+                                       // per thread at 256 threads, 16 at 512)
 constexpr int kPartAlign = 256;        // a multiple of every layout's tokens per iteration
 constexpr int kSelCand = kRankMax + 8; // threshold-bin candidates ranked in LDS
 constexpr int kMinGroups = 512;        // parts shrink (to 256 tokens) until the grid has this many
