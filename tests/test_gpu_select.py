@@ -48,6 +48,8 @@ CASES = [
     (1, 8, 8, 65536, 128, "bf16", 1500, "12000 candidates: 1024-thread merge"),
     (2, 8, 2, 32768, 128, "bf16", 12000, "fallback: candidates more than a quarter of the row"),
     (16, 32, 8, 32768, 128, "bf16", 3276, "fallback at 10x sparsity"),
+    (32, 64, 8, 2 * 8192 + 768, 64, "f32", 300, "f32, head_dim 64, 768 parts: 256-thread parts"),
+    (16, 32, 8, 2 * 8192, 64, "bf16", 300, "bf16, head_dim 64, 256 parts: 512-thread parts"),
 ]
 
 
