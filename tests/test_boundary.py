@@ -571,6 +571,38 @@ def test_bench_oracle_baseline_on_small_workloads(tmp_path):
         assert "%d units" % want in cpu["sample"], (name, cpu["sample"])
 
 
+def test_bench_perhead_oracle_baseline_on_a_small_workload():
+    """The cpu_baseline leg of bench.py --perhead (the oracle's per-query-head
+    step: each head's exact scores, its top-k and its attention) on a
+    shrunken llama32k workload: every row timed, the figures positive and
+    finite, and each head's set is its own top-k (the planted keys of its KV
+    head lead every head of the group)."""
+    import dataclasses
+    import math
+
+    import numpy as np
+
+    import bench
+    import oracle as O
+    import sa_synth as S
+    c = dataclasses.replace(S.CONFIGS["llama32k"], batch=2, ctx_len=2048, k=40, n_planted=20)
+    w = S.Workload(c, 0)
+    cpu = bench.perhead_cpu_baseline(w, 10 ** 6, 60.0)
+    rows = c.batch * c.n_q_heads
+    assert cpu["cores"] == 1 and cpu["kind"] == "oracle"
+    assert "%d of the %d query-head rows" % (rows, rows) in cpu["sample"], cpu["sample"]
+    for v in (cpu["value"], cpu["steps_per_s"], cpu["attend_steps_per_s"]):
+        assert v > 0 and math.isfinite(v), cpu
+    # the unit the leg times, for one head: its own top-k holds its KV head's planted keys
+    scale = O.default_scale(c.head_dim)
+    qf = O.widen(w.q(0, batch=(0, 1))[0])
+    kf = O.widen(w.k(0, batch=(0, 1))[0])
+    for h in (0, c.n_q_heads - 1):
+        sel = O.topk(O.scores_exact(qf[h:h + 1], kf[h // c.group], scale), c.k)
+        planted = np.asarray(w.planted(0, 0, h // c.group))
+        assert np.isin(planted, sel).all(), h
+
+
 @pytest.mark.parametrize("lang,compiler", [("c", "gcc"), ("c++", "g++")])
 def test_header_compiles_as_c_and_cxx(tmp_path, lang, compiler):
     """include/sa.h is a C header usable from C and C++, and its enumerations
