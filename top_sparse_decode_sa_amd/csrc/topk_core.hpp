@@ -27,6 +27,7 @@ struct SharedT {
   uint32_t hist2[3][256];  // digit passes of a register row, one histogram per pass
   uint32_t tot[NT / 64];
   uint32_t digit, above, count, T, cgt, base;
+  uint32_t bc[4];  // a leader wave's selection, broadcast to the workgroup
 };
 
 // Workgroup-wide exclusive prefix sum; also returns the total.  Uses sh.tot
@@ -219,8 +220,10 @@ __device__ __forceinline__ uint32_t wave_select_bin(const uint32_t* h, uint32_t 
 //   HIST: sh.hist already holds the 12-bit histogram of the row's keys (the
 //     caller counted them as they were produced), so the load adds nothing.
 //
-// Phases, each wave finding every digit itself (wave_select_bin) so that the
-// only barriers are those that complete a histogram:
+// Phases; wave 0 finds each digit (wave_select_bin) and ranks the last
+// candidates, and hands the result to the other waves through LDS (one wave's
+// scans instead of every wave's: with several waves per SIMD the repeated
+// scans cost more issue cycles than the barriers that broadcast the result):
 //   1. histogram of the top 12 key bits; the bin d1 of the k-th largest key;
 //   2. within bin d1, 8-, 8- and 4-bit digit passes over the keys still
 //      matching (one histogram each) until at most kRankMax keys remain or all
@@ -262,8 +265,21 @@ __device__ __forceinline__ void reg_row_topk(Load load, int n, int32_t k, Emit e
       }
   }
   __syncthreads();
-  uint32_t above, cnt;
-  const uint32_t d1 = wave_select_bin<kBins>(sh.hist, (uint32_t)k, &above, &cnt);
+  // wave 0 finds the digit and hands it to the others (one wave's scan of
+  // the histogram instead of every wave's)
+  if (wave == 0) {
+    uint32_t a0, c0;
+    const uint32_t d0 = wave_select_bin<kBins>(sh.hist, (uint32_t)k, &a0, &c0);
+    if (lane == 0) {
+      sh.bc[0] = d0;
+      sh.bc[1] = a0;
+      sh.bc[2] = c0;
+    }
+  }
+  __syncthreads();
+  const uint32_t d1 = sh.bc[0];
+  const uint32_t above = sh.bc[1];
+  uint32_t cnt = sh.bc[2];
   uint32_t kleft = (uint32_t)k - above;
   uint32_t prefix = d1 << 20, mask = 0xfff00000u;
 
@@ -297,11 +313,22 @@ __device__ __forceinline__ void reg_row_topk(Load load, int n, int32_t k, Emit e
         if (((m_cand >> (4 * j + e)) & 1u) && (key[j][e] & mask) == prefix)
           atomicAdd(&h2[(key[j][e] >> shift) & dmask], 1u);
     __syncthreads();
-    uint32_t a2, c2, d2;
-    if (level < 2)
-      d2 = wave_select_bin<256>(h2, kleft, &a2, &c2);
-    else
-      d2 = wave_select_bin<16>(h2, kleft, &a2, &c2);
+    if (wave == 0) {
+      uint32_t a, c, d;
+      if (level < 2)
+        d = wave_select_bin<256>(h2, kleft, &a, &c);
+      else
+        d = wave_select_bin<16>(h2, kleft, &a, &c);
+      if (lane == 0) {
+        sh.bc[0] = d;
+        sh.bc[1] = a;
+        sh.bc[2] = c;
+      }
+    }
+    __syncthreads();
+    // (bc is written again only after the next level's or the ranking's
+    // barrier, which every wave reaches after this read)
+    const uint32_t d2 = sh.bc[0], a2 = sh.bc[1], c2 = sh.bc[2];
     prefix |= d2 << shift;
     mask |= dmask << shift;
     kleft -= a2;
@@ -341,19 +368,28 @@ __device__ __forceinline__ void reg_row_topk(Load load, int n, int32_t k, Emit e
     // a key (key 0, last position)
     if (tid < 4 && cnt + tid < ((cnt + 3u) & ~3u)) cand[cnt + tid] = make_uint2(0u, 0xffffffffu);
     __syncthreads();
-    const uint2 me = cand[lane < (int)cnt ? lane : 0];
-    uint32_t rank = 0;
-    for (uint32_t i = 0; i < cnt; i += 4) {
-      uint2 o[4];
+    // wave 0 ranks them and hands T and need to the others
+    if (wave == 0) {
+      const uint2 me = cand[lane < (int)cnt ? lane : 0];
+      uint32_t rank = 0;
+      for (uint32_t i = 0; i < cnt; i += 4) {
+        uint2 o[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) o[u] = cand[i + u];
+        for (int u = 0; u < 4; ++u) o[u] = cand[i + u];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) rank += (o[u].x > me.x || (o[u].x == me.x && o[u].y < me.y)) ? 1u : 0u;
+        for (int u = 0; u < 4; ++u) rank += (o[u].x > me.x || (o[u].x == me.x && o[u].y < me.y)) ? 1u : 0u;
+      }
+      const uint64_t at = __ballot(lane < (int)cnt && rank == kleft - 1);
+      const uint32_t t = __shfl(me.x, __builtin_ctzll(at), 64);
+      const uint64_t gt = __ballot(lane < (int)cnt && me.x > t);
+      if (lane == 0) {
+        sh.bc[0] = t;
+        sh.bc[1] = kleft - (uint32_t)__builtin_popcountll(gt);
+      }
     }
-    const uint64_t at = __ballot(lane < (int)cnt && rank == kleft - 1);
-    T = __shfl(me.x, __builtin_ctzll(at), 64);
-    const uint64_t gt = __ballot(lane < (int)cnt && me.x > T);
-    need = kleft - (uint32_t)__builtin_popcountll(gt);
+    __syncthreads();
+    T = sh.bc[0];
+    need = sh.bc[1];
   }
   uint32_t m_gt = m_above, m_eq = 0;  // kept above T, equal to T
 #pragma unroll
