@@ -778,9 +778,19 @@ __global__ __launch_bounds__(kThreads) void topk_mw_finish(const float* __restri
   }
   // the second digit (key bits 19..8) from the collected histogram of bin
   // d1; its keys (the sub-bin) are copied to `sub` and resolved there
-  uint32_t above2, c2;
-  const uint32_t d2 = wave_select_bin<kBins>(sh.hist, kleft, &above2, &c2);
-  __syncthreads();  // every wave has read sh.hist before resolve may reuse it
+  // (wave 0 finds it and hands it to the other waves, as the register top-k
+  // does; after the barrier resolve may reuse sh.hist)
+  if ((tid >> 6) == 0) {
+    uint32_t a, c;
+    const uint32_t d = wave_select_bin<kBins>(sh.hist, kleft, &a, &c);
+    if (tid == 0) {
+      sh.bc[0] = d;
+      sh.bc[1] = a;
+      sh.bc[2] = c;
+    }
+  }
+  __syncthreads();
+  const uint32_t d2 = sh.bc[0], above2 = sh.bc[1], c2 = sh.bc[2];
   const uint32_t kleft2 = kleft - above2;
   const uint32_t prefix2 = prefix | (d2 << 8), mask2 = 0xffffff00u;
   uint2* sub = cand + (kMwCand + 32);  // [c2 <= kRankCap, padded]
